@@ -1,0 +1,225 @@
+"""Routed FP8 (E4M3, 128x128 block-scaled) MoE expert FFN for MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``include/moe_fp8.h``
+(``libmoe_fp8.so``): it checks dtypes, devices, shapes and contiguity of
+torch tensors and passes raw device pointers and the current HIP stream.
+Every step of the layer runs in the library's HIP kernels; there is no
+Python or CPU fallback -- if the library is not built, every call raises.
+PyTorch only supplies device memory and streams.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_fp8.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID = -1
+MOE_ERR_UNSUPPORTED = -2
+MOE_ERR_WORKSPACE = -3
+MOE_ERR_HIP = -4
+
+MAX_EXPERTS = 256
+MAX_TOPK = 16
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+
+
+class WsLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in (
+        "topk_ids", "topk_w", "xq", "xs", "counts", "offsets", "sorted", "active",
+        "num_active", "gate_up", "act2", "act2_scale", "partial", "total")] + [("path", ctypes.c_int)]
+
+
+_SIGS = {
+    "moe_fp8_status_string": (ctypes.c_char_p, [_I]),
+    "moe_fp8_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
+    "moe_fp8_bind_workspace": (_I, [_P, _SZ]),
+    "moe_fp8_forward": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "moe_fp8_forward_ws": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _SZ, _P]),
+    "moe_fp8_workspace_layout": (_I, [_I, _I, _I, _I, _I, ctypes.POINTER(WsLayout)]),
+    "router_topk": (_I, [_P, _I, _I, _I, _P, _P, _P]),
+    "moe_fp8_act_quant": (_I, [_P, _I, _I, _P, _P, _P]),
+    "moe_fp8_group_workspace_bytes": (_SZ, [_I, _I, _I]),
+    "moe_fp8_group": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
+    "moe_fp8_quantize_weight_block128": (_I, [_P, _I64, _I, _I, _P, _P, _P]),
+    "moe_fp8_encode_e4m3": (_I, [_P, _I64, _P, _P]),
+}
+
+
+def lib():
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run fp8_block_scaled_router_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().moe_fp8_status_string(int(status)).decode()
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != MOE_OK:
+        raise MoeError(rc, what)
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t: torch.Tensor):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, dtype, name, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def workspace_bytes(M: int, h: int, i: int, E: int, k: int) -> int:
+    return int(lib().moe_fp8_workspace_bytes(M, h, i, E, k))
+
+
+def workspace_layout(M: int, h: int, i: int, E: int, k: int) -> WsLayout:
+    L = WsLayout()
+    _check(lib().moe_fp8_workspace_layout(M, h, i, E, k, ctypes.byref(L)), "moe_fp8_workspace_layout")
+    return L
+
+
+def alloc_workspace(M: int, h: int, i: int, E: int, k: int, device=None) -> torch.Tensor:
+    n = max(workspace_bytes(M, h, i, E, k), 256)
+    return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+
+
+_bound = {}
+
+
+def bind_workspace(ws: torch.Tensor | None) -> None:
+    """Bind `ws` as the workspace moe_fp8_forward uses on ws's device (the
+    tensor is kept alive here while bound); None unbinds the current device."""
+    if ws is None:
+        _check(lib().moe_fp8_bind_workspace(None, 0), "moe_fp8_bind_workspace")
+        _bound.pop(torch.cuda.current_device(), None)
+        return
+    _dev(ws, torch.uint8, "workspace")
+    with torch.cuda.device(ws.device):
+        _check(lib().moe_fp8_bind_workspace(_ptr(ws), ws.numel()), "moe_fp8_bind_workspace")
+    _bound[ws.device.index] = ws
+
+
+def _layer_args(x, router_logits, w13, s13, w2, s2, k, out):
+    M, h = x.shape
+    E = router_logits.shape[1]
+    i = w2.shape[2]
+    _dev(x, torch.bfloat16, "x", (M, h))
+    _dev(router_logits, torch.float32, "router_logits", (M, E))
+    _dev(w13, torch.float8_e4m3fn, "w13", (E, 2 * i, h))
+    _dev(s13, torch.float32, "s13", (E, 2 * i // 128, h // 128))
+    _dev(w2, torch.float8_e4m3fn, "w2", (E, h, i))
+    _dev(s2, torch.float32, "s2", (E, h // 128, i // 128))
+    if out is None:
+        out = torch.empty((M, h), dtype=torch.bfloat16, device=x.device)
+    _dev(out, torch.bfloat16, "out", (M, h))
+    return M, h, i, E, out
+
+
+def moe_fp8_forward(x, router_logits, w13, s13, w2, s2, k: int, out=None, stream=None):
+    """The layer with the workspace bound by bind_workspace()."""
+    M, h, i, E, out = _layer_args(x, router_logits, w13, s13, w2, s2, k, out)
+    rc = lib().moe_fp8_forward(_ptr(x), _ptr(router_logits), _ptr(w13), _ptr(s13), _ptr(w2), _ptr(s2),
+                               _ptr(out), M, h, i, E, int(k), _stream(stream))
+    _check(rc, "moe_fp8_forward")
+    return out
+
+
+def moe_fp8_forward_ws(x, router_logits, w13, s13, w2, s2, k: int, workspace, out=None, stream=None):
+    """The layer with an explicit workspace tensor (uint8, on the same device)."""
+    M, h, i, E, out = _layer_args(x, router_logits, w13, s13, w2, s2, k, out)
+    _dev(workspace, torch.uint8, "workspace")
+    rc = lib().moe_fp8_forward_ws(_ptr(x), _ptr(router_logits), _ptr(w13), _ptr(s13), _ptr(w2),
+                                  _ptr(s2), _ptr(out), M, h, i, E, int(k), _ptr(workspace),
+                                  workspace.numel(), _stream(stream))
+    _check(rc, "moe_fp8_forward_ws")
+    return out
+
+
+def router_topk(logits, k: int, stream=None):
+    M, E = logits.shape
+    _dev(logits, torch.float32, "logits")
+    ids = torch.empty((M, k), dtype=torch.int32, device=logits.device)
+    w = torch.empty((M, k), dtype=torch.float32, device=logits.device)
+    _check(lib().router_topk(_ptr(logits), M, E, int(k), _ptr(ids), _ptr(w), _stream(stream)), "router_topk")
+    return ids, w
+
+
+def act_quant(x, stream=None):
+    M, K = x.shape
+    _dev(x, torch.bfloat16, "x")
+    q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    s = torch.empty((M, K // 128), dtype=torch.float32, device=x.device)
+    _check(lib().moe_fp8_act_quant(_ptr(x), M, K, _ptr(q), _ptr(s), _stream(stream)), "moe_fp8_act_quant")
+    return q, s
+
+
+def group(topk_ids, E: int, stream=None):
+    _dev(topk_ids, torch.int32, "topk_ids")
+    M, k = topk_ids.shape
+    dev = topk_ids.device
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    srt = torch.empty(M * k, dtype=torch.int32, device=dev)
+    nws = max(int(lib().moe_fp8_group_workspace_bytes(M, E, k)), 256)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    _check(lib().moe_fp8_group(_ptr(topk_ids), M, E, k, _ptr(counts), _ptr(offsets), _ptr(srt),
+                               _ptr(ws), nws, _stream(stream)), "moe_fp8_group")
+    return counts, offsets, srt
+
+
+def quantize_weight_block128(w, stream=None):
+    """fp32 [B, N, K] on the GPU -> (float8_e4m3fn [B, N, K], fp32 scales [B, N/128, K/128])."""
+    _dev(w, torch.float32, "w")
+    B, N, K = w.shape
+    q = torch.empty((B, N, K), dtype=torch.float8_e4m3fn, device=w.device)
+    s = torch.empty((B, N // 128, K // 128), dtype=torch.float32, device=w.device)
+    _check(lib().moe_fp8_quantize_weight_block128(_ptr(w), B, N, K, _ptr(q), _ptr(s), _stream(stream)),
+           "moe_fp8_quantize_weight_block128")
+    return q, s
+
+
+def encode_e4m3(v, stream=None):
+    _dev(v, torch.float32, "v")
+    out = torch.empty(v.shape, dtype=torch.uint8, device=v.device)
+    _check(lib().moe_fp8_encode_e4m3(_ptr(v), v.numel(), _ptr(out), _stream(stream)), "moe_fp8_encode_e4m3")
+    return out

@@ -1,0 +1,136 @@
+// group.hip -- deterministic grouping of the M*k routes by expert
+// (Netra Kernel README, MoE prefill pair: the metadata stage; Inferact
+// amd-kernels README, atomics rule: atomics may count, never decide order).
+//
+// Pass 1: one workgroup per chunk of routes counts routes per expert with
+// LDS atomic increments (an integer count does not depend on their order).
+// Pass 2: one wave per chunk derives every expert's global offset and its
+// chunk-local start from the chunk histograms, then scatters the chunk's
+// routes in route order, 64 at a time: a lane's rank among equal experts in
+// its batch comes from a ballot match over the 9 bits of the expert id, so
+// the sorted order is route id ascending inside each expert by construction.
+// Chunk 0 also writes counts, offsets and the ascending list of experts that
+// received routes.
+#include "device.h"
+#include "launch.h"
+
+namespace moe {
+
+constexpr int kChunk = 4096;
+
+int group_chunks(int R) { return R <= 0 ? 1 : (R + kChunk - 1) / kChunk; }
+
+__global__ __launch_bounds__(256) void group_hist_kernel(const int32_t* __restrict__ ids, int R, int E,
+                                                         int32_t* __restrict__ hist) {
+    __shared__ int cnt[256];
+    for (int e = threadIdx.x; e < E; e += 256) cnt[e] = 0;
+    __syncthreads();
+    const int beg = blockIdx.x * kChunk;
+    const int end = min(R, beg + kChunk);
+    for (int p = beg + threadIdx.x; p < end; p += 256) {
+        const int e = ids[p];
+        if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);   // ids outside [0, E) are dropped
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 256) hist[(size_t)blockIdx.x * E + e] = cnt[e];
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(v, d, kWave);
+        if (lane >= d) v += o;
+    }
+    return v;
+}
+
+__global__ __launch_bounds__(64) void group_scatter_kernel(
+    const int32_t* __restrict__ ids, int R, int E, int nchunks, const int32_t* __restrict__ hist,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted,
+    int32_t* __restrict__ active, int32_t* __restrict__ num_active) {
+    __shared__ int base[256];
+    const int chunk = blockIdx.x;
+    const int lane = threadIdx.x;
+    // Lane l owns experts 4l .. 4l+3.
+    int tot[4], pre[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = 4 * lane + j;
+        int s = 0, p = 0;
+        if (e < E) {
+            for (int c = 0; c < nchunks; ++c) {
+                const int v = hist[(size_t)c * E + e];
+                if (c < chunk) p += v;
+                s += v;
+            }
+        }
+        tot[j] = s;
+        pre[j] = p;
+    }
+    const int lsum = tot[0] + tot[1] + tot[2] + tot[3];
+    const int lact = (tot[0] > 0) + (tot[1] > 0) + (tot[2] > 0) + (tot[3] > 0);
+    const int incl = wave_incl_scan(lsum, lane);
+    const int iact = wave_incl_scan(lact, lane);
+    int run = incl - lsum, arun = iact - lact;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = 4 * lane + j;
+        if (e < E) {
+            base[e] = run + pre[j];
+            if (chunk == 0) {
+                offsets[e] = run;
+                counts[e] = tot[j];
+                if (tot[j] > 0) active[arun] = e;
+            }
+        }
+        run += tot[j];
+        arun += (tot[j] > 0);
+    }
+    if (chunk == 0 && lane == 63) {
+        offsets[E] = incl;
+        *num_active = iact;
+    }
+    __syncthreads();
+
+    const int beg = chunk * kChunk;
+    const int end = min(R, beg + kChunk);
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int p0 = beg; p0 < end; p0 += 64) {
+        const int p = p0 + lane;
+        int e = p < end ? ids[p] : 0x1FF;
+        const bool valid = (unsigned)e < (unsigned)E;
+        if (!valid) e = 0x1FF;
+        uint64_t same = ~0ull;
+#pragma unroll
+        for (int b = 0; b < 9; ++b) {
+            const bool bit = (e >> b) & 1;
+            const uint64_t bal = __ballot(bit);
+            same &= bit ? bal : ~bal;
+        }
+        const int rank = __popcll(same & below);
+        const bool last = (same >> lane) == 1ull;   // highest lane of its expert in this batch
+        int pos = 0;
+        if (valid) pos = base[e] + rank;
+        __syncthreads();
+        if (valid) {
+            sorted[pos] = p;
+            if (last) base[e] += __popcll(same);
+        }
+        __syncthreads();
+    }
+}
+
+hipError_t launch_group(const int32_t* ids, int R, int E, int32_t* hist, int32_t* counts,
+                        int32_t* offsets, int32_t* sorted, int32_t* active, int32_t* num_active,
+                        hipStream_t stream) {
+    const int nchunks = group_chunks(R);
+    hipLaunchKernelGGL(group_hist_kernel, dim3(nchunks), dim3(256), 0, stream, ids, R, E, hist);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(group_scatter_kernel, dim3(nchunks), dim3(64), 0, stream, ids, R, E, nchunks,
+                       hist, counts, offsets, sorted, active, num_active);
+    return hipGetLastError();
+}
+
+}  // namespace moe

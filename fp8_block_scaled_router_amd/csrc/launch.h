@@ -1,0 +1,47 @@
+// launch.h -- host-side launchers of the gfx950 kernels (internal to the
+// library; the public C ABI is include/moe_fp8.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Router and/or 1x128 activation quantisation, one workgroup per token.
+enum { kRoute = 1, kQuant = 2 };
+hipError_t launch_route_quant(const float* logits, const uint16_t* x, int M, int E, int k, int h,
+                              int32_t* ids, float* tw, uint8_t* xq, float* xs, int what,
+                              hipStream_t stream);
+
+// Grouping of R routes by expert: per-chunk histograms, then an ordered
+// scatter.  `hist` holds group_chunks(R) * E ints.
+int group_chunks(int R);
+hipError_t launch_group(const int32_t* ids, int R, int E, int32_t* hist, int32_t* counts,
+                        int32_t* offsets, int32_t* sorted, int32_t* active, int32_t* num_active,
+                        hipStream_t stream);
+
+// Weight-streaming grouped GEMMs (few tokens per expert).
+struct StreamArgs {
+    const int32_t* offsets;
+    const int32_t* sorted;
+    const int32_t* active;
+    const int32_t* num_active;
+    int max_slots;   // upper bound on the number of distinct experts (min(E, M*k))
+    int h, i, k;
+};
+hipError_t launch_stream_gate_up(const StreamArgs& a, const uint8_t* xq, const float* xs,
+                                 const uint8_t* w13, const float* s13, float* g, hipStream_t stream);
+hipError_t launch_stream_down(const StreamArgs& a, const float* g, const uint8_t* w2, const float* s2,
+                              float* y, hipStream_t stream);
+
+// Fixed-order combine of the k route partials of each token into bf16.
+hipError_t launch_combine(const float* y, const float* tw, int M, int k, int h, uint16_t* out,
+                          hipStream_t stream);
+
+// Utilities.
+hipError_t launch_quant_weight(const float* w, int64_t batch, int N, int K, uint8_t* q, float* s,
+                               hipStream_t stream);
+hipError_t launch_encode_e4m3(const float* in, int64_t n, uint8_t* out, hipStream_t stream);
+
+}  // namespace moe

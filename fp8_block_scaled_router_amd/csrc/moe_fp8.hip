@@ -1,0 +1,316 @@
+// moe_fp8.hip -- the C ABI (include/moe_fp8.h): argument checks, workspace
+// layout, per-device workspace binding and the enqueue of the layer's
+// kernels on the caller's stream.
+//
+// Interface style follows the Netra Kernel README (runtime C ABI: bind
+// persistent buffers, launch on a caller-provided stream) and the Netra
+// compiler architecture page (compile/init/launch flow: the launch path does
+// a numeric guard and launches, with no allocation, lookup or parsing;
+// unsupported contracts return a fallback status).
+#include <mutex>
+
+#include "../../include/moe_fp8.h"
+#include "launch.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxDevices = 64;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Binding {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_bind_mu;
+Binding g_bind[kMaxDevices];
+
+// Shape checks shared by every entry point of the layer.
+int check_shape(int M, int h, int i, int E, int k) {
+    if (M < 0 || h <= 0 || i <= 0 || E <= 0 || k <= 0) return MOE_ERR_INVALID;
+    if (h % 128 != 0 || i % 128 != 0) return MOE_ERR_UNSUPPORTED;
+    if (h > MOE_FP8_MAX_HIDDEN || i > MOE_FP8_MAX_INTERMEDIATE) return MOE_ERR_UNSUPPORTED;
+    if (E > MOE_FP8_MAX_EXPERTS || k > MOE_FP8_MAX_TOPK || k > E) return MOE_ERR_UNSUPPORTED;
+    if ((int64_t)M * k > (int64_t)1 << 28) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+struct Layout {
+    moe_fp8_ws_layout pub;
+    size_t hist;   // grouping scratch: group_chunks(R) * E ints
+};
+
+void make_layout(int M, int h, int i, int E, int k, Layout* L) {
+    const size_t R = (size_t)M * k;
+    size_t cur = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = cur;
+        cur = align_up(cur + bytes);
+        return o;
+    };
+    moe_fp8_ws_layout& p = L->pub;
+    p.topk_ids = take(R * 4);
+    p.topk_w = take(R * 4);
+    p.xq = take((size_t)M * h);
+    p.xs = take((size_t)M * (h / 128) * 4);
+    p.counts = take((size_t)E * 4);
+    p.offsets = take((size_t)(E + 1) * 4);
+    p.sorted = take(R * 4);
+    p.active = take((size_t)E * 4);
+    p.num_active = take(4);
+    L->hist = take((size_t)moe::group_chunks((int)R) * E * 4);
+    p.path = 0;
+    p.gate_up = take(R * 2 * i * 4);
+    p.act2 = (size_t)-1;
+    p.act2_scale = (size_t)-1;
+    p.partial = take(R * h * 4);
+    p.total = cur;
+}
+
+template <typename T>
+T* at(void* base, size_t off) {
+    return reinterpret_cast<T*>(static_cast<uint8_t*>(base) + off);
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Kernels of one forward, in launch order (the streaming path).
+struct NameList {
+    const char* names[5] = {"route_quant_kernel", "group_hist+group_scatter",
+                            "stream_gate_up_kernel", "stream_down_kernel", "combine_kernel"};
+    int size() const { return 5; }
+    const char* operator[](int j) const { return names[j]; }
+};
+const NameList kForwardKernelNames;
+
+// Records events[j] (when given) before stage j, and events[n] after the last.
+struct EventHook {
+    hipEvent_t* ev;
+    int n;
+    int next = 0;
+    hipStream_t s;
+    hipError_t mark() {
+        if (!ev || next >= n) return hipSuccess;
+        return hipEventRecord(ev[next++], s);
+    }
+};
+
+int run_forward(const void* x, const float* router_logits, const void* w13, const float* s13,
+                const void* w2, const float* s2, void* out, int M, int h, int i, int E, int k,
+                void* workspace, size_t workspace_bytes, hipEvent_t* events, int n_events,
+                hipStream_t stream) {
+    int rc = check_shape(M, h, i, E, k);
+    if (rc != MOE_OK) return rc;
+    if (M == 0) return MOE_OK;
+    if (!x || !router_logits || !w13 || !s13 || !w2 || !s2 || !out) return MOE_ERR_INVALID;
+    if (!aligned16(x) || !aligned16(router_logits) || !aligned16(w13) || !aligned16(s13) ||
+        !aligned16(w2) || !aligned16(s2) || !aligned16(out))
+        return MOE_ERR_INVALID;
+    Layout L;
+    make_layout(M, h, i, E, k, &L);
+    if (!workspace || ((uintptr_t)workspace % kAlign) != 0 || workspace_bytes < L.pub.total)
+        return MOE_ERR_WORKSPACE;
+
+    const moe_fp8_ws_layout& p = L.pub;
+    const int R = M * k;
+    int32_t* ids = at<int32_t>(workspace, p.topk_ids);
+    float* tw = at<float>(workspace, p.topk_w);
+    uint8_t* xq = at<uint8_t>(workspace, p.xq);
+    float* xs = at<float>(workspace, p.xs);
+    int32_t* counts = at<int32_t>(workspace, p.counts);
+    int32_t* offsets = at<int32_t>(workspace, p.offsets);
+    int32_t* sorted = at<int32_t>(workspace, p.sorted);
+    int32_t* active = at<int32_t>(workspace, p.active);
+    int32_t* num_active = at<int32_t>(workspace, p.num_active);
+    int32_t* hist = at<int32_t>(workspace, L.hist);
+    float* g = at<float>(workspace, p.gate_up);
+    float* y = at<float>(workspace, p.partial);
+    EventHook hook{events, n_events, 0, stream};
+
+#define MOE_STEP(call)                                      \
+    do {                                                    \
+        if (hook.mark() != hipSuccess) return MOE_ERR_HIP; \
+        rc = hip_status(call);                              \
+        if (rc != MOE_OK) return rc;                        \
+    } while (0)
+
+    MOE_STEP(moe::launch_route_quant(router_logits, static_cast<const uint16_t*>(x), M, E, k, h,
+                                     ids, tw, xq, xs, moe::kRoute | moe::kQuant, stream));
+    MOE_STEP(moe::launch_group(ids, R, E, hist, counts, offsets, sorted, active, num_active,
+                               stream));
+    moe::StreamArgs sa;
+    sa.offsets = offsets;
+    sa.sorted = sorted;
+    sa.active = active;
+    sa.num_active = num_active;
+    sa.max_slots = E < R ? E : R;
+    sa.h = h;
+    sa.i = i;
+    sa.k = k;
+    MOE_STEP(moe::launch_stream_gate_up(sa, xq, xs, static_cast<const uint8_t*>(w13), s13, g,
+                                        stream));
+    MOE_STEP(moe::launch_stream_down(sa, g, static_cast<const uint8_t*>(w2), s2, y, stream));
+    MOE_STEP(moe::launch_combine(y, tw, M, k, h, static_cast<uint16_t*>(out), stream));
+#undef MOE_STEP
+    return hook.mark() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_fp8_status_string(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported shape";
+        case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+        case MOE_ERR_HIP: return "HIP error";
+        default: return "unknown status";
+    }
+}
+
+int moe_fp8_workspace_layout(int M, int h, int i, int E, int k, moe_fp8_ws_layout* layout) {
+    if (!layout) return MOE_ERR_INVALID;
+    const int rc = check_shape(M, h, i, E, k);
+    if (rc != MOE_OK) return rc;
+    Layout L;
+    make_layout(M, h, i, E, k, &L);
+    *layout = L.pub;
+    return MOE_OK;
+}
+
+size_t moe_fp8_workspace_bytes(int M, int h, int i, int E, int k) {
+    if (M == 0 || check_shape(M, h, i, E, k) != MOE_OK) return 0;
+    Layout L;
+    make_layout(M, h, i, E, k, &L);
+    return L.pub.total;
+}
+
+int moe_fp8_bind_workspace(void* dev_ptr, size_t bytes) {
+    if (dev_ptr && ((uintptr_t)dev_ptr % kAlign) != 0) return MOE_ERR_INVALID;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_bind_mu);
+    g_bind[dev].ptr = dev_ptr;
+    g_bind[dev].bytes = dev_ptr ? bytes : 0;
+    return MOE_OK;
+}
+
+int moe_fp8_forward_ws(const void* x, const float* router_logits, const void* w13,
+                       const float* s13, const void* w2, const float* s2, void* out, int M, int h,
+                       int i, int E, int k, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+    return run_forward(x, router_logits, w13, s13, w2, s2, out, M, h, i, E, k, workspace,
+                       workspace_bytes, nullptr, 0, stream);
+}
+
+int moe_fp8_forward_ws_timed(const void* x, const float* router_logits, const void* w13,
+                             const float* s13, const void* w2, const float* s2, void* out, int M,
+                             int h, int i, int E, int k, void* workspace, size_t workspace_bytes,
+                             hipEvent_t* events, int n_events, hipStream_t stream) {
+    if (!events) return MOE_ERR_INVALID;
+    const int n = moe_fp8_forward_kernel_count(M, h, i, E, k);
+    if (n < 0) return n;
+    if (n_events < n + 1) return MOE_ERR_INVALID;
+    return run_forward(x, router_logits, w13, s13, w2, s2, out, M, h, i, E, k, workspace,
+                       workspace_bytes, events, n_events, stream);
+}
+
+int moe_fp8_forward_kernel_count(int M, int h, int i, int E, int k) {
+    const int rc = check_shape(M, h, i, E, k);
+    if (rc != MOE_OK) return rc;
+    if (M == 0) return 0;
+    return kForwardKernelNames.size();
+}
+
+const char* moe_fp8_forward_kernel_name(int M, int h, int i, int E, int k, int j) {
+    const int n = moe_fp8_forward_kernel_count(M, h, i, E, k);
+    if (n <= 0 || j < 0 || j >= n) return nullptr;
+    return kForwardKernelNames[j];
+}
+
+int moe_fp8_forward(const void* x, const float* router_logits, const void* w13, const float* s13,
+                    const void* w2, const float* s2, void* out, int M, int h, int i, int E, int k,
+                    hipStream_t stream) {
+    const int rc = check_shape(M, h, i, E, k);
+    if (rc != MOE_OK) return rc;
+    if (M == 0) return MOE_OK;
+    if (!x || !router_logits || !w13 || !s13 || !w2 || !s2 || !out) return MOE_ERR_INVALID;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+    Binding b;
+    {
+        std::lock_guard<std::mutex> lock(g_bind_mu);
+        b = g_bind[dev];
+    }
+    if (!b.ptr) return MOE_ERR_WORKSPACE;
+    return moe_fp8_forward_ws(x, router_logits, w13, s13, w2, s2, out, M, h, i, E, k, b.ptr, b.bytes,
+                              stream);
+}
+
+int router_topk(const float* logits, int M, int E, int k, int32_t* topk_ids, float* topk_w,
+                hipStream_t stream) {
+    if (M < 0 || E <= 0 || k <= 0) return MOE_ERR_INVALID;
+    if (E > MOE_FP8_MAX_EXPERTS || k > MOE_FP8_MAX_TOPK || k > E) return MOE_ERR_UNSUPPORTED;
+    if (M == 0) return MOE_OK;
+    if (!logits || !topk_ids || !topk_w) return MOE_ERR_INVALID;
+    return hip_status(moe::launch_route_quant(logits, nullptr, M, E, k, 128, topk_ids, topk_w,
+                                              nullptr, nullptr, moe::kRoute, stream));
+}
+
+int moe_fp8_act_quant(const void* x, int M, int K, uint8_t* q, float* s, hipStream_t stream) {
+    if (M < 0 || K <= 0) return MOE_ERR_INVALID;
+    if (K % 128 != 0 || K > MOE_FP8_MAX_HIDDEN) return MOE_ERR_UNSUPPORTED;
+    if (M == 0) return MOE_OK;
+    if (!x || !q || !s) return MOE_ERR_INVALID;
+    if (!aligned16(x) || !aligned16(q)) return MOE_ERR_INVALID;
+    return hip_status(moe::launch_route_quant(nullptr, static_cast<const uint16_t*>(x), M, 1, 1, K,
+                                              nullptr, nullptr, q, s, moe::kQuant, stream));
+}
+
+size_t moe_fp8_group_workspace_bytes(int M, int E, int k) {
+    if (M < 0 || E <= 0 || k <= 0 || E > MOE_FP8_MAX_EXPERTS) return 0;
+    return align_up((size_t)moe::group_chunks(M * k) * E * 4 + 2 * (size_t)E * 4 + 64);
+}
+
+int moe_fp8_group(const int32_t* topk_ids, int M, int E, int k, int32_t* counts, int32_t* offsets,
+                  int32_t* sorted_route_ids, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream) {
+    if (M < 0 || E <= 0 || k <= 0) return MOE_ERR_INVALID;
+    if (E > MOE_FP8_MAX_EXPERTS || k > MOE_FP8_MAX_TOPK || k > E) return MOE_ERR_UNSUPPORTED;
+    if ((int64_t)M * k > (int64_t)1 << 28) return MOE_ERR_UNSUPPORTED;
+    if (!counts || !offsets) return MOE_ERR_INVALID;
+    if (M > 0 && (!topk_ids || !sorted_route_ids)) return MOE_ERR_INVALID;
+    if (!workspace || workspace_bytes < moe_fp8_group_workspace_bytes(M, E, k))
+        return MOE_ERR_WORKSPACE;
+    const int R = M * k;
+    int32_t* hist = static_cast<int32_t*>(workspace);
+    int32_t* active = hist + (size_t)moe::group_chunks(R) * E;
+    int32_t* num_active = active + E;
+    return hip_status(moe::launch_group(topk_ids, R, E, hist, counts, offsets, sorted_route_ids,
+                                        active, num_active, stream));
+}
+
+int moe_fp8_quantize_weight_block128(const float* w, int64_t batch, int N, int K, uint8_t* q,
+                                     float* s, hipStream_t stream) {
+    if (batch < 0 || N <= 0 || K <= 0) return MOE_ERR_INVALID;
+    if (N % 128 != 0 || K % 128 != 0) return MOE_ERR_UNSUPPORTED;
+    if (batch == 0) return MOE_OK;
+    if (!w || !q || !s || !aligned16(w) || !aligned16(q)) return MOE_ERR_INVALID;
+    return hip_status(moe::launch_quant_weight(w, batch, N, K, q, s, stream));
+}
+
+int moe_fp8_encode_e4m3(const float* in, int64_t n, uint8_t* out, hipStream_t stream) {
+    if (n < 0) return MOE_ERR_INVALID;
+    if (n == 0) return MOE_OK;
+    if (!in || !out) return MOE_ERR_INVALID;
+    return hip_status(moe::launch_encode_e4m3(in, n, out, stream));
+}
+
+}  // extern "C"

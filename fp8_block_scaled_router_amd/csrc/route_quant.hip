@@ -1,0 +1,196 @@
+// route_quant.hip -- router top-k and per-token 1x128 FP8 activation
+// quantisation (gfx950, wave64).
+//
+// Router (Netra Kernel README capability table, "BF16 routing" family;
+// kernel-laboratory README, decode and verification routing kernels): one
+// wave per token.  Each lane holds up to four logits (experts lane + 64j).
+// A pick is the wave-wide maximum of the 64-bit key (order-preserving bits of
+// the logit, 0xFFFF - expert), so equal logits go to the lower expert index
+// and -0 equals +0; the reduction runs DPP inside each 16-lane row and two
+// cross-row exchanges.  k rounds pick k experts in rank order; the weights
+// are exp(l - l_max) of the picks divided by their sum in rank order (the
+// full softmax denominator cancels in the renormalisation).
+//
+// Activation quantisation (Netra compiler architecture page: FP8 activation
+// with fp32 activation-scale tensors): one 16-lane DPP row per 128-column
+// group, eight bf16 per lane from one 16-byte load; amax by a DPP row
+// reduction, s = amax / 448, q = E4M3(x / s).
+#include "device.h"
+#include "launch.h"
+
+namespace moe {
+
+__device__ __forceinline__ void router_wave(const float* __restrict__ l, int E, int k,
+                                            int32_t* __restrict__ ids, float* __restrict__ w,
+                                            int lane) {
+    uint32_t key[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = lane + 64 * j;
+        key[j] = (e < E) ? float_order_key(l[e]) : 0u;
+    }
+    int picked[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        picked[r] = 0;
+        if (r < k) {
+            uint32_t hi = 0u, lo = 0u;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (key[j] > hi) {           // strict: lower j (lower expert) wins ties
+                    hi = key[j];
+                    lo = 0xFFFFu - (uint32_t)(lane + 64 * j);
+                }
+            }
+            wave_key_max(hi, lo);
+            int e = (int)(0xFFFFu - lo);
+            e = (hi == 0u || e >= E) ? E - 1 : e;   // only for NaN logits (outside the contract)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (lane + 64 * j == e) key[j] = 0u;
+            picked[r] = e;
+        }
+    }
+    // Renormalised softmax weights of the picks; every lane computes the same
+    // rank-order sum, lane r stores weight r.
+    const float lmax = l[picked[0]];
+    float ex[16];
+    float sum = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        ex[r] = 0.0f;
+        if (r < k) {
+            ex[r] = expf(l[picked[r]] - lmax);
+            sum += ex[r];
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        if (r < k && lane == r) {
+            ids[r] = picked[r];
+            w[r] = ex[r] / sum;
+        }
+    }
+}
+
+__device__ __forceinline__ void act_quant_row(const uint16_t* __restrict__ x, int K,
+                                              uint8_t* __restrict__ q, float* __restrict__ s,
+                                              int wave, int nwaves, int lane) {
+    const int G = K / 128;
+    const int sub = lane & 15;
+    for (int g0 = wave * 4; g0 < G; g0 += nwaves * 4) {
+        const int g = g0 + (lane >> 4);
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = 0.0f;
+        if (g < G) {
+            const uint4 u = *reinterpret_cast<const uint4*>(x + g * 128 + sub * 8);
+            v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x);
+            v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
+            v[4] = bf16_lo(u.z); v[5] = bf16_hi(u.z);
+            v[6] = bf16_lo(u.w); v[7] = bf16_hi(u.w);
+        }
+        float a = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(v[j]));
+        a = row16_max(a);
+        const float sc = a / kE4M3Max;
+        if (g < G) {
+            *reinterpret_cast<uint2*>(q + g * 128 + sub * 8) = quant8(v, sc);
+            if (sub == 0) s[g] = sc;
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void route_quant_kernel(
+    const float* __restrict__ logits, const uint16_t* __restrict__ x, int E, int k, int h,
+    int32_t* __restrict__ ids, float* __restrict__ tw, uint8_t* __restrict__ xq,
+    float* __restrict__ xs, int what) {
+    const int t = blockIdx.x;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if ((what & kRoute) && wave == 0)
+        router_wave(logits + (size_t)t * E, E, k, ids + (size_t)t * k, tw + (size_t)t * k, lane);
+    if (what & kQuant)
+        act_quant_row(x + (size_t)t * h, h, xq + (size_t)t * h, xs + (size_t)t * (h / 128), wave, 4,
+                      lane);
+}
+
+hipError_t launch_route_quant(const float* logits, const uint16_t* x, int M, int E, int k, int h,
+                              int32_t* ids, float* tw, uint8_t* xq, float* xs, int what,
+                              hipStream_t stream) {
+    if (M <= 0) return hipSuccess;
+    hipLaunchKernelGGL(route_quant_kernel, dim3(M), dim3(256), 0, stream, logits, x, E, k, h, ids,
+                       tw, xq, xs, what);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------ utilities
+
+__global__ __launch_bounds__(256) void encode_e4m3_kernel(const float* __restrict__ in, int64_t n,
+                                                          uint8_t* __restrict__ out) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x * 4;
+    for (int64_t j = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; j < n; j += stride) {
+        float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        const int m = (n - j) < 4 ? (int)(n - j) : 4;
+        for (int u = 0; u < m; ++u) v[u] = in[j + u];
+        const uint32_t c = e4m3x4(v[0], v[1], v[2], v[3]);
+        for (int u = 0; u < m; ++u) out[j + u] = (uint8_t)(c >> (8 * u));
+    }
+}
+
+hipError_t launch_encode_e4m3(const float* in, int64_t n, uint8_t* out, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    int64_t blocks = (n + 1023) / 1024;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(encode_e4m3_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, in, n, out);
+    return hipGetLastError();
+}
+
+// One workgroup per 128x128 block: amax, s = amax / 448, codes E4M3(w / s).
+__global__ __launch_bounds__(256) void quant_weight_kernel(const float* __restrict__ w, int N, int K,
+                                                           uint8_t* __restrict__ q,
+                                                           float* __restrict__ s) {
+    const int NB = N / 128, KB = K / 128;
+    const int64_t blk = blockIdx.x;
+    const int64_t b = blk / ((int64_t)NB * KB);
+    const int nb = (int)((blk / KB) % NB), kb = (int)(blk % KB);
+    const int tid = threadIdx.x;
+    const int row = tid >> 1, col0 = (tid & 1) * 64;
+    const float* src = w + ((b * N + (int64_t)nb * 128 + row) * K) + (int64_t)kb * 128 + col0;
+    uint8_t* dst = q + ((b * N + (int64_t)nb * 128 + row) * K) + (int64_t)kb * 128 + col0;
+    float v[64];
+    float a = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+        const float4 f = reinterpret_cast<const float4*>(src)[u];
+        v[4 * u] = f.x; v[4 * u + 1] = f.y; v[4 * u + 2] = f.z; v[4 * u + 3] = f.w;
+        a = fmaxf(a, fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w))));
+    }
+    a = row16_max(a);
+    a = fmaxf(a, __shfl_xor(a, 16, kWave));
+    a = fmaxf(a, __shfl_xor(a, 32, kWave));
+    __shared__ float part[4];
+    if ((tid & 63) == 0) part[tid >> 6] = a;
+    __syncthreads();
+    a = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+    const float sc = a / kE4M3Max;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        uint2 c0 = quant8(&v[16 * u], sc);
+        uint2 c1 = quant8(&v[16 * u + 8], sc);
+        reinterpret_cast<uint4*>(dst)[u] = make_uint4(c0.x, c0.y, c1.x, c1.y);
+    }
+    if (tid == 0) s[blk] = sc;
+}
+
+hipError_t launch_quant_weight(const float* w, int64_t batch, int N, int K, uint8_t* q, float* s,
+                               hipStream_t stream) {
+    const int64_t blocks = batch * (N / 128) * (K / 128);
+    if (blocks <= 0) return hipSuccess;
+    if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(quant_weight_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, w, N, K, q,
+                       s);
+    return hipGetLastError();
+}
+
+}  // namespace moe

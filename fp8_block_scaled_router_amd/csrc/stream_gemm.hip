@@ -1,0 +1,215 @@
+// stream_gemm.hip -- weight-streaming grouped FP8 GEMMs for batches with few
+// tokens per expert (decode and verify).
+//
+// Each wave owns 16 weight rows of one expert and streams them once from HBM
+// (K contiguous, 128 bytes per row per K block: four lanes of a row read one
+// full 128-byte line), feeding v_mfma_f32_16x16x128 with the weights as the A
+// operand and up to 16 of the expert's routes as the B operand (unused
+// columns are zero).  One MFMA covers one 128-wide K block, so the block
+// scales are applied per block: acc += blk * (s_act[token, kb] * s_w[e, n/128, kb])
+// (Netra Kernel README capability table: explicit block-scale semantics).
+//
+// Gate/up writes FP32 results per route (Netra compiler architecture page:
+// gate/up FP32).  Down starts by recomputing SiLU(gate) * up and its 1x128
+// FP8 requantisation for its routes into LDS, then streams w2 the same way
+// and writes one fp32 partial row per route (Netra Kernel README, MoE
+// prefill pair: SiLU and quantisation, then down-partial).
+#include "device.h"
+#include "launch.h"
+
+namespace moe {
+
+constexpr int kRowsPerWave = 16;
+constexpr int kWavesPerGroup = 4;
+constexpr int kRowsPerGroup = kRowsPerWave * kWavesPerGroup;  // 64
+constexpr int kUnroll = 8;                                   // K blocks in flight per wave
+
+__global__ __launch_bounds__(256) void stream_gate_up_kernel(
+    const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ w13,
+    const float* __restrict__ s13, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ sorted, const int32_t* __restrict__ active,
+    const int32_t* __restrict__ num_active, float* __restrict__ g, int h, int i, int k) {
+    const int slot = blockIdx.y;
+    if (slot >= *num_active) return;
+    const int e = active[slot];
+    const int beg = offsets[e], cnt = offsets[e + 1] - beg;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int N = 2 * i, KB = h / 128;
+    const int n0 = blockIdx.x * kRowsPerGroup + wave * kRowsPerWave;
+    const int col = lane & 15, kg = lane >> 4;
+    const uint8_t* wrow = w13 + ((size_t)e * N + n0 + col) * h + kg * 32;
+    const float* ws = s13 + ((size_t)e * (N / 128) + n0 / 128) * KB;
+
+    for (int j0 = 0; j0 < cnt; j0 += 16) {
+        const bool valid = j0 + col < cnt;
+        const int p = valid ? sorted[beg + j0 + col] : 0;
+        const int t = p / k;
+        const uint8_t* xrow = xq + (size_t)t * h + kg * 32;
+        const float* xsr = xs + (size_t)t * KB;
+        v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int kb0 = 0; kb0 < KB; kb0 += kUnroll) {
+            v8i A[kUnroll], B[kUnroll];
+            float sc[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int kb = kb0 + u;
+                if (kb < KB) {
+                    A[u] = load32(wrow + kb * 128);
+                    B[u] = valid ? load32(xrow + kb * 128) : zero8();
+                    sc[u] = (valid ? xsr[kb] : 0.0f) * ws[kb];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int kb = kb0 + u;
+                if (kb < KB) {
+                    const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+                    const v4f blk = mfma_16x16x128_e4m3(A[u], B[u], z);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) acc[v] = fmaf(blk[v], sc[u], acc[v]);
+                }
+            }
+        }
+        if (valid)
+            *reinterpret_cast<float4*>(g + (size_t)p * N + n0 + kg * 4) =
+                make_float4(acc[0], acc[1], acc[2], acc[3]);
+    }
+}
+
+// SiLU(gate) * up of one 128-column group for one route on one 16-lane row,
+// requantised to E4M3 (amax over the row by DPP).
+__device__ __forceinline__ void silu_quant_row(const float* __restrict__ gate,
+                                               const float* __restrict__ up, int sub,
+                                               uint8_t* __restrict__ q, float* __restrict__ s,
+                                               bool write_scale) {
+    const float4 g0 = reinterpret_cast<const float4*>(gate + sub * 8)[0];
+    const float4 g1 = reinterpret_cast<const float4*>(gate + sub * 8)[1];
+    const float4 u0 = reinterpret_cast<const float4*>(up + sub * 8)[0];
+    const float4 u1 = reinterpret_cast<const float4*>(up + sub * 8)[1];
+    const float a[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    const float b[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+    float v[8];
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        v[j] = (a[j] / (1.0f + expf(-a[j]))) * b[j];
+        m = fmaxf(m, fabsf(v[j]));
+    }
+    m = row16_max(m);
+    const float sc = m / kE4M3Max;
+    *reinterpret_cast<uint2*>(q + sub * 8) = quant8(v, sc);
+    if (write_scale) *s = sc;
+}
+
+__global__ __launch_bounds__(256) void stream_down_kernel(
+    const float* __restrict__ g, const uint8_t* __restrict__ w2, const float* __restrict__ s2,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted,
+    const int32_t* __restrict__ active, const int32_t* __restrict__ num_active,
+    float* __restrict__ y, int h, int i, int k) {
+    extern __shared__ uint8_t lds[];
+    const int slot = blockIdx.y;
+    if (slot >= *num_active) return;
+    const int e = active[slot];
+    const int beg = offsets[e], cnt = offsets[e + 1] - beg;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int IB = i / 128;
+    const int astride = i + 16;                         // padded LDS row of one route's codes
+    uint8_t* a2l = lds;                                 // [16][astride]
+    float* a2sl = reinterpret_cast<float*>(lds + 16 * astride);   // [16][IB]
+    const int n0 = blockIdx.x * kRowsPerGroup + wave * kRowsPerWave;
+    const int col = lane & 15, kg = lane >> 4;
+    const uint8_t* wrow = w2 + ((size_t)e * h + n0 + col) * i + kg * 32;
+    const float* ws = s2 + ((size_t)e * (h / 128) + n0 / 128) * IB;
+
+    for (int j0 = 0; j0 < cnt; j0 += 16) {
+        const int nr = min(16, cnt - j0);
+        __syncthreads();
+        for (int task = wave * 4 + (lane >> 4); task < nr * IB; task += 16) {
+            const int jr = task / IB, b = task - jr * IB;
+            const int p = sorted[beg + j0 + jr];
+            const float* gate = g + (size_t)p * 2 * i + b * 128;
+            silu_quant_row(gate, gate + i, lane & 15, a2l + jr * astride + b * 128, a2sl + jr * IB + b,
+                           (lane & 15) == 0);
+        }
+        __syncthreads();
+        const bool valid = col < nr;
+        const int p = valid ? sorted[beg + j0 + col] : 0;
+        v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int kb0 = 0; kb0 < IB; kb0 += kUnroll) {
+            v8i A[kUnroll], B[kUnroll];
+            float sc[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int kb = kb0 + u;
+                if (kb < IB) {
+                    A[u] = load32(wrow + kb * 128);
+                    B[u] = valid ? load32(a2l + col * astride + kb * 128 + kg * 32) : zero8();
+                    sc[u] = (valid ? a2sl[col * IB + kb] : 0.0f) * ws[kb];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int kb = kb0 + u;
+                if (kb < IB) {
+                    const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+                    const v4f blk = mfma_16x16x128_e4m3(A[u], B[u], z);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) acc[v] = fmaf(blk[v], sc[u], acc[v]);
+                }
+            }
+        }
+        if (valid)
+            *reinterpret_cast<float4*>(y + (size_t)p * h + n0 + kg * 4) =
+                make_float4(acc[0], acc[1], acc[2], acc[3]);
+    }
+}
+
+hipError_t launch_stream_gate_up(const StreamArgs& a, const uint8_t* xq, const float* xs,
+                                 const uint8_t* w13, const float* s13, float* g, hipStream_t stream) {
+    const dim3 grid((2 * a.i) / kRowsPerGroup, a.max_slots);
+    hipLaunchKernelGGL(stream_gate_up_kernel, grid, dim3(256), 0, stream, xq, xs, w13, s13, a.offsets,
+                       a.sorted, a.active, a.num_active, g, a.h, a.i, a.k);
+    return hipGetLastError();
+}
+
+static size_t stream_down_lds_bytes(int i) { return (size_t)16 * (i + 16) + (size_t)16 * (i / 128) * 4; }
+
+hipError_t launch_stream_down(const StreamArgs& a, const float* g, const uint8_t* w2, const float* s2,
+                              float* y, hipStream_t stream) {
+    const dim3 grid(a.h / kRowsPerGroup, a.max_slots);
+    hipLaunchKernelGGL(stream_down_kernel, grid, dim3(256), stream_down_lds_bytes(a.i), stream, g, w2,
+                       s2, a.offsets, a.sorted, a.active, a.num_active, y, a.h, a.i, a.k);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------- combine
+
+// out[t, n] = bf16( sum_{r < k} w[t, r] * y[t*k + r, n] ), r ascending,
+// multiply then add, from 0 (Inferact amd-kernels README, atomics rule).
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
+                                                      const float* __restrict__ tw, int k, int h,
+                                                      uint16_t* __restrict__ out) {
+#pragma clang fp contract(off)
+    const int t = blockIdx.y;
+    const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
+    if (n >= h) return;
+    float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+    for (int r = 0; r < k; ++r) {
+        const float w = tw[(size_t)t * k + r];
+        const float4 v = *reinterpret_cast<const float4*>(y + ((size_t)t * k + r) * h + n);
+        a0 = a0 + w * v.x;
+        a1 = a1 + w * v.y;
+        a2 = a2 + w * v.z;
+        a3 = a3 + w * v.w;
+    }
+    *reinterpret_cast<uint2*>(out + (size_t)t * h + n) = make_uint2(bf16x2(a0, a1), bf16x2(a2, a3));
+}
+
+hipError_t launch_combine(const float* y, const float* tw, int M, int k, int h, uint16_t* out,
+                          hipStream_t stream) {
+    const dim3 grid((h / 4 + 255) / 256, M);
+    hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, stream, y, tw, k, h, out);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,187 @@
+/*
+ * moe_fp8.h -- C ABI of the routed FP8 (E4M3, 128x128 block-scaled)
+ * mixture-of-experts expert FFN for AMD Instinct MI355X (gfx950, wave64).
+ *
+ * The layer (stage order of the Netra Kernel README, MoE prefill pair:
+ * routing, gate/up, SiLU and quantisation, down-partial, route reducer):
+ *   1. router: softmax over E fp32 logits, top-k by logit (ties go to the
+ *      lower expert index), weights renormalised over the k picks;
+ *   2. per-token 1x128 FP8 activation quantisation (fp32 scale per 128
+ *      columns, Netra compiler architecture page: FP8 activation plus
+ *      fp32 activation-scale tensors);
+ *   3. grouping of the M*k routes by expert (counts, offsets, routes sorted
+ *      by expert then route id);
+ *   4. block-scaled FP8 gate/up GEMM with FP32 results;
+ *   5. SiLU(gate) * up, requantised to FP8 per 128 columns;
+ *   6. block-scaled FP8 down GEMM, one fp32 partial row per route;
+ *   7. combine: out[t] = bf16( sum over r = 0..k-1 of w[t,r] * partial[t*k+r] ),
+ *      summed in rank order with no atomic adds (Inferact amd-kernels README,
+ *      atomics rule).
+ * Formats (Netra Kernel README capability table; kernel-laboratory README
+ * supported-targets table): E4M3 is the OCP "FN" variant (max 448, NaN at
+ * 0x7F/0xFF); a block scale is amax/448 in fp32 and dequantisation is
+ * code * scale; conversion to E4M3 rounds to nearest even and saturates.
+ *
+ * General conventions (Netra Kernel README, runtime C ABI; Netra compiler
+ * architecture page, compile/init/launch flow):
+ *  - Every tensor pointer is caller-owned DEVICE memory on the current HIP
+ *    device, row-major and contiguous, 16-byte aligned.  Inputs are never
+ *    written.  Outputs are fully overwritten.
+ *  - Work is enqueued on `stream`; calls return after the enqueue.  The
+ *    launch path allocates nothing and never synchronises, so a forward can
+ *    be captured into a HIP graph.
+ *  - Arguments are checked on the host before any HIP call; a rejected call
+ *    enqueues nothing.  No C++ exception crosses the ABI.
+ *  - Results are bitwise deterministic: identical inputs give identical
+ *    outputs on every run.
+ *  - Two forwards that share a workspace must not run concurrently (use one
+ *    workspace per stream).
+ */
+#ifndef MOE_FP8_H
+#define MOE_FP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID = -1,      /* null pointer, negative size, misaligned pointer */
+    MOE_ERR_UNSUPPORTED = -2,  /* shape outside what the kernels are built for: the caller falls back */
+    MOE_ERR_WORKSPACE = -3,    /* no workspace bound / workspace too small */
+    MOE_ERR_HIP = -4           /* a HIP call or kernel launch failed */
+};
+
+/* Shape limits of this build. */
+#define MOE_FP8_MAX_EXPERTS 256
+#define MOE_FP8_MAX_TOPK 16
+#define MOE_FP8_MAX_HIDDEN 16384        /* h */
+#define MOE_FP8_MAX_INTERMEDIATE 2048   /* i */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* moe_fp8_status_string(int status);
+
+/* Bytes of device workspace a forward with these sizes needs (0 for M == 0
+ * or an unsupported shape). */
+size_t moe_fp8_workspace_bytes(int M, int h, int i, int E, int k);
+
+/* Bind `bytes` of device memory at `dev_ptr` (256-byte aligned) as the
+ * workspace moe_fp8_forward uses on the CURRENT device.  The library keeps
+ * the pointer, not the memory: the caller owns it and must keep it alive
+ * while bound.  Passing NULL unbinds.  Not on the launch path; call it once
+ * before capturing graphs.  Returns MOE_ERR_INVALID on misalignment. */
+int moe_fp8_bind_workspace(void* dev_ptr, size_t bytes);
+
+/* The whole layer with the workspace bound to the current device.
+ *   x              bf16 [M, h]
+ *   router_logits  fp32 [M, E]
+ *   w13            e4m3 [E, 2i, h]; rows [0, i) are the gate projection,
+ *                  rows [i, 2i) the up projection
+ *   s13            fp32 [E, 2i/128, h/128]  (one scale per 128x128 block)
+ *   w2             e4m3 [E, h, i]
+ *   s2             fp32 [E, h/128, i/128]
+ *   out            bf16 [M, h]
+ * Requires h % 128 == 0, i % 128 == 0, 1 <= k <= min(E, 16), E <= 256.
+ * M == 0 is a no-op that returns MOE_OK. */
+int moe_fp8_forward(const void* x, const float* router_logits,
+                    const void* w13, const float* s13,
+                    const void* w2, const float* s2,
+                    void* out, int M, int h, int i, int E, int k,
+                    hipStream_t stream);
+
+/* Same, with an explicit workspace of `workspace_bytes` bytes (256-byte
+ * aligned device memory, at least moe_fp8_workspace_bytes(M, h, i, E, k)).
+ * After the call the workspace holds the forward's intermediates at the
+ * offsets moe_fp8_workspace_layout reports. */
+int moe_fp8_forward_ws(const void* x, const float* router_logits,
+                       const void* w13, const float* s13,
+                       const void* w2, const float* s2,
+                       void* out, int M, int h, int i, int E, int k,
+                       void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/* Measurement variant of moe_fp8_forward_ws: additionally records
+ * events[j] on `stream` just before the j-th stage of the forward and
+ * events[n] after the last, where n = moe_fp8_forward_kernel_count(...);
+ * n_events must be at least n + 1.  Event j..j+1 then brackets stage j, whose
+ * kernel names moe_fp8_forward_kernel_name reports.  The events are
+ * caller-created (hipEventCreate); results are those of moe_fp8_forward_ws. */
+int moe_fp8_forward_ws_timed(const void* x, const float* router_logits,
+                             const void* w13, const float* s13,
+                             const void* w2, const float* s2,
+                             void* out, int M, int h, int i, int E, int k,
+                             void* workspace, size_t workspace_bytes,
+                             hipEvent_t* events, int n_events, hipStream_t stream);
+
+/* Number of stages a forward with these sizes runs (0 for M == 0, a negative
+ * status for a rejected shape) and the kernel name(s) of stage j (static
+ * string, NULL when j is out of range). */
+int moe_fp8_forward_kernel_count(int M, int h, int i, int E, int k);
+const char* moe_fp8_forward_kernel_name(int M, int h, int i, int E, int k, int j);
+
+/* Byte offsets of the intermediates inside a forward's workspace; a field is
+ * (size_t)-1 when the path chosen for these sizes does not materialise it. */
+typedef struct {
+    size_t topk_ids;    /* int32 [M, k]          rank order            */
+    size_t topk_w;      /* fp32  [M, k]                                 */
+    size_t xq;          /* e4m3  [M, h]                                 */
+    size_t xs;          /* fp32  [M, h/128]                             */
+    size_t counts;      /* int32 [E]                                    */
+    size_t offsets;     /* int32 [E + 1]                                */
+    size_t sorted;      /* int32 [M*k]  route ids p = t*k + r           */
+    size_t active;      /* int32 [E]    experts with a route, ascending */
+    size_t num_active;  /* int32 [1]                                    */
+    size_t gate_up;     /* fp32  [M*k, 2i]  by route id                 */
+    size_t act2;        /* e4m3  [M*k, i]   by route id                 */
+    size_t act2_scale;  /* fp32  [M*k, i/128]                           */
+    size_t partial;     /* fp32  [M*k, h]   by route id                 */
+    size_t total;       /* bytes                                        */
+    int    path;        /* 0 = weight-streaming path, 1 = tiled MFMA path */
+} moe_fp8_ws_layout;
+
+/* Fills *layout for these sizes.  Returns MOE_ERR_UNSUPPORTED / INVALID as
+ * moe_fp8_forward would. */
+int moe_fp8_workspace_layout(int M, int h, int i, int E, int k, moe_fp8_ws_layout* layout);
+
+/* Step 1 alone (the same kernel the forward runs).
+ *   logits fp32 [M, E] -> topk_ids int32 [M, k] (rank order: descending
+ *   logit, ties to the lower expert index), topk_w fp32 [M, k] (softmax
+ *   probabilities of the picks renormalised to sum to 1). */
+int router_topk(const float* logits, int M, int E, int k,
+                int32_t* topk_ids, float* topk_w, hipStream_t stream);
+
+/* Step 2 alone: rows of bf16 [M, K] -> q e4m3 [M, K], s fp32 [M, K/128];
+ * s = amax/448 of each 1x128 group, q = E4M3(x / s), all-zero groups give
+ * s = 0 and zero codes.  K % 128 == 0. */
+int moe_fp8_act_quant(const void* x, int M, int K, uint8_t* q, float* s,
+                      hipStream_t stream);
+
+/* Step 3 alone: topk_ids int32 [M*k] with values in [0, E) ->
+ *   counts int32 [E], offsets int32 [E + 1] (exclusive scan of counts),
+ *   sorted_route_ids int32 [M*k] (route ids grouped by expert ascending and
+ *   ascending inside each expert).
+ * Uses `workspace` (device, >= moe_fp8_group_workspace_bytes(M, E, k)). */
+size_t moe_fp8_group_workspace_bytes(int M, int E, int k);
+int moe_fp8_group(const int32_t* topk_ids, int M, int E, int k,
+                  int32_t* counts, int32_t* offsets, int32_t* sorted_route_ids,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Weight preparation (not on the forward path): fp32 [batch, N, K] ->
+ * codes e4m3 [batch, N, K] and scales fp32 [batch, N/128, K/128], one scale
+ * amax/448 per 128x128 block.  N % 128 == 0, K % 128 == 0. */
+int moe_fp8_quantize_weight_block128(const float* w, int64_t batch, int N, int K,
+                                     uint8_t* q, float* s, hipStream_t stream);
+
+/* The device E4M3 encoder every kernel uses, applied elementwise:
+ * out[j] = E4M3(in[j]) (nearest, ties to even, saturating to +-448). */
+int moe_fp8_encode_e4m3(const float* in, int64_t n, uint8_t* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_FP8_H */

@@ -1,0 +1,124 @@
+"""C-ABI checks that need no GPU: every function include/*.h declares is
+exported by libmoe_fp8.so, and argument checks return the documented status
+before any HIP call."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for hdr in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(hdr).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        for m in re.finditer(r"^[A-Za-z_][\w \*]*?\b([A-Za-z_]\w*)\s*\(", text, flags=re.M):
+            name = m.group(1)
+            if name not in ("if", "while", "for", "sizeof", "defined"):
+                names.add(name)
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import fp8_block_scaled_router_amd as moe
+    if not os.path.exists(moe.LIB_PATH):
+        from fp8_block_scaled_router_amd import build
+        build.build()
+    return moe.lib()
+
+
+def test_header_declares_the_expected_entry_points():
+    names = _declared_functions()
+    for required in ("moe_fp8_forward", "router_topk", "moe_fp8_forward_ws", "moe_fp8_group",
+                     "moe_fp8_act_quant", "moe_fp8_workspace_bytes", "moe_fp8_bind_workspace"):
+        assert required in names
+    assert len(names) >= 12
+
+
+def test_every_declared_symbol_is_exported(lib):
+    missing = [n for n in _declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_status_strings(lib):
+    import fp8_block_scaled_router_amd as moe
+    assert moe.status_string(0) == "ok"
+    for s in (-1, -2, -3, -4):
+        assert moe.status_string(s) not in ("ok", "unknown status")
+    assert moe.status_string(12345) == "unknown status"
+
+
+FAKE = ctypes.c_void_p(0x100000)   # aligned, never dereferenced: checks fail first
+
+
+def _fwd_ws(lib, M, h, i, E, k, ptr=FAKE, ws=FAKE, nws=0):
+    return lib.moe_fp8_forward_ws(ptr, ptr, ptr, ptr, ptr, ptr, ptr, M, h, i, E, k, ws, nws, None)
+
+
+def test_forward_argument_checks(lib):
+    import fp8_block_scaled_router_amd as moe
+    assert _fwd_ws(lib, -1, 256, 128, 8, 2) == moe.MOE_ERR_INVALID
+    assert _fwd_ws(lib, 4, 0, 128, 8, 2) == moe.MOE_ERR_INVALID
+    assert _fwd_ws(lib, 4, 200, 128, 8, 2) == moe.MOE_ERR_UNSUPPORTED      # h % 128
+    assert _fwd_ws(lib, 4, 256, 100, 8, 2) == moe.MOE_ERR_UNSUPPORTED      # i % 128
+    assert _fwd_ws(lib, 4, 256, 128, 300, 2) == moe.MOE_ERR_UNSUPPORTED    # E > 256
+    assert _fwd_ws(lib, 4, 256, 128, 8, 9) == moe.MOE_ERR_UNSUPPORTED      # k > E
+    assert _fwd_ws(lib, 4, 256, 128, 64, 17) == moe.MOE_ERR_UNSUPPORTED    # k > 16
+    assert _fwd_ws(lib, 0, 256, 128, 8, 2) == moe.MOE_OK                   # M == 0: no-op
+    assert _fwd_ws(lib, 4, 256, 128, 8, 2, ptr=ctypes.c_void_p(0)) == moe.MOE_ERR_INVALID
+    assert _fwd_ws(lib, 4, 256, 128, 8, 2, ptr=ctypes.c_void_p(0x100004)) == moe.MOE_ERR_INVALID
+    need = moe.workspace_bytes(4, 256, 128, 8, 2)
+    assert _fwd_ws(lib, 4, 256, 128, 8, 2, ws=ctypes.c_void_p(0), nws=need) == moe.MOE_ERR_WORKSPACE
+    assert _fwd_ws(lib, 4, 256, 128, 8, 2, nws=need - 1) == moe.MOE_ERR_WORKSPACE
+    assert _fwd_ws(lib, 4, 256, 128, 8, 2, ws=ctypes.c_void_p(0x100010), nws=need) == moe.MOE_ERR_WORKSPACE
+
+
+def test_other_entry_argument_checks(lib):
+    import fp8_block_scaled_router_amd as moe
+    assert lib.router_topk(FAKE, -1, 8, 2, FAKE, FAKE, None) == moe.MOE_ERR_INVALID
+    assert lib.router_topk(FAKE, 4, 8, 9, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.router_topk(FAKE, 4, 257, 2, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.router_topk(FAKE, 0, 8, 2, FAKE, FAKE, None) == moe.MOE_OK
+    assert lib.router_topk(None, 4, 8, 2, FAKE, FAKE, None) == moe.MOE_ERR_INVALID
+    assert lib.moe_fp8_act_quant(FAKE, 4, 100, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_fp8_act_quant(None, 4, 128, FAKE, FAKE, None) == moe.MOE_ERR_INVALID
+    assert lib.moe_fp8_group(FAKE, 4, 8, 2, FAKE, FAKE, FAKE, FAKE, 0, None) == moe.MOE_ERR_WORKSPACE
+    assert lib.moe_fp8_group(FAKE, 4, 8, 9, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_fp8_quantize_weight_block128(FAKE, 1, 100, 128, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_fp8_quantize_weight_block128(FAKE, -1, 128, 128, FAKE, FAKE, None) == moe.MOE_ERR_INVALID
+    assert lib.moe_fp8_encode_e4m3(FAKE, -5, FAKE, None) == moe.MOE_ERR_INVALID
+    assert lib.moe_fp8_encode_e4m3(FAKE, 0, FAKE, None) == moe.MOE_OK
+    assert lib.moe_fp8_bind_workspace(ctypes.c_void_p(0x100010), 1024) == moe.MOE_ERR_INVALID
+    assert lib.moe_fp8_workspace_bytes(0, 256, 128, 8, 2) == 0
+    assert lib.moe_fp8_workspace_bytes(4, 200, 128, 8, 2) == 0
+
+
+@pytest.mark.parametrize("M,h,i,E,k", [(4, 256, 128, 8, 2), (1, 2048, 768, 128, 8),
+                                       (12, 2048, 768, 128, 8), (64, 6144, 768, 128, 4),
+                                       (8192, 2048, 768, 128, 8)])
+def test_workspace_layout_regions(lib, M, h, i, E, k):
+    import fp8_block_scaled_router_amd as moe
+    L = moe.workspace_layout(M, h, i, E, k)
+    R = M * k
+    sizes = {"topk_ids": 4 * R, "topk_w": 4 * R, "xq": M * h, "xs": 4 * M * h // 128,
+             "counts": 4 * E, "offsets": 4 * (E + 1), "sorted": 4 * R, "active": 4 * E,
+             "num_active": 4, "gate_up": 4 * R * 2 * i, "act2": R * i, "act2_scale": 4 * R * i // 128,
+             "partial": 4 * R * h}
+    spans = []
+    for name, n in sizes.items():
+        off = getattr(L, name)
+        if off == 2 ** 64 - 1:
+            continue
+        assert off % 256 == 0
+        assert off + n <= L.total
+        spans.append((off, off + n, name))
+    spans.sort()
+    for a, b in zip(spans, spans[1:]):
+        assert a[1] <= b[0], (a, b)
+    assert L.total == moe.workspace_bytes(M, h, i, E, k)

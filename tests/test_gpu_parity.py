@@ -1,0 +1,317 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bit-exact: router ids, activation codes and scales, grouping (counts,
+offsets, sorted route ids), weight block quantisation, the E4M3 encoder.
+Within the output bar of gpu_util.check_output: the layer output.  Plus
+run-to-run and graph-replay determinism and the edge cases of the method.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import Layer, check_output, log, read_ws, to_dev_bf16, to_host_bits
+
+pytestmark = pytest.mark.gpu
+
+CONFIG_IDS = [0, 1, 2, 3, 4]
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import fp8_block_scaled_router_amd as moe
+    moe.lib()
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def moe_mod(dev):
+    import fp8_block_scaled_router_amd as moe
+    return moe
+
+
+# ------------------------------------------------------------------ formats
+
+def test_encode_e4m3_all_fp32_in_range(dev, moe_mod):
+    """Every fp32 bit pattern with |v| <= 448 (both signs), plus saturation."""
+    hi = np.float32(448.0).view(np.uint32).item()
+    chunk = 1 << 26
+    for sign in (0, 0x80000000):
+        for start in range(0, hi + 1, chunk):
+            bits = np.arange(start, min(hi + 1, start + chunk), dtype=np.uint32) | np.uint32(sign)
+            v = bits.view(np.float32)
+            log(f"encode sweep sign={sign >> 31} start={start:#x} n={v.size}")
+            got = moe_mod.encode_e4m3(torch.from_numpy(v).to(dev)).cpu().numpy()
+            ref = oracle.e4m3_encode_array(v)
+            bad = np.nonzero(got != ref)[0]
+            assert bad.size == 0, [(float(v[j]), int(got[j]), int(ref[j])) for j in bad[:8]]
+    big = np.float32([448.5, 463.9, 464.0, 465.0, 1e4, 3e38, np.inf, -448.5, -1e30, -np.inf])
+    got = moe_mod.encode_e4m3(torch.from_numpy(big).to(dev)).cpu().numpy()
+    assert np.array_equal(got, oracle.e4m3_encode_array(big))
+
+
+def test_weight_quant_matches_oracle(dev, moe_mod):
+    rng = np.random.default_rng(12)
+    w = (rng.standard_normal((3, 256, 384)) * rng.uniform(0.01, 10, (3, 1, 1))).astype(np.float32)
+    w[1, 0:128, 0:128] = 0.0
+    w[2, 128:256, 256:384] *= 1e-30
+    log("weight quant [3,256,384]")
+    q, s = moe_mod.quantize_weight_block128(torch.from_numpy(w).to(dev))
+    qr, sr = oracle.quant_weight_block128(w)
+    assert np.array_equal(s.cpu().numpy(), sr)
+    assert np.array_equal(q.view(torch.uint8).cpu().numpy(), qr)
+
+
+# ------------------------------------------------------------------- router
+
+@pytest.mark.parametrize("ci", CONFIG_IDS)
+def test_router_matches_oracle(dev, moe_mod, ci):
+    cfg = synth.CONFIGS[ci]
+    logits = synth.make_logits(cfg, synth.default_seed(ci))
+    log(f"router {cfg.name}")
+    ids, w = moe_mod.router_topk(torch.from_numpy(logits).to(dev), cfg.k)
+    ids_r, w_r = oracle.router(logits, cfg.k)
+    assert np.array_equal(ids.cpu().numpy(), ids_r)
+    np.testing.assert_allclose(w.cpu().numpy(), w_r, rtol=0, atol=1e-6)
+
+
+def test_router_edge_cases(dev, moe_mod):
+    cases = []
+    z = np.zeros((4, 16), np.float32)
+    z[1, [3, 9, 12]] = 1.0
+    z[2, :] = -0.0
+    z[2, 5] = 0.0
+    z[3, :] = np.float32(-3.5)
+    cases.append((z, 4))
+    rng = np.random.default_rng(3)
+    cases.append((rng.standard_normal((5, 256)).astype(np.float32), 16))      # E=256, k=16
+    cases.append((rng.standard_normal((3, 12)).astype(np.float32), 12))       # k = E
+    cases.append((rng.standard_normal((7, 1)).astype(np.float32), 1))         # E = 1
+    q = (rng.integers(-3, 3, (64, 128)) * 0.5).astype(np.float32)             # many ties
+    cases.append((q, 8))
+    cases.append((rng.standard_normal((3, 130)).astype(np.float32) * 1e4, 7))  # ragged E, huge spread
+    for logits, k in cases:
+        log(f"router edge E={logits.shape[1]} k={k}")
+        ids, w = moe_mod.router_topk(torch.from_numpy(logits).to(dev), k)
+        ids_r, w_r = oracle.router(logits, k)
+        assert np.array_equal(ids.cpu().numpy(), ids_r)
+        np.testing.assert_allclose(w.cpu().numpy(), w_r, rtol=0, atol=1e-6)
+
+
+# ------------------------------------------------------------ act quant
+
+@pytest.mark.parametrize("ci", CONFIG_IDS)
+def test_act_quant_matches_oracle(dev, moe_mod, ci):
+    cfg = synth.CONFIGS[ci]
+    x = synth.make_x(cfg, synth.default_seed(ci))
+    log(f"act quant {cfg.name}")
+    q, s = moe_mod.act_quant(to_dev_bf16(x, dev))
+    qr, sr = oracle.act_quant(x)
+    assert np.array_equal(s.cpu().numpy(), sr)
+    assert np.array_equal(q.cpu().numpy(), qr)
+
+
+def test_act_quant_edge_cases(dev, moe_mod):
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((6, 384)).astype(np.float32)
+    x[0] = 0.0                         # all-zero token
+    x[1, :128] = -0.0                  # negative zeros, zero group
+    x[2, 5] = -0.0                     # a negative zero in a live group
+    x[3] *= 1e-6                       # subnormal E4M3 codes
+    x[4, 7] = 3e38                     # huge amax: everything else rounds to zero
+    x[5, 128:256] = 1.0                # constant group
+    xb = synth.to_bf16_bits(x)
+    q, s = moe_mod.act_quant(to_dev_bf16(xb, dev))
+    qr, sr = oracle.act_quant(xb)
+    assert np.array_equal(s.cpu().numpy(), sr)
+    assert np.array_equal(q.cpu().numpy(), qr)
+
+
+# ------------------------------------------------------------- grouping
+
+@pytest.mark.parametrize("ci", CONFIG_IDS)
+def test_group_matches_oracle(dev, moe_mod, ci):
+    cfg = synth.CONFIGS[ci]
+    ids, _ = oracle.router(synth.make_logits(cfg, synth.default_seed(ci)), cfg.k)
+    log(f"group {cfg.name}")
+    c, o, s = moe_mod.group(torch.from_numpy(ids).to(dev), cfg.E)
+    cr, orr, sr = oracle.group(ids.ravel(), cfg.E)
+    assert np.array_equal(c.cpu().numpy(), cr)
+    assert np.array_equal(o.cpu().numpy(), orr)
+    assert np.array_equal(s.cpu().numpy(), sr)
+
+
+@pytest.mark.parametrize("M,E,k,skew", [(1, 128, 8, False), (25000, 256, 4, True),
+                                        (4097, 8, 1, False), (3, 256, 16, False), (10000, 1, 1, False)])
+def test_group_random(dev, moe_mod, M, E, k, skew):
+    rng = np.random.default_rng(M + E + k)
+    if skew:
+        p = (np.arange(1, E + 1) ** -1.5)
+        ids = rng.choice(E, (M, k), p=p / p.sum()).astype(np.int32)
+    else:
+        ids = rng.integers(0, E, (M, k)).astype(np.int32)
+    log(f"group random M={M} E={E} k={k}")
+    c, o, s = moe_mod.group(torch.from_numpy(ids).to(dev), E)
+    cr, orr, sr = oracle.group(ids.ravel(), E)
+    assert np.array_equal(c.cpu().numpy(), cr)
+    assert np.array_equal(o.cpu().numpy(), orr)
+    assert np.array_equal(s.cpu().numpy(), sr)
+
+
+# ----------------------------------------------------------- whole layer
+
+def _run(moe_mod, L: Layer):
+    M, h, i, E, k = L.dims
+    ws = moe_mod.alloc_workspace(M, h, i, E, k, device=L.dev)
+    out = moe_mod.moe_fp8_forward_ws(L.tx, L.tl, L.t13, L.ts13, L.t2, L.ts2, k, ws)
+    torch.cuda.synchronize()
+    return out, ws
+
+
+def _check_intermediates(moe_mod, L: Layer, ws, inter, tokens=None):
+    M, h, i, E, k = L.dims
+    lay = moe_mod.workspace_layout(M, h, i, E, k)
+    ids = read_ws(ws, lay.topk_ids, M * k, np.int32).reshape(M, k)
+    tw = read_ws(ws, lay.topk_w, M * k, np.float32).reshape(M, k)
+    xq = read_ws(ws, lay.xq, M * h, np.uint8).reshape(M, h)
+    xs = read_ws(ws, lay.xs, M * h // 128, np.float32).reshape(M, h // 128)
+    sel = slice(None) if tokens is None else tokens
+    assert np.array_equal(ids[sel], inter["ids"])
+    np.testing.assert_allclose(tw[sel], inter["topk_w"], rtol=0, atol=1e-6)
+    assert np.array_equal(xq[sel], inter["xq"])
+    assert np.array_equal(xs[sel], inter["xs"])
+    counts = read_ws(ws, lay.counts, E, np.int32)
+    offsets = read_ws(ws, lay.offsets, E + 1, np.int32)
+    srt = read_ws(ws, lay.sorted, M * k, np.int32)
+    cr, orr, sr = oracle.group(ids.ravel(), E)       # full-batch grouping of the (checked) ids
+    assert np.array_equal(counts, cr) and np.array_equal(offsets, orr) and np.array_equal(srt, sr)
+    nact = int(read_ws(ws, lay.num_active, 1, np.int32)[0])
+    act = read_ws(ws, lay.active, E, np.int32)[:nact]
+    assert np.array_equal(act, np.nonzero(cr)[0])
+
+
+@pytest.mark.parametrize("ci", [0, 1, 2, 3])
+def test_forward_matches_oracle(dev, moe_mod, ci):
+    cfg = synth.CONFIGS[ci]
+    log(f"forward {cfg.name}: inputs")
+    L = Layer(cfg, synth.default_seed(ci), dev)
+    log(f"forward {cfg.name}: gpu")
+    out, ws = _run(moe_mod, L)
+    log(f"forward {cfg.name}: oracle")
+    ref, inter = L.oracle(intermediates=True)
+    _check_intermediates(moe_mod, L, ws, inter)
+    err, mx, cos = check_output(to_host_bits(out), ref)
+    log(f"forward {cfg.name}: max|err| {err:.3g} max|ref| {mx:.3g} min cos {cos:.6f}")
+
+
+def test_forward_prefill_sampled(dev, moe_mod):
+    """M=8192 at full size in the launch configuration of the benchmark; the
+    oracle computes a sample of tokens (each token's output depends only on
+    its own inputs) and the full routing/grouping."""
+    ci = 4
+    cfg = synth.CONFIGS[ci]
+    log(f"forward {cfg.name}: inputs")
+    L = Layer(cfg, synth.default_seed(ci), dev)
+    log(f"forward {cfg.name}: gpu")
+    out, ws = _run(moe_mod, L)
+    ids_all, _ = oracle.router(L.logits, cfg.k)
+    rare = [int(np.nonzero((ids_all == e).any(1))[0][0]) for e in range(cfg.E - 8, cfg.E)
+            if (ids_all == e).any()]
+    rng = np.random.default_rng(0)
+    tokens = np.unique(np.concatenate([np.arange(8), np.arange(cfg.M - 8, cfg.M),
+                                       rng.choice(cfg.M, 24, replace=False), rare])).astype(np.int64)
+    log(f"forward {cfg.name}: oracle on {tokens.size} tokens")
+    ref, inter = L.oracle(tokens=tokens, intermediates=True)
+    _check_intermediates(moe_mod, L, ws, inter, tokens=tokens)
+    got = to_host_bits(out)[tokens]
+    err, mx, cos = check_output(got, ref)
+    log(f"forward {cfg.name}: max|err| {err:.3g} max|ref| {mx:.3g} min cos {cos:.6f}")
+
+
+@pytest.mark.parametrize("ci", [1, 2])
+def test_forward_deterministic_eager_and_graph(dev, moe_mod, ci):
+    cfg = synth.CONFIGS[ci]
+    L = Layer(cfg, synth.default_seed(ci), dev)
+    M, h, i, E, k = L.dims
+    ws = moe_mod.alloc_workspace(M, h, i, E, k, device=dev)
+    out0 = moe_mod.moe_fp8_forward_ws(L.tx, L.tl, L.t13, L.ts13, L.t2, L.ts2, k, ws)
+    torch.cuda.synchronize()
+    ref = out0.clone()
+    log(f"determinism {cfg.name}: 20 eager runs")
+    for _ in range(20):
+        o = moe_mod.moe_fp8_forward_ws(L.tx, L.tl, L.t13, L.ts13, L.t2, L.ts2, k, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), ref.view(torch.int16))
+    log(f"determinism {cfg.name}: graph capture")
+    gout = torch.empty_like(ref)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        moe_mod.moe_fp8_forward_ws(L.tx, L.tl, L.t13, L.ts13, L.t2, L.ts2, k, ws, out=gout)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        moe_mod.moe_fp8_forward_ws(L.tx, L.tl, L.t13, L.ts13, L.t2, L.ts2, k, ws, out=gout)
+    log(f"determinism {cfg.name}: 20 graph replays")
+    for r in range(20):
+        gout.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(gout.view(torch.int16), ref.view(torch.int16)), f"replay {r}"
+        # eager work between replays
+        moe_mod.moe_fp8_forward_ws(L.tx, L.tl, L.t13, L.ts13, L.t2, L.ts2, k, ws)
+        torch.cuda.synchronize()
+
+
+def _custom_layer(dev, M, h, i, E, k, seed, logits_kind="normal"):
+    cfg = synth.LayerConfig(f"m{M}_h{h}_i{i}_e{E}_top{k}", M, h, i, E, k, logits_kind, "edge case")
+    return Layer(cfg, seed, dev)
+
+
+@pytest.mark.parametrize("M,h,i,E,k", [
+    (3, 384, 256, 6, 3),        # ragged K-block counts (3 and 2)
+    (40, 256, 128, 2, 1),       # 20 routes per expert: two token groups per expert
+    (5, 256, 128, 1, 1),        # one expert, k = 1
+    (4, 256, 128, 8, 8),        # k = E
+    (7, 1280, 640, 256, 16),    # E = 256, k = 16
+    (1, 128, 128, 4, 2),        # smallest dims
+])
+def test_forward_edge_shapes(dev, moe_mod, M, h, i, E, k):
+    log(f"edge forward M={M} h={h} i={i} E={E} k={k}")
+    L = _custom_layer(dev, M, h, i, E, k, seed=M * 31 + h)
+    out, ws = _run(moe_mod, L)
+    ref, inter = L.oracle(intermediates=True)
+    _check_intermediates(moe_mod, L, ws, inter)
+    check_output(to_host_bits(out), ref)
+
+
+def test_forward_zero_input_and_empty(dev, moe_mod):
+    L = _custom_layer(dev, 4, 256, 128, 8, 2, seed=5)
+    L.tx.zero_()
+    out, _ = _run(moe_mod, L)
+    assert torch.count_nonzero(out.view(torch.int16)).item() == 0
+    # M == 0 is a no-op
+    e = torch.empty((0, 256), dtype=torch.bfloat16, device=dev)
+    el = torch.empty((0, 8), dtype=torch.float32, device=dev)
+    ws = torch.empty(256, dtype=torch.uint8, device=dev)
+    o = moe_mod.moe_fp8_forward_ws(e, el, L.t13, L.ts13, L.t2, L.ts2, 2, ws)
+    assert o.shape == (0, 256)
+
+
+def test_forward_bound_workspace(dev, moe_mod):
+    L = _custom_layer(dev, 4, 256, 128, 8, 2, seed=6)
+    M, h, i, E, k = L.dims
+    ws = moe_mod.alloc_workspace(M, h, i, E, k, device=dev)
+    moe_mod.bind_workspace(ws)
+    try:
+        out = moe_mod.moe_fp8_forward(L.tx, L.tl, L.t13, L.ts13, L.t2, L.ts2, k)
+        torch.cuda.synchronize()
+    finally:
+        moe_mod.bind_workspace(None)
+    check_output(to_host_bits(out), L.oracle())
+    with pytest.raises(moe_mod.MoeError):
+        moe_mod.moe_fp8_forward(L.tx, L.tl, L.t13, L.ts13, L.t2, L.ts2, k)
