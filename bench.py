@@ -1,0 +1,294 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed FP8 block-scaled MoE layer on one MI355X.
+
+One step = one forward of the whole layer (router top-k, 1x128 activation
+quantisation, grouping, gate/up GEMM, SiLU-mul requantisation, down GEMM,
+fixed-order combine) over one batch of synthetic input already resident in
+HBM.  The default workload is the one-token decode layer
+(M=1, h=2048, i=768, E=128, top-8).
+
+Timing: the forwards of C rotation copies (distinct weight copies and
+inputs, together far larger than the 256 MB Infinity Cache, so every step
+streams its experts from HBM) are captured in one HIP graph; W warm-up steps,
+then exactly K timed steps between a synchronisation and HIP events on both
+sides.  A second pass launches the same forwards with HIP events recorded
+between their stages (queued behind a spin kernel so the events bracket
+execution only) and reports the dominant stage's mean duration against its
+roofline.  The CPU baseline is the oracle (plain C, all host
+threads) on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
+MALL_BYTES = 256 << 20         # Infinity Cache
+METRIC = "MoE-layer tokens/s; %HBM peak at M=1/12 and %FP8 MFMA peak at M=8192"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--config", type=int, default=1, help="layer shape index (0..4); 1 = decode M=1")
+    ap.add_argument("--copies", type=int, default=0, help="rotation copies (0 = enough to exceed 4x the Infinity Cache)")
+    ap.add_argument("--timing-replays", type=int, default=20)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=None)
+    return ap.parse_args()
+
+
+def weight_bytes_per_expert(cfg):
+    w13 = 2 * cfg.i * cfg.h + (2 * cfg.i // 128) * (cfg.h // 128) * 4
+    w2 = cfg.h * cfg.i + (cfg.h // 128) * (cfg.i // 128) * 4
+    return w13, w2
+
+
+def stage_work(cfg, stage, U):
+    """Algorithmic bytes (HBM-bound stages) and FLOPs of one launch of a stage."""
+    M, h, i, k = cfg.M, cfg.h, cfg.i, cfg.k
+    w13, w2 = weight_bytes_per_expert(cfg)
+    act = M * h + M * (h // 128) * 4
+    if stage.startswith("stream_gate_up") or stage.startswith("gate_up"):
+        return U * w13 + act, 4.0 * M * k * h * i
+    if stage.startswith("stream_down") or stage.startswith("down"):
+        return U * w2, 2.0 * M * k * h * i
+    if stage.startswith("route_quant"):
+        return M * h * 2 + M * cfg.E * 4 + act + M * k * 8, 0.0
+    if stage.startswith("combine"):
+        return M * h * 2 + M * k * 4, 0.0
+    if stage.startswith("fused"):
+        return U * (w13 + w2) + M * h * 2 * 2 + M * cfg.E * 4, 6.0 * M * k * h * i
+    return 0, 0.0
+
+
+def source_digest(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, workload):
+    """HBM traffic per launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))[f"{workload}:{kernel}"]
+    except (KeyError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != source_digest(rec["sources"]):
+        return None
+    return rec["bytes_per_launch"]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the layer is not sharded across GPUs", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fp8_block_scaled_router_amd as moe
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    moe.lib()
+    dev = torch.device("cuda:0")
+    cfg = synth.CONFIGS[args.config]
+    seed = synth.default_seed(args.config) if args.seed is None else args.seed
+    M, h, i, E, k = cfg.M, cfg.h, cfg.i, cfg.E, cfg.k
+    w13b, w2b = weight_bytes_per_expert(cfg)
+    wbytes = E * (w13b + w2b)
+
+    # ---- inputs: weights drawn on the host, quantised on the GPU by the library
+    t0 = time.time()
+    w13_f = synth.make_w13_f32(cfg, seed)
+    w2_f = synth.make_w2_f32(cfg, seed)
+    q13, s13 = moe.quantize_weight_block128(torch.from_numpy(w13_f).to(dev))
+    q2, s2 = moe.quantize_weight_block128(torch.from_numpy(w2_f).to(dev))
+    torch.cuda.synchronize()
+    # Rotation: enough weight copies that a copy's experts are touched again
+    # only after >= 4x the Infinity Cache of other traffic (distinct experts
+    # per step measured with the library's own router on copy 0).
+    ids0, _ = moe.router_topk(torch.from_numpy(synth.make_logits(cfg, seed, copy=0)).to(dev), k)
+    U0 = int(torch.unique(ids0).numel())
+    step_bytes = U0 * (w13b + w2b)
+    C = args.copies or max(2, math.ceil(4 * MALL_BYTES / step_bytes) + 1)
+    C = max(1, min(C, int((48 << 30) // wbytes)))
+    W = [(q13, s13, q2, s2)] + [(q13.clone(), s13.clone(), q2.clone(), s2.clone()) for _ in range(C - 1)]
+    X, Lg, WS, OUT = [], [], [], []
+    for c in range(C):
+        xb = synth.make_x(cfg, seed, copy=c)
+        X.append(torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev))
+        Lg.append(torch.from_numpy(synth.make_logits(cfg, seed, copy=c)).to(dev))
+        WS.append(moe.alloc_workspace(M, h, i, E, k, device=dev))
+        OUT.append(torch.empty((M, h), dtype=torch.bfloat16, device=dev))
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+
+    def fwd(c):
+        a = W[c]
+        moe.moe_fp8_forward_ws(X[c], Lg[c], a[0], a[1], a[2], a[3], k, WS[c], out=OUT[c])
+
+    # eager warm-up of every copy, then distinct experts per copy
+    for c in range(C):
+        fwd(c)
+    torch.cuda.synchronize()
+    lay = moe.workspace_layout(M, h, i, E, k)
+    U = [int(WS[c][lay.num_active:lay.num_active + 4].view(torch.int32).item()) for c in range(C)]
+    assert all(torch.isfinite(OUT[c].float()).all().item() for c in range(C))
+
+    # ---- graphs: all C forwards, and the first r forwards for a remainder
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+
+    def capture(n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for c in range(n):
+                fwd(c)
+        return g
+
+    g_all = capture(C)
+    rem = args.steps % C
+    g_rem = capture(rem) if rem else None
+
+    def run_steps(n):
+        for _ in range(n // C):
+            g_all.replay()
+        r = n % C
+        if r:
+            if r == rem:
+                g_rem.replay()
+            else:
+                for c in range(r):
+                    fwd(c)
+
+    run_steps(args.warmup)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    run_steps(args.steps)
+    e1.record()
+    torch.cuda.synchronize()
+    total_ms = e0.elapsed_time(e1)
+    ms_per_step = total_ms / args.steps
+    tokens_per_s = M / (ms_per_step / 1e3)
+
+    # ---- per-stage durations from HIP events between the stages
+    names = moe.forward_kernel_names(M, h, i, E, k)
+    nst = len(names)
+    evs = [moe.HipEvents(nst + 1) for _ in range(C)]
+
+    def fwd_timed(c):
+        a = W[c]
+        moe.moe_fp8_forward_ws_timed(X[c], Lg[c], a[0], a[1], a[2], a[3], k, WS[c], evs[c], out=OUT[c])
+
+    # Events recorded inside a captured graph cannot be queried on this
+    # runtime, so the stages are launched eagerly behind a GPU spin kernel:
+    # the host enqueues every stage and event before the GPU reaches them, so
+    # each event pair brackets one stage's execution, not host latency.
+    sums = np.zeros(nst)
+    count = 0
+    for _ in range(args.timing_replays):
+        torch.cuda.synchronize()
+        torch.cuda._sleep(5_000_000)
+        for c in range(C):
+            fwd_timed(c)
+        torch.cuda.synchronize()
+        for c in range(C):
+            sums += [evs[c].elapsed_ms(j, j + 1) for j in range(nst)]
+        count += C
+    timing_mode = "eager behind a spin kernel"
+    stage_ms = sums / count
+    dom = int(np.argmax(stage_ms))
+    U_mean = float(np.mean(U))
+    abytes, aflops = stage_work(cfg, names[dom], U_mean)
+    dom_s = stage_ms[dom] / 1e3
+    bound = "hbm" if M <= 64 else "mfma"
+    if bound == "hbm":
+        achieved = abytes / dom_s / 1e9
+        peak, unit = HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved = aflops / dom_s / 1e12
+        peak, unit = FP8_PEAK_TFLOPS, "TFLOP/s"
+    roofline = {"bound": bound, "kernel": names[dom], "achieved": round(achieved, 2), "peak": peak,
+                "unit": unit, "frac": round(achieved / peak, 4),
+                "traffic": load_traffic(names[dom], cfg.name),
+                "avg_launch_us": round(stage_ms[dom] * 1e3, 3),
+                "algorithmic_bytes_per_launch": int(abytes),
+                "algorithmic_flops_per_launch": aflops,
+                "timing": f"HIP events between stages, {timing_mode} replay, {count} launches"}
+    for ev in evs:
+        ev.close()
+
+    # ---- CPU baseline: the oracle on a bounded sample of the same workload
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        q13h, s13h = oracle.quant_weight_block128(w13_f)
+        q2h, s2h = oracle.quant_weight_block128(w2_f)
+        del w13_f, w2_f
+        batch = max(1, min(M, 64))
+        done, t_cpu, first = 0, 0.0, 0
+        while t_cpu < args.cpu_seconds and done < 1 << 16:
+            xb = synth.make_x(cfg, seed, copy=C + 1, M=batch, first_token=first)
+            lb = synth.make_logits(cfg, seed, copy=C + 1, M=batch, first_token=first)
+            t1 = time.perf_counter()
+            oracle.moe_forward(xb, lb, q13h, s13h, q2h, s2h, k)
+            t_cpu += time.perf_counter() - t1
+            done += batch
+            first += batch
+        cpu = {"value": round(done / t_cpu, 3), "unit": "tokens/s", "cores": oracle.get_threads(),
+               "kind": "oracle",
+               "sample": f"{done} tokens of {cfg.name} in batches of {batch}, {t_cpu:.1f} s wall"}
+
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3 (fp32 accumulate)",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "M": M, "h": h, "i": i, "E": E, "k": k,
+                   "rotation_copies": C, "distinct_experts_mean": U_mean,
+                   "layer_bytes_per_step": int(U_mean * (w13b + w2b) + M * h * 4 + M * E * 4),
+                   "timing": "HIP graph of C forwards, events around K steps",
+                   "stage_us": {n: round(v * 1e3, 3) for n, v in zip(names, stage_ms)},
+                   "setup_s": round(setup_s, 1)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

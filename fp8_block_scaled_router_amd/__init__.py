@@ -58,6 +58,9 @@ _SIGS = {
     "moe_fp8_group": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "moe_fp8_quantize_weight_block128": (_I, [_P, _I64, _I, _I, _P, _P, _P]),
     "moe_fp8_encode_e4m3": (_I, [_P, _I64, _P, _P]),
+    "moe_fp8_forward_ws_timed": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _SZ, _P, _I, _P]),
+    "moe_fp8_forward_kernel_count": (_I, [_I, _I, _I, _I, _I]),
+    "moe_fp8_forward_kernel_name": (ctypes.c_char_p, [_I, _I, _I, _I, _I, _I]),
 }
 
 
@@ -222,4 +225,53 @@ def encode_e4m3(v, stream=None):
     _dev(v, torch.float32, "v")
     out = torch.empty(v.shape, dtype=torch.uint8, device=v.device)
     _check(lib().moe_fp8_encode_e4m3(_ptr(v), v.numel(), _ptr(out), _stream(stream)), "moe_fp8_encode_e4m3")
+    return out
+
+
+def forward_kernel_names(M: int, h: int, i: int, E: int, k: int) -> list:
+    n = lib().moe_fp8_forward_kernel_count(M, h, i, E, k)
+    if n < 0:
+        raise MoeError(n, "moe_fp8_forward_kernel_count")
+    return [lib().moe_fp8_forward_kernel_name(M, h, i, E, k, j).decode() for j in range(n)]
+
+
+class HipEvents:
+    """A set of HIP timing events (hipEventCreate), for moe_fp8_forward_ws_timed."""
+
+    def __init__(self, n: int):
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), _P, _P]
+        self._hip.hipEventDestroy.argtypes = [_P]
+        self.handles = (ctypes.c_void_p * n)()
+        for j in range(n):
+            ev = ctypes.c_void_p()
+            if self._hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.handles[j] = ev
+        self.n = n
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        rc = self._hip.hipEventElapsedTime(ctypes.byref(ms), self.handles[a], self.handles[b])
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def close(self):
+        for j in range(self.n):
+            if self.handles[j]:
+                self._hip.hipEventDestroy(self.handles[j])
+                self.handles[j] = None
+
+
+def moe_fp8_forward_ws_timed(x, router_logits, w13, s13, w2, s2, k: int, workspace, events: HipEvents,
+                             out=None, stream=None):
+    """moe_fp8_forward_ws that also records events between its stages."""
+    M, h, i, E, out = _layer_args(x, router_logits, w13, s13, w2, s2, k, out)
+    _dev(workspace, torch.uint8, "workspace")
+    rc = lib().moe_fp8_forward_ws_timed(_ptr(x), _ptr(router_logits), _ptr(w13), _ptr(s13), _ptr(w2),
+                                        _ptr(s2), _ptr(out), M, h, i, E, int(k), _ptr(workspace),
+                                        workspace.numel(), events.handles, events.n, _stream(stream))
+    _check(rc, "moe_fp8_forward_ws_timed")
     return out
