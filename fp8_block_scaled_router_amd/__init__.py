@@ -42,7 +42,12 @@ class MoeError(RuntimeError):
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "topk_ids", "topk_w", "xq", "xs", "counts", "offsets", "sorted", "active",
-        "num_active", "gate_up", "act2", "act2_scale", "partial", "total")] + [("path", ctypes.c_int)]
+        "num_active", "gate_up", "act2", "act2_scale", "partial", "sync_error", "total")] + [
+        ("path", ctypes.c_int)]
+
+
+PATH_STREAM = 0
+PATH_FUSED_DECODE = 2
 
 
 _SIGS = {
@@ -61,6 +66,7 @@ _SIGS = {
     "moe_fp8_forward_ws_timed": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _SZ, _P, _I, _P]),
     "moe_fp8_forward_kernel_count": (_I, [_I, _I, _I, _I, _I]),
     "moe_fp8_forward_kernel_name": (ctypes.c_char_p, [_I, _I, _I, _I, _I, _I]),
+    "moe_fp8_workspace_init": (_I, [_P, _SZ, _P]),
 }
 
 
@@ -122,8 +128,22 @@ def workspace_layout(M: int, h: int, i: int, E: int, k: int) -> WsLayout:
 
 
 def alloc_workspace(M: int, h: int, i: int, E: int, k: int, device=None) -> torch.Tensor:
-    n = max(workspace_bytes(M, h, i, E, k), 256)
-    return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+    """A workspace for these sizes; its synchronisation words start at zero."""
+    n = max(workspace_bytes(M, h, i, E, k), 32768)
+    ws = torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+    workspace_init(ws)
+    return ws
+
+
+def workspace_init(ws: torch.Tensor, stream=None) -> None:
+    _dev(ws, torch.uint8, "workspace")
+    _check(lib().moe_fp8_workspace_init(_ptr(ws), ws.numel(), _stream(stream)), "moe_fp8_workspace_init")
+
+
+def workspace_error(ws: torch.Tensor, M: int, h: int, i: int, E: int, k: int) -> int:
+    """The workspace's sticky error word (0 = every wait completed)."""
+    off = workspace_layout(M, h, i, E, k).sync_error
+    return int(ws[off:off + 4].view(torch.int32).item())
 
 
 _bound = {}

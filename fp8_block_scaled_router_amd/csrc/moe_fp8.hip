@@ -10,6 +10,7 @@
 #include <mutex>
 
 #include "../../include/moe_fp8.h"
+#include "fused_decode.h"
 #include "launch.h"
 
 namespace {
@@ -43,15 +44,20 @@ struct Layout {
     size_t hist;   // grouping scratch: group_chunks(R) * E ints
 };
 
+int choose_path(int M, int h, int i, int E, int k) {
+    return moe::fused_supported(M, h, i, E, k) ? MOE_FP8_PATH_FUSED_DECODE : MOE_FP8_PATH_STREAM;
+}
+
 void make_layout(int M, int h, int i, int E, int k, Layout* L) {
     const size_t R = (size_t)M * k;
-    size_t cur = 0;
+    size_t cur = moe::kSyncBytes;   // synchronisation words first
     auto take = [&](size_t bytes) {
         const size_t o = cur;
         cur = align_up(cur + bytes);
         return o;
     };
     moe_fp8_ws_layout& p = L->pub;
+    p.sync_error = moe::kSyncErr;
     p.topk_ids = take(R * 4);
     p.topk_w = take(R * 4);
     p.xq = take((size_t)M * h);
@@ -62,10 +68,15 @@ void make_layout(int M, int h, int i, int E, int k, Layout* L) {
     p.active = take((size_t)E * 4);
     p.num_active = take(4);
     L->hist = take((size_t)moe::group_chunks((int)R) * E * 4);
-    p.path = 0;
+    p.path = choose_path(M, h, i, E, k);
     p.gate_up = take(R * 2 * i * 4);
-    p.act2 = (size_t)-1;
-    p.act2_scale = (size_t)-1;
+    if (p.path == MOE_FP8_PATH_FUSED_DECODE) {
+        p.act2 = take(R * i);
+        p.act2_scale = take(R * (i / 128) * 4);
+    } else {
+        p.act2 = (size_t)-1;
+        p.act2_scale = (size_t)-1;
+    }
     p.partial = take(R * h * 4);
     p.total = cur;
 }
@@ -77,14 +88,16 @@ T* at(void* base, size_t off) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
-// Kernels of one forward, in launch order (the streaming path).
-struct NameList {
-    const char* names[5] = {"route_quant_kernel", "group_hist+group_scatter",
-                            "stream_gate_up_kernel", "stream_down_kernel", "combine_kernel"};
-    int size() const { return 5; }
-    const char* operator[](int j) const { return names[j]; }
-};
-const NameList kForwardKernelNames;
+// Kernels of one forward, in launch order, per path.
+const char* const kStreamStages[] = {"route_quant_kernel", "group_hist+group_scatter",
+                                     "stream_gate_up_kernel", "stream_down_kernel",
+                                     "combine_kernel"};
+const char* const kFusedStages[] = {"fused_decode_kernel"};
+
+int stage_count(int path) { return path == MOE_FP8_PATH_FUSED_DECODE ? 1 : 5; }
+const char* stage_name(int path, int j) {
+    return path == MOE_FP8_PATH_FUSED_DECODE ? kFusedStages[j] : kStreamStages[j];
+}
 
 // Records events[j] (when given) before stage j, and events[n] after the last.
 struct EventHook {
@@ -129,6 +142,7 @@ int run_forward(const void* x, const float* router_logits, const void* w13, cons
     float* g = at<float>(workspace, p.gate_up);
     float* y = at<float>(workspace, p.partial);
     EventHook hook{events, n_events, 0, stream};
+    uint32_t* sync = at<uint32_t>(workspace, 0);
 
 #define MOE_STEP(call)                                      \
     do {                                                    \
@@ -137,6 +151,42 @@ int run_forward(const void* x, const float* router_logits, const void* w13, cons
         if (rc != MOE_OK) return rc;                        \
     } while (0)
 
+    if (p.path == MOE_FP8_PATH_FUSED_DECODE) {
+        moe::FusedArgs fa;
+        fa.x = static_cast<const uint16_t*>(x);
+        fa.logits = router_logits;
+        fa.w13 = static_cast<const uint8_t*>(w13);
+        fa.s13 = s13;
+        fa.w2 = static_cast<const uint8_t*>(w2);
+        fa.s2 = s2;
+        fa.out = static_cast<uint16_t*>(out);
+        fa.M = M;
+        fa.h = h;
+        fa.i = i;
+        fa.E = E;
+        fa.k = k;
+        fa.umax = E < R ? E : R;
+        fa.ids = ids;
+        fa.tw = tw;
+        fa.xq = xq;
+        fa.xs = xs;
+        fa.counts = counts;
+        fa.offsets = offsets;
+        fa.sorted = sorted;
+        fa.active = active;
+        fa.num_active = num_active;
+        fa.g = g;
+        fa.a2 = at<uint8_t>(workspace, p.act2);
+        fa.a2s = at<float>(workspace, p.act2_scale);
+        fa.y = y;
+        fa.gate_tix = sync + moe::kSyncGateTix / 4;
+        fa.done = sync + moe::kSyncDone / 4;
+        fa.comb_tix = sync + moe::kSyncCombTix / 4;
+        fa.exit_cnt = sync + moe::kSyncExit / 4;
+        fa.err = sync + moe::kSyncErr / 4;
+        MOE_STEP(moe::launch_fused_decode(fa, stream));
+        return hook.mark() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    }
     MOE_STEP(moe::launch_route_quant(router_logits, static_cast<const uint16_t*>(x), M, E, k, h,
                                      ids, tw, xq, xs, moe::kRoute | moe::kQuant, stream));
     MOE_STEP(moe::launch_group(ids, R, E, hist, counts, offsets, sorted, active, num_active,
@@ -195,6 +245,8 @@ int moe_fp8_bind_workspace(void* dev_ptr, size_t bytes) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
     if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+    if (dev_ptr && bytes < moe::kSyncBytes) return MOE_ERR_WORKSPACE;
+    if (dev_ptr && hipMemset(dev_ptr, 0, moe::kSyncBytes) != hipSuccess) return MOE_ERR_HIP;
     std::lock_guard<std::mutex> lock(g_bind_mu);
     g_bind[dev].ptr = dev_ptr;
     g_bind[dev].bytes = dev_ptr ? bytes : 0;
@@ -225,13 +277,20 @@ int moe_fp8_forward_kernel_count(int M, int h, int i, int E, int k) {
     const int rc = check_shape(M, h, i, E, k);
     if (rc != MOE_OK) return rc;
     if (M == 0) return 0;
-    return kForwardKernelNames.size();
+    return stage_count(choose_path(M, h, i, E, k));
 }
 
 const char* moe_fp8_forward_kernel_name(int M, int h, int i, int E, int k, int j) {
     const int n = moe_fp8_forward_kernel_count(M, h, i, E, k);
     if (n <= 0 || j < 0 || j >= n) return nullptr;
-    return kForwardKernelNames[j];
+    return stage_name(choose_path(M, h, i, E, k), j);
+}
+
+int moe_fp8_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!workspace || ((uintptr_t)workspace % kAlign) != 0) return MOE_ERR_INVALID;
+    if (workspace_bytes < moe::kSyncBytes) return MOE_ERR_WORKSPACE;
+    return hip_status(moe::launch_zero_words(static_cast<uint32_t*>(workspace), moe::kSyncBytes / 4,
+                                             stream));
 }
 
 int moe_fp8_forward(const void* x, const float* router_logits, const void* w13, const float* s13,

@@ -57,6 +57,12 @@ enum {
     MOE_ERR_HIP = -4           /* a HIP call or kernel launch failed */
 };
 
+/* Forward paths (chosen from the sizes alone, see moe_fp8_workspace_layout):
+ * small batches run the whole layer in one persistent kernel; larger ones
+ * run router+quant, grouping, gate/up, down and combine kernels. */
+#define MOE_FP8_PATH_STREAM 0
+#define MOE_FP8_PATH_FUSED_DECODE 2
+
 /* Shape limits of this build. */
 #define MOE_FP8_MAX_EXPERTS 256
 #define MOE_FP8_MAX_TOPK 16
@@ -70,12 +76,27 @@ const char* moe_fp8_status_string(int status);
  * or an unsupported shape). */
 size_t moe_fp8_workspace_bytes(int M, int h, int i, int E, int k);
 
+/* Workspaces.  The first 32 KiB of every workspace hold synchronisation
+ * counters that must be zero before the workspace's first forward; every
+ * forward leaves them zero again.  moe_fp8_bind_workspace zeroes them;
+ * a caller-managed workspace is zeroed once with moe_fp8_workspace_init (or
+ * allocated zero-filled).  The word at moe_fp8_ws_layout.sync_error stays 0
+ * unless a wait between workgroups timed out (a broken device or a corrupted
+ * workspace), in which case it is set and that forward's output is invalid. */
+
 /* Bind `bytes` of device memory at `dev_ptr` (256-byte aligned) as the
- * workspace moe_fp8_forward uses on the CURRENT device.  The library keeps
- * the pointer, not the memory: the caller owns it and must keep it alive
- * while bound.  Passing NULL unbinds.  Not on the launch path; call it once
- * before capturing graphs.  Returns MOE_ERR_INVALID on misalignment. */
+ * workspace moe_fp8_forward uses on the CURRENT device, and zero its
+ * synchronisation words (synchronously).  The library keeps the pointer, not
+ * the memory: the caller owns it and must keep it alive while bound.
+ * Passing NULL unbinds.  Not on the launch path; call it once before
+ * capturing graphs.  Returns MOE_ERR_INVALID on misalignment and
+ * MOE_ERR_WORKSPACE below 32 KiB. */
 int moe_fp8_bind_workspace(void* dev_ptr, size_t bytes);
+
+/* Zero the synchronisation words of a workspace (a kernel on `stream`, so it
+ * may be captured).  Needed once before the first forward on a workspace that
+ * was not allocated zero-filled. */
+int moe_fp8_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* The whole layer with the workspace bound to the current device.
  *   x              bf16 [M, h]
@@ -140,8 +161,9 @@ typedef struct {
     size_t act2;        /* e4m3  [M*k, i]   by route id                 */
     size_t act2_scale;  /* fp32  [M*k, i/128]                           */
     size_t partial;     /* fp32  [M*k, h]   by route id                 */
+    size_t sync_error;  /* uint32 error word (0 = no wait timed out)    */
     size_t total;       /* bytes                                        */
-    int    path;        /* 0 = weight-streaming path, 1 = tiled MFMA path */
+    int    path;        /* MOE_FP8_PATH_*                               */
 } moe_fp8_ws_layout;
 
 /* Fills *layout for these sizes.  Returns MOE_ERR_UNSUPPORTED / INVALID as

@@ -171,8 +171,15 @@ def _run(moe_mod, L: Layer):
     return out, ws
 
 
+def _check_sync_clean(ws):
+    """Every forward leaves the synchronisation words zero and no wait timed out."""
+    words = ws[:32768].view(torch.int32).cpu().numpy()
+    assert not words.any(), f"sync words not reset: {np.nonzero(words)[0][:10]}"
+
+
 def _check_intermediates(moe_mod, L: Layer, ws, inter, tokens=None):
     M, h, i, E, k = L.dims
+    _check_sync_clean(ws)
     lay = moe_mod.workspace_layout(M, h, i, E, k)
     ids = read_ws(ws, lay.topk_ids, M * k, np.int32).reshape(M, k)
     tw = read_ws(ws, lay.topk_w, M * k, np.float32).reshape(M, k)
@@ -315,3 +322,42 @@ def test_forward_bound_workspace(dev, moe_mod):
     check_output(to_host_bits(out), L.oracle())
     with pytest.raises(moe_mod.MoeError):
         moe_mod.moe_fp8_forward(L.tx, L.tl, L.t13, L.ts13, L.t2, L.ts2, k)
+
+
+def test_fused_path_m_sweep_and_shared_workspace(dev, moe_mod):
+    """Small batches M = 1..16 on the one-kernel path, all through ONE workspace
+    sized for the largest, in a row: ragged M, and sync words that must come
+    back clean after every forward whatever the previous shape was."""
+    h, i, E, k = 2048, 768, 128, 8
+    cfg16 = synth.LayerConfig("m16", 16, h, i, E, k, "normal", "sweep")
+    big = Layer(cfg16, 777, dev)
+    assert moe_mod.workspace_layout(16, h, i, E, k).path == moe_mod.PATH_FUSED_DECODE
+    ws = moe_mod.alloc_workspace(16, h, i, E, k, device=dev)
+    for M in (1, 2, 3, 5, 8, 13, 16, 1):
+        log(f"fused sweep M={M}")
+        cfg = synth.LayerConfig(f"m{M}", M, h, i, E, k, "normal", "sweep")
+        L = Layer(cfg, 777, dev, x=big.x[:M], logits=big.logits[:M],
+                  weights=(big.q13, big.s13, big.q2, big.s2))
+        out = moe_mod.moe_fp8_forward_ws(L.tx, L.tl, L.t13, L.ts13, L.t2, L.ts2, k, ws)
+        torch.cuda.synchronize()
+        _check_sync_clean(ws)
+        check_output(to_host_bits(out), L.oracle())
+
+
+def test_stream_then_fused_on_one_workspace(dev, moe_mod):
+    """A workspace used by the multi-kernel path and then the fused path."""
+    h, i, E, k = 256, 128, 8, 2
+    cfg = synth.LayerConfig("m40", 40, h, i, E, k, "normal", "mix")
+    L40 = Layer(cfg, 91, dev)
+    assert moe_mod.workspace_layout(40, h, i, E, k).path == moe_mod.PATH_STREAM
+    ws = moe_mod.alloc_workspace(40, h, i, E, k, device=dev)
+    out = moe_mod.moe_fp8_forward_ws(L40.tx, L40.tl, L40.t13, L40.ts13, L40.t2, L40.ts2, k, ws)
+    torch.cuda.synchronize()
+    check_output(to_host_bits(out), L40.oracle())
+    cfg4 = synth.LayerConfig("m4", 4, h, i, E, k, "normal", "mix")
+    L4 = Layer(cfg4, 91, dev, x=L40.x[:4], logits=L40.logits[:4],
+               weights=(L40.q13, L40.s13, L40.q2, L40.s2))
+    out = moe_mod.moe_fp8_forward_ws(L4.tx, L4.tl, L4.t13, L4.ts13, L4.t2, L4.ts2, k, ws)
+    torch.cuda.synchronize()
+    _check_sync_clean(ws)
+    check_output(to_host_bits(out), L4.oracle())
