@@ -67,6 +67,7 @@ _SIGS = {
     "moe_fp8_forward_kernel_count": (_I, [_I, _I, _I, _I, _I]),
     "moe_fp8_forward_kernel_name": (ctypes.c_char_p, [_I, _I, _I, _I, _I, _I]),
     "moe_fp8_workspace_init": (_I, [_P, _SZ, _P]),
+    "moe_fp8_workspace_head_bytes": (_SZ, []),
 }
 
 
@@ -129,7 +130,7 @@ def workspace_layout(M: int, h: int, i: int, E: int, k: int) -> WsLayout:
 
 def alloc_workspace(M: int, h: int, i: int, E: int, k: int, device=None) -> torch.Tensor:
     """A workspace for these sizes; its synchronisation words start at zero."""
-    n = max(workspace_bytes(M, h, i, E, k), 32768)
+    n = max(workspace_bytes(M, h, i, E, k), int(lib().moe_fp8_workspace_head_bytes()))
     ws = torch.empty(n, dtype=torch.uint8, device=device or "cuda")
     workspace_init(ws)
     return ws
@@ -144,6 +145,10 @@ def workspace_error(ws: torch.Tensor, M: int, h: int, i: int, E: int, k: int) ->
     """The workspace's sticky error word (0 = every wait completed)."""
     off = workspace_layout(M, h, i, E, k).sync_error
     return int(ws[off:off + 4].view(torch.int32).item())
+
+
+SYNC_EPOCH_OFFSET = 0     # forwards of the one-kernel path run on a workspace
+SYNC_EXIT_OFFSET = 256    # zero between forwards
 
 
 _bound = {}

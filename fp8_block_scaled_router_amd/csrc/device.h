@@ -39,18 +39,37 @@ __device__ __forceinline__ uint32_t bf16x2(float lo, float hi) {
     return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-// Quantise eight floats that share the scale s (s == 0 gives zero codes).
-// The quotient is the correctly rounded fp32 division v / s.
+// E4M3 codes of four values v / s, exactly E4M3(RN_fp32(v / s)) (the
+// correctly rounded fp32 quotient, then E4M3 rounding), without a division
+// on the common path.  q = v * rcp(s) is within 2^-22 (relative) of v / s
+// (v_rcp_f32 is accurate to 1 ulp), so RN_fp32(v / s) lies strictly between
+// q * (1 - 2^-20) and q * (1 + 2^-20).  E4M3 rounding is monotone: when both
+// ends give the same code, that is the code of RN_fp32(v / s).  Otherwise
+// (v / s within a hair of an E4M3 rounding boundary) the exact division
+// decides.  Tiny scales, whose reciprocal could overflow, take the division.
+__device__ __forceinline__ uint32_t quant4(float v0, float v1, float v2, float v3, float s,
+                                           float r) {
+    const float lo = 1.0f - 0x1.0p-20f, hi = 1.0f + 0x1.0p-20f;
+    const float q0 = v0 * r, q1 = v1 * r, q2 = v2 * r, q3 = v3 * r;
+    const uint32_t a = e4m3x4(q0 * lo, q1 * lo, q2 * lo, q3 * lo);
+    const uint32_t b = e4m3x4(q0 * hi, q1 * hi, q2 * hi, q3 * hi);
+    if (__builtin_expect(a == b && s >= 0x1.0p-100f, 1)) return a;
+    return e4m3x4(v0 / s, v1 / s, v2 / s, v3 / s);
+}
+
+// Quantise eight floats that share the scale s (s == 0 gives zero codes):
+// codes E4M3(RN_fp32(v / s)).
 __device__ __forceinline__ uint2 quant8(const float v[8], float s) {
-    uint2 r;
+    uint2 c;
     if (s == 0.0f) {
-        r.x = 0u;
-        r.y = 0u;
+        c.x = 0u;
+        c.y = 0u;
     } else {
-        r.x = e4m3x4(v[0] / s, v[1] / s, v[2] / s, v[3] / s);
-        r.y = e4m3x4(v[4] / s, v[5] / s, v[6] / s, v[7] / s);
+        const float r = __builtin_amdgcn_rcpf(s);
+        c.x = quant4(v[0], v[1], v[2], v[3], s, r);
+        c.y = quant4(v[4], v[5], v[6], v[7], s, r);
     }
-    return r;
+    return c;
 }
 
 // ------------------------------------------------------------ reductions
@@ -98,6 +117,28 @@ __device__ __forceinline__ void key_step_xor(uint32_t& hi, uint32_t& lo, int mas
     key_max(hi, lo, ohi, olo);
 }
 
+// Inclusive prefix sum over the 64 lanes, DPP only: shifts of 1, 2, 4, 8
+// inside each row of 16, then the row totals carried by row_bcast:15 and
+// row_bcast:31.
+__device__ __forceinline__ int wave_scan_incl(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15 -> rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31 -> rows 2, 3
+    return v;
+}
+
+// Unsigned max over the 16 lanes of each DPP row.
+__device__ __forceinline__ uint32_t row16_max_u(uint32_t v) {
+    v = max(v, dpp_u<kDppQuadXor1>(v));
+    v = max(v, dpp_u<kDppQuadXor2>(v));
+    v = max(v, dpp_u<kDppRowHalfMirror>(v));
+    v = max(v, dpp_u<kDppRowMirror>(v));
+    return v;
+}
+
 // Wave-wide lexicographic max of 64-bit keys: DPP inside each row of 16
 // lanes, then two cross-row exchanges.  Every lane gets the result.
 __device__ __forceinline__ void wave_key_max(uint32_t& hi, uint32_t& lo) {
@@ -116,6 +157,52 @@ __device__ __forceinline__ uint32_t float_order_key(float v) {
     if (v == 0.0f) v = 0.0f;
     uint32_t u = __float_as_uint(v);
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ------------------------------------------- exchange between workgroups
+//
+// Data handed from one workgroup to another goes through agent-coherent
+// stores and loads (relaxed agent-scope atomics: sc1, visible across the
+// XCDs' separate L2s), and a writer waits for its own stores to complete
+// before the workgroup counts a ticket.  This orders exactly the exchanged
+// words without the whole-L2 write-back and invalidation an agent-scope fence
+// costs on gfx950.
+
+__device__ __forceinline__ void st_agent(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(uint32_t* p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
+    return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void st_agent64(uint64_t* p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_agent64(const uint64_t* p) {
+    return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A value with the tag of the forward that wrote it, in one 64-bit word
+// (stored and loaded whole, so a reader sees either the old word or the new).
+__device__ __forceinline__ uint64_t ll_pack(float v, uint32_t tag) {
+    return (uint64_t)__float_as_uint(v) | ((uint64_t)tag << 32);
+}
+__device__ __forceinline__ float ll_value(uint64_t w) { return __uint_as_float((uint32_t)w); }
+__device__ __forceinline__ uint32_t ll_tag(uint64_t w) { return (uint32_t)(w >> 32); }
+
+// Wait until every vector-memory operation this wave issued has completed
+// (s_waitcnt vmcnt(0)); the signal fences keep the compiler from moving
+// memory operations across it.
+__device__ __forceinline__ void wait_vmem() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // ----------------------------------------------------------------- MFMA

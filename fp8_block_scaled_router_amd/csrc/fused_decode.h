@@ -19,8 +19,7 @@ struct FusedArgs {
     const float* s2;
     uint16_t* out;
     int M, h, i, E, k;
-    int umax;  // min(E, M*k): bound on the number of experts with routes
-    // intermediates published / exchanged through the workspace
+    // routing and quantisation published by workgroup 0 (inspection)
     int32_t* ids;
     float* tw;
     uint8_t* xq;
@@ -30,29 +29,26 @@ struct FusedArgs {
     int32_t* sorted;
     int32_t* active;
     int32_t* num_active;
-    float* g;
-    uint8_t* a2;
-    float* a2s;
-    float* y;
-    // synchronisation words (zero between forwards)
-    uint32_t* gate_tix;  // [umax][i/128]
-    uint32_t* done;      // [umax]
-    uint32_t* comb_tix;  // [M][h/64]
-    uint32_t* exit_cnt;  // [1]
-    uint32_t* err;       // [1], sticky: set when a wait timed out
+    // exchange buffers: 64-bit (value, forward tag) words
+    uint64_t* g_ll;   // [M*k][2i] gate/up results by route
+    uint64_t* y_ll;   // [M*k][h]  down partials by route
+    // synchronisation words
+    uint32_t* sync;
 };
 
 bool fused_supported(int M, int h, int i, int E, int k);
 size_t fused_lds_bytes(int M, int h, int i, int E, int k);
 hipError_t launch_fused_decode(const FusedArgs& args, hipStream_t stream);
 
-// Sync-word region at the start of every workspace.
+// Sync-word region at the start of every workspace, then the fused path's
+// exchange region (fixed place, so no other path ever writes there).
 constexpr size_t kSyncBytes = 32768;
-constexpr size_t kSyncGateTix = 0;              // 4096 words
-constexpr size_t kSyncDone = 16384;             // 256 words
-constexpr size_t kSyncCombTix = 17408;          // 2048 words
-constexpr size_t kSyncExit = 25600;             // 1 word
-constexpr size_t kSyncErr = 25856;              // 1 word
+constexpr size_t kSyncEpoch = 0;                // word: forwards run on this workspace
+constexpr size_t kSyncExit = 256;               // word: workgroups finished in this forward
+constexpr size_t kSyncErr = 512;                // word: sticky error (a wait timed out)
+constexpr size_t kLLBytes = (size_t)8 << 20;    // g_ll (4 MiB) + y_ll (4 MiB)
+constexpr size_t kLLOffset = kSyncBytes;
+constexpr size_t kWorkspaceHead = kSyncBytes + kLLBytes;   // zero-initialised part
 hipError_t launch_zero_words(uint32_t* p, size_t words, hipStream_t stream);
 
 }  // namespace moe

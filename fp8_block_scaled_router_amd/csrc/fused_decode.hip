@@ -2,33 +2,39 @@
 // batches (M <= 16 tokens): decode and speculative verification.
 //
 // Every workgroup first recomputes, on chip, what it needs from the batch:
-// the router top-k of all M tokens (one wave per token, DPP/cross-lane
-// argmax), the 1x128 E4M3 activation codes of all tokens (into LDS) and the
-// grouping of the M*k routes by expert (ballot ranks).  Nothing then stands
-// between the kernel start and the first weight load but the logits and x
-// reads.  Work is split in two task lists:
+// the router top-k of all M tokens (one wave per token: DPP row maxima,
+// scalar readlanes and ballots; the picked logits come back out of the keys),
+// the 1x128 E4M3 activation codes of all tokens (into LDS) and the grouping
+// of the M*k routes by expert (ballot ranks, DPP prefix sums).  Work is then
+// split in two task lists:
 //
 //  A task (expert slot u, 128-column group jg, quarter q): 32 gate rows and
 //    the matching 32 up rows of w13[e_u], K = h, streamed once with
 //    v_mfma_f32_16x16x128_f8f6f4 (weights as A, the expert's <= 16 routes as
 //    B), per-128-K-block scale promotion; FP32 results per route (Netra
-//    compiler architecture page: gate/up FP32).  A ticket counts the four
-//    quarters of (u, jg); the last one computes SiLU(gate) * up for the
-//    group and requantises it to E4M3 per 128 columns (Netra Kernel README,
-//    MoE prefill pair: SiLU and quantisation), then counts the group done.
-//  B task (expert slot u, 64-row tile of w2[e_u]): loads its weights into
-//    registers before it waits for expert u's activations, then computes the
-//    fp32 partial rows of u's routes (down-partial).  A ticket per (token,
-//    tile) counts the token's k routes; the last one sums the k partials in
-//    rank order and writes bf16 (route reducer; Inferact amd-kernels README,
-//    atomics rule: atomics only count, sums run in a fixed order).
+//    compiler architecture page: gate/up FP32).
+//  B task (expert slot u, 64-row tile of w2[e_u]): its weights are loaded
+//    into registers before the workgroup's gate/up work is computed; it then
+//    computes SiLU(gate) * up of u's routes and their 1x128 E4M3
+//    requantisation straight into LDS (Netra Kernel README, MoE prefill pair:
+//    SiLU and quantisation), and the fp32 partial rows (down-partial).
+//  Combine: the workgroup that owns a token's last-rank route for a tile
+//    sums that tile's k partials in rank order and writes bf16 (route
+//    reducer; Inferact amd-kernels README, atomics rule: no atomic sums, a
+//    fixed order).  It does so only after all of its own B tasks.
 //
-// Synchronisation words live at the start of the workspace.  They must be
-// zero before the first forward and every forward leaves them zero (the last
-// arriver of each ticket resets it, the last workgroup to exit resets the
-// done counters).  Waits are bounded in time; a timeout sets a sticky error
-// word instead of hanging.  The grid never exceeds the number of workgroups
-// that can be resident at once, so every awaited task is always running.
+// Exchange between workgroups: each gate/up result and each partial is one
+// 64-bit word (value, tag of this forward) written and read with
+// agent-coherent stores and loads; a consumer polls the words it needs until
+// they carry this forward's tag.  The data is its own flag, so there are no
+// counters to contend on and no cache-wide fences.  The tag is the
+// workspace's forward count plus one, read at the start; the last workgroup
+// to exit advances it (and, once every 2^32 forwards, clears the exchange
+// region so that no stale word can ever carry a current tag).  Waits are
+// bounded in time; a timeout sets a sticky error word instead of hanging.
+// Tasks only wait on tasks of an earlier phase, and the grid never exceeds
+// the number of workgroups that can be resident at once, so every awaited
+// task is always running.
 #include "device.h"
 #include "fused_decode.h"
 
@@ -36,70 +42,68 @@ namespace moe {
 
 constexpr int kFusedMaxM = 16;
 constexpr int kFusedMaxIB = 8;              // i <= 1024
+constexpr int kMaxKB = 16;                  // gate/up K blocks loaded per batch
 constexpr int kQuarters = 4;                // A task: 32 gate + 32 up rows
 constexpr int kDownRows = 64;               // B task rows
 constexpr uint64_t kWaitTicks = 100000000;  // 1 s of the 100 MHz constant clock
 
-// ---------------------------------------------------------------------
-// routing of one token on one wave, results to LDS
-
-__device__ __forceinline__ void route_token(const float* __restrict__ l, int E, int k,
-                                            int* ids_l, float* w_l, int lane) {
-    uint32_t key[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int e = lane + 64 * j;
-        key[j] = (e < E) ? float_order_key(l[e]) : 0u;
-    }
-    int picked[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        picked[r] = 0;
-        if (r < k) {
-            uint32_t hi = 0u, lo = 0u;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (key[j] > hi) {
-                    hi = key[j];
-                    lo = 0xFFFFu - (uint32_t)(lane + 64 * j);
-                }
-            }
-            wave_key_max(hi, lo);
-            int e = (int)(0xFFFFu - lo);
-            e = (hi == 0u || e >= E) ? E - 1 : e;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (lane + 64 * j == e) key[j] = 0u;
-            picked[r] = e;
-        }
-    }
-    const float lmax = l[picked[0]];
-    float ex[16];
-    float sum = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        ex[r] = 0.0f;
-        if (r < k) {
-            ex[r] = expf(l[picked[r]] - lmax);
-            sum += ex[r];
-        }
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        if (r < k && lane == r) {
-            ids_l[r] = picked[r];
-            w_l[r] = ex[r] / sum;
-        }
-    }
+// Inverse of float_order_key (for a key of +-0 it returns +0).
+__device__ __forceinline__ float key_to_float(uint32_t key) {
+    const uint32_t u = (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key;
+    return __uint_as_float(u);
 }
 
-__device__ __forceinline__ int wave_incl_scan_i(int v, int lane) {
+__device__ __forceinline__ uint32_t readlane_u(uint32_t v, int lane) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
+}
+
+// Router of one token on one wave; lane l holds the logits of experts
+// l + 64j.  Each pick: a DPP max over each 16-lane row, the four row maxima
+// read into scalars, and the lowest expert index holding that key found by
+// ballot (ties go to the lower index, -0 equals +0).  Lane r keeps pick r;
+// the weights exp(l_r - l_0) / sum are summed in rank order.
+__device__ __forceinline__ void route_fast(const float lg[4], int E, int k, int* ids_l,
+                                           float* w_l, int lane) {
+    uint32_t key[4];
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int o = __shfl_up(v, d, kWave);
-        if (lane >= d) v += o;
+    for (int j = 0; j < 4; ++j) key[j] = (lane + 64 * j < E) ? float_order_key(lg[j]) : 0u;
+    int my_pick = 0;
+    float my_l = 0.0f, l0 = 0.0f;
+#pragma unroll 1
+    for (int r = 0; r < k; ++r) {
+        uint32_t m = max(max(key[0], key[1]), max(key[2], key[3]));
+        m = row16_max_u(m);
+        const uint32_t smax = max(max(readlane_u(m, 0), readlane_u(m, 16)),
+                                  max(readlane_u(m, 32), readlane_u(m, 48)));
+        int e = E - 1;   // only reached for NaN logits (outside the contract)
+        if (smax != 0u) {
+            const uint64_t b0 = __ballot(key[0] == smax);
+            const uint64_t b1 = __ballot(key[1] == smax);
+            const uint64_t b2 = __ballot(key[2] == smax);
+            const uint64_t b3 = __ballot(key[3] == smax);
+            e = b0 ? __builtin_ctzll(b0)
+              : b1 ? 64 + __builtin_ctzll(b1)
+              : b2 ? 128 + __builtin_ctzll(b2)
+              : b3 ? 192 + __builtin_ctzll(b3) : E - 1;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (lane + 64 * j == e) key[j] = 0u;
+        const float lv = key_to_float(smax);
+        if (r == 0) l0 = lv;
+        if (lane == r) {
+            my_pick = e;
+            my_l = lv;
+        }
     }
-    return v;
+    const float ex = lane < k ? expf(my_l - l0) : 0.0f;
+    float sum = 0.0f;
+#pragma unroll 1
+    for (int r = 0; r < k; ++r) sum += __uint_as_float(readlane_u(__float_as_uint(ex), r));
+    if (lane < k) {
+        ids_l[lane] = my_pick;
+        w_l[lane] = ex / sum;
+    }
 }
 
 // Lanes holding the same expert id (9-bit ids; 0x1FF = no route).
@@ -114,20 +118,37 @@ __device__ __forceinline__ uint64_t match_id(int e) {
     return same;
 }
 
-__device__ __forceinline__ void silu_quant_group(const float* __restrict__ gate,
-                                                 const float* __restrict__ up, int sub,
-                                                 uint8_t* __restrict__ q, float* __restrict__ s) {
-    const float4 g0 = reinterpret_cast<const float4*>(gate + sub * 8)[0];
-    const float4 g1 = reinterpret_cast<const float4*>(gate + sub * 8)[1];
-    const float4 u0 = reinterpret_cast<const float4*>(up + sub * 8)[0];
-    const float4 u1 = reinterpret_cast<const float4*>(up + sub * 8)[1];
-    const float a[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-    const float b[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+// SiLU(gate) * up of one 128-column group of one route on one 16-lane row,
+// requantised to E4M3 into LDS.  The lane's 16 gate/up words are loaded
+// together and reloaded together until they all carry this forward's tag.
+__device__ __forceinline__ void silu_quant_ll(const uint64_t* __restrict__ gate,
+                                              const uint64_t* __restrict__ up, int sub,
+                                              uint32_t tag, uint32_t* err, uint8_t* q, float* s) {
+    uint64_t wg[8], wu[8];
+    uint64_t t0 = 0;
+    for (int tries = 0;; ++tries) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            wg[j] = ld_agent64(gate + sub * 8 + j);
+            wu[j] = ld_agent64(up + sub * 8 + j);
+        }
+        bool ok = true;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ok = ok && ll_tag(wg[j]) == tag && ll_tag(wu[j]) == tag;
+        if (ok) break;
+        if (tries == 0) t0 = wall_clock64();
+        if (wall_clock64() - t0 > kWaitTicks) {
+            atomicOr(err, 1u);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
     float v[8];
     float m = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        v[j] = (a[j] / (1.0f + expf(-a[j]))) * b[j];
+        const float a = ll_value(wg[j]);
+        v[j] = (a / (1.0f + expf(-a))) * ll_value(wu[j]);
         m = fmaxf(m, fabsf(v[j]));
     }
     m = row16_max(m);
@@ -136,28 +157,13 @@ __device__ __forceinline__ void silu_quant_group(const float* __restrict__ gate,
     if (sub == 0) *s = sc;
 }
 
-// Thread 0 waits until *ctr >= target (bounded), then the workgroup acquires.
-__device__ __forceinline__ void wait_count(uint32_t* ctr, uint32_t target, uint32_t* err) {
-    if (threadIdx.x == 0) {
-        const uint64_t t0 = wall_clock64();
-        while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-            __builtin_amdgcn_s_sleep(1);
-            if (wall_clock64() - t0 > kWaitTicks) {
-                atomicOr(err, 1u);
-                break;
-            }
-        }
-    }
-    __syncthreads();
-    __threadfence();
-}
-
 __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
     extern __shared__ __align__(16) uint8_t smem[];
     const int M = a.M, h = a.h, i = a.i, E = a.E, k = a.k;
     const int R = M * k, G = h / 128, IB = i / 128, KB = h / 128, N13 = 2 * i;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int col = lane & 15, kg = lane >> 4;
+    uint32_t* err = a.sync + kSyncErr / 4;
 
     // ---- LDS carve (all offsets 16-byte aligned)
     uint8_t* xq_l = smem;                                            // [M][h]
@@ -167,77 +173,282 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
     int* off_l = reinterpret_cast<int*>(w_l + ((R + 3) & ~3));       // [E+1]
     int* act_l = off_l + ((E + 1 + 3) & ~3);                         // [E]
     int* srt_l = act_l + ((E + 3) & ~3);                             // [R]
-    int* base_l = srt_l + ((R + 3) & ~3);                            // [E]
-    int* misc_l = base_l + ((E + 3) & ~3);                           // [32]
+    int* cnt_l = srt_l + ((R + 3) & ~3);                             // [E]
+    int* misc_l = cnt_l + ((E + 3) & ~3);                            // [32]
     uint8_t* a2_l = reinterpret_cast<uint8_t*>(misc_l + 32);         // [16][i + 16]
     const int a2_stride = i + 16;
     float* a2s_l = reinterpret_cast<float*>(a2_l + 16 * a2_stride);  // [16][IB]
 
-    // ---- phase 0: routing, activation codes and grouping, on every workgroup
-    for (int t = wave; t < M; t += 4)
-        route_token(a.logits + (size_t)t * E, E, k, ids_l + t * k, w_l + t * k, lane);
-    for (int task = wave * 4 + (lane >> 4); task < M * G; task += 16) {
-        const int t = task / G, g = task - t * G;
-        const uint4 u = *reinterpret_cast<const uint4*>(a.x + (size_t)t * h + g * 128 + col * 8);
-        float v[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
-                      bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w)};
-        float m = 0.0f;
+    // ---- phase 0: tag, routing, activation codes and grouping.  The first
+    // token's logits and the first batch of x rows are requested before any
+    // of them is used.
+    if (tid == 0) misc_l[3] = (int)(ld_agent(a.sync + kSyncEpoch / 4) + 1u);
+    const int nq = M * G;   // 16-lane rows of activation groups
+    const int qbase = wave * 4 + (lane >> 4);
+    uint4 xr[4];
+    auto x_load = [&](int base) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
-        m = row16_max(m);
-        const float sc = m / kE4M3Max;
-        *reinterpret_cast<uint2*>(xq_l + t * h + g * 128 + col * 8) = quant8(v, sc);
-        if (col == 0) xs_l[t * G + g] = sc;
+        for (int s4 = 0; s4 < 4; ++s4) {
+            const int task = base + 16 * s4;
+            if (task < nq) {
+                const int t = task / G, g = task - t * G;
+                xr[s4] = *reinterpret_cast<const uint4*>(a.x + (size_t)t * h + g * 128 + col * 8);
+            }
+        }
+    };
+    float lg[4];
+    auto l_load = [&](int t) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = lane + 64 * j;
+            lg[j] = (t < M && e < E) ? a.logits[(size_t)t * E + e] : 0.0f;
+        }
+    };
+    l_load(wave);
+    x_load(qbase);
+#pragma unroll 1
+    for (int t = wave; t < M; t += 4) {
+        if (t != wave) l_load(t);
+        route_fast(lg, E, k, ids_l + t * k, w_l + t * k, lane);
+    }
+#pragma unroll 1
+    for (int base = qbase; base < nq; base += 64) {
+        if (base != qbase) x_load(base);
+#pragma unroll 1
+        for (int s4 = 0; s4 < 4; ++s4) {
+            const int task = base + 16 * s4;
+            if (task < nq) {
+                const int t = task / G, g = task - t * G;
+                const uint4 u = s4 == 0 ? xr[0] : s4 == 1 ? xr[1] : s4 == 2 ? xr[2] : xr[3];
+                float v[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
+                              bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w)};
+                float m = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+                m = row16_max(m);
+                const float sc = m / kE4M3Max;
+                *reinterpret_cast<uint2*>(xq_l + t * h + g * 128 + col * 8) = quant8(v, sc);
+                if (col == 0) xs_l[t * G + g] = sc;
+            }
+        }
     }
     __syncthreads();
     if (wave == 0) {
-        // counts per expert (lane owns experts 4l..4l+3), then offsets and the
-        // ascending list of experts with routes
-        for (int e = lane; e < E; e += 64) base_l[e] = 0;
-        for (int p0 = 0; p0 < R; p0 += 64) {
-            const int p = p0 + lane;
-            const int e = p < R ? ids_l[p] : 0x1FF;
-            const uint64_t same = match_id(e);
-            if (p < R && (same >> lane) == 1ull) base_l[e] += __popcll(same);
-        }
-        int tot[4];
+        // counts and each route's rank inside its expert (ballot match per
+        // 64 routes), then offsets and the active list by DPP prefix sums,
+        // then the routes in (expert, route id) order
+        for (int e = lane; e < E; e += 64) cnt_l[e] = 0;
+        const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        int lr[4], ee[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) tot[j] = (4 * lane + j < E) ? base_l[4 * lane + j] : 0;
-        const int lsum = tot[0] + tot[1] + tot[2] + tot[3];
-        const int lact = (tot[0] > 0) + (tot[1] > 0) + (tot[2] > 0) + (tot[3] > 0);
-        const int incl = wave_incl_scan_i(lsum, lane);
-        const int iact = wave_incl_scan_i(lact, lane);
+        for (int b = 0; b < 4; ++b) {
+            lr[b] = 0;
+            ee[b] = 0x1FF;
+            if (64 * b < R) {
+                const int p = 64 * b + lane;
+                const int e = p < R ? ids_l[p] : 0x1FF;
+                const uint64_t same = match_id(e);
+                if (p < R) {
+                    lr[b] = cnt_l[e] + __popcll(same & below);
+                    ee[b] = e;
+                    if ((same >> lane) == 1ull) cnt_l[e] += __popcll(same);
+                }
+            }
+        }
+        int c[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) c[j] = (4 * lane + j < E) ? cnt_l[4 * lane + j] : 0;
+        const int lsum = c[0] + c[1] + c[2] + c[3];
+        const int lact = (c[0] > 0) + (c[1] > 0) + (c[2] > 0) + (c[3] > 0);
+        const int incl = wave_scan_incl(lsum);
+        const int iact = wave_scan_incl(lact);
         int run = incl - lsum, arun = iact - lact;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int e = 4 * lane + j;
             if (e < E) {
                 off_l[e] = run;
-                base_l[e] = run;
-                if (tot[j] > 0) act_l[arun] = e;
+                if (c[j] > 0) act_l[arun] = e;
             }
-            run += tot[j];
-            arun += (tot[j] > 0);
+            run += c[j];
+            arun += (c[j] > 0);
         }
         if (lane == 63) {
             off_l[E] = incl;
             misc_l[0] = iact;
         }
-        const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-        for (int p0 = 0; p0 < R; p0 += 64) {
-            const int p = p0 + lane;
-            const int e = p < R ? ids_l[p] : 0x1FF;
-            const uint64_t same = match_id(e);
-            int pos = 0;
-            if (p < R) pos = base_l[e] + __popcll(same & below);
-            if (p < R) {
-                srt_l[pos] = p;
-                if ((same >> lane) == 1ull) base_l[e] += __popcll(same);
-            }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int p = 64 * b + lane;
+            if (p < R) srt_l[off_l[ee[b]] + lr[b]] = p;
         }
     }
     __syncthreads();
     const int U = misc_l[0];
+    const uint32_t tag = (uint32_t)misc_l[3];
+    const int nA = U * IB * kQuarters;
+    const int NT = h / kDownRows;
+    const int nB = U * NT;
+
+    // ---- prefetch: the first gate/up task's first K batch and the first
+    // down task's weights, all in flight before anything is computed
+    v8i Aw[kMaxKB];
+    float Asc[kMaxKB];
+    v8i Bw[kFusedMaxIB];
+    float Bsc[kFusedMaxIB];
+    auto a_geom = [&](int task, int& u, int& e, int& row0) {
+        u = task / (IB * kQuarters);
+        const int rem = task - u * IB * kQuarters;
+        const int jg = rem / kQuarters, q = rem - jg * kQuarters;
+        e = act_l[u];
+        row0 = (wave >> 1) * i + jg * 128 + q * 32 + (wave & 1) * 16;
+    };
+    auto a_load = [&](int e, int row0, int kb0) {
+        const uint8_t* wrow = a.w13 + ((size_t)e * N13 + row0 + col) * h + kg * 32;
+        const float* ws = a.s13 + ((size_t)e * (N13 / 128) + row0 / 128) * KB;
+#pragma unroll
+        for (int u8 = 0; u8 < kMaxKB; ++u8) {
+            if (kb0 + u8 < KB) {
+                Aw[u8] = load32(wrow + (kb0 + u8) * 128);
+                Asc[u8] = ws[kb0 + u8];
+            }
+        }
+    };
+    auto b_load = [&](int task) {
+        const int u = task / NT, nt = task - u * NT;
+        const int e = act_l[u];
+        const int n0 = nt * kDownRows + wave * 16;
+        const uint8_t* wrow = a.w2 + ((size_t)e * h + n0 + col) * i + kg * 32;
+        const float* ws = a.s2 + ((size_t)e * (h / 128) + n0 / 128) * IB;
+#pragma unroll
+        for (int kb = 0; kb < kFusedMaxIB; ++kb) {
+            if (kb < IB) {
+                Bw[kb] = load32(wrow + kb * 128);
+                Bsc[kb] = ws[kb];
+            }
+        }
+    };
+    if ((int)blockIdx.x < nA) {
+        int u, e, row0;
+        a_geom(blockIdx.x, u, e, row0);
+        a_load(e, row0, 0);
+    }
+    if ((int)blockIdx.x < nB) b_load(blockIdx.x);
+
+    // ---- phase 1: gate/up quarters
+    for (int task = blockIdx.x; task < nA; task += gridDim.x) {
+        int u, e, row0;
+        a_geom(task, u, e, row0);
+        const int beg = off_l[e], cnt = off_l[e + 1] - beg;
+        const bool valid = col < cnt;
+        const int p = valid ? srt_l[beg + col] : 0;
+        const int t = p / k;
+        const uint8_t* xrow = xq_l + t * h + kg * 32;
+        const float* xsr = xs_l + t * G;
+        v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int kb0 = 0; kb0 < KB; kb0 += kMaxKB) {
+            if (kb0 > 0 || task != (int)blockIdx.x) a_load(e, row0, kb0);
+#pragma unroll
+            for (int u8 = 0; u8 < kMaxKB; ++u8) {
+                const int kb = kb0 + u8;
+                if (kb < KB) {
+                    const v8i B = valid ? load32(xrow + kb * 128) : zero8();
+                    const float sc = (valid ? xsr[kb] : 0.0f) * Asc[u8];
+                    const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+                    const v4f blk = mfma_16x16x128_e4m3(Aw[u8], B, z);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) acc[v] = fmaf(blk[v], sc, acc[v]);
+                }
+            }
+        }
+        if (valid) {
+            uint64_t* gp = a.g_ll + (size_t)p * N13 + row0 + kg * 4;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) st_agent64(gp + v, ll_pack(acc[v], tag));
+        }
+    }
+
+    // ---- phase 2: down tiles
+    for (int task = blockIdx.x; task < nB; task += gridDim.x) {
+        const int u = task / NT, nt = task - u * NT;
+        const int e = act_l[u];
+        const int beg = off_l[e], cnt = off_l[e + 1] - beg;
+        const int n0 = nt * kDownRows + wave * 16;
+        if (task != (int)blockIdx.x) b_load(task);
+#pragma unroll 1
+        for (int r2 = wave * 4 + (lane >> 4); r2 < cnt * IB; r2 += 16) {
+            const int jr = r2 / IB, b = r2 - jr * IB;
+            const uint64_t* gr = a.g_ll + (size_t)srt_l[beg + jr] * N13 + b * 128;
+            silu_quant_ll(gr, gr + i, col, tag, err, a2_l + jr * a2_stride + b * 128,
+                          a2s_l + jr * IB + b);
+        }
+        __syncthreads();
+        const bool valid = col < cnt;
+        const int p = valid ? srt_l[beg + col] : 0;
+        v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kb = 0; kb < kFusedMaxIB; ++kb) {
+            if (kb < IB) {
+                const v8i B = valid ? load32(a2_l + col * a2_stride + kb * 128 + kg * 32) : zero8();
+                const float sc = (valid ? a2s_l[col * IB + kb] : 0.0f) * Bsc[kb];
+                const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+                const v4f blk = mfma_16x16x128_e4m3(Bw[kb], B, z);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[v] = fmaf(blk[v], sc, acc[v]);
+            }
+        }
+        if (valid) {
+            uint64_t* yp = a.y_ll + (size_t)p * h + n0 + kg * 4;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) st_agent64(yp + v, ll_pack(acc[v], tag));
+        }
+        __syncthreads();
+    }
+
+    // ---- phase 3: combine the tiles of the tokens whose last-rank route this
+    // workgroup computed (after all of its own down tiles)
+    for (int task = blockIdx.x; task < nB; task += gridDim.x) {
+        const int u = task / NT, nt = task - u * NT;
+        const int e = act_l[u];
+        const int beg = off_l[e], cnt = off_l[e + 1] - beg;
+        for (int jr = 0; jr < cnt; ++jr) {
+            const int pr = srt_l[beg + jr];
+            if (pr % k != k - 1) continue;
+            const int t = pr / k;
+            if (tid < kDownRows) {
+#pragma clang fp contract(off)
+                // the k partials of column n, loaded together until all are
+                // from this forward, then summed in rank order
+                const int n = nt * kDownRows + tid;
+                const uint64_t* yc = a.y_ll + (size_t)t * k * h + n;
+                uint64_t w[16];
+                uint64_t t0 = 0;
+                for (int tries = 0;; ++tries) {
+                    bool ok = true;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        if (r < k) {
+                            w[r] = ld_agent64(yc + (size_t)r * h);
+                            ok = ok && ll_tag(w[r]) == tag;
+                        }
+                    }
+                    if (ok) break;
+                    if (tries == 0) t0 = wall_clock64();
+                    if (wall_clock64() - t0 > kWaitTicks) {
+                        atomicOr(err, 1u);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+                float accum = 0.0f;
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (r < k) accum = accum + w_l[t * k + r] * ll_value(w[r]);
+                __bf16 bv = (__bf16)accum;
+                a.out[(size_t)t * h + n] = __builtin_bit_cast(uint16_t, bv);
+            }
+        }
+    }
 
     // Workgroup 0 publishes the batch's routing and quantisation (inspection).
     if (blockIdx.x == 0) {
@@ -260,167 +471,27 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
         for (int j = tid; j < M * G; j += 256) a.xs[j] = xs_l[j];
     }
 
-    // ---- phase 1: gate/up quarters
-    const int nA = U * IB * kQuarters;
-    for (int task = blockIdx.x; task < nA; task += gridDim.x) {
-        const int u = task / (IB * kQuarters);
-        const int rem = task - u * IB * kQuarters;
-        const int jg = rem / kQuarters, q = rem - jg * kQuarters;
-        const int e = act_l[u];
-        const int beg = off_l[e], cnt = off_l[e + 1] - beg;
-        const int row0 = (wave >> 1) * i + jg * 128 + q * 32 + (wave & 1) * 16;
-        const uint8_t* wrow = a.w13 + ((size_t)e * N13 + row0 + col) * h + kg * 32;
-        const float* ws = a.s13 + ((size_t)e * (N13 / 128) + row0 / 128) * KB;
-        const bool valid = col < cnt;
-        const int p = valid ? srt_l[beg + col] : 0;
-        const int t = p / k;
-        const uint8_t* xrow = xq_l + t * h + kg * 32;
-        const float* xsr = xs_l + t * G;
-        v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int kb0 = 0; kb0 < KB; kb0 += 8) {
-            v8i A[8];
-            float ws8[8];
-#pragma unroll
-            for (int u8 = 0; u8 < 8; ++u8) {
-                if (kb0 + u8 < KB) {
-                    A[u8] = load32(wrow + (kb0 + u8) * 128);
-                    ws8[u8] = ws[kb0 + u8];
-                }
-            }
-#pragma unroll
-            for (int u8 = 0; u8 < 8; ++u8) {
-                const int kb = kb0 + u8;
-                if (kb < KB) {
-                    const v8i B = valid ? load32(xrow + kb * 128) : zero8();
-                    const float sc = (valid ? xsr[kb] : 0.0f) * ws8[u8];
-                    const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
-                    const v4f blk = mfma_16x16x128_e4m3(A[u8], B, z);
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) acc[v] = fmaf(blk[v], sc, acc[v]);
-                }
-            }
-        }
-        if (valid)
-            *reinterpret_cast<float4*>(a.g + (size_t)p * N13 + row0 + kg * 4) =
-                make_float4(acc[0], acc[1], acc[2], acc[3]);
-        __threadfence();
-        __syncthreads();
-        if (tid == 0) {
-            const uint32_t old = atomicAdd(a.gate_tix + u * IB + jg, 1u);
-            misc_l[1] = (old == kQuarters - 1);
-        }
-        __syncthreads();
-        if (misc_l[1]) {
-            __threadfence();
-            for (int jr = wave * 4 + (lane >> 4); jr < cnt; jr += 16) {
-                const int pr = srt_l[beg + jr];
-                const float* gr = a.g + (size_t)pr * N13 + jg * 128;
-                silu_quant_group(gr, gr + i, col, a.a2 + (size_t)pr * i + jg * 128,
-                                 a.a2s + (size_t)pr * IB + jg);
-            }
-            __threadfence();
-            __syncthreads();
-            if (tid == 0) {
-                __hip_atomic_store(a.gate_tix + u * IB + jg, 0u, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-                atomicAdd(a.done + u, 1u);
-            }
-        }
-        __syncthreads();
-    }
-
-    // ---- phase 2: down tiles, then the fixed-order combine
-    const int NT = h / kDownRows;
-    const int nB = U * NT;
-    for (int task = blockIdx.x; task < nB; task += gridDim.x) {
-        const int u = task / NT, nt = task - u * NT;
-        const int e = act_l[u];
-        const int beg = off_l[e], cnt = off_l[e + 1] - beg;
-        const int n0 = nt * kDownRows + wave * 16;
-        const uint8_t* wrow = a.w2 + ((size_t)e * h + n0 + col) * i + kg * 32;
-        const float* ws = a.s2 + ((size_t)e * (h / 128) + n0 / 128) * IB;
-        v8i W[kFusedMaxIB];
-        float ws8[kFusedMaxIB];
-#pragma unroll
-        for (int kb = 0; kb < kFusedMaxIB; ++kb) {
-            if (kb < IB) {
-                W[kb] = load32(wrow + kb * 128);
-                ws8[kb] = ws[kb];
-            }
-        }
-        wait_count(a.done + u, (uint32_t)IB, a.err);
-        for (int idx = tid; idx < cnt * (i / 16); idx += 256) {
-            const int jr = idx / (i / 16), c16 = idx - jr * (i / 16);
-            const int pr = srt_l[beg + jr];
-            *reinterpret_cast<uint4*>(a2_l + jr * a2_stride + c16 * 16) =
-                *reinterpret_cast<const uint4*>(a.a2 + (size_t)pr * i + c16 * 16);
-        }
-        for (int idx = tid; idx < cnt * IB; idx += 256) {
-            const int jr = idx / IB, b = idx - jr * IB;
-            a2s_l[jr * IB + b] = a.a2s[(size_t)srt_l[beg + jr] * IB + b];
-        }
-        __syncthreads();
-        const bool valid = col < cnt;
-        const int p = valid ? srt_l[beg + col] : 0;
-        v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int kb = 0; kb < kFusedMaxIB; ++kb) {
-            if (kb < IB) {
-                const v8i B = valid ? load32(a2_l + col * a2_stride + kb * 128 + kg * 32) : zero8();
-                const float sc = (valid ? a2s_l[col * IB + kb] : 0.0f) * ws8[kb];
-                const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
-                const v4f blk = mfma_16x16x128_e4m3(W[kb], B, z);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) acc[v] = fmaf(blk[v], sc, acc[v]);
-            }
-        }
-        if (valid)
-            *reinterpret_cast<float4*>(a.y + (size_t)p * h + n0 + kg * 4) =
-                make_float4(acc[0], acc[1], acc[2], acc[3]);
-        __threadfence();
-        __syncthreads();
-        if (tid < cnt) {
-            const int pr = srt_l[beg + tid];
-            const int t = pr / k;
-            const uint32_t old = atomicAdd(a.comb_tix + t * NT + nt, 1u);
-            misc_l[2 + tid] = (old == (uint32_t)(k - 1)) ? t : -1;
-        }
-        __syncthreads();
-        bool any = false;
-        for (int jr = 0; jr < cnt; ++jr) any |= misc_l[2 + jr] >= 0;
-        if (any) {
-            __threadfence();
-            for (int jr = 0; jr < cnt; ++jr) {
-                const int t = misc_l[2 + jr];
-                if (t < 0) continue;
-                if (tid < kDownRows) {
-#pragma clang fp contract(off)
-                    const int n = nt * kDownRows + tid;
-                    float accum = 0.0f;
-                    for (int r = 0; r < k; ++r)
-                        accum = accum + w_l[t * k + r] * a.y[((size_t)t * k + r) * h + n];
-                    __bf16 b = (__bf16)accum;
-                    a.out[(size_t)t * h + n] = __builtin_bit_cast(uint16_t, b);
-                }
-                if (tid == 0)
-                    __hip_atomic_store(a.comb_tix + t * NT + nt, 0u, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
-        __syncthreads();
-    }
-
-    // ---- exit: the last workgroup resets the done counters
+    // ---- exit: the last workgroup advances the forward count
     __syncthreads();
     if (tid == 0) {
-        __threadfence();
-        const uint32_t old = atomicAdd(a.exit_cnt, 1u);
-        if (old == gridDim.x - 1) {
-            for (int u = 0; u < a.umax; ++u)
-                __hip_atomic_store(a.done + u, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(a.exit_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __threadfence();
+        const uint32_t old = atomicAdd(a.sync + kSyncExit / 4, 1u);
+        misc_l[4] = (old == gridDim.x - 1);
+    }
+    __syncthreads();
+    if (misc_l[4]) {
+        const uint32_t epoch = tag - 1u;
+        if (epoch + 2u == 0u) {
+            // the next tag would be 0, the value of a cleared word: clear the
+            // exchange region and start counting again
+            uint64_t* ll = a.g_ll;
+            for (size_t j = tid; j < kLLBytes / 8; j += 256) st_agent64(ll + j, 0ull);
+            wait_vmem();
+            __syncthreads();
+            if (tid == 0) st_agent(a.sync + kSyncEpoch / 4, 0u);
+        } else if (tid == 0) {
+            st_agent(a.sync + kSyncEpoch / 4, epoch + 1u);
         }
+        if (tid == 0) st_agent(a.sync + kSyncExit / 4, 0u);
     }
 }
 
@@ -431,14 +502,15 @@ size_t fused_lds_bytes(int M, int h, int i, int E, int k) {
     b += r4(M * G) * 4;
     b += r4(R) * 4 * 2;
     b += r4(E + 1) * 4 + r4(E) * 4 + r4(R) * 4 + r4(E) * 4 + 32 * 4;
-    b += (size_t)16 * (i + 16) + (size_t)16 * IB * 4;
+    b += (size_t)16 * (i + 16) + ((size_t)16 * kFusedMaxIB + 64) * 4;   // a2, a2 scales, router scratch
     return (b + 15) & ~(size_t)15;
 }
 
 bool fused_supported(int M, int h, int i, int E, int k) {
+    const size_t R = (size_t)M * k, words = kLLBytes / 16;   // each exchange buffer: 4 MiB
     return M >= 1 && M <= kFusedMaxM && k <= 16 && E <= 256 && h % 128 == 0 && i % 128 == 0 &&
            i / 128 <= kFusedMaxIB && (size_t)M * h <= 32768 && h % kDownRows == 0 &&
-           (size_t)M * (h / kDownRows) <= 2048 && fused_lds_bytes(M, h, i, E, k) <= 64 * 1024;
+           R * 2 * i <= words && R * h <= words && fused_lds_bytes(M, h, i, E, k) <= 64 * 1024;
 }
 
 // Workgroups that can be resident at once, per device (queried once).
@@ -468,7 +540,8 @@ hipError_t launch_fused_decode(const FusedArgs& args, hipStream_t stream) {
     const int cap = resident_capacity(lds);
     if (cap <= 0) return hipErrorInvalidConfiguration;
     const int IB = args.i / 128;
-    const int want = std::max(args.umax * IB * kQuarters, args.umax * (args.h / kDownRows));
+    const int umax = std::min(args.E, args.M * args.k);
+    const int want = std::max(umax * IB * kQuarters, umax * (args.h / kDownRows));
     const int grid = std::max(1, std::min(cap, want));
     hipLaunchKernelGGL(fused_decode_kernel, dim3(grid), dim3(256), lds, stream, args);
     return hipGetLastError();

@@ -50,7 +50,7 @@ int choose_path(int M, int h, int i, int E, int k) {
 
 void make_layout(int M, int h, int i, int E, int k, Layout* L) {
     const size_t R = (size_t)M * k;
-    size_t cur = moe::kSyncBytes;   // synchronisation words first
+    size_t cur = moe::kWorkspaceHead;   // synchronisation words and exchange region first
     auto take = [&](size_t bytes) {
         const size_t o = cur;
         cur = align_up(cur + bytes);
@@ -69,15 +69,15 @@ void make_layout(int M, int h, int i, int E, int k, Layout* L) {
     p.num_active = take(4);
     L->hist = take((size_t)moe::group_chunks((int)R) * E * 4);
     p.path = choose_path(M, h, i, E, k);
-    p.gate_up = take(R * 2 * i * 4);
+    p.act2 = (size_t)-1;        // requantised activations stay on chip on both paths
+    p.act2_scale = (size_t)-1;
     if (p.path == MOE_FP8_PATH_FUSED_DECODE) {
-        p.act2 = take(R * i);
-        p.act2_scale = take(R * (i / 128) * 4);
+        p.gate_up = (size_t)-1;   // exchanged as tagged words in the workspace head
+        p.partial = (size_t)-1;
     } else {
-        p.act2 = (size_t)-1;
-        p.act2_scale = (size_t)-1;
+        p.gate_up = take(R * 2 * i * 4);
+        p.partial = take(R * h * 4);
     }
-    p.partial = take(R * h * 4);
     p.total = cur;
 }
 
@@ -139,8 +139,8 @@ int run_forward(const void* x, const float* router_logits, const void* w13, cons
     int32_t* active = at<int32_t>(workspace, p.active);
     int32_t* num_active = at<int32_t>(workspace, p.num_active);
     int32_t* hist = at<int32_t>(workspace, L.hist);
-    float* g = at<float>(workspace, p.gate_up);
-    float* y = at<float>(workspace, p.partial);
+    float* g = p.path == MOE_FP8_PATH_STREAM ? at<float>(workspace, p.gate_up) : nullptr;
+    float* y = p.path == MOE_FP8_PATH_STREAM ? at<float>(workspace, p.partial) : nullptr;
     EventHook hook{events, n_events, 0, stream};
     uint32_t* sync = at<uint32_t>(workspace, 0);
 
@@ -165,7 +165,6 @@ int run_forward(const void* x, const float* router_logits, const void* w13, cons
         fa.i = i;
         fa.E = E;
         fa.k = k;
-        fa.umax = E < R ? E : R;
         fa.ids = ids;
         fa.tw = tw;
         fa.xq = xq;
@@ -175,15 +174,9 @@ int run_forward(const void* x, const float* router_logits, const void* w13, cons
         fa.sorted = sorted;
         fa.active = active;
         fa.num_active = num_active;
-        fa.g = g;
-        fa.a2 = at<uint8_t>(workspace, p.act2);
-        fa.a2s = at<float>(workspace, p.act2_scale);
-        fa.y = y;
-        fa.gate_tix = sync + moe::kSyncGateTix / 4;
-        fa.done = sync + moe::kSyncDone / 4;
-        fa.comb_tix = sync + moe::kSyncCombTix / 4;
-        fa.exit_cnt = sync + moe::kSyncExit / 4;
-        fa.err = sync + moe::kSyncErr / 4;
+        fa.g_ll = at<uint64_t>(workspace, moe::kLLOffset);
+        fa.y_ll = at<uint64_t>(workspace, moe::kLLOffset + moe::kLLBytes / 2);
+        fa.sync = sync;
         MOE_STEP(moe::launch_fused_decode(fa, stream));
         return hook.mark() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
     }
@@ -245,8 +238,8 @@ int moe_fp8_bind_workspace(void* dev_ptr, size_t bytes) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
     if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
-    if (dev_ptr && bytes < moe::kSyncBytes) return MOE_ERR_WORKSPACE;
-    if (dev_ptr && hipMemset(dev_ptr, 0, moe::kSyncBytes) != hipSuccess) return MOE_ERR_HIP;
+    if (dev_ptr && bytes < moe::kWorkspaceHead) return MOE_ERR_WORKSPACE;
+    if (dev_ptr && hipMemset(dev_ptr, 0, moe::kWorkspaceHead) != hipSuccess) return MOE_ERR_HIP;
     std::lock_guard<std::mutex> lock(g_bind_mu);
     g_bind[dev].ptr = dev_ptr;
     g_bind[dev].bytes = dev_ptr ? bytes : 0;
@@ -286,11 +279,13 @@ const char* moe_fp8_forward_kernel_name(int M, int h, int i, int E, int k, int j
     return stage_name(choose_path(M, h, i, E, k), j);
 }
 
+size_t moe_fp8_workspace_head_bytes(void) { return moe::kWorkspaceHead; }
+
 int moe_fp8_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (!workspace || ((uintptr_t)workspace % kAlign) != 0) return MOE_ERR_INVALID;
-    if (workspace_bytes < moe::kSyncBytes) return MOE_ERR_WORKSPACE;
-    return hip_status(moe::launch_zero_words(static_cast<uint32_t*>(workspace), moe::kSyncBytes / 4,
-                                             stream));
+    if (workspace_bytes < moe::kWorkspaceHead) return MOE_ERR_WORKSPACE;
+    return hip_status(moe::launch_zero_words(static_cast<uint32_t*>(workspace),
+                                             moe::kWorkspaceHead / 4, stream));
 }
 
 int moe_fp8_forward(const void* x, const float* router_logits, const void* w13, const float* s13,

@@ -76,13 +76,15 @@ const char* moe_fp8_status_string(int status);
  * or an unsupported shape). */
 size_t moe_fp8_workspace_bytes(int M, int h, int i, int E, int k);
 
-/* Workspaces.  The first 32 KiB of every workspace hold synchronisation
- * counters that must be zero before the workspace's first forward; every
- * forward leaves them zero again.  moe_fp8_bind_workspace zeroes them;
- * a caller-managed workspace is zeroed once with moe_fp8_workspace_init (or
- * allocated zero-filled).  The word at moe_fp8_ws_layout.sync_error stays 0
- * unless a wait between workgroups timed out (a broken device or a corrupted
- * workspace), in which case it is set and that forward's output is invalid. */
+/* Workspaces.  The first 8 MiB + 32 KiB of every workspace (the "head")
+ * hold synchronisation words and the exchange buffers of the one-kernel
+ * small-batch path; the head must be zero before the workspace's first
+ * forward and is then maintained by the forwards themselves.
+ * moe_fp8_bind_workspace zeroes it; a caller-managed workspace is zeroed once
+ * with moe_fp8_workspace_init (or allocated zero-filled).  The word at
+ * moe_fp8_ws_layout.sync_error stays 0 unless a wait between workgroups
+ * timed out (a broken device or a corrupted workspace), in which case it is
+ * set and that forward's output is invalid. */
 
 /* Bind `bytes` of device memory at `dev_ptr` (256-byte aligned) as the
  * workspace moe_fp8_forward uses on the CURRENT device, and zero its
@@ -90,12 +92,15 @@ size_t moe_fp8_workspace_bytes(int M, int h, int i, int E, int k);
  * the memory: the caller owns it and must keep it alive while bound.
  * Passing NULL unbinds.  Not on the launch path; call it once before
  * capturing graphs.  Returns MOE_ERR_INVALID on misalignment and
- * MOE_ERR_WORKSPACE below 32 KiB. */
+ * MOE_ERR_WORKSPACE when it is smaller than the head. */
 int moe_fp8_bind_workspace(void* dev_ptr, size_t bytes);
 
-/* Zero the synchronisation words of a workspace (a kernel on `stream`, so it
- * may be captured).  Needed once before the first forward on a workspace that
- * was not allocated zero-filled. */
+/* Bytes of the workspace head (every workspace is at least this large). */
+size_t moe_fp8_workspace_head_bytes(void);
+
+/* Zero the head of a workspace (a kernel on `stream`, so it may be
+ * captured).  Needed once before the first forward on a workspace that was
+ * not allocated zero-filled. */
 int moe_fp8_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* The whole layer with the workspace bound to the current device.

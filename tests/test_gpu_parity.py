@@ -172,9 +172,14 @@ def _run(moe_mod, L: Layer):
 
 
 def _check_sync_clean(ws):
-    """Every forward leaves the synchronisation words zero and no wait timed out."""
+    """Between forwards the exit counter is zero, no wait timed out, and only
+    the forward-count word is set."""
     words = ws[:32768].view(torch.int32).cpu().numpy()
-    assert not words.any(), f"sync words not reset: {np.nonzero(words)[0][:10]}"
+    assert words[256 // 4] == 0, "exit counter not reset"
+    assert words[512 // 4] == 0, "a wait between workgroups timed out"
+    rest = words.copy()
+    rest[0] = 0
+    assert not rest.any(), f"unexpected sync words: {np.nonzero(rest)[0][:10]}"
 
 
 def _check_intermediates(moe_mod, L: Layer, ws, inter, tokens=None):
@@ -333,7 +338,7 @@ def test_fused_path_m_sweep_and_shared_workspace(dev, moe_mod):
     big = Layer(cfg16, 777, dev)
     assert moe_mod.workspace_layout(16, h, i, E, k).path == moe_mod.PATH_FUSED_DECODE
     ws = moe_mod.alloc_workspace(16, h, i, E, k, device=dev)
-    for M in (1, 2, 3, 5, 8, 13, 16, 1):
+    for n, M in enumerate((1, 2, 3, 5, 8, 13, 16, 1)):
         log(f"fused sweep M={M}")
         cfg = synth.LayerConfig(f"m{M}", M, h, i, E, k, "normal", "sweep")
         L = Layer(cfg, 777, dev, x=big.x[:M], logits=big.logits[:M],
@@ -341,6 +346,7 @@ def test_fused_path_m_sweep_and_shared_workspace(dev, moe_mod):
         out = moe_mod.moe_fp8_forward_ws(L.tx, L.tl, L.t13, L.ts13, L.t2, L.ts2, k, ws)
         torch.cuda.synchronize()
         _check_sync_clean(ws)
+        assert int(ws[:4].view(torch.int32).item()) == n + 1, "one forward = one tag"
         check_output(to_host_bits(out), L.oracle())
 
 
