@@ -47,6 +47,7 @@ class WsLayout(ctypes.Structure):
 
 
 PATH_STREAM = 0
+PATH_PREFILL = 1
 PATH_FUSED_DECODE = 2
 
 

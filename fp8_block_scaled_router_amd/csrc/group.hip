@@ -9,8 +9,10 @@
 // routes in route order, 64 at a time: a lane's rank among equal experts in
 // its batch comes from a ballot match over the 9 bits of the expert id, so
 // the sorted order is route id ascending inside each expert by construction.
-// Chunk 0 also writes counts, offsets and the ascending list of experts that
-// received routes.
+// Chunk 0 also writes counts, offsets, the ascending list of experts that
+// received routes and, when asked, each expert's first M-tile index for a
+// grouped GEMM with tile_m routes per tile (exclusive scan of
+// ceil(count / tile_m)).
 #include "device.h"
 #include "launch.h"
 
@@ -48,7 +50,8 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 __global__ __launch_bounds__(64) void group_scatter_kernel(
     const int32_t* __restrict__ ids, int R, int E, int nchunks, const int32_t* __restrict__ hist,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted,
-    int32_t* __restrict__ active, int32_t* __restrict__ num_active) {
+    int32_t* __restrict__ active, int32_t* __restrict__ num_active, int tile_m,
+    int32_t* __restrict__ mtile_off) {
     __shared__ int base[256];
     const int chunk = blockIdx.x;
     const int lane = threadIdx.x;
@@ -70,9 +73,22 @@ __global__ __launch_bounds__(64) void group_scatter_kernel(
     }
     const int lsum = tot[0] + tot[1] + tot[2] + tot[3];
     const int lact = (tot[0] > 0) + (tot[1] > 0) + (tot[2] > 0) + (tot[3] > 0);
+    int ltiles = 0;
+    if (tile_m > 0)
+        for (int j = 0; j < 4; ++j) ltiles += (tot[j] + tile_m - 1) / tile_m;
     const int incl = wave_incl_scan(lsum, lane);
     const int iact = wave_incl_scan(lact, lane);
-    int run = incl - lsum, arun = iact - lact;
+    const int itil = wave_incl_scan(ltiles, lane);
+    int run = incl - lsum, arun = iact - lact, trun = itil - ltiles;
+    if (chunk == 0 && tile_m > 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = 4 * lane + j;
+            if (e < E) mtile_off[e] = trun;
+            trun += (tot[j] + tile_m - 1) / tile_m;
+        }
+        if (lane == 63) mtile_off[E] = itil;
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int e = 4 * lane + j;
@@ -123,13 +139,13 @@ __global__ __launch_bounds__(64) void group_scatter_kernel(
 
 hipError_t launch_group(const int32_t* ids, int R, int E, int32_t* hist, int32_t* counts,
                         int32_t* offsets, int32_t* sorted, int32_t* active, int32_t* num_active,
-                        hipStream_t stream) {
+                        hipStream_t stream, int tile_m, int32_t* mtile_off) {
     const int nchunks = group_chunks(R);
     hipLaunchKernelGGL(group_hist_kernel, dim3(nchunks), dim3(256), 0, stream, ids, R, E, hist);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(group_scatter_kernel, dim3(nchunks), dim3(64), 0, stream, ids, R, E, nchunks,
-                       hist, counts, offsets, sorted, active, num_active);
+                       hist, counts, offsets, sorted, active, num_active, tile_m, mtile_off);
     return hipGetLastError();
 }
 

@@ -19,7 +19,7 @@ hipError_t launch_route_quant(const float* logits, const uint16_t* x, int M, int
 int group_chunks(int R);
 hipError_t launch_group(const int32_t* ids, int R, int E, int32_t* hist, int32_t* counts,
                         int32_t* offsets, int32_t* sorted, int32_t* active, int32_t* num_active,
-                        hipStream_t stream);
+                        hipStream_t stream, int tile_m = 0, int32_t* mtile_off = nullptr);
 
 // Weight-streaming grouped GEMMs (few tokens per expert).
 struct StreamArgs {
@@ -34,6 +34,26 @@ hipError_t launch_stream_gate_up(const StreamArgs& a, const uint8_t* xq, const f
                                  const uint8_t* w13, const float* s13, float* g, hipStream_t stream);
 hipError_t launch_stream_down(const StreamArgs& a, const float* g, const uint8_t* w2, const float* s2,
                               float* y, hipStream_t stream);
+
+// Tiled grouped GEMMs for many tokens per expert.
+struct PrefillArgs {
+    const uint8_t* xq;
+    const float* xs;
+    const uint8_t* w13;
+    const float* s13;
+    const uint8_t* w2;
+    const float* s2;
+    const int32_t* offsets;
+    const int32_t* sorted;
+    const int32_t* mtile_off;   // [E + 1] first M-tile of each expert
+    uint8_t* a2;                // [R][i]   requantised activations, sorted-route order
+    float* a2s;                 // [R][i/128]
+    float* y;                   // [R][h]   fp32 partials by route id
+    int h, i, E, k;
+};
+int prefill_tile_m();
+bool prefill_supported(int h, int i);
+hipError_t launch_prefill(const PrefillArgs& a, int R, hipStream_t stream);
 
 // Fixed-order combine of the k route partials of each token into bf16.
 hipError_t launch_combine(const float* y, const float* tw, int M, int k, int h, uint16_t* out,

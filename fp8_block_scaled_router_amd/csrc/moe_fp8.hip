@@ -41,11 +41,14 @@ int check_shape(int M, int h, int i, int E, int k) {
 
 struct Layout {
     moe_fp8_ws_layout pub;
-    size_t hist;   // grouping scratch: group_chunks(R) * E ints
+    size_t hist;        // grouping scratch: group_chunks(R) * E ints
+    size_t mtile_off;   // prefill path: [E + 1] ints
 };
 
 int choose_path(int M, int h, int i, int E, int k) {
-    return moe::fused_supported(M, h, i, E, k) ? MOE_FP8_PATH_FUSED_DECODE : MOE_FP8_PATH_STREAM;
+    if (moe::fused_supported(M, h, i, E, k)) return MOE_FP8_PATH_FUSED_DECODE;
+    if ((int64_t)M * k >= (int64_t)32 * E && moe::prefill_supported(h, i)) return MOE_FP8_PATH_PREFILL;
+    return MOE_FP8_PATH_STREAM;
 }
 
 void make_layout(int M, int h, int i, int E, int k, Layout* L) {
@@ -69,15 +72,19 @@ void make_layout(int M, int h, int i, int E, int k, Layout* L) {
     p.num_active = take(4);
     L->hist = take((size_t)moe::group_chunks((int)R) * E * 4);
     p.path = choose_path(M, h, i, E, k);
-    p.act2 = (size_t)-1;        // requantised activations stay on chip on both paths
+    L->mtile_off = take((size_t)(E + 1) * 4);
+    p.gate_up = (size_t)-1;
+    p.act2 = (size_t)-1;
     p.act2_scale = (size_t)-1;
-    if (p.path == MOE_FP8_PATH_FUSED_DECODE) {
-        p.gate_up = (size_t)-1;   // exchanged as tagged words in the workspace head
-        p.partial = (size_t)-1;
-    } else {
+    p.partial = (size_t)-1;
+    if (p.path == MOE_FP8_PATH_STREAM) {
         p.gate_up = take(R * 2 * i * 4);
         p.partial = take(R * h * 4);
-    }
+    } else if (p.path == MOE_FP8_PATH_PREFILL) {
+        p.act2 = take(R * i);
+        p.act2_scale = take(R * (i / 128) * 4);
+        p.partial = take(R * h * 4);
+    }   // the fused path exchanges its intermediates as tagged words in the head
     p.total = cur;
 }
 
@@ -93,10 +100,17 @@ const char* const kStreamStages[] = {"route_quant_kernel", "group_hist+group_sca
                                      "stream_gate_up_kernel", "stream_down_kernel",
                                      "combine_kernel"};
 const char* const kFusedStages[] = {"fused_decode_kernel"};
+const char* const kPrefillStages[] = {"route_quant_kernel", "group_hist+group_scatter",
+                                      "prefill_gate_up_kernel+prefill_down_kernel",
+                                      "combine_kernel"};
 
-int stage_count(int path) { return path == MOE_FP8_PATH_FUSED_DECODE ? 1 : 5; }
+int stage_count(int path) {
+    return path == MOE_FP8_PATH_FUSED_DECODE ? 1 : path == MOE_FP8_PATH_PREFILL ? 4 : 5;
+}
 const char* stage_name(int path, int j) {
-    return path == MOE_FP8_PATH_FUSED_DECODE ? kFusedStages[j] : kStreamStages[j];
+    if (path == MOE_FP8_PATH_FUSED_DECODE) return kFusedStages[j];
+    if (path == MOE_FP8_PATH_PREFILL) return kPrefillStages[j];
+    return kStreamStages[j];
 }
 
 // Records events[j] (when given) before stage j, and events[n] after the last.
@@ -140,7 +154,8 @@ int run_forward(const void* x, const float* router_logits, const void* w13, cons
     int32_t* num_active = at<int32_t>(workspace, p.num_active);
     int32_t* hist = at<int32_t>(workspace, L.hist);
     float* g = p.path == MOE_FP8_PATH_STREAM ? at<float>(workspace, p.gate_up) : nullptr;
-    float* y = p.path == MOE_FP8_PATH_STREAM ? at<float>(workspace, p.partial) : nullptr;
+    float* y = p.path != MOE_FP8_PATH_FUSED_DECODE ? at<float>(workspace, p.partial) : nullptr;
+    int32_t* mtile_off = at<int32_t>(workspace, L.mtile_off);
     EventHook hook{events, n_events, 0, stream};
     uint32_t* sync = at<uint32_t>(workspace, 0);
 
@@ -182,6 +197,30 @@ int run_forward(const void* x, const float* router_logits, const void* w13, cons
     }
     MOE_STEP(moe::launch_route_quant(router_logits, static_cast<const uint16_t*>(x), M, E, k, h,
                                      ids, tw, xq, xs, moe::kRoute | moe::kQuant, stream));
+    if (p.path == MOE_FP8_PATH_PREFILL) {
+        MOE_STEP(moe::launch_group(ids, R, E, hist, counts, offsets, sorted, active, num_active,
+                                   stream, moe::prefill_tile_m(), mtile_off));
+        moe::PrefillArgs pa;
+        pa.xq = xq;
+        pa.xs = xs;
+        pa.w13 = static_cast<const uint8_t*>(w13);
+        pa.s13 = s13;
+        pa.w2 = static_cast<const uint8_t*>(w2);
+        pa.s2 = s2;
+        pa.offsets = offsets;
+        pa.sorted = sorted;
+        pa.mtile_off = mtile_off;
+        pa.a2 = at<uint8_t>(workspace, p.act2);
+        pa.a2s = at<float>(workspace, p.act2_scale);
+        pa.y = y;
+        pa.h = h;
+        pa.i = i;
+        pa.E = E;
+        pa.k = k;
+        MOE_STEP(moe::launch_prefill(pa, R, stream));
+        MOE_STEP(moe::launch_combine(y, tw, M, k, h, static_cast<uint16_t*>(out), stream));
+        return hook.mark() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    }
     MOE_STEP(moe::launch_group(ids, R, E, hist, counts, offsets, sorted, active, num_active,
                                stream));
     moe::StreamArgs sa;

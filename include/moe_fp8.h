@@ -58,9 +58,12 @@ enum {
 };
 
 /* Forward paths (chosen from the sizes alone, see moe_fp8_workspace_layout):
- * small batches run the whole layer in one persistent kernel; larger ones
- * run router+quant, grouping, gate/up, down and combine kernels. */
+ * small batches (M <= 16) run the whole layer in one persistent kernel;
+ * batches with few routes per expert run weight-streaming GEMMs; batches
+ * with many routes per expert (M*k >= 32*E) run tiled MFMA grouped GEMMs
+ * with the SiLU requantisation fused into the gate/up epilogue. */
 #define MOE_FP8_PATH_STREAM 0
+#define MOE_FP8_PATH_PREFILL 1
 #define MOE_FP8_PATH_FUSED_DECODE 2
 
 /* Shape limits of this build. */
@@ -163,8 +166,8 @@ typedef struct {
     size_t active;      /* int32 [E]    experts with a route, ascending */
     size_t num_active;  /* int32 [1]                                    */
     size_t gate_up;     /* fp32  [M*k, 2i]  by route id                 */
-    size_t act2;        /* e4m3  [M*k, i]   by route id                 */
-    size_t act2_scale;  /* fp32  [M*k, i/128]                           */
+    size_t act2;        /* e4m3  [M*k, i]   in sorted-route order       */
+    size_t act2_scale;  /* fp32  [M*k, i/128] in sorted-route order     */
     size_t partial;     /* fp32  [M*k, h]   by route id                 */
     size_t sync_error;  /* uint32 error word (0 = no wait timed out)    */
     size_t total;       /* bytes                                        */

@@ -38,8 +38,93 @@ def bf16_ulp(v: np.ndarray) -> np.ndarray:
     return 2.0 ** (np.maximum(e, -126) - 7)
 
 
-def check_output(got_bits: np.ndarray, ref_bits: np.ndarray, rel=REL_TOL, cos_min=COS_MIN):
-    """Returns (max_abs_err, max_ref, min_cos); raises AssertionError on failure."""
+# The gfx950 FP8 MFMA sums each 128-product block with a precision of about
+# 2^-17 of the block's sum of |products| (measured: up to 7e-6; pinned by
+# test_mfma_block_sum_accuracy), against 2^-24 for the oracle's fp32 sum.  A
+# GPU gate/up value therefore lies within MFMA_REL * sum|terms| of the exact
+# value, which is what the flagging below propagates.
+MFMA_REL = 2e-5
+
+
+def _T64():
+    return torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+
+
+def _e4m3_codes(v: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(np.clip(v, -448.0, 448.0), dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def gate_up_terms(layer, inter) -> np.ndarray:
+    """sum over k of |x_k * w_nk| * |scales| for every gate/up value [R, 2i]
+    (float64, from the same codes the kernels read)."""
+    T = _T64()
+    ids, xq, xs = inter["ids"], inter["xq"], inter["xs"].astype(np.float64)
+    M, k = ids.shape
+    I2, h = layer.q13.shape[1], layer.q13.shape[2]
+    KB = h // 128
+    mag = np.zeros((M * k, I2))
+    for p in range(M * k):
+        t, e = p // k, ids.ravel()[p]
+        W = np.abs(T[layer.q13[e]]).reshape(I2, KB, 128)
+        a = np.abs(T[xq[t]]).reshape(KB, 128)
+        blk = np.einsum("nbk,bk->nb", W, a)
+        sc = np.repeat(np.abs(layer.s13[e].astype(np.float64)), 128, axis=0) * xs[t][None, :]
+        mag[p] = (blk * sc).sum(1)
+    return mag
+
+
+def flagged_codes(layer, inter, rel=MFMA_REL):
+    """(lo, hi, s) for every requantised value [R, i]: the E4M3 codes at the two
+    ends of the interval the quotient v / s can reach when each gate/up value
+    is off by at most rel * sum|terms| (propagated through SiLU(gate) * up and
+    through the group's scale amax / 448).  lo == hi where the decision is
+    clear of every rounding boundary; elsewhere either code is a correct
+    result of the method."""
+    g = inter["g"].astype(np.float64)
+    i = g.shape[1] // 2
+    dg = rel * gate_up_terms(layer, inter)
+    a, u = g[:, :i], g[:, i:]
+    da, du = dg[:, :i], dg[:, i:]
+    sig = 1.0 / (1.0 + np.exp(-a))
+    silu = a * sig
+    dsilu = sig * (1.0 + a * (1.0 - sig))
+    v = silu * u
+    dv = 1.1 * (np.abs(dsilu) * da * (np.abs(u) + du) + np.abs(silu) * du)
+    s = np.repeat(inter["a2s"].astype(np.float64), 128, axis=1)
+    R = g.shape[0]
+    ds = np.repeat(dv.reshape(R, i // 128, 128).max(-1), 128, axis=1) / 448.0
+    with np.errstate(divide="ignore", invalid="ignore"):
+        pos = s > 0
+        q = np.where(pos, v / np.where(pos, s, 1.0), 0.0)
+        dq = np.where(pos, dv / np.where(pos, s, 1.0) + np.abs(q) * ds / np.where(pos, s, 1.0), 0.0)
+    return _e4m3_codes(q - dq), _e4m3_codes(q + dq), s
+
+
+def flip_allowance(layer, inter) -> np.ndarray:
+    """Largest change of the output [M, h] that the flagged requantisation
+    decisions can cause: the gap between the two codes times the scale, times
+    |w2 column|, times the routing weight."""
+    T = _T64()
+    lo, hi, s = flagged_codes(layer, inter)
+    step = np.abs(T[hi] - T[lo]) * s                # [R, i], 0 where clear
+    ids, tw = inter["ids"], inter["topk_w"]
+    M, k = ids.shape
+    h = layer.q2.shape[1]
+    allow = np.zeros((M, h))
+    for p in np.nonzero(step.any(axis=1))[0]:
+        t, r = divmod(int(p), k)
+        e = ids[t, r]
+        W2 = T[layer.q2[e]] * np.repeat(np.repeat(layer.s2[e].astype(np.float64), 128, 0), 128, 1)
+        allow[t] += abs(tw[t, r]) * (np.abs(W2) @ step[p])
+    return allow
+
+
+def check_output(got_bits: np.ndarray, ref_bits: np.ndarray, rel=REL_TOL, cos_min=COS_MIN,
+                 allowance=None):
+    """Returns (max_abs_err, max_ref, min_cos); raises AssertionError on failure.
+    `allowance` (same shape) widens the elementwise bar by the effect of
+    flagged E4M3 code flips (see flip_allowance)."""
     got = bf16_bits_to_f64(got_bits)
     ref = bf16_bits_to_f64(ref_bits)
     assert got.shape == ref.shape
@@ -50,6 +135,8 @@ def check_output(got_bits: np.ndarray, ref_bits: np.ndarray, rel=REL_TOL, cos_mi
         return 0.0, 0.0, 1.0
     err = np.abs(got - ref)
     tol = rel * mx + bf16_ulp(ref)
+    if allowance is not None:
+        tol = tol + allowance * (1 + 1e-6)
     bad = err > tol
     if bad.any():
         idx = np.argwhere(bad)[:5]
@@ -62,8 +149,14 @@ def check_output(got_bits: np.ndarray, ref_bits: np.ndarray, rel=REL_TOL, cos_mi
         if na == 0.0 and nb == 0.0:
             continue
         c = float(a @ b / (na * nb)) if na > 0 and nb > 0 else 0.0
+        bar = cos_min
+        if allowance is not None and nb > 0:
+            # a deviation d with ||d|| <= ||allowance_t|| lowers the cosine by
+            # at most about ||d||^2 / (2 ||b||^2); allow twice that
+            ratio = np.linalg.norm(allowance[t]) / nb
+            bar = min(cos_min, 1.0 - ratio * ratio)
+        assert c >= bar, f"token {t}: cosine {c} < {bar}"
         min_cos = min(min_cos, c)
-    assert min_cos >= cos_min, f"cosine {min_cos} < {cos_min}"
     return float(err.max()), float(mx), min_cos
 
 

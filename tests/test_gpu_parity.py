@@ -9,9 +9,11 @@ import numpy as np
 import pytest
 import torch
 
+import gpu_util
 import oracle
 import synth
-from gpu_util import Layer, check_output, log, read_ws, to_dev_bf16, to_host_bits
+from gpu_util import (Layer, check_output, flagged_codes, flip_allowance, log, read_ws,
+                      to_dev_bf16, to_host_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -203,6 +205,24 @@ def _check_intermediates(moe_mod, L: Layer, ws, inter, tokens=None):
     nact = int(read_ws(ws, lay.num_active, 1, np.int32)[0])
     act = read_ws(ws, lay.active, E, np.int32)[:nact]
     assert np.array_equal(act, np.nonzero(cr)[0])
+    if lay.path == moe_mod.PATH_PREFILL and tokens is None:
+        # requantised activations (sorted-route order): the oracle's codes,
+        # except where the decision sits on a rounding boundary, where either
+        # neighbouring code is the method's result
+        R = M * k
+        a2 = read_ws(ws, lay.act2, R * i, np.uint8).reshape(R, i)
+        a2_by_route = np.empty_like(a2)
+        a2_by_route[srt] = a2
+        lo, hi, _ = flagged_codes(L, inter)
+        ref = inter["a2"]
+        clear = lo == hi
+        assert np.array_equal(a2_by_route[clear], ref[clear]), "requantised codes differ"
+        # elsewhere any code between the two ends (the bracket can span more
+        # than one step where the scale is small against the error bound)
+        T = gpu_util._T64()
+        fl = ~clear
+        got = T[a2_by_route[fl]]
+        assert np.all((got >= T[lo[fl]]) & (got <= T[hi[fl]])), "requantised code outside its bracket"
 
 
 @pytest.mark.parametrize("ci", [0, 1, 2, 3])
@@ -291,14 +311,46 @@ def _custom_layer(dev, M, h, i, E, k, seed, logits_kind="normal"):
     (4, 256, 128, 8, 8),        # k = E
     (7, 1280, 640, 256, 16),    # E = 256, k = 16
     (1, 128, 128, 4, 2),        # smallest dims
+    (300, 256, 128, 4, 2),      # tiled path: ragged 128-route tiles per expert
+    (1000, 512, 384, 8, 3),     # tiled path: several tiles per expert, 3 groups
+    (130, 256, 256, 1, 1),      # tiled path: one expert, a 2-route last tile
 ])
 def test_forward_edge_shapes(dev, moe_mod, M, h, i, E, k):
-    log(f"edge forward M={M} h={h} i={i} E={E} k={k}")
+    log(f"edge forward M={M} h={h} i={i} E={E} k={k} "
+        f"path={moe_mod.workspace_layout(M, h, i, E, k).path}")
     L = _custom_layer(dev, M, h, i, E, k, seed=M * 31 + h)
     out, ws = _run(moe_mod, L)
     ref, inter = L.oracle(intermediates=True)
     _check_intermediates(moe_mod, L, ws, inter)
-    check_output(to_host_bits(out), ref)
+    check_output(to_host_bits(out), ref, allowance=flip_allowance(L, inter))
+
+
+def test_mfma_block_sum_accuracy(dev, moe_mod):
+    """The FP8 MFMA block sums: every materialised gate/up value of the
+    weight-streaming path lies within MFMA_REL * sum|terms| of the exact
+    float64 value computed from the same codes and scales (the bound the
+    flip analysis of the small test shapes relies on)."""
+    M, h, i, E, k = 40, 512, 256, 4, 2
+    L = _custom_layer(dev, M, h, i, E, k, seed=4242)
+    lay = moe_mod.workspace_layout(M, h, i, E, k)
+    assert lay.path == moe_mod.PATH_STREAM
+    out, ws = _run(moe_mod, L)
+    ref, inter = L.oracle(intermediates=True)
+    R = M * k
+    g = read_ws(ws, lay.gate_up, R * 2 * i, np.float32).reshape(R, 2 * i).astype(np.float64)
+    T = gpu_util._T64()
+    ids, xq, xs = inter["ids"].ravel(), inter["xq"], inter["xs"].astype(np.float64)
+    KB = h // 128
+    exact = np.zeros((R, 2 * i))
+    for p in range(R):
+        W = T[L.q13[ids[p]]].reshape(2 * i, KB, 128)
+        a = T[xq[p // k]].reshape(KB, 128)
+        sc = np.repeat(L.s13[ids[p]].astype(np.float64), 128, axis=0) * xs[p // k][None, :]
+        exact[p] = (np.einsum("nbk,bk->nb", W, a) * sc).sum(1)
+    mag = gpu_util.gate_up_terms(L, inter)
+    rel = np.abs(g - exact) / mag
+    log(f"MFMA block sums: max |gpu - exact| / sum|terms| = {rel.max():.3g}")
+    assert rel.max() <= gpu_util.MFMA_REL
 
 
 def test_forward_zero_input_and_empty(dev, moe_mod):
