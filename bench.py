@@ -61,10 +61,15 @@ def stage_work(cfg, stage, U):
     M, h, i, k = cfg.M, cfg.h, cfg.i, cfg.k
     w13, w2 = weight_bytes_per_expert(cfg)
     act = M * h + M * (h // 128) * 4
-    if stage.startswith("stream_gate_up") or stage.startswith("gate_up"):
+    if stage.startswith("stream_gate_up"):
         return U * w13 + act, 4.0 * M * k * h * i
-    if stage.startswith("stream_down") or stage.startswith("down"):
+    if stage.startswith("stream_down"):
         return U * w2, 2.0 * M * k * h * i
+    if stage.startswith("prefill_gate_up"):
+        # weights once, activation rows per route in, E4M3 codes + scales out
+        return U * w13 + M * k * (h + i + (h // 128 + i // 128) * 4), 4.0 * M * k * h * i
+    if stage.startswith("prefill_down"):
+        return U * w2 + M * k * (i + (i // 128) * 4 + h * 4), 2.0 * M * k * h * i
     if stage.startswith("route_quant"):
         return M * h * 2 + M * cfg.E * 4 + act + M * k * 8, 0.0
     if stage.startswith("combine"):

@@ -20,13 +20,21 @@ FLAGS = [
 ]
 
 
+# Per-source extra flags.  The prefill GEMMs promote every MFMA result with
+# VALU arithmetic, so the MFMAs write ordinary VGPRs (no copies out of
+# accumulation registers); their inline-asm LDS copies clobber M0 on purpose.
+EXTRA_FLAGS = {
+    "prefill_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-Wno-inline-asm"],
+}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src, verbose):
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

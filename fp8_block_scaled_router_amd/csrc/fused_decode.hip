@@ -496,7 +496,7 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
 }
 
 size_t fused_lds_bytes(int M, int h, int i, int E, int k) {
-    const int R = M * k, G = h / 128, IB = i / 128;
+    const int R = M * k, G = h / 128;
     auto r4 = [](int v) { return (size_t)((v + 3) & ~3); };
     size_t b = (size_t)M * h;
     b += r4(M * G) * 4;

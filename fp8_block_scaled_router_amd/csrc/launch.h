@@ -52,8 +52,9 @@ struct PrefillArgs {
     int h, i, E, k;
 };
 int prefill_tile_m();
-bool prefill_supported(int h, int i);
-hipError_t launch_prefill(const PrefillArgs& a, int R, hipStream_t stream);
+bool prefill_supported(int M, int h, int i, int k);
+hipError_t launch_prefill_gate_up(const PrefillArgs& a, int R, hipStream_t stream);
+hipError_t launch_prefill_down(const PrefillArgs& a, int R, hipStream_t stream);
 
 // Fixed-order combine of the k route partials of each token into bf16.
 hipError_t launch_combine(const float* y, const float* tw, int M, int k, int h, uint16_t* out,

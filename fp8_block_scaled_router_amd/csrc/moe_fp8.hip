@@ -47,7 +47,7 @@ struct Layout {
 
 int choose_path(int M, int h, int i, int E, int k) {
     if (moe::fused_supported(M, h, i, E, k)) return MOE_FP8_PATH_FUSED_DECODE;
-    if ((int64_t)M * k >= (int64_t)32 * E && moe::prefill_supported(h, i)) return MOE_FP8_PATH_PREFILL;
+    if ((int64_t)M * k >= (int64_t)32 * E && moe::prefill_supported(M, h, i, k)) return MOE_FP8_PATH_PREFILL;
     return MOE_FP8_PATH_STREAM;
 }
 
@@ -101,11 +101,11 @@ const char* const kStreamStages[] = {"route_quant_kernel", "group_hist+group_sca
                                      "combine_kernel"};
 const char* const kFusedStages[] = {"fused_decode_kernel"};
 const char* const kPrefillStages[] = {"route_quant_kernel", "group_hist+group_scatter",
-                                      "prefill_gate_up_kernel+prefill_down_kernel",
+                                      "prefill_gate_up_kernel", "prefill_down_kernel",
                                       "combine_kernel"};
 
 int stage_count(int path) {
-    return path == MOE_FP8_PATH_FUSED_DECODE ? 1 : path == MOE_FP8_PATH_PREFILL ? 4 : 5;
+    return path == MOE_FP8_PATH_FUSED_DECODE ? 1 : 5;
 }
 const char* stage_name(int path, int j) {
     if (path == MOE_FP8_PATH_FUSED_DECODE) return kFusedStages[j];
@@ -217,7 +217,8 @@ int run_forward(const void* x, const float* router_logits, const void* w13, cons
         pa.i = i;
         pa.E = E;
         pa.k = k;
-        MOE_STEP(moe::launch_prefill(pa, R, stream));
+        MOE_STEP(moe::launch_prefill_gate_up(pa, R, stream));
+        MOE_STEP(moe::launch_prefill_down(pa, R, stream));
         MOE_STEP(moe::launch_combine(y, tw, M, k, h, static_cast<uint16_t*>(out), stream));
         return hook.mark() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
     }

@@ -7,45 +7,78 @@
 //
 // gate/up: one workgroup per (M-tile, 128-column group jg).  Its weight tile
 // is the 128 gate rows and the 128 up rows of group jg of w13[e] (256 x h),
-// its activation tile the E4M3 rows of the tile's tokens.  Per 128-wide K
-// block (one scale block) both tiles are staged through LDS (double
-// buffered: the next block's global loads are in flight while the current
-// one feeds the MFMAs), each wave computes a 64-route x (64 gate + 64 up)
-// quarter with v_mfma_f32_16x16x128_f8f6f4 (weights as A, routes as B) and
-// promotes every block with its two scales: acc += blk * (s_w * s_act)
-// (Netra Kernel README capability table: explicit 128x128 block scales).
-// Because the tile holds a whole 128-column group of both halves, the
-// epilogue computes SiLU(gate) * up and its 1x128 E4M3 requantisation on the
-// spot (Netra Kernel README, MoE prefill pair: gate/up then SiLU and
-// quantisation in the producer) and writes the codes in sorted-route order.
+// its activation tile the E4M3 rows of the tile's tokens.  down: one
+// workgroup per (M-tile, 256-row tile of w2[e]) over K = i.
 //
-// down: one workgroup per (M-tile, 256-row tile of w2[e]); same pipeline over
-// K = i, fp32 partial rows written by route id (down-partial).
+// Both kernels share one main loop, built for gfx950:
+//  * 8 waves; each owns 64 weight rows x 64 routes = 4 x 4 tiles of
+//    v_mfma_f32_16x16x128_f8f6f4 (weights as A, routes as B), two waves per
+//    SIMD so one wave's promotion arithmetic overlaps the other's MFMAs.
+//  * Every 128-wide K block (one scale block) of both operand tiles (48 KiB)
+//    is copied global -> LDS by global_load_lds_dwordx4 (no register
+//    staging) into one of three stage buffers: two blocks are in flight while
+//    the third feeds the MFMAs.
+//  * LDS rows are 128 bytes with a 16-byte-slot swizzle that keeps each
+//    lane's 32 K bytes in order and spreads the 16 rows of a fragment over
+//    all banks (see lo_slot).
+//  * Promotion with the two block scales (Netra Kernel README, capability
+//    table: explicit 128x128 block scales): acc += blk * (s_w * s_act) in
+//    fp32, issued four MFMAs after the MFMA that produced blk.
+// gate/up's epilogue computes SiLU(gate) * up and its 1x128 E4M3
+// requantisation on the spot (Netra Kernel README, MoE prefill pair) and
+// writes codes in sorted-route order; down writes fp32 partial rows by route
+// id (the down-partial of the same README).
 //
 // Workgroups are handed to XCDs round-robin; the tile order gives each XCD a
-// contiguous range of tiles, so the tiles that share an activation tile (and
-// the M-tiles of one expert, which share weights) meet in the same L2.
+// contiguous range of tiles, so the M-tiles of one expert (which share its
+// weights) meet in the same L2.
 #include "device.h"
 #include "launch.h"
 
 namespace moe {
+namespace {
 
-constexpr int kPBM = 128;          // routes per tile
-constexpr int kPBN = 256;          // weight rows per tile
-constexpr int kLdsRow = 128 + 16;  // one 128-byte K block per row, padded
+constexpr int kBM = 128;                      // routes per tile
+constexpr int kBN = 256;                      // weight rows per tile
+constexpr int kThreads = 512;                 // 8 waves
+constexpr int kAB = kBN * 128;                // weight bytes per stage
+constexpr int kBB = kBM * 128;                // activation bytes per stage
+constexpr int kXS = 8 * 256;                  // activation scales per stage: 256 B per wave, 64 used
+constexpr int kStage = kAB + kBB + kXS;
+constexpr int kDmaA = kAB / 1024 / 8;         // 1 KiB copies per wave per stage
+constexpr int kDmaB = kBB / 1024 / 8;
+constexpr int kVmemPerStage = kDmaA + kDmaB + 1;   // + one copy of 16 route scales
+constexpr int kLag = 4;                       // promotion trails its MFMA
+constexpr int kMaxKB = 128;                   // weight-scale table: K blocks (h <= 16384)
+
+static_assert(kDmaA == 4 && kDmaB == 2, "stage copy split");
+
+// gfx9 s_waitcnt immediate waiting until at most n vector-memory operations
+// are outstanding (expcnt and lgkmcnt left at their maxima).
+constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
+
+// Row r of a 16-row fragment holds its 32-byte K group kg as two 16-byte
+// halves: the lower half in slot lo_slot(r, kg), the upper in lo_slot ^ 4.
+// Over the 16 rows the lower halves of one kg cover all 16 slots of a
+// 256-byte bank window (and every 8 consecutive rows all 8 slots of a 128-byte
+// window), so fragment reads are free of bank conflicts; because only the
+// slot, not the order of the two halves, depends on the row, every lane sees
+// its K bytes in the same order.
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int lo_slot(int r, int kg) {
+    const int x = swz(r);
+    return (kg ^ (x & 3)) | (x & 4);
+}
+// Inverse: 16-byte K chunk (2 * kg + upper) stored in slot p of row r.
+__device__ __forceinline__ int chunk_of(int r, int p) {
+    const int x = swz(r);
+    return 2 * ((p & 3) ^ (x & 3)) + (((p ^ x) >> 2) & 1);
+}
 
 __device__ __forceinline__ int xcd_tile(int b, int nb) {
     const int per = nb / 8;   // the grid is a multiple of 8
     return (b % 8) * per + b / 8;
-}
-
-__device__ __forceinline__ v8i lds32(const uint8_t* p) {
-    const uint4* q = reinterpret_cast<const uint4*>(p);
-    const uint4 u0 = q[0], u1 = q[1];
-    v8i r;
-    r[0] = (int)u0.x; r[1] = (int)u0.y; r[2] = (int)u0.z; r[3] = (int)u0.w;
-    r[4] = (int)u1.x; r[5] = (int)u1.y; r[6] = (int)u1.z; r[7] = (int)u1.w;
-    return r;
 }
 
 // Expert owning M-tile mt: the largest e with mtile_off[e] <= mt.
@@ -58,173 +91,243 @@ __device__ __forceinline__ int tile_expert(const int32_t* __restrict__ mtile_off
     return lo;
 }
 
-// Staging of one 128-wide K block of a 256-row A tile and a 128-row B tile:
-// thread t moves A chunks t + 256j (j < 8) and B chunks t + 256j (j < 4),
-// chunk c = 16 bytes at row c / 8, column 16 * (c % 8).
-struct Stage {
-    uint4 ra[8];
-    uint4 rb[4];
+__device__ __forceinline__ v8i frag(const uint8_t* lo, const uint8_t* hi) {
+    const uint4 u0 = *reinterpret_cast<const uint4*>(lo);
+    const uint4 u1 = *reinterpret_cast<const uint4*>(hi);
+    v8i r;
+    r[0] = (int)u0.x; r[1] = (int)u0.y; r[2] = (int)u0.z; r[3] = (int)u0.w;
+    r[4] = (int)u1.x; r[5] = (int)u1.y; r[6] = (int)u1.z; r[7] = (int)u1.w;
+    return r;
+}
+
+__device__ __forceinline__ void block_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// State of the shared main loop: wave-uniform bases (scalar registers) and
+// 32-bit per-lane offsets (the prefill path is only taken when activation
+// and requantised tensors stay below 2 GiB).
+struct Loop {
+    const uint8_t* gA;              // weight copies of K block 0 start here ...
+    const uint8_t* gB;              // ... activation copies here
+    const float* gX;                // ... activation-scale copies here (element kb of a route's row)
+    uint32_t offA[kDmaA], offB[kDmaB];   // ... plus these per-lane byte offsets
+    uint32_t offX;                  // ... and this per-lane element offset
+    int wave;                       // wave index (uniform)
+    // fragment reads: lane's lower / upper half of weight tile 0 and route tile 0
+    int a_lo, a_hi, b_lo, b_hi;
+    int x_off;                      // byte offset of the lane's route-tile-0 scale in a stage
+    int a_step[4];                  // byte offsets of weight tiles 1..3 from tile 0 (constants)
 };
 
-template <typename ARow, typename BRow>
-__device__ __forceinline__ void stage_load(Stage& s, int tid, int kb, ARow arow, BRow brow) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int c = tid + 256 * j;
-        s.ra[j] = *reinterpret_cast<const uint4*>(arow(c >> 3) + kb * 128 + (c & 7) * 16);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int c = tid + 256 * j;
-        const uint8_t* src = brow(c >> 3);
-        s.rb[j] = src ? *reinterpret_cast<const uint4*>(src + kb * 128 + (c & 7) * 16)
-                      : make_uint4(0u, 0u, 0u, 0u);
-    }
+// global -> LDS copies.  Written as inline assembly so that the compiler
+// does not track them: the K loop's explicit s_waitcnt / s_barrier pairs are
+// the only synchronisation of the stage buffers, and the loop issues no
+// other vector-memory operation whose waits the compiler would place.  M0
+// holds the wave's LDS destination; lane l's data lands at M0 + 16 l (4 l
+// for the dword form).  One wait state separates the M0 write from the copy.
+__device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "s"(lds), "v"(src) : "memory", "m0");
+}
+__device__ __forceinline__ void copy4_to_lds(const void* src, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+                 :: "s"(lds), "v"(src) : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-__device__ __forceinline__ void stage_store(const Stage& s, int tid, uint8_t* As, uint8_t* Bs) {
+// Issue the copies of K block kb into stage buffer st.
+__device__ __forceinline__ void issue_stage(const Loop& L, uint8_t* st, int kb) {
+    const uint8_t* gA = L.gA + (size_t)kb * 128;
+    const uint8_t* gB = L.gB + (size_t)kb * 128;
+    const uint32_t base = lds_addr(st);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int c = tid + 256 * j;
-        *reinterpret_cast<uint4*>(As + (c >> 3) * kLdsRow + (c & 7) * 16) = s.ra[j];
-    }
+    for (int q = 0; q < kDmaA; ++q) copy16_to_lds(gA + L.offA[q], base + (L.wave * kDmaA + q) * 1024);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int c = tid + 256 * j;
-        *reinterpret_cast<uint4*>(Bs + (c >> 3) * kLdsRow + (c & 7) * 16) = s.rb[j];
-    }
+    for (int q = 0; q < kDmaB; ++q) copy16_to_lds(gB + L.offB[q], base + kAB + (L.wave * kDmaB + q) * 1024);
+    // scales of routes 16 wave .. +16 (lanes 16..63 repeat lanes 0..15)
+    copy4_to_lds(L.gX + L.offX + kb, base + kAB + kBB + L.wave * 256);
 }
 
-// One K block on one wave: 8 weight tiles (rows wrow0[j] .. +16 of the LDS A
-// tile) x 4 route tiles (rows wm*64 + 16m of the LDS B tile), promoted with
-// scale ws[j] * xs[m].
-__device__ __forceinline__ void block_mma(v4f acc[8][4], const uint8_t* As, const uint8_t* Bs,
-                                          const int wrow0[8], int tok0, int col, int kg,
-                                          const float ws[8], const float xsv[4]) {
-    v8i B[4];
+// One K block on one wave: 4 weight tiles x 4 route tiles, promotion of tile
+// (j, m) with sw[j] * (activation scale of route tile m).
+__device__ __forceinline__ void block_mma(v4f acc[16], const Loop& L, const uint8_t* st, const float sw[4]) {
+    v8i A[4], B[4];
+    float xr[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) B[m] = lds32(Bs + (tok0 + 16 * m + col) * kLdsRow + kg * 32);
+    for (int m = 0; m < 4; ++m) B[m] = frag(st + L.b_lo + m * 2048, st + L.b_hi + m * 2048);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const v8i A = lds32(As + (wrow0[j] + col) * kLdsRow + kg * 32);
+    for (int j = 0; j < 4; ++j) A[j] = frag(st + L.a_lo + L.a_step[j], st + L.a_hi + L.a_step[j]);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
-            const v4f blk = mfma_16x16x128_e4m3(A, B[m], z);
-            const float sc = ws[j] * xsv[m];
+    for (int m = 0; m < 4; ++m) xr[m] = *reinterpret_cast<const float*>(st + L.x_off + m * 256);
+    // tile t's product lands in ring[t % kLag]; it is promoted just before
+    // the MFMA of tile t + kLag reuses that slot
+    v4f ring[kLag];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc[j][m][v] = fmaf(blk[v], sc, acc[j][m][v]);
+    for (int t = 0; t < 16 + kLag; ++t) {
+        if (t >= kLag) {
+            const int u = t - kLag;
+            const float sc = sw[u >> 2] * xr[u & 3];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[u][v] = fmaf(ring[u % kLag][v], sc, acc[u][v]);
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+        }
+        if (t < 16) {
+            ring[t % kLag] = mfma_16x16x128_e4m3(A[t >> 2], B[t & 3], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
     }
 }
 
+// The whole K loop: KB blocks through three stage buffers.  Each step
+// issues the copies of block kb + 2, waits until this wave's copies of block
+// kb have landed (the two newer stages may stay in flight), and a barrier
+// makes every wave's copies visible; a second barrier after the MFMAs frees
+// the buffer for the copies issued by the next step.  sw_of(kb, sw) fills
+// the wave's four weight-tile scales of block kb.
+template <typename SwOf>
+__device__ __forceinline__ void k_loop(v4f acc[16], const Loop& L, int KB, uint8_t* stages, SwOf sw_of) {
+    float sw[4];
+    issue_stage(L, stages, 0);
+    if (KB > 1) issue_stage(L, stages + kStage, 1);
+    int rd = 0;   // stage buffer of block kb
+    for (int kb = 0; kb < KB; ++kb) {
+        if (kb + 2 < KB) {
+            issue_stage(L, stages + (rd == 0 ? 2 : rd - 1) * kStage, kb + 2);
+            __builtin_amdgcn_s_waitcnt(vm_wait(2 * kVmemPerStage));
+        } else if (kb + 1 < KB) {
+            __builtin_amdgcn_s_waitcnt(vm_wait(kVmemPerStage));
+        } else {
+            __builtin_amdgcn_s_waitcnt(vm_wait(0));
+        }
+        block_barrier();
+        sw_of(kb, sw);
+        block_mma(acc, L, stages + rd * kStage, sw);
+        block_barrier();
+        rd = rd == 2 ? 0 : rd + 1;
+    }
+}
+
+// Fragment read offsets of this lane: row col of a 16-row tile, K group kg;
+// weight tile 0 starts at LDS row a_row0, route tile 0 at row b_row0.
+__device__ __forceinline__ void lane_geometry(Loop& L, int lane, int a_row0, int b_row0) {
+    const int col = lane & 15, kg = lane >> 4;
+    const int lo = lo_slot(col, kg);
+    L.a_lo = (a_row0 + col) * 128 + lo * 16;
+    L.a_hi = (a_row0 + col) * 128 + (lo ^ 4) * 16;
+    L.b_lo = kAB + (b_row0 + col) * 128 + lo * 16;
+    L.b_hi = kAB + (b_row0 + col) * 128 + (lo ^ 4) * 16;
+    L.x_off = kAB + kBB + (b_row0 / 16) * 256 + col * 4;
+}
+
+}  // namespace
+
 // ----------------------------------------------------------------- gate/up
 
-__global__ __launch_bounds__(256, 1) void prefill_gate_up_kernel(PrefillArgs a) {
-    extern __shared__ __align__(16) uint8_t smem[];
+__global__ __launch_bounds__(kThreads, 1) void prefill_gate_up_kernel(PrefillArgs a) {
+    __shared__ __align__(16) uint8_t stages[3 * kStage];
+    __shared__ int tok_l[kBM];
+    __shared__ float amax_l[4][kBM];
+    __shared__ float sw_l[2][kMaxKB];   // gate / up weight scales of group jg, per K block
+
     const int h = a.h, i = a.i, E = a.E, k = a.k;
     const int KB = h / 128, IB = i / 128, N13 = 2 * i;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int col = lane & 15, kg = lane >> 4;
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wr = wave & 1, wn = wave >> 1;   // routes 64 wr .. +64; gate/up columns 32 wn .. +32
 
-    const int L = xcd_tile(blockIdx.x, gridDim.x);
-    const int mt = L / IB, jg = L - mt * IB;
+    const int T = xcd_tile(blockIdx.x, gridDim.x);
+    const int mt = T / IB, jg = T - mt * IB;
     if (mt >= a.mtile_off[E]) return;
-    const int e = tile_expert(a.mtile_off, E, mt);
-    const int beg = a.offsets[e] + (mt - a.mtile_off[e]) * kPBM;
-    const int rows = min(kPBM, a.offsets[e + 1] - beg);
+    const int e = __builtin_amdgcn_readfirstlane(tile_expert(a.mtile_off, E, mt));
+    const int beg = __builtin_amdgcn_readfirstlane(a.offsets[e] + (mt - a.mtile_off[e]) * kBM);
+    const int rows = __builtin_amdgcn_readfirstlane(min(kBM, a.offsets[e + 1] - beg));
 
-    uint8_t* As = smem;                                          // [2][256][kLdsRow]
-    uint8_t* Bs = As + 2 * kPBN * kLdsRow;                       // [2][128][kLdsRow]
-    int* tok_l = reinterpret_cast<int*>(Bs + 2 * kPBM * kLdsRow);  // [128] token, -1 = padding
-    float* amax_l = reinterpret_cast<float*>(tok_l + kPBM);      // [2][128]
-    float* xs_l = amax_l + 2 * kPBM;                             // [128][KB]
-
-    for (int r = tid; r < kPBM; r += 256) tok_l[r] = r < rows ? a.sorted[beg + r] / k : -1;
-    __syncthreads();
-    for (int idx = tid; idx < kPBM * KB; idx += 256) {
-        const int r = idx / KB, kb = idx - r * KB;
-        const int t = tok_l[r];
-        xs_l[idx] = t >= 0 ? a.xs[(size_t)t * KB + kb] : 0.0f;
+    // padding rows repeat the tile's last route (their outputs are dropped)
+    for (int r = tid; r < kBM; r += kThreads) tok_l[r] = a.sorted[beg + min(r, rows - 1)] / k;
+    {
+        const float* sg = a.s13 + ((size_t)e * (N13 / 128) + jg) * KB;
+        const float* su = a.s13 + ((size_t)e * (N13 / 128) + IB + jg) * KB;
+        for (int j = tid; j < KB; j += kThreads) {
+            sw_l[0][j] = sg[j];
+            sw_l[1][j] = su[j];
+        }
     }
-
-    const uint8_t* wbase = a.w13 + (size_t)e * N13 * h;
-    auto arow = [&](int r) {   // LDS row r: gate rows of group jg, then up rows
-        const int wr = r < 128 ? jg * 128 + r : i + jg * 128 + (r - 128);
-        return wbase + (size_t)wr * h;
-    };
-    auto brow = [&](int r) -> const uint8_t* {
-        const int t = tok_l[r];
-        return t >= 0 ? a.xq + (size_t)t * h : nullptr;
-    };
-    const float* sg = a.s13 + ((size_t)e * (N13 / 128) + jg) * KB;
-    const float* su = a.s13 + ((size_t)e * (N13 / 128) + IB + jg) * KB;
-
-    int wrow0[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) wrow0[j] = (j < 4 ? 0 : 128) + wn * 64 + 16 * (j & 3);
-    const int tok0 = wm * 64;
-
-    v4f acc[8][4];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) acc[j][m] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-
-    Stage st;
-    stage_load(st, tid, 0, arow, brow);
-    stage_store(st, tid, As, Bs);
     __syncthreads();
-    for (int kb = 0; kb < KB; ++kb) {
-        const int cur = kb & 1;
-        if (kb + 1 < KB) stage_load(st, tid, kb + 1, arow, brow);
-        float ws[8], xsv[4];
-        const float g = sg[kb], u = su[kb];
+
+    // weight tiles: gate rows 32 wn + {0, 16}, up rows 128 + 32 wn + {0, 16};
+    // route tiles 64 wr + 16 m
+    Loop L;
+    lane_geometry(L, lane, 32 * wn, 64 * wr);
+    L.a_step[0] = 0;
+    L.a_step[1] = 16 * 128;
+    L.a_step[2] = 128 * 128;
+    L.a_step[3] = 144 * 128;
+    L.wave = wave;
+    L.gA = a.w13 + (size_t)e * N13 * h;
+    L.gB = a.xq;
+    L.gX = a.xs;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) ws[j] = j < 4 ? g : u;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) xsv[m] = xs_l[(tok0 + 16 * m + col) * KB + kb];
-        block_mma(acc, As + cur * kPBN * kLdsRow, Bs + cur * kPBM * kLdsRow, wrow0, tok0, col, kg,
-                  ws, xsv);
-        if (kb + 1 < KB) stage_store(st, tid, As + (cur ^ 1) * kPBN * kLdsRow,
-                                     Bs + (cur ^ 1) * kPBM * kLdsRow);
-        __syncthreads();
+    for (int q = 0; q < kDmaA; ++q) {
+        const int r = (wave * kDmaA + q) * 8 + (lane >> 3);
+        const int wrow = r < 128 ? jg * 128 + r : i + jg * 128 + (r - 128);
+        L.offA[q] = (uint32_t)(wrow * h + chunk_of(r, lane & 7) * 16);
     }
+#pragma unroll
+    for (int q = 0; q < kDmaB; ++q) {
+        const int r = (wave * kDmaB + q) * 8 + (lane >> 3);
+        L.offB[q] = (uint32_t)(tok_l[r] * h + chunk_of(r, lane & 7) * 16);
+    }
+    L.offX = (uint32_t)(tok_l[16 * wave + (lane & 15)] * KB);
+
+    auto sw_of = [&](int kb, float sw[4]) {
+        const float g = sw_l[0][kb], u = sw_l[1][kb];
+        sw[0] = g; sw[1] = g; sw[2] = u; sw[3] = u;
+    };
+
+    v4f acc[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    k_loop(acc, L, KB, stages, sw_of);
 
     // ---- epilogue: SiLU(gate) * up, 1x128 requantisation of group jg.
-    // Lane: route tok0 + 16m + col; gate/up columns wn*64 + 16jj + 4kg + v.
-    float pm[4];
+    // Tile t = 4 j + m: weight tile j (gate j = 0, 1; up j = 2, 3), route
+    // tile m.  Lane: route 64 wr + 16 m + col; gate/up columns
+    // 32 wn + 16 j + 4 kg + v of group jg.
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-        pm[m] = 0.0f;
+        float pm = 0.0f;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const float gt = acc[jj][m][v], up = acc[jj + 4][m][v];
+                const float gt = acc[4 * j + m][v], up = acc[4 * (j + 2) + m][v];
                 const float val = (gt / (1.0f + expf(-gt))) * up;
-                acc[jj][m][v] = val;
-                pm[m] = fmaxf(pm[m], fabsf(val));
+                acc[4 * j + m][v] = val;
+                pm = fmaxf(pm, fabsf(val));
             }
-        pm[m] = fmaxf(pm[m], __shfl_xor(pm[m], 16, kWave));
-        pm[m] = fmaxf(pm[m], __shfl_xor(pm[m], 32, kWave));
-        if (kg == 0) amax_l[wn * kPBM + tok0 + 16 * m + col] = pm[m];
+        pm = fmaxf(pm, __shfl_xor(pm, 16, kWave));
+        pm = fmaxf(pm, __shfl_xor(pm, 32, kWave));
+        if (kg == 0) amax_l[wn][64 * wr + 16 * m + col] = pm;
     }
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-        const int r = tok0 + 16 * m + col;
+        const int r = 64 * wr + 16 * m + col;
         if (r >= rows) continue;
-        const float sc = fmaxf(amax_l[r], amax_l[kPBM + r]) / kE4M3Max;
+        const float sc =
+            fmaxf(fmaxf(amax_l[0][r], amax_l[1][r]), fmaxf(amax_l[2][r], amax_l[3][r])) / kE4M3Max;
         const size_t pos = (size_t)(beg + r);
-        uint32_t* dst = reinterpret_cast<uint32_t*>(a.a2 + pos * i + jg * 128 + wn * 64 + 4 * kg);
+        uint32_t* dst = reinterpret_cast<uint32_t*>(a.a2 + pos * i + jg * 128 + 32 * wn + 4 * kg);
         const float rc = sc != 0.0f ? __builtin_amdgcn_rcpf(sc) : 0.0f;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const uint32_t q = sc == 0.0f ? 0u
-                : quant4(acc[jj][m][0], acc[jj][m][1], acc[jj][m][2], acc[jj][m][3], sc, rc);
-            dst[4 * jj] = q;   // columns wn*64 + 16jj + 4kg .. +3
+        for (int j = 0; j < 2; ++j) {
+            const v4f vv = acc[4 * j + m];
+            dst[4 * j] = sc == 0.0f ? 0u : quant4(vv[0], vv[1], vv[2], vv[3], sc, rc);   // columns + 16 j
         }
         if (wn == 0 && kg == 0) a.a2s[pos * IB + jg] = sc;
     }
@@ -232,118 +335,102 @@ __global__ __launch_bounds__(256, 1) void prefill_gate_up_kernel(PrefillArgs a) 
 
 // -------------------------------------------------------------------- down
 
-__global__ __launch_bounds__(256, 1) void prefill_down_kernel(PrefillArgs a) {
-    extern __shared__ __align__(16) uint8_t smem[];
+__global__ __launch_bounds__(kThreads, 1) void prefill_down_kernel(PrefillArgs a) {
+    __shared__ __align__(16) uint8_t stages[3 * kStage];
+    __shared__ int prt_l[kBM];
+    __shared__ float sw_l[2][kMaxKB];   // weight scales of the tile's two 128-row blocks, per K block
+
     const int h = a.h, i = a.i, E = a.E;
-    const int IB = i / 128, NT = h / kPBN;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int IB = i / 128, NT = h / kBN;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int col = lane & 15, kg = lane >> 4;
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wr = wave & 1, wn = wave >> 1;   // routes 64 wr .. +64; output rows 64 wn .. +64
 
-    const int L = xcd_tile(blockIdx.x, gridDim.x);
-    const int mt = L / NT, nt = L - mt * NT;
+    const int T = xcd_tile(blockIdx.x, gridDim.x);
+    const int mt = T / NT, nt = T - mt * NT;
     if (mt >= a.mtile_off[E]) return;
-    const int e = tile_expert(a.mtile_off, E, mt);
-    const int beg = a.offsets[e] + (mt - a.mtile_off[e]) * kPBM;
-    const int rows = min(kPBM, a.offsets[e + 1] - beg);
+    const int e = __builtin_amdgcn_readfirstlane(tile_expert(a.mtile_off, E, mt));
+    const int beg = __builtin_amdgcn_readfirstlane(a.offsets[e] + (mt - a.mtile_off[e]) * kBM);
+    const int rows = __builtin_amdgcn_readfirstlane(min(kBM, a.offsets[e + 1] - beg));
 
-    uint8_t* As = smem;
-    uint8_t* Bs = As + 2 * kPBN * kLdsRow;
-    int* prt_l = reinterpret_cast<int*>(Bs + 2 * kPBM * kLdsRow);   // [128] route id, -1 = padding
-    float* xs_l = reinterpret_cast<float*>(prt_l + kPBM);         // [128][IB]
-
-    for (int r = tid; r < kPBM; r += 256) prt_l[r] = r < rows ? a.sorted[beg + r] : -1;
-    for (int idx = tid; idx < kPBM * IB; idx += 256) {
-        const int r = idx / IB, kb = idx - r * IB;
-        xs_l[idx] = r < rows ? a.a2s[(size_t)(beg + r) * IB + kb] : 0.0f;
+    for (int r = tid; r < kBM; r += kThreads) prt_l[r] = r < rows ? a.sorted[beg + r] : -1;
+    {
+        const float* sb = a.s2 + ((size_t)e * (h / 128) + 2 * nt) * IB;   // blocks 2 nt, 2 nt + 1
+        for (int j = tid; j < 2 * IB; j += kThreads) sw_l[j / IB][j % IB] = sb[j];
     }
     __syncthreads();
 
-    const uint8_t* wbase = a.w2 + ((size_t)e * h + (size_t)nt * kPBN) * i;
-    auto arow = [&](int r) { return wbase + (size_t)r * i; };
-    auto brow = [&](int r) -> const uint8_t* {
-        return r < rows ? a.a2 + (size_t)(beg + r) * i : nullptr;
+    // weight tiles: rows 64 wn + 16 j (scale block wn / 2); route tiles 64 wr + 16 m
+    Loop L;
+    lane_geometry(L, lane, 64 * wn, 64 * wr);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) L.a_step[j] = j * 16 * 128;
+    L.wave = wave;
+    L.gA = a.w2 + ((size_t)e * h + (size_t)nt * kBN) * i;
+    L.gB = a.a2 + (size_t)beg * i;
+    L.gX = a.a2s + (size_t)beg * IB;
+#pragma unroll
+    for (int q = 0; q < kDmaA; ++q) {
+        const int r = (wave * kDmaA + q) * 8 + (lane >> 3);
+        L.offA[q] = (uint32_t)(r * i + chunk_of(r, lane & 7) * 16);
+    }
+#pragma unroll
+    for (int q = 0; q < kDmaB; ++q) {
+        const int r = (wave * kDmaB + q) * 8 + (lane >> 3);
+        L.offB[q] = (uint32_t)(min(r, rows - 1) * i + chunk_of(r, lane & 7) * 16);   // padding repeats the last route
+    }
+    L.offX = (uint32_t)(min(16 * wave + (lane & 15), rows - 1) * IB);
+
+    const int sblk = wn >> 1;
+    auto sw_of = [&](int kb, float sw[4]) {
+        const float w = sw_l[sblk][kb];
+        sw[0] = w; sw[1] = w; sw[2] = w; sw[3] = w;
     };
-    // the wave's 128 weight rows lie in one 128-row scale block
-    const float* sw = a.s2 + ((size_t)e * (h / 128) + (nt * kPBN + wn * 128) / 128) * IB;
 
-    int wrow0[8];
+    v4f acc[16];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) wrow0[j] = wn * 128 + 16 * j;
-    const int tok0 = wm * 64;
+    for (int t = 0; t < 16; ++t) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    k_loop(acc, L, IB, stages, sw_of);
+    __syncthreads();   // prt_l
 
-    v4f acc[8][4];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) acc[j][m] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-
-    Stage st;
-    stage_load(st, tid, 0, arow, brow);
-    stage_store(st, tid, As, Bs);
-    __syncthreads();
-    for (int kb = 0; kb < IB; ++kb) {
-        const int cur = kb & 1;
-        if (kb + 1 < IB) stage_load(st, tid, kb + 1, arow, brow);
-        float ws[8], xsv[4];
-        const float w = sw[kb];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) ws[j] = w;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) xsv[m] = xs_l[(tok0 + 16 * m + col) * IB + kb];
-        block_mma(acc, As + cur * kPBN * kLdsRow, Bs + cur * kPBM * kLdsRow, wrow0, tok0, col, kg,
-                  ws, xsv);
-        if (kb + 1 < IB) stage_store(st, tid, As + (cur ^ 1) * kPBN * kLdsRow,
-                                     Bs + (cur ^ 1) * kPBM * kLdsRow);
-        __syncthreads();
-    }
-
-    // ---- epilogue: fp32 partial rows by route id
+    // ---- epilogue: fp32 partial rows by route id; lane holds output rows
+    // nt * 256 + 64 wn + 16 j + 4 kg + v of route 64 wr + 16 m + col.
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-        const int r = tok0 + 16 * m + col;
-        const int p = prt_l[r];
+        const int p = prt_l[64 * wr + 16 * m + col];
         if (p < 0) continue;
+        float* dst = a.y + (size_t)p * h + nt * kBN + 64 * wn + 4 * kg;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            float* dst = a.y + (size_t)p * h + nt * kPBN + wrow0[j] + 4 * kg;
-            *reinterpret_cast<float4*>(dst) =
-                make_float4(acc[j][m][0], acc[j][m][1], acc[j][m][2], acc[j][m][3]);
+        for (int j = 0; j < 4; ++j) {
+            const v4f vv = acc[4 * j + m];
+            *reinterpret_cast<float4*>(dst + 16 * j) = make_float4(vv[0], vv[1], vv[2], vv[3]);
         }
     }
 }
 
-static size_t gate_up_lds(int h) {
-    return (size_t)2 * (kPBN + kPBM) * kLdsRow + kPBM * 4 + 2 * kPBM * 4 + (size_t)kPBM * (h / 128) * 4;
-}
-static size_t down_lds(int i) {
-    return (size_t)2 * (kPBN + kPBM) * kLdsRow + kPBM * 4 + (size_t)kPBM * (i / 128) * 4;
-}
+int prefill_tile_m() { return kBM; }
 
-int prefill_tile_m() { return kPBM; }
-
-bool prefill_supported(int h, int i) {
-    return h % kPBN == 0 && i % 128 == 0 && gate_up_lds(h) <= 160 * 1024 && down_lds(i) <= 160 * 1024;
+bool prefill_supported(int M, int h, int i, int k) {
+    const int64_t lim = (int64_t)1 << 31;   // 32-bit per-lane offsets
+    return h % kBN == 0 && i % 128 == 0 && (int64_t)M * h < lim && (int64_t)M * k * i < lim &&
+           (int64_t)M * (h / 128) < lim;
 }
 
 static int round8(int v) { return (v + 7) / 8 * 8; }
 
-hipError_t launch_prefill(const PrefillArgs& a, int R, hipStream_t stream) {
-    static bool configured = false;
-    if (!configured) {
-        hipFuncSetAttribute((const void*)prefill_gate_up_kernel,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        hipFuncSetAttribute((const void*)prefill_down_kernel,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        configured = true;
-    }
-    const int max_mt = R / kPBM + a.E;   // >= sum over experts of ceil(count / 128)
-    const int g1 = round8(max_mt * (a.i / 128));
-    hipLaunchKernelGGL(prefill_gate_up_kernel, dim3(g1), dim3(256), gate_up_lds(a.h), stream, a);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    const int g2 = round8(max_mt * (a.h / kPBN));
-    hipLaunchKernelGGL(prefill_down_kernel, dim3(g2), dim3(256), down_lds(a.i), stream, a);
+// Upper bound on the M-tiles of R routes over E experts: sum over experts of
+// ceil(count / 128) <= R / 128 + E.
+static int max_mtiles(int R, int E) { return R / kBM + E; }
+
+hipError_t launch_prefill_gate_up(const PrefillArgs& a, int R, hipStream_t stream) {
+    const int g = round8(max_mtiles(R, a.E) * (a.i / 128));
+    hipLaunchKernelGGL(prefill_gate_up_kernel, dim3(g), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill_down(const PrefillArgs& a, int R, hipStream_t stream) {
+    const int g = round8(max_mtiles(R, a.E) * (a.h / kBN));
+    hipLaunchKernelGGL(prefill_down_kernel, dim3(g), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
