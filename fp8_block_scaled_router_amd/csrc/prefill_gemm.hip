@@ -81,8 +81,24 @@ __device__ __forceinline__ int xcd_tile(int b, int nb) {
     return (b % 8) * per + b / 8;
 }
 
+// Per-tile routing metadata, staged in LDS with one coalesced load so a
+// tile's set-up costs one global round trip instead of a chain of dependent
+// ones.
+constexpr int kMaxE = 256;
+struct TileMeta {
+    int mtile_off[kMaxE + 1];   // first M-tile of each expert
+    int offsets[kMaxE + 1];     // first sorted route of each expert
+};
+
+__device__ __forceinline__ void load_meta(TileMeta& m, const PrefillArgs& a, int tid) {
+    for (int j = tid; j <= a.E; j += kThreads) {
+        m.mtile_off[j] = a.mtile_off[j];
+        m.offsets[j] = a.offsets[j];
+    }
+}
+
 // Expert owning M-tile mt: the largest e with mtile_off[e] <= mt.
-__device__ __forceinline__ int tile_expert(const int32_t* __restrict__ mtile_off, int E, int mt) {
+__device__ __forceinline__ int tile_expert(const int* mtile_off, int E, int mt) {
     int lo = 0, hi = E;
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
@@ -183,12 +199,13 @@ __device__ __forceinline__ void block_mma(v4f acc[16], const Loop& L, const uint
     }
 }
 
-// The whole K loop: KB blocks through three stage buffers.  Each step
-// issues the copies of block kb + 2, waits until this wave's copies of block
-// kb have landed (the two newer stages may stay in flight), and a barrier
-// makes every wave's copies visible; a second barrier after the MFMAs frees
-// the buffer for the copies issued by the next step.  sw_of(kb, sw) fills
-// the wave's four weight-tile scales of block kb.
+// The whole K loop: KB blocks through three stage buffers, one barrier per
+// block.  Step kb waits until this wave's copies of block kb have landed
+// (block kb + 1 may stay in flight), and the barrier both makes every wave's
+// copies of block kb visible and certifies that every wave has finished
+// reading block kb - 1; only then are the copies of block kb + 2 issued, into
+// kb - 1's buffer, so two blocks are in flight while block kb is multiplied.
+// sw_of(kb, sw) fills the wave's four weight-tile scales of block kb.
 template <typename SwOf>
 __device__ __forceinline__ void k_loop(v4f acc[16], const Loop& L, int KB, uint8_t* stages, SwOf sw_of) {
     float sw[4];
@@ -196,20 +213,15 @@ __device__ __forceinline__ void k_loop(v4f acc[16], const Loop& L, int KB, uint8
     if (KB > 1) issue_stage(L, stages + kStage, 1);
     int rd = 0;   // stage buffer of block kb
     for (int kb = 0; kb < KB; ++kb) {
-        if (kb + 2 < KB) {
-            issue_stage(L, stages + (rd == 0 ? 2 : rd - 1) * kStage, kb + 2);
-            __builtin_amdgcn_s_waitcnt(vm_wait(2 * kVmemPerStage));
-        } else if (kb + 1 < KB) {
-            __builtin_amdgcn_s_waitcnt(vm_wait(kVmemPerStage));
-        } else {
-            __builtin_amdgcn_s_waitcnt(vm_wait(0));
-        }
+        if (kb + 1 < KB) __builtin_amdgcn_s_waitcnt(vm_wait(kVmemPerStage));
+        else __builtin_amdgcn_s_waitcnt(vm_wait(0));
         block_barrier();
+        if (kb + 2 < KB) issue_stage(L, stages + (rd == 0 ? 2 : rd - 1) * kStage, kb + 2);
         sw_of(kb, sw);
         block_mma(acc, L, stages + rd * kStage, sw);
-        block_barrier();
         rd = rd == 2 ? 0 : rd + 1;
     }
+    block_barrier();   // every wave is done with the stage buffers
 }
 
 // Fragment read offsets of this lane: row col of a 16-row tile, K group kg;
@@ -233,6 +245,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_gate_up_kernel(PrefillArg
     __shared__ int tok_l[kBM];
     __shared__ float amax_l[4][kBM];
     __shared__ float sw_l[2][kMaxKB];   // gate / up weight scales of group jg, per K block
+    __shared__ TileMeta meta;
 
     const int h = a.h, i = a.i, E = a.E, k = a.k;
     const int KB = h / 128, IB = i / 128, N13 = 2 * i;
@@ -242,10 +255,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_gate_up_kernel(PrefillArg
 
     const int T = xcd_tile(blockIdx.x, gridDim.x);
     const int mt = T / IB, jg = T - mt * IB;
-    if (mt >= a.mtile_off[E]) return;
-    const int e = __builtin_amdgcn_readfirstlane(tile_expert(a.mtile_off, E, mt));
-    const int beg = __builtin_amdgcn_readfirstlane(a.offsets[e] + (mt - a.mtile_off[e]) * kBM);
-    const int rows = __builtin_amdgcn_readfirstlane(min(kBM, a.offsets[e + 1] - beg));
+    load_meta(meta, a, tid);
+    __syncthreads();
+    if (mt >= meta.mtile_off[E]) return;
+    const int e = __builtin_amdgcn_readfirstlane(tile_expert(meta.mtile_off, E, mt));
+    const int beg = __builtin_amdgcn_readfirstlane(meta.offsets[e] + (mt - meta.mtile_off[e]) * kBM);
+    const int rows = __builtin_amdgcn_readfirstlane(min(kBM, meta.offsets[e + 1] - beg));
 
     // padding rows repeat the tile's last route (their outputs are dropped)
     for (int r = tid; r < kBM; r += kThreads) tok_l[r] = a.sorted[beg + min(r, rows - 1)] / k;
@@ -297,7 +312,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_gate_up_kernel(PrefillArg
     // ---- epilogue: SiLU(gate) * up, 1x128 requantisation of group jg.
     // Tile t = 4 j + m: weight tile j (gate j = 0, 1; up j = 2, 3), route
     // tile m.  Lane: route 64 wr + 16 m + col; gate/up columns
-    // 32 wn + 16 j + 4 kg + v of group jg.
+    // 32 wn + 16 j + 4 kg + v of group jg.  SiLU uses the hardware exp2 and
+    // reciprocal (a few ulp from the correctly rounded quotient; the FP8
+    // block sums feeding it carry far larger error).
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
         float pm = 0.0f;
@@ -306,7 +323,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_gate_up_kernel(PrefillArg
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const float gt = acc[4 * j + m][v], up = acc[4 * (j + 2) + m][v];
-                const float val = (gt / (1.0f + expf(-gt))) * up;
+                const float val = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
                 acc[4 * j + m][v] = val;
                 pm = fmaxf(pm, fabsf(val));
             }
@@ -315,21 +332,33 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_gate_up_kernel(PrefillArg
         if (kg == 0) amax_l[wn][64 * wr + 16 * m + col] = pm;
     }
     __syncthreads();
+    // codes go to a 128 x 128 tile in the (now idle) stage buffers, rows of
+    // 144 bytes so the 4-byte writes of 16 routes hit distinct banks, then
+    // leave as whole 128-byte rows
+    uint8_t* codes = stages;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
         const int r = 64 * wr + 16 * m + col;
-        if (r >= rows) continue;
         const float sc =
             fmaxf(fmaxf(amax_l[0][r], amax_l[1][r]), fmaxf(amax_l[2][r], amax_l[3][r])) / kE4M3Max;
-        const size_t pos = (size_t)(beg + r);
-        uint32_t* dst = reinterpret_cast<uint32_t*>(a.a2 + pos * i + jg * 128 + 32 * wn + 4 * kg);
         const float rc = sc != 0.0f ? __builtin_amdgcn_rcpf(sc) : 0.0f;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const v4f vv = acc[4 * j + m];
-            dst[4 * j] = sc == 0.0f ? 0u : quant4(vv[0], vv[1], vv[2], vv[3], sc, rc);   // columns + 16 j
+            *reinterpret_cast<uint32_t*>(codes + r * 144 + 32 * wn + 16 * j + 4 * kg) =
+                sc == 0.0f ? 0u : quant4(vv[0], vv[1], vv[2], vv[3], sc, rc);
         }
-        if (wn == 0 && kg == 0) a.a2s[pos * IB + jg] = sc;
+        if (wn == 0 && kg == 0 && r < rows) a.a2s[(size_t)(beg + r) * IB + jg] = sc;
+    }
+    __syncthreads();
+    {
+        const int r = tid >> 2, c = (tid & 3) * 32;   // 4 threads per route row, 32 bytes each
+        if (r < rows) {
+            const uint4* src = reinterpret_cast<const uint4*>(codes + r * 144 + c);
+            uint4* dst = reinterpret_cast<uint4*>(a.a2 + (size_t)(beg + r) * i + jg * 128 + c);
+            dst[0] = src[0];
+            dst[1] = src[1];
+        }
     }
 }
 
@@ -339,6 +368,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_down_kernel(PrefillArgs a
     __shared__ __align__(16) uint8_t stages[3 * kStage];
     __shared__ int prt_l[kBM];
     __shared__ float sw_l[2][kMaxKB];   // weight scales of the tile's two 128-row blocks, per K block
+    __shared__ TileMeta meta;
 
     const int h = a.h, i = a.i, E = a.E;
     const int IB = i / 128, NT = h / kBN;
@@ -348,10 +378,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_down_kernel(PrefillArgs a
 
     const int T = xcd_tile(blockIdx.x, gridDim.x);
     const int mt = T / NT, nt = T - mt * NT;
-    if (mt >= a.mtile_off[E]) return;
-    const int e = __builtin_amdgcn_readfirstlane(tile_expert(a.mtile_off, E, mt));
-    const int beg = __builtin_amdgcn_readfirstlane(a.offsets[e] + (mt - a.mtile_off[e]) * kBM);
-    const int rows = __builtin_amdgcn_readfirstlane(min(kBM, a.offsets[e + 1] - beg));
+    load_meta(meta, a, tid);
+    __syncthreads();
+    if (mt >= meta.mtile_off[E]) return;
+    const int e = __builtin_amdgcn_readfirstlane(tile_expert(meta.mtile_off, E, mt));
+    const int beg = __builtin_amdgcn_readfirstlane(meta.offsets[e] + (mt - meta.mtile_off[e]) * kBM);
+    const int rows = __builtin_amdgcn_readfirstlane(min(kBM, meta.offsets[e + 1] - beg));
 
     for (int r = tid; r < kBM; r += kThreads) prt_l[r] = r < rows ? a.sorted[beg + r] : -1;
     {
