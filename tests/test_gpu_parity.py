@@ -382,23 +382,29 @@ def test_forward_bound_workspace(dev, moe_mod):
 
 
 def test_fused_path_m_sweep_and_shared_workspace(dev, moe_mod):
-    """Small batches M = 1..16 on the one-kernel path, all through ONE workspace
-    sized for the largest, in a row: ragged M, and sync words that must come
-    back clean after every forward whatever the previous shape was."""
+    """Small batches M = 1..16 through ONE workspace sized for the largest, in
+    a row: ragged M, the one-kernel path up to M = 8 and the multi-kernel
+    path above, and sync words that must come back clean after every forward
+    whatever the previous shape was (only the one-kernel path advances the
+    epoch tag)."""
     h, i, E, k = 2048, 768, 128, 8
     cfg16 = synth.LayerConfig("m16", 16, h, i, E, k, "normal", "sweep")
     big = Layer(cfg16, 777, dev)
-    assert moe_mod.workspace_layout(16, h, i, E, k).path == moe_mod.PATH_FUSED_DECODE
+    assert moe_mod.workspace_layout(8, h, i, E, k).path == moe_mod.PATH_FUSED_DECODE
+    assert moe_mod.workspace_layout(9, h, i, E, k).path == moe_mod.PATH_STREAM
     ws = moe_mod.alloc_workspace(16, h, i, E, k, device=dev)
-    for n, M in enumerate((1, 2, 3, 5, 8, 13, 16, 1)):
-        log(f"fused sweep M={M}")
+    fused = 0
+    for M in (1, 2, 3, 5, 8, 13, 16, 1, 9, 4):
+        lay = moe_mod.workspace_layout(M, h, i, E, k)
+        log(f"sweep M={M} path={lay.path}")
         cfg = synth.LayerConfig(f"m{M}", M, h, i, E, k, "normal", "sweep")
         L = Layer(cfg, 777, dev, x=big.x[:M], logits=big.logits[:M],
                   weights=(big.q13, big.s13, big.q2, big.s2))
         out = moe_mod.moe_fp8_forward_ws(L.tx, L.tl, L.t13, L.ts13, L.t2, L.ts2, k, ws)
         torch.cuda.synchronize()
         _check_sync_clean(ws)
-        assert int(ws[:4].view(torch.int32).item()) == n + 1, "one forward = one tag"
+        fused += lay.path == moe_mod.PATH_FUSED_DECODE
+        assert int(ws[:4].view(torch.int32).item()) == fused, "one fused forward = one tag"
         check_output(to_host_bits(out), L.oracle())
 
 
