@@ -183,6 +183,8 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
     // token's logits and the first batch of x rows are requested before any
     // of them is used.
     if (tid == 0) misc_l[3] = (int)(ld_agent(a.sync + kSyncEpoch / 4) + 1u);
+    uint32_t* bm_l = reinterpret_cast<uint32_t*>(misc_l + 8);   // experts present in the batch
+    if (tid < 8) bm_l[tid] = 0u;
     const int nq = M * G;   // 16-lane rows of activation groups
     const int qbase = wave * 4 + (lane >> 4);
     uint4 xr[4];
@@ -211,15 +213,90 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
         if (t != wave) l_load(t);
         route_fast(lg, E, k, ids_l + t * k, w_l + t * k, lane);
     }
+    // the active experts (ascending) right after routing, so that the weight
+    // prefetch below is in flight while the activations are quantised and
+    // the routes grouped
+    __syncthreads();
+    for (int p = tid; p < R; p += 256) atomicOr(&bm_l[ids_l[p] >> 5], 1u << (ids_l[p] & 31));
+    __syncthreads();
+    if (wave == 0) {
+        int c[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = 4 * lane + j;
+            c[j] = e < E ? (int)((bm_l[e >> 5] >> (e & 31)) & 1u) : 0;
+        }
+        const int lact = c[0] + c[1] + c[2] + c[3];
+        const int iact = wave_scan_incl(lact);
+        int arun = iact - lact;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (c[j]) act_l[arun++] = 4 * lane + j;
+        if (lane == 63) misc_l[0] = iact;
+    }
+    __syncthreads();
+    const int U = misc_l[0];
+    const uint32_t tag = (uint32_t)misc_l[3];
+    const int nA = U * IB * kQuarters;
+    const int NT = h / kDownRows;
+    const int nB = U * NT;
+
+    // ---- prefetch: the first gate/up task's first K batch (or, without gate/up
+    // work, the first down task's weights)
+    // weights in registers; each task's 16 (8) block scales arrive as one
+    // lane-indexed load (lane j holds block j's scale) and are read back with
+    // readlane
+    v8i Aw[kMaxKB];
+    float Asc_v = 0.0f;
+    v8i Bw[kFusedMaxIB];
+    float Bsc_v = 0.0f;
+    auto a_geom = [&](int task, int& u, int& e, int& row0) {
+        u = task / (IB * kQuarters);
+        const int rem = task - u * IB * kQuarters;
+        const int jg = rem / kQuarters, q = rem - jg * kQuarters;
+        e = act_l[u];
+        row0 = (wave >> 1) * i + jg * 128 + q * 32 + (wave & 1) * 16;
+    };
+    auto a_load = [&](int e, int row0, int kb0) {
+        const uint8_t* wrow = a.w13 + ((size_t)e * N13 + row0 + col) * h + kg * 32 + kb0 * 128;
+        const float* ws = a.s13 + ((size_t)e * (N13 / 128) + row0 / 128) * KB + kb0;
+        const int nkb = min(KB - kb0, kMaxKB);
+        if (lane < nkb) Asc_v = ws[lane];
+#pragma unroll
+        for (int u8 = 0; u8 < kMaxKB; ++u8)
+            if (u8 < nkb) Aw[u8] = load32(wrow + u8 * 128);
+    };
+    auto b_load = [&](int task) {
+        const int u = task / NT, nt = task - u * NT;
+        const int e = act_l[u];
+        const int n0 = nt * kDownRows + wave * 16;
+        const uint8_t* wrow = a.w2 + ((size_t)e * h + n0 + col) * i + kg * 32;
+        const float* ws = a.s2 + ((size_t)e * (h / 128) + n0 / 128) * IB;
+        if (lane < IB) Bsc_v = ws[lane];
+#pragma unroll
+        for (int kb = 0; kb < kFusedMaxIB; ++kb)
+            if (kb < IB) Bw[kb] = load32(wrow + kb * 128);
+    };
+    // nothing from phase 0 is still in flight (its loads were consumed);
+    // saying so keeps the compiler from draining the prefetch below later on
+    wait_vmem();
+    if ((int)blockIdx.x < nA) {
+        int u, e, row0;
+        a_geom(blockIdx.x, u, e, row0);
+        a_load(e, row0, 0);
+    } else if ((int)blockIdx.x < nB) {
+        b_load(blockIdx.x);   // no gate/up work here: fetch the down tile now
+    }
+
 #pragma unroll 1
     for (int base = qbase; base < nq; base += 64) {
         if (base != qbase) x_load(base);
-#pragma unroll 1
+#pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
             const int task = base + 16 * s4;
             if (task < nq) {
                 const int t = task / G, g = task - t * G;
-                const uint4 u = s4 == 0 ? xr[0] : s4 == 1 ? xr[1] : s4 == 2 ? xr[2] : xr[3];
+                const uint4 u = xr[s4];
                 float v[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
                               bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w)};
                 float m = 0.0f;
@@ -235,8 +312,8 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
     __syncthreads();
     if (wave == 0) {
         // counts and each route's rank inside its expert (ballot match per
-        // 64 routes), then offsets and the active list by DPP prefix sums,
-        // then the routes in (expert, route id) order
+        // 64 routes), then offsets by a DPP prefix sum, then the routes in
+        // (expert, route id) order
         for (int e = lane; e < E; e += 64) cnt_l[e] = 0;
         const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
         int lr[4], ee[4];
@@ -259,24 +336,15 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) c[j] = (4 * lane + j < E) ? cnt_l[4 * lane + j] : 0;
         const int lsum = c[0] + c[1] + c[2] + c[3];
-        const int lact = (c[0] > 0) + (c[1] > 0) + (c[2] > 0) + (c[3] > 0);
         const int incl = wave_scan_incl(lsum);
-        const int iact = wave_scan_incl(lact);
-        int run = incl - lsum, arun = iact - lact;
+        int run = incl - lsum;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int e = 4 * lane + j;
-            if (e < E) {
-                off_l[e] = run;
-                if (c[j] > 0) act_l[arun] = e;
-            }
+            if (e < E) off_l[e] = run;
             run += c[j];
-            arun += (c[j] > 0);
         }
-        if (lane == 63) {
-            off_l[E] = incl;
-            misc_l[0] = iact;
-        }
+        if (lane == 63) off_l[E] = incl;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const int p = 64 * b + lane;
@@ -284,56 +352,6 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
         }
     }
     __syncthreads();
-    const int U = misc_l[0];
-    const uint32_t tag = (uint32_t)misc_l[3];
-    const int nA = U * IB * kQuarters;
-    const int NT = h / kDownRows;
-    const int nB = U * NT;
-
-    // ---- prefetch: the first gate/up task's first K batch and the first
-    // down task's weights, all in flight before anything is computed
-    v8i Aw[kMaxKB];
-    float Asc[kMaxKB];
-    v8i Bw[kFusedMaxIB];
-    float Bsc[kFusedMaxIB];
-    auto a_geom = [&](int task, int& u, int& e, int& row0) {
-        u = task / (IB * kQuarters);
-        const int rem = task - u * IB * kQuarters;
-        const int jg = rem / kQuarters, q = rem - jg * kQuarters;
-        e = act_l[u];
-        row0 = (wave >> 1) * i + jg * 128 + q * 32 + (wave & 1) * 16;
-    };
-    auto a_load = [&](int e, int row0, int kb0) {
-        const uint8_t* wrow = a.w13 + ((size_t)e * N13 + row0 + col) * h + kg * 32;
-        const float* ws = a.s13 + ((size_t)e * (N13 / 128) + row0 / 128) * KB;
-#pragma unroll
-        for (int u8 = 0; u8 < kMaxKB; ++u8) {
-            if (kb0 + u8 < KB) {
-                Aw[u8] = load32(wrow + (kb0 + u8) * 128);
-                Asc[u8] = ws[kb0 + u8];
-            }
-        }
-    };
-    auto b_load = [&](int task) {
-        const int u = task / NT, nt = task - u * NT;
-        const int e = act_l[u];
-        const int n0 = nt * kDownRows + wave * 16;
-        const uint8_t* wrow = a.w2 + ((size_t)e * h + n0 + col) * i + kg * 32;
-        const float* ws = a.s2 + ((size_t)e * (h / 128) + n0 / 128) * IB;
-#pragma unroll
-        for (int kb = 0; kb < kFusedMaxIB; ++kb) {
-            if (kb < IB) {
-                Bw[kb] = load32(wrow + kb * 128);
-                Bsc[kb] = ws[kb];
-            }
-        }
-    };
-    if ((int)blockIdx.x < nA) {
-        int u, e, row0;
-        a_geom(blockIdx.x, u, e, row0);
-        a_load(e, row0, 0);
-    }
-    if ((int)blockIdx.x < nB) b_load(blockIdx.x);
 
     // ---- phase 1: gate/up quarters
     for (int task = blockIdx.x; task < nA; task += gridDim.x) {
@@ -353,7 +371,7 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
                 const int kb = kb0 + u8;
                 if (kb < KB) {
                     const v8i B = valid ? load32(xrow + kb * 128) : zero8();
-                    const float sc = (valid ? xsr[kb] : 0.0f) * Asc[u8];
+                    const float sc = (valid ? xsr[kb] : 0.0f) * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Asc_v), u8));
                     const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
                     const v4f blk = mfma_16x16x128_e4m3(Aw[u8], B, z);
 #pragma unroll
@@ -367,6 +385,12 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
             for (int v = 0; v < 4; ++v) st_agent64(gp + v, ll_pack(acc[v], tag));
         }
     }
+
+    // The down tile's weights are fetched only now by workgroups that had
+    // gate/up work: they are not needed before the gate/up results of the
+    // whole route are in, and fetching them earlier only competes with the
+    // gate/up weights for bandwidth.
+    if ((int)blockIdx.x < nA && (int)blockIdx.x < nB) b_load(blockIdx.x);
 
     // ---- phase 2: down tiles
     for (int task = blockIdx.x; task < nB; task += gridDim.x) {
@@ -390,7 +414,8 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
         for (int kb = 0; kb < kFusedMaxIB; ++kb) {
             if (kb < IB) {
                 const v8i B = valid ? load32(a2_l + col * a2_stride + kb * 128 + kg * 32) : zero8();
-                const float sc = (valid ? a2s_l[col * IB + kb] : 0.0f) * Bsc[kb];
+                const float sc = (valid ? a2s_l[col * IB + kb] : 0.0f) *
+                                 __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Bsc_v), kb));
                 const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
                 const v4f blk = mfma_16x16x128_e4m3(Bw[kb], B, z);
 #pragma unroll
