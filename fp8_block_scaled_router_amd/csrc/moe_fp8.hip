@@ -46,11 +46,11 @@ struct Layout {
 };
 
 // Largest batch sent to the one-kernel decode path: it recomputes routing
-// and quantisation in every workgroup, which stops paying off above this
-// (measured on MI355X at h = 2048, i = 768, E = 128, k = 8: the two paths
-// tie near M = 8 with uniform routing; the multi-kernel path is 15% faster
-// at M = 12 with shared-bias routing).
-constexpr int kFusedPathMaxM = 8;
+// and quantisation in every workgroup and moves each step's results between
+// workgroups through memory, which stops paying off above this (measured on
+// MI355X at h = 2048, i = 768, E = 128, k = 8, uniform routing: one kernel
+// 38.6 / 47.1 / 55.0 us at M = 2 / 3 / 4, multi-kernel 44.5 / 47.8 / 50.3).
+constexpr int kFusedPathMaxM = 3;
 
 int choose_path(int M, int h, int i, int E, int k) {
     if (M <= kFusedPathMaxM && moe::fused_supported(M, h, i, E, k)) return MOE_FP8_PATH_FUSED_DECODE;

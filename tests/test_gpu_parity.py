@@ -383,18 +383,18 @@ def test_forward_bound_workspace(dev, moe_mod):
 
 def test_fused_path_m_sweep_and_shared_workspace(dev, moe_mod):
     """Small batches M = 1..16 through ONE workspace sized for the largest, in
-    a row: ragged M, the one-kernel path up to M = 8 and the multi-kernel
+    a row: ragged M, the one-kernel path up to M = 3 and the multi-kernel
     path above, and sync words that must come back clean after every forward
     whatever the previous shape was (only the one-kernel path advances the
     epoch tag)."""
     h, i, E, k = 2048, 768, 128, 8
     cfg16 = synth.LayerConfig("m16", 16, h, i, E, k, "normal", "sweep")
     big = Layer(cfg16, 777, dev)
-    assert moe_mod.workspace_layout(8, h, i, E, k).path == moe_mod.PATH_FUSED_DECODE
-    assert moe_mod.workspace_layout(9, h, i, E, k).path == moe_mod.PATH_STREAM
+    assert moe_mod.workspace_layout(3, h, i, E, k).path == moe_mod.PATH_FUSED_DECODE
+    assert moe_mod.workspace_layout(4, h, i, E, k).path == moe_mod.PATH_STREAM
     ws = moe_mod.alloc_workspace(16, h, i, E, k, device=dev)
     fused = 0
-    for M in (1, 2, 3, 5, 8, 13, 16, 1, 9, 4):
+    for M in (1, 2, 3, 5, 8, 13, 16, 1, 9, 4, 2):
         lay = moe_mod.workspace_layout(M, h, i, E, k)
         log(f"sweep M={M} path={lay.path}")
         cfg = synth.LayerConfig(f"m{M}", M, h, i, E, k, "normal", "sweep")
