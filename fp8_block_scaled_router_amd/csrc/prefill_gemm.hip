@@ -32,6 +32,8 @@
 // Workgroups are handed to XCDs round-robin; the tile order gives each XCD a
 // contiguous range of tiles, so the M-tiles of one expert (which share its
 // weights) meet in the same L2.
+#include <algorithm>
+
 #include "device.h"
 #include "launch.h"
 
@@ -74,11 +76,6 @@ __device__ __forceinline__ int lo_slot(int r, int kg) {
 __device__ __forceinline__ int chunk_of(int r, int p) {
     const int x = swz(r);
     return 2 * ((p & 3) ^ (x & 3)) + (((p ^ x) >> 2) & 1);
-}
-
-__device__ __forceinline__ int xcd_tile(int b, int nb) {
-    const int per = nb / 8;   // the grid is a multiple of 8
-    return (b % 8) * per + b / 8;
 }
 
 // Per-tile routing metadata, staged in LDS with one coalesced load so a
@@ -205,12 +202,17 @@ __device__ __forceinline__ void block_mma(v4f acc[16], const Loop& L, const uint
 // copies of block kb visible and certifies that every wave has finished
 // reading block kb - 1; only then are the copies of block kb + 2 issued, into
 // kb - 1's buffer, so two blocks are in flight while block kb is multiplied.
-// sw_of(kb, sw) fills the wave's four weight-tile scales of block kb.
+// sw_of(kb, sw) fills the wave's four weight-tile scales of block kb.  The
+// copies of blocks 0 and 1 (into buffers 0 and 1) are issued by the caller,
+// possibly long before (issue_first).
+__device__ __forceinline__ void issue_first(const Loop& L, int KB, uint8_t* stages) {
+    issue_stage(L, stages, 0);
+    if (KB > 1) issue_stage(L, stages + kStage, 1);
+}
+
 template <typename SwOf>
 __device__ __forceinline__ void k_loop(v4f acc[16], const Loop& L, int KB, uint8_t* stages, SwOf sw_of) {
     float sw[4];
-    issue_stage(L, stages, 0);
-    if (KB > 1) issue_stage(L, stages + kStage, 1);
     int rd = 0;   // stage buffer of block kb
     for (int kb = 0; kb < KB; ++kb) {
         if (kb + 1 < KB) __builtin_amdgcn_s_waitcnt(vm_wait(kVmemPerStage));
@@ -236,85 +238,86 @@ __device__ __forceinline__ void lane_geometry(Loop& L, int lane, int a_row0, int
     L.x_off = kAB + kBB + (b_row0 / 16) * 256 + col * 4;
 }
 
+// Both kernels are persistent: one workgroup per CU walks the tiles of its
+// XCD's contiguous share (tile t of share x goes to workgroup x + 8 c with
+// c = t mod (grid / 8)), so an expert's M-tiles still meet in one L2.  The
+// next tile's token list and weight scales are requested at the start of the
+// current tile's K loop, and the copies of its first two K blocks are issued
+// before the current tile's epilogue, which then runs in their shadow.
+struct TileSpan {
+    int next, end, step;   // tile walk of this workgroup
+};
+
+__device__ __forceinline__ TileSpan tile_span(int n_tiles) {
+    const int per_x = gridDim.x / 8, x = blockIdx.x % 8, c = blockIdx.x / 8;
+    const int P = (n_tiles + 7) / 8;
+    return TileSpan{x * P + c, min(n_tiles, (x + 1) * P), per_x};
+}
+
+struct TileInfo {
+    int mt, sub;   // M-tile and column group (gate/up) or row tile (down)
+    int e, beg, rows;
+};
+
+__device__ __forceinline__ TileInfo decode_tile(const TileMeta& meta, int E, int per_mt, int T) {
+    TileInfo t;
+    t.mt = T / per_mt;
+    t.sub = T - t.mt * per_mt;
+    t.e = __builtin_amdgcn_readfirstlane(tile_expert(meta.mtile_off, E, t.mt));
+    t.beg = __builtin_amdgcn_readfirstlane(meta.offsets[t.e] + (t.mt - meta.mtile_off[t.e]) * kBM);
+    t.rows = __builtin_amdgcn_readfirstlane(min(kBM, meta.offsets[t.e + 1] - t.beg));
+    return t;
+}
+
 }  // namespace
 
 // ----------------------------------------------------------------- gate/up
 
-__global__ __launch_bounds__(kThreads, 1) void prefill_gate_up_kernel(PrefillArgs a) {
-    __shared__ __align__(16) uint8_t stages[3 * kStage];
-    __shared__ int tok_l[kBM];
-    __shared__ float amax_l[4][kBM];
-    __shared__ float sw_l[2][kMaxKB];   // gate / up weight scales of group jg, per K block
-    __shared__ TileMeta meta;
+namespace {
 
-    const int h = a.h, i = a.i, E = a.E, k = a.k;
-    const int KB = h / 128, IB = i / 128, N13 = 2 * i;
-    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-    const int col = lane & 15, kg = lane >> 4;
-    const int wr = wave & 1, wn = wave >> 1;   // routes 64 wr .. +64; gate/up columns 32 wn .. +32
-
-    const int T = xcd_tile(blockIdx.x, gridDim.x);
-    const int mt = T / IB, jg = T - mt * IB;
-    load_meta(meta, a, tid);
-    __syncthreads();
-    if (mt >= meta.mtile_off[E]) return;
-    const int e = __builtin_amdgcn_readfirstlane(tile_expert(meta.mtile_off, E, mt));
-    const int beg = __builtin_amdgcn_readfirstlane(meta.offsets[e] + (mt - meta.mtile_off[e]) * kBM);
-    const int rows = __builtin_amdgcn_readfirstlane(min(kBM, meta.offsets[e + 1] - beg));
-
-    // padding rows repeat the tile's last route (their outputs are dropped)
-    for (int r = tid; r < kBM; r += kThreads) tok_l[r] = a.sorted[beg + min(r, rows - 1)] / k;
-    {
-        const float* sg = a.s13 + ((size_t)e * (N13 / 128) + jg) * KB;
-        const float* su = a.s13 + ((size_t)e * (N13 / 128) + IB + jg) * KB;
-        for (int j = tid; j < KB; j += kThreads) {
-            sw_l[0][j] = sg[j];
-            sw_l[1][j] = su[j];
-        }
-    }
-    __syncthreads();
-
-    // weight tiles: gate rows 32 wn + {0, 16}, up rows 128 + 32 wn + {0, 16};
-    // route tiles 64 wr + 16 m
+// Loop state of a gate/up tile whose token list is in tok (LDS).
+__device__ __forceinline__ Loop gate_up_loop(const PrefillArgs& a, const TileInfo& t, const int* tok, int wave,
+                                             int lane) {
+    const int h = a.h, i = a.i, KB = h / 128, N13 = 2 * i;
+    const int wr = wave & 1, wn = wave >> 1;
     Loop L;
-    lane_geometry(L, lane, 32 * wn, 64 * wr);
+    lane_geometry(L, lane, 32 * wn, 64 * wr);   // gate rows 32 wn + {0, 16}, up rows 128 + 32 wn + {0, 16}
     L.a_step[0] = 0;
     L.a_step[1] = 16 * 128;
     L.a_step[2] = 128 * 128;
     L.a_step[3] = 144 * 128;
     L.wave = wave;
-    L.gA = a.w13 + (size_t)e * N13 * h;
+    L.gA = a.w13 + (size_t)t.e * N13 * h;
     L.gB = a.xq;
     L.gX = a.xs;
 #pragma unroll
     for (int q = 0; q < kDmaA; ++q) {
         const int r = (wave * kDmaA + q) * 8 + (lane >> 3);
-        const int wrow = r < 128 ? jg * 128 + r : i + jg * 128 + (r - 128);
+        const int wrow = r < 128 ? t.sub * 128 + r : i + t.sub * 128 + (r - 128);
         L.offA[q] = (uint32_t)(wrow * h + chunk_of(r, lane & 7) * 16);
     }
 #pragma unroll
     for (int q = 0; q < kDmaB; ++q) {
         const int r = (wave * kDmaB + q) * 8 + (lane >> 3);
-        L.offB[q] = (uint32_t)(tok_l[r] * h + chunk_of(r, lane & 7) * 16);
+        L.offB[q] = (uint32_t)(tok[r] * h + chunk_of(r, lane & 7) * 16);
     }
-    L.offX = (uint32_t)(tok_l[16 * wave + (lane & 15)] * KB);
+    L.offX = (uint32_t)(tok[16 * wave + (lane & 15)] * KB);
+    return L;
+}
 
-    auto sw_of = [&](int kb, float sw[4]) {
-        const float g = sw_l[0][kb], u = sw_l[1][kb];
-        sw[0] = g; sw[1] = g; sw[2] = u; sw[3] = u;
-    };
-
-    v4f acc[16];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    k_loop(acc, L, KB, stages, sw_of);
-
-    // ---- epilogue: SiLU(gate) * up, 1x128 requantisation of group jg.
-    // Tile t = 4 j + m: weight tile j (gate j = 0, 1; up j = 2, 3), route
-    // tile m.  Lane: route 64 wr + 16 m + col; gate/up columns
-    // 32 wn + 16 j + 4 kg + v of group jg.  SiLU uses the hardware exp2 and
-    // reciprocal (a few ulp from the correctly rounded quotient; the FP8
-    // block sums feeding it carry far larger error).
+// Epilogue of a gate/up tile: SiLU(gate) * up and the 1x128 requantisation
+// of group t.sub.  Tile u = 4 j + m: weight tile j (gate j = 0, 1; up j = 2,
+// 3), route tile m.  Lane: route 64 wr + 16 m + col; gate/up columns
+// 32 wn + 16 j + 4 kg + v of the group.  SiLU uses the hardware exp2 and
+// reciprocal (a few ulp from the correctly rounded quotient; the FP8 block
+// sums feeding it carry far larger error).  The codes are staged in LDS
+// (codes, rows of 144 bytes so the 4-byte writes of 16 routes hit distinct
+// banks) and leave as whole 128-byte rows.
+__device__ __forceinline__ void gate_up_epilogue(const PrefillArgs& a, const TileInfo& t, v4f acc[16],
+                                                 float (*amax_l)[kBM], uint8_t* codes, int tid) {
+    const int i = a.i, IB = i / 128;
+    const int wave = tid >> 6, lane = tid & 63, col = lane & 15, kg = lane >> 4;
+    const int wr = wave & 1, wn = wave >> 1;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
         float pm = 0.0f;
@@ -332,10 +335,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_gate_up_kernel(PrefillArg
         if (kg == 0) amax_l[wn][64 * wr + 16 * m + col] = pm;
     }
     __syncthreads();
-    // codes go to a 128 x 128 tile in the (now idle) stage buffers, rows of
-    // 144 bytes so the 4-byte writes of 16 routes hit distinct banks, then
-    // leave as whole 128-byte rows
-    uint8_t* codes = stages;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
         const int r = 64 * wr + 16 * m + col;
@@ -348,59 +347,105 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_gate_up_kernel(PrefillArg
             *reinterpret_cast<uint32_t*>(codes + r * 144 + 32 * wn + 16 * j + 4 * kg) =
                 sc == 0.0f ? 0u : quant4(vv[0], vv[1], vv[2], vv[3], sc, rc);
         }
-        if (wn == 0 && kg == 0 && r < rows) a.a2s[(size_t)(beg + r) * IB + jg] = sc;
+        if (wn == 0 && kg == 0 && r < t.rows) a.a2s[(size_t)(t.beg + r) * IB + t.sub] = sc;
     }
     __syncthreads();
-    {
-        const int r = tid >> 2, c = (tid & 3) * 32;   // 4 threads per route row, 32 bytes each
-        if (r < rows) {
-            const uint4* src = reinterpret_cast<const uint4*>(codes + r * 144 + c);
-            uint4* dst = reinterpret_cast<uint4*>(a.a2 + (size_t)(beg + r) * i + jg * 128 + c);
-            dst[0] = src[0];
-            dst[1] = src[1];
+    const int r = tid >> 2, c = (tid & 3) * 32;   // 4 threads per route row, 32 bytes each
+    if (r < t.rows) {
+        const uint4* src = reinterpret_cast<const uint4*>(codes + r * 144 + c);
+        uint4* dst = reinterpret_cast<uint4*>(a.a2 + (size_t)(t.beg + r) * i + t.sub * 128 + c);
+        dst[0] = src[0];
+        dst[1] = src[1];
+    }
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(kThreads, 1) void prefill_gate_up_kernel(PrefillArgs a) {
+    __shared__ __align__(16) uint8_t stages[3 * kStage];
+    __shared__ int tok_l[2][kBM];               // token of each route row, per tile parity
+    __shared__ float amax_l[4][kBM];
+    __shared__ float sw_l[2][2][kMaxKB];        // gate / up weight scales per K block, per tile parity
+    __shared__ TileMeta meta;
+
+    const int h = a.h, i = a.i, E = a.E, k = a.k;
+    const int KB = h / 128, IB = i / 128, N13 = 2 * i;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+
+    load_meta(meta, a, tid);
+    __syncthreads();
+    TileSpan span = tile_span(meta.mtile_off[E] * IB);
+    if (span.next >= span.end) return;
+
+    auto scales = [&](const TileInfo& t, int j, int half) {
+        return a.s13[((size_t)t.e * (N13 / 128) + half * IB + t.sub) * KB + j];
+    };
+    TileInfo t = decode_tile(meta, E, IB, span.next);
+    int par = 0;
+    // padding rows repeat the tile's last route (their outputs are dropped)
+    for (int r = tid; r < kBM; r += kThreads) tok_l[0][r] = a.sorted[t.beg + min(r, t.rows - 1)] / k;
+    for (int j = tid; j < KB; j += kThreads) {
+        sw_l[0][0][j] = scales(t, j, 0);
+        sw_l[0][1][j] = scales(t, j, 1);
+    }
+    __syncthreads();
+    Loop L = gate_up_loop(a, t, tok_l[0], wave, lane);
+    issue_first(L, KB, stages);
+
+    for (;;) {
+        span.next += span.step;
+        const bool more = span.next < span.end;
+        TileInfo tn = t;
+        int tok_n = 0;
+        float sg_n = 0.0f, su_n = 0.0f;
+        if (more) {   // the next tile's lists, in flight during this tile's K loop
+            tn = decode_tile(meta, E, IB, span.next);
+            if (tid < kBM) tok_n = a.sorted[tn.beg + min(tid, tn.rows - 1)] / k;
+            if (tid < KB) {
+                sg_n = scales(tn, tid, 0);
+                su_n = scales(tn, tid, 1);
+            }
         }
+        auto sw_of = [&](int kb, float sw[4]) {
+            const float g = sw_l[par][0][kb], u = sw_l[par][1][kb];
+            sw[0] = g; sw[1] = g; sw[2] = u; sw[3] = u;
+        };
+        v4f acc[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) acc[u] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        k_loop(acc, L, KB, stages, sw_of);   // ends with every wave done with the stage buffers
+        if (more) {
+            if (tid < kBM) tok_l[par ^ 1][tid] = tok_n;
+            if (tid < KB) {
+                sw_l[par ^ 1][0][tid] = sg_n;
+                sw_l[par ^ 1][1][tid] = su_n;
+            }
+            __syncthreads();
+            L = gate_up_loop(a, tn, tok_l[par ^ 1], wave, lane);
+            issue_first(L, KB, stages);   // buffers 0 and 1; the epilogue stages codes in buffer 2
+        }
+        gate_up_epilogue(a, t, acc, amax_l, stages + 2 * kStage, tid);
+        if (!more) break;
+        t = tn;
+        par ^= 1;
     }
 }
 
 // -------------------------------------------------------------------- down
 
-__global__ __launch_bounds__(kThreads, 1) void prefill_down_kernel(PrefillArgs a) {
-    __shared__ __align__(16) uint8_t stages[3 * kStage];
-    __shared__ int prt_l[kBM];
-    __shared__ float sw_l[2][kMaxKB];   // weight scales of the tile's two 128-row blocks, per K block
-    __shared__ TileMeta meta;
+namespace {
 
-    const int h = a.h, i = a.i, E = a.E;
-    const int IB = i / 128, NT = h / kBN;
-    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-    const int col = lane & 15, kg = lane >> 4;
-    const int wr = wave & 1, wn = wave >> 1;   // routes 64 wr .. +64; output rows 64 wn .. +64
-
-    const int T = xcd_tile(blockIdx.x, gridDim.x);
-    const int mt = T / NT, nt = T - mt * NT;
-    load_meta(meta, a, tid);
-    __syncthreads();
-    if (mt >= meta.mtile_off[E]) return;
-    const int e = __builtin_amdgcn_readfirstlane(tile_expert(meta.mtile_off, E, mt));
-    const int beg = __builtin_amdgcn_readfirstlane(meta.offsets[e] + (mt - meta.mtile_off[e]) * kBM);
-    const int rows = __builtin_amdgcn_readfirstlane(min(kBM, meta.offsets[e + 1] - beg));
-
-    for (int r = tid; r < kBM; r += kThreads) prt_l[r] = r < rows ? a.sorted[beg + r] : -1;
-    {
-        const float* sb = a.s2 + ((size_t)e * (h / 128) + 2 * nt) * IB;   // blocks 2 nt, 2 nt + 1
-        for (int j = tid; j < 2 * IB; j += kThreads) sw_l[j / IB][j % IB] = sb[j];
-    }
-    __syncthreads();
-
-    // weight tiles: rows 64 wn + 16 j (scale block wn / 2); route tiles 64 wr + 16 m
+__device__ __forceinline__ Loop down_loop(const PrefillArgs& a, const TileInfo& t, int wave, int lane) {
+    const int h = a.h, i = a.i, IB = i / 128;
+    const int wr = wave & 1, wn = wave >> 1;
     Loop L;
-    lane_geometry(L, lane, 64 * wn, 64 * wr);
+    lane_geometry(L, lane, 64 * wn, 64 * wr);   // weight rows 64 wn + 16 j; route tiles 64 wr + 16 m
 #pragma unroll
     for (int j = 0; j < 4; ++j) L.a_step[j] = j * 16 * 128;
     L.wave = wave;
-    L.gA = a.w2 + ((size_t)e * h + (size_t)nt * kBN) * i;
-    L.gB = a.a2 + (size_t)beg * i;
-    L.gX = a.a2s + (size_t)beg * IB;
+    L.gA = a.w2 + ((size_t)t.e * h + (size_t)t.sub * kBN) * i;
+    L.gB = a.a2 + (size_t)t.beg * i;
+    L.gX = a.a2s + (size_t)t.beg * IB;
 #pragma unroll
     for (int q = 0; q < kDmaA; ++q) {
         const int r = (wave * kDmaA + q) * 8 + (lane >> 3);
@@ -409,34 +454,85 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_down_kernel(PrefillArgs a
 #pragma unroll
     for (int q = 0; q < kDmaB; ++q) {
         const int r = (wave * kDmaB + q) * 8 + (lane >> 3);
-        L.offB[q] = (uint32_t)(min(r, rows - 1) * i + chunk_of(r, lane & 7) * 16);   // padding repeats the last route
+        L.offB[q] = (uint32_t)(min(r, t.rows - 1) * i + chunk_of(r, lane & 7) * 16);   // padding repeats the last route
     }
-    L.offX = (uint32_t)(min(16 * wave + (lane & 15), rows - 1) * IB);
+    L.offX = (uint32_t)(min(16 * wave + (lane & 15), t.rows - 1) * IB);
+    return L;
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(kThreads, 1) void prefill_down_kernel(PrefillArgs a) {
+    __shared__ __align__(16) uint8_t stages[3 * kStage];
+    __shared__ int prt_l[2][kBM];               // route id of each row (-1: padding), per tile parity
+    __shared__ float sw_l[2][2][kMaxKB];        // the tile's two 128-row scale blocks, per tile parity
+    __shared__ TileMeta meta;
+
+    const int h = a.h, i = a.i, E = a.E;
+    const int IB = i / 128, NT = h / kBN;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int col = lane & 15, kg = lane >> 4;
+    const int wr = wave & 1, wn = wave >> 1;
+
+    load_meta(meta, a, tid);
+    __syncthreads();
+    TileSpan span = tile_span(meta.mtile_off[E] * NT);
+    if (span.next >= span.end) return;
+
+    auto scale = [&](const TileInfo& t, int j) {   // j < 2 IB: blocks 2 sub and 2 sub + 1
+        return a.s2[((size_t)t.e * (h / 128) + 2 * t.sub) * IB + j];
+    };
+    TileInfo t = decode_tile(meta, E, NT, span.next);
+    int par = 0;
+    for (int r = tid; r < kBM; r += kThreads) prt_l[0][r] = r < t.rows ? a.sorted[t.beg + r] : -1;
+    for (int j = tid; j < 2 * IB; j += kThreads) sw_l[0][j / IB][j % IB] = scale(t, j);
+    __syncthreads();
+    Loop L = down_loop(a, t, wave, lane);
+    issue_first(L, IB, stages);
 
     const int sblk = wn >> 1;
-    auto sw_of = [&](int kb, float sw[4]) {
-        const float w = sw_l[sblk][kb];
-        sw[0] = w; sw[1] = w; sw[2] = w; sw[3] = w;
-    };
-
-    v4f acc[16];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    k_loop(acc, L, IB, stages, sw_of);
-    __syncthreads();   // prt_l
-
-    // ---- epilogue: fp32 partial rows by route id; lane holds output rows
-    // nt * 256 + 64 wn + 16 j + 4 kg + v of route 64 wr + 16 m + col.
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const int p = prt_l[64 * wr + 16 * m + col];
-        if (p < 0) continue;
-        float* dst = a.y + (size_t)p * h + nt * kBN + 64 * wn + 4 * kg;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const v4f vv = acc[4 * j + m];
-            *reinterpret_cast<float4*>(dst + 16 * j) = make_float4(vv[0], vv[1], vv[2], vv[3]);
+    for (;;) {
+        span.next += span.step;
+        const bool more = span.next < span.end;
+        TileInfo tn = t;
+        int prt_n = -1;
+        float sw_n = 0.0f;
+        if (more) {
+            tn = decode_tile(meta, E, NT, span.next);
+            if (tid < kBM) prt_n = tid < tn.rows ? a.sorted[tn.beg + tid] : -1;
+            if (tid < 2 * IB) sw_n = scale(tn, tid);
         }
+        auto sw_of = [&](int kb, float sw[4]) {
+            const float w = sw_l[par][sblk][kb];
+            sw[0] = w; sw[1] = w; sw[2] = w; sw[3] = w;
+        };
+        v4f acc[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) acc[u] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        k_loop(acc, L, IB, stages, sw_of);
+        if (more) {
+            if (tid < kBM) prt_l[par ^ 1][tid] = prt_n;
+            if (tid < 2 * IB) sw_l[par ^ 1][tid / IB][tid % IB] = sw_n;
+            __syncthreads();
+            L = down_loop(a, tn, wave, lane);
+            issue_first(L, IB, stages);
+        }
+        // fp32 partial rows by route id; lane holds output rows
+        // sub * 256 + 64 wn + 16 j + 4 kg + v of route 64 wr + 16 m + col
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int p = prt_l[par][64 * wr + 16 * m + col];
+            if (p < 0) continue;
+            float* dst = a.y + (size_t)p * h + t.sub * kBN + 64 * wn + 4 * kg;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const v4f vv = acc[4 * j + m];
+                *reinterpret_cast<float4*>(dst + 16 * j) = make_float4(vv[0], vv[1], vv[2], vv[3]);
+            }
+        }
+        if (!more) break;
+        t = tn;
+        par ^= 1;
     }
 }
 
@@ -448,20 +544,31 @@ bool prefill_supported(int M, int h, int i, int k) {
            (int64_t)M * (h / 128) < lim;
 }
 
-static int round8(int v) { return (v + 7) / 8 * 8; }
-
-// Upper bound on the M-tiles of R routes over E experts: sum over experts of
-// ceil(count / 128) <= R / 128 + E.
-static int max_mtiles(int R, int E) { return R / kBM + E; }
+// One workgroup per CU (the grid must be a multiple of 8, one share per XCD).
+static int persistent_grid() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    static int cached[64] = {0};
+    if (dev < 0 || dev >= 64) return 0;
+    if (cached[dev] == 0) {
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cached[dev] = std::max(8, cus / 8 * 8);
+    }
+    return cached[dev];
+}
 
 hipError_t launch_prefill_gate_up(const PrefillArgs& a, int R, hipStream_t stream) {
-    const int g = round8(max_mtiles(R, a.E) * (a.i / 128));
+    (void)R;
+    const int g = persistent_grid();
+    if (g <= 0) return hipErrorInvalidDevice;
     hipLaunchKernelGGL(prefill_gate_up_kernel, dim3(g), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
 hipError_t launch_prefill_down(const PrefillArgs& a, int R, hipStream_t stream) {
-    const int g = round8(max_mtiles(R, a.E) * (a.h / kBN));
+    (void)R;
+    const int g = persistent_grid();
+    if (g <= 0) return hipErrorInvalidDevice;
     hipLaunchKernelGGL(prefill_down_kernel, dim3(g), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
