@@ -46,6 +46,7 @@ constexpr size_t kSyncBytes = 32768;
 constexpr size_t kSyncEpoch = 0;                // word: forwards run on this workspace
 constexpr size_t kSyncExit = 256;               // word: workgroups finished in this forward
 constexpr size_t kSyncErr = 512;                // word: sticky error (a wait timed out)
+constexpr size_t kSyncArrive = 1024;            // word: routing workgroups counted in (grouping tail)
 constexpr size_t kLLBytes = (size_t)8 << 20;    // g_ll (4 MiB) + y_ll (4 MiB)
 constexpr size_t kLLOffset = kSyncBytes;
 constexpr size_t kWorkspaceHead = kSyncBytes + kLLBytes;   // zero-initialised part

@@ -14,6 +14,15 @@ hipError_t launch_route_quant(const float* logits, const uint16_t* x, int M, int
                               int32_t* ids, float* tw, uint8_t* xq, float* xs, int what,
                               hipStream_t stream);
 
+// The same plus the grouping of all routes, in one launch, for batches of at
+// most kGroupTailRoutes routes; arrivals is a zero word that the launch
+// leaves at zero.
+constexpr int kGroupTailRoutes = 256;
+hipError_t launch_route_quant_group(const float* logits, const uint16_t* x, int M, int E, int k, int h,
+                                    int32_t* ids, float* tw, uint8_t* xq, float* xs, int32_t* counts,
+                                    int32_t* offsets, int32_t* sorted, int32_t* active,
+                                    int32_t* num_active, uint32_t* arrivals, hipStream_t stream);
+
 // Grouping of R routes by expert: per-chunk histograms, then an ordered
 // scatter.  `hist` holds group_chunks(R) * E ints.
 int group_chunks(int R);

@@ -106,17 +106,26 @@ int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 const char* const kStreamStages[] = {"route_quant_kernel", "group_hist+group_scatter",
                                      "stream_gate_up_kernel", "stream_down_kernel",
                                      "combine_kernel"};
+const char* const kStreamSmallStages[] = {"route_quant_group_kernel", "stream_gate_up_kernel",
+                                          "stream_down_kernel", "combine_kernel"};
 const char* const kFusedStages[] = {"fused_decode_kernel"};
 const char* const kPrefillStages[] = {"route_quant_kernel", "group_hist+group_scatter",
                                       "prefill_gate_up_kernel", "prefill_down_kernel",
                                       "combine_kernel"};
 
-int stage_count(int path) {
-    return path == MOE_FP8_PATH_FUSED_DECODE ? 1 : 5;
+// The streaming path routes, quantises and groups in one launch when the
+// batch has few enough routes.
+bool small_group(int M, int k) { return (int64_t)M * k <= moe::kGroupTailRoutes; }
+
+int stage_count(int path, int M, int k) {
+    if (path == MOE_FP8_PATH_FUSED_DECODE) return 1;
+    if (path == MOE_FP8_PATH_STREAM && small_group(M, k)) return 4;
+    return 5;
 }
-const char* stage_name(int path, int j) {
+const char* stage_name(int path, int M, int k, int j) {
     if (path == MOE_FP8_PATH_FUSED_DECODE) return kFusedStages[j];
     if (path == MOE_FP8_PATH_PREFILL) return kPrefillStages[j];
+    if (small_group(M, k)) return kStreamSmallStages[j];
     return kStreamStages[j];
 }
 
@@ -202,8 +211,14 @@ int run_forward(const void* x, const float* router_logits, const void* w13, cons
         MOE_STEP(moe::launch_fused_decode(fa, stream));
         return hook.mark() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
     }
-    MOE_STEP(moe::launch_route_quant(router_logits, static_cast<const uint16_t*>(x), M, E, k, h,
-                                     ids, tw, xq, xs, moe::kRoute | moe::kQuant, stream));
+    if (p.path == MOE_FP8_PATH_STREAM && small_group(M, k)) {
+        MOE_STEP(moe::launch_route_quant_group(router_logits, static_cast<const uint16_t*>(x), M, E, k, h,
+                                               ids, tw, xq, xs, counts, offsets, sorted, active,
+                                               num_active, sync + moe::kSyncArrive / 4, stream));
+    } else {
+        MOE_STEP(moe::launch_route_quant(router_logits, static_cast<const uint16_t*>(x), M, E, k, h,
+                                         ids, tw, xq, xs, moe::kRoute | moe::kQuant, stream));
+    }
     if (p.path == MOE_FP8_PATH_PREFILL) {
         MOE_STEP(moe::launch_group(ids, R, E, hist, counts, offsets, sorted, active, num_active,
                                    stream, moe::prefill_tile_m(), mtile_off));
@@ -229,8 +244,9 @@ int run_forward(const void* x, const float* router_logits, const void* w13, cons
         MOE_STEP(moe::launch_combine(y, tw, M, k, h, static_cast<uint16_t*>(out), stream));
         return hook.mark() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
     }
-    MOE_STEP(moe::launch_group(ids, R, E, hist, counts, offsets, sorted, active, num_active,
-                               stream));
+    if (!small_group(M, k))
+        MOE_STEP(moe::launch_group(ids, R, E, hist, counts, offsets, sorted, active, num_active,
+                                   stream));
     moe::StreamArgs sa;
     sa.offsets = offsets;
     sa.sorted = sorted;
@@ -317,13 +333,13 @@ int moe_fp8_forward_kernel_count(int M, int h, int i, int E, int k) {
     const int rc = check_shape(M, h, i, E, k);
     if (rc != MOE_OK) return rc;
     if (M == 0) return 0;
-    return stage_count(choose_path(M, h, i, E, k));
+    return stage_count(choose_path(M, h, i, E, k), M, k);
 }
 
 const char* moe_fp8_forward_kernel_name(int M, int h, int i, int E, int k, int j) {
     const int n = moe_fp8_forward_kernel_count(M, h, i, E, k);
     if (n <= 0 || j < 0 || j >= n) return nullptr;
-    return stage_name(choose_path(M, h, i, E, k), j);
+    return stage_name(choose_path(M, h, i, E, k), M, k, j);
 }
 
 size_t moe_fp8_workspace_head_bytes(void) { return moe::kWorkspaceHead; }

@@ -20,9 +20,11 @@
 
 namespace moe {
 
+// coherent: store the ids with device-coherent stores (read by another
+// workgroup of the same launch).
 __device__ __forceinline__ void router_wave(const float* __restrict__ l, int E, int k,
                                             int32_t* __restrict__ ids, float* __restrict__ w,
-                                            int lane) {
+                                            int lane, bool coherent = false) {
     uint32_t key[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -67,7 +69,8 @@ __device__ __forceinline__ void router_wave(const float* __restrict__ l, int E, 
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         if (r < k && lane == r) {
-            ids[r] = picked[r];
+            if (coherent) st_agent(reinterpret_cast<uint32_t*>(ids) + r, (uint32_t)picked[r]);
+            else ids[r] = picked[r];
             w[r] = ex[r] / sum;
         }
     }
@@ -121,6 +124,104 @@ hipError_t launch_route_quant(const float* logits, const uint16_t* x, int M, int
     if (M <= 0) return hipSuccess;
     hipLaunchKernelGGL(route_quant_kernel, dim3(M), dim3(256), 0, stream, logits, x, E, k, h, ids,
                        tw, xq, xs, what);
+    return hipGetLastError();
+}
+
+// Lanes holding the same expert id (9-bit ids; 0x1FF = no route).
+__device__ __forceinline__ uint64_t same_expert(int e) {
+    uint64_t same = ~0ull;
+#pragma unroll
+    for (int b = 0; b < 9; ++b) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t bal = __ballot(bit);
+        same &= bit ? bal : ~bal;
+    }
+    return same;
+}
+
+// Router, activation quantisation and grouping in one launch, for batches of
+// at most kGroupTailRoutes routes.  Each workgroup routes and quantises one
+// token; its ids go out with device-coherent stores, then it counts itself
+// in.  The last workgroup to arrive groups every route on one wave (ballot
+// matches give each route's rank inside its expert in route order, DPP
+// prefix sums the offsets and the active list) and resets the counter.  No
+// workgroup ever waits for another.
+__global__ __launch_bounds__(256) void route_quant_group_kernel(
+    const float* __restrict__ logits, const uint16_t* __restrict__ x, int E, int k, int h,
+    int32_t* __restrict__ ids, float* __restrict__ tw, uint8_t* __restrict__ xq, float* __restrict__ xs,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted,
+    int32_t* __restrict__ active, int32_t* __restrict__ num_active, uint32_t* arrivals) {
+    __shared__ int cnt_l[256];
+    __shared__ int last_l;
+    const int t = blockIdx.x, M = gridDim.x, R = M * k;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    if (wave == 0) router_wave(logits + (size_t)t * E, E, k, ids + (size_t)t * k, tw + (size_t)t * k, lane, true);
+    act_quant_row(x + (size_t)t * h, h, xq + (size_t)t * h, xs + (size_t)t * (h / 128), wave, 4, lane);
+    if (tid == 0) {
+        wait_vmem();   // this wave's id stores have completed
+        last_l = atomicAdd(arrivals, 1u) == (uint32_t)(M - 1);
+    }
+    __syncthreads();
+    if (!last_l || wave != 0) return;
+
+    for (int e = lane; e < E; e += 64) cnt_l[e] = 0;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int lr[4], ee[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        lr[b] = 0;
+        ee[b] = 0x1FF;
+        if (64 * b < R) {
+            const int p = 64 * b + lane;
+            const int e = p < R ? (int)ld_agent(reinterpret_cast<const uint32_t*>(ids) + p) : 0x1FF;
+            const uint64_t same = same_expert(e);
+            if (p < R) {
+                lr[b] = cnt_l[e] + __popcll(same & below);
+                ee[b] = e;
+                if ((same >> lane) == 1ull) cnt_l[e] += __popcll(same);
+            }
+        }
+    }
+    int c[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c[j] = (4 * lane + j < E) ? cnt_l[4 * lane + j] : 0;
+    const int lsum = c[0] + c[1] + c[2] + c[3];
+    const int lact = (c[0] > 0) + (c[1] > 0) + (c[2] > 0) + (c[3] > 0);
+    const int incl = wave_scan_incl(lsum);
+    const int iact = wave_scan_incl(lact);
+    int run = incl - lsum, arun = iact - lact;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = 4 * lane + j;
+        if (e < E) {
+            cnt_l[e] = run;   // becomes the offset
+            offsets[e] = run;
+            counts[e] = c[j];
+            if (c[j] > 0) active[arun] = e;
+        }
+        run += c[j];
+        arun += (c[j] > 0);
+    }
+    if (lane == 63) {
+        offsets[E] = incl;
+        *num_active = iact;
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const int p = 64 * b + lane;
+        if (p < R) sorted[cnt_l[ee[b]] + lr[b]] = p;
+    }
+    if (lane == 0) st_agent(arrivals, 0u);
+}
+
+hipError_t launch_route_quant_group(const float* logits, const uint16_t* x, int M, int E, int k, int h,
+                                    int32_t* ids, float* tw, uint8_t* xq, float* xs, int32_t* counts,
+                                    int32_t* offsets, int32_t* sorted, int32_t* active,
+                                    int32_t* num_active, uint32_t* arrivals, hipStream_t stream) {
+    if (M <= 0) return hipSuccess;
+    if ((int64_t)M * k > kGroupTailRoutes || E > 256) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(route_quant_group_kernel, dim3(M), dim3(256), 0, stream, logits, x, E, k, h, ids,
+                       tw, xq, xs, counts, offsets, sorted, active, num_active, arrivals);
     return hipGetLastError();
 }
 
