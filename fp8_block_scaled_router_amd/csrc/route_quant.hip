@@ -79,51 +79,59 @@ __device__ __forceinline__ void router_wave(const float* __restrict__ l, int E, 
 __device__ __forceinline__ void act_quant_row(const uint16_t* __restrict__ x, int K,
                                               uint8_t* __restrict__ q, float* __restrict__ s,
                                               int wave, int nwaves, int lane) {
+    // Each 16-lane row of a wave takes one 128-wide group per step; up to
+    // eight steps' loads are issued before any group is processed.
     const int G = K / 128;
     const int sub = lane & 15;
-    for (int g0 = wave * 4; g0 < G; g0 += nwaves * 4) {
-        const int g = g0 + (lane >> 4);
-        float v[8];
+    const int steps = (G + 4 * nwaves - 1) / (4 * nwaves);
+    for (int st0 = 0; st0 < steps; st0 += 8) {
+        uint4 u[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = 0.0f;
-        if (g < G) {
-            const uint4 u = *reinterpret_cast<const uint4*>(x + g * 128 + sub * 8);
-            v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x);
-            v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
-            v[4] = bf16_lo(u.z); v[5] = bf16_hi(u.z);
-            v[6] = bf16_lo(u.w); v[7] = bf16_hi(u.w);
+        for (int j = 0; j < 8; ++j) {
+            const int g = ((st0 + j) * nwaves + wave) * 4 + (lane >> 4);
+            u[j] = make_uint4(0u, 0u, 0u, 0u);
+            if (st0 + j < steps && g < G) u[j] = *reinterpret_cast<const uint4*>(x + g * 128 + sub * 8);
         }
-        float a = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(v[j]));
-        a = row16_max(a);
-        const float sc = a / kE4M3Max;
-        if (g < G) {
-            *reinterpret_cast<uint2*>(q + g * 128 + sub * 8) = quant8(v, sc);
-            if (sub == 0) s[g] = sc;
+        for (int j = 0; j < 8; ++j) {
+            if (st0 + j >= steps) break;
+            const int g = ((st0 + j) * nwaves + wave) * 4 + (lane >> 4);
+            float v[8] = {bf16_lo(u[j].x), bf16_hi(u[j].x), bf16_lo(u[j].y), bf16_hi(u[j].y),
+                          bf16_lo(u[j].z), bf16_hi(u[j].z), bf16_lo(u[j].w), bf16_hi(u[j].w)};
+            float a = 0.0f;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) a = fmaxf(a, fabsf(v[c]));
+            a = row16_max(a);
+            const float sc = a / kE4M3Max;
+            if (g < G) {
+                *reinterpret_cast<uint2*>(q + g * 128 + sub * 8) = quant8(v, sc);
+                if (sub == 0) s[g] = sc;
+            }
         }
     }
 }
 
+// One wave per token, four tokens per workgroup: the wave routes its token
+// and then quantises its row.
 __global__ __launch_bounds__(256) void route_quant_kernel(
-    const float* __restrict__ logits, const uint16_t* __restrict__ x, int E, int k, int h,
+    const float* __restrict__ logits, const uint16_t* __restrict__ x, int M, int E, int k, int h,
     int32_t* __restrict__ ids, float* __restrict__ tw, uint8_t* __restrict__ xq,
     float* __restrict__ xs, int what) {
-    const int t = blockIdx.x;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    if ((what & kRoute) && wave == 0)
+    const int t = blockIdx.x * 4 + wave;
+    if (t >= M) return;
+    if (what & kRoute)
         router_wave(logits + (size_t)t * E, E, k, ids + (size_t)t * k, tw + (size_t)t * k, lane);
     if (what & kQuant)
-        act_quant_row(x + (size_t)t * h, h, xq + (size_t)t * h, xs + (size_t)t * (h / 128), wave, 4,
-                      lane);
+        act_quant_row(x + (size_t)t * h, h, xq + (size_t)t * h, xs + (size_t)t * (h / 128), 0, 1, lane);
 }
 
 hipError_t launch_route_quant(const float* logits, const uint16_t* x, int M, int E, int k, int h,
                               int32_t* ids, float* tw, uint8_t* xq, float* xs, int what,
                               hipStream_t stream) {
     if (M <= 0) return hipSuccess;
-    hipLaunchKernelGGL(route_quant_kernel, dim3(M), dim3(256), 0, stream, logits, x, E, k, h, ids,
-                       tw, xq, xs, what);
+    hipLaunchKernelGGL(route_quant_kernel, dim3((M + 3) / 4), dim3(256), 0, stream, logits, x, M, E, k, h,
+                       ids, tw, xq, xs, what);
     return hipGetLastError();
 }
 

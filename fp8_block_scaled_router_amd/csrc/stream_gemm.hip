@@ -199,14 +199,25 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     const int t = blockIdx.y;
     const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (n >= h) return;
+    // every rank's partial is requested before the rank-order sum starts
+    float4 v[16];
+    float w[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        if (r < k) {
+            w[r] = tw[(size_t)t * k + r];
+            v[r] = *reinterpret_cast<const float4*>(y + ((size_t)t * k + r) * h + n);
+        }
+    }
     float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
-    for (int r = 0; r < k; ++r) {
-        const float w = tw[(size_t)t * k + r];
-        const float4 v = *reinterpret_cast<const float4*>(y + ((size_t)t * k + r) * h + n);
-        a0 = a0 + w * v.x;
-        a1 = a1 + w * v.y;
-        a2 = a2 + w * v.z;
-        a3 = a3 + w * v.w;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        if (r < k) {
+            a0 = a0 + w[r] * v[r].x;
+            a1 = a1 + w[r] * v[r].y;
+            a2 = a2 + w[r] * v[r].z;
+            a3 = a3 + w[r] * v[r].w;
+        }
     }
     *reinterpret_cast<uint2*>(out + (size_t)t * h + n) = make_uint2(bf16x2(a0, a1), bf16x2(a2, a3));
 }
