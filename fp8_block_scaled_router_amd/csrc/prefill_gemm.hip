@@ -23,7 +23,8 @@
 //    all banks (see lo_slot).
 //  * Promotion with the two block scales (Netra Kernel README, capability
 //    table: explicit 128x128 block scales): acc += blk * (s_w * s_act) in
-//    fp32, issued four MFMAs after the MFMA that produced blk.
+//    fp32, one K block after the MFMA that produced blk, so the promotion
+//    arithmetic never waits on an MFMA result.
 // gate/up's epilogue computes SiLU(gate) * up and its 1x128 E4M3
 // requantisation on the spot (Netra Kernel README, MoE prefill pair) and
 // writes codes in sorted-route order; down writes fp32 partial rows by route
@@ -50,7 +51,6 @@ constexpr int kStage = kAB + kBB + kXS;
 constexpr int kDmaA = kAB / 1024 / 8;         // 1 KiB copies per wave per stage
 constexpr int kDmaB = kBB / 1024 / 8;
 constexpr int kVmemPerStage = kDmaA + kDmaB + 1;   // + one copy of 16 route scales
-constexpr int kLag = 4;                       // promotion trails its MFMA
 constexpr int kMaxKB = 128;                   // weight-scale table: K blocks (h <= 16384)
 
 static_assert(kDmaA == 4 && kDmaB == 2, "stage copy split");
@@ -166,9 +166,14 @@ __device__ __forceinline__ void issue_stage(const Loop& L, uint8_t* st, int kb) 
     copy4_to_lds(L.gX + L.offX + kb, base + kAB + kBB + L.wave * 256);
 }
 
-// One K block on one wave: 4 weight tiles x 4 route tiles, promotion of tile
-// (j, m) with sw[j] * (activation scale of route tile m).
-__device__ __forceinline__ void block_mma(v4f acc[16], const Loop& L, const uint8_t* st, const float sw[4]) {
+// One K block on one wave: 4 weight tiles x 4 route tiles.  The raw block
+// products of the previous K block (blk, with per-tile scales sw_p[j] *
+// xr_p[m]) are promoted into acc just before the MFMA that overwrites them,
+// so no promotion waits on the MFMA that has just been issued; this block's
+// scales are handed back in sw_p / xr_p for the next call (before the first
+// block, blk and the scales are zero, so that promotion adds zeros).
+__device__ __forceinline__ void block_mma(v4f acc[16], v4f blk[16], float sw_p[4], float xr_p[4], const Loop& L,
+                                          const uint8_t* st, const float sw[4]) {
     v8i A[4], B[4];
     float xr[4];
 #pragma unroll
@@ -177,22 +182,17 @@ __device__ __forceinline__ void block_mma(v4f acc[16], const Loop& L, const uint
     for (int j = 0; j < 4; ++j) A[j] = frag(st + L.a_lo + L.a_step[j], st + L.a_hi + L.a_step[j]);
 #pragma unroll
     for (int m = 0; m < 4; ++m) xr[m] = *reinterpret_cast<const float*>(st + L.x_off + m * 256);
-    // tile t's product lands in ring[t % kLag]; it is promoted just before
-    // the MFMA of tile t + kLag reuses that slot
-    v4f ring[kLag];
 #pragma unroll
-    for (int t = 0; t < 16 + kLag; ++t) {
-        if (t >= kLag) {
-            const int u = t - kLag;
-            const float sc = sw[u >> 2] * xr[u & 3];
+    for (int t = 0; t < 16; ++t) {
+        const float sc = sw_p[t >> 2] * xr_p[t & 3];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc[u][v] = fmaf(ring[u % kLag][v], sc, acc[u][v]);
-            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-        }
-        if (t < 16) {
-            ring[t % kLag] = mfma_16x16x128_e4m3(A[t >> 2], B[t & 3], v4f{0.0f, 0.0f, 0.0f, 0.0f});
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        }
+        for (int v = 0; v < 4; ++v) acc[t][v] = fmaf(blk[t][v], sc, acc[t][v]);
+        blk[t] = mfma_16x16x128_e4m3(A[t >> 2], B[t & 3], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        sw_p[j] = sw[j];
+        xr_p[j] = xr[j];
     }
 }
 
@@ -212,7 +212,10 @@ __device__ __forceinline__ void issue_first(const Loop& L, int KB, uint8_t* stag
 
 template <typename SwOf>
 __device__ __forceinline__ void k_loop(v4f acc[16], const Loop& L, int KB, uint8_t* stages, SwOf sw_of) {
-    float sw[4];
+    float sw[4], sw_p[4] = {0.0f, 0.0f, 0.0f, 0.0f}, xr_p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    v4f blk[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) blk[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     int rd = 0;   // stage buffer of block kb
     for (int kb = 0; kb < KB; ++kb) {
         if (kb + 1 < KB) __builtin_amdgcn_s_waitcnt(vm_wait(kVmemPerStage));
@@ -220,10 +223,16 @@ __device__ __forceinline__ void k_loop(v4f acc[16], const Loop& L, int KB, uint8
         block_barrier();
         if (kb + 2 < KB) issue_stage(L, stages + (rd == 0 ? 2 : rd - 1) * kStage, kb + 2);
         sw_of(kb, sw);
-        block_mma(acc, L, stages + rd * kStage, sw);
+        block_mma(acc, blk, sw_p, xr_p, L, stages + rd * kStage, sw);
         rd = rd == 2 ? 0 : rd + 1;
     }
     block_barrier();   // every wave is done with the stage buffers
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {   // promotion of the last block
+        const float sc = sw_p[t >> 2] * xr_p[t & 3];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[t][v] = fmaf(blk[t][v], sc, acc[t][v]);
+    }
 }
 
 // Fragment read offsets of this lane: row col of a 16-row tile, K group kg;
