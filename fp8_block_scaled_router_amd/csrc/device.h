@@ -158,6 +158,10 @@ __device__ __forceinline__ uint32_t float_order_key(float v) {
     uint32_t u = __float_as_uint(v);
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+// Inverse of float_order_key (for a key of +-0 it returns +0).
+__device__ __forceinline__ float float_from_order_key(uint32_t key) {
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
 
 // ------------------------------------------- exchange between workgroups
 //

@@ -47,12 +47,6 @@ constexpr int kQuarters = 4;                // A task: 32 gate + 32 up rows
 constexpr int kDownRows = 64;               // B task rows
 constexpr uint64_t kWaitTicks = 100000000;  // 1 s of the 100 MHz constant clock
 
-// Inverse of float_order_key (for a key of +-0 it returns +0).
-__device__ __forceinline__ float key_to_float(uint32_t key) {
-    const uint32_t u = (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key;
-    return __uint_as_float(u);
-}
-
 __device__ __forceinline__ uint32_t readlane_u(uint32_t v, int lane) {
     return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
 }
@@ -89,7 +83,7 @@ __device__ __forceinline__ void route_fast(const float lg[4], int E, int k, int*
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             if (lane + 64 * j == e) key[j] = 0u;
-        const float lv = key_to_float(smax);
+        const float lv = float_from_order_key(smax);
         if (r == 0) l0 = lv;
         if (lane == r) {
             my_pick = e;

@@ -6,7 +6,7 @@
 // LDS atomic increments (an integer count does not depend on their order).
 // Pass 2: one wave per chunk derives every expert's global offset and its
 // chunk-local start from the chunk histograms, then scatters the chunk's
-// routes in route order, 64 at a time: a lane's rank among equal experts in
+// routes in route order, 64 at a time (ids requested 16 batches ahead): a lane's rank among equal experts in
 // its batch comes from a ballot match over the 9 bits of the expert id, so
 // the sorted order is route id ascending inside each expert by construction.
 // Chunk 0 also writes counts, offsets, the ascending list of experts that
@@ -55,21 +55,26 @@ __global__ __launch_bounds__(64) void group_scatter_kernel(
     __shared__ int base[256];
     const int chunk = blockIdx.x;
     const int lane = threadIdx.x;
-    // Lane l owns experts 4l .. 4l+3.
-    int tot[4], pre[4];
+    // Lane l owns experts 4l .. 4l+3; the histograms of 8 chunks are
+    // requested together, so the prefix costs one memory round trip per 8
+    // chunks instead of one per chunk.
+    int tot[4] = {0, 0, 0, 0}, pre[4] = {0, 0, 0, 0};
+    for (int c0 = 0; c0 < nchunks; c0 += 8) {
+        int v[8][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int e = 4 * lane + j;
-        int s = 0, p = 0;
-        if (e < E) {
-            for (int c = 0; c < nchunks; ++c) {
-                const int v = hist[(size_t)c * E + e];
-                if (c < chunk) p += v;
-                s += v;
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int e = 4 * lane + j, c = c0 + u;
+                v[u][j] = (e < E && c < nchunks) ? hist[(size_t)c * E + e] : 0;
             }
-        }
-        tot[j] = s;
-        pre[j] = p;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (c0 + u < chunk) pre[j] += v[u][j];
+                tot[j] += v[u][j];
+            }
     }
     const int lsum = tot[0] + tot[1] + tot[2] + tot[3];
     const int lact = (tot[0] > 0) + (tot[1] > 0) + (tot[2] > 0) + (tot[3] > 0);
@@ -112,28 +117,40 @@ __global__ __launch_bounds__(64) void group_scatter_kernel(
     const int beg = chunk * kChunk;
     const int end = min(R, beg + kChunk);
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int p0 = beg; p0 < end; p0 += 64) {
-        const int p = p0 + lane;
-        int e = p < end ? ids[p] : 0x1FF;
-        const bool valid = (unsigned)e < (unsigned)E;
-        if (!valid) e = 0x1FF;
-        uint64_t same = ~0ull;
+    // the ids of 16 batches are requested together
+    for (int q0 = beg; q0 < end; q0 += 16 * 64) {
+        int ev[16];
 #pragma unroll
-        for (int b = 0; b < 9; ++b) {
-            const bool bit = (e >> b) & 1;
-            const uint64_t bal = __ballot(bit);
-            same &= bit ? bal : ~bal;
+        for (int u = 0; u < 16; ++u) {
+            const int p = q0 + 64 * u + lane;
+            ev[u] = p < end ? ids[p] : 0x1FF;
         }
-        const int rank = __popcll(same & below);
-        const bool last = (same >> lane) == 1ull;   // highest lane of its expert in this batch
-        int pos = 0;
-        if (valid) pos = base[e] + rank;
-        __syncthreads();
-        if (valid) {
-            sorted[pos] = p;
-            if (last) base[e] += __popcll(same);
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int p0 = q0 + 64 * u;
+            if (p0 >= end) break;
+            const int p = p0 + lane;
+            int e = ev[u];
+            const bool valid = (unsigned)e < (unsigned)E;
+            if (!valid) e = 0x1FF;
+            uint64_t same = ~0ull;
+#pragma unroll
+            for (int b = 0; b < 9; ++b) {
+                const bool bit = (e >> b) & 1;
+                const uint64_t bal = __ballot(bit);
+                same &= bit ? bal : ~bal;
+            }
+            const int rank = __popcll(same & below);
+            const bool last = (same >> lane) == 1ull;   // highest lane of its expert in this batch
+            int pos = 0;
+            if (valid) pos = base[e] + rank;
+            __syncthreads();
+            if (valid) {
+                sorted[pos] = p;
+                if (last) base[e] += __popcll(same);
+            }
+            __syncthreads();
         }
-        __syncthreads();
     }
 }
 

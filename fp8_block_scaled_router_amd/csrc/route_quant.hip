@@ -32,9 +32,11 @@ __device__ __forceinline__ void router_wave(const float* __restrict__ l, int E, 
         key[j] = (e < E) ? float_order_key(l[e]) : 0u;
     }
     int picked[16];
+    float pl[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         picked[r] = 0;
+        pl[r] = 0.0f;
         if (r < k) {
             uint32_t hi = 0u, lo = 0u;
 #pragma unroll
@@ -51,18 +53,19 @@ __device__ __forceinline__ void router_wave(const float* __restrict__ l, int E, 
             for (int j = 0; j < 4; ++j)
                 if (lane + 64 * j == e) key[j] = 0u;
             picked[r] = e;
+            pl[r] = float_from_order_key(hi);   // the pick's logit (-0 comes back as +0)
         }
     }
     // Renormalised softmax weights of the picks; every lane computes the same
     // rank-order sum, lane r stores weight r.
-    const float lmax = l[picked[0]];
+    const float lmax = pl[0];
     float ex[16];
     float sum = 0.0f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         ex[r] = 0.0f;
         if (r < k) {
-            ex[r] = expf(l[picked[r]] - lmax);
+            ex[r] = expf(pl[r] - lmax);
             sum += ex[r];
         }
     }
@@ -76,39 +79,61 @@ __device__ __forceinline__ void router_wave(const float* __restrict__ l, int E, 
     }
 }
 
+// Each 16-lane row of a wave takes one 128-wide group per step; the loads of
+// kQuantBatch steps (from step st0) are issued before any group is processed.
+constexpr int kQuantBatch = 4;
+__device__ __forceinline__ int act_quant_steps(int K, int nwaves) { return (K / 128 + 4 * nwaves - 1) / (4 * nwaves); }
+
+__device__ __forceinline__ void act_quant_load(const uint16_t* __restrict__ x, int K, int st0, int wave, int nwaves,
+                                               int lane, uint4 u[kQuantBatch]) {
+    const int G = K / 128, steps = act_quant_steps(K, nwaves), sub = lane & 15;
+#pragma unroll
+    for (int j = 0; j < kQuantBatch; ++j) {
+        const int g = ((st0 + j) * nwaves + wave) * 4 + (lane >> 4);
+        u[j] = make_uint4(0u, 0u, 0u, 0u);
+        if (st0 + j < steps && g < G) u[j] = *reinterpret_cast<const uint4*>(x + g * 128 + sub * 8);
+    }
+}
+
+__device__ __forceinline__ void act_quant_process(int K, uint8_t* __restrict__ q, float* __restrict__ s, int st0,
+                                                  int wave, int nwaves, int lane, const uint4 u[kQuantBatch]) {
+    const int G = K / 128, steps = act_quant_steps(K, nwaves), sub = lane & 15;
+#pragma unroll
+    for (int j = 0; j < kQuantBatch; ++j) {
+        if (st0 + j >= steps) break;
+        const int g = ((st0 + j) * nwaves + wave) * 4 + (lane >> 4);
+        float v[8] = {bf16_lo(u[j].x), bf16_hi(u[j].x), bf16_lo(u[j].y), bf16_hi(u[j].y),
+                      bf16_lo(u[j].z), bf16_hi(u[j].z), bf16_lo(u[j].w), bf16_hi(u[j].w)};
+        float a = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) a = fmaxf(a, fabsf(v[c]));
+        a = row16_max(a);
+        const float sc = a / kE4M3Max;
+        if (g < G) {
+            *reinterpret_cast<uint2*>(q + g * 128 + sub * 8) = quant8(v, sc);
+            if (sub == 0) s[g] = sc;
+        }
+    }
+}
+
+// Quantise the rest of a row whose first kQuantBatch steps' loads are in u.
+__device__ __forceinline__ void act_quant_finish(const uint16_t* __restrict__ x, int K, uint8_t* __restrict__ q,
+                                                 float* __restrict__ s, int wave, int nwaves, int lane,
+                                                 uint4 u[kQuantBatch]) {
+    const int steps = act_quant_steps(K, nwaves);
+    act_quant_process(K, q, s, 0, wave, nwaves, lane, u);
+    for (int st0 = kQuantBatch; st0 < steps; st0 += kQuantBatch) {
+        act_quant_load(x, K, st0, wave, nwaves, lane, u);
+        act_quant_process(K, q, s, st0, wave, nwaves, lane, u);
+    }
+}
+
 __device__ __forceinline__ void act_quant_row(const uint16_t* __restrict__ x, int K,
                                               uint8_t* __restrict__ q, float* __restrict__ s,
                                               int wave, int nwaves, int lane) {
-    // Each 16-lane row of a wave takes one 128-wide group per step; up to
-    // eight steps' loads are issued before any group is processed.
-    const int G = K / 128;
-    const int sub = lane & 15;
-    const int steps = (G + 4 * nwaves - 1) / (4 * nwaves);
-    for (int st0 = 0; st0 < steps; st0 += 8) {
-        uint4 u[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int g = ((st0 + j) * nwaves + wave) * 4 + (lane >> 4);
-            u[j] = make_uint4(0u, 0u, 0u, 0u);
-            if (st0 + j < steps && g < G) u[j] = *reinterpret_cast<const uint4*>(x + g * 128 + sub * 8);
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if (st0 + j >= steps) break;
-            const int g = ((st0 + j) * nwaves + wave) * 4 + (lane >> 4);
-            float v[8] = {bf16_lo(u[j].x), bf16_hi(u[j].x), bf16_lo(u[j].y), bf16_hi(u[j].y),
-                          bf16_lo(u[j].z), bf16_hi(u[j].z), bf16_lo(u[j].w), bf16_hi(u[j].w)};
-            float a = 0.0f;
-#pragma unroll
-            for (int c = 0; c < 8; ++c) a = fmaxf(a, fabsf(v[c]));
-            a = row16_max(a);
-            const float sc = a / kE4M3Max;
-            if (g < G) {
-                *reinterpret_cast<uint2*>(q + g * 128 + sub * 8) = quant8(v, sc);
-                if (sub == 0) s[g] = sc;
-            }
-        }
-    }
+    uint4 u[kQuantBatch];
+    act_quant_load(x, K, 0, wave, nwaves, lane, u);
+    act_quant_finish(x, K, q, s, wave, nwaves, lane, u);
 }
 
 // One wave per token, four tokens per workgroup: the wave routes its token
@@ -163,8 +188,10 @@ __global__ __launch_bounds__(256) void route_quant_group_kernel(
     __shared__ int last_l;
     const int t = blockIdx.x, M = gridDim.x, R = M * k;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    uint4 u[kQuantBatch];   // the row's first loads are in flight while wave 0 routes
+    act_quant_load(x + (size_t)t * h, h, 0, wave, 4, lane, u);
     if (wave == 0) router_wave(logits + (size_t)t * E, E, k, ids + (size_t)t * k, tw + (size_t)t * k, lane, true);
-    act_quant_row(x + (size_t)t * h, h, xq + (size_t)t * h, xs + (size_t)t * (h / 128), wave, 4, lane);
+    act_quant_finish(x + (size_t)t * h, h, xq + (size_t)t * h, xs + (size_t)t * (h / 128), wave, 4, lane, u);
     if (tid == 0) {
         wait_vmem();   // this wave's id stores have completed
         last_l = atomicAdd(arrivals, 1u) == (uint32_t)(M - 1);

@@ -200,23 +200,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (n >= h) return;
     // every rank's partial is requested before the rank-order sum starts
-    float4 v[16];
+    v4f v[16];   // streaming loads: every partial is read once
     float w[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         if (r < k) {
             w[r] = tw[(size_t)t * k + r];
-            v[r] = *reinterpret_cast<const float4*>(y + ((size_t)t * k + r) * h + n);
+            v[r] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(y + ((size_t)t * k + r) * h + n));
         }
     }
     float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         if (r < k) {
-            a0 = a0 + w[r] * v[r].x;
-            a1 = a1 + w[r] * v[r].y;
-            a2 = a2 + w[r] * v[r].z;
-            a3 = a3 + w[r] * v[r].w;
+            a0 = a0 + w[r] * v[r][0];
+            a1 = a1 + w[r] * v[r][1];
+            a2 = a2 + w[r] * v[r][2];
+            a3 = a3 + w[r] * v[r][3];
         }
     }
     *reinterpret_cast<uint2*>(out + (size_t)t * h + n) = make_uint2(bf16x2(a0, a1), bf16x2(a2, a3));
