@@ -51,7 +51,7 @@ constexpr int kStage = kAB + kBB + kXS;
 constexpr int kDmaA = kAB / 1024 / 8;         // 1 KiB copies per wave per stage
 constexpr int kDmaB = kBB / 1024 / 8;
 constexpr int kVmemPerStage = kDmaA + kDmaB + 1;   // + one copy of 16 route scales
-constexpr int kMaxKB = 128;                   // weight-scale table: K blocks (h <= 16384)
+constexpr int kMaxKB = 128;                   // scale tables: K blocks (h, i <= 16384)
 
 static_assert(kDmaA == 4 && kDmaB == 2, "stage copy split");
 
@@ -210,8 +210,11 @@ __device__ __forceinline__ void issue_first(const Loop& L, int KB, uint8_t* stag
     if (KB > 1) issue_stage(L, stages + kStage, 1);
 }
 
-template <typename SwOf>
-__device__ __forceinline__ void k_loop(v4f acc[16], const Loop& L, int KB, uint8_t* stages, SwOf sw_of) {
+// after_first() runs once, right after the first barrier: every wave has
+// then finished whatever it did before the loop.
+template <typename SwOf, typename AfterFirst>
+__device__ __forceinline__ void k_loop(v4f acc[16], const Loop& L, int KB, uint8_t* stages, SwOf sw_of,
+                                       AfterFirst after_first) {
     float sw[4], sw_p[4] = {0.0f, 0.0f, 0.0f, 0.0f}, xr_p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     v4f blk[16];
 #pragma unroll
@@ -222,6 +225,7 @@ __device__ __forceinline__ void k_loop(v4f acc[16], const Loop& L, int KB, uint8
         else __builtin_amdgcn_s_waitcnt(vm_wait(0));
         block_barrier();
         if (kb + 2 < KB) issue_stage(L, stages + (rd == 0 ? 2 : rd - 1) * kStage, kb + 2);
+        if (kb == 0) after_first();
         sw_of(kb, sw);
         block_mma(acc, blk, sw_p, xr_p, L, stages + rd * kStage, sw);
         rd = rd == 2 ? 0 : rd + 1;
@@ -285,7 +289,8 @@ __device__ __forceinline__ TileInfo decode_tile(const TileMeta& meta, int E, int
 namespace {
 
 // Loop state of a gate/up tile whose token list is in tok (LDS).
-__device__ __forceinline__ Loop gate_up_loop(const PrefillArgs& a, const TileInfo& t, const int* tok, int wave,
+// rt: the tile's route ids by row (padding rows repeat the last route).
+__device__ __forceinline__ Loop gate_up_loop(const PrefillArgs& a, const TileInfo& t, const int* rt, int wave,
                                              int lane) {
     const int h = a.h, i = a.i, KB = h / 128, N13 = 2 * i;
     const int wr = wave & 1, wn = wave >> 1;
@@ -308,9 +313,9 @@ __device__ __forceinline__ Loop gate_up_loop(const PrefillArgs& a, const TileInf
 #pragma unroll
     for (int q = 0; q < kDmaB; ++q) {
         const int r = (wave * kDmaB + q) * 8 + (lane >> 3);
-        L.offB[q] = (uint32_t)(tok[r] * h + chunk_of(r, lane & 7) * 16);
+        L.offB[q] = (uint32_t)(rt[r] / a.k * h + chunk_of(r, lane & 7) * 16);
     }
-    L.offX = (uint32_t)(tok[16 * wave + (lane & 15)] * KB);
+    L.offX = (uint32_t)(rt[16 * wave + (lane & 15)] / a.k * KB);
     return L;
 }
 
@@ -372,7 +377,7 @@ __device__ __forceinline__ void gate_up_epilogue(const PrefillArgs& a, const Til
 
 __global__ __launch_bounds__(kThreads, 1) void prefill_gate_up_kernel(PrefillArgs a) {
     __shared__ __align__(16) uint8_t stages[3 * kStage];
-    __shared__ int tok_l[2][kBM];               // token of each route row, per tile parity
+    __shared__ int rt_l[2][kBM];                // route id of each row, per tile parity
     __shared__ float amax_l[4][kBM];
     __shared__ float sw_l[2][2][kMaxKB];        // gate / up weight scales per K block, per tile parity
     __shared__ TileMeta meta;
@@ -392,29 +397,38 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_gate_up_kernel(PrefillArg
     TileInfo t = decode_tile(meta, E, IB, span.next);
     int par = 0;
     // padding rows repeat the tile's last route (their outputs are dropped)
-    for (int r = tid; r < kBM; r += kThreads) tok_l[0][r] = a.sorted[t.beg + min(r, t.rows - 1)] / k;
+    for (int r = tid; r < kBM; r += kThreads) rt_l[0][r] = a.sorted[t.beg + min(r, t.rows - 1)];
     for (int j = tid; j < KB; j += kThreads) {
         sw_l[0][0][j] = scales(t, j, 0);
         sw_l[0][1][j] = scales(t, j, 1);
     }
     __syncthreads();
-    Loop L = gate_up_loop(a, t, tok_l[0], wave, lane);
+    Loop L = gate_up_loop(a, t, rt_l[0], wave, lane);
     issue_first(L, KB, stages);
 
     for (;;) {
         span.next += span.step;
         const bool more = span.next < span.end;
         TileInfo tn = t;
-        int tok_n = 0;
-        float sg_n = 0.0f, su_n = 0.0f;
-        if (more) {   // the next tile's lists, in flight during this tile's K loop
-            tn = decode_tile(meta, E, IB, span.next);
-            if (tid < kBM) tok_n = a.sorted[tn.beg + min(tid, tn.rows - 1)] / k;
-            if (tid < KB) {
-                sg_n = scales(tn, tid, 0);
-                su_n = scales(tn, tid, 1);
+        if (more) tn = decode_tile(meta, E, IB, span.next);
+        // The next tile's route ids (waves 0, 1) and gate / up scales (waves
+        // 2, 3) are copied straight into the other parity's LDS lists during
+        // this tile's K loop (once its first barrier shows that no wave still
+        // reads them), and its last wait and barrier also cover these copies.
+        // No register receives them, so the tile loop carries no load the
+        // compiler would wait for.
+        auto next_lists = [&]() {
+            if (!more) return;
+            if (wave < 2) {
+                const int r = 64 * wave + lane;
+                copy4_to_lds(a.sorted + tn.beg + min(r, tn.rows - 1), lds_addr(&rt_l[par ^ 1][64 * wave]));
+            } else if (wave < 4) {
+                const int half = wave - 2;
+                const float* src = a.s13 + ((size_t)tn.e * (N13 / 128) + half * IB + tn.sub) * KB;
+                for (int c = 0; 64 * c < KB; ++c)
+                    copy4_to_lds(src + min(64 * c + lane, KB - 1), lds_addr(&sw_l[par ^ 1][half][64 * c]));
             }
-        }
+        };
         auto sw_of = [&](int kb, float sw[4]) {
             const float g = sw_l[par][0][kb], u = sw_l[par][1][kb];
             sw[0] = g; sw[1] = g; sw[2] = u; sw[3] = u;
@@ -422,15 +436,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_gate_up_kernel(PrefillArg
         v4f acc[16];
 #pragma unroll
         for (int u = 0; u < 16; ++u) acc[u] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-        k_loop(acc, L, KB, stages, sw_of);   // ends with every wave done with the stage buffers
+        k_loop(acc, L, KB, stages, sw_of, next_lists);   // ends with every wave done with the stage buffers
         if (more) {
-            if (tid < kBM) tok_l[par ^ 1][tid] = tok_n;
-            if (tid < KB) {
-                sw_l[par ^ 1][0][tid] = sg_n;
-                sw_l[par ^ 1][1][tid] = su_n;
-            }
-            __syncthreads();
-            L = gate_up_loop(a, tn, tok_l[par ^ 1], wave, lane);
+            L = gate_up_loop(a, tn, rt_l[par ^ 1], wave, lane);
             issue_first(L, KB, stages);   // buffers 0 and 1; the epilogue stages codes in buffer 2
         }
         gate_up_epilogue(a, t, acc, amax_l, stages + 2 * kStage, tid);
@@ -473,8 +481,8 @@ __device__ __forceinline__ Loop down_loop(const PrefillArgs& a, const TileInfo& 
 
 __global__ __launch_bounds__(kThreads, 1) void prefill_down_kernel(PrefillArgs a) {
     __shared__ __align__(16) uint8_t stages[3 * kStage];
-    __shared__ int prt_l[2][kBM];               // route id of each row (-1: padding), per tile parity
-    __shared__ float sw_l[2][2][kMaxKB];        // the tile's two 128-row scale blocks, per tile parity
+    __shared__ int prt_l[2][kBM];               // route id of each row (padding repeats the last), per tile parity
+    __shared__ float sw_l[2][2 * kMaxKB];       // the tile's two 128-row scale blocks, per tile parity
     __shared__ TileMeta meta;
 
     const int h = a.h, i = a.i, E = a.E;
@@ -493,8 +501,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_down_kernel(PrefillArgs a
     };
     TileInfo t = decode_tile(meta, E, NT, span.next);
     int par = 0;
-    for (int r = tid; r < kBM; r += kThreads) prt_l[0][r] = r < t.rows ? a.sorted[t.beg + r] : -1;
-    for (int j = tid; j < 2 * IB; j += kThreads) sw_l[0][j / IB][j % IB] = scale(t, j);
+    for (int r = tid; r < kBM; r += kThreads) prt_l[0][r] = a.sorted[t.beg + min(r, t.rows - 1)];
+    for (int j = tid; j < 2 * IB; j += kThreads) sw_l[0][j] = scale(t, j);
     __syncthreads();
     Loop L = down_loop(a, t, wave, lane);
     issue_first(L, IB, stages);
@@ -504,25 +512,29 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_down_kernel(PrefillArgs a
         span.next += span.step;
         const bool more = span.next < span.end;
         TileInfo tn = t;
-        int prt_n = -1;
-        float sw_n = 0.0f;
-        if (more) {
-            tn = decode_tile(meta, E, NT, span.next);
-            if (tid < kBM) prt_n = tid < tn.rows ? a.sorted[tn.beg + tid] : -1;
-            if (tid < 2 * IB) sw_n = scale(tn, tid);
-        }
+        if (more) tn = decode_tile(meta, E, NT, span.next);
+        // the next tile's lists, copied straight into LDS as in the gate/up
+        // kernel (the previous tile's epilogue read this parity's route list)
+        auto next_lists = [&]() {
+            if (!more) return;
+            if (wave < 2) {
+                const int r = 64 * wave + lane;
+                copy4_to_lds(a.sorted + tn.beg + min(r, tn.rows - 1), lds_addr(&prt_l[par ^ 1][64 * wave]));
+            } else if (64 * (wave - 2) < 2 * IB) {
+                const int c = wave - 2;
+                const float* src = a.s2 + ((size_t)tn.e * (h / 128) + 2 * tn.sub) * IB;
+                copy4_to_lds(src + min(64 * c + lane, 2 * IB - 1), lds_addr(&sw_l[par ^ 1][64 * c]));
+            }
+        };
         auto sw_of = [&](int kb, float sw[4]) {
-            const float w = sw_l[par][sblk][kb];
+            const float w = sw_l[par][sblk * IB + kb];
             sw[0] = w; sw[1] = w; sw[2] = w; sw[3] = w;
         };
         v4f acc[16];
 #pragma unroll
         for (int u = 0; u < 16; ++u) acc[u] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-        k_loop(acc, L, IB, stages, sw_of);
+        k_loop(acc, L, IB, stages, sw_of, next_lists);
         if (more) {
-            if (tid < kBM) prt_l[par ^ 1][tid] = prt_n;
-            if (tid < 2 * IB) sw_l[par ^ 1][tid / IB][tid % IB] = sw_n;
-            __syncthreads();
             L = down_loop(a, tn, wave, lane);
             issue_first(L, IB, stages);
         }
@@ -530,8 +542,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_down_kernel(PrefillArgs a
         // sub * 256 + 64 wn + 16 j + 4 kg + v of route 64 wr + 16 m + col
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const int p = prt_l[par][64 * wr + 16 * m + col];
-            if (p < 0) continue;
+            const int row = 64 * wr + 16 * m + col;
+            if (row >= t.rows) continue;
+            const int p = prt_l[par][row];
             float* dst = a.y + (size_t)p * h + t.sub * kBN + 64 * wn + 4 * kg;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -549,8 +562,8 @@ int prefill_tile_m() { return kBM; }
 
 bool prefill_supported(int M, int h, int i, int k) {
     const int64_t lim = (int64_t)1 << 31;   // 32-bit per-lane offsets
-    return h % kBN == 0 && i % 128 == 0 && (int64_t)M * h < lim && (int64_t)M * k * i < lim &&
-           (int64_t)M * (h / 128) < lim;
+    return h % kBN == 0 && i % 128 == 0 && h <= 128 * kMaxKB && i <= 128 * kMaxKB && (int64_t)M * h < lim &&
+           (int64_t)M * k * i < lim && (int64_t)M * (h / 128) < lim;
 }
 
 // One workgroup per CU (the grid must be a multiple of 8, one share per XCD).
