@@ -136,17 +136,75 @@ __device__ __forceinline__ void act_quant_row(const uint16_t* __restrict__ x, in
     act_quant_finish(x, K, q, s, wave, nwaves, lane, u);
 }
 
-// One wave per token, four tokens per workgroup: the wave routes its token
-// and then quantises its row.
-__global__ __launch_bounds__(256) void route_quant_kernel(
+// Router of four tokens on one wave: DPP row r (16 lanes) routes token
+// t0 + r, lane j of a row holding the logits of experts j, j + 16, ...
+// A pick is the row-wide maximum of the same 64-bit key as in router_wave,
+// reduced by four DPP steps inside the row, so a round costs no cross-row
+// exchange and a quarter of router_wave's lanes per token.  The pick's logit
+// is the same in every lane of the row, so each round adds its exponential
+// to the rank-order sum right away; lane j keeps pick j.
+__device__ __forceinline__ void router_rows16(const float* __restrict__ logits, int t0, int M, int E, int k,
+                                              int32_t* __restrict__ ids, float* __restrict__ w, int lane) {
+    const int r = lane >> 4, j = lane & 15, t = t0 + r;
+    const bool live = t < M;
+    const float* l = logits + (size_t)(live ? t : t0) * E;
+    const int nq = (E + 15) >> 4;   // logits per lane (uniform)
+    uint32_t key[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int e = j + 16 * q;
+        key[q] = (q < nq && e < E) ? float_order_key(l[e]) : 0u;
+    }
+    int my_e = 0;
+    float lmax = 0.0f, sum = 0.0f, my_ex = 0.0f;
+    for (int rr = 0; rr < k; ++rr) {
+        uint32_t hi = 0u, lo = 0u;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            if (q < nq && key[q] > hi) {   // strict: lower q (lower expert) wins ties
+                hi = key[q];
+                lo = 0xFFFFu - (uint32_t)(j + 16 * q);
+            }
+        }
+        key_step_dpp<kDppQuadXor1>(hi, lo);
+        key_step_dpp<kDppQuadXor2>(hi, lo);
+        key_step_dpp<kDppRowHalfMirror>(hi, lo);
+        key_step_dpp<kDppRowMirror>(hi, lo);
+        int e = (int)(0xFFFFu - lo);
+        e = (hi == 0u || e >= E) ? E - 1 : e;   // only for NaN logits (outside the contract)
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+            if (j + 16 * q == e) key[q] = 0u;
+        const float lv = float_from_order_key(hi);
+        if (rr == 0) lmax = lv;
+        const float ex = expf(lv - lmax);
+        sum += ex;
+        if (j == rr) {
+            my_e = e;
+            my_ex = ex;
+        }
+    }
+    if (live && j < k) {
+        ids[(size_t)t * k + j] = my_e;
+        w[(size_t)t * k + j] = my_ex / sum;
+    }
+}
+
+// Four tokens per workgroup of five waves: wave 4 routes the four tokens
+// (router_rows16) while waves 0-3 quantise one row each.
+constexpr int kRouteQuantThreads = 5 * kWave;
+__global__ __launch_bounds__(kRouteQuantThreads) void route_quant_kernel(
     const float* __restrict__ logits, const uint16_t* __restrict__ x, int M, int E, int k, int h,
     int32_t* __restrict__ ids, float* __restrict__ tw, uint8_t* __restrict__ xq,
     float* __restrict__ xs, int what) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + wave;
+    const int t0 = blockIdx.x * 4;
+    if (wave == 4) {
+        if (what & kRoute) router_rows16(logits, t0, M, E, k, ids, tw, lane);
+        return;
+    }
+    const int t = t0 + wave;
     if (t >= M) return;
-    if (what & kRoute)
-        router_wave(logits + (size_t)t * E, E, k, ids + (size_t)t * k, tw + (size_t)t * k, lane);
     if (what & kQuant)
         act_quant_row(x + (size_t)t * h, h, xq + (size_t)t * h, xs + (size_t)t * (h / 128), 0, 1, lane);
 }
@@ -155,7 +213,7 @@ hipError_t launch_route_quant(const float* logits, const uint16_t* x, int M, int
                               int32_t* ids, float* tw, uint8_t* xq, float* xs, int what,
                               hipStream_t stream) {
     if (M <= 0) return hipSuccess;
-    hipLaunchKernelGGL(route_quant_kernel, dim3((M + 3) / 4), dim3(256), 0, stream, logits, x, M, E, k, h,
+    hipLaunchKernelGGL(route_quant_kernel, dim3((M + 3) / 4), dim3(kRouteQuantThreads), 0, stream, logits, x, M, E, k, h,
                        ids, tw, xq, xs, what);
     return hipGetLastError();
 }
