@@ -111,10 +111,34 @@ __device__ __forceinline__ void key_step_dpp(uint32_t& hi, uint32_t& lo) {
     key_max(hi, lo, ohi, olo);
 }
 
-__device__ __forceinline__ void key_step_xor(uint32_t& hi, uint32_t& lo, int mask) {
-    uint32_t ohi = (uint32_t)__shfl_xor((int)hi, mask, kWave);
-    uint32_t olo = (uint32_t)__shfl_xor((int)lo, mask, kWave);
-    key_max(hi, lo, ohi, olo);
+// gfx950 row swaps with both operands v: for every lane, the two halves of
+// the result are v of rows (2q, 2q + 1) (permlane16) or of rows (q, q + 2)
+// (permlane32) at the lane's position, so one VALU instruction (no LDS
+// crossbar) gives each lane its partner row's value.
+__device__ __forceinline__ void key_step_rows16(uint32_t& hi, uint32_t& lo) {
+    const auto h = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    const auto l = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    hi = h[0];
+    lo = l[0];
+    key_max(hi, lo, h[1], l[1]);
+}
+__device__ __forceinline__ void key_step_rows32(uint32_t& hi, uint32_t& lo) {
+    const auto h = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    const auto l = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    hi = h[0];
+    lo = l[0];
+    key_max(hi, lo, h[1], l[1]);
+}
+// Max of v over lanes l, l ^ 16 (and l ^ 32) for v >= 0 (amax reductions).
+__device__ __forceinline__ float xor16_max(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float xor32_max(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
 
 // Inclusive prefix sum over the 64 lanes, DPP only: shifts of 1, 2, 4, 8
@@ -140,14 +164,14 @@ __device__ __forceinline__ uint32_t row16_max_u(uint32_t v) {
 }
 
 // Wave-wide lexicographic max of 64-bit keys: DPP inside each row of 16
-// lanes, then two cross-row exchanges.  Every lane gets the result.
+// lanes, then the two row swaps.  Every lane gets the result.
 __device__ __forceinline__ void wave_key_max(uint32_t& hi, uint32_t& lo) {
     key_step_dpp<kDppQuadXor1>(hi, lo);
     key_step_dpp<kDppQuadXor2>(hi, lo);
     key_step_dpp<kDppRowHalfMirror>(hi, lo);
     key_step_dpp<kDppRowMirror>(hi, lo);
-    key_step_xor(hi, lo, 16);
-    key_step_xor(hi, lo, 32);
+    key_step_rows16(hi, lo);
+    key_step_rows32(hi, lo);
 }
 
 // Order-preserving map of an fp32 value to an unsigned key; -0 and +0 map to

@@ -344,8 +344,8 @@ __device__ __forceinline__ void gate_up_epilogue(const PrefillArgs& a, const Til
                 acc[4 * j + m][v] = val;
                 pm = fmaxf(pm, fabsf(val));
             }
-        pm = fmaxf(pm, __shfl_xor(pm, 16, kWave));
-        pm = fmaxf(pm, __shfl_xor(pm, 32, kWave));
+        pm = xor16_max(pm);
+        pm = xor32_max(pm);
         if (kg == 0) amax_l[wn][64 * wr + 16 * m + col] = pm;
     }
     __syncthreads();

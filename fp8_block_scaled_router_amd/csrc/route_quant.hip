@@ -361,8 +361,8 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const float* __restri
         a = fmaxf(a, fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w))));
     }
     a = row16_max(a);
-    a = fmaxf(a, __shfl_xor(a, 16, kWave));
-    a = fmaxf(a, __shfl_xor(a, 32, kWave));
+    a = xor16_max(a);
+    a = xor32_max(a);
     __shared__ float part[4];
     if ((tid & 63) == 0) part[tid >> 6] = a;
     __syncthreads();
