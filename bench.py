@@ -11,10 +11,10 @@ Timing: the forwards of C rotation copies (distinct weight copies and
 inputs, together far larger than the 256 MB Infinity Cache, so every step
 streams its experts from HBM) are captured in one HIP graph; W warm-up steps,
 then exactly K timed steps between a synchronisation and HIP events on both
-sides.  A second pass launches the same forwards with HIP events recorded
-between their stages (queued behind a spin kernel so the events bracket
-execution only) and reports the dominant stage's mean duration against its
-roofline.  The CPU baseline is the oracle (plain C, all host
+sides.  A second pass times graph replays of the same forwards cut after
+their first j stages (j = 1..n, HIP events around the replays); the
+differences give each stage's mean duration, and the dominant stage is
+reported against its roofline.  The CPU baseline is the oracle (plain C, all host
 threads) on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -47,6 +47,13 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 3 plain device-to-device copies of MIB MiB (counter calibration) and exit")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="rocprofv3 --pmc output folders of FETCH_SIZE / WRITE_SIZE runs of a workload and of "
+                         "the copy calibration: record the kernel's HBM bytes per launch in profiles/traffic.json")
+    ap.add_argument("--pmc-kernel", default=None, help="kernel for --pmc-summary")
+    ap.add_argument("--pmc-copy-mib", type=int, default=1024, help="copy size of the calibration runs")
     return ap.parse_args()
 
 
@@ -54,6 +61,83 @@ def weight_bytes_per_expert(cfg):
     w13 = 2 * cfg.i * cfg.h + (2 * cfg.i // 128) * (cfg.h // 128) * 4
     w2 = cfg.h * cfg.i + (cfg.h // 128) * (cfg.i // 128) * 4
     return w13, w2
+
+
+# Sources whose text decides each measured kernel (traffic records are tied
+# to their digest).
+KERNEL_SOURCES = {
+    "fused_decode_kernel": ["fp8_block_scaled_router_amd/csrc/fused_decode.hip",
+                            "fp8_block_scaled_router_amd/csrc/fused_decode.h",
+                            "fp8_block_scaled_router_amd/csrc/device.h"],
+    "stream_gate_up_kernel": ["fp8_block_scaled_router_amd/csrc/stream_gemm.hip",
+                              "fp8_block_scaled_router_amd/csrc/device.h"],
+    "prefill_gate_up_kernel": ["fp8_block_scaled_router_amd/csrc/prefill_gemm.hip",
+                               "fp8_block_scaled_router_amd/csrc/device.h",
+                               "fp8_block_scaled_router_amd/csrc/launch.h"],
+}
+KERNEL_SOURCES["stream_down_kernel"] = KERNEL_SOURCES["stream_gate_up_kernel"]
+KERNEL_SOURCES["prefill_down_kernel"] = KERNEL_SOURCES["prefill_gate_up_kernel"]
+
+
+def copy_calibration(mib):
+    """Three plain device-to-device copies of a known size: rocprofv3's
+    FETCH_SIZE / WRITE_SIZE of these dispatches calibrate the counters."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "copies": 3}))
+
+
+def pmc_mean_kb(folder, name_prefix, largest_grid=False):
+    """Mean Counter_Value (KiB) over the dispatches of one kernel in a
+    rocprofv3 --pmc CSV folder (largest grid only, if asked)."""
+    import csv
+    import glob
+    rows = []
+    for path in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            if r["Kernel_Name"].startswith(name_prefix):
+                rows.append((int(r["Grid_Size"]), float(r["Counter_Value"])))
+    if not rows:
+        raise SystemExit(f"no dispatch of {name_prefix} in {folder}")
+    if largest_grid:
+        g = max(r[0] for r in rows)
+        rows = [r for r in rows if r[0] == g]
+    return sum(v for _, v in rows) / len(rows), len(rows)
+
+
+def pmc_summary(args):
+    fetch_dir, write_dir, cfetch_dir, cwrite_dir = args.pmc_summary
+    kernel = args.pmc_kernel
+    import synth
+    cfg = synth.CONFIGS[args.config]
+    copy_bytes = args.pmc_copy_mib << 20
+    cf, ncf = pmc_mean_kb(cfetch_dir, "__amd_rocclr_copyBuffer", largest_grid=True)
+    cw, ncw = pmc_mean_kb(cwrite_dir, "__amd_rocclr_copyBuffer", largest_grid=True)
+    f_scale, w_scale = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    fk, nf = pmc_mean_kb(fetch_dir, f"moe::{kernel}(")
+    wk, nw = pmc_mean_kb(write_dir, f"moe::{kernel}(")
+    fetch, write = fk * 1024 * f_scale, wk * 1024 * w_scale
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    db = json.load(open(path)) if os.path.exists(path) else {}
+    srcs = KERNEL_SOURCES[kernel]
+    db[f"{cfg.name}:{kernel}"] = {
+        "bytes_per_launch": int(round(fetch + write)),
+        "fetch_bytes_per_launch": int(round(fetch)), "write_bytes_per_launch": int(round(write)),
+        "raw_fetch_kib": round(fk, 1), "raw_write_kib": round(wk, 1), "dispatches": [nf, nw],
+        "copy_calibration": {"bytes": copy_bytes, "fetch_kib": round(cf, 1), "write_kib": round(cw, 1),
+                             "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)},
+        "sources": srcs, "source_sha256_16": source_digest(srcs),
+    }
+    with open(path, "w") as f:
+        json.dump(db, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(db[f"{cfg.name}:{kernel}"]))
 
 
 def stage_work(cfg, stage, U):
@@ -73,7 +157,7 @@ def stage_work(cfg, stage, U):
     if stage.startswith("route_quant"):
         return M * h * 2 + M * cfg.E * 4 + act + M * k * 8, 0.0
     if stage.startswith("combine"):
-        return M * h * 2 + M * k * 4, 0.0
+        return M * k * h * 4 + M * h * 2 + M * k * 4, 0.0   # fp32 partials in, bf16 out
     if stage.startswith("fused"):
         return U * (w13 + w2) + M * h * 2 * 2 + M * cfg.E * 4, 6.0 * M * k * h * i
     return 0, 0.0
@@ -104,6 +188,12 @@ def load_traffic(kernel, workload):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+    if args.pmc_summary:
+        pmc_summary(args)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "the layer is not sharded across GPUs", file=sys.stderr)
@@ -202,32 +292,46 @@ def main():
     ms_per_step = total_ms / args.steps
     tokens_per_s = M / (ms_per_step / 1e3)
 
-    # ---- per-stage durations from HIP events between the stages
+    # ---- per-stage durations: HIP-graph replays of the C forwards cut after
+    # their first j stages (j = 1..n), timed by HIP events on the launch
+    # stream; stage j's duration is T(j) - T(j - 1) per forward.  No event
+    # sits between stages, so a short stage is not charged the event's own
+    # cost, and the stages run back to back as in the timed steps.  The
+    # replays wait behind a GPU spin kernel while the host queues them.
     names = moe.forward_kernel_names(M, h, i, E, k)
     nst = len(names)
-    evs = [moe.HipEvents(nst + 1) for _ in range(C)]
 
-    def fwd_timed(c):
-        a = W[c]
-        moe.moe_fp8_forward_ws_timed(X[c], Lg[c], a[0], a[1], a[2], a[3], k, WS[c], evs[c], out=OUT[c])
+    def capture_prefix(j):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for c in range(C):
+                a = W[c]
+                moe.moe_fp8_forward_ws_prefix(X[c], Lg[c], a[0], a[1], a[2], a[3], k, WS[c], j, out=OUT[c])
+        return g
 
-    # Events recorded inside a captured graph cannot be queried on this
-    # runtime, so the stages are launched eagerly behind a GPU spin kernel:
-    # the host enqueues every stage and event before the GPU reaches them, so
-    # each event pair brackets one stage's execution, not host latency.
-    sums = np.zeros(nst)
-    count = 0
-    for _ in range(args.timing_replays):
+    reps = max(1, args.timing_replays)
+    T = [0.0]
+    for j in range(1, nst + 1):
+        gj = g_all if j == nst else capture_prefix(j)
+        gj.replay()
         torch.cuda.synchronize()
-        torch.cuda._sleep(5_000_000)
-        for c in range(C):
-            fwd_timed(c)
+        # the replays are queued behind a GPU spin, so that a short prefix
+        # is timed on the GPU, not at the host's launch rate
+        torch.cuda._sleep(20_000_000)
+        e0.record()
+        for _ in range(reps):
+            gj.replay()
+        e1.record()
         torch.cuda.synchronize()
-        for c in range(C):
-            sums += [evs[c].elapsed_ms(j, j + 1) for j in range(nst)]
-        count += C
-    timing_mode = "eager behind a spin kernel"
-    stage_ms = sums / count
+        T.append(e0.elapsed_time(e1) / (reps * C))
+        if gj is not g_all:
+            del gj
+    stage_ms = np.maximum(np.diff(np.array(T)), 0.0)
+    count = reps * C
+    timing_mode = "HIP-graph replays of forwards cut after each stage, differences"
+    # the full forwards leave every copy's output complete again
+    run_steps(C)
+    torch.cuda.synchronize()
     dom = int(np.argmax(stage_ms))
     U_mean = float(np.mean(U))
     abytes, aflops = stage_work(cfg, names[dom], U_mean)
@@ -245,9 +349,7 @@ def main():
                 "avg_launch_us": round(stage_ms[dom] * 1e3, 3),
                 "algorithmic_bytes_per_launch": int(abytes),
                 "algorithmic_flops_per_launch": aflops,
-                "timing": f"HIP events between stages, {timing_mode} replay, {count} launches"}
-    for ev in evs:
-        ev.close()
+                "timing": f"{timing_mode}, {count} forwards per cut"}
 
     # ---- CPU baseline: the oracle on a bounded sample of the same workload
     cpu = None

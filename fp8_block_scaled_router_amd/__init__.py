@@ -65,6 +65,7 @@ _SIGS = {
     "moe_fp8_quantize_weight_block128": (_I, [_P, _I64, _I, _I, _P, _P, _P]),
     "moe_fp8_encode_e4m3": (_I, [_P, _I64, _P, _P]),
     "moe_fp8_forward_ws_timed": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _SZ, _P, _I, _P]),
+    "moe_fp8_forward_ws_prefix": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _SZ, _I, _P]),
     "moe_fp8_forward_kernel_count": (_I, [_I, _I, _I, _I, _I]),
     "moe_fp8_forward_kernel_name": (ctypes.c_char_p, [_I, _I, _I, _I, _I, _I]),
     "moe_fp8_workspace_init": (_I, [_P, _SZ, _P]),
@@ -289,6 +290,18 @@ class HipEvents:
             if self.handles[j]:
                 self._hip.hipEventDestroy(self.handles[j])
                 self.handles[j] = None
+
+
+def moe_fp8_forward_ws_prefix(x, router_logits, w13, s13, w2, s2, k: int, workspace, n_stages: int,
+                              out=None, stream=None):
+    """moe_fp8_forward_ws cut after its first n_stages stages (measurement)."""
+    M, h, i, E, out = _layer_args(x, router_logits, w13, s13, w2, s2, k, out)
+    _dev(workspace, torch.uint8, "workspace")
+    rc = lib().moe_fp8_forward_ws_prefix(_ptr(x), _ptr(router_logits), _ptr(w13), _ptr(s13), _ptr(w2),
+                                         _ptr(s2), _ptr(out), M, h, i, E, int(k), _ptr(workspace),
+                                         workspace.numel(), int(n_stages), _stream(stream))
+    _check(rc, "moe_fp8_forward_ws_prefix")
+    return out
 
 
 def moe_fp8_forward_ws_timed(x, router_logits, w13, s13, w2, s2, k: int, workspace, events: HipEvents,

@@ -130,21 +130,26 @@ const char* stage_name(int path, int M, int k, int j) {
 }
 
 // Records events[j] (when given) before stage j, and events[n] after the last.
+// Stage bookkeeping of one forward: an optional event before every stage
+// and after the last, and an optional cut after `limit` stages.
 struct EventHook {
     hipEvent_t* ev;
     int n;
     int next = 0;
     hipStream_t s;
+    int limit = 1 << 30;
+    int stage = 0;
     hipError_t mark() {
         if (!ev || next >= n) return hipSuccess;
         return hipEventRecord(ev[next++], s);
     }
+    bool cut() { return stage++ >= limit; }
 };
 
 int run_forward(const void* x, const float* router_logits, const void* w13, const float* s13,
                 const void* w2, const float* s2, void* out, int M, int h, int i, int E, int k,
                 void* workspace, size_t workspace_bytes, hipEvent_t* events, int n_events,
-                hipStream_t stream) {
+                hipStream_t stream, int n_stages = 1 << 30) {
     int rc = check_shape(M, h, i, E, k);
     if (rc != MOE_OK) return rc;
     if (M == 0) return MOE_OK;
@@ -172,11 +177,12 @@ int run_forward(const void* x, const float* router_logits, const void* w13, cons
     float* g = p.path == MOE_FP8_PATH_STREAM ? at<float>(workspace, p.gate_up) : nullptr;
     float* y = p.path != MOE_FP8_PATH_FUSED_DECODE ? at<float>(workspace, p.partial) : nullptr;
     int32_t* mtile_off = at<int32_t>(workspace, L.mtile_off);
-    EventHook hook{events, n_events, 0, stream};
+    EventHook hook{events, n_events, 0, stream, n_stages};
     uint32_t* sync = at<uint32_t>(workspace, 0);
 
 #define MOE_STEP(call)                                      \
     do {                                                    \
+        if (hook.cut()) return MOE_OK;                      \
         if (hook.mark() != hipSuccess) return MOE_ERR_HIP; \
         rc = hip_status(call);                              \
         if (rc != MOE_OK) return rc;                        \
@@ -327,6 +333,17 @@ int moe_fp8_forward_ws_timed(const void* x, const float* router_logits, const vo
     if (n_events < n + 1) return MOE_ERR_INVALID;
     return run_forward(x, router_logits, w13, s13, w2, s2, out, M, h, i, E, k, workspace,
                        workspace_bytes, events, n_events, stream);
+}
+
+int moe_fp8_forward_ws_prefix(const void* x, const float* router_logits, const void* w13,
+                              const float* s13, const void* w2, const float* s2, void* out, int M,
+                              int h, int i, int E, int k, void* workspace, size_t workspace_bytes,
+                              int n_stages, hipStream_t stream) {
+    const int n = moe_fp8_forward_kernel_count(M, h, i, E, k);
+    if (n < 0) return n;
+    if (n_stages < 0 || n_stages > n) return MOE_ERR_INVALID;
+    return run_forward(x, router_logits, w13, s13, w2, s2, out, M, h, i, E, k, workspace,
+                       workspace_bytes, nullptr, 0, stream, n_stages);
 }
 
 int moe_fp8_forward_kernel_count(int M, int h, int i, int E, int k) {

@@ -147,6 +147,20 @@ int moe_fp8_forward_ws_timed(const void* x, const float* router_logits,
                              void* workspace, size_t workspace_bytes,
                              hipEvent_t* events, int n_events, hipStream_t stream);
 
+/* Measurement variant of moe_fp8_forward_ws: runs only the first n_stages
+ * stages of the forward (0 <= n_stages <= moe_fp8_forward_kernel_count(...),
+ * else MOE_ERR_INVALID), so that HIP-graph replays of forwards cut after
+ * successive stages time each stage without events between stages.  A cut
+ * forward leaves `out` and the later intermediates unwritten; with n_stages
+ * equal to the stage count it is moe_fp8_forward_ws.  Same arguments,
+ * ownership and errors as moe_fp8_forward_ws otherwise. */
+int moe_fp8_forward_ws_prefix(const void* x, const float* router_logits,
+                              const void* w13, const float* s13,
+                              const void* w2, const float* s2,
+                              void* out, int M, int h, int i, int E, int k,
+                              void* workspace, size_t workspace_bytes,
+                              int n_stages, hipStream_t stream);
+
 /* Number of stages a forward with these sizes runs (0 for M == 0, a negative
  * status for a rejected shape) and the kernel name(s) of stage j (static
  * string, NULL when j is out of range). */

@@ -299,6 +299,32 @@ def test_forward_deterministic_eager_and_graph(dev, moe_mod, ci):
         torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("ci", [0, 1, 2])
+def test_forward_prefix_stages(dev, moe_mod, ci):
+    """The measurement entry point cut after all stages is the forward itself;
+    cut earlier it leaves the workspace usable; other stage counts are
+    rejected."""
+    cfg = synth.CONFIGS[ci]
+    L = Layer(cfg, synth.default_seed(ci), dev)
+    M, h, i, E, k = L.dims
+    names = moe_mod.forward_kernel_names(M, h, i, E, k)
+    log(f"prefix stages {cfg.name}: {names}")
+    ws = moe_mod.alloc_workspace(M, h, i, E, k, device=dev)
+    ref = moe_mod.moe_fp8_forward_ws(L.tx, L.tl, L.t13, L.ts13, L.t2, L.ts2, k, ws).clone()
+    torch.cuda.synchronize()
+    for j in range(len(names) + 1):
+        moe_mod.moe_fp8_forward_ws_prefix(L.tx, L.tl, L.t13, L.ts13, L.t2, L.ts2, k, ws, j)
+        torch.cuda.synchronize()
+    out = torch.zeros_like(ref)
+    moe_mod.moe_fp8_forward_ws_prefix(L.tx, L.tl, L.t13, L.ts13, L.t2, L.ts2, k, ws, len(names), out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    for bad in (-1, len(names) + 1):
+        with pytest.raises(moe_mod.MoeError):
+            moe_mod.moe_fp8_forward_ws_prefix(L.tx, L.tl, L.t13, L.ts13, L.t2, L.ts2, k, ws, bad)
+    _check_sync_clean(ws)
+
+
 def _custom_layer(dev, M, h, i, E, k, seed, logits_kind="normal"):
     cfg = synth.LayerConfig(f"m{M}_h{h}_i{i}_e{E}_top{k}", M, h, i, E, k, logits_kind, "edge case")
     return Layer(cfg, seed, dev)
