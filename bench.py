@@ -164,10 +164,14 @@ def stage_work(cfg, stage, U):
 
 
 def source_digest(paths):
+    """Digest of the sources' code lines (lines that are whole // comments are
+    left out, so editing a comment keeps a measurement valid)."""
     h = hashlib.sha256()
     for p in paths:
         with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+            for line in f:
+                if not line.lstrip().startswith(b"//"):
+                    h.update(line)
     return h.hexdigest()[:16]
 
 

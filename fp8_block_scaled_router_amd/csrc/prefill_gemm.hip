@@ -5,10 +5,11 @@
 // route id).  An M-tile is 128 consecutive sorted routes of one expert; the
 // grouping pass also numbers every expert's M-tiles (mtile_off).
 //
-// gate/up: one workgroup per (M-tile, 128-column group jg).  Its weight tile
-// is the 128 gate rows and the 128 up rows of group jg of w13[e] (256 x h),
-// its activation tile the E4M3 rows of the tile's tokens.  down: one
-// workgroup per (M-tile, 256-row tile of w2[e]) over K = i.
+// gate/up tiles are (M-tile, 128-column group jg): the weight tile is the 128
+// gate rows and the 128 up rows of group jg of w13[e] (256 x h), the
+// activation tile the E4M3 rows of the tile's tokens.  down tiles are
+// (M-tile, 256-row tile of w2[e]) over K = i.  Both kernels are persistent:
+// one workgroup per CU walks the tiles of its XCD's share.
 //
 // Both kernels share one main loop, built for gfx950:
 //  * 8 waves; each owns 64 weight rows x 64 routes = 4 x 4 tiles of
@@ -20,7 +21,10 @@
 //    the third feeds the MFMAs.
 //  * LDS rows are 128 bytes with a 16-byte-slot swizzle that keeps each
 //    lane's 32 K bytes in order and spreads the 16 rows of a fragment over
-//    all banks (see lo_slot).
+//    all banks (lo_slot / chunk_of in device.h).
+//  * The next tile's route list and scales are copied straight into LDS
+//    during the current K loop, and its first two K blocks are issued before
+//    the current tile's epilogue.
 //  * Promotion with the two block scales (Netra Kernel README, capability
 //    table: explicit 128x128 block scales): acc += blk * (s_w * s_act) in
 //    fp32, one K block after the MFMA that produced blk, so the promotion
@@ -30,7 +34,7 @@
 // writes codes in sorted-route order; down writes fp32 partial rows by route
 // id (the down-partial of the same README).
 //
-// Workgroups are handed to XCDs round-robin; the tile order gives each XCD a
+// Workgroups are handed to XCDs round-robin; each XCD's workgroups walk a
 // contiguous range of tiles, so the M-tiles of one expert (which share its
 // weights) meet in the same L2.
 #include <algorithm>
