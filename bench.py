@@ -152,10 +152,12 @@ def stage_work(cfg, stage, U):
     if stage.startswith("prefill_gate_up"):
         # weights once, activation rows per route in, E4M3 codes + scales out
         return U * w13 + M * k * (h + i + (h // 128 + i // 128) * 4), 4.0 * M * k * h * i
-    if stage.startswith("prefill_down"):
-        return U * w2 + M * k * (i + (i // 128) * 4 + h * 4), 2.0 * M * k * h * i
+    if stage.startswith("prefill_down"):   # bf16 partials out
+        return U * w2 + M * k * (i + (i // 128) * 4 + h * 2), 2.0 * M * k * h * i
     if stage.startswith("route_quant"):
         return M * h * 2 + M * cfg.E * 4 + act + M * k * 8, 0.0
+    if stage.startswith("combine_bf16"):
+        return M * k * h * 2 + M * h * 2 + M * k * 4, 0.0   # bf16 partials in, bf16 out
     if stage.startswith("combine"):
         return M * k * h * 4 + M * h * 2 + M * k * 4, 0.0   # fp32 partials in, bf16 out
     if stage.startswith("fused"):

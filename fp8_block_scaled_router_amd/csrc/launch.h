@@ -57,7 +57,7 @@ struct PrefillArgs {
     const int32_t* mtile_off;   // [E + 1] first M-tile of each expert
     uint8_t* a2;                // [R][i]   requantised activations, sorted-route order
     float* a2s;                 // [R][i/128]
-    float* y;                   // [R][h]   fp32 partials by route id
+    uint16_t* y;                // [R][h]   bf16 partials by route id
     int h, i, E, k;
 };
 int prefill_tile_m();
@@ -68,6 +68,9 @@ hipError_t launch_prefill_down(const PrefillArgs& a, int R, hipStream_t stream);
 // Fixed-order combine of the k route partials of each token into bf16.
 hipError_t launch_combine(const float* y, const float* tw, int M, int k, int h, uint16_t* out,
                           hipStream_t stream);
+// Same, for bf16 partials (the prefill path).
+hipError_t launch_combine_bf16(const uint16_t* y, const float* tw, int M, int k, int h, uint16_t* out,
+                               hipStream_t stream);
 
 // Utilities.
 hipError_t launch_quant_weight(const float* w, int64_t batch, int N, int K, uint8_t* q, float* s,

@@ -90,7 +90,7 @@ void make_layout(int M, int h, int i, int E, int k, Layout* L) {
     } else if (p.path == MOE_FP8_PATH_PREFILL) {
         p.act2 = take(R * i);
         p.act2_scale = take(R * (i / 128) * 4);
-        p.partial = take(R * h * 4);
+        p.partial = take(R * h * 2);   // bf16 partials
     }   // the fused path exchanges its intermediates as tagged words in the head
     p.total = cur;
 }
@@ -111,7 +111,7 @@ const char* const kStreamSmallStages[] = {"route_quant_group_kernel", "stream_ga
 const char* const kFusedStages[] = {"fused_decode_kernel"};
 const char* const kPrefillStages[] = {"route_quant_kernel", "group_hist+group_scatter",
                                       "prefill_gate_up_kernel", "prefill_down_kernel",
-                                      "combine_kernel"};
+                                      "combine_bf16_kernel"};
 
 // The streaming path routes, quantises and groups in one launch when the
 // batch has few enough routes.
@@ -240,14 +240,14 @@ int run_forward(const void* x, const float* router_logits, const void* w13, cons
         pa.mtile_off = mtile_off;
         pa.a2 = at<uint8_t>(workspace, p.act2);
         pa.a2s = at<float>(workspace, p.act2_scale);
-        pa.y = y;
+        pa.y = at<uint16_t>(workspace, p.partial);
         pa.h = h;
         pa.i = i;
         pa.E = E;
         pa.k = k;
         MOE_STEP(moe::launch_prefill_gate_up(pa, R, stream));
         MOE_STEP(moe::launch_prefill_down(pa, R, stream));
-        MOE_STEP(moe::launch_combine(y, tw, M, k, h, static_cast<uint16_t*>(out), stream));
+        MOE_STEP(moe::launch_combine_bf16(pa.y, tw, M, k, h, static_cast<uint16_t*>(out), stream));
         return hook.mark() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
     }
     if (!small_group(M, k))

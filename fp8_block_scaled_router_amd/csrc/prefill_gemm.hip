@@ -31,7 +31,7 @@
 //    arithmetic never waits on an MFMA result.
 // gate/up's epilogue computes SiLU(gate) * up and its 1x128 E4M3
 // requantisation on the spot (Netra Kernel README, MoE prefill pair) and
-// writes codes in sorted-route order; down writes fp32 partial rows by route
+// writes codes in sorted-route order; down writes bf16 partial rows by route
 // id (the down-partial of the same README).
 //
 // Workgroups are handed to XCDs round-robin; each XCD's workgroups walk a
@@ -524,18 +524,19 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_down_kernel(PrefillArgs a
             L = down_loop(a, tn, wave, lane);
             issue_first(L, IB, stages);
         }
-        // fp32 partial rows by route id; lane holds output rows
-        // sub * 256 + 64 wn + 16 j + 4 kg + v of route 64 wr + 16 m + col
+        // bf16 partial rows (round to nearest even) by route id; lane holds
+        // output rows sub * 256 + 64 wn + 16 j + 4 kg + v of route
+        // 64 wr + 16 m + col
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int row = 64 * wr + 16 * m + col;
             if (row >= t.rows) continue;
             const int p = prt_l[par][row];
-            float* dst = a.y + (size_t)p * h + t.sub * kBN + 64 * wn + 4 * kg;
+            uint16_t* dst = a.y + (size_t)p * h + t.sub * kBN + 64 * wn + 4 * kg;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const v4f vv = acc[4 * j + m];
-                *reinterpret_cast<float4*>(dst + 16 * j) = make_float4(vv[0], vv[1], vv[2], vv[3]);
+                *reinterpret_cast<uint2*>(dst + 16 * j) = make_uint2(bf16x2(vv[0], vv[1]), bf16x2(vv[2], vv[3]));
             }
         }
         if (!more) break;

@@ -230,6 +230,45 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     *reinterpret_cast<uint2*>(out + (size_t)t * h + n) = make_uint2(bf16x2(a0, a1), bf16x2(a2, a3));
 }
 
+// The same combine over bf16 partials: eight columns per thread.
+__global__ __launch_bounds__(256) void combine_bf16_kernel(const uint16_t* __restrict__ y,
+                                                           const float* __restrict__ tw, int k, int h,
+                                                           uint16_t* __restrict__ out) {
+#pragma clang fp contract(off)
+    const int t = blockIdx.y;
+    const int n = (blockIdx.x * 256 + threadIdx.x) * 8;
+    if (n >= h) return;
+    v4i v[16];   // streaming loads: every partial is read once
+    float w[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        if (r < k) {
+            w[r] = tw[(size_t)t * k + r];
+            v[r] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(y + ((size_t)t * k + r) * h + n));
+        }
+    }
+    float a[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        if (r < k) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                a[2 * q] = a[2 * q] + w[r] * bf16_lo((uint32_t)v[r][q]);
+                a[2 * q + 1] = a[2 * q + 1] + w[r] * bf16_hi((uint32_t)v[r][q]);
+            }
+        }
+    }
+    *reinterpret_cast<uint4*>(out + (size_t)t * h + n) =
+        make_uint4(bf16x2(a[0], a[1]), bf16x2(a[2], a[3]), bf16x2(a[4], a[5]), bf16x2(a[6], a[7]));
+}
+
+hipError_t launch_combine_bf16(const uint16_t* y, const float* tw, int M, int k, int h, uint16_t* out,
+                               hipStream_t stream) {
+    const dim3 grid((h / 8 + 255) / 256, M);
+    hipLaunchKernelGGL(combine_bf16_kernel, grid, dim3(256), 0, stream, y, tw, k, h, out);
+    return hipGetLastError();
+}
+
 hipError_t launch_combine(const float* y, const float* tw, int M, int k, int h, uint16_t* out,
                           hipStream_t stream) {
     const dim3 grid((h / 4 + 255) / 256, M);

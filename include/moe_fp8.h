@@ -13,7 +13,8 @@
  *      by expert then route id);
  *   4. block-scaled FP8 gate/up GEMM with FP32 results;
  *   5. SiLU(gate) * up, requantised to FP8 per 128 columns;
- *   6. block-scaled FP8 down GEMM, one fp32 partial row per route;
+ *   6. block-scaled FP8 down GEMM, one partial row per route (fp32; bf16
+ *      on the prefill path, inside the output tolerance);
  *   7. combine: out[t] = bf16( sum over r = 0..k-1 of w[t,r] * partial[t*k+r] ),
  *      summed in rank order with no atomic adds (Inferact amd-kernels README,
  *      atomics rule).
@@ -182,7 +183,7 @@ typedef struct {
     size_t gate_up;     /* fp32  [M*k, 2i]  by route id                 */
     size_t act2;        /* e4m3  [M*k, i]   in sorted-route order       */
     size_t act2_scale;  /* fp32  [M*k, i/128] in sorted-route order     */
-    size_t partial;     /* fp32  [M*k, h]   by route id                 */
+    size_t partial;     /* [M*k, h] by route id: fp32 on the streaming path, bf16 on the prefill path */
     size_t sync_error;  /* uint32 error word (0 = no wait timed out)    */
     size_t total;       /* bytes                                        */
     int    path;        /* MOE_FP8_PATH_*                               */

@@ -109,7 +109,7 @@ def test_workspace_layout_regions(lib, M, h, i, E, k):
     sizes = {"topk_ids": 4 * R, "topk_w": 4 * R, "xq": M * h, "xs": 4 * M * h // 128,
              "counts": 4 * E, "offsets": 4 * (E + 1), "sorted": 4 * R, "active": 4 * E,
              "num_active": 4, "gate_up": 4 * R * 2 * i, "act2": R * i, "act2_scale": 4 * R * i // 128,
-             "partial": 4 * R * h}
+             "partial": (2 if L.path == moe.PATH_PREFILL else 4) * R * h}   # bf16 / fp32 partials
     spans = []
     for name, n in sizes.items():
         off = getattr(L, name)
