@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--config", type=int, default=1, help="layer shape index (0..4); 1 = decode M=1")
+    ap.add_argument("--config", type=int, default=1, help="layer shape index (0..5); 1 = decode M=1")
     ap.add_argument("--copies", type=int, default=0, help="rotation copies (0 = enough to exceed 4x the Infinity Cache)")
     ap.add_argument("--timing-replays", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -342,7 +342,11 @@ def main():
     U_mean = float(np.mean(U))
     abytes, aflops = stage_work(cfg, names[dom], U_mean)
     dom_s = stage_ms[dom] / 1e3
-    bound = "hbm" if M <= 64 else "mfma"
+    # the forward's bound: its algorithmic bytes (selected weights, x, logits,
+    # out) against its FLOPs, each over its peak
+    fw_bytes = U_mean * sum(weight_bytes_per_expert(cfg)) + M * h * 4 + M * E * 4
+    fw_flops = 6.0 * M * k * h * i
+    bound = "hbm" if fw_bytes / (HBM_PEAK_GBS * 1e9) >= fw_flops / (FP8_PEAK_TFLOPS * 1e12) else "mfma"
     if bound == "hbm":
         achieved = abytes / dom_s / 1e9
         peak, unit = HBM_PEAK_GBS, "GB/s"

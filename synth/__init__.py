@@ -11,6 +11,8 @@ Input recipe for each shape:
   x        bf16 of N(0, 1)                                     [M, h]
   logits   fp32 N(0, 1)                                        [M, E]
            shared_bias: + b[e], b ~ N(0, sd=2) drawn once per batch
+           request_bias: + b[q, e] for the request q = t // request_tokens of
+                        token t, one b[q] ~ N(0, sd=2) per request
            zipf:        + ln p_e, p_e = (e+1)^-1.1 / sum_j (j+1)^-1.1
   w13      fp32 N(0, sd=1/sqrt(h)) [E, 2i, h]; rows [0,i) gate, [i,2i) up
   w2       fp32 N(0, sd=1/sqrt(i)) [E, h, i]
@@ -68,8 +70,9 @@ class LayerConfig:
     i: int
     E: int
     k: int
-    logits: str          # "normal" | "shared_bias" | "zipf"
+    logits: str          # "normal" | "shared_bias" | "request_bias" | "zipf"
     description: str
+    request_tokens: int = 0   # tokens per request ("request_bias" only)
 
     @property
     def routes(self) -> int:
@@ -87,6 +90,9 @@ CONFIGS = [
                 "wide-hidden decode batch"),
     LayerConfig("prefill_m8192_h2048_i768_e128_top8", 8192, 2048, 768, 128, 8, "zipf",
                 "prefill with a Zipf(1.1) expert-popularity prior"),
+    LayerConfig("verify_m768_h2048_i768_e128_top8", 768, 2048, 768, 128, 8, "request_bias",
+                "verify batch of 64 requests x 12 tokens, an expert bias N(0, sd=2) per request",
+                request_tokens=12),
 ]
 
 
@@ -130,6 +136,14 @@ def make_logits(cfg: LayerConfig, seed: int, copy: int = 0, M: int | None = None
     if cfg.logits == "shared_bias":
         bias = normal(seed, TAG_BIAS + COPY_TAG_STRIDE * copy, (cfg.E,), std=2.0, dtype=np.float64)
         return (base + bias[None, :]).astype(np.float32)
+    if cfg.logits == "request_bias":
+        q = cfg.request_tokens
+        req = np.arange(first_token, first_token + M) // q
+        r0 = int(req[0]) if M else 0
+        nreq = int(req[-1]) - r0 + 1 if M else 0
+        bias = normal(seed, TAG_BIAS + COPY_TAG_STRIDE * copy, (nreq, cfg.E), std=2.0,
+                      first=r0 * cfg.E, dtype=np.float64)
+        return (base + bias[req - r0]).astype(np.float32)
     if cfg.logits == "zipf":
         return (base + zipf_log_prior(cfg.E)[None, :]).astype(np.float32)
     raise ValueError(cfg.logits)

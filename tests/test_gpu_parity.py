@@ -17,7 +17,7 @@ from gpu_util import (Layer, check_output, flagged_codes, flip_allowance, log, r
 
 pytestmark = pytest.mark.gpu
 
-CONFIG_IDS = [0, 1, 2, 3, 4]
+CONFIG_IDS = [0, 1, 2, 3, 4, 5]
 
 
 @pytest.fixture(scope="module")
@@ -225,7 +225,7 @@ def _check_intermediates(moe_mod, L: Layer, ws, inter, tokens=None):
         assert np.all((got >= T[lo[fl]]) & (got <= T[hi[fl]])), "requantised code outside its bracket"
 
 
-@pytest.mark.parametrize("ci", [0, 1, 2, 3])
+@pytest.mark.parametrize("ci", [0, 1, 2, 3, 5])
 def test_forward_matches_oracle(dev, moe_mod, ci):
     cfg = synth.CONFIGS[ci]
     log(f"forward {cfg.name}: inputs")

@@ -185,3 +185,22 @@ def test_routing_weights_sum_to_one(oracle_mod, synth_mod):
         ids, w = oracle_mod.router(logits, cfg.k)
         assert np.all(np.abs(w.astype(np.float64).sum(1) - 1.0) <= cfg.k * 2.0 ** -23)
         assert np.all(w > 0) and np.all(np.diff(w, axis=1) <= 0)   # rank order = descending weight
+
+
+def test_request_bias_logits_are_per_request(synth_mod):
+    """The M=768 verify batch: tokens of one request share their expert bias,
+    so within a request the logit differences are those of the N(0,1) base;
+    and any token window reproduces the same rows."""
+    cfg = synth_mod.CONFIGS[5]
+    assert cfg.M == 64 * cfg.request_tokens
+    seed = synth_mod.default_seed(5)
+    full = synth_mod.make_logits(cfg, seed).astype(np.float64)
+    win = synth_mod.make_logits(cfg, seed, M=30, first_token=101)
+    assert np.array_equal(win, full[101:131].astype(np.float32))
+    base = synth_mod.normal(seed, synth_mod.TAG_LOGITS, (cfg.M, cfg.E), dtype=np.float64)
+    bias = full - base
+    q = cfg.request_tokens
+    per_req = bias.reshape(64, q, cfg.E)
+    assert np.allclose(per_req, per_req[:, :1, :], atol=1e-5)       # one bias per request
+    assert abs(per_req[:, 0, :].std() - 2.0) < 0.1                   # sd 2
+    assert not np.allclose(per_req[0, 0], per_req[1, 0], atol=0.5)  # requests differ
