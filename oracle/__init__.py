@@ -46,6 +46,7 @@ def lib():
             "oracle_quant_weight_block128": (None, [_P, _I64, _I, _I, _P, _P]),
             "oracle_router": (None, [_P, _I, _I, _I, _P, _P]),
             "oracle_act_quant": (None, [_P, _I, _I, _P, _P]),
+            "oracle_rmsnorm_act_quant": (None, [_P, _P, ctypes.c_float, _I, _I, _P, _P, _P]),
             "oracle_group": (None, [_P, _I, _I, _P, _P, _P]),
             "oracle_block_gemm": (None, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P]),
             "oracle_silu_mul_quant": (None, [_P, _I, _I, _P, _P]),
@@ -130,6 +131,20 @@ def act_quant(x_bits: np.ndarray):
     s = np.empty((M, K // 128), dtype=np.float32)
     lib().oracle_act_quant(px, M, K, q.ctypes.data, s.ctypes.data)
     return q, s
+
+
+def rmsnorm_act_quant(x_bits: np.ndarray, gamma: np.ndarray, eps: float):
+    """RMSNorm of bf16 rows to bf16, then the 1x128 quantisation (see
+    oracle_rmsnorm_act_quant).  Returns (y bf16 bits, codes, scales)."""
+    x, px = _c(x_bits, np.uint16)
+    g, pg = _c(gamma, np.float32)
+    M, K = x.shape
+    assert g.shape == (K,) and K % 128 == 0
+    y = np.empty((M, K), dtype=np.uint16)
+    q = np.empty((M, K), dtype=np.uint8)
+    s = np.empty((M, K // 128), dtype=np.float32)
+    lib().oracle_rmsnorm_act_quant(px, pg, float(eps), M, K, y.ctypes.data, q.ctypes.data, s.ctypes.data)
+    return y, q, s
 
 
 def group(ids: np.ndarray, E: int):

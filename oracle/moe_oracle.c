@@ -228,6 +228,41 @@ void oracle_act_quant(const uint16_t* x, int M, int K, uint8_t* q, float* s)
 }
 
 /* ------------------------------------------------------------------ */
+/* Front end: RMSNorm to bf16, then the 1x128 quantisation above        */
+/* ------------------------------------------------------------------ */
+
+void oracle_rmsnorm_act_quant(const uint16_t* x, const float* gamma, float eps, int M, int K,
+                              uint16_t* y, uint8_t* q, float* s)
+{
+    const int KB = K / 128;
+    #pragma omp parallel for schedule(static)
+    for (int t = 0; t < M; ++t) {
+        const uint16_t* xr = x + (int64_t)t * K;
+        uint16_t* yr = y + (int64_t)t * K;
+        /* mean of squares and its inverse square root, in float64 */
+        double ss = 0.0;
+        for (int c = 0; c < K; ++c) {
+            const double v = (double)oracle_bf16_decode(xr[c]);
+            ss += v * v;
+        }
+        const double ms = ss / (double)K;
+        const float r = (float)(1.0 / sqrt(ms + (double)eps));
+        /* normalised, weighted, rounded to bf16 */
+        for (int c = 0; c < K; ++c) {
+            const float n = oracle_bf16_decode(xr[c]) * r;
+            const float wv = n * gamma[c];
+            yr[c] = oracle_bf16_encode(wv);
+        }
+        /* the layer's activation quantisation of the bf16 row */
+        float row[128];
+        for (int g = 0; g < KB; ++g) {
+            for (int j = 0; j < 128; ++j) row[j] = oracle_bf16_decode(yr[g * 128 + j]);
+            s[(int64_t)t * KB + g] = quant_group(row, 128, 1, q + (int64_t)t * K + g * 128, 1);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
 /* O2: router -- softmax, top-k on logits (ties to lower index), renorm */
 /* ------------------------------------------------------------------ */
 

@@ -106,6 +106,19 @@ void oracle_silu_mul_quant(const float* g, int R, int I, uint8_t* a2, float* a2s
 /* y fp32 [M*k][H], w fp32 [M][k] -> out bf16 bits [M][H] */
 void oracle_combine(const float* y, const float* w, int M, int k, int H, uint16_t* out);
 
+/* Front end before the layer (normalisation and quantisation fusion of the
+ * Netra Kernel README directory map, gfx950 norm family): RMSNorm of bf16
+ * rows, rounded to bf16, then the 1x128 quantisation of oracle_act_quant.
+ * Per row: ss = sum of x^2 in float64 (every square is exact), r =
+ * fp32(1 / sqrt(ss / K + eps)) with the sum, division, square root and
+ * reciprocal in float64 and one rounding to fp32 at the end; y[c] =
+ * bf16_rne(fp32(fp32(x[c] * r) * gamma[c])).  gamma is the fp32 norm weight
+ * (1 + w for a zero-centred weight w).
+ * x bf16 bits [M][K], gamma fp32 [K] -> y bf16 bits [M][K], q e4m3 [M][K],
+ * s fp32 [M][K/128]. */
+void oracle_rmsnorm_act_quant(const uint16_t* x, const float* gamma, float eps, int M, int K,
+                              uint16_t* y, uint8_t* q, float* s);
+
 /* Intermediates of one forward, all optional (NULL = not wanted). */
 typedef struct {
     int32_t* ids;      /* [M*k]      */
