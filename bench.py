@@ -54,6 +54,8 @@ def parse():
                          "the copy calibration: record the kernel's HBM bytes per launch in profiles/traffic.json")
     ap.add_argument("--pmc-kernel", default=None, help="kernel for --pmc-summary")
     ap.add_argument("--pmc-copy-mib", type=int, default=1024, help="copy size of the calibration runs")
+    ap.add_argument("--front-end", action="store_true",
+                    help="time the RMSNorm + 1x128 quantisation front end alone on --config's activations")
     return ap.parse_args()
 
 
@@ -192,6 +194,78 @@ def load_traffic(kernel, workload):
     return rec["bytes_per_launch"]
 
 
+def front_end_bench(args):
+    """The RMSNorm + 1x128 E4M3 quantisation front end alone, on the
+    activation rows of a layer shape: inputs and outputs rotated over copies
+    that together exceed 4x the Infinity Cache, C launches per HIP graph,
+    events around K launches on the launch stream.  HBM roofline from the
+    algorithmic bytes: x in (2h per row), codes, scales and the bf16
+    normalised rows out (h + h/32 + 2h per row), the norm weight once."""
+    import numpy as np
+    import torch
+
+    import fp8_block_scaled_router_amd as moe
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    moe.lib()
+    dev = torch.device("cuda:0")
+    cfg = synth.CONFIGS[args.config]
+    seed = synth.default_seed(args.config) if args.seed is None else args.seed
+    M, h = cfg.M, cfg.h
+    eps = 1e-6
+    row_bytes = 2 * h + h + (h // 128) * 4 + 2 * h
+    launch_bytes = M * row_bytes + 4 * h
+    C = args.copies or max(2, math.ceil(4 * MALL_BYTES / (M * row_bytes)) + 1)
+    C = min(C, 4096)
+    x0 = torch.from_numpy(synth.make_x(cfg, seed).view(np.int16)).view(torch.bfloat16).to(dev)
+    gamma = torch.from_numpy(np.random.default_rng(seed).uniform(0.5, 1.5, h).astype(np.float32)).to(dev)
+    X = [x0] + [x0.clone() for _ in range(C - 1)]
+    OUT = [(torch.empty((M, h), dtype=torch.bfloat16, device=dev),
+            torch.empty((M, h), dtype=torch.uint8, device=dev),
+            torch.empty((M, h // 128), dtype=torch.float32, device=dev)) for _ in range(C)]
+    for c in range(C):
+        moe.rmsnorm_act_quant(X[c], gamma, eps, out=OUT[c])
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for c in range(C):
+            moe.rmsnorm_act_quant(X[c], gamma, eps, out=OUT[c])
+    reps_w = max(1, args.warmup // C)
+    reps = max(1, args.steps // C)
+    for _ in range(reps_w):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(20_000_000)   # queue the replays behind a spin so the GPU, not the host, sets the pace
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (reps * C)
+    achieved = launch_bytes / (ms / 1e3) / 1e9
+    line = {
+        "metric": "front end rows/s (RMSNorm + 1x128 E4M3 quantisation)",
+        "value": round(M / (ms / 1e3), 2), "unit": "rows/s", "n_gpus": 1,
+        "steps": reps * C, "warmup": reps_w * C, "ms_per_step": round(ms, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 in, f64 row sums, e4m3 out", "data": "synthetic",
+        "config": {"workload": f"rmsnorm_quant_m{M}_h{h}", "M": M, "h": h, "rotation_copies": C,
+                   "timing": "HIP graph of C launches, events around the replays"},
+        "roofline": {"bound": "hbm", "kernel": "rmsnorm_quant_kernel", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "avg_launch_us": round(ms * 1e3, 3),
+                     "algorithmic_bytes_per_launch": int(launch_bytes)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -204,6 +278,9 @@ def main():
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "the layer is not sharded across GPUs", file=sys.stderr)
         sys.exit(2)
+    if args.front_end:
+        front_end_bench(args)
+        return
 
     import numpy as np
     import torch

@@ -60,6 +60,7 @@ _SIGS = {
     "moe_fp8_workspace_layout": (_I, [_I, _I, _I, _I, _I, ctypes.POINTER(WsLayout)]),
     "router_topk": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "moe_fp8_act_quant": (_I, [_P, _I, _I, _P, _P, _P]),
+    "moe_fp8_rmsnorm_act_quant": (_I, [_P, _P, ctypes.c_float, _I, _I, _P, _P, _P, _P]),
     "moe_fp8_group_workspace_bytes": (_SZ, [_I, _I, _I]),
     "moe_fp8_group": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "moe_fp8_quantize_weight_block128": (_I, [_P, _I64, _I, _I, _P, _P, _P]),
@@ -221,6 +222,29 @@ def act_quant(x, stream=None):
     s = torch.empty((M, K // 128), dtype=torch.float32, device=x.device)
     _check(lib().moe_fp8_act_quant(_ptr(x), M, K, _ptr(q), _ptr(s), _stream(stream)), "moe_fp8_act_quant")
     return q, s
+
+
+def rmsnorm_act_quant(x, gamma, eps: float, want_y: bool = True, out=None, stream=None):
+    """bf16 [M, h] rows and fp32 [h] norm weight -> (y bf16 [M, h] or None,
+    E4M3 codes uint8 [M, h], fp32 scales [M, h/128]).  `out` = (y or None,
+    q, s) writes into existing tensors."""
+    M, h = x.shape
+    _dev(x, torch.bfloat16, "x")
+    _dev(gamma, torch.float32, "gamma")
+    if out is not None:
+        y, q, s = out
+        if y is not None:
+            _dev(y, torch.bfloat16, "y", (M, h))
+        _dev(q, torch.uint8, "q", (M, h))
+        _dev(s, torch.float32, "s", (M, h // 128))
+    else:
+        y = torch.empty((M, h), dtype=torch.bfloat16, device=x.device) if want_y else None
+        q = torch.empty((M, h), dtype=torch.uint8, device=x.device)
+        s = torch.empty((M, h // 128), dtype=torch.float32, device=x.device)
+    _check(lib().moe_fp8_rmsnorm_act_quant(_ptr(x), _ptr(gamma), float(eps), M, h,
+                                           _ptr(y) if y is not None else None, _ptr(q), _ptr(s),
+                                           _stream(stream)), "moe_fp8_rmsnorm_act_quant")
+    return y, q, s
 
 
 def group(topk_ids, E: int, stream=None):

@@ -72,6 +72,13 @@ hipError_t launch_combine(const float* y, const float* tw, int M, int k, int h, 
 hipError_t launch_combine_bf16(const uint16_t* y, const float* tw, int M, int k, int h, uint16_t* out,
                                hipStream_t stream);
 
+// RMSNorm of bf16 rows fused with the 1x128 activation quantisation; y
+// (bf16 [M][h], the normalised rows) may be null.  h % 128 == 0,
+// h <= kFrontMaxHidden.
+constexpr int kFrontMaxHidden = 8192;
+hipError_t launch_rmsnorm_quant(const uint16_t* x, const float* gamma, float eps, int M, int h,
+                                uint16_t* y, uint8_t* q, float* s, hipStream_t stream);
+
 // Utilities.
 hipError_t launch_quant_weight(const float* w, int64_t batch, int N, int K, uint8_t* q, float* s,
                                hipStream_t stream);

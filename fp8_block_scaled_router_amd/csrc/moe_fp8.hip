@@ -408,6 +408,18 @@ int moe_fp8_act_quant(const void* x, int M, int K, uint8_t* q, float* s, hipStre
                                               nullptr, nullptr, q, s, moe::kQuant, stream));
 }
 
+int moe_fp8_rmsnorm_act_quant(const void* x, const float* gamma, float eps, int M, int h, void* y,
+                              uint8_t* q, float* s, hipStream_t stream) {
+    if (M < 0 || h <= 0 || !(eps >= 0.0f) || eps > 3.0e38f) return MOE_ERR_INVALID;
+    if (h % 128 != 0 || h > moe::kFrontMaxHidden) return MOE_ERR_UNSUPPORTED;
+    if (M == 0) return MOE_OK;
+    if (!x || !gamma || !q || !s) return MOE_ERR_INVALID;
+    if (!aligned16(x) || !aligned16(gamma) || !aligned16(q) || !aligned16(s) || (y && !aligned16(y)))
+        return MOE_ERR_INVALID;
+    return hip_status(moe::launch_rmsnorm_quant(static_cast<const uint16_t*>(x), gamma, eps, M, h,
+                                                static_cast<uint16_t*>(y), q, s, stream));
+}
+
 size_t moe_fp8_group_workspace_bytes(int M, int E, int k) {
     if (M < 0 || E <= 0 || k <= 0 || E > MOE_FP8_MAX_EXPERTS) return 0;
     return align_up((size_t)moe::group_chunks(M * k) * E * 4 + 2 * (size_t)E * 4 + 64);

@@ -206,6 +206,24 @@ int router_topk(const float* logits, int M, int E, int k,
 int moe_fp8_act_quant(const void* x, int M, int K, uint8_t* q, float* s,
                       hipStream_t stream);
 
+/* The step before step 2 (the gfx950 "normalization and quantization
+ * fusions" family of the Netra Kernel README directory map): RMSNorm of bf16
+ * rows fused with the 1x128 quantisation, one pass over x.
+ *   x     bf16 [M, h] (device, 16-byte aligned, read only)
+ *   gamma fp32 [h], the norm weight (pass 1 + w for a zero-centred weight w)
+ *   eps   >= 0, finite
+ *   y     bf16 [M, h] normalised rows, or NULL when not wanted
+ *   q, s  e4m3 [M, h] and fp32 [M, h/128], exactly what moe_fp8_act_quant
+ *         gives for y
+ * Per row: ss = sum of x^2 (exact squares, float64 sum), r = fp32(1 /
+ * sqrt(ss/h + eps)) computed in float64 and rounded once, y = bf16_rne(
+ * fp32(fp32(x * r) * gamma)).  All buffers are caller-owned device memory.
+ * h % 128 == 0 and h <= 8192 (else MOE_ERR_UNSUPPORTED); a null or
+ * misaligned pointer, M < 0 or a bad eps gives MOE_ERR_INVALID; M == 0 is a
+ * no-op.  Enqueued on `stream`. */
+int moe_fp8_rmsnorm_act_quant(const void* x, const float* gamma, float eps, int M, int h,
+                              void* y, uint8_t* q, float* s, hipStream_t stream);
+
 /* Step 3 alone: topk_ids int32 [M*k] with values in [0, E) ->
  *   counts int32 [E], offsets int32 [E + 1] (exclusive scan of counts),
  *   sorted_route_ids int32 [M*k] (route ids grouped by expert ascending and

@@ -88,6 +88,15 @@ def test_other_entry_argument_checks(lib):
     assert lib.router_topk(None, 4, 8, 2, FAKE, FAKE, None) == moe.MOE_ERR_INVALID
     assert lib.moe_fp8_act_quant(FAKE, 4, 100, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
     assert lib.moe_fp8_act_quant(None, 4, 128, FAKE, FAKE, None) == moe.MOE_ERR_INVALID
+    rq = lib.moe_fp8_rmsnorm_act_quant
+    assert rq(FAKE, FAKE, 1e-6, 4, 200, None, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert rq(FAKE, FAKE, 1e-6, 4, 8192 + 128, None, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert rq(FAKE, FAKE, -1.0, 4, 2048, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID
+    assert rq(FAKE, FAKE, float("nan"), 4, 2048, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID
+    assert rq(FAKE, FAKE, 1e-6, -1, 2048, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID
+    assert rq(FAKE, None, 1e-6, 4, 2048, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID
+    assert rq(FAKE, FAKE, 1e-6, 4, 2048, ctypes.c_void_p(0x100008), FAKE, FAKE, None) == moe.MOE_ERR_INVALID
+    assert rq(FAKE, FAKE, 1e-6, 0, 2048, None, FAKE, FAKE, None) == moe.MOE_OK
     assert lib.moe_fp8_group(FAKE, 4, 8, 2, FAKE, FAKE, FAKE, FAKE, 0, None) == moe.MOE_ERR_WORKSPACE
     assert lib.moe_fp8_group(FAKE, 4, 8, 9, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == moe.MOE_ERR_UNSUPPORTED
     assert lib.moe_fp8_quantize_weight_block128(FAKE, 1, 100, 128, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
