@@ -47,6 +47,7 @@ def lib():
             "oracle_router": (None, [_P, _I, _I, _I, _P, _P]),
             "oracle_act_quant": (None, [_P, _I, _I, _P, _P]),
             "oracle_rmsnorm_act_quant": (None, [_P, _P, ctypes.c_float, _I, _I, _P, _P, _P]),
+            "oracle_router_logits": (None, [_P, _P, _I, _I, _I, _P]),
             "oracle_group": (None, [_P, _I, _I, _P, _P, _P]),
             "oracle_block_gemm": (None, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _P]),
             "oracle_silu_mul_quant": (None, [_P, _I, _I, _P, _P]),
@@ -131,6 +132,19 @@ def act_quant(x_bits: np.ndarray):
     s = np.empty((M, K // 128), dtype=np.float32)
     lib().oracle_act_quant(px, M, K, q.ctypes.data, s.ctypes.data)
     return q, s
+
+
+def router_logits(x_bits: np.ndarray, wr_bits: np.ndarray):
+    """BF16 routing logits fp32 [M, E] of bf16 rows [M, K] and a bf16 router
+    weight [E, K] (see oracle_router_logits)."""
+    x, px = _c(x_bits, np.uint16)
+    w, pw = _c(wr_bits, np.uint16)
+    M, K = x.shape
+    E = w.shape[0]
+    assert w.shape == (E, K)
+    out = np.empty((M, E), dtype=np.float32)
+    lib().oracle_router_logits(px, pw, M, K, E, out.ctypes.data)
+    return out
 
 
 def rmsnorm_act_quant(x_bits: np.ndarray, gamma: np.ndarray, eps: float):

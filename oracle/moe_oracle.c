@@ -228,6 +228,25 @@ void oracle_act_quant(const uint16_t* x, int M, int K, uint8_t* q, float* s)
 }
 
 /* ------------------------------------------------------------------ */
+/* BF16 routing logits                                                  */
+/* ------------------------------------------------------------------ */
+
+void oracle_router_logits(const uint16_t* x, const uint16_t* wr, int M, int K, int E, float* logits)
+{
+    #pragma omp parallel for schedule(static)
+    for (int t = 0; t < M; ++t) {
+        const uint16_t* xr = x + (int64_t)t * K;
+        for (int e = 0; e < E; ++e) {
+            const uint16_t* w = wr + (int64_t)e * K;
+            double acc = 0.0;
+            for (int j = 0; j < K; ++j)
+                acc += (double)oracle_bf16_decode(xr[j]) * (double)oracle_bf16_decode(w[j]);
+            logits[(int64_t)t * E + e] = (float)acc;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
 /* Front end: RMSNorm to bf16, then the 1x128 quantisation above        */
 /* ------------------------------------------------------------------ */
 

@@ -106,6 +106,14 @@ void oracle_silu_mul_quant(const float* g, int R, int I, uint8_t* a2, float* a2s
 /* y fp32 [M*k][H], w fp32 [M][k] -> out bf16 bits [M][H] */
 void oracle_combine(const float* y, const float* w, int M, int k, int H, uint16_t* out);
 
+/* BF16 routing (Netra Kernel README capability table: BF16 routing among the
+ * gfx950 operation families): router logits from bf16 hidden rows x [M][K]
+ * and a bf16 router weight wr [E][K]: logits[t][e] = fp32( sum over j of
+ * x[t][j] * wr[e][j] ), every product exact, the sum in float64 in ascending
+ * j, one rounding to fp32.  The ids and weights then come from
+ * oracle_router on these logits. */
+void oracle_router_logits(const uint16_t* x, const uint16_t* wr, int M, int K, int E, float* logits);
+
 /* Front end before the layer (normalisation and quantisation fusion of the
  * Netra Kernel README directory map, gfx950 norm family): RMSNorm of bf16
  * rows, rounded to bf16, then the 1x128 quantisation of oracle_act_quant.

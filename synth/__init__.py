@@ -16,6 +16,7 @@ Input recipe for each shape:
            zipf:        + ln p_e, p_e = (e+1)^-1.1 / sum_j (j+1)^-1.1
   w13      fp32 N(0, sd=1/sqrt(h)) [E, 2i, h]; rows [0,i) gate, [i,2i) up
   w2       fp32 N(0, sd=1/sqrt(i)) [E, h, i]
+  wr       bf16 N(0, sd=1/sqrt(h)) [E, h], the router weight of BF16 routing (tag 6)
 Each tensor is its own stream (seed, tag); rotation copy c adds 256*c to the
 tag, so copies are independent draws.
 """
@@ -31,7 +32,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libsynth.so")
 _lib = None
 
-TAG_X, TAG_LOGITS, TAG_BIAS, TAG_W13, TAG_W2 = 1, 2, 3, 4, 5
+TAG_X, TAG_LOGITS, TAG_BIAS, TAG_W13, TAG_W2, TAG_WR = 1, 2, 3, 4, 5, 6
 COPY_TAG_STRIDE = 256
 
 
@@ -147,6 +148,12 @@ def make_logits(cfg: LayerConfig, seed: int, copy: int = 0, M: int | None = None
     if cfg.logits == "zipf":
         return (base + zipf_log_prior(cfg.E)[None, :]).astype(np.float32)
     raise ValueError(cfg.logits)
+
+
+def make_wr(cfg: LayerConfig, seed: int) -> np.ndarray:
+    """bf16 bit patterns [E, h] of a router weight N(0, sd=1/sqrt(h)), so that
+    x . wr has roughly unit variance, like the N(0,1) logits above."""
+    return to_bf16_bits(normal(seed, TAG_WR, (cfg.E, cfg.h), std=1.0 / np.sqrt(cfg.h)))
 
 
 def make_w13_f32(cfg: LayerConfig, seed: int, experts=None) -> np.ndarray:
