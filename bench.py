@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--pmc-copy-mib", type=int, default=1024, help="copy size of the calibration runs")
     ap.add_argument("--front-end", action="store_true",
                     help="time the RMSNorm + 1x128 quantisation front end alone on --config's activations")
+    ap.add_argument("--router-gemm", action="store_true",
+                    help="time BF16 routing fused with the top-k alone on --config's activations")
     return ap.parse_args()
 
 
@@ -194,6 +196,91 @@ def load_traffic(kernel, workload):
     return rec["bytes_per_launch"]
 
 
+def time_single_kernel(launch, C, args):
+    """Mean duration of one launch: launch(c) for the C rotation copies
+    captured in one HIP graph on a side stream, W warm-up launches, then
+    K launches between HIP events on that stream, queued behind a GPU spin so
+    that the GPU, not the host, sets the pace.  Returns (ms per launch,
+    replays, warm-up replays)."""
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for c in range(C):
+            launch(c)
+    reps_w = max(1, args.warmup // C)
+    reps = max(1, args.steps // C)
+    with torch.cuda.stream(side):
+        for _ in range(reps_w):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(20_000_000)
+        e0.record(side)
+        for _ in range(reps):
+            g.replay()
+        e1.record(side)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * C), reps, reps_w
+
+
+def router_gemm_bench(args):
+    """BF16 routing fused with the top-k alone, on the activation rows of a
+    layer shape and a bf16 router weight N(0, 1/sqrt(h)) [E, h]: x and the
+    weight rotated over copies that together exceed 4x the Infinity Cache.
+    HBM roofline from the algorithmic bytes: x (2h per row) and the router
+    weight (2Eh) in, logits (4E per row), ids and weights (8k per row) out."""
+    import numpy as np
+    import torch
+
+    import fp8_block_scaled_router_amd as moe
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    moe.lib()
+    dev = torch.device("cuda:0")
+    cfg = synth.CONFIGS[args.config]
+    seed = synth.default_seed(args.config) if args.seed is None else args.seed
+    M, h, E, k = cfg.M, cfg.h, cfg.E, cfg.k
+    copy_bytes = 2 * M * h + 2 * E * h + M * (4 * E + 8 * k)
+    C = args.copies or max(2, math.ceil(4 * MALL_BYTES / copy_bytes) + 1)
+    C = min(C, 4096)
+    x0 = torch.from_numpy(synth.make_x(cfg, seed).view(np.int16)).view(torch.bfloat16).to(dev)
+    w0 = torch.from_numpy(synth.make_wr(cfg, seed).view(np.int16)).view(torch.bfloat16).to(dev)
+    X = [x0] + [x0.clone() for _ in range(C - 1)]
+    W = [w0] + [w0.clone() for _ in range(C - 1)]
+    OUT = [(torch.empty((M, E), dtype=torch.float32, device=dev),
+            torch.empty((M, k), dtype=torch.int32, device=dev),
+            torch.empty((M, k), dtype=torch.float32, device=dev)) for _ in range(C)]
+    for c in range(C):
+        moe.router_gemm_topk(X[c], W[c], k, out=OUT[c])
+    torch.cuda.synchronize()
+    ms, reps, reps_w = time_single_kernel(lambda c: moe.router_gemm_topk(X[c], W[c], k, out=OUT[c]), C, args)
+    achieved = copy_bytes / (ms / 1e3) / 1e9
+    flops = 2.0 * M * h * E
+    line = {
+        "metric": "BF16 routing tokens/s (router logits GEMM fused with top-k)",
+        "value": round(M / (ms / 1e3), 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": reps * C, "warmup": reps_w * C, "ms_per_step": round(ms, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 in, fp32 accumulate", "data": "synthetic",
+        "config": {"workload": f"router_gemm_topk_m{M}_h{h}_e{E}_top{k}", "M": M, "h": h, "E": E, "k": k,
+                   "rotation_copies": C, "timing": "HIP graph of C launches, events around the replays"},
+        "roofline": {"bound": "hbm", "kernel": "router_gemm_topk_kernel", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "avg_launch_us": round(ms * 1e3, 3),
+                     "algorithmic_bytes_per_launch": int(copy_bytes),
+                     "algorithmic_flops_per_launch": flops,
+                     "bf16_mfma_frac": round(flops / (ms / 1e3) / 2.5e15, 4)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def front_end_bench(args):
     """The RMSNorm + 1x128 E4M3 quantisation front end alone, on the
     activation rows of a layer shape: inputs and outputs rotated over copies
@@ -229,25 +316,7 @@ def front_end_bench(args):
     for c in range(C):
         moe.rmsnorm_act_quant(X[c], gamma, eps, out=OUT[c])
     torch.cuda.synchronize()
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=side):
-        for c in range(C):
-            moe.rmsnorm_act_quant(X[c], gamma, eps, out=OUT[c])
-    reps_w = max(1, args.warmup // C)
-    reps = max(1, args.steps // C)
-    for _ in range(reps_w):
-        g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda._sleep(20_000_000)   # queue the replays behind a spin so the GPU, not the host, sets the pace
-    e0.record()
-    for _ in range(reps):
-        g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / (reps * C)
+    ms, reps, reps_w = time_single_kernel(lambda c: moe.rmsnorm_act_quant(X[c], gamma, eps, out=OUT[c]), C, args)
     achieved = launch_bytes / (ms / 1e3) / 1e9
     line = {
         "metric": "front end rows/s (RMSNorm + 1x128 E4M3 quantisation)",
@@ -280,6 +349,9 @@ def main():
         sys.exit(2)
     if args.front_end:
         front_end_bench(args)
+        return
+    if args.router_gemm:
+        router_gemm_bench(args)
         return
 
     import numpy as np

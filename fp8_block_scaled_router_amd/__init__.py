@@ -59,6 +59,7 @@ _SIGS = {
     "moe_fp8_forward_ws": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _SZ, _P]),
     "moe_fp8_workspace_layout": (_I, [_I, _I, _I, _I, _I, ctypes.POINTER(WsLayout)]),
     "router_topk": (_I, [_P, _I, _I, _I, _P, _P, _P]),
+    "moe_fp8_router_gemm_topk": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P]),
     "moe_fp8_act_quant": (_I, [_P, _I, _I, _P, _P, _P]),
     "moe_fp8_rmsnorm_act_quant": (_I, [_P, _P, ctypes.c_float, _I, _I, _P, _P, _P, _P]),
     "moe_fp8_group_workspace_bytes": (_SZ, [_I, _I, _I]),
@@ -213,6 +214,31 @@ def router_topk(logits, k: int, stream=None):
     w = torch.empty((M, k), dtype=torch.float32, device=logits.device)
     _check(lib().router_topk(_ptr(logits), M, E, int(k), _ptr(ids), _ptr(w), _stream(stream)), "router_topk")
     return ids, w
+
+
+def router_gemm_topk(x, wr, k: int, want_logits: bool = True, out=None, stream=None):
+    """BF16 routing fused with the top-k: bf16 hidden rows x [M, h] and a bf16
+    router weight wr [E, h] -> (logits fp32 [M, E] or None, ids int32 [M, k],
+    weights fp32 [M, k]).  `out` = (logits or None, ids, w) writes into
+    existing tensors."""
+    M, h = x.shape
+    E = wr.shape[0]
+    _dev(x, torch.bfloat16, "x")
+    _dev(wr, torch.bfloat16, "wr", (E, h))
+    if out is not None:
+        logits, ids, w = out
+        if logits is not None:
+            _dev(logits, torch.float32, "logits", (M, E))
+        _dev(ids, torch.int32, "ids", (M, k))
+        _dev(w, torch.float32, "w", (M, k))
+    else:
+        logits = torch.empty((M, E), dtype=torch.float32, device=x.device) if want_logits else None
+        ids = torch.empty((M, k), dtype=torch.int32, device=x.device)
+        w = torch.empty((M, k), dtype=torch.float32, device=x.device)
+    _check(lib().moe_fp8_router_gemm_topk(_ptr(x), _ptr(wr), M, h, E, int(k),
+                                          _ptr(logits) if logits is not None else None, _ptr(ids), _ptr(w),
+                                          _stream(stream)), "moe_fp8_router_gemm_topk")
+    return logits, ids, w
 
 
 def act_quant(x, stream=None):

@@ -14,6 +14,12 @@ hipError_t launch_route_quant(const float* logits, const uint16_t* x, int M, int
                               int32_t* ids, float* tw, uint8_t* xq, float* xs, int what,
                               hipStream_t stream);
 
+// BF16 routing logits x . wr^T (bf16 rows, fp32 accumulation) and the
+// router top-k on them, 32 tokens per workgroup; logits may be null.
+// h % 128 == 0, 1 <= E <= 256, 1 <= k <= min(E, 16).
+hipError_t launch_router_gemm_topk(const uint16_t* x, const uint16_t* wr, int M, int h, int E, int k,
+                                   float* logits, int32_t* ids, float* tw, hipStream_t stream);
+
 // The same plus the grouping of all routes, in one launch, for batches of at
 // most kGroupTailRoutes routes; arrivals is a zero word that the launch
 // leaves at zero.

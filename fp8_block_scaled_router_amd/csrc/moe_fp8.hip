@@ -398,6 +398,19 @@ int router_topk(const float* logits, int M, int E, int k, int32_t* topk_ids, flo
                                               nullptr, nullptr, moe::kRoute, stream));
 }
 
+int moe_fp8_router_gemm_topk(const void* x, const void* wr, int M, int h, int E, int k, float* logits,
+                             int32_t* topk_ids, float* topk_w, hipStream_t stream) {
+    if (M < 0 || h <= 0 || E <= 0 || k <= 0) return MOE_ERR_INVALID;
+    if (h % 128 != 0 || h > MOE_FP8_MAX_HIDDEN || E > MOE_FP8_MAX_EXPERTS || k > MOE_FP8_MAX_TOPK || k > E)
+        return MOE_ERR_UNSUPPORTED;
+    if (M == 0) return MOE_OK;
+    if (!x || !wr || !topk_ids || !topk_w) return MOE_ERR_INVALID;
+    if (!aligned16(x) || !aligned16(wr)) return MOE_ERR_INVALID;
+    return hip_status(moe::launch_router_gemm_topk(static_cast<const uint16_t*>(x),
+                                                   static_cast<const uint16_t*>(wr), M, h, E, k, logits,
+                                                   topk_ids, topk_w, stream));
+}
+
 int moe_fp8_act_quant(const void* x, int M, int K, uint8_t* q, float* s, hipStream_t stream) {
     if (M < 0 || K <= 0) return MOE_ERR_INVALID;
     if (K % 128 != 0 || K > MOE_FP8_MAX_HIDDEN) return MOE_ERR_UNSUPPORTED;

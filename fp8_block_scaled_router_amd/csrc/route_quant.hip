@@ -318,6 +318,129 @@ hipError_t launch_route_quant_group(const float* logits, const uint16_t* x, int 
     return hipGetLastError();
 }
 
+// ------------------------------------------------ BF16 routing logits + top-k
+//
+// BF16 routing (Netra Kernel README capability table; Inferact amd-kernels
+// README, routing entries): logits[t][e] = sum_j x[t][j] * wr[e][j] over bf16
+// hidden rows and a bf16 router weight, then the top-k of step 1 on those
+// logits, in one launch.  Each workgroup takes 32 tokens (two 16-row MFMA
+// fragments) and every expert; its four waves split K (wave w takes the
+// 128-column steps w, w + 4, ...), so each wave streams a quarter of the
+// router weight with all of a step's loads in flight at once.  A lane reads
+// 32 contiguous bytes of its row per load pair, so the four lanes of a row
+// cover whole 128-byte lines.  v_mfma_f32_16x16x32_bf16 accumulates in fp32:
+// every bf16 product is exact in fp32, the additions are not (the oracle
+// rounds a float64 sum once).  The four partial tiles are added in LDS in wave
+// order, each element by one thread (deterministic), the 32 x E logits go out to `logits` when asked, and
+// router_rows16 routes the 32 tokens from LDS, four per wave per pass.
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+constexpr int kRgTokens = 32;
+
+__device__ __forceinline__ v4f mfma_16x16x32_bf16(const uint4& a, const uint4& b, const v4f& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c,
+                                                   0, 0, 0);
+}
+
+// 16 bytes of a row at element offset k0 + 64 p + 8 hf + 16 q (the lane's
+// piece u = 2 p + hf of a 128-column step); A and B use the same positions.
+__device__ __forceinline__ void load_step(const uint16_t* __restrict__ rowq, int k0, uint4 f[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) f[u] = *reinterpret_cast<const uint4*>(rowq + k0 + 64 * (u >> 1) + 8 * (u & 1));
+}
+
+// NFMAX: expert fragments the template holds (E <= 16 * NFMAX), loaded eight
+// at a time per step.
+template <int NFMAX>
+__global__ __launch_bounds__(256) void router_gemm_topk_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int M, int h, int E, int k,
+    float* __restrict__ logits, int32_t* __restrict__ ids, float* __restrict__ tw) {
+    __shared__ float part[4][kRgTokens * 16 * NFMAX];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int row = lane & 15, q = lane >> 4;
+    const int t0 = blockIdx.x * kRgTokens;
+    const int Ml = min(kRgTokens, M - t0);
+    const int NF = (E + 15) >> 4;
+    const int nsteps = h / 128;
+
+    // Rows past M or E read a live row instead; their results are dropped.
+    const uint16_t* xp[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        const int t = t0 + 16 * m + row;
+        xp[m] = x + (size_t)(t < M ? t : t0) * h + 16 * q;
+    }
+    v4f acc[2][NFMAX];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int j = 0; j < NFMAX; ++j) acc[m][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    for (int st = wave; st < nsteps; st += 4) {
+        const int k0 = 128 * st;
+        uint4 a[2][4];
+        load_step(xp[0], k0, a[0]);
+        load_step(xp[1], k0, a[1]);
+#pragma unroll
+        for (int c = 0; c < NFMAX; c += 8) {
+            if (c < NF) {
+                uint4 b[8][4];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int e = 16 * (c + j) + row;
+                    load_step(wr + (size_t)(e < E ? e : 0) * h + 16 * q, k0, b[j]);
+                }
+                // Keep every load of the step ahead of the first MFMA: left to
+                // itself the scheduler sinks each load to its use and the step
+                // becomes a chain of dependent memory round trips.
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+#pragma unroll
+                        for (int m = 0; m < 2; ++m)
+                            acc[m][c + j] = mfma_16x16x32_bf16(a[m][u], b[j][u], acc[m][c + j]);
+            }
+        }
+    }
+    // Lane (row, q) of tile (m, j) holds expert 16 j + row of tokens
+    // 16 m + 4 q + v.  Each wave stores its partial tile, then every thread
+    // adds the four partials of its elements in wave order.
+#pragma unroll
+    for (int j = 0; j < NFMAX; ++j) {
+        const int e = 16 * j + row;
+        if (e < E)
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) part[wave][(16 * m + 4 * q + v) * E + e] = acc[m][j][v];
+    }
+    __syncthreads();
+    float* lg = part[0];
+    for (int idx = tid; idx < kRgTokens * E; idx += 256)
+        lg[idx] = ((part[0][idx] + part[1][idx]) + part[2][idx]) + part[3][idx];
+    __syncthreads();
+    if (logits)
+        for (int idx = tid; idx < Ml * E; idx += 256) logits[(size_t)t0 * E + idx] = lg[idx];
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+        const int tl = 16 * pass + 4 * wave;
+        if (tl < Ml) router_rows16(lg, tl, Ml, E, k, ids + (size_t)t0 * k, tw + (size_t)t0 * k, lane);
+    }
+}
+
+hipError_t launch_router_gemm_topk(const uint16_t* x, const uint16_t* wr, int M, int h, int E, int k,
+                                   float* logits, int32_t* ids, float* tw, hipStream_t stream) {
+    if (M <= 0) return hipSuccess;
+    if (E < 1 || E > 256 || h % 128 != 0) return hipErrorInvalidValue;
+    const dim3 grid((M + kRgTokens - 1) / kRgTokens), block(256);
+    if (E <= 128)
+        hipLaunchKernelGGL(router_gemm_topk_kernel<8>, grid, block, 0, stream, x, wr, M, h, E, k, logits, ids, tw);
+    else
+        hipLaunchKernelGGL(router_gemm_topk_kernel<16>, grid, block, 0, stream, x, wr, M, h, E, k, logits, ids, tw);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------ utilities
 
 __global__ __launch_bounds__(256) void encode_e4m3_kernel(const float* __restrict__ in, int64_t n,

@@ -200,6 +200,25 @@ int moe_fp8_workspace_layout(int M, int h, int i, int E, int k, moe_fp8_ws_layou
 int router_topk(const float* logits, int M, int E, int k,
                 int32_t* topk_ids, float* topk_w, hipStream_t stream);
 
+/* BF16 routing, the step before step 1 (Netra Kernel README capability
+ * table: BF16 routing among the gfx950 operation families), fused with the
+ * top-k of router_topk in one launch:
+ *   x bf16 [M, h] (hidden rows), wr bf16 [E, h] (router weight, one row per
+ *   expert) -> logits fp32 [M, E] = x . wr^T (optional: null skips the
+ *   store), topk_ids int32 [M, k] and topk_w fp32 [M, k] exactly as
+ *   router_topk computes them from those logits.
+ * The products are exact; the sums are fp32 matrix-core accumulations, so a
+ * logit may differ from the correctly rounded sum by a small multiple of
+ * 2^-24 * sum_j |x_j wr_j|, and two experts whose logits lie that close may
+ * swap ranks.  Deterministic: the same inputs give the same bits.
+ * All buffers are caller-owned device memory; x and wr 16-byte aligned.
+ * h % 128 == 0 and h <= MOE_FP8_MAX_HIDDEN, E <= MOE_FP8_MAX_EXPERTS,
+ * 1 <= k <= min(E, MOE_FP8_MAX_TOPK) (else MOE_ERR_UNSUPPORTED); a null or
+ * misaligned pointer or a negative size gives MOE_ERR_INVALID; M == 0 is a
+ * no-op.  Enqueued on `stream`. */
+int moe_fp8_router_gemm_topk(const void* x, const void* wr, int M, int h, int E, int k,
+                             float* logits, int32_t* topk_ids, float* topk_w, hipStream_t stream);
+
 /* Step 2 alone: rows of bf16 [M, K] -> q e4m3 [M, K], s fp32 [M, K/128];
  * s = amax/448 of each 1x128 group, q = E4M3(x / s), all-zero groups give
  * s = 0 and zero codes.  K % 128 == 0. */

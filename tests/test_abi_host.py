@@ -97,6 +97,18 @@ def test_other_entry_argument_checks(lib):
     assert rq(FAKE, None, 1e-6, 4, 2048, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID
     assert rq(FAKE, FAKE, 1e-6, 4, 2048, ctypes.c_void_p(0x100008), FAKE, FAKE, None) == moe.MOE_ERR_INVALID
     assert rq(FAKE, FAKE, 1e-6, 0, 2048, None, FAKE, FAKE, None) == moe.MOE_OK
+    rg = lib.moe_fp8_router_gemm_topk
+    assert rg(FAKE, FAKE, 4, 200, 8, 2, None, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED   # h % 128
+    assert rg(FAKE, FAKE, 4, 16384 + 128, 8, 2, None, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert rg(FAKE, FAKE, 4, 256, 257, 2, None, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED  # E > 256
+    assert rg(FAKE, FAKE, 4, 256, 8, 9, None, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED    # k > E
+    assert rg(FAKE, FAKE, 4, 256, 64, 17, None, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED  # k > 16
+    assert rg(FAKE, FAKE, -1, 256, 8, 2, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID
+    assert rg(FAKE, FAKE, 4, 256, 8, 0, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID
+    assert rg(FAKE, None, 4, 256, 8, 2, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID
+    assert rg(FAKE, FAKE, 4, 256, 8, 2, None, None, FAKE, None) == moe.MOE_ERR_INVALID
+    assert rg(ctypes.c_void_p(0x100002), FAKE, 4, 256, 8, 2, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID
+    assert rg(FAKE, FAKE, 0, 256, 8, 2, None, FAKE, FAKE, None) == moe.MOE_OK
     assert lib.moe_fp8_group(FAKE, 4, 8, 2, FAKE, FAKE, FAKE, FAKE, 0, None) == moe.MOE_ERR_WORKSPACE
     assert lib.moe_fp8_group(FAKE, 4, 8, 9, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == moe.MOE_ERR_UNSUPPORTED
     assert lib.moe_fp8_quantize_weight_block128(FAKE, 1, 100, 128, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
