@@ -429,11 +429,79 @@ __global__ __launch_bounds__(256) void router_gemm_topk_kernel(
     }
 }
 
+// The same logits for few tokens, spread over the experts: workgroup
+// (token tile, expert fragment f) computes 32 tokens x experts 16 f .. 16 f + 15
+// and stores them to `logits`; the row router then runs as a second launch.
+// Each logit follows the arithmetic of router_gemm_topk_kernel exactly (wave w
+// sums the steps w, w + 4, ... in ascending order, four MFMAs per step, and the
+// four partials are added in wave order), so both paths give the same bits.
+// A wave issues the loads of up to three of its steps before their MFMAs.
+__global__ __launch_bounds__(256) void router_logits_split_kernel(const uint16_t* __restrict__ x,
+                                                                  const uint16_t* __restrict__ wr, int M, int h,
+                                                                  int E, float* __restrict__ logits) {
+    __shared__ float part[4][kRgTokens * 16];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int row = lane & 15, q = lane >> 4;
+    const int t0 = blockIdx.x * kRgTokens, f = blockIdx.y;
+    const int Ml = min(kRgTokens, M - t0);
+    const int nsteps = h / 128;
+    const uint16_t* xp[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        const int t = t0 + 16 * m + row;
+        xp[m] = x + (size_t)(t < M ? t : t0) * h + 16 * q;
+    }
+    const int e = 16 * f + row;
+    const uint16_t* wp = wr + (size_t)(e < E ? e : 0) * h + 16 * q;
+    v4f acc[2] = {v4f{0.0f, 0.0f, 0.0f, 0.0f}, v4f{0.0f, 0.0f, 0.0f, 0.0f}};
+    for (int st0 = wave; st0 < nsteps; st0 += 12) {
+        uint4 a[3][2][4], b[3][4];
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+            const int k0 = 128 * min(st0 + 4 * r, nsteps - 1);
+            load_step(xp[0], k0, a[r][0]);
+            load_step(xp[1], k0, a[r][1]);
+            load_step(wp, k0, b[r]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int r = 0; r < 3; ++r)
+            if (st0 + 4 * r < nsteps)
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int m = 0; m < 2; ++m) acc[m] = mfma_16x16x32_bf16(a[r][m][u], b[r][u], acc[m]);
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) part[wave][(16 * m + 4 * q + v) * 16 + row] = acc[m][v];
+    __syncthreads();
+    for (int idx = tid; idx < kRgTokens * 16; idx += 256) {
+        const int t = idx >> 4, ee = 16 * f + (idx & 15);
+        if (t < Ml && ee < E)
+            logits[(size_t)(t0 + t) * E + ee] = ((part[0][idx] + part[1][idx]) + part[2][idx]) + part[3][idx];
+    }
+}
+
+// Token tiles below which the experts are spread over workgroups (when the
+// caller keeps the logits): under it the fused kernel would leave most CUs
+// idle while one workgroup per tile streams the whole router weight.
+constexpr int kRgSplitTiles = 128;
+
 hipError_t launch_router_gemm_topk(const uint16_t* x, const uint16_t* wr, int M, int h, int E, int k,
                                    float* logits, int32_t* ids, float* tw, hipStream_t stream) {
     if (M <= 0) return hipSuccess;
     if (E < 1 || E > 256 || h % 128 != 0) return hipErrorInvalidValue;
-    const dim3 grid((M + kRgTokens - 1) / kRgTokens), block(256);
+    const int tiles = (M + kRgTokens - 1) / kRgTokens;
+    if (logits && tiles < kRgSplitTiles) {
+        hipLaunchKernelGGL(router_logits_split_kernel, dim3(tiles, (E + 15) / 16), dim3(256), 0, stream, x, wr, M, h,
+                           E, logits);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        return launch_route_quant(logits, nullptr, M, E, k, 128, ids, tw, nullptr, nullptr, kRoute, stream);
+    }
+    const dim3 grid(tiles), block(256);
     if (E <= 128)
         hipLaunchKernelGGL(router_gemm_topk_kernel<8>, grid, block, 0, stream, x, wr, M, h, E, k, logits, ids, tw);
     else

@@ -210,7 +210,11 @@ int router_topk(const float* logits, int M, int E, int k,
  * The products are exact; the sums are fp32 matrix-core accumulations, so a
  * logit may differ from the correctly rounded sum by a small multiple of
  * 2^-24 * sum_j |x_j wr_j|, and two experts whose logits lie that close may
- * swap ranks.  Deterministic: the same inputs give the same bits.
+ * swap ranks.  Deterministic: the same inputs give the same bits, and a
+ * token's logits do not depend on M or on whether `logits` is null.  With
+ * `logits` non-null and M <= 4064 the call is two launches (the logits spread
+ * over workgroups by expert, then router_topk's kernel on them); otherwise
+ * one launch computes the logits and the top-k together.
  * All buffers are caller-owned device memory; x and wr 16-byte aligned.
  * h % 128 == 0 and h <= MOE_FP8_MAX_HIDDEN, E <= MOE_FP8_MAX_EXPERTS,
  * 1 <= k <= min(E, MOE_FP8_MAX_TOPK) (else MOE_ERR_UNSUPPORTED); a null or

@@ -167,3 +167,21 @@ def test_router_gemm_topk_empty(moe_mod):
     lg, ids, w = moe_mod.router_gemm_topk(x, wr, 2)
     torch.cuda.synchronize()
     assert lg.shape == (0, 8) and ids.shape == (0, 2) and w.shape == (0, 2)
+
+
+def test_router_gemm_split_and_fused_paths_agree(moe_mod):
+    """Few tokens with logits kept take the expert-split kernel plus the row
+    router; many tokens (or no logits) take the fused kernel.  Both sum each
+    logit in the same order, so the same rows give the same bits either way."""
+    rng = np.random.default_rng(23)
+    h, E, k = 1280, 200, 6
+    xb = synth.to_bf16_bits(rng.standard_normal((4160, h)))
+    wb = synth.to_bf16_bits(rng.standard_normal((E, h)) / np.sqrt(h))
+    lg_big, ids_big, w_big = _run(moe_mod, xb, wb, k)                 # 130 tiles: fused
+    for rows in (1, 33, 100):
+        lg, ids, w = _run(moe_mod, xb[:rows], wb, k)                  # split + row router
+        _, ids_f, w_f = _run(moe_mod, xb[:rows], wb, k, want_logits=False)   # fused
+        assert np.array_equal(lg.view(np.uint32), lg_big[:rows].view(np.uint32))
+        assert np.array_equal(ids, ids_big[:rows]) and np.array_equal(ids_f, ids)
+        assert np.array_equal(w.view(np.uint32), w_big[:rows].view(np.uint32))
+        assert np.array_equal(w_f.view(np.uint32), w.view(np.uint32))
