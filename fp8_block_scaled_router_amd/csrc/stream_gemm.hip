@@ -57,25 +57,33 @@ __global__ __launch_bounds__(256) void stream_gate_up_kernel(
         const float* xsr = xs + (size_t)t * KB;
         v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
         for (int kb0 = 0; kb0 < KB; kb0 += kUnrollUp) {
+            // Every load of the batch is issued before any of them is used: the
+            // scales are multiplied only in the MFMA loop (a product here would
+            // make the wave wait for all earlier loads of the batch, since the
+            // memory counter retires in order), and a column past the expert's
+            // routes reads route 0's row (finite codes) and gets a zero scale.
             v8i A[kUnrollUp], B[kUnrollUp];
-            float sc[kUnrollUp];
+            float xsv[kUnrollUp], wsv[kUnrollUp];
 #pragma unroll
             for (int u = 0; u < kUnrollUp; ++u) {
                 const int kb = kb0 + u;
                 if (kb < KB) {
                     A[u] = load_lines(wrow + kb * 128, h, lane);
-                    B[u] = valid ? load32(xrow + kb * 128) : zero8();
-                    sc[u] = (valid ? xsr[kb] : 0.0f) * ws[kb];
+                    B[u] = load32(xrow + kb * 128);
+                    xsv[u] = xsr[kb];
+                    wsv[u] = ws[kb];
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int u = 0; u < kUnrollUp; ++u) {
                 const int kb = kb0 + u;
                 if (kb < KB) {
+                    const float sc = valid ? xsv[u] * wsv[u] : 0.0f;
                     const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
                     const v4f blk = mfma_16x16x128_e4m3(lines_to_frag(A[u], &bounce[wave][u & 1][0], lane, col, kg), B[u], z);
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) acc[v] = fmaf(blk[v], sc[u], acc[v]);
+                    for (int v = 0; v < 4; ++v) acc[v] = fmaf(blk[v], sc, acc[v]);
                 }
             }
         }
@@ -150,25 +158,37 @@ __global__ __launch_bounds__(256) void stream_down_kernel(
         const int p = valid ? sorted[beg + j0 + col] : 0;
         v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
         for (int kb0 = 0; kb0 < IB; kb0 += kUnrollDown) {
+            // As in gate/up: all loads of the batch first, scales multiplied
+            // in the MFMA loop.  The activation codes are read from LDS for
+            // every column; a column past the routes gets a zero scale.
             v8i A[kUnrollDown], B[kUnrollDown];
-            float sc[kUnrollDown];
+            float asv[kUnrollDown], wsv[kUnrollDown];
 #pragma unroll
             for (int u = 0; u < kUnrollDown; ++u) {
                 const int kb = kb0 + u;
                 if (kb < IB) {
                     A[u] = load_lines(wrow + kb * 128, i, lane);
+                    wsv[u] = ws[kb];
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < kUnrollDown; ++u) {
+                const int kb = kb0 + u;
+                if (kb < IB) {
                     B[u] = valid ? load32(a2l + col * astride + kb * 128 + kg * 32) : zero8();
-                    sc[u] = (valid ? a2sl[col * IB + kb] : 0.0f) * ws[kb];
+                    asv[u] = valid ? a2sl[col * IB + kb] : 0.0f;
                 }
             }
 #pragma unroll
             for (int u = 0; u < kUnrollDown; ++u) {
                 const int kb = kb0 + u;
                 if (kb < IB) {
+                    const float sc = asv[u] * wsv[u];
                     const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
                     const v4f blk = mfma_16x16x128_e4m3(lines_to_frag(A[u], bnc + (u & 1) * 2048, lane, col, kg), B[u], z);
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) acc[v] = fmaf(blk[v], sc[u], acc[v]);
+                    for (int v = 0; v < 4; ++v) acc[v] = fmaf(blk[v], sc, acc[v]);
                 }
             }
         }
