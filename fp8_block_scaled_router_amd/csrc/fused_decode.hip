@@ -176,7 +176,10 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
     // ---- phase 0: tag, routing, activation codes and grouping.  The first
     // token's logits and the first batch of x rows are requested before any
     // of them is used.
-    if (tid == 0) misc_l[3] = (int)(ld_agent(a.sync + kSyncEpoch / 4) + 1u);
+    // The forward count is read now and stored to LDS only after routing, so
+    // that its load does not hold up the logits and x loads behind it.
+    uint32_t epoch = 0u;
+    if (tid == 0) epoch = ld_agent(a.sync + kSyncEpoch / 4);
     uint32_t* bm_l = reinterpret_cast<uint32_t*>(misc_l + 8);   // experts present in the batch
     if (tid < 8) bm_l[tid] = 0u;
     const int nq = M * G;   // 16-lane rows of activation groups
@@ -207,6 +210,8 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
         if (t != wave) l_load(t);
         route_fast(lg, E, k, ids_l + t * k, w_l + t * k, lane);
     }
+    asm volatile("" : "+v"(epoch));   // the count is first needed here
+    if (tid == 0) misc_l[3] = (int)(epoch + 1u);
     // the active experts (ascending) right after routing, so that the weight
     // prefetch below is in flight while the activations are quantised and
     // the routes grouped

@@ -25,12 +25,14 @@ namespace moe {
 __device__ __forceinline__ void router_wave(const float* __restrict__ l, int E, int k,
                                             int32_t* __restrict__ ids, float* __restrict__ w,
                                             int lane, bool coherent = false) {
+    // The four loads are unconditional (an index past E reads expert E - 1
+    // and its key is dropped), so they are issued together.
+    float lv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lv[j] = l[min(lane + 64 * j, E - 1)];
     uint32_t key[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int e = lane + 64 * j;
-        key[j] = (e < E) ? float_order_key(l[e]) : 0u;
-    }
+    for (int j = 0; j < 4; ++j) key[j] = (lane + 64 * j < E) ? float_order_key(lv[j]) : 0u;
     int picked[16];
     float pl[16];
 #pragma unroll
@@ -149,11 +151,17 @@ __device__ __forceinline__ void router_rows16(const float* __restrict__ logits, 
     const bool live = t < M;
     const float* l = logits + (size_t)(live ? t : t0) * E;
     const int nq = (E + 15) >> 4;   // logits per lane (uniform)
+    // Unconditional loads (an index past E reads expert E - 1 and its key is
+    // dropped): under a per-lane condition each load was waited for before
+    // the next was issued.
+    float lv[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) lv[q] = l[min(j + 16 * q, E - 1)];
     uint32_t key[16];
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
         const int e = j + 16 * q;
-        key[q] = (q < nq && e < E) ? float_order_key(l[e]) : 0u;
+        key[q] = (q < nq && e < E) ? float_order_key(lv[q]) : 0u;
     }
     int my_e = 0;
     float lmax = 0.0f, sum = 0.0f, my_ex = 0.0f;
