@@ -54,6 +54,12 @@ def lib():
             "oracle_combine": (None, [_P, _P, _I, _I, _I, _P]),
             "oracle_moe_forward": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                                         ctypes.POINTER(_Dbg)]),
+            "oracle_e2m1_decode": (ctypes.c_float, [ctypes.c_uint8]),
+            "oracle_e2m1_encode": (ctypes.c_uint8, [ctypes.c_float]),
+            "oracle_e8m0_decode": (ctypes.c_double, [ctypes.c_uint8]),
+            "oracle_mxfp4_quantize": (None, [_P, _I64, _I, _P, _P]),
+            "oracle_moe_forward_mxfp4": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
+                                              ctypes.POINTER(_Dbg)]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -243,3 +249,77 @@ def moe_forward(x_bits, logits, w13, s13, w2, s2, k: int, intermediates: bool = 
 
 def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+# ------------------------------------------------------------ MXFP4 variant
+
+def e2m1_decode(code: int) -> float:
+    return float(lib().oracle_e2m1_decode(int(code)))
+
+
+def e2m1_encode(v: float) -> int:
+    return int(lib().oracle_e2m1_encode(float(v)))
+
+
+def e8m0_decode(code: int) -> float:
+    return float(lib().oracle_e8m0_decode(int(code)))
+
+
+def mxfp4_quantize(w: np.ndarray):
+    """fp32 [..., K] -> (codes uint8 [..., K/2], E8M0 scales uint8 [..., K/32])
+    (see oracle_mxfp4_quantize)."""
+    w, pw = _c(w, np.float32)
+    K = w.shape[-1]
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    rows = w.size // K
+    codes = np.empty(w.shape[:-1] + (K // 2,), np.uint8)
+    scales = np.empty(w.shape[:-1] + (K // 32,), np.uint8)
+    lib().oracle_mxfp4_quantize(pw, rows, K, codes.ctypes.data, scales.ctypes.data)
+    return codes, scales
+
+
+def mxfp4_dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """float64 values of MXFP4 rows: nibble decode by the oracle's table times
+    2^(scale - 127)."""
+    T = np.array([e2m1_decode(c) for c in range(16)], np.float64)
+    lo, hi = codes & 15, codes >> 4
+    vals = np.stack([T[lo], T[hi]], axis=-1).reshape(codes.shape[:-1] + (codes.shape[-1] * 2,))
+    sc = np.ldexp(1.0, scales.astype(np.int64) - 127)
+    return vals * np.repeat(sc, 32, axis=-1)
+
+
+def moe_forward_mxfp4(x_bits, logits, w13, e13, w2, e2, k: int, intermediates: bool = False):
+    """Whole layer with MXFP4 weights; returns bf16 bits [M, h] (and a dict of
+    intermediates: ids, topk_w, xq, xs, g, a2, a2s, y)."""
+    x, px = _c(x_bits, np.uint16)
+    logits, pl = _c(logits, np.float32)
+    w13, p13 = _c(w13, np.uint8)
+    e13, pe13 = _c(e13, np.uint8)
+    w2, p2 = _c(w2, np.uint8)
+    e2, pe2 = _c(e2, np.uint8)
+    M, h = x.shape
+    E, I2, hh = w13.shape
+    i = I2 // 2
+    if hh * 2 != h or logits.shape != (M, E) or w2.shape != (E, h, i // 2) or e13.shape != (E, I2, h // 32) \
+            or e2.shape != (E, h, i // 32):
+        raise ValueError("inconsistent shapes")
+    out = np.empty((M, h), dtype=np.uint16)
+    dbg = None
+    arrays = {}
+    if intermediates:
+        R = M * k
+        arrays = dict(ids=np.empty(R, np.int32), topk_w=np.empty(R, np.float32),
+                      xq=np.empty((M, h), np.uint8), xs=np.empty((M, h // 128), np.float32),
+                      g=np.empty((R, 2 * i), np.float32), a2=np.empty((R, i), np.uint8),
+                      a2s=np.empty((R, i // 128), np.float32), y=np.empty((R, h), np.float32))
+        dbg = _Dbg(**{n: a.ctypes.data for n, a in arrays.items()})
+    rc = lib().oracle_moe_forward_mxfp4(px, pl, p13, pe13, p2, pe2, out.ctypes.data, M, h, i, E, k,
+                                        ctypes.byref(dbg) if dbg is not None else None)
+    if rc != 0:
+        raise ValueError(f"oracle_moe_forward_mxfp4 rejected the shape (rc={rc})")
+    if intermediates:
+        arrays["ids"] = arrays["ids"].reshape(M, k)
+        arrays["topk_w"] = arrays["topk_w"].reshape(M, k)
+        return out, arrays
+    return out

@@ -477,3 +477,146 @@ int oracle_moe_forward(const uint16_t* x, const float* logits,
     free(a2s); free(y); free(gs); free(ys);
     return 0;
 }
+
+/* ------------------------------------------------------------------ */
+/* MXFP4 weight variant                                                 */
+/* ------------------------------------------------------------------ */
+
+/* E2M1 (OCP MX FP4): bit 3 sign, bits 2..1 exponent (bias 1), bit 0
+ * mantissa.  Exponent 0 is subnormal (m * 0.5); otherwise (1 + m/2) *
+ * 2^(e - 1).  No infinities or NaN; the largest magnitude is 6. */
+static const float E2M1[16] = {
+    0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f,
+    -0.0f, -0.5f, -1.0f, -1.5f, -2.0f, -3.0f, -4.0f, -6.0f,
+};
+
+float oracle_e2m1_decode(uint8_t code) { return E2M1[code & 15]; }
+
+/* Nearest E2M1 value; a tie goes to the code whose mantissa bit is 0
+ * (round to nearest even); |v| above 6 gives +-6; the sign of zero is kept.
+ * Found by comparing |v| with each non-negative value in ascending order. */
+uint8_t oracle_e2m1_encode(float v)
+{
+    const uint8_t sign = signbit(v) ? 8 : 0;
+    const double a = fabs((double)v);
+    if (isnan(v)) return 7;
+    if (a >= 6.0) return (uint8_t)(sign | 7);   /* saturation (also keeps huge |v| exact) */
+    int best = 0;
+    for (int c = 1; c < 8; ++c) {
+        const double dc = fabs(a - (double)E2M1[c]), db = fabs(a - (double)E2M1[best]);
+        if (dc < db || (dc == db && (c & 1) == 0)) best = c;
+    }
+    return (uint8_t)(sign | best);
+}
+
+/* E8M0 block scale: 2^(code - 127); code 255 is NaN (never produced here). */
+double oracle_e8m0_decode(uint8_t code) { return code == 255 ? NAN : ldexp(1.0, (int)code - 127); }
+
+/* OCP MX quantisation of fp32 rows [rows][K] in blocks of 32 along K:
+ * shared exponent e = floor(log2(amax)) - 2 (2 = the largest E2M1 exponent),
+ * clamped to [-127, 127], scale code e + 127; element code = E2M1(w * 2^-e)
+ * (exact scaling by a power of two).  amax == 0 gives scale code 0 and zero
+ * codes.  codes [rows][K/2]: element 2j in the low nibble of byte j, 2j + 1
+ * in the high nibble; scales [rows][K/32]. */
+void oracle_mxfp4_quantize(const float* w, int64_t rows, int K, uint8_t* codes, uint8_t* scales)
+{
+    const int nb = K / 32;
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int b = 0; b < nb; ++b) {
+            const float* v = w + r * K + (int64_t)b * 32;
+            double amax = 0.0;
+            for (int j = 0; j < 32; ++j) amax = fmax(amax, fabs((double)v[j]));
+            int e = -127;
+            if (amax > 0.0) {
+                int ex;
+                frexp(amax, &ex);          /* amax = f * 2^ex, f in [0.5, 1) */
+                e = (ex - 1) - 2;          /* floor(log2(amax)) - 2 */
+                if (e < -127) e = -127;
+                if (e > 127) e = 127;
+            }
+            scales[r * nb + b] = (uint8_t)(amax > 0.0 ? e + 127 : 0);
+            for (int j = 0; j < 32; j += 2) {
+                uint8_t c0 = 0, c1 = 0;
+                if (amax > 0.0) {
+                    c0 = oracle_e2m1_encode((float)ldexp((double)v[j], -e));
+                    c1 = oracle_e2m1_encode((float)ldexp((double)v[j + 1], -e));
+                }
+                codes[r * (K / 2) + (int64_t)b * 16 + j / 2] = (uint8_t)(c0 | (c1 << 4));
+            }
+        }
+    }
+}
+
+/* One GEMM row of the MXFP4 variant: out[n] = fp32( sum over k of
+ * E2M1(W[n][k]) * 2^(S[n][k/32] - 127) * E4M3(a[k]) * as[k/128] ), every
+ * term exact in float64, summed in float64 in ascending k, rounded once. */
+static void mx_gemm_row(const uint8_t* a, const float* as, const uint8_t* W, const uint8_t* S,
+                        int N, int K, float* out)
+{
+    for (int n = 0; n < N; ++n) {
+        const uint8_t* wr = W + (int64_t)n * (K / 2);
+        const uint8_t* sr = S + (int64_t)n * (K / 32);
+        double acc = 0.0;
+        for (int kk = 0; kk < K; ++kk) {
+            const uint8_t c = (uint8_t)((wr[kk / 2] >> ((kk & 1) * 4)) & 15);
+            const double wv = (double)E2M1[c] * oracle_e8m0_decode(sr[kk / 32]);
+            acc += wv * (double)E4M3[a[kk]] * (double)as[kk / 128];
+        }
+        out[n] = (float)acc;
+    }
+}
+
+int oracle_moe_forward_mxfp4(const uint16_t* x, const float* logits,
+                             const uint8_t* w13, const uint8_t* e13,
+                             const uint8_t* w2, const uint8_t* e2,
+                             uint16_t* out, int M, int h, int i, int E, int k,
+                             oracle_intermediates* dbg)
+{
+    if (M < 0 || h <= 0 || i <= 0 || E <= 0 || k < 1 || k > E) return -1;
+    if (h % 128 != 0 || i % 128 != 0) return -1;
+    if (M == 0) return 0;
+    const int R = M * k;
+    int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)R);
+    float* tw = (float*)malloc(sizeof(float) * (size_t)R);
+    uint8_t* xq = (uint8_t*)malloc((size_t)M * h);
+    float* xs = (float*)malloc(sizeof(float) * (size_t)M * (h / 128));
+    float* g = (float*)malloc(sizeof(float) * (size_t)R * 2 * i);
+    uint8_t* a2 = (uint8_t*)malloc((size_t)R * i);
+    float* a2s = (float*)malloc(sizeof(float) * (size_t)R * (i / 128));
+    float* y = (float*)malloc(sizeof(float) * (size_t)R * h);
+
+    /* routing and the 1x128 activation quantisation as in the FP8 layer */
+    oracle_router(logits, M, E, k, ids, tw);
+    oracle_act_quant(x, M, h, xq, xs);
+    /* gate/up per route (route p = t * k + r reads token t, expert ids[p]) */
+    #pragma omp parallel for schedule(dynamic)
+    for (int p = 0; p < R; ++p) {
+        const int t = p / k, e = ids[p];
+        mx_gemm_row(xq + (int64_t)t * h, xs + (int64_t)t * (h / 128),
+                    w13 + (int64_t)e * 2 * i * (h / 2), e13 + (int64_t)e * 2 * i * (h / 32),
+                    2 * i, h, g + (int64_t)p * 2 * i);
+    }
+    oracle_silu_mul_quant(g, R, i, a2, a2s);
+    #pragma omp parallel for schedule(dynamic)
+    for (int p = 0; p < R; ++p) {
+        const int e = ids[p];
+        mx_gemm_row(a2 + (int64_t)p * i, a2s + (int64_t)p * (i / 128),
+                    w2 + (int64_t)e * h * (i / 2), e2 + (int64_t)e * h * (i / 32),
+                    h, i, y + (int64_t)p * h);
+    }
+    oracle_combine(y, tw, M, k, h, out);
+
+    if (dbg) {
+        if (dbg->ids) memcpy(dbg->ids, ids, sizeof(int32_t) * (size_t)R);
+        if (dbg->topk_w) memcpy(dbg->topk_w, tw, sizeof(float) * (size_t)R);
+        if (dbg->xq) memcpy(dbg->xq, xq, (size_t)M * h);
+        if (dbg->xs) memcpy(dbg->xs, xs, sizeof(float) * (size_t)M * (h / 128));
+        if (dbg->g) memcpy(dbg->g, g, sizeof(float) * (size_t)R * 2 * i);
+        if (dbg->a2) memcpy(dbg->a2, a2, (size_t)R * i);
+        if (dbg->a2s) memcpy(dbg->a2s, a2s, sizeof(float) * (size_t)R * (i / 128));
+        if (dbg->y) memcpy(dbg->y, y, sizeof(float) * (size_t)R * h);
+    }
+    free(ids); free(tw); free(xq); free(xs); free(g); free(a2); free(a2s); free(y);
+    return 0;
+}

@@ -153,6 +153,38 @@ int oracle_moe_forward(const uint16_t* x, const float* logits,
                        uint16_t* out, int M, int h, int i, int E, int k,
                        oracle_intermediates* dbg);
 
+/* MXFP4 weight variant (Inferact amd-kernels README, naming section: the
+ * MoE kernel moe/mxfp4_h6144_i768_e128_top4; Netra Kernel README, targets
+ * table: MXFP4 checkpoints, and its real-checkpoint checks against staged
+ * FP64 dequantised-MXFP4 references).  Weights are OCP MX FP4: E2M1
+ * elements with one E8M0 power-of-two scale per 32 consecutive K elements.
+ * Activations stay E4M3 with 1x128 fp32 scales, as in the FP8 layer.
+ *  - E2M1 decode: explicit 16-entry table; encode: nearest value, ties to
+ *    the code with mantissa bit 0, saturating to +-6, sign of zero kept.
+ *  - E8M0 decode: 2^(code - 127).
+ *  - Quantisation per 1x32 block: e = floor(log2(amax)) - 2, clamped to
+ *    [-127, 127]; scale code e + 127; element codes E2M1(w * 2^-e); an
+ *    all-zero block has scale code 0 and zero codes.
+ *  - GEMMs: every term E2M1 * 2^(s - 127) * E4M3 * activation scale is
+ *    exact in float64; they are summed in float64 in ascending K and the sum
+ *    is rounded once to fp32 (gate/up results and down partials are fp32).
+ *  - Everything else (routing, activation quantisation, SiLU-mul
+ *    requantisation, rank-order combine) as in oracle_moe_forward. */
+float oracle_e2m1_decode(uint8_t code);
+uint8_t oracle_e2m1_encode(float v);
+double oracle_e8m0_decode(uint8_t code);
+/* w fp32 [rows][K] -> codes [rows][K/2] (element 2j low nibble of byte j),
+ * scales E8M0 [rows][K/32].  K % 32 == 0. */
+void oracle_mxfp4_quantize(const float* w, int64_t rows, int K, uint8_t* codes, uint8_t* scales);
+/* Whole layer with MXFP4 weights: w13 [E][2i][h/2] + e13 [E][2i][h/32];
+ * w2 [E][h][i/2] + e2 [E][h][i/32].  Other arguments and intermediates as in
+ * oracle_moe_forward (counts, offsets and sorted are not filled). */
+int oracle_moe_forward_mxfp4(const uint16_t* x, const float* logits,
+                             const uint8_t* w13, const uint8_t* e13,
+                             const uint8_t* w2, const uint8_t* e2,
+                             uint16_t* out, int M, int h, int i, int E, int k,
+                             oracle_intermediates* dbg);
+
 #ifdef __cplusplus
 }
 #endif
