@@ -60,6 +60,8 @@ _SIGS = {
     "moe_fp8_workspace_layout": (_I, [_I, _I, _I, _I, _I, ctypes.POINTER(WsLayout)]),
     "router_topk": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "moe_fp8_router_gemm_topk": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P]),
+    "moe_mxfp4_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
+    "moe_mxfp4_forward_ws": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _SZ, _P]),
     "moe_fp8_act_quant": (_I, [_P, _I, _I, _P, _P, _P]),
     "moe_fp8_rmsnorm_act_quant": (_I, [_P, _P, ctypes.c_float, _I, _I, _P, _P, _P, _P]),
     "moe_fp8_group_workspace_bytes": (_SZ, [_I, _I, _I]),
@@ -214,6 +216,42 @@ def router_topk(logits, k: int, stream=None):
     w = torch.empty((M, k), dtype=torch.float32, device=logits.device)
     _check(lib().router_topk(_ptr(logits), M, E, int(k), _ptr(ids), _ptr(w), _stream(stream)), "router_topk")
     return ids, w
+
+
+def mxfp4_workspace_bytes(M: int, h: int, i: int, E: int, k: int) -> int:
+    return int(lib().moe_mxfp4_workspace_bytes(M, h, i, E, k))
+
+
+def alloc_mxfp4_workspace(M: int, h: int, i: int, E: int, k: int, device=None) -> torch.Tensor:
+    """A workspace for moe_mxfp4_forward_ws with its head cleared."""
+    n = mxfp4_workspace_bytes(M, h, i, E, k)
+    if n == 0:
+        raise MoeError(MOE_ERR_UNSUPPORTED, "moe_mxfp4_workspace_bytes")
+    ws = torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+    workspace_init(ws)
+    return ws
+
+
+def moe_mxfp4_forward_ws(x, router_logits, w13, e13, w2, e2, k: int, workspace, out=None, stream=None):
+    """The layer with MXFP4 weights: w13 uint8 codes [E, 2i, h/2] + e13 uint8
+    E8M0 scales [E, 2i, h/32], w2 [E, h, i/2] + e2 [E, h, i/32]."""
+    M, h = x.shape
+    E = router_logits.shape[1]
+    i = w2.shape[2] * 2
+    _dev(x, torch.bfloat16, "x", (M, h))
+    _dev(router_logits, torch.float32, "router_logits", (M, E))
+    _dev(w13, torch.uint8, "w13", (E, 2 * i, h // 2))
+    _dev(e13, torch.uint8, "e13", (E, 2 * i, h // 32))
+    _dev(w2, torch.uint8, "w2", (E, h, i // 2))
+    _dev(e2, torch.uint8, "e2", (E, h, i // 32))
+    _dev(workspace, torch.uint8, "workspace")
+    if out is None:
+        out = torch.empty((M, h), dtype=torch.bfloat16, device=x.device)
+    _dev(out, torch.bfloat16, "out", (M, h))
+    _check(lib().moe_mxfp4_forward_ws(_ptr(x), _ptr(router_logits), _ptr(w13), _ptr(e13), _ptr(w2), _ptr(e2),
+                                      _ptr(out), M, h, i, E, int(k), _ptr(workspace), workspace.numel(),
+                                      _stream(stream)), "moe_mxfp4_forward_ws")
+    return out
 
 
 def router_gemm_topk(x, wr, k: int, want_logits: bool = True, out=None, stream=None):

@@ -50,6 +50,14 @@ hipError_t launch_stream_gate_up(const StreamArgs& a, const uint8_t* xq, const f
 hipError_t launch_stream_down(const StreamArgs& a, const float* g, const uint8_t* w2, const float* s2,
                               float* y, hipStream_t stream);
 
+// The same GEMMs with MXFP4 weights (E2M1 codes two per byte along K, E8M0
+// scales per 32 K elements: w13 [E][2i][h/2] + e13 [E][2i][h/32], w2
+// [E][h][i/2] + e2 [E][h][i/32]).
+hipError_t launch_stream_gate_up_mx(const StreamArgs& a, const uint8_t* xq, const float* xs, const uint8_t* w13,
+                                    const uint8_t* e13, float* g, hipStream_t stream);
+hipError_t launch_stream_down_mx(const StreamArgs& a, const float* g, const uint8_t* w2, const uint8_t* e2,
+                                 float* y, hipStream_t stream);
+
 // Tiled grouped GEMMs for many tokens per expert.
 struct PrefillArgs {
     const uint8_t* xq;

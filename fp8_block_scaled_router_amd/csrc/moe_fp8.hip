@@ -58,7 +58,7 @@ int choose_path(int M, int h, int i, int E, int k) {
     return MOE_FP8_PATH_STREAM;
 }
 
-void make_layout(int M, int h, int i, int E, int k, Layout* L) {
+void make_layout(int M, int h, int i, int E, int k, Layout* L, bool stream_only = false) {
     const size_t R = (size_t)M * k;
     size_t cur = moe::kWorkspaceHead;   // synchronisation words and exchange region first
     auto take = [&](size_t bytes) {
@@ -78,7 +78,7 @@ void make_layout(int M, int h, int i, int E, int k, Layout* L) {
     p.active = take((size_t)E * 4);
     p.num_active = take(4);
     L->hist = take((size_t)moe::group_chunks((int)R) * E * 4);
-    p.path = choose_path(M, h, i, E, k);
+    p.path = stream_only ? MOE_FP8_PATH_STREAM : choose_path(M, h, i, E, k);
     L->mtile_off = take((size_t)(E + 1) * 4);
     p.gate_up = (size_t)-1;
     p.act2 = (size_t)-1;
@@ -270,9 +270,84 @@ int run_forward(const void* x, const float* router_logits, const void* w13, cons
     return hook.mark() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+// The MXFP4-weight layer: routing, quantisation and grouping as in the FP8
+// layer, then the MXFP4 streaming GEMMs and the fp32 combine.
+int run_forward_mx(const void* x, const float* router_logits, const void* w13, const void* e13, const void* w2,
+                   const void* e2, void* out, int M, int h, int i, int E, int k, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
+    int rc = check_shape(M, h, i, E, k);
+    if (rc != MOE_OK) return rc;
+    if (M == 0) return MOE_OK;
+    if (!x || !router_logits || !w13 || !e13 || !w2 || !e2 || !out) return MOE_ERR_INVALID;
+    if (!aligned16(x) || !aligned16(router_logits) || !aligned16(w13) || !aligned16(w2) || !aligned16(out) ||
+        ((uintptr_t)e13 & 3u) != 0 || ((uintptr_t)e2 & 3u) != 0)
+        return MOE_ERR_INVALID;
+    Layout L;
+    make_layout(M, h, i, E, k, &L, true);
+    if (!workspace || ((uintptr_t)workspace % kAlign) != 0 || workspace_bytes < L.pub.total)
+        return MOE_ERR_WORKSPACE;
+    const moe_fp8_ws_layout& p = L.pub;
+    const int R = M * k;
+    int32_t* ids = at<int32_t>(workspace, p.topk_ids);
+    float* tw = at<float>(workspace, p.topk_w);
+    uint8_t* xq = at<uint8_t>(workspace, p.xq);
+    float* xs = at<float>(workspace, p.xs);
+    int32_t* counts = at<int32_t>(workspace, p.counts);
+    int32_t* offsets = at<int32_t>(workspace, p.offsets);
+    int32_t* sorted = at<int32_t>(workspace, p.sorted);
+    int32_t* active = at<int32_t>(workspace, p.active);
+    int32_t* num_active = at<int32_t>(workspace, p.num_active);
+    int32_t* hist = at<int32_t>(workspace, L.hist);
+    float* g = at<float>(workspace, p.gate_up);
+    float* y = at<float>(workspace, p.partial);
+    uint32_t* sync = at<uint32_t>(workspace, 0);
+    if (small_group(M, k)) {
+        rc = hip_status(moe::launch_route_quant_group(router_logits, static_cast<const uint16_t*>(x), M, E, k, h,
+                                                      ids, tw, xq, xs, counts, offsets, sorted, active,
+                                                      num_active, sync + moe::kSyncArrive / 4, stream));
+    } else {
+        rc = hip_status(moe::launch_route_quant(router_logits, static_cast<const uint16_t*>(x), M, E, k, h, ids,
+                                                tw, xq, xs, moe::kRoute | moe::kQuant, stream));
+        if (rc == MOE_OK)
+            rc = hip_status(moe::launch_group(ids, R, E, hist, counts, offsets, sorted, active, num_active,
+                                              stream));
+    }
+    if (rc != MOE_OK) return rc;
+    moe::StreamArgs sa;
+    sa.offsets = offsets;
+    sa.sorted = sorted;
+    sa.active = active;
+    sa.num_active = num_active;
+    sa.max_slots = E < R ? E : R;
+    sa.h = h;
+    sa.i = i;
+    sa.k = k;
+    rc = hip_status(moe::launch_stream_gate_up_mx(sa, xq, xs, static_cast<const uint8_t*>(w13),
+                                                  static_cast<const uint8_t*>(e13), g, stream));
+    if (rc != MOE_OK) return rc;
+    rc = hip_status(moe::launch_stream_down_mx(sa, g, static_cast<const uint8_t*>(w2),
+                                               static_cast<const uint8_t*>(e2), y, stream));
+    if (rc != MOE_OK) return rc;
+    return hip_status(moe::launch_combine(y, tw, M, k, h, static_cast<uint16_t*>(out), stream));
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t moe_mxfp4_workspace_bytes(int M, int h, int i, int E, int k) {
+    if (M == 0 || check_shape(M, h, i, E, k) != MOE_OK) return 0;
+    Layout L;
+    make_layout(M, h, i, E, k, &L, true);
+    return L.pub.total;
+}
+
+int moe_mxfp4_forward_ws(const void* x, const float* router_logits, const void* w13, const void* e13,
+                         const void* w2, const void* e2, void* out, int M, int h, int i, int E, int k,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return run_forward_mx(x, router_logits, w13, e13, w2, e2, out, M, h, i, E, k, workspace, workspace_bytes,
+                          stream);
+}
 
 const char* moe_fp8_status_string(int status) {
     switch (status) {

@@ -1,0 +1,221 @@
+// mxfp4_gemm.hip -- weight-streaming grouped GEMMs with MXFP4 weights (OCP MX
+// FP4: E2M1 elements, one E8M0 scale per 32 consecutive K elements) and E4M3
+// activations with 1x128 fp32 scales, for batches with few tokens per expert.
+//
+// The MXFP4 MoE kernel of the Inferact amd-kernels README (naming section,
+// moe/mxfp4_h6144_i768_e128_top4) at the layer's wide-decode shape.  Each wave
+// owns 16 weight rows of one expert and streams them once from HBM (K
+// contiguous, 64 bytes of codes per row per 128-wide K block, four E8M0
+// scales per row per block), feeding gfx950's block-scaled
+// v_mfma_scale_f32_16x16x128_f8f6f4 with the weights as an FP4 A operand and
+// up to 16 of the expert's routes as an FP8 B operand.
+//
+// Operand layout of that instruction with FP4 A and FP8 B (measured with
+// one-hot operands): lane l (row l % 16, group g = l / 16) supplies 32 A
+// nibbles and one E8M0 scale that applies to all of them, so giving group g
+// MX block g of the K block (bytes 16 g .. 16 g + 15 of the row's 64) matches
+// one scale per block.  Those 32 nibbles pair with the FP8 bytes that lane
+// group g' = g of B holds as bytes [16 g', 16 g' + 16) followed by
+// [64 + 16 g', 64 + 16 g' + 16) of the activation's 128-byte K block.  The
+// activation scale is applied after the MFMA, once per K block (the B scale
+// is fixed at 1).
+#include "device.h"
+#include "launch.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kMxRowsPerWave = 16;
+constexpr int kMxRowsPerGroup = 64;
+constexpr int kMxUnrollUp = 4;
+constexpr int kMxUnrollDown = 2;
+constexpr int kE8M0One = 127;
+
+__device__ __forceinline__ v4f mfma_fp4_e4m3(const uint4& a, const v8i& b, int scale_a, const v4f& c) {
+    const v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, b, c, 4, 0, 0, scale_a, 0, kE8M0One);
+}
+
+// The B operand of one 128-byte activation K block for lane group g.
+__device__ __forceinline__ v8i act_operand(const uint8_t* blk, int g) {
+    const uint4 lo = *reinterpret_cast<const uint4*>(blk + 16 * g);
+    const uint4 hi = *reinterpret_cast<const uint4*>(blk + 64 + 16 * g);
+    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+// SiLU(gate) * up of one 128-column group of one route on one 16-lane row,
+// requantised to E4M3 (the same arithmetic as the FP8 streaming path).
+__device__ __forceinline__ void silu_quant_row_mx(const float* __restrict__ gate, const float* __restrict__ up,
+                                                  int sub, uint8_t* __restrict__ q, float* __restrict__ s,
+                                                  bool write_scale) {
+    const float4 g0 = reinterpret_cast<const float4*>(gate + sub * 8)[0];
+    const float4 g1 = reinterpret_cast<const float4*>(gate + sub * 8)[1];
+    const float4 u0 = reinterpret_cast<const float4*>(up + sub * 8)[0];
+    const float4 u1 = reinterpret_cast<const float4*>(up + sub * 8)[1];
+    const float a[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    const float b[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+    float v[8];
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        v[j] = (a[j] / (1.0f + expf(-a[j]))) * b[j];
+        m = fmaxf(m, fabsf(v[j]));
+    }
+    m = row16_max(m);
+    const float sc = m / kE4M3Max;
+    *reinterpret_cast<uint2*>(q + sub * 8) = quant8(v, sc);
+    if (write_scale) *s = sc;
+}
+
+}  // namespace
+
+// g[p][n] for every route p of the expert in slot blockIdx.y and the 64
+// weight rows of blockIdx.x: sum over K blocks of the block-scaled MFMA sum
+// times the activation scale of the block.
+__global__ __launch_bounds__(256) void stream_gate_up_mx_kernel(
+    const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ w13,
+    const uint8_t* __restrict__ e13, const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted,
+    const int32_t* __restrict__ active, const int32_t* __restrict__ num_active, float* __restrict__ g, int h,
+    int i, int k) {
+    const int slot = blockIdx.y;
+    if (slot >= *num_active) return;
+    const int e = active[slot];
+    const int beg = offsets[e], cnt = offsets[e + 1] - beg;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int N = 2 * i, KB = h / 128;
+    const int n0 = blockIdx.x * kMxRowsPerGroup + wave * kMxRowsPerWave;
+    const int col = lane & 15, grp = lane >> 4;
+    // A: lane (row col, group grp) -> 16 bytes of codes and one scale per K block
+    const uint8_t* wrow = w13 + ((size_t)e * N + n0 + col) * (h / 2) + 16 * grp;
+    const uint8_t* srow = e13 + ((size_t)e * N + n0 + col) * (h / 32);
+
+    for (int j0 = 0; j0 < cnt; j0 += 16) {
+        const bool valid = j0 + col < cnt;
+        const int p = valid ? sorted[beg + j0 + col] : sorted[beg];
+        const int t = p / k;
+        const uint8_t* xrow = xq + (size_t)t * h;
+        const float* xsr = xs + (size_t)t * KB;
+        v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int kb0 = 0; kb0 < KB; kb0 += kMxUnrollUp) {
+            // every load of the batch before its first MFMA
+            uint4 A[kMxUnrollUp];
+            v8i B[kMxUnrollUp];
+            uint32_t sw[kMxUnrollUp];
+            float xsv[kMxUnrollUp];
+#pragma unroll
+            for (int u = 0; u < kMxUnrollUp; ++u) {
+                const int kb = kb0 + u;
+                if (kb < KB) {
+                    A[u] = *reinterpret_cast<const uint4*>(wrow + kb * 64);
+                    sw[u] = *reinterpret_cast<const uint32_t*>(srow + 4 * kb);
+                    B[u] = act_operand(xrow + kb * 128, grp);
+                    xsv[u] = xsr[kb];
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < kMxUnrollUp; ++u) {
+                const int kb = kb0 + u;
+                if (kb < KB) {
+                    const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+                    const v4f blk = mfma_fp4_e4m3(A[u], B[u], (int)((sw[u] >> (8 * grp)) & 0xFFu), z);
+                    const float sc = valid ? xsv[u] : 0.0f;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) acc[v] = fmaf(blk[v], sc, acc[v]);
+                }
+            }
+        }
+        if (valid)
+            *reinterpret_cast<float4*>(g + (size_t)p * N + n0 + grp * 4) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    }
+}
+
+__host__ __device__ inline size_t mx_down_lds_bytes(int i) {
+    return ((size_t)16 * (i + 16) + (size_t)16 * (i / 128) * 4 + 15) & ~(size_t)15;
+}
+
+// y[p][n]: SiLU(gate) * up of up to 16 routes requantised into LDS, then the
+// expert's w2 rows streamed with the same block-scaled MFMA.
+__global__ __launch_bounds__(256) void stream_down_mx_kernel(
+    const float* __restrict__ g, const uint8_t* __restrict__ w2, const uint8_t* __restrict__ e2,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted, const int32_t* __restrict__ active,
+    const int32_t* __restrict__ num_active, float* __restrict__ y, int h, int i, int k) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    const int slot = blockIdx.y;
+    if (slot >= *num_active) return;
+    const int e = active[slot];
+    const int beg = offsets[e], cnt = offsets[e + 1] - beg;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int IB = i / 128;
+    const int astride = i + 16;
+    uint8_t* a2l = lds;                                            // [16][astride]
+    float* a2sl = reinterpret_cast<float*>(lds + 16 * astride);    // [16][IB]
+    const int n0 = blockIdx.x * kMxRowsPerGroup + wave * kMxRowsPerWave;
+    const int col = lane & 15, grp = lane >> 4;
+    const uint8_t* wrow = w2 + ((size_t)e * h + n0 + col) * (i / 2) + 16 * grp;
+    const uint8_t* srow = e2 + ((size_t)e * h + n0 + col) * (i / 32);
+
+    for (int j0 = 0; j0 < cnt; j0 += 16) {
+        const int nr = min(16, cnt - j0);
+        __syncthreads();
+        for (int task = wave * 4 + (lane >> 4); task < nr * IB; task += 16) {
+            const int jr = task / IB, b = task - jr * IB;
+            const int p = sorted[beg + j0 + jr];
+            const float* gate = g + (size_t)p * 2 * i + b * 128;
+            silu_quant_row_mx(gate, gate + i, lane & 15, a2l + jr * astride + b * 128, a2sl + jr * IB + b,
+                              (lane & 15) == 0);
+        }
+        __syncthreads();
+        const bool valid = col < nr;
+        const int p = valid ? sorted[beg + j0 + col] : 0;
+        v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int kb0 = 0; kb0 < IB; kb0 += kMxUnrollDown) {
+            uint4 A[kMxUnrollDown];
+            uint32_t sw[kMxUnrollDown];
+#pragma unroll
+            for (int u = 0; u < kMxUnrollDown; ++u) {
+                const int kb = kb0 + u;
+                if (kb < IB) {
+                    A[u] = *reinterpret_cast<const uint4*>(wrow + kb * 64);
+                    sw[u] = *reinterpret_cast<const uint32_t*>(srow + 4 * kb);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < kMxUnrollDown; ++u) {
+                const int kb = kb0 + u;
+                if (kb < IB) {
+                    // rows of the LDS tile past the routes are never read into a
+                    // stored result (their columns get a zero scale)
+                    const v8i B = act_operand(a2l + col * astride + kb * 128, grp);
+                    const float sc = valid ? a2sl[col * IB + kb] : 0.0f;
+                    const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+                    const v4f blk = mfma_fp4_e4m3(A[u], B, (int)((sw[u] >> (8 * grp)) & 0xFFu), z);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) acc[v] = fmaf(blk[v], sc, acc[v]);
+                }
+            }
+        }
+        if (valid)
+            *reinterpret_cast<float4*>(y + (size_t)p * h + n0 + grp * 4) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    }
+}
+
+hipError_t launch_stream_gate_up_mx(const StreamArgs& a, const uint8_t* xq, const float* xs, const uint8_t* w13,
+                                    const uint8_t* e13, float* g, hipStream_t stream) {
+    const dim3 grid((2 * a.i) / kMxRowsPerGroup, a.max_slots);
+    hipLaunchKernelGGL(stream_gate_up_mx_kernel, grid, dim3(256), 0, stream, xq, xs, w13, e13, a.offsets,
+                       a.sorted, a.active, a.num_active, g, a.h, a.i, a.k);
+    return hipGetLastError();
+}
+
+hipError_t launch_stream_down_mx(const StreamArgs& a, const float* g, const uint8_t* w2, const uint8_t* e2,
+                                 float* y, hipStream_t stream) {
+    const dim3 grid(a.h / kMxRowsPerGroup, a.max_slots);
+    hipLaunchKernelGGL(stream_down_mx_kernel, grid, dim3(256), mx_down_lds_bytes(a.i), stream, g, w2, e2,
+                       a.offsets, a.sorted, a.active, a.num_active, y, a.h, a.i, a.k);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -223,6 +223,29 @@ int router_topk(const float* logits, int M, int E, int k,
 int moe_fp8_router_gemm_topk(const void* x, const void* wr, int M, int h, int E, int k,
                              float* logits, int32_t* topk_ids, float* topk_w, hipStream_t stream);
 
+/* The layer with MXFP4 expert weights (Inferact amd-kernels README, naming
+ * section: moe/mxfp4_h6144_i768_e128_top4; Netra Kernel README, targets
+ * table: MXFP4 checkpoints).  Weights are OCP MX FP4: E2M1 codes packed two
+ * per byte along K (element 2j in the low nibble of byte j) with one E8M0
+ * scale (2^(c - 127)) per 32 consecutive K elements:
+ *   w13 [E, 2i, h/2] codes + e13 [E, 2i, h/32] scales (rows [0,i) gate),
+ *   w2  [E, h, i/2]  codes + e2  [E, h, i/32]  scales.
+ * Routing, the 1x128 E4M3 activation quantisation, the SiLU-mul
+ * requantisation and the rank-order combine are those of moe_fp8_forward;
+ * the GEMMs run on the block-scaled FP4 x FP8 matrix cores and accumulate in
+ * fp32 (the result differs from the float64 dequantised reference by the
+ * matrix cores' block-sum rounding).  Every batch size takes the
+ * weight-streaming kernels.  The workspace (>= moe_mxfp4_workspace_bytes,
+ * 256-byte aligned) follows the rules of moe_fp8_forward_ws: its head must
+ * be zero before the first forward (moe_fp8_workspace_init).  x, logits, out,
+ * w13 and w2 16-byte aligned, e13 and e2 4-byte aligned, else
+ * MOE_ERR_INVALID; shapes as moe_fp8_forward_ws.  Enqueued on `stream`. */
+size_t moe_mxfp4_workspace_bytes(int M, int h, int i, int E, int k);
+int moe_mxfp4_forward_ws(const void* x, const float* router_logits,
+                         const void* w13, const void* e13, const void* w2, const void* e2,
+                         void* out, int M, int h, int i, int E, int k,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Step 2 alone: rows of bf16 [M, K] -> q e4m3 [M, K], s fp32 [M, K/128];
  * s = amax/448 of each 1x128 group, q = E4M3(x / s), all-zero groups give
  * s = 0 and zero codes.  K % 128 == 0. */

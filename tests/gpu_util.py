@@ -74,7 +74,7 @@ def gate_up_terms(layer, inter) -> np.ndarray:
     return mag
 
 
-def flagged_codes(layer, inter, rel=MFMA_REL):
+def flagged_codes(layer, inter, rel=MFMA_REL, terms=None):
     """(lo, hi, s) for every requantised value [R, i]: the E4M3 codes at the two
     ends of the interval the quotient v / s can reach when each gate/up value
     is off by at most rel * sum|terms| (propagated through SiLU(gate) * up and
@@ -83,7 +83,7 @@ def flagged_codes(layer, inter, rel=MFMA_REL):
     result of the method."""
     g = inter["g"].astype(np.float64)
     i = g.shape[1] // 2
-    dg = rel * gate_up_terms(layer, inter)
+    dg = rel * (gate_up_terms(layer, inter) if terms is None else terms)
     a, u = g[:, :i], g[:, i:]
     da, du = dg[:, :i], dg[:, i:]
     sig = 1.0 / (1.0 + np.exp(-a))
@@ -101,12 +101,13 @@ def flagged_codes(layer, inter, rel=MFMA_REL):
     return _e4m3_codes(q - dq), _e4m3_codes(q + dq), s
 
 
-def flip_allowance(layer, inter) -> np.ndarray:
+def flip_allowance(layer, inter, terms=None, w2_dense=None) -> np.ndarray:
     """Largest change of the output [M, h] that the flagged requantisation
     decisions can cause: the gap between the two codes times the scale, times
-    |w2 column|, times the routing weight."""
+    |w2 column|, times the routing weight.  `terms` and `w2_dense(e)` (float64
+    [h, i]) replace the FP8 layer's own for another weight format."""
     T = _T64()
-    lo, hi, s = flagged_codes(layer, inter)
+    lo, hi, s = flagged_codes(layer, inter, terms=terms)
     step = np.abs(T[hi] - T[lo]) * s                # [R, i], 0 where clear
     ids, tw = inter["ids"], inter["topk_w"]
     M, k = ids.shape
@@ -115,7 +116,10 @@ def flip_allowance(layer, inter) -> np.ndarray:
     for p in np.nonzero(step.any(axis=1))[0]:
         t, r = divmod(int(p), k)
         e = ids[t, r]
-        W2 = T[layer.q2[e]] * np.repeat(np.repeat(layer.s2[e].astype(np.float64), 128, 0), 128, 1)
+        if w2_dense is not None:
+            W2 = w2_dense(e)
+        else:
+            W2 = T[layer.q2[e]] * np.repeat(np.repeat(layer.s2[e].astype(np.float64), 128, 0), 128, 1)
         allow[t] += abs(tw[t, r]) * (np.abs(W2) @ step[p])
     return allow
 

@@ -97,6 +97,17 @@ def test_other_entry_argument_checks(lib):
     assert rq(FAKE, None, 1e-6, 4, 2048, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID
     assert rq(FAKE, FAKE, 1e-6, 4, 2048, ctypes.c_void_p(0x100008), FAKE, FAKE, None) == moe.MOE_ERR_INVALID
     assert rq(FAKE, FAKE, 1e-6, 0, 2048, None, FAKE, FAKE, None) == moe.MOE_OK
+    mx = lib.moe_mxfp4_forward_ws
+    need = lib.moe_mxfp4_workspace_bytes(4, 256, 128, 8, 2)
+    assert need > 0 and lib.moe_mxfp4_workspace_bytes(4, 200, 128, 8, 2) == 0
+    W = ctypes.c_void_p(0x100000)
+    assert mx(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 200, 128, 8, 2, W, need, None) == moe.MOE_ERR_UNSUPPORTED
+    assert mx(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 256, 128, 8, 9, W, need, None) == moe.MOE_ERR_UNSUPPORTED
+    assert mx(FAKE, FAKE, FAKE, ctypes.c_void_p(0x100002), FAKE, FAKE, FAKE, 4, 256, 128, 8, 2, W, need,
+              None) == moe.MOE_ERR_INVALID                                  # scales not 4-byte aligned
+    assert mx(FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, 256, 128, 8, 2, W, need, None) == moe.MOE_ERR_INVALID
+    assert mx(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 256, 128, 8, 2, W, need - 1, None) == moe.MOE_ERR_WORKSPACE
+    assert mx(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 256, 128, 8, 2, W, 0, None) == moe.MOE_OK
     rg = lib.moe_fp8_router_gemm_topk
     assert rg(FAKE, FAKE, 4, 200, 8, 2, None, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED   # h % 128
     assert rg(FAKE, FAKE, 4, 16384 + 128, 8, 2, None, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
