@@ -58,7 +58,11 @@ def parse():
                     help="time the RMSNorm + 1x128 quantisation front end alone on --config's activations")
     ap.add_argument("--router-gemm", action="store_true",
                     help="time BF16 routing fused with the top-k alone on --config's activations")
-    return ap.parse_args()
+    ap.add_argument("--mxfp4", action="store_true",
+                    help="time the layer with MXFP4 expert weights (default shape: the wide-decode batch)")
+    args = ap.parse_args()
+    args.config_given = any(a == "--config" or a.startswith("--config=") for a in sys.argv[1:])
+    return args
 
 
 def weight_bytes_per_expert(cfg):
@@ -281,6 +285,101 @@ def router_gemm_bench(args):
     print(json.dumps(line), flush=True)
 
 
+def mxfp4_bench(args):
+    """The layer with MXFP4 expert weights (E2M1 codes, E8M0 scale per 32 K
+    elements) on --config's shape (default: the wide-decode batch, the MXFP4
+    kernel's h 6144 / i 768 / E 128 / top-4).  The codes are uniform random
+    bytes and the scales random powers of two near 2^-8 (values do not change
+    the streamed bytes; routing comes from the shape's own logits).  Weight
+    copies, inputs and workspaces rotate over C copies that together exceed
+    4x the Infinity Cache; stage durations from graph replays of forwards cut
+    after each stage, as in the FP8 bench."""
+    import numpy as np
+    import torch
+
+    import fp8_block_scaled_router_amd as moe
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    moe.lib()
+    dev = torch.device("cuda:0")
+    ci = args.config if args.config_given else 3
+    cfg = synth.CONFIGS[ci]
+    seed = synth.default_seed(ci) if args.seed is None else args.seed
+    M, h, i, E, k = cfg.M, cfg.h, cfg.i, cfg.E, cfg.k
+    w13b = 2 * i * (h // 2) + 2 * i * (h // 32)
+    w2b = h * (i // 2) + h * (i // 32)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+
+    def weights():
+        return (torch.randint(0, 256, (E, 2 * i, h // 2), dtype=torch.uint8, device=dev, generator=gen),
+                torch.randint(117, 122, (E, 2 * i, h // 32), dtype=torch.uint8, device=dev, generator=gen),
+                torch.randint(0, 256, (E, h, i // 2), dtype=torch.uint8, device=dev, generator=gen),
+                torch.randint(117, 122, (E, h, i // 32), dtype=torch.uint8, device=dev, generator=gen))
+
+    ids0, _ = moe.router_topk(torch.from_numpy(synth.make_logits(cfg, seed, copy=0)).to(dev), k)
+    U0 = int(torch.unique(ids0).numel())
+    C = args.copies or max(2, math.ceil(4 * MALL_BYTES / (U0 * (w13b + w2b))) + 1)
+    C = max(1, min(C, int((48 << 30) // (E * (w13b + w2b)))))
+    W = [weights() for _ in range(C)]
+    X, Lg, WS, OUT = [], [], [], []
+    for c in range(C):
+        X.append(torch.from_numpy(synth.make_x(cfg, seed, copy=c).view(np.int16)).view(torch.bfloat16).to(dev))
+        Lg.append(torch.from_numpy(synth.make_logits(cfg, seed, copy=c)).to(dev))
+        WS.append(moe.alloc_mxfp4_workspace(M, h, i, E, k, device=dev))
+        OUT.append(torch.empty((M, h), dtype=torch.bfloat16, device=dev))
+    U = []
+    for c in range(C):
+        ids, _ = moe.router_topk(Lg[c], k)
+        U.append(int(torch.unique(ids).numel()))
+    torch.cuda.synchronize()
+
+    def fwd(c, n=None):
+        a = W[c]
+        moe.moe_mxfp4_forward_ws(X[c], Lg[c], a[0], a[1], a[2], a[3], k, WS[c], out=OUT[c], n_stages=n)
+
+    for c in range(C):
+        fwd(c)
+    torch.cuda.synchronize()
+    assert all(torch.isfinite(OUT[c].float()).all().item() for c in range(C))
+    ms, reps, reps_w = time_single_kernel(lambda c: fwd(c), C, args)
+    names = moe.moe_mxfp4_stage_names(M, k)
+    T = [0.0]
+    for j in range(1, len(names) + 1):
+        tj, _, _ = time_single_kernel(lambda c, j=j: fwd(c, j), C, args)
+        T.append(tj)
+    stage_ms = np.maximum(np.diff(np.array(T)), 0.0)
+    dom = int(np.argmax(stage_ms))
+    Um = float(np.mean(U))
+    work = {"stream_gate_up_mx_kernel": Um * w13b + M * h + 4 * M * h / 128,
+            "stream_down_mx_kernel": Um * w2b,
+            "combine_kernel": 4 * M * k * h + 2 * M * h + 4 * M * k}
+    abytes = work.get(names[dom], 0.0)
+    achieved = abytes / (stage_ms[dom] / 1e3) / 1e9
+    fw_bytes = Um * (w13b + w2b) + M * h * 4 + M * E * 4
+    line = {
+        "metric": "MXFP4 MoE-layer tokens/s",
+        "value": round(M / (ms / 1e3), 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": reps * C, "warmup": reps_w * C, "ms_per_step": round(ms, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "e2m1 weights x e4m3 activations (fp32 accumulate)", "data": "synthetic",
+        "config": {"workload": cfg.name.replace("decode_", "mxfp4_decode_") if "decode" in cfg.name else "mxfp4_" + cfg.name,
+                   "M": M, "h": h, "i": i, "E": E, "k": k, "rotation_copies": C, "distinct_experts_mean": Um,
+                   "layer_bytes_per_step": int(fw_bytes),
+                   "stage_us": {n: round(float(t) * 1e3, 3) for n, t in zip(names, stage_ms)},
+                   "timing": "HIP graph of C forwards; stages from graphs of forwards cut after each stage"},
+        "roofline": {"bound": "hbm", "kernel": names[dom], "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_us": round(stage_ms[dom] * 1e3, 3), "algorithmic_bytes_per_launch": int(abytes),
+                     "forward_hbm_frac": round(fw_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def front_end_bench(args):
     """The RMSNorm + 1x128 E4M3 quantisation front end alone, on the
     activation rows of a layer shape: inputs and outputs rotated over copies
@@ -352,6 +451,9 @@ def main():
         return
     if args.router_gemm:
         router_gemm_bench(args)
+        return
+    if args.mxfp4:
+        mxfp4_bench(args)
         return
 
     import numpy as np

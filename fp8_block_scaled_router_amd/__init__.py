@@ -62,6 +62,7 @@ _SIGS = {
     "moe_fp8_router_gemm_topk": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P]),
     "moe_mxfp4_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "moe_mxfp4_forward_ws": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _SZ, _P]),
+    "moe_mxfp4_forward_ws_prefix": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _SZ, _I, _P]),
     "moe_fp8_act_quant": (_I, [_P, _I, _I, _P, _P, _P]),
     "moe_fp8_rmsnorm_act_quant": (_I, [_P, _P, ctypes.c_float, _I, _I, _P, _P, _P, _P]),
     "moe_fp8_group_workspace_bytes": (_SZ, [_I, _I, _I]),
@@ -232,9 +233,17 @@ def alloc_mxfp4_workspace(M: int, h: int, i: int, E: int, k: int, device=None) -
     return ws
 
 
-def moe_mxfp4_forward_ws(x, router_logits, w13, e13, w2, e2, k: int, workspace, out=None, stream=None):
+def moe_mxfp4_stage_names(M: int, k: int) -> list:
+    """Kernels of one MXFP4 forward in launch order (the prefix stages)."""
+    head = ["route_quant_group_kernel"] if M * k <= 256 else ["route_quant_kernel", "group_hist+group_scatter"]
+    return head + ["stream_gate_up_mx_kernel", "stream_down_mx_kernel", "combine_kernel"]
+
+
+def moe_mxfp4_forward_ws(x, router_logits, w13, e13, w2, e2, k: int, workspace, out=None, stream=None,
+                         n_stages: int | None = None):
     """The layer with MXFP4 weights: w13 uint8 codes [E, 2i, h/2] + e13 uint8
-    E8M0 scales [E, 2i, h/32], w2 [E, h, i/2] + e2 [E, h, i/32]."""
+    E8M0 scales [E, 2i, h/32], w2 [E, h, i/2] + e2 [E, h, i/32].  n_stages
+    cuts the forward after its first n launches (measurement)."""
     M, h = x.shape
     E = router_logits.shape[1]
     i = w2.shape[2] * 2
@@ -248,9 +257,15 @@ def moe_mxfp4_forward_ws(x, router_logits, w13, e13, w2, e2, k: int, workspace, 
     if out is None:
         out = torch.empty((M, h), dtype=torch.bfloat16, device=x.device)
     _dev(out, torch.bfloat16, "out", (M, h))
-    _check(lib().moe_mxfp4_forward_ws(_ptr(x), _ptr(router_logits), _ptr(w13), _ptr(e13), _ptr(w2), _ptr(e2),
-                                      _ptr(out), M, h, i, E, int(k), _ptr(workspace), workspace.numel(),
-                                      _stream(stream)), "moe_mxfp4_forward_ws")
+    if n_stages is None:
+        _check(lib().moe_mxfp4_forward_ws(_ptr(x), _ptr(router_logits), _ptr(w13), _ptr(e13), _ptr(w2),
+                                          _ptr(e2), _ptr(out), M, h, i, E, int(k), _ptr(workspace),
+                                          workspace.numel(), _stream(stream)), "moe_mxfp4_forward_ws")
+    else:
+        _check(lib().moe_mxfp4_forward_ws_prefix(_ptr(x), _ptr(router_logits), _ptr(w13), _ptr(e13), _ptr(w2),
+                                                 _ptr(e2), _ptr(out), M, h, i, E, int(k), _ptr(workspace),
+                                                 workspace.numel(), int(n_stages), _stream(stream)),
+               "moe_mxfp4_forward_ws_prefix")
     return out
 
 

@@ -274,7 +274,7 @@ int run_forward(const void* x, const float* router_logits, const void* w13, cons
 // layer, then the MXFP4 streaming GEMMs and the fp32 combine.
 int run_forward_mx(const void* x, const float* router_logits, const void* w13, const void* e13, const void* w2,
                    const void* e2, void* out, int M, int h, int i, int E, int k, void* workspace,
-                   size_t workspace_bytes, hipStream_t stream) {
+                   size_t workspace_bytes, hipStream_t stream, int n_stages = 1 << 30) {
     int rc = check_shape(M, h, i, E, k);
     if (rc != MOE_OK) return rc;
     if (M == 0) return MOE_OK;
@@ -301,18 +301,22 @@ int run_forward_mx(const void* x, const float* router_logits, const void* w13, c
     float* g = at<float>(workspace, p.gate_up);
     float* y = at<float>(workspace, p.partial);
     uint32_t* sync = at<uint32_t>(workspace, 0);
+    EventHook hook{nullptr, 0, 0, stream, n_stages};
+#define MOE_STEP(call)                 \
+    do {                               \
+        if (hook.cut()) return MOE_OK; \
+        rc = hip_status(call);         \
+        if (rc != MOE_OK) return rc;   \
+    } while (0)
     if (small_group(M, k)) {
-        rc = hip_status(moe::launch_route_quant_group(router_logits, static_cast<const uint16_t*>(x), M, E, k, h,
-                                                      ids, tw, xq, xs, counts, offsets, sorted, active,
-                                                      num_active, sync + moe::kSyncArrive / 4, stream));
+        MOE_STEP(moe::launch_route_quant_group(router_logits, static_cast<const uint16_t*>(x), M, E, k, h, ids, tw,
+                                               xq, xs, counts, offsets, sorted, active, num_active,
+                                               sync + moe::kSyncArrive / 4, stream));
     } else {
-        rc = hip_status(moe::launch_route_quant(router_logits, static_cast<const uint16_t*>(x), M, E, k, h, ids,
-                                                tw, xq, xs, moe::kRoute | moe::kQuant, stream));
-        if (rc == MOE_OK)
-            rc = hip_status(moe::launch_group(ids, R, E, hist, counts, offsets, sorted, active, num_active,
-                                              stream));
+        MOE_STEP(moe::launch_route_quant(router_logits, static_cast<const uint16_t*>(x), M, E, k, h, ids, tw, xq,
+                                         xs, moe::kRoute | moe::kQuant, stream));
+        MOE_STEP(moe::launch_group(ids, R, E, hist, counts, offsets, sorted, active, num_active, stream));
     }
-    if (rc != MOE_OK) return rc;
     moe::StreamArgs sa;
     sa.offsets = offsets;
     sa.sorted = sorted;
@@ -322,13 +326,13 @@ int run_forward_mx(const void* x, const float* router_logits, const void* w13, c
     sa.h = h;
     sa.i = i;
     sa.k = k;
-    rc = hip_status(moe::launch_stream_gate_up_mx(sa, xq, xs, static_cast<const uint8_t*>(w13),
-                                                  static_cast<const uint8_t*>(e13), g, stream));
-    if (rc != MOE_OK) return rc;
-    rc = hip_status(moe::launch_stream_down_mx(sa, g, static_cast<const uint8_t*>(w2),
-                                               static_cast<const uint8_t*>(e2), y, stream));
-    if (rc != MOE_OK) return rc;
-    return hip_status(moe::launch_combine(y, tw, M, k, h, static_cast<uint16_t*>(out), stream));
+    MOE_STEP(moe::launch_stream_gate_up_mx(sa, xq, xs, static_cast<const uint8_t*>(w13),
+                                           static_cast<const uint8_t*>(e13), g, stream));
+    MOE_STEP(moe::launch_stream_down_mx(sa, g, static_cast<const uint8_t*>(w2), static_cast<const uint8_t*>(e2),
+                                        y, stream));
+    MOE_STEP(moe::launch_combine(y, tw, M, k, h, static_cast<uint16_t*>(out), stream));
+#undef MOE_STEP
+    return MOE_OK;
 }
 
 }  // namespace
@@ -347,6 +351,14 @@ int moe_mxfp4_forward_ws(const void* x, const float* router_logits, const void* 
                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
     return run_forward_mx(x, router_logits, w13, e13, w2, e2, out, M, h, i, E, k, workspace, workspace_bytes,
                           stream);
+}
+
+int moe_mxfp4_forward_ws_prefix(const void* x, const float* router_logits, const void* w13, const void* e13,
+                                const void* w2, const void* e2, void* out, int M, int h, int i, int E, int k,
+                                void* workspace, size_t workspace_bytes, int n_stages, hipStream_t stream) {
+    if (n_stages < 0) return MOE_ERR_INVALID;
+    return run_forward_mx(x, router_logits, w13, e13, w2, e2, out, M, h, i, E, k, workspace, workspace_bytes,
+                          stream, n_stages);
 }
 
 const char* moe_fp8_status_string(int status) {

@@ -4,7 +4,7 @@
 //
 // The MXFP4 MoE kernel of the Inferact amd-kernels README (naming section,
 // moe/mxfp4_h6144_i768_e128_top4) at the layer's wide-decode shape.  Each wave
-// owns 16 weight rows of one expert and streams them once from HBM (K
+// owns 32 weight rows (two A fragments) of one expert and streams them once from HBM (K
 // contiguous, 64 bytes of codes per row per 128-wide K block, four E8M0
 // scales per row per block), feeding gfx950's block-scaled
 // v_mfma_scale_f32_16x16x128_f8f6f4 with the weights as an FP4 A operand and
@@ -26,8 +26,8 @@ namespace moe {
 
 namespace {
 
-constexpr int kMxRowsPerWave = 16;
-constexpr int kMxRowsPerGroup = 64;
+constexpr int kMxRowsPerWave = 32;               // two A fragments
+constexpr int kMxRowsPerGroup = 4 * kMxRowsPerWave;
 constexpr int kMxUnrollUp = 4;
 constexpr int kMxUnrollDown = 2;
 constexpr int kE8M0One = 127;
@@ -70,9 +70,29 @@ __device__ __forceinline__ void silu_quant_row_mx(const float* __restrict__ gate
 
 }  // namespace
 
-// g[p][n] for every route p of the expert in slot blockIdx.y and the 64
-// weight rows of blockIdx.x: sum over K blocks of the block-scaled MFMA sum
-// times the activation scale of the block.
+// Scales of K blocks kb0 .. min(kb0 + 3, KB - 1) of one weight row (four
+// bytes per K block, one per MX block): one 16-byte load when the row's
+// scales are 16-byte aligned and all four blocks exist, else dwords.
+__device__ __forceinline__ uint4 load_scales4(const uint8_t* srow, int kb0, int KB, bool vec) {
+    if (vec && kb0 + 4 <= KB) return *reinterpret_cast<const uint4*>(srow + 4 * kb0);
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(srow + 4 * kb0);
+    uint4 r = make_uint4(0u, 0u, 0u, 0u);
+    r.x = p[0];
+    if (kb0 + 1 < KB) r.y = p[1];
+    if (kb0 + 2 < KB) r.z = p[2];
+    if (kb0 + 3 < KB) r.w = p[3];
+    return r;
+}
+
+__device__ __forceinline__ int scale_of(const uint4& s4, int u, int grp) {
+    const uint32_t w = u == 0 ? s4.x : u == 1 ? s4.y : u == 2 ? s4.z : s4.w;
+    return (int)((w >> (8 * grp)) & 0xFFu);
+}
+
+// g[p][n] for every route p of the expert in slot blockIdx.y and the 128
+// weight rows of blockIdx.x (32 per wave: two A fragments share each
+// activation operand, halving the activation loads per weight byte): sum
+// over K blocks of the block-scaled MFMA sum times the activation scale.
 __global__ __launch_bounds__(256) void stream_gate_up_mx_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ w13,
     const uint8_t* __restrict__ e13, const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted,
@@ -86,9 +106,16 @@ __global__ __launch_bounds__(256) void stream_gate_up_mx_kernel(
     const int N = 2 * i, KB = h / 128;
     const int n0 = blockIdx.x * kMxRowsPerGroup + wave * kMxRowsPerWave;
     const int col = lane & 15, grp = lane >> 4;
-    // A: lane (row col, group grp) -> 16 bytes of codes and one scale per K block
-    const uint8_t* wrow = w13 + ((size_t)e * N + n0 + col) * (h / 2) + 16 * grp;
-    const uint8_t* srow = e13 + ((size_t)e * N + n0 + col) * (h / 32);
+    const bool vec = ((h / 32) & 15) == 0 && ((uintptr_t)e13 & 15u) == 0;
+    // A: lane (row col of fragment f, group grp) -> 16 bytes of codes and one
+    // scale per K block
+    const uint8_t* wrow[2];
+    const uint8_t* srow[2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+        wrow[f] = w13 + ((size_t)e * N + n0 + 16 * f + col) * (h / 2) + 16 * grp;
+        srow[f] = e13 + ((size_t)e * N + n0 + 16 * f + col) * (h / 32);
+    }
 
     for (int j0 = 0; j0 < cnt; j0 += 16) {
         const bool valid = j0 + col < cnt;
@@ -96,19 +123,20 @@ __global__ __launch_bounds__(256) void stream_gate_up_mx_kernel(
         const int t = p / k;
         const uint8_t* xrow = xq + (size_t)t * h;
         const float* xsr = xs + (size_t)t * KB;
-        v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        v4f acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
         for (int kb0 = 0; kb0 < KB; kb0 += kMxUnrollUp) {
             // every load of the batch before its first MFMA
-            uint4 A[kMxUnrollUp];
+            uint4 A[2][kMxUnrollUp], S[2];
             v8i B[kMxUnrollUp];
-            uint32_t sw[kMxUnrollUp];
             float xsv[kMxUnrollUp];
+#pragma unroll
+            for (int f = 0; f < 2; ++f) S[f] = load_scales4(srow[f], kb0, KB, vec);
 #pragma unroll
             for (int u = 0; u < kMxUnrollUp; ++u) {
                 const int kb = kb0 + u;
                 if (kb < KB) {
-                    A[u] = *reinterpret_cast<const uint4*>(wrow + kb * 64);
-                    sw[u] = *reinterpret_cast<const uint32_t*>(srow + 4 * kb);
+#pragma unroll
+                    for (int f = 0; f < 2; ++f) A[f][u] = *reinterpret_cast<const uint4*>(wrow[f] + kb * 64);
                     B[u] = act_operand(xrow + kb * 128, grp);
                     xsv[u] = xsr[kb];
                 }
@@ -118,16 +146,22 @@ __global__ __launch_bounds__(256) void stream_gate_up_mx_kernel(
             for (int u = 0; u < kMxUnrollUp; ++u) {
                 const int kb = kb0 + u;
                 if (kb < KB) {
-                    const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
-                    const v4f blk = mfma_fp4_e4m3(A[u], B[u], (int)((sw[u] >> (8 * grp)) & 0xFFu), z);
                     const float sc = valid ? xsv[u] : 0.0f;
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) acc[v] = fmaf(blk[v], sc, acc[v]);
+                    for (int f = 0; f < 2; ++f) {
+                        const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+                        const v4f blk = mfma_fp4_e4m3(A[f][u], B[u], scale_of(S[f], u, grp), z);
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) acc[f][v] = fmaf(blk[v], sc, acc[f][v]);
+                    }
                 }
             }
         }
         if (valid)
-            *reinterpret_cast<float4*>(g + (size_t)p * N + n0 + grp * 4) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+#pragma unroll
+            for (int f = 0; f < 2; ++f)
+                *reinterpret_cast<float4*>(g + (size_t)p * N + n0 + 16 * f + grp * 4) =
+                    make_float4(acc[f][0], acc[f][1], acc[f][2], acc[f][3]);
     }
 }
 
@@ -136,7 +170,7 @@ __host__ __device__ inline size_t mx_down_lds_bytes(int i) {
 }
 
 // y[p][n]: SiLU(gate) * up of up to 16 routes requantised into LDS, then the
-// expert's w2 rows streamed with the same block-scaled MFMA.
+// expert's w2 rows (32 per wave) streamed with the same block-scaled MFMA.
 __global__ __launch_bounds__(256) void stream_down_mx_kernel(
     const float* __restrict__ g, const uint8_t* __restrict__ w2, const uint8_t* __restrict__ e2,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted, const int32_t* __restrict__ active,
@@ -153,8 +187,13 @@ __global__ __launch_bounds__(256) void stream_down_mx_kernel(
     float* a2sl = reinterpret_cast<float*>(lds + 16 * astride);    // [16][IB]
     const int n0 = blockIdx.x * kMxRowsPerGroup + wave * kMxRowsPerWave;
     const int col = lane & 15, grp = lane >> 4;
-    const uint8_t* wrow = w2 + ((size_t)e * h + n0 + col) * (i / 2) + 16 * grp;
-    const uint8_t* srow = e2 + ((size_t)e * h + n0 + col) * (i / 32);
+    const uint8_t* wrow[2];
+    const uint8_t* srow[2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+        wrow[f] = w2 + ((size_t)e * h + n0 + 16 * f + col) * (i / 2) + 16 * grp;
+        srow[f] = e2 + ((size_t)e * h + n0 + 16 * f + col) * (i / 32);
+    }
 
     for (int j0 = 0; j0 < cnt; j0 += 16) {
         const int nr = min(16, cnt - j0);
@@ -169,17 +208,19 @@ __global__ __launch_bounds__(256) void stream_down_mx_kernel(
         __syncthreads();
         const bool valid = col < nr;
         const int p = valid ? sorted[beg + j0 + col] : 0;
-        v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        v4f acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
         for (int kb0 = 0; kb0 < IB; kb0 += kMxUnrollDown) {
-            uint4 A[kMxUnrollDown];
-            uint32_t sw[kMxUnrollDown];
+            uint4 A[2][kMxUnrollDown];
+            uint32_t sw[2][kMxUnrollDown];
 #pragma unroll
             for (int u = 0; u < kMxUnrollDown; ++u) {
                 const int kb = kb0 + u;
-                if (kb < IB) {
-                    A[u] = *reinterpret_cast<const uint4*>(wrow + kb * 64);
-                    sw[u] = *reinterpret_cast<const uint32_t*>(srow + 4 * kb);
-                }
+                if (kb < IB)
+#pragma unroll
+                    for (int f = 0; f < 2; ++f) {
+                        A[f][u] = *reinterpret_cast<const uint4*>(wrow[f] + kb * 64);
+                        sw[f][u] = *reinterpret_cast<const uint32_t*>(srow[f] + 4 * kb);
+                    }
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -190,15 +231,21 @@ __global__ __launch_bounds__(256) void stream_down_mx_kernel(
                     // stored result (their columns get a zero scale)
                     const v8i B = act_operand(a2l + col * astride + kb * 128, grp);
                     const float sc = valid ? a2sl[col * IB + kb] : 0.0f;
-                    const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
-                    const v4f blk = mfma_fp4_e4m3(A[u], B, (int)((sw[u] >> (8 * grp)) & 0xFFu), z);
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) acc[v] = fmaf(blk[v], sc, acc[v]);
+                    for (int f = 0; f < 2; ++f) {
+                        const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+                        const v4f blk = mfma_fp4_e4m3(A[f][u], B, (int)((sw[f][u] >> (8 * grp)) & 0xFFu), z);
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) acc[f][v] = fmaf(blk[v], sc, acc[f][v]);
+                    }
                 }
             }
         }
         if (valid)
-            *reinterpret_cast<float4*>(y + (size_t)p * h + n0 + grp * 4) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+#pragma unroll
+            for (int f = 0; f < 2; ++f)
+                *reinterpret_cast<float4*>(y + (size_t)p * h + n0 + 16 * f + grp * 4) =
+                    make_float4(acc[f][0], acc[f][1], acc[f][2], acc[f][3]);
     }
 }
 

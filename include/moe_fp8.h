@@ -245,6 +245,15 @@ int moe_mxfp4_forward_ws(const void* x, const float* router_logits,
                          const void* w13, const void* e13, const void* w2, const void* e2,
                          void* out, int M, int h, int i, int E, int k,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+/* Measurement: the same forward cut after its first n_stages launches (the
+ * stages are route+quant(+group), [group], gate/up, down, combine; graph
+ * replays of cut forwards give per-stage durations).  n_stages < 0 gives
+ * MOE_ERR_INVALID. */
+int moe_mxfp4_forward_ws_prefix(const void* x, const float* router_logits,
+                                const void* w13, const void* e13, const void* w2, const void* e2,
+                                void* out, int M, int h, int i, int E, int k,
+                                void* workspace, size_t workspace_bytes, int n_stages,
+                                hipStream_t stream);
 
 /* Step 2 alone: rows of bf16 [M, K] -> q e4m3 [M, K], s fp32 [M, K/128];
  * s = amax/448 of each 1x128 group, q = E4M3(x / s), all-zero groups give
