@@ -54,6 +54,7 @@ def parse():
                          "the copy calibration: record the kernel's HBM bytes per launch in profiles/traffic.json")
     ap.add_argument("--pmc-kernel", default=None, help="kernel for --pmc-summary")
     ap.add_argument("--pmc-copy-mib", type=int, default=1024, help="copy size of the calibration runs")
+    ap.add_argument("--pmc-workload", default=None, help="workload name of the record (default: --config's)")
     ap.add_argument("--front-end", action="store_true",
                     help="time the RMSNorm + 1x128 quantisation front end alone on --config's activations")
     ap.add_argument("--router-gemm", action="store_true",
@@ -84,6 +85,9 @@ KERNEL_SOURCES = {
                                "fp8_block_scaled_router_amd/csrc/launch.h"],
 }
 KERNEL_SOURCES["stream_down_kernel"] = KERNEL_SOURCES["stream_gate_up_kernel"]
+KERNEL_SOURCES["stream_gate_up_mx_kernel"] = ["fp8_block_scaled_router_amd/csrc/mxfp4_gemm.hip",
+                                              "fp8_block_scaled_router_amd/csrc/device.h"]
+KERNEL_SOURCES["stream_down_mx_kernel"] = KERNEL_SOURCES["stream_gate_up_mx_kernel"]
 KERNEL_SOURCES["prefill_down_kernel"] = KERNEL_SOURCES["prefill_gate_up_kernel"]
 
 
@@ -134,7 +138,8 @@ def pmc_summary(args):
     path = os.path.join(ROOT, "profiles", "traffic.json")
     db = json.load(open(path)) if os.path.exists(path) else {}
     srcs = KERNEL_SOURCES[kernel]
-    db[f"{cfg.name}:{kernel}"] = {
+    name = args.pmc_workload or cfg.name
+    db[f"{name}:{kernel}"] = {
         "bytes_per_launch": int(round(fetch + write)),
         "fetch_bytes_per_launch": int(round(fetch)), "write_bytes_per_launch": int(round(write)),
         "raw_fetch_kib": round(fk, 1), "raw_write_kib": round(wk, 1), "dispatches": [nf, nw],
@@ -145,7 +150,7 @@ def pmc_summary(args):
     with open(path, "w") as f:
         json.dump(db, f, indent=1, sort_keys=True)
         f.write("\n")
-    print(json.dumps(db[f"{cfg.name}:{kernel}"]))
+    print(json.dumps(db[f"{name}:{kernel}"]))
 
 
 def stage_work(cfg, stage, U):
@@ -360,19 +365,21 @@ def mxfp4_bench(args):
     abytes = work.get(names[dom], 0.0)
     achieved = abytes / (stage_ms[dom] / 1e3) / 1e9
     fw_bytes = Um * (w13b + w2b) + M * h * 4 + M * E * 4
+    workload = "mxfp4_" + cfg.name
     line = {
         "metric": "MXFP4 MoE-layer tokens/s",
         "value": round(M / (ms / 1e3), 2), "unit": "tokens/s", "n_gpus": 1,
         "steps": reps * C, "warmup": reps_w * C, "ms_per_step": round(ms, 6),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "e2m1 weights x e4m3 activations (fp32 accumulate)", "data": "synthetic",
-        "config": {"workload": cfg.name.replace("decode_", "mxfp4_decode_") if "decode" in cfg.name else "mxfp4_" + cfg.name,
+        "config": {"workload": workload,
                    "M": M, "h": h, "i": i, "E": E, "k": k, "rotation_copies": C, "distinct_experts_mean": Um,
                    "layer_bytes_per_step": int(fw_bytes),
                    "stage_us": {n: round(float(t) * 1e3, 3) for n, t in zip(names, stage_ms)},
                    "timing": "HIP graph of C forwards; stages from graphs of forwards cut after each stage"},
         "roofline": {"bound": "hbm", "kernel": names[dom], "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": load_traffic(names[dom], workload),
                      "avg_launch_us": round(stage_ms[dom] * 1e3, 3), "algorithmic_bytes_per_launch": int(abytes),
                      "forward_hbm_frac": round(fw_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
         "cpu_baseline": None,
