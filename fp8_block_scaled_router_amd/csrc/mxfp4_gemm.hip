@@ -89,26 +89,37 @@ __device__ __forceinline__ int scale_of(const uint4& s4, int u, int grp) {
     return (int)((w >> (8 * grp)) & 0xFFu);
 }
 
+// Activation staging of the gate/up kernel: a batch of kMxUnrollUp K blocks
+// of the 16 routes of a column block, one 528-byte LDS row per route (512
+// bytes plus 16 of padding, so the 16 routes' fragment reads hit distinct
+// banks), two buffers.
+constexpr int kMxStageRow = 128 * kMxUnrollUp + 16;
+constexpr int kMxStageBytes = 16 * kMxStageRow;
+
 // g[p][n] for every route p of the expert in slot blockIdx.y and the 128
 // weight rows of blockIdx.x (32 per wave: two A fragments share each
-// activation operand, halving the activation loads per weight byte): sum
-// over K blocks of the block-scaled MFMA sum times the activation scale.
+// activation operand): sum over K blocks of the block-scaled MFMA sum times
+// the activation scale.  The activation operands come from LDS: each batch of
+// four K blocks of the column block's 16 routes is fetched once per
+// workgroup (32 bytes per thread), not once per wave, so the waves' vector
+// memory requests are the weights'; the next batch's weights, scales and
+// activations are requested before the current batch is multiplied.
 __global__ __launch_bounds__(256) void stream_gate_up_mx_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ w13,
     const uint8_t* __restrict__ e13, const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted,
     const int32_t* __restrict__ active, const int32_t* __restrict__ num_active, float* __restrict__ g, int h,
     int i, int k) {
+    __shared__ __align__(16) uint8_t stage[2][kMxStageBytes];
     const int slot = blockIdx.y;
     if (slot >= *num_active) return;
     const int e = active[slot];
     const int beg = offsets[e], cnt = offsets[e + 1] - beg;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int N = 2 * i, KB = h / 128;
+    const int nb = (KB + kMxUnrollUp - 1) / kMxUnrollUp;
     const int n0 = blockIdx.x * kMxRowsPerGroup + wave * kMxRowsPerWave;
     const int col = lane & 15, grp = lane >> 4;
     const bool vec = ((h / 32) & 15) == 0 && ((uintptr_t)e13 & 15u) == 0;
-    // A: lane (row col of fragment f, group grp) -> 16 bytes of codes and one
-    // scale per K block
     const uint8_t* wrow[2];
     const uint8_t* srow[2];
 #pragma unroll
@@ -116,47 +127,65 @@ __global__ __launch_bounds__(256) void stream_gate_up_mx_kernel(
         wrow[f] = w13 + ((size_t)e * N + n0 + 16 * f + col) * (h / 2) + 16 * grp;
         srow[f] = e13 + ((size_t)e * N + n0 + 16 * f + col) * (h / 32);
     }
+    // staging thread: route sr of the column block, 32-byte piece sp of a batch
+    const int sr = tid >> 4, sp = tid & 15;
 
     for (int j0 = 0; j0 < cnt; j0 += 16) {
         const bool valid = j0 + col < cnt;
         const int p = valid ? sorted[beg + j0 + col] : sorted[beg];
-        const int t = p / k;
-        const uint8_t* xrow = xq + (size_t)t * h;
-        const float* xsr = xs + (size_t)t * KB;
+        const float* xsr = xs + (size_t)(p / k) * KB;
+        const int ps = j0 + sr < cnt ? sorted[beg + j0 + sr] : sorted[beg];
+        const uint8_t* xst = xq + (size_t)(ps / k) * h + 32 * (sp & 3);
+
+        // Two register sets (batch b uses set b & 1 and stage buffer b & 1);
+        // the loop below is unrolled by two so that each set has a name.
+        uint4 A0[2][kMxUnrollUp], S0[2], X0a, X0b, A1[2][kMxUnrollUp], S1[2], X1a, X1b;
+        float C0[kMxUnrollUp], C1[kMxUnrollUp];   // activation scales of the batch
         v4f acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
-        for (int kb0 = 0; kb0 < KB; kb0 += kMxUnrollUp) {
-            // every load of the batch before its first MFMA
-            uint4 A[2][kMxUnrollUp], S[2];
-            v8i B[kMxUnrollUp];
-            float xsv[kMxUnrollUp];
-#pragma unroll
-            for (int f = 0; f < 2; ++f) S[f] = load_scales4(srow[f], kb0, KB, vec);
-#pragma unroll
-            for (int u = 0; u < kMxUnrollUp; ++u) {
-                const int kb = kb0 + u;
-                if (kb < KB) {
-#pragma unroll
-                    for (int f = 0; f < 2; ++f) A[f][u] = *reinterpret_cast<const uint4*>(wrow[f] + kb * 64);
-                    B[u] = act_operand(xrow + kb * 128, grp);
-                    xsv[u] = xsr[kb];
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int u = 0; u < kMxUnrollUp; ++u) {
-                const int kb = kb0 + u;
-                if (kb < KB) {
-                    const float sc = valid ? xsv[u] : 0.0f;
-#pragma unroll
-                    for (int f = 0; f < 2; ++f) {
-                        const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
-                        const v4f blk = mfma_fp4_e4m3(A[f][u], B[u], scale_of(S[f], u, grp), z);
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) acc[f][v] = fmaf(blk[v], sc, acc[f][v]);
-                    }
-                }
-            }
+#define MX_ISSUE(A, S, Xa, Xb, C, b)                                                                       \
+    do {                                                                                             \
+        const int kb0_ = (b) * kMxUnrollUp;                                                          \
+        _Pragma("unroll") for (int f = 0; f < 2; ++f) S[f] = load_scales4(srow[f], kb0_, KB, vec);   \
+        _Pragma("unroll") for (int u = 0; u < kMxUnrollUp; ++u) if (kb0_ + u < KB) {                 \
+            _Pragma("unroll") for (int f = 0; f < 2; ++f)                                            \
+                A[f][u] = *reinterpret_cast<const uint4*>(wrow[f] + (kb0_ + u) * 64);                \
+            C[u] = xsr[kb0_ + u];                                                                    \
+        }                                                                                            \
+        /* past the last K block the piece reloads the last one (never read) */                    \
+        const int kbs_ = min(kb0_ + sp / 4, KB - 1);                                                 \
+        Xa = *reinterpret_cast<const uint4*>(xst + kbs_ * 128);                                      \
+        Xb = *reinterpret_cast<const uint4*>(xst + kbs_ * 128 + 16);                                 \
+    } while (0)
+#define MX_STEP(A, S, Xa, Xb, C, An, Sn, Xna, Xnb, Cn, bi, b)                                                        \
+    do {                                                                                             \
+        const int kb0_ = (b) * kMxUnrollUp;                                                          \
+        uint8_t* st_ = stage[bi];                                                                    \
+        *reinterpret_cast<uint4*>(st_ + sr * kMxStageRow + 32 * sp) = Xa;                           \
+        *reinterpret_cast<uint4*>(st_ + sr * kMxStageRow + 32 * sp + 16) = Xb;                      \
+        __syncthreads(); /* the batch's activations are in LDS; the other buffer is free */         \
+        if ((b) + 1 < nb) MX_ISSUE(An, Sn, Xna, Xnb, Cn, (b) + 1);                                           \
+        __builtin_amdgcn_sched_barrier(0);                                                           \
+        _Pragma("unroll") for (int u = 0; u < kMxUnrollUp; ++u) {                                    \
+            const int kb = kb0_ + u;                                                                 \
+            if (kb < KB) {                                                                           \
+                const v8i B = act_operand(st_ + col * kMxStageRow + u * 128, grp);                   \
+                const float sc = valid ? C[u] : 0.0f;                                                \
+                _Pragma("unroll") for (int f = 0; f < 2; ++f) {                                      \
+                    const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};                                          \
+                    const v4f blk = mfma_fp4_e4m3(A[f][u], B, scale_of(S[f], u, grp), z);            \
+                    _Pragma("unroll") for (int v = 0; v < 4; ++v) acc[f][v] = fmaf(blk[v], sc, acc[f][v]); \
+                }                                                                                    \
+            }                                                                                        \
+        }                                                                                            \
+    } while (0)
+        MX_ISSUE(A0, S0, X0a, X0b, C0, 0);
+        for (int b = 0; b < nb; b += 2) {
+            MX_STEP(A0, S0, X0a, X0b, C0, A1, S1, X1a, X1b, C1, 0, b);
+            if (b + 1 < nb) MX_STEP(A1, S1, X1a, X1b, C1, A0, S0, X0a, X0b, C0, 1, b + 1);
         }
+#undef MX_STEP
+#undef MX_ISSUE
+        __syncthreads();   // the stage buffers are reused by the next column block
         if (valid)
 #pragma unroll
             for (int f = 0; f < 2; ++f)
