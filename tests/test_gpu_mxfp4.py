@@ -133,10 +133,13 @@ def test_mxfp4_wide_decode_shape_sampled(moe_mod):
     _check_layer(moe_mod, L, tokens=[0, 1, 17, 30, 41, 63])
 
 
-@pytest.mark.parametrize("M,h,i,E,k", [(1, 128, 128, 1, 1), (300, 256, 128, 4, 2), (7, 640, 384, 16, 5)])
+@pytest.mark.parametrize("M,h,i,E,k", [(1, 128, 128, 1, 1), (300, 256, 128, 4, 2), (7, 640, 384, 16, 5),
+                                       (5, 256, 2048, 2, 1)])
 def test_mxfp4_edge_shapes(moe_mod, M, h, i, E, k):
     """One expert and one K block; a batch beyond the one-launch grouping (300
-    tokens, several 16-route column blocks per expert); ragged K batches."""
+    tokens, several 16-route column blocks per expert); ragged K batches and
+    scale rows not 16-byte aligned (h 640); the largest intermediate size
+    (i 2048: 16 K blocks in the down GEMM)."""
     cfg = synth.LayerConfig("mx_edge", M, h, i, E, k, "normal", "test shape")
     _check_layer(moe_mod, _MxLayer(cfg, 91 + M))
 
