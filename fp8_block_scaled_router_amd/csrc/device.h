@@ -164,6 +164,15 @@ __device__ __forceinline__ uint32_t row16_max_u(uint32_t v) {
     return v;
 }
 
+// Unsigned min over the 16 lanes of each DPP row.
+__device__ __forceinline__ uint32_t row16_min_u(uint32_t v) {
+    v = min(v, dpp_u<kDppQuadXor1>(v));
+    v = min(v, dpp_u<kDppQuadXor2>(v));
+    v = min(v, dpp_u<kDppRowHalfMirror>(v));
+    v = min(v, dpp_u<kDppRowMirror>(v));
+    return v;
+}
+
 // Wave-wide lexicographic max of 64-bit keys: DPP inside each row of 16
 // lanes, then the two row swaps.  Every lane gets the result.
 __device__ __forceinline__ void wave_key_max(uint32_t& hi, uint32_t& lo) {

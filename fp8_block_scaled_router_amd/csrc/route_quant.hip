@@ -139,53 +139,72 @@ __device__ __forceinline__ void act_quant_row(const uint16_t* __restrict__ x, in
 }
 
 // Router of four tokens on one wave: DPP row r (16 lanes) routes token
-// t0 + r, lane j of a row holding the logits of experts j, j + 16, ...
-// A pick is the row-wide maximum of the same 64-bit key as in router_wave,
-// reduced by four DPP steps inside the row, so a round costs no cross-row
-// exchange and a quarter of router_wave's lanes per token.  The pick's logit
-// is the same in every lane of the row, so each round adds its exponential
-// to the rank-order sum right away; lane j keeps pick j.
-__device__ __forceinline__ void router_rows16(const float* __restrict__ logits, int t0, int M, int E, int k,
-                                              int32_t* __restrict__ ids, float* __restrict__ w, int lane) {
+// t0 + r, lane j of a row holding the logits of experts j, j + 16, ...  Each
+// lane first sorts its NQ candidates once (bitonic network on (key
+// descending, expert ascending), key = order-preserving bits of the logit),
+// so a round only looks at the lanes' heads: the row maximum of the head
+// keys, then the lowest expert among the heads that reach it (four DPP steps
+// each, inside the row), and the winning lane pops its head.  Equal logits go
+// to the lower expert index and -0 equals +0.  The pick's logit is the same
+// in every lane of the row, so each round adds its exponential to the
+// rank-order sum right away; lane j keeps pick j.
+template <int NQ>
+__device__ __forceinline__ void router_rows16_nq(const float* __restrict__ logits, int t0, int M, int E, int k,
+                                                 int32_t* __restrict__ ids, float* __restrict__ w, int lane) {
     const int r = lane >> 4, j = lane & 15, t = t0 + r;
     const bool live = t < M;
     const float* l = logits + (size_t)(live ? t : t0) * E;
-    const int nq = (E + 15) >> 4;   // logits per lane (uniform)
     // Unconditional loads (an index past E reads expert E - 1 and its key is
     // dropped): under a per-lane condition each load was waited for before
     // the next was issued.
-    float lv[16];
+    float lv[NQ];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) lv[q] = l[min(j + 16 * q, E - 1)];
-    uint32_t key[16];
+    for (int q = 0; q < NQ; ++q) lv[q] = l[min(j + 16 * q, E - 1)];
+    uint32_t key[NQ], idx[NQ];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-        const int e = j + 16 * q;
-        key[q] = (q < nq && e < E) ? float_order_key(lv[q]) : 0u;
+    for (int q = 0; q < NQ; ++q) {
+        idx[q] = (uint32_t)(j + 16 * q);
+        key[q] = (int)idx[q] < E ? float_order_key(lv[q]) : 0u;
+    }
+#pragma unroll
+    for (int kk = 2; kk <= NQ; kk *= 2) {
+#pragma unroll
+        for (int jj = kk / 2; jj > 0; jj /= 2) {
+#pragma unroll
+            for (int a = 0; a < NQ; ++a) {
+                const int b = a ^ jj;
+                if (b > a) {
+                    // ((a & kk) == 0): slot a takes the element that comes first
+                    const bool b_first = key[b] > key[a] || (key[b] == key[a] && idx[b] < idx[a]);
+                    const bool swap = ((a & kk) == 0) == b_first;
+                    const uint32_t ka = key[a], ia = idx[a];
+                    key[a] = swap ? key[b] : ka;
+                    idx[a] = swap ? idx[b] : ia;
+                    key[b] = swap ? ka : key[b];
+                    idx[b] = swap ? ia : idx[b];
+                }
+            }
+        }
     }
     int my_e = 0;
     float lmax = 0.0f, sum = 0.0f, my_ex = 0.0f;
     for (int rr = 0; rr < k; ++rr) {
-        uint32_t hi = 0u, lo = 0u;
+        const uint32_t m = row16_max_u(key[0]);
+        int e = (int)row16_min_u(key[0] == m ? idx[0] : 0xFFFFu);
+        e = (m == 0u || e >= E) ? E - 1 : e;   // only for NaN logits (outside the contract)
+        // The pop as a bit mask the compiler cannot see through: as a
+        // condition it became a register-indexed select chain.
+        uint32_t pm = ((int)idx[0] == e && key[0] != 0u) ? 0xFFFFFFFFu : 0u;
+        asm volatile("" : "+v"(pm));
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            if (q < nq && key[q] > hi) {   // strict: lower q (lower expert) wins ties
-                hi = key[q];
-                lo = 0xFFFFu - (uint32_t)(j + 16 * q);
-            }
+        for (int q = 0; q + 1 < NQ; ++q) {
+            key[q] = (key[q + 1] & pm) | (key[q] & ~pm);
+            idx[q] = (idx[q + 1] & pm) | (idx[q] & ~pm);
         }
-        key_step_dpp<kDppQuadXor1>(hi, lo);
-        key_step_dpp<kDppQuadXor2>(hi, lo);
-        key_step_dpp<kDppRowHalfMirror>(hi, lo);
-        key_step_dpp<kDppRowMirror>(hi, lo);
-        int e = (int)(0xFFFFu - lo);
-        e = (hi == 0u || e >= E) ? E - 1 : e;   // only for NaN logits (outside the contract)
-#pragma unroll
-        for (int q = 0; q < 16; ++q)
-            if (j + 16 * q == e) key[q] = 0u;
-        const float lv = float_from_order_key(hi);
-        if (rr == 0) lmax = lv;
-        const float ex = expf(lv - lmax);
+        key[NQ - 1] &= ~pm;
+        const float pv = float_from_order_key(m);
+        if (rr == 0) lmax = pv;
+        const float ex = expf(pv - lmax);
         sum += ex;
         if (j == rr) {
             my_e = e;
@@ -196,6 +215,16 @@ __device__ __forceinline__ void router_rows16(const float* __restrict__ logits, 
         ids[(size_t)t * k + j] = my_e;
         w[(size_t)t * k + j] = my_ex / sum;
     }
+}
+
+__device__ __forceinline__ void router_rows16(const float* __restrict__ logits, int t0, int M, int E, int k,
+                                              int32_t* __restrict__ ids, float* __restrict__ w, int lane) {
+    if (E <= 64)
+        router_rows16_nq<4>(logits, t0, M, E, k, ids, w, lane);
+    else if (E <= 128)
+        router_rows16_nq<8>(logits, t0, M, E, k, ids, w, lane);
+    else
+        router_rows16_nq<16>(logits, t0, M, E, k, ids, w, lane);
 }
 
 // Four tokens per workgroup of five waves: wave 4 routes the four tokens
