@@ -2,14 +2,14 @@
 // quantisation (gfx950, wave64).
 //
 // Router (Netra Kernel README capability table, "BF16 routing" family;
-// kernel-laboratory README, decode and verification routing kernels): one
-// wave per token.  Each lane holds up to four logits (experts lane + 64j).
-// A pick is the wave-wide maximum of the 64-bit key (order-preserving bits of
-// the logit, 0xFFFF - expert), so equal logits go to the lower expert index
-// and -0 equals +0; the reduction runs DPP inside each 16-lane row and two
-// cross-row exchanges.  k rounds pick k experts in rank order; the weights
-// are exp(l - l_max) of the picks divided by their sum in rank order (the
-// full softmax denominator cancels in the renormalisation).
+// kernel-laboratory README, decode and verification routing kernels): a
+// token's logits are spread over a wave (experts lane + 64q) or over a
+// 16-lane row (experts lane + 16q); each lane sorts its own candidates once,
+// and each of the k rounds takes the largest head key of the group, the
+// lowest expert among the heads that reach it (so equal logits go to the
+// lower expert index, and -0 equals +0), and pops that head.  The weights are
+// exp(l - l_max) of the picks divided by their sum in rank order (the full
+// softmax denominator cancels in the renormalisation).
 //
 // Activation quantisation (Netra compiler architecture page: FP8 activation
 // with fp32 activation-scale tensors): one 16-lane DPP row per 128-column
@@ -20,65 +20,104 @@
 
 namespace moe {
 
+// A lane's router candidates: keys (order-preserving bits of the logits, 0 =
+// none) and their experts.  Bitonic network into pick order: key descending,
+// expert ascending on equal keys.
+template <int NQ>
+__device__ __forceinline__ void sort_candidates(uint32_t (&key)[NQ], uint32_t (&idx)[NQ]) {
+#pragma unroll
+    for (int kk = 2; kk <= NQ; kk *= 2) {
+#pragma unroll
+        for (int jj = kk / 2; jj > 0; jj /= 2) {
+#pragma unroll
+            for (int a = 0; a < NQ; ++a) {
+                const int b = a ^ jj;
+                if (b > a) {
+                    // ((a & kk) == 0): slot a takes the element that comes first
+                    const bool b_first = key[b] > key[a] || (key[b] == key[a] && idx[b] < idx[a]);
+                    const bool swap = ((a & kk) == 0) == b_first;
+                    const uint32_t ka = key[a], ia = idx[a];
+                    key[a] = swap ? key[b] : ka;
+                    idx[a] = swap ? idx[b] : ia;
+                    key[b] = swap ? ka : key[b];
+                    idx[b] = swap ? ia : idx[b];
+                }
+            }
+        }
+    }
+}
+
+// The lane whose head is expert e drops it.  The pop is a bit mask the
+// compiler cannot see through: as a condition the shift became a
+// register-indexed select chain.
+template <int NQ>
+__device__ __forceinline__ void pop_candidate(uint32_t (&key)[NQ], uint32_t (&idx)[NQ], int e) {
+    uint32_t pm = ((int)idx[0] == e && key[0] != 0u) ? 0xFFFFFFFFu : 0u;
+    asm volatile("" : "+v"(pm));
+#pragma unroll
+    for (int q = 0; q + 1 < NQ; ++q) {
+        key[q] = (key[q + 1] & pm) | (key[q] & ~pm);
+        idx[q] = (idx[q + 1] & pm) | (idx[q] & ~pm);
+    }
+    key[NQ - 1] &= ~pm;
+}
+
+// Router of one token on one wave: lane l holds the logits of experts
+// l + 64 q, sorted once per lane (key descending, expert ascending).  A pick
+// is the wave maximum of the lanes' head keys, then the lowest expert among
+// the heads that reach it; the winning lane pops its head.  Equal logits go
+// to the lower expert index and -0 equals +0.  Each pick's exp(l - l_0) is
+// added to the rank-order sum as it comes; lane r stores pick r.
 // coherent: store the ids with device-coherent stores (read by another
 // workgroup of the same launch).
+template <int NQ>
+__device__ __forceinline__ void router_wave_nq(const float* __restrict__ l, int E, int k,
+                                               int32_t* __restrict__ ids, float* __restrict__ w,
+                                               int lane, bool coherent) {
+    // Unconditional loads (an index past E reads expert E - 1 and its key is
+    // dropped), issued together.
+    float lv[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) lv[q] = l[min(lane + 64 * q, E - 1)];
+    uint32_t key[NQ], idx[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        idx[q] = (uint32_t)(lane + 64 * q);
+        key[q] = (int)idx[q] < E ? float_order_key(lv[q]) : 0u;
+    }
+    sort_candidates<NQ>(key, idx);
+    int my_e = 0;
+    float lmax = 0.0f, sum = 0.0f, my_ex = 0.0f;
+    for (int rr = 0; rr < k; ++rr) {
+        const uint32_t m = wave_max_u(key[0]);
+        int e = (int)wave_min_u(key[0] == m ? idx[0] : 0xFFFFu);
+        e = (m == 0u || e >= E) ? E - 1 : e;   // only for NaN logits (outside the contract)
+        pop_candidate<NQ>(key, idx, e);
+        const float pv = float_from_order_key(m);   // the pick's logit (-0 comes back as +0)
+        if (rr == 0) lmax = pv;
+        const float ex = expf(pv - lmax);
+        sum += ex;
+        if (lane == rr) {
+            my_e = e;
+            my_ex = ex;
+        }
+    }
+    if (lane < k) {
+        if (coherent) st_agent(reinterpret_cast<uint32_t*>(ids) + lane, (uint32_t)my_e);
+        else ids[lane] = my_e;
+        w[lane] = my_ex / sum;
+    }
+}
+
 __device__ __forceinline__ void router_wave(const float* __restrict__ l, int E, int k,
                                             int32_t* __restrict__ ids, float* __restrict__ w,
                                             int lane, bool coherent = false) {
-    // The four loads are unconditional (an index past E reads expert E - 1
-    // and its key is dropped), so they are issued together.
-    float lv[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) lv[j] = l[min(lane + 64 * j, E - 1)];
-    uint32_t key[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) key[j] = (lane + 64 * j < E) ? float_order_key(lv[j]) : 0u;
-    int picked[16];
-    float pl[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        picked[r] = 0;
-        pl[r] = 0.0f;
-        if (r < k) {
-            uint32_t hi = 0u, lo = 0u;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (key[j] > hi) {           // strict: lower j (lower expert) wins ties
-                    hi = key[j];
-                    lo = 0xFFFFu - (uint32_t)(lane + 64 * j);
-                }
-            }
-            wave_key_max(hi, lo);
-            int e = (int)(0xFFFFu - lo);
-            e = (hi == 0u || e >= E) ? E - 1 : e;   // only for NaN logits (outside the contract)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (lane + 64 * j == e) key[j] = 0u;
-            picked[r] = e;
-            pl[r] = float_from_order_key(hi);   // the pick's logit (-0 comes back as +0)
-        }
-    }
-    // Renormalised softmax weights of the picks; every lane computes the same
-    // rank-order sum, lane r stores weight r.
-    const float lmax = pl[0];
-    float ex[16];
-    float sum = 0.0f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        ex[r] = 0.0f;
-        if (r < k) {
-            ex[r] = expf(pl[r] - lmax);
-            sum += ex[r];
-        }
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        if (r < k && lane == r) {
-            if (coherent) st_agent(reinterpret_cast<uint32_t*>(ids) + r, (uint32_t)picked[r]);
-            else ids[r] = picked[r];
-            w[r] = ex[r] / sum;
-        }
-    }
+    if (E <= 64)
+        router_wave_nq<1>(l, E, k, ids, w, lane, coherent);
+    else if (E <= 128)
+        router_wave_nq<2>(l, E, k, ids, w, lane, coherent);
+    else
+        router_wave_nq<4>(l, E, k, ids, w, lane, coherent);
 }
 
 // Each 16-lane row of a wave takes one 128-wide group per step; the loads of
@@ -166,42 +205,14 @@ __device__ __forceinline__ void router_rows16_nq(const float* __restrict__ logit
         idx[q] = (uint32_t)(j + 16 * q);
         key[q] = (int)idx[q] < E ? float_order_key(lv[q]) : 0u;
     }
-#pragma unroll
-    for (int kk = 2; kk <= NQ; kk *= 2) {
-#pragma unroll
-        for (int jj = kk / 2; jj > 0; jj /= 2) {
-#pragma unroll
-            for (int a = 0; a < NQ; ++a) {
-                const int b = a ^ jj;
-                if (b > a) {
-                    // ((a & kk) == 0): slot a takes the element that comes first
-                    const bool b_first = key[b] > key[a] || (key[b] == key[a] && idx[b] < idx[a]);
-                    const bool swap = ((a & kk) == 0) == b_first;
-                    const uint32_t ka = key[a], ia = idx[a];
-                    key[a] = swap ? key[b] : ka;
-                    idx[a] = swap ? idx[b] : ia;
-                    key[b] = swap ? ka : key[b];
-                    idx[b] = swap ? ia : idx[b];
-                }
-            }
-        }
-    }
+    sort_candidates<NQ>(key, idx);
     int my_e = 0;
     float lmax = 0.0f, sum = 0.0f, my_ex = 0.0f;
     for (int rr = 0; rr < k; ++rr) {
         const uint32_t m = row16_max_u(key[0]);
         int e = (int)row16_min_u(key[0] == m ? idx[0] : 0xFFFFu);
         e = (m == 0u || e >= E) ? E - 1 : e;   // only for NaN logits (outside the contract)
-        // The pop as a bit mask the compiler cannot see through: as a
-        // condition it became a register-indexed select chain.
-        uint32_t pm = ((int)idx[0] == e && key[0] != 0u) ? 0xFFFFFFFFu : 0u;
-        asm volatile("" : "+v"(pm));
-#pragma unroll
-        for (int q = 0; q + 1 < NQ; ++q) {
-            key[q] = (key[q + 1] & pm) | (key[q] & ~pm);
-            idx[q] = (idx[q + 1] & pm) | (idx[q] & ~pm);
-        }
-        key[NQ - 1] &= ~pm;
+        pop_candidate<NQ>(key, idx, e);
         const float pv = float_from_order_key(m);
         if (rr == 0) lmax = pv;
         const float ex = expf(pv - lmax);
