@@ -164,32 +164,6 @@ __device__ __forceinline__ uint32_t row16_max_u(uint32_t v) {
     return v;
 }
 
-// Unsigned min over the 16 lanes of each DPP row.
-__device__ __forceinline__ uint32_t row16_min_u(uint32_t v) {
-    v = min(v, dpp_u<kDppQuadXor1>(v));
-    v = min(v, dpp_u<kDppQuadXor2>(v));
-    v = min(v, dpp_u<kDppRowHalfMirror>(v));
-    v = min(v, dpp_u<kDppRowMirror>(v));
-    return v;
-}
-
-// Unsigned max / min over the whole wave (DPP inside each row of 16, then
-// the two row swaps); every lane gets the result.
-__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
-    v = row16_max_u(v);
-    auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-    v = max(p[0], p[1]);
-    p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-    return max(p[0], p[1]);
-}
-__device__ __forceinline__ uint32_t wave_min_u(uint32_t v) {
-    v = row16_min_u(v);
-    auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-    v = min(p[0], p[1]);
-    p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-    return min(p[0], p[1]);
-}
-
 // Wave-wide lexicographic max of 64-bit keys: DPP inside each row of 16
 // lanes, then the two row swaps.  Every lane gets the result.
 __device__ __forceinline__ void wave_key_max(uint32_t& hi, uint32_t& lo) {
