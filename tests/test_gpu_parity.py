@@ -351,6 +351,28 @@ def test_forward_edge_shapes(dev, moe_mod, M, h, i, E, k):
     check_output(to_host_bits(out), ref, allowance=flip_allowance(L, inter))
 
 
+@pytest.mark.parametrize("M,E,k", [(12, 40, 8), (20, 128, 8), (9, 200, 16)])
+def test_forward_tied_logits_stream_path(dev, moe_mod, M, E, k):
+    """Exact ties through the stream path's route launch (one wave per
+    token, up to one, two or four logits per lane): logits on a 0.5 grid, a
+    row of mixed -0 / +0 and a constant row.  The ids (lower expert first on
+    equal logits, -0 equal to +0), weights and grouping must match the
+    oracle's exactly, and the output within the flip allowance."""
+    h, i = 256, 128
+    assert moe_mod.workspace_layout(M, h, i, E, k).path == moe_mod.PATH_STREAM
+    rng = np.random.default_rng(M * 7 + E)
+    logits = (rng.integers(-3, 4, (M, E)) * 0.5).astype(np.float32)
+    logits[0] = np.where(rng.random(E) < 0.5, np.float32(-0.0), np.float32(0.0))
+    logits[1] = np.float32(-3.5)
+    cfg = synth.LayerConfig(f"m{M}_h{h}_i{i}_e{E}_top{k}", M, h, i, E, k, "normal", "tied logits")
+    L = Layer(cfg, 77 + E, dev, logits=logits)
+    log(f"tied-logit forward M={M} E={E} k={k}")
+    out, ws = _run(moe_mod, L)
+    ref, inter = L.oracle(intermediates=True)
+    _check_intermediates(moe_mod, L, ws, inter)
+    check_output(to_host_bits(out), ref, allowance=flip_allowance(L, inter))
+
+
 def test_mfma_block_sum_accuracy(dev, moe_mod):
     """The FP8 MFMA block sums: every materialised gate/up value of the
     weight-streaming path lies within MFMA_REL * sum|terms| of the exact
