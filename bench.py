@@ -44,8 +44,14 @@ def parse():
     ap.add_argument("--config", type=int, default=1, help="layer shape index (0..5); 1 = decode M=1")
     ap.add_argument("--copies", type=int, default=0, help="rotation copies (0 = enough to exceed 4x the Infinity Cache)")
     ap.add_argument("--timing-replays", type=int, default=20)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=9.0,
+                    help="CPU time of the headline shape's oracle baseline (three runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-configs", action="store_true", help="CPU baseline of the headline shape only")
+    ap.add_argument("--no-other-configs", action="store_true", help="skip the records of the other layer shapes")
+    ap.add_argument("--no-floors", action="store_true", help="skip the empty-launch and streaming-read frames")
+    ap.add_argument("--other-steps", type=int, default=200,
+                    help="timed forwards of each other layer shape (rounded up to whole rotations)")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 3 plain device-to-device copies of MIB MiB (counter calibration) and exit")
@@ -441,6 +447,334 @@ def front_end_bench(args):
     print(json.dumps(line), flush=True)
 
 
+def forward_work(cfg, U_mean):
+    """Algorithmic bytes (selected experts' weights and scales, x, logits,
+    out) and FLOPs of one whole forward."""
+    M, h, i, E, k = cfg.M, cfg.h, cfg.i, cfg.E, cfg.k
+    return U_mean * sum(weight_bytes_per_expert(cfg)) + M * h * 4 + M * E * 4, 6.0 * M * k * h * i
+
+
+def forward_bound(cfg, fw_bytes, fw_flops):
+    return "hbm" if fw_bytes / (HBM_PEAK_GBS * 1e9) >= fw_flops / (FP8_PEAK_TFLOPS * 1e12) else "mfma"
+
+
+def frac_of(bound, nbytes, flops, seconds):
+    """(achieved, peak, unit, frac) of a piece of work done in `seconds`."""
+    if bound == "hbm":
+        a = nbytes / seconds / 1e9
+        return a, HBM_PEAK_GBS, "GB/s", a / HBM_PEAK_GBS
+    a = flops / seconds / 1e12
+    return a, FP8_PEAK_TFLOPS, "TFLOP/s", a / FP8_PEAK_TFLOPS
+
+
+def make_device_weights(moe, cfg, seed, dev, copy):
+    """Expert weights drawn on the GPU (N(0, 1/sqrt(K)), torch's seeded
+    generator) and block-quantised by the library: the timing runs of the
+    other shapes need the distribution, not the oracle's bytes."""
+    import torch
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed * 1000 + copy)
+    q13, s13 = moe.quantize_weight_block128(torch.randn((cfg.E, 2 * cfg.i, cfg.h), generator=g, device=dev)
+                                            / math.sqrt(cfg.h))
+    q2, s2 = moe.quantize_weight_block128(torch.randn((cfg.E, cfg.h, cfg.i), generator=g, device=dev)
+                                          / math.sqrt(cfg.i))
+    torch.cuda.synchronize()
+    return q13, s13, q2, s2
+
+
+def rotation_copies(cfg, U0, args):
+    w13b, w2b = weight_bytes_per_expert(cfg)
+    step_bytes = U0 * (w13b + w2b)
+    C = args.copies or max(2, math.ceil(4 * MALL_BYTES / step_bytes) + 1)
+    return max(1, min(C, int((48 << 30) // (cfg.E * (w13b + w2b)))))
+
+
+def time_layer(moe, cfg, W, X, Lg, WS, OUT, steps, warmup, timing_replays):
+    """Graph-replay timing of the C rotation copies' forwards: W warm-up and
+    exactly `steps` timed forwards between a synchronisation and HIP events
+    on both sides; then stage durations from graphs of the same forwards cut
+    after their first j stages.  Returns (ms per forward, stage names, stage
+    ms, number of forwards per cut)."""
+    import numpy as np
+    import torch
+    M, h, i, E, k = cfg.M, cfg.h, cfg.i, cfg.E, cfg.k
+    C = len(W)
+
+    def fwd(c, n=None):
+        a = W[c]
+        if n is None:
+            moe.moe_fp8_forward_ws(X[c], Lg[c], a[0], a[1], a[2], a[3], k, WS[c], out=OUT[c])
+        else:
+            moe.moe_fp8_forward_ws_prefix(X[c], Lg[c], a[0], a[1], a[2], a[3], k, WS[c], n, out=OUT[c])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+
+    def capture(n, cut=None):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for c in range(n):
+                fwd(c, cut)
+        return g
+
+    g_all = capture(C)
+    rem = steps % C
+    g_rem = capture(rem) if rem else None
+
+    def run_steps(n):
+        for _ in range(n // C):
+            g_all.replay()
+        r = n % C
+        if r:
+            if r == rem:
+                g_rem.replay()
+            else:
+                for c in range(r):
+                    fwd(c)
+
+    run_steps(warmup)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    run_steps(steps)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / steps
+
+    # Stage j's duration is T(j) - T(j - 1) per forward, T(j) from replays of
+    # the forwards cut after their first j stages, queued behind a GPU spin so
+    # that short prefixes are timed on the GPU, not at the host's launch rate.
+    names = moe.forward_kernel_names(M, h, i, E, k)
+    nst = len(names)
+    reps = max(1, timing_replays)
+    T = [0.0]
+    for j in range(1, nst + 1):
+        gj = g_all if j == nst else capture(C, j)
+        gj.replay()
+        torch.cuda.synchronize()
+        torch.cuda._sleep(20_000_000)
+        e0.record()
+        for _ in range(reps):
+            gj.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        T.append(e0.elapsed_time(e1) / (reps * C))
+        if gj is not g_all:
+            del gj
+    run_steps(C)   # the full forwards leave every copy's output complete again
+    torch.cuda.synchronize()
+    return ms_per_step, names, np.maximum(np.diff(np.array(T)), 0.0), reps * C
+
+
+def layer_record(cfg, names, stage_ms, U_mean, ms_per_step, count, traffic_workload=None):
+    """The roofline of the dominant stage (algorithmic work of one launch over
+    its mean duration) and of the whole forward (its algorithmic work over the
+    time per forward)."""
+    import numpy as np
+    fw_bytes, fw_flops = forward_work(cfg, U_mean)
+    bound = forward_bound(cfg, fw_bytes, fw_flops)
+    dom = int(np.argmax(stage_ms))
+    abytes, aflops = stage_work(cfg, names[dom], U_mean)
+    achieved, peak, unit, frac = frac_of(bound, abytes, aflops, stage_ms[dom] / 1e3)
+    fa, _, _, ff = frac_of(bound, fw_bytes, fw_flops, ms_per_step / 1e3)
+    roofline = {"bound": bound, "kernel": names[dom], "achieved": round(achieved, 2), "peak": peak,
+                "unit": unit, "frac": round(frac, 4),
+                "traffic": load_traffic(names[dom], traffic_workload or cfg.name),
+                "avg_launch_us": round(stage_ms[dom] * 1e3, 3),
+                "algorithmic_bytes_per_launch": int(abytes),
+                "algorithmic_flops_per_launch": aflops,
+                "timing": f"HIP-graph replays of forwards cut after each stage, differences, "
+                          f"{count} forwards per cut"}
+    forward = {"bound": bound, "achieved": round(fa, 2), "peak": peak, "unit": unit, "frac": round(ff, 4),
+               "algorithmic_bytes": int(fw_bytes), "algorithmic_flops": fw_flops,
+               "timing": "HIP graph of the rotation copies' forwards, events around the timed steps"}
+    return roofline, forward
+
+
+def launch_and_read_floors(moe, n_launch, fw_bytes, C, dev):
+    """Two frames for a forward's time: (1) a graph of C * n_launch empty
+    kernels, per forward (what the launches cost by themselves); (2) one
+    streaming-read kernel over fw_bytes, rotated over C buffers (the best
+    time one launch reaches on the forward's algorithmic bytes), swept over
+    grids of 256..2048 workgroups."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps=20):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            fn()
+        g.replay()
+        torch.cuda.synchronize()
+        torch.cuda._sleep(20_000_000)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        del g
+        return e0.elapsed_time(e1) / reps
+
+    empty_ms = timed(lambda: [moe.probe_empty(256) for _ in range(C * n_launch)]) / C
+    nb = (int(fw_bytes) + 15) // 16 * 16
+    bufs = [torch.full((nb,), 1, dtype=torch.uint8, device=dev) for _ in range(C)]
+    sink = torch.empty(4 * 2048, dtype=torch.int32, device=dev)
+    best = None
+    for grid in (256, 512, 1024, 2048):
+        ms = timed(lambda: [moe.probe_read(b, grid, sink) for b in bufs]) / C
+        if best is None or ms < best[0]:
+            best = (ms, grid)
+    del bufs
+    return {"empty_kernels_per_forward": n_launch, "empty_graph_us_per_forward": round(empty_ms * 1e3, 3),
+            "read_bytes": nb, "read_us": round(best[0] * 1e3, 3), "read_grid": best[1],
+            "read_GBps": round(nb / (best[0] / 1e3) / 1e9, 1),
+            "timing": "HIP graphs of C launches per forward, events around 20 replays"}
+
+
+def other_config_records(moe, args, skip, dev):
+    """Per-shape records of every other configured layer shape: tokens/s,
+    the dominant stage against its roofline and the whole forward against
+    the forward's bound (weights drawn on the GPU; x and logits from the
+    shape's own recipe)."""
+    import numpy as np
+    import torch
+    import synth
+    out = {}
+    for ci, cfg in enumerate(synth.CONFIGS):
+        if ci == skip:
+            continue
+        t0 = time.time()
+        seed = synth.default_seed(ci)
+        M, h, i, E, k = cfg.M, cfg.h, cfg.i, cfg.E, cfg.k
+        ids0, _ = moe.router_topk(torch.from_numpy(synth.make_logits(cfg, seed, copy=0)).to(dev), k)
+        C = rotation_copies(cfg, int(torch.unique(ids0).numel()), args)
+        W = [make_device_weights(moe, cfg, seed, dev, c) for c in range(C)]
+        X, Lg, WS, OUT = [], [], [], []
+        for c in range(C):
+            X.append(torch.from_numpy(synth.make_x(cfg, seed, copy=c).view(np.int16)).view(torch.bfloat16).to(dev))
+            Lg.append(torch.from_numpy(synth.make_logits(cfg, seed, copy=c)).to(dev))
+            WS.append(moe.alloc_workspace(M, h, i, E, k, device=dev))
+            OUT.append(torch.empty((M, h), dtype=torch.bfloat16, device=dev))
+        for c in range(C):
+            a = W[c]
+            moe.moe_fp8_forward_ws(X[c], Lg[c], a[0], a[1], a[2], a[3], k, WS[c], out=OUT[c])
+        torch.cuda.synchronize()
+        lay = moe.workspace_layout(M, h, i, E, k)
+        U = [int(WS[c][lay.num_active:lay.num_active + 4].view(torch.int32).item()) for c in range(C)]
+        assert all(torch.isfinite(OUT[c].float()).all().item() for c in range(C))
+        steps = C * max(1, math.ceil(args.other_steps / C))
+        ms, names, stage_ms, count = time_layer(moe, cfg, W, X, Lg, WS, OUT, steps, C, args.timing_replays)
+        errs = [moe.workspace_error(WS[c]) for c in range(C)]
+        U_mean = float(np.mean(U))
+        roofline, forward = layer_record(cfg, names, stage_ms, U_mean, ms, count)
+        out[cfg.name] = {
+            "tokens_per_s": round(M / (ms / 1e3), 2), "ms_per_step": round(ms, 6), "steps": steps,
+            "path": {0: "stream", 1: "prefill", 2: "one-kernel"}[lay.path],
+            "rotation_copies": C, "distinct_experts_mean": U_mean,
+            "stage_us": {n: round(v * 1e3, 3) for n, v in zip(names, stage_ms)},
+            "roofline": roofline, "forward": forward, "sync_errors": int(sum(e != 0 for e in errs)),
+            "weights": "GPU-drawn N(0, 1/sqrt(K)), library block quantisation",
+            "wall_s": round(time.time() - t0, 1)}
+        print(f"bench: {cfg.name} {out[cfg.name]['tokens_per_s']} tok/s, {ms * 1e3:.1f} us/forward",
+              file=sys.stderr, flush=True)
+        del W, X, Lg, WS, OUT
+        torch.cuda.empty_cache()
+    return out
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_rate(oracle, synth, cfg, seed, weights, batch, min_s, runs, threads, max_tokens=1 << 16, reuse=False):
+    """Median over `runs` of the oracle's tokens/s on consecutive batches of
+    `batch` fresh tokens of the shape (the same first batch again and again
+    with `reuse`), at least `min_s` seconds or `max_tokens` tokens per run,
+    with `threads` OpenMP threads.  Returns (median tokens/s, tokens per run)."""
+    import statistics
+    q13h, s13h, q2h, s2h = weights
+    oracle.set_threads(threads)
+    rates, first, done_total = [], 0, 0
+    for _ in range(runs):
+        done, t = 0, 0.0
+        while t < min_s and done < max_tokens:
+            xb = synth.make_x(cfg, seed, copy=97, M=batch, first_token=first)
+            lb = synth.make_logits(cfg, seed, copy=97, M=batch, first_token=first)
+            t1 = time.perf_counter()
+            oracle.moe_forward(xb, lb, q13h, s13h, q2h, s2h, cfg.k)
+            t += time.perf_counter() - t1
+            done += batch
+            first += 0 if reuse else batch
+        rates.append(done / t)
+        done_total = done
+    return statistics.median(rates), done_total
+
+
+def cpu_baselines(cfg_head, seed_head, host_weights, args):
+    """The oracle (plain C, OpenMP over rows) on the host cores: the headline
+    shape on all threads (median of 3 runs of about args.cpu_seconds / 3 s),
+    then every shape on all threads and on one thread (median of 3 runs of
+    about 1 s; the prefill shape once, on 512 tokens)."""
+    import numpy as np
+    import oracle
+    import synth
+    nthreads = os.cpu_count() or 1
+    oracle.set_threads(nthreads)
+    used = oracle.get_threads()
+    batch = max(1, min(cfg_head.M, 64))
+    head, n = cpu_rate(oracle, synth, cfg_head, seed_head, host_weights, batch, args.cpu_seconds / 3, 3, used)
+    cpu = {"value": round(head, 3), "unit": "tokens/s", "cores": used, "kind": "oracle",
+           "sample": f"median of 3 runs of {n} tokens of {cfg_head.name} in batches of {batch}",
+           "cpu_model": cpu_model()}
+    if args.no_cpu_configs:
+        return cpu
+    per = {}
+    for ci, cfg in enumerate(synth.CONFIGS):
+        seed = synth.default_seed(ci)
+        b = max(1, min(cfg.M, 64))
+        reuse = False
+        if (cfg.h, cfg.i, cfg.E) == (cfg_head.h, cfg_head.i, cfg_head.E):
+            weights, wnote = host_weights, f"weights of {cfg_head.name} (same sizes)"
+        else:
+            # one batch of b tokens run again and again; only the experts it
+            # selects are drawn (the oracle reads no other expert)
+            b = max(1, min(cfg.M, 4 if cfg.h > 4096 else 64))
+            reuse = True
+            ids, _ = oracle.router(synth.make_logits(cfg, seed, copy=97, M=b), cfg.k)
+            experts = sorted(set(int(e) for e in np.unique(ids)))
+            w13 = np.zeros((cfg.E, 2 * cfg.i, cfg.h), np.float32)
+            w2 = np.zeros((cfg.E, cfg.h, cfg.i), np.float32)
+            w13[experts] = synth.make_w13_f32(cfg, seed, experts)
+            w2[experts] = synth.make_w2_f32(cfg, seed, experts)
+            q13, s13 = oracle.quant_weight_block128(w13)
+            q2, s2 = oracle.quant_weight_block128(w2)
+            del w13, w2
+            weights, wnote = (q13, s13, q2, s2), f"the shape's own weights; one batch of {b} tokens repeated"
+        rec = {"weights": wnote}
+        if cfg.M >= 4096:
+            r, n = cpu_rate(oracle, synth, cfg, seed, weights, 512, 1e-9, 1, used, max_tokens=512)
+            rec.update(all_threads=round(r, 3), all_threads_sample=f"1 run of {n} tokens in one batch")
+        else:
+            r, n = cpu_rate(oracle, synth, cfg, seed, weights, b, 1.0, 3, used, reuse=reuse)
+            rec.update(all_threads=round(r, 3), all_threads_sample=f"median of 3 runs of {n} tokens, batches of {b}")
+            r1, n1 = cpu_rate(oracle, synth, cfg, seed, weights, b, 1.0, 3, 1, reuse=reuse)
+            rec.update(one_thread=round(r1, 3), one_thread_sample=f"median of 3 runs of {n1} tokens, batches of {b}")
+        oracle.set_threads(used)
+        per[cfg.name] = rec
+        print(f"bench: cpu {cfg.name} {rec}", file=sys.stderr, flush=True)
+    cpu["per_config"] = per
+    return cpu
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -478,7 +812,6 @@ def main():
     seed = synth.default_seed(args.config) if args.seed is None else args.seed
     M, h, i, E, k = cfg.M, cfg.h, cfg.i, cfg.E, cfg.k
     w13b, w2b = weight_bytes_per_expert(cfg)
-    wbytes = E * (w13b + w2b)
 
     # ---- inputs: weights drawn on the host, quantised on the GPU by the library
     t0 = time.time()
@@ -491,10 +824,7 @@ def main():
     # only after >= 4x the Infinity Cache of other traffic (distinct experts
     # per step measured with the library's own router on copy 0).
     ids0, _ = moe.router_topk(torch.from_numpy(synth.make_logits(cfg, seed, copy=0)).to(dev), k)
-    U0 = int(torch.unique(ids0).numel())
-    step_bytes = U0 * (w13b + w2b)
-    C = args.copies or max(2, math.ceil(4 * MALL_BYTES / step_bytes) + 1)
-    C = max(1, min(C, int((48 << 30) // wbytes)))
+    C = rotation_copies(cfg, int(torch.unique(ids0).numel()), args)
     W = [(q13, s13, q2, s2)] + [(q13.clone(), s13.clone(), q2.clone(), s2.clone()) for _ in range(C - 1)]
     X, Lg, WS, OUT = [], [], [], []
     for c in range(C):
@@ -506,139 +836,44 @@ def main():
     torch.cuda.synchronize()
     setup_s = time.time() - t0
 
-    def fwd(c):
-        a = W[c]
-        moe.moe_fp8_forward_ws(X[c], Lg[c], a[0], a[1], a[2], a[3], k, WS[c], out=OUT[c])
-
     # eager warm-up of every copy, then distinct experts per copy
     for c in range(C):
-        fwd(c)
+        a = W[c]
+        moe.moe_fp8_forward_ws(X[c], Lg[c], a[0], a[1], a[2], a[3], k, WS[c], out=OUT[c])
     torch.cuda.synchronize()
     lay = moe.workspace_layout(M, h, i, E, k)
     U = [int(WS[c][lay.num_active:lay.num_active + 4].view(torch.int32).item()) for c in range(C)]
     assert all(torch.isfinite(OUT[c].float()).all().item() for c in range(C))
 
-    # ---- graphs: all C forwards, and the first r forwards for a remainder
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-
-    def capture(n):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=side):
-            for c in range(n):
-                fwd(c)
-        return g
-
-    g_all = capture(C)
-    rem = args.steps % C
-    g_rem = capture(rem) if rem else None
-
-    def run_steps(n):
-        for _ in range(n // C):
-            g_all.replay()
-        r = n % C
-        if r:
-            if r == rem:
-                g_rem.replay()
-            else:
-                for c in range(r):
-                    fwd(c)
-
-    run_steps(args.warmup)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    run_steps(args.steps)
-    e1.record()
-    torch.cuda.synchronize()
-    total_ms = e0.elapsed_time(e1)
-    ms_per_step = total_ms / args.steps
+    ms_per_step, names, stage_ms, count = time_layer(moe, cfg, W, X, Lg, WS, OUT, args.steps, args.warmup,
+                                                     args.timing_replays)
+    errs = [moe.workspace_error(WS[c]) for c in range(C)]
+    if any(errs):
+        print(f"bench.py: a wait between workgroups timed out in {sum(e != 0 for e in errs)} workspaces",
+              file=sys.stderr)
+        sys.exit(3)
     tokens_per_s = M / (ms_per_step / 1e3)
-
-    # ---- per-stage durations: HIP-graph replays of the C forwards cut after
-    # their first j stages (j = 1..n), timed by HIP events on the launch
-    # stream; stage j's duration is T(j) - T(j - 1) per forward.  No event
-    # sits between stages, so a short stage is not charged the event's own
-    # cost, and the stages run back to back as in the timed steps.  The
-    # replays wait behind a GPU spin kernel while the host queues them.
-    names = moe.forward_kernel_names(M, h, i, E, k)
-    nst = len(names)
-
-    def capture_prefix(j):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=side):
-            for c in range(C):
-                a = W[c]
-                moe.moe_fp8_forward_ws_prefix(X[c], Lg[c], a[0], a[1], a[2], a[3], k, WS[c], j, out=OUT[c])
-        return g
-
-    reps = max(1, args.timing_replays)
-    T = [0.0]
-    for j in range(1, nst + 1):
-        gj = g_all if j == nst else capture_prefix(j)
-        gj.replay()
-        torch.cuda.synchronize()
-        # the replays are queued behind a GPU spin, so that a short prefix
-        # is timed on the GPU, not at the host's launch rate
-        torch.cuda._sleep(20_000_000)
-        e0.record()
-        for _ in range(reps):
-            gj.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        T.append(e0.elapsed_time(e1) / (reps * C))
-        if gj is not g_all:
-            del gj
-    stage_ms = np.maximum(np.diff(np.array(T)), 0.0)
-    count = reps * C
-    timing_mode = "HIP-graph replays of forwards cut after each stage, differences"
-    # the full forwards leave every copy's output complete again
-    run_steps(C)
-    torch.cuda.synchronize()
-    dom = int(np.argmax(stage_ms))
     U_mean = float(np.mean(U))
-    abytes, aflops = stage_work(cfg, names[dom], U_mean)
-    dom_s = stage_ms[dom] / 1e3
-    # the forward's bound: its algorithmic bytes (selected weights, x, logits,
-    # out) against its FLOPs, each over its peak
-    fw_bytes = U_mean * sum(weight_bytes_per_expert(cfg)) + M * h * 4 + M * E * 4
-    fw_flops = 6.0 * M * k * h * i
-    bound = "hbm" if fw_bytes / (HBM_PEAK_GBS * 1e9) >= fw_flops / (FP8_PEAK_TFLOPS * 1e12) else "mfma"
-    if bound == "hbm":
-        achieved = abytes / dom_s / 1e9
-        peak, unit = HBM_PEAK_GBS, "GB/s"
-    else:
-        achieved = aflops / dom_s / 1e12
-        peak, unit = FP8_PEAK_TFLOPS, "TFLOP/s"
-    roofline = {"bound": bound, "kernel": names[dom], "achieved": round(achieved, 2), "peak": peak,
-                "unit": unit, "frac": round(achieved / peak, 4),
-                "traffic": load_traffic(names[dom], cfg.name),
-                "avg_launch_us": round(stage_ms[dom] * 1e3, 3),
-                "algorithmic_bytes_per_launch": int(abytes),
-                "algorithmic_flops_per_launch": aflops,
-                "timing": f"{timing_mode}, {count} forwards per cut"}
+    roofline, forward = layer_record(cfg, names, stage_ms, U_mean, ms_per_step, count)
+    fw_bytes, _ = forward_work(cfg, U_mean)
+    floors = None
+    if not args.no_floors:
+        floors = launch_and_read_floors(moe, len(names), fw_bytes, C, dev)
+    del W, X, Lg, WS, OUT
+    torch.cuda.empty_cache()
 
-    # ---- CPU baseline: the oracle on a bounded sample of the same workload
+    others = None
+    if not args.no_other_configs:
+        others = other_config_records(moe, args, args.config, dev)
+
+    # ---- CPU baseline: the oracle on bounded samples of the same workloads
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
         q13h, s13h = oracle.quant_weight_block128(w13_f)
         q2h, s2h = oracle.quant_weight_block128(w2_f)
         del w13_f, w2_f
-        batch = max(1, min(M, 64))
-        done, t_cpu, first = 0, 0.0, 0
-        while t_cpu < args.cpu_seconds and done < 1 << 16:
-            xb = synth.make_x(cfg, seed, copy=C + 1, M=batch, first_token=first)
-            lb = synth.make_logits(cfg, seed, copy=C + 1, M=batch, first_token=first)
-            t1 = time.perf_counter()
-            oracle.moe_forward(xb, lb, q13h, s13h, q2h, s2h, k)
-            t_cpu += time.perf_counter() - t1
-            done += batch
-            first += batch
-        cpu = {"value": round(done / t_cpu, 3), "unit": "tokens/s", "cores": oracle.get_threads(),
-               "kind": "oracle",
-               "sample": f"{done} tokens of {cfg.name} in batches of {batch}, {t_cpu:.1f} s wall"}
+        cpu = cpu_baselines(cfg, seed, (q13h, s13h, q2h, s2h), args)
 
     line = {
         "metric": METRIC,
@@ -654,12 +889,16 @@ def main():
         "dtype": "e4m3 (fp32 accumulate)",
         "data": "synthetic",
         "config": {"workload": cfg.name, "M": M, "h": h, "i": i, "E": E, "k": k,
+                   "path": {0: "stream", 1: "prefill", 2: "one-kernel"}[lay.path],
                    "rotation_copies": C, "distinct_experts_mean": U_mean,
-                   "layer_bytes_per_step": int(U_mean * (w13b + w2b) + M * h * 4 + M * E * 4),
+                   "layer_bytes_per_step": int(fw_bytes),
                    "timing": "HIP graph of C forwards, events around K steps",
                    "stage_us": {n: round(v * 1e3, 3) for n, v in zip(names, stage_ms)},
                    "setup_s": round(setup_s, 1)},
         "roofline": roofline,
+        "forward": forward,
+        "floors": floors,
+        "configs": others,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

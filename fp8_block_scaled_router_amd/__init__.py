@@ -75,6 +75,9 @@ _SIGS = {
     "moe_fp8_forward_kernel_name": (ctypes.c_char_p, [_I, _I, _I, _I, _I, _I]),
     "moe_fp8_workspace_init": (_I, [_P, _SZ, _P]),
     "moe_fp8_workspace_head_bytes": (_SZ, []),
+    "moe_fp8_workspace_status": (_I, [_P, _SZ, _I, ctypes.POINTER(ctypes.c_uint32), _P]),
+    "moe_fp8_probe_empty": (_I, [_I, _P]),
+    "moe_fp8_probe_read": (_I, [_P, _SZ, _I, _P, _P]),
 }
 
 
@@ -148,10 +151,32 @@ def workspace_init(ws: torch.Tensor, stream=None) -> None:
     _check(lib().moe_fp8_workspace_init(_ptr(ws), ws.numel(), _stream(stream)), "moe_fp8_workspace_init")
 
 
-def workspace_error(ws: torch.Tensor, M: int, h: int, i: int, E: int, k: int) -> int:
-    """The workspace's sticky error word (0 = every wait completed)."""
-    off = workspace_layout(M, h, i, E, k).sync_error
-    return int(ws[off:off + 4].view(torch.int32).item())
+def workspace_error(ws: torch.Tensor, clear: bool = False, stream=None) -> int:
+    """The workspace's sticky error word after the work queued on `stream`
+    (0 = every wait between workgroups completed; otherwise a forward's wait
+    timed out and its output is invalid); `clear` resets it.  Synchronises
+    the stream."""
+    _dev(ws, torch.uint8, "workspace")
+    flags = ctypes.c_uint32(0)
+    _check(lib().moe_fp8_workspace_status(_ptr(ws), ws.numel(), int(bool(clear)), ctypes.byref(flags),
+                                          _stream(stream)), "moe_fp8_workspace_status")
+    return int(flags.value)
+
+
+def probe_empty(grid: int, stream=None) -> None:
+    """Measurement: one empty kernel of `grid` 256-thread workgroups."""
+    _check(lib().moe_fp8_probe_empty(int(grid), _stream(stream)), "moe_fp8_probe_empty")
+
+
+def probe_read(src: torch.Tensor, grid: int, sink: torch.Tensor, stream=None) -> None:
+    """Measurement: one kernel of `grid` workgroups streaming all of `src`
+    (uint8, size a multiple of 16) from HBM; sink is int32 [>= 4 * grid]."""
+    _dev(src, torch.uint8, "src")
+    _dev(sink, torch.int32, "sink")
+    if sink.numel() < 4 * grid:
+        raise ValueError("sink must hold 4 * grid words")
+    _check(lib().moe_fp8_probe_read(_ptr(src), src.numel(), int(grid), _ptr(sink), _stream(stream)),
+           "moe_fp8_probe_read")
 
 
 SYNC_EPOCH_OFFSET = 0     # forwards of the one-kernel path run on a workspace

@@ -1,5 +1,5 @@
-// fused_decode.h -- arguments and launcher of the one-kernel small-batch
-// forward (internal to the library).
+// fused_decode.h -- arguments and launcher of the one-kernel decode forward
+// (internal to the library).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -30,13 +30,16 @@ struct FusedArgs {
     int32_t* active;
     int32_t* num_active;
     // exchange buffers: 64-bit (value, forward tag) words
-    uint64_t* g_ll;   // [M*k][2i] gate/up results by route
-    uint64_t* y_ll;   // [M*k][h]  down partials by route
+    uint64_t* v_ll;   // [M*k][i]       SiLU(gate) * up by route
+    uint64_t* t_ll;   // [M*k][i/128][h] down block terms by route and K block
     // synchronisation words
     uint32_t* sync;
 };
 
 bool fused_supported(int M, int h, int i, int E, int k);
+int fused_parts(int M, int i, int E, int k);
+// Words of the v exchange buffer; t follows it, rounded up to 32 words.
+inline size_t fused_v_words(int M, int i, int k) { return ((size_t)M * k * i + 31) & ~(size_t)31; }
 size_t fused_lds_bytes(int M, int h, int i, int E, int k);
 hipError_t launch_fused_decode(const FusedArgs& args, hipStream_t stream);
 
@@ -47,7 +50,7 @@ constexpr size_t kSyncEpoch = 0;                // word: forwards run on this wo
 constexpr size_t kSyncExit = 256;               // word: workgroups finished in this forward
 constexpr size_t kSyncErr = 512;                // word: sticky error (a wait timed out)
 constexpr size_t kSyncArrive = 1024;            // word: routing workgroups counted in (grouping tail)
-constexpr size_t kLLBytes = (size_t)8 << 20;    // g_ll (4 MiB) + y_ll (4 MiB)
+constexpr size_t kLLBytes = (size_t)8 << 20;    // v_ll, then t_ll
 constexpr size_t kLLOffset = kSyncBytes;
 constexpr size_t kWorkspaceHead = kSyncBytes + kLLBytes;   // zero-initialised part
 hipError_t launch_zero_words(uint32_t* p, size_t words, hipStream_t stream);

@@ -1,50 +1,57 @@
-// fused_decode.hip -- the whole layer in one persistent kernel for small
-// batches (M <= 16 tokens): decode and speculative verification.
+// fused_decode.hip -- the whole layer in one kernel for one or two tokens
+// (decode).
 //
-// Every workgroup first recomputes, on chip, what it needs from the batch:
-// the router top-k of all M tokens (one wave per token: DPP row maxima,
-// scalar readlanes and ballots; the picked logits come back out of the keys),
-// the 1x128 E4M3 activation codes of all tokens (into LDS) and the grouping
-// of the M*k routes by expert (ballot ranks, DPP prefix sums).  Work is then
-// split in two task lists:
+// The work is cut along the expert intermediate dimension.  A unit is
+// (active expert slot u, 128-column block ib of the intermediate); P
+// workgroups (parts, P = 8 or 4) share each unit.  Part q of unit (u, ib)
+// owns
+//   - 128/P gate rows ib*128 + q*128/P .. of w13[e_u] and the matching up
+//     rows, over K = h: the gate/up GEMM of those columns (Netra compiler
+//     architecture page: gate/up with FP32 results), K blocks split over the
+//     four waves;
+//   - rows q*h/P .. (q+1)*h/P of w2[e_u], columns ib*128 .. +128: one 128-wide
+//     K block of the down GEMM for those output rows.
+// Because the SiLU-mul requantisation groups are exactly the 128-column
+// blocks of the intermediate (the 1x128 activation quantisation of the down
+// GEMM's input), a unit's down-partial needs only the unit's own gate/up
+// columns.  So as soon as a workgroup knows its expert it requests every
+// weight byte it will ever use (w13 first, then w2) into registers: the whole
+// selected-expert stream of the forward is in flight at once, and no
+// workgroup waits for another before its weights arrive.
 //
-//  A task (expert slot u, 128-column group jg, quarter q): 32 gate rows and
-//    the matching 32 up rows of w13[e_u], K = h, streamed once with
-//    v_mfma_f32_16x16x128_f8f6f4 (weights as A, the expert's <= 16 routes as
-//    B), per-128-K-block scale promotion; FP32 results per route (Netra
-//    compiler architecture page: gate/up FP32).
-//  B task (expert slot u, 64-row tile of w2[e_u]): its weights are loaded
-//    into registers before the workgroup's gate/up work is computed; it then
-//    computes SiLU(gate) * up of u's routes and their 1x128 E4M3
-//    requantisation straight into LDS (Netra Kernel README, MoE prefill pair:
-//    SiLU and quantisation), and the fp32 partial rows (down-partial).
-//  Combine: the workgroup that owns a token's last-rank route for a tile
-//    sums that tile's k partials in rank order and writes bf16 (route
-//    reducer; Inferact amd-kernels README, atomics rule: no atomic sums, a
-//    fixed order).  It does so only after all of its own B tasks.
+// Exchanges between workgroups (each value one 64-bit word: value | tag of
+// this forward, written and read with agent-scope relaxed atomics; the data
+// is its own flag):
+//   v  [route][i]      SiLU(gate) * up of each part's columns; every part of
+//                      the unit reads all 128 of its block, takes amax/448 and
+//                      the E4M3 codes itself (identical inputs, identical
+//                      codes), then multiplies its w2 rows.
+//   t  [route][ib][h]  the down GEMM's block terms blk * (a2s * s2): the K
+//                      block ib's contribution to the partial of each route.
+// Combine (route reducer; Inferact amd-kernels README, atomics rule: a fixed
+// order, no atomic adds): per 64 output columns, y_r = sum of t over the
+// blocks ib ascending (the down GEMM's per-block accumulation order), then
+// out = bf16(sum over ranks r ascending of w_r * y_r).
 //
-// Exchange between workgroups: each gate/up result and each partial is one
-// 64-bit word (value, tag of this forward) written and read with
-// agent-coherent stores and loads; a consumer polls the words it needs until
-// they carry this forward's tag.  The data is its own flag, so there are no
-// counters to contend on and no cache-wide fences.  The tag is the
-// workspace's forward count plus one, read at the start; the last workgroup
-// to exit advances it (and, once every 2^32 forwards, clears the exchange
-// region so that no stale word can ever carry a current tag).  Waits are
-// bounded in time; a timeout sets a sticky error word instead of hanging.
-// Tasks only wait on tasks of an earlier phase, and the grid never exceeds
-// the number of workgroups that can be resident at once, so every awaited
-// task is always running.
+// Every workgroup first recomputes what it needs from the batch: the router
+// top-k of all M tokens (one wave per token), the active experts, the
+// grouping of the routes, and the 1x128 E4M3 activation codes of all tokens
+// (into LDS).  Waits are bounded in time: a wait that times out sets the
+// workspace's sticky error word and the late value is replaced by NaN, which
+// reaches the output.  Every awaited value is produced by a workgroup that is
+// resident at the same time (the grid never exceeds the resident capacity)
+// and that waits on nothing but its unit's peers before producing it.  The
+// last workgroup to exit advances the forward tag.
 #include "device.h"
 #include "fused_decode.h"
 
 namespace moe {
 
-constexpr int kFusedMaxM = 16;
+constexpr int kFusedMaxM = 4;
 constexpr int kFusedMaxIB = 8;              // i <= 1024
-constexpr int kMaxKB = 16;                  // gate/up K blocks loaded per batch
-constexpr int kQuarters = 4;                // A task: 32 gate + 32 up rows
-constexpr int kDownRows = 64;               // B task rows
+constexpr int kFusedMaxKB = 16;             // h <= 2048
+constexpr int kFusedMaxGrid = 512;          // two workgroups per CU on 256 CUs
+constexpr int kKBW = kFusedMaxKB / 4;       // K blocks of gate/up per wave
 constexpr uint64_t kWaitTicks = 100000000;  // 1 s of the 100 MHz constant clock
 
 __device__ __forceinline__ uint32_t readlane_u(uint32_t v, int lane) {
@@ -112,89 +119,141 @@ __device__ __forceinline__ uint64_t match_id(int e) {
     return same;
 }
 
-// SiLU(gate) * up of one 128-column group of one route on one 16-lane row,
-// requantised to E4M3 into LDS.  The lane's 16 gate/up words are loaded
-// together and reloaded together until they all carry this forward's tag.
-__device__ __forceinline__ void silu_quant_ll(const uint64_t* __restrict__ gate,
-                                              const uint64_t* __restrict__ up, int sub,
-                                              uint32_t tag, uint32_t* err, uint8_t* q, float* s) {
-    uint64_t wg[8], wu[8];
+// Waiting on words that other workgroups write.  Heavy polling of a line
+// slows the stores that other CUs direct at it (measured: with every lane of
+// many workgroups re-reading all of its words, a producer's stores stalled
+// until the pollers gave up), so a wait first polls one sentinel word per
+// producer -- the last word that producer writes into the range -- with one
+// load per lane and a growing sleep between rounds, then reads the data once
+// and re-reads only while some word still lacks the tag.
+
+// Lane-wise: loads *p until it carries `tag` (lanes with p == nullptr are
+// done at once).  Returns false when the wait timed out (the sticky error
+// word is then set).
+__device__ __forceinline__ bool wait_sentinel(const uint64_t* p, uint32_t tag, uint32_t* err) {
     uint64_t t0 = 0;
+    int nap = 1;
     for (int tries = 0;; ++tries) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            wg[j] = ld_agent64(gate + sub * 8 + j);
-            wu[j] = ld_agent64(up + sub * 8 + j);
-        }
-        bool ok = true;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) ok = ok && ll_tag(wg[j]) == tag && ll_tag(wu[j]) == tag;
-        if (ok) break;
+        const bool ok = p == nullptr || ll_tag(ld_agent64(p)) == tag;
+        if (__ballot(!ok) == 0ull) return true;
         if (tries == 0) t0 = wall_clock64();
         if (wall_clock64() - t0 > kWaitTicks) {
             atomicOr(err, 1u);
-            break;
+            return false;
         }
-        __builtin_amdgcn_s_sleep(1);
+        for (int z = 0; z < nap; ++z) __builtin_amdgcn_s_sleep(2);
+        nap = nap < 8 ? 2 * nap : 8;
     }
-    float v[8];
-    float m = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const float a = ll_value(wg[j]);
-        v[j] = (a / (1.0f + expf(-a))) * ll_value(wu[j]);
-        m = fmaxf(m, fabsf(v[j]));
-    }
-    m = row16_max(m);
-    const float sc = m / kE4M3Max;
-    *reinterpret_cast<uint2*>(q + sub * 8) = quant8(v, sc);
-    if (sub == 0) *s = sc;
 }
 
+// Loads the tagged words p[0..N) (issued together, no conditions; every
+// pointer must address a word written in this forward) until each carries
+// `tag`.  Returns false when the wait timed out.
+template <int N>
+__device__ __forceinline__ bool read_words(const uint64_t* const (&p)[N], uint32_t tag, uint64_t (&w)[N],
+                                           uint32_t* err) {
+    uint64_t t0 = 0;
+    for (int tries = 0;; ++tries) {
+        bool ok = true;
+#pragma unroll
+        for (int j = 0; j < N; ++j) w[j] = ld_agent64(p[j]);
+#pragma unroll
+        for (int j = 0; j < N; ++j) ok = ok && ll_tag(w[j]) == tag;
+        if (__ballot(!ok) == 0ull) return true;
+        if (tries == 0) t0 = wall_clock64();
+        if (wall_clock64() - t0 > kWaitTicks) {
+            atomicOr(err, 1u);
+            return ok;
+        }
+        __builtin_amdgcn_s_sleep(8);
+    }
+}
+
+// LDS carve of one workgroup (all offsets 16-byte aligned).
+struct FusedLds {
+    size_t xq, xs, ids, w, off, act, srt, cnt, misc, sc13, sc2, blk, a2, a2s, y, bounce, total;
+};
+
+__host__ __device__ inline size_t r16(size_t v) { return (v + 15) & ~(size_t)15; }
+
+template <int P, int MM>
+__host__ __device__ inline FusedLds fused_lds(int M, int h, int E, int k) {
+    constexpr int NT = 128 / P / 16;
+    const int R = M * k, G = h / 128;
+    FusedLds L;
+    size_t o = 0;
+    L.xq = o;     o += r16((size_t)M * h);
+    L.xs = o;     o += r16((size_t)M * G * 4);
+    L.ids = o;    o += r16((size_t)R * 4);
+    L.w = o;      o += r16((size_t)R * 4);
+    L.off = o;    o += r16((size_t)(E + 1) * 4);
+    L.act = o;    o += r16((size_t)E * 4);
+    L.srt = o;    o += r16((size_t)R * 4);
+    L.cnt = o;    o += r16((size_t)E * 4);
+    L.misc = o;   o += 32 * 4;
+    L.sc13 = o;   o += 2 * kFusedMaxKB * 4;
+    L.sc2 = o;    o += 16 * 4;
+    L.blk = o;    o += (size_t)2 * NT * kFusedMaxKB * 16 * MM * 4;
+    L.a2 = o;     o += (size_t)MM * 128;
+    L.a2s = o;    o += 16;
+    L.y = o;      o += (size_t)16 * 64 * 4;
+    L.bounce = o; o += (size_t)4 * 2 * 2048;
+    L.total = o;
+    return L;
+}
+
+template <int P, int MM>
 __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
+    constexpr int NT = 128 / P / 16;            // 16-row tiles of gate (and of up) per part
+    // w2 tiles go to waves kDW0..3: with P = 8 wave 0 holds none, so that its
+    // loads of the exchanged values (the vector memory counter retires in
+    // issue order) never wait behind the w2 stream.
+    constexpr int kDW0 = P == 8 ? 1 : 0;
+    constexpr int kDWN = 4 - kDW0;
+    constexpr int NDT = (2048 / P / 16 + kDWN - 1) / kDWN;   // down tiles per wave at h = 2048
     extern __shared__ __align__(16) uint8_t smem[];
     const int M = a.M, h = a.h, i = a.i, E = a.E, k = a.k;
     const int R = M * k, G = h / 128, IB = i / 128, KB = h / 128, N13 = 2 * i;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int col = lane & 15, kg = lane >> 4;
     uint32_t* err = a.sync + kSyncErr / 4;
+    const int q = blockIdx.x % P, uid = blockIdx.x / P;
+    const int u = uid / IB, ib = uid - u * IB;
+    const int drows = h / P, ndt = drows / 16;   // this part's w2 rows and their 16-row tiles
+    const int nb0 = (q * drows) / 128;           // first 128-row block of those rows
 
-    // ---- LDS carve (all offsets 16-byte aligned)
-    uint8_t* xq_l = smem;                                            // [M][h]
-    float* xs_l = reinterpret_cast<float*>(xq_l + M * h);            // [M][G]
-    int* ids_l = reinterpret_cast<int*>(xs_l + ((M * G + 3) & ~3));  // [R]
-    float* w_l = reinterpret_cast<float*>(ids_l + ((R + 3) & ~3));   // [R]
-    int* off_l = reinterpret_cast<int*>(w_l + ((R + 3) & ~3));       // [E+1]
-    int* act_l = off_l + ((E + 1 + 3) & ~3);                         // [E]
-    int* srt_l = act_l + ((E + 3) & ~3);                             // [R]
-    int* cnt_l = srt_l + ((R + 3) & ~3);                             // [E]
-    int* misc_l = cnt_l + ((E + 3) & ~3);                            // [32]
-    uint8_t* a2_l = reinterpret_cast<uint8_t*>(misc_l + 32);         // [16][i + 16]
-    const int a2_stride = i + 16;
-    float* a2s_l = reinterpret_cast<float*>(a2_l + 16 * a2_stride);  // [16][IB]
+    const FusedLds Lo = fused_lds<P, MM>(M, h, E, k);
+    uint8_t* xq_l = smem + Lo.xq;                                   // [M][h]
+    float* xs_l = reinterpret_cast<float*>(smem + Lo.xs);          // [M][G]
+    int* ids_l = reinterpret_cast<int*>(smem + Lo.ids);            // [R]
+    float* w_l = reinterpret_cast<float*>(smem + Lo.w);            // [R]
+    int* off_l = reinterpret_cast<int*>(smem + Lo.off);            // [E+1]
+    int* act_l = reinterpret_cast<int*>(smem + Lo.act);            // [E]
+    int* srt_l = reinterpret_cast<int*>(smem + Lo.srt);            // [R]
+    int* cnt_l = reinterpret_cast<int*>(smem + Lo.cnt);            // [E]
+    int* misc_l = reinterpret_cast<int*>(smem + Lo.misc);          // [32]
+    float* sc13_l = reinterpret_cast<float*>(smem + Lo.sc13);      // [2][kFusedMaxKB] gate, up
+    float* sc2_l = reinterpret_cast<float*>(smem + Lo.sc2);        // [16]
+    float* blk_l = reinterpret_cast<float*>(smem + Lo.blk);        // [2NT][kFusedMaxKB][16][MM]
+    uint8_t* a2_l = smem + Lo.a2;                                   // [MM][128]
+    float* a2s_l = reinterpret_cast<float*>(smem + Lo.a2s);        // [MM]
+    float* y_l = reinterpret_cast<float*>(smem + Lo.y);            // [16][64]
+    uint8_t* bounce = smem + Lo.bounce + wave * 4096;               // [2][2048] per wave
 
-    // ---- phase 0: tag, routing, activation codes and grouping.  The first
-    // token's logits and the first batch of x rows are requested before any
-    // of them is used.
-    // The forward count is read now and stored to LDS only after routing, so
-    // that its load does not hold up the logits and x loads behind it.
+    // ---- phase 0: tag, routing of every token, active experts
     uint32_t epoch = 0u;
     if (tid == 0) epoch = ld_agent(a.sync + kSyncEpoch / 4);
     uint32_t* bm_l = reinterpret_cast<uint32_t*>(misc_l + 8);   // experts present in the batch
     if (tid < 8) bm_l[tid] = 0u;
-    const int nq = M * G;   // 16-lane rows of activation groups
+    const int nq = M * G;   // 16-lane rows of activation groups (<= 64)
     const int qbase = wave * 4 + (lane >> 4);
     uint4 xr[4];
-    auto x_load = [&](int base) {
 #pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-            const int task = base + 16 * s4;
-            if (task < nq) {
-                const int t = task / G, g = task - t * G;
-                xr[s4] = *reinterpret_cast<const uint4*>(a.x + (size_t)t * h + g * 128 + col * 8);
-            }
-        }
-    };
+    for (int s4 = 0; s4 < 4; ++s4) {
+        const int task = min(qbase + 16 * s4, nq - 1);
+        const int t = task / G, g = task - t * G;
+        xr[s4] = *reinterpret_cast<const uint4*>(a.x + (size_t)t * h + g * 128 + col * 8);
+    }
     float lg[4];
     auto l_load = [&](int t) {
 #pragma unroll
@@ -204,7 +263,6 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
         }
     };
     l_load(wave);
-    x_load(qbase);
 #pragma unroll 1
     for (int t = wave; t < M; t += 4) {
         if (t != wave) l_load(t);
@@ -212,9 +270,6 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
     }
     asm volatile("" : "+v"(epoch));   // the count is first needed here
     if (tid == 0) misc_l[3] = (int)(epoch + 1u);
-    // the active experts (ascending) right after routing, so that the weight
-    // prefetch below is in flight while the activations are quantised and
-    // the routes grouped
     __syncthreads();
     for (int p = tid; p < R; p += 256) atomicOr(&bm_l[ids_l[p] >> 5], 1u << (ids_l[p] & 31));
     __syncthreads();
@@ -236,98 +291,84 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
     __syncthreads();
     const int U = misc_l[0];
     const uint32_t tag = (uint32_t)misc_l[3];
-    const int nA = U * IB * kQuarters;
-    const int NT = h / kDownRows;
-    const int nB = U * NT;
+    const bool has_unit = u < U;
+    const int e = has_unit ? act_l[u] : 0;
 
-    // ---- prefetch: the first gate/up task's first K batch (or, without gate/up
-    // work, the first down task's weights)
-    // weights in registers; each task's 16 (8) block scales arrive as one
-    // lane-indexed load (lane j holds block j's scale) and are read back with
-    // readlane
-    v8i Aw[kMaxKB];
-    float Asc_v = 0.0f;
-    v8i Bw[kFusedMaxIB];
-    float Bsc_v = 0.0f;
-    auto a_geom = [&](int task, int& u, int& e, int& row0) {
-        u = task / (IB * kQuarters);
-        const int rem = task - u * IB * kQuarters;
-        const int jg = rem / kQuarters, q = rem - jg * kQuarters;
-        e = act_l[u];
-        row0 = (wave >> 1) * i + jg * 128 + q * 32 + (wave & 1) * 16;
-    };
-    auto a_load = [&](int e, int row0, int kb0) {
-        const uint8_t* wrow = a.w13 + ((size_t)e * N13 + row0 + col) * h + kg * 32 + kb0 * 128;
-        const float* ws = a.s13 + ((size_t)e * (N13 / 128) + row0 / 128) * KB + kb0;
-        const int nkb = min(KB - kb0, kMaxKB);
-        if (lane < nkb) Asc_v = ws[lane];
-#pragma unroll
-        for (int u8 = 0; u8 < kMaxKB; ++u8)
-            if (u8 < nkb) Aw[u8] = load32(wrow + u8 * 128);
-    };
-    auto b_load = [&](int task) {
-        const int u = task / NT, nt = task - u * NT;
-        const int e = act_l[u];
-        const int n0 = nt * kDownRows + wave * 16;
-        const uint8_t* wrow = a.w2 + ((size_t)e * h + n0 + col) * i + kg * 32;
-        const float* ws = a.s2 + ((size_t)e * (h / 128) + n0 / 128) * IB;
-        if (lane < IB) Bsc_v = ws[lane];
-#pragma unroll
-        for (int kb = 0; kb < kFusedMaxIB; ++kb)
-            if (kb < IB) Bw[kb] = load32(wrow + kb * 128);
-    };
-    // nothing from phase 0 is still in flight (its loads were consumed);
-    // saying so keeps the compiler from draining the prefetch below later on
+    // ---- every weight byte of the part requested now: block scales first,
+    // then w13 (the gate/up tiles, this wave's K blocks kb = wave + 4j), then
+    // w2 (this wave's 16-row down tiles), each tile as whole 128-byte lines.
+    // Nothing from phase 0 is still in flight; saying so keeps the compiler
+    // from draining these loads at the waits below.
     wait_vmem();
-    if ((int)blockIdx.x < nA) {
-        int u, e, row0;
-        a_geom(blockIdx.x, u, e, row0);
-        a_load(e, row0, 0);
-    } else if ((int)blockIdx.x < nB) {
-        b_load(blockIdx.x);   // no gate/up work here: fetch the down tile now
-    }
-
-#pragma unroll 1
-    for (int base = qbase; base < nq; base += 64) {
-        if (base != qbase) x_load(base);
+    v8i A[2 * NT][kKBW];
+    v8i D[NDT];
+    float sc_v = 0.0f;
+    if (has_unit) {
+        if (wave == 0) {
+            if (lane < 2 * KB) {
+                const int blk_row = lane < KB ? ib : IB + ib;
+                sc_v = a.s13[((size_t)e * (N13 / 128) + blk_row) * KB + (lane < KB ? lane : lane - KB)];
+            } else if (lane >= 32 && lane - 32 <= (q * drows + drows - 1) / 128 - nb0) {
+                sc_v = a.s2[((size_t)e * (h / 128) + nb0 + lane - 32) * IB + ib];
+            }
+        }
+        // Unconditional loads (a K block or tile past the end re-reads the last
+        // one and is not used): a conditionally loaded register would be
+        // copied into place after its load, which makes the wave wait for it.
 #pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-            const int task = base + 16 * s4;
-            if (task < nq) {
-                const int t = task / G, g = task - t * G;
-                const uint4 u = xr[s4];
-                float v[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
-                              bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w)};
-                float m = 0.0f;
+        for (int t2 = 0; t2 < 2 * NT; ++t2) {
+            const int row = (t2 < NT ? 0 : i) + ib * 128 + q * (128 / P) + (t2 % NT) * 16;
+            const uint8_t* base = a.w13 + ((size_t)e * N13 + row) * h;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
-                m = row16_max(m);
-                const float sc = m / kE4M3Max;
-                *reinterpret_cast<uint2*>(xq_l + t * h + g * 128 + col * 8) = quant8(v, sc);
-                if (col == 0) xs_l[t * G + g] = sc;
+            for (int j = 0; j < kKBW; ++j) A[t2][j] = load_lines(base + min(wave + 4 * j, KB - 1) * 128, h, lane);
+        }
+        if (wave >= kDW0) {
+#pragma unroll
+            for (int j = 0; j < NDT; ++j) {
+                const int tt = min(wave - kDW0 + kDWN * j, ndt - 1);
+                D[j] = load_lines(a.w2 + ((size_t)e * h + q * drows + tt * 16) * i + ib * 128, i, lane);
             }
         }
     }
-    __syncthreads();
+
+    // ---- activation codes of every token into LDS (while the weights
+    // stream): M * h / 128 <= 64 groups, one 16-lane row each
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+        const int task = qbase + 16 * s4;
+        if (task < nq) {
+            const int t = task / G, g = task - t * G;
+            const uint4 uu = xr[s4];
+            float v[8] = {bf16_lo(uu.x), bf16_hi(uu.x), bf16_lo(uu.y), bf16_hi(uu.y),
+                          bf16_lo(uu.z), bf16_hi(uu.z), bf16_lo(uu.w), bf16_hi(uu.w)};
+            float m = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+            m = row16_max(m);
+            const float sc = m / kE4M3Max;
+            *reinterpret_cast<uint2*>(xq_l + t * h + g * 128 + col * 8) = quant8(v, sc);
+            if (col == 0) xs_l[t * G + g] = sc;
+        }
+    }
     if (wave == 0) {
         // counts and each route's rank inside its expert (ballot match per
         // 64 routes), then offsets by a DPP prefix sum, then the routes in
         // (expert, route id) order
-        for (int e = lane; e < E; e += 64) cnt_l[e] = 0;
+        for (int ee = lane; ee < E; ee += 64) cnt_l[ee] = 0;
         const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-        int lr[4], ee[4];
+        int lr[4], ee4[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             lr[b] = 0;
-            ee[b] = 0x1FF;
+            ee4[b] = 0x1FF;
             if (64 * b < R) {
                 const int p = 64 * b + lane;
-                const int e = p < R ? ids_l[p] : 0x1FF;
-                const uint64_t same = match_id(e);
+                const int ep = p < R ? ids_l[p] : 0x1FF;
+                const uint64_t same = match_id(ep);
                 if (p < R) {
-                    lr[b] = cnt_l[e] + __popcll(same & below);
-                    ee[b] = e;
-                    if ((same >> lane) == 1ull) cnt_l[e] += __popcll(same);
+                    lr[b] = cnt_l[ep] + __popcll(same & below);
+                    ee4[b] = ep;
+                    if ((same >> lane) == 1ull) cnt_l[ep] += __popcll(same);
                 }
             }
         }
@@ -339,139 +380,208 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
         int run = incl - lsum;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int e = 4 * lane + j;
-            if (e < E) off_l[e] = run;
+            const int ej = 4 * lane + j;
+            if (ej < E) off_l[ej] = run;
             run += c[j];
         }
         if (lane == 63) off_l[E] = incl;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const int p = 64 * b + lane;
-            if (p < R) srt_l[off_l[ee[b]] + lr[b]] = p;
+            if (p < R) srt_l[off_l[ee4[b]] + lr[b]] = p;
+        }
+        // the block scales (the first loads of the batch to arrive)
+        if (has_unit) {
+            if (lane < 2 * KB) sc13_l[lane < KB ? lane : kFusedMaxKB + lane - KB] = sc_v;
+            if (lane >= 32 && lane < 48) sc2_l[lane - 32] = sc_v;
         }
     }
     __syncthreads();
 
-    // ---- phase 1: gate/up quarters
-    for (int task = blockIdx.x; task < nA; task += gridDim.x) {
-        int u, e, row0;
-        a_geom(task, u, e, row0);
-        const int beg = off_l[e], cnt = off_l[e + 1] - beg;
-        const bool valid = col < cnt;
-        const int p = valid ? srt_l[beg + col] : 0;
-        const int t = p / k;
-        const uint8_t* xrow = xq_l + t * h + kg * 32;
-        const float* xsr = xs_l + t * G;
-        v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int kb0 = 0; kb0 < KB; kb0 += kMaxKB) {
-            if (kb0 > 0 || task != (int)blockIdx.x) a_load(e, row0, kb0);
+    // The code below is straight-line wherever it touches memory: loads use
+    // clamped (always valid) addresses and unused values are dropped by
+    // selects, because a load under a lane-dependent condition makes the
+    // compiler copy its result into place after a wait for it.
+    const int beg = has_unit ? off_l[e] : 0;
+    const int cnt = has_unit ? off_l[e + 1] - beg : 0;   // routes of expert e (<= M <= MM)
+    const int cntc = cnt > 0 ? cnt : 1;
+    const bool valid = col < cnt;
+    const int pc = srt_l[beg + min(col, cntc - 1)];        // route of MFMA column col (clamped)
+    const v8i zero = zero8();
+
+    // ---- gate/up: raw MFMA block sums of this wave's K blocks into LDS
+    if (has_unit) {
+        const int tc = pc / k;
 #pragma unroll
-            for (int u8 = 0; u8 < kMaxKB; ++u8) {
-                const int kb = kb0 + u8;
-                if (kb < KB) {
-                    const v8i B = valid ? load32(xrow + kb * 128) : zero8();
-                    const float sc = (valid ? xsr[kb] : 0.0f) * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Asc_v), u8));
+        for (int j = 0; j < kKBW; ++j) {
+            const int kb = wave + 4 * j;
+            if (kb < KB) {
+                v8i B = load32(xq_l + tc * h + kb * 128 + kg * 32);
+                B = valid ? B : zero;
+#pragma unroll
+                for (int t2 = 0; t2 < 2 * NT; ++t2) {
                     const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
-                    const v4f blk = mfma_16x16x128_e4m3(Aw[u8], B, z);
+                    const v4f blk = mfma_16x16x128_e4m3(lines_to_frag(A[t2][j], bounce + (t2 & 1) * 2048, lane, col, kg),
+                                                        B, z);
+                    if (valid) {
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) acc[v] = fmaf(blk[v], sc, acc[v]);
+                        for (int v = 0; v < 4; ++v)
+                            blk_l[((t2 * kFusedMaxKB + kb) * 16 + 4 * kg + v) * MM + col] = blk[v];
+                    }
                 }
             }
         }
-        if (valid) {
-            uint64_t* gp = a.g_ll + (size_t)p * N13 + row0 + kg * 4;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) st_agent64(gp + v, ll_pack(acc[v], tag));
-        }
     }
+    __syncthreads();
 
-    // The down tile's weights are fetched only now by workgroups that had
-    // gate/up work: they are not needed before the gate/up results of the
-    // whole route are in, and fetching them earlier only competes with the
-    // gate/up weights for bandwidth.
-    if ((int)blockIdx.x < nA && (int)blockIdx.x < nB) b_load(blockIdx.x);
-
-    // ---- phase 2: down tiles
-    for (int task = blockIdx.x; task < nB; task += gridDim.x) {
-        const int u = task / NT, nt = task - u * NT;
-        const int e = act_l[u];
-        const int beg = off_l[e], cnt = off_l[e + 1] - beg;
-        const int n0 = nt * kDownRows + wave * 16;
-        if (task != (int)blockIdx.x) b_load(task);
-#pragma unroll 1
-        for (int r2 = wave * 4 + (lane >> 4); r2 < cnt * IB; r2 += 16) {
-            const int jr = r2 / IB, b = r2 - jr * IB;
-            const uint64_t* gr = a.g_ll + (size_t)srt_l[beg + jr] * N13 + b * 128;
-            silu_quant_ll(gr, gr + i, col, tag, err, a2_l + jr * a2_stride + b * 128,
-                          a2s_l + jr * IB + b);
-        }
-        __syncthreads();
-        const bool valid = col < cnt;
-        const int p = valid ? srt_l[beg + col] : 0;
-        v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    // ---- block promotion in K order: acc += blk * (s_act * s_w), the scale
+    // product rounded first, then SiLU(gate) * up, published for the unit's
+    // parts; one lane per (route, gate/up row pair)
+    if (has_unit && wave == 0) {
 #pragma unroll
-        for (int kb = 0; kb < kFusedMaxIB; ++kb) {
-            if (kb < IB) {
-                const v8i B = valid ? load32(a2_l + col * a2_stride + kb * 128 + kg * 32) : zero8();
-                const float sc = (valid ? a2s_l[col * IB + kb] : 0.0f) *
-                                 __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Bsc_v), kb));
-                const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
-                const v4f blk = mfma_16x16x128_e4m3(Bw[kb], B, z);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) acc[v] = fmaf(blk[v], sc, acc[v]);
-            }
-        }
-        if (valid) {
-            uint64_t* yp = a.y_ll + (size_t)p * h + n0 + kg * 4;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) st_agent64(yp + v, ll_pack(acc[v], tag));
-        }
-        __syncthreads();
-    }
-
-    // ---- phase 3: combine the tiles of the tokens whose last-rank route this
-    // workgroup computed (after all of its own down tiles)
-    for (int task = blockIdx.x; task < nB; task += gridDim.x) {
-        const int u = task / NT, nt = task - u * NT;
-        const int e = act_l[u];
-        const int beg = off_l[e], cnt = off_l[e + 1] - beg;
-        for (int jr = 0; jr < cnt; ++jr) {
-            const int pr = srt_l[beg + jr];
-            if (pr % k != k - 1) continue;
-            const int t = pr / k;
-            if (tid < kDownRows) {
+        for (int rep = 0; rep < (MM * 16 * NT + 63) / 64; ++rep) {
 #pragma clang fp contract(off)
-                // the k partials of column n, loaded together until all are
-                // from this forward, then summed in rank order
-                const int n = nt * kDownRows + tid;
-                const uint64_t* yc = a.y_ll + (size_t)t * k * h + n;
-                uint64_t w[16];
-                uint64_t t0 = 0;
-                for (int tries = 0;; ++tries) {
-                    bool ok = true;
+            const int L = lane + 64 * rep;
+            const int c = min(L / (16 * NT), cntc - 1), r = L % (16 * NT);
+            const int tg = r >> 4, rr = r & 15;
+            const int p = srt_l[beg + c];
+            const float* xsr = xs_l + (p / k) * G;
+            float xv[kFusedMaxKB], bg[kFusedMaxKB], bu[kFusedMaxKB];
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        if (r < k) {
-                            w[r] = ld_agent64(yc + (size_t)r * h);
-                            ok = ok && ll_tag(w[r]) == tag;
-                        }
-                    }
-                    if (ok) break;
-                    if (tries == 0) t0 = wall_clock64();
-                    if (wall_clock64() - t0 > kWaitTicks) {
-                        atomicOr(err, 1u);
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(1);
-                }
-                float accum = 0.0f;
+            for (int kb = 0; kb < kFusedMaxKB; ++kb) {
+                xv[kb] = xsr[kb];   // past G: other LDS words, dropped below
+                bg[kb] = blk_l[((tg * kFusedMaxKB + kb) * 16 + rr) * MM + c];
+                bu[kb] = blk_l[(((NT + tg) * kFusedMaxKB + kb) * 16 + rr) * MM + c];
+            }
+            float ag = 0.0f, au = 0.0f;
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (r < k) accum = accum + w_l[t * k + r] * ll_value(w[r]);
-                __bf16 bv = (__bf16)accum;
-                a.out[(size_t)t * h + n] = __builtin_bit_cast(uint16_t, bv);
+            for (int kb = 0; kb < kFusedMaxKB; ++kb) {
+                const float tg_ = bg[kb] * (xv[kb] * sc13_l[kb]);
+                const float tu_ = bu[kb] * (xv[kb] * sc13_l[kFusedMaxKB + kb]);
+                ag = ag + (kb < KB ? tg_ : -0.0f);   // -0 added leaves any value unchanged
+                au = au + (kb < KB ? tu_ : -0.0f);
+            }
+            const float v = (ag / (1.0f + expf(-ag))) * au;
+            if (L < cnt * 16 * NT) st_agent64(a.v_ll + (size_t)p * i + ib * 128 + q * (128 / P) + r, ll_pack(v, tag));
+        }
+
+        // the unit's 128 SiLU-mul values of each route, from all its parts:
+        // first the sentinel of every (route, part) -- the part's last column
+        // -- then the values (lane l takes values 4(l % 32) .. +3; clamped
+        // routes re-read a real one); amax, the scale amax/448 and the E4M3
+        // codes into LDS
+        const uint64_t* sent = nullptr;
+        if (lane < cnt * P) {
+            const int c = lane / P, qq = lane - c * P;
+            sent = a.v_ll + (size_t)srt_l[beg + c] * i + ib * 128 + qq * (128 / P) + 128 / P - 1;
+        }
+        bool ok = wait_sentinel(sent, tag, err);
+        const uint64_t* ptrs[4 * MM];
+#pragma unroll
+        for (int c = 0; c < MM; ++c) {
+            const uint64_t* vp = a.v_ll + (size_t)srt_l[beg + min(c, cntc - 1)] * i + ib * 128 + 4 * (lane & 31);
+#pragma unroll
+            for (int m4 = 0; m4 < 4; ++m4) ptrs[4 * c + m4] = vp + m4;
+        }
+        uint64_t w[4 * MM];
+        ok = read_words<4 * MM>(ptrs, tag, w, err) && ok;
+        const bool all_ok = __ballot(!ok) == 0ull;
+#pragma unroll
+        for (int c = 0; c < MM; ++c) {
+            if (c < cnt) {
+                float v4[4];
+#pragma unroll
+                for (int m4 = 0; m4 < 4; ++m4) v4[m4] = ll_value(w[4 * c + m4]);
+                float m = fmaxf(fmaxf(fabsf(v4[0]), fabsf(v4[1])), fmaxf(fabsf(v4[2]), fabsf(v4[3])));
+                m = xor16_max(row16_max(m));   // lanes l and l + 32 hold the same values
+                const float sc = all_ok ? m / kE4M3Max : __builtin_nanf("");
+                const uint32_t codes = sc != 0.0f ? quant4(v4[0], v4[1], v4[2], v4[3], sc, __builtin_amdgcn_rcpf(sc)) : 0u;
+                if (lane < 32) *reinterpret_cast<uint32_t*>(a2_l + c * 128 + 4 * lane) = codes;
+                if (lane == 0) a2s_l[c] = sc;
             }
         }
+    }
+    __syncthreads();
+
+    // ---- down: this part's rows times the unit's K block, published as block
+    // terms blk * (a2s * s2) per route
+    if (has_unit && wave >= kDW0) {
+        const int cl = min(col, MM - 1);
+        v8i B = load32(a2_l + cl * 128 + kg * 32);
+        B = valid ? B : zero;
+        const float a2sv = a2s_l[cl];
+#pragma unroll
+        for (int j = 0; j < NDT; ++j) {
+            const int tt = wave - kDW0 + kDWN * j;
+            if (tt < ndt) {
+                const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+                const v4f blk = mfma_16x16x128_e4m3(lines_to_frag(D[j], bounce + (j & 1) * 2048, lane, col, kg), B, z);
+                const int n0 = q * drows + tt * 16;
+                const float sc = a2sv * sc2_l[n0 / 128 - nb0];
+                if (valid) {
+                    uint64_t* tp = a.t_ll + ((size_t)pc * IB + ib) * h + n0 + 4 * kg;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) st_agent64(tp + v, ll_pack(blk[v] * sc, tag));
+                }
+            }
+        }
+    }
+
+    // ---- combine 64 output columns of a token: wave w sums the block terms
+    // of ranks w, w + 4, ... over the blocks ascending, then wave 0 adds the
+    // ranks in order with their routing weights
+    const int nct = M * (h / 64);
+    for (int ct = blockIdx.x; ct < nct; ct += gridDim.x) {
+        const int t = ct / (h / 64), n = (ct - t * (h / 64)) * 64 + lane;
+        // sentinels first: lane j < (ranks of this wave) * IB polls the last
+        // column of this tile in the term row of (rank wave + 4 (j / IB),
+        // block j % IB); then every rank and block slot reads a real word
+        // (clamped duplicates of live words)
+        const int nr = k > wave ? (k - wave + 3) / 4 : 0;   // ranks of this wave
+        const uint64_t* sent = nullptr;
+        if (lane < nr * IB) {
+            const int rj = lane / IB, b = lane - rj * IB;
+            sent = a.t_ll + ((size_t)(t * k + wave + 4 * rj) * IB + b) * h + (n - lane) + 63;
+        }
+        bool ok = wait_sentinel(sent, tag, err);
+        const uint64_t* ptrs[4 * kFusedMaxIB];
+#pragma unroll
+        for (int rj = 0; rj < 4; ++rj) {
+            const int r = min(wave + 4 * rj, k - 1);
+#pragma unroll
+            for (int b = 0; b < kFusedMaxIB; ++b)
+                ptrs[rj * kFusedMaxIB + b] = a.t_ll + ((size_t)(t * k + r) * IB + min(b, IB - 1)) * h + n;
+        }
+        uint64_t w[4 * kFusedMaxIB];
+        ok = read_words<4 * kFusedMaxIB>(ptrs, tag, w, err) && ok;
+#pragma unroll
+        for (int rj = 0; rj < 4; ++rj) {
+#pragma clang fp contract(off)
+            float y = 0.0f;
+#pragma unroll
+            for (int b = 0; b < kFusedMaxIB; ++b) y = y + (b < IB ? ll_value(w[rj * kFusedMaxIB + b]) : -0.0f);
+            const int r = wave + 4 * rj;
+            if (r < k) y_l[r * 64 + lane] = ok ? y : __builtin_nanf("");
+        }
+        __syncthreads();
+        if (wave == 0) {
+#pragma clang fp contract(off)
+            float wv[16], yv[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                wv[r] = w_l[min(t * k + r, R - 1)];
+                yv[r] = y_l[r * 64 + lane];
+            }
+            float acc = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float term = wv[r] * yv[r];
+                acc = acc + (r < k ? term : -0.0f);
+            }
+            __bf16 bv = (__bf16)acc;
+            a.out[(size_t)t * h + n] = __builtin_bit_cast(uint16_t, bv);
+        }
+        __syncthreads();
     }
 
     // Workgroup 0 publishes the batch's routing and quantisation (inspection).
@@ -481,10 +591,10 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
             a.tw[p] = w_l[p];
             a.sorted[p] = srt_l[p];
         }
-        for (int e = tid; e < E; e += 256) {
-            a.offsets[e] = off_l[e];
-            a.counts[e] = off_l[e + 1] - off_l[e];
-            a.active[e] = e < U ? act_l[e] : 0;
+        for (int ee = tid; ee < E; ee += 256) {
+            a.offsets[ee] = off_l[ee];
+            a.counts[ee] = off_l[ee + 1] - off_l[ee];
+            a.active[ee] = ee < U ? act_l[ee] : 0;
         }
         if (tid == 0) {
             a.offsets[E] = off_l[E];
@@ -503,72 +613,100 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
     }
     __syncthreads();
     if (misc_l[4]) {
-        const uint32_t epoch = tag - 1u;
-        if (epoch + 2u == 0u) {
+        const uint32_t ep = tag - 1u;
+        if (ep + 2u == 0u) {
             // the next tag would be 0, the value of a cleared word: clear the
             // exchange region and start counting again
-            uint64_t* ll = a.g_ll;
+            uint64_t* ll = a.v_ll;
             for (size_t j = tid; j < kLLBytes / 8; j += 256) st_agent64(ll + j, 0ull);
             wait_vmem();
             __syncthreads();
             if (tid == 0) st_agent(a.sync + kSyncEpoch / 4, 0u);
         } else if (tid == 0) {
-            st_agent(a.sync + kSyncEpoch / 4, epoch + 1u);
+            st_agent(a.sync + kSyncEpoch / 4, ep + 1u);
         }
         if (tid == 0) st_agent(a.sync + kSyncExit / 4, 0u);
     }
 }
 
+// Parts per unit for a batch: 8 when the grid of every possible unit fits,
+// else 4, else 0 (not supported).
+int fused_parts(int M, int i, int E, int k) {
+    const int umax = std::min(E, M * k);
+    const int units = umax * (i / 128);
+    if (units * 8 <= kFusedMaxGrid) return 8;
+    if (units * 4 <= kFusedMaxGrid) return 4;
+    return 0;
+}
+
+template <int P>
+static size_t lds_for(int M, int h, int E, int k) {
+    switch (M) {
+        case 1: return fused_lds<P, 1>(M, h, E, k).total;
+        case 2: return fused_lds<P, 2>(M, h, E, k).total;
+        case 3: return fused_lds<P, 3>(M, h, E, k).total;
+        default: return fused_lds<P, 4>(M, h, E, k).total;
+    }
+}
+
 size_t fused_lds_bytes(int M, int h, int i, int E, int k) {
-    const int R = M * k, G = h / 128;
-    auto r4 = [](int v) { return (size_t)((v + 3) & ~3); };
-    size_t b = (size_t)M * h;
-    b += r4(M * G) * 4;
-    b += r4(R) * 4 * 2;
-    b += r4(E + 1) * 4 + r4(E) * 4 + r4(R) * 4 + r4(E) * 4 + 32 * 4;
-    b += (size_t)16 * (i + 16) + ((size_t)16 * kFusedMaxIB + 64) * 4;   // a2, a2 scales, router scratch
-    return (b + 15) & ~(size_t)15;
+    const int P = fused_parts(M, i, E, k);
+    if (P == 8) return lds_for<8>(M, h, E, k);
+    if (P == 4) return lds_for<4>(M, h, E, k);
+    return 0;
 }
 
 bool fused_supported(int M, int h, int i, int E, int k) {
-    const size_t R = (size_t)M * k, words = kLLBytes / 16;   // each exchange buffer: 4 MiB
-    return M >= 1 && M <= kFusedMaxM && k <= 16 && E <= 256 && h % 128 == 0 && i % 128 == 0 &&
-           i / 128 <= kFusedMaxIB && (size_t)M * h <= 32768 && h % kDownRows == 0 &&
-           R * 2 * i <= words && R * h <= words && fused_lds_bytes(M, h, i, E, k) <= 64 * 1024;
+    const size_t R = (size_t)M * k, IB = (size_t)i / 128;
+    return M >= 1 && M <= kFusedMaxM && k <= 16 && E <= 256 && h % 128 == 0 && h <= 128 * kFusedMaxKB &&
+           (size_t)M * (h / 128) <= 64 &&
+           i % 128 == 0 && IB <= kFusedMaxIB && fused_parts(M, i, E, k) > 0 &&
+           fused_v_words(M, i, k) + R * IB * h <= kLLBytes / 8 && fused_lds_bytes(M, h, i, E, k) <= 64 * 1024;
 }
 
-// Workgroups that can be resident at once, per device (queried once).
-static int resident_capacity(size_t lds) {
+// Launches one instance after checking that its whole grid can be resident
+// at once (the workgroups wait on each other); the occupancy is queried once
+// per device and LDS size.
+template <int P, int MM>
+static hipError_t launch_instance(const FusedArgs& args, int grid, size_t lds, hipStream_t stream) {
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
     static int cached_cu[64] = {0};
     static size_t cached_lds[64] = {0};
     static int cached_blocks[64] = {0};
-    if (dev < 0 || dev >= 64) return 0;
     if (cached_cu[dev] == 0 || cached_lds[dev] != lds) {
         int cu = 0, nb = 0;
         if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            return 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fused_decode_kernel, 256, lds) !=
-            hipSuccess)
-            return 0;
+            return hipErrorInvalidDevice;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fused_decode_kernel<P, MM>, 256, lds) != hipSuccess)
+            return hipErrorInvalidConfiguration;
         cached_cu[dev] = cu;
         cached_blocks[dev] = nb;
         cached_lds[dev] = lds;
     }
-    return cached_cu[dev] * cached_blocks[dev];
+    if (cached_cu[dev] * cached_blocks[dev] < grid) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((fused_decode_kernel<P, MM>), dim3(grid), dim3(256), lds, stream, args);
+    return hipGetLastError();
+}
+
+template <int P>
+static hipError_t launch_parts(const FusedArgs& args, int grid, size_t lds, hipStream_t stream) {
+    switch (args.M) {
+        case 1: return launch_instance<P, 1>(args, grid, lds, stream);
+        case 2: return launch_instance<P, 2>(args, grid, lds, stream);
+        case 3: return launch_instance<P, 3>(args, grid, lds, stream);
+        case 4: return launch_instance<P, 4>(args, grid, lds, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_fused_decode(const FusedArgs& args, hipStream_t stream) {
+    const int P = fused_parts(args.M, args.i, args.E, args.k);
     const size_t lds = fused_lds_bytes(args.M, args.h, args.i, args.E, args.k);
-    const int cap = resident_capacity(lds);
-    if (cap <= 0) return hipErrorInvalidConfiguration;
-    const int IB = args.i / 128;
-    const int umax = std::min(args.E, args.M * args.k);
-    const int want = std::max(umax * IB * kQuarters, umax * (args.h / kDownRows));
-    const int grid = std::max(1, std::min(cap, want));
-    hipLaunchKernelGGL(fused_decode_kernel, dim3(grid), dim3(256), lds, stream, args);
-    return hipGetLastError();
+    const int grid = std::min(args.E, args.M * args.k) * (args.i / 128) * P;
+    if (P == 8) return launch_parts<8>(args, grid, lds, stream);
+    if (P == 4) return launch_parts<4>(args, grid, lds, stream);
+    return hipErrorInvalidValue;
 }
 
 __global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* __restrict__ p, size_t n) {

@@ -93,6 +93,12 @@ constexpr int kFrontMaxHidden = 8192;
 hipError_t launch_rmsnorm_quant(const uint16_t* x, const float* gamma, float eps, int M, int h,
                                 uint16_t* y, uint8_t* q, float* s, hipStream_t stream);
 
+// Measurement kernels (not on the forward path): an empty kernel of `grid`
+// 256-thread workgroups, and a streaming read of `bytes` (a multiple of 16)
+// that leaves 4 * grid words at `sink`.
+hipError_t launch_probe_empty(int grid, hipStream_t stream);
+hipError_t launch_probe_read(const void* src, size_t bytes, int grid, uint32_t* sink, hipStream_t stream);
+
 // Utilities.
 hipError_t launch_quant_weight(const float* w, int64_t batch, int N, int K, uint8_t* q, float* s,
                                hipStream_t stream);

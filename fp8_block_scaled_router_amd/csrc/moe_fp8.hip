@@ -45,15 +45,12 @@ struct Layout {
     size_t mtile_off;   // prefill path: [E + 1] ints
 };
 
-// Largest batch sent to the one-kernel decode path: it recomputes routing
-// and quantisation in every workgroup and moves each step's results between
-// workgroups through memory, which stops paying off above this (measured on
-// MI355X at h = 2048, i = 768, E = 128, k = 8, uniform routing: one kernel
-// 38.6 / 47.1 / 55.0 us at M = 2 / 3 / 4, multi-kernel 44.5 / 47.8 / 50.3).
-constexpr int kFusedPathMaxM = 3;
-
+// The one-kernel decode path takes every batch it supports: its grid (one
+// workgroup per eighth or quarter of an (expert, 128-column intermediate
+// block) unit, for every expert the batch could select) must be resident at
+// once, which limits it to one or two tokens at the layer shapes.
 int choose_path(int M, int h, int i, int E, int k) {
-    if (M <= kFusedPathMaxM && moe::fused_supported(M, h, i, E, k)) return MOE_FP8_PATH_FUSED_DECODE;
+    if (moe::fused_supported(M, h, i, E, k)) return MOE_FP8_PATH_FUSED_DECODE;
     if ((int64_t)M * k >= (int64_t)32 * E && moe::prefill_supported(M, h, i, k)) return MOE_FP8_PATH_PREFILL;
     return MOE_FP8_PATH_STREAM;
 }
@@ -211,8 +208,8 @@ int run_forward(const void* x, const float* router_logits, const void* w13, cons
         fa.sorted = sorted;
         fa.active = active;
         fa.num_active = num_active;
-        fa.g_ll = at<uint64_t>(workspace, moe::kLLOffset);
-        fa.y_ll = at<uint64_t>(workspace, moe::kLLOffset + moe::kLLBytes / 2);
+        fa.v_ll = at<uint64_t>(workspace, moe::kLLOffset);
+        fa.t_ll = fa.v_ll + moe::fused_v_words(M, i, k);
         fa.sync = sync;
         MOE_STEP(moe::launch_fused_decode(fa, stream));
         return hook.mark() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
@@ -453,6 +450,28 @@ int moe_fp8_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t 
     if (workspace_bytes < moe::kWorkspaceHead) return MOE_ERR_WORKSPACE;
     return hip_status(moe::launch_zero_words(static_cast<uint32_t*>(workspace),
                                              moe::kWorkspaceHead / 4, stream));
+}
+
+int moe_fp8_workspace_status(void* workspace, size_t workspace_bytes, int clear, uint32_t* flags,
+                             hipStream_t stream) {
+    if (!workspace || !flags || ((uintptr_t)workspace % kAlign) != 0) return MOE_ERR_INVALID;
+    if (workspace_bytes < moe::kWorkspaceHead) return MOE_ERR_WORKSPACE;
+    uint32_t* word = at<uint32_t>(workspace, moe::kSyncErr);
+    if (hipMemcpyAsync(flags, word, 4, hipMemcpyDeviceToHost, stream) != hipSuccess) return MOE_ERR_HIP;
+    if (clear && moe::launch_zero_words(word, 1, stream) != hipSuccess) return MOE_ERR_HIP;
+    return hip_status(hipStreamSynchronize(stream));
+}
+
+int moe_fp8_probe_empty(int grid, hipStream_t stream) {
+    if (grid < 1 || grid > (1 << 20)) return MOE_ERR_INVALID;
+    return hip_status(moe::launch_probe_empty(grid, stream));
+}
+
+int moe_fp8_probe_read(const void* src, size_t bytes, int grid, uint32_t* sink, hipStream_t stream) {
+    if (!src || !sink || !aligned16(src) || bytes % 16 != 0 || grid < 1 || grid > (1 << 20))
+        return MOE_ERR_INVALID;
+    if (bytes == 0) return MOE_OK;
+    return hip_status(moe::launch_probe_read(src, bytes, grid, sink, stream));
 }
 
 int moe_fp8_forward(const void* x, const float* router_logits, const void* w13, const float* s13,

@@ -90,6 +90,17 @@ size_t moe_fp8_workspace_bytes(int M, int h, int i, int E, int k);
  * timed out (a broken device or a corrupted workspace), in which case it is
  * set and that forward's output is invalid. */
 
+/* Reads the sticky error word of a workspace into *flags (0: every wait
+ * between workgroups completed; nonzero: a wait of some earlier forward on
+ * this workspace timed out and that forward's output is invalid -- it also
+ * holds NaN where the late data was needed), after the work already queued
+ * on `stream`; with `clear` nonzero the word is then reset to 0.  `flags` is
+ * host memory.  Synchronises `stream`: not for the launch path or graph
+ * capture.  MOE_ERR_INVALID on a null or misaligned pointer,
+ * MOE_ERR_WORKSPACE when the workspace is smaller than the head. */
+int moe_fp8_workspace_status(void* workspace, size_t workspace_bytes, int clear, uint32_t* flags,
+                             hipStream_t stream);
+
 /* Bind `bytes` of device memory at `dev_ptr` (256-byte aligned) as the
  * workspace moe_fp8_forward uses on the CURRENT device, and zero its
  * synchronisation words (synchronously).  The library keeps the pointer, not
@@ -193,7 +204,9 @@ typedef struct {
  * moe_fp8_forward would. */
 int moe_fp8_workspace_layout(int M, int h, int i, int E, int k, moe_fp8_ws_layout* layout);
 
-/* Step 1 alone (the same kernel the forward runs).
+/* Step 1 alone (the same kernel the forward runs): the routing stage that
+ * opens the Netra Kernel README's MoE prefill pair and the M=1 MoE objects of
+ * the Netra compiler architecture page (scope paragraph).
  *   logits fp32 [M, E] -> topk_ids int32 [M, k] (rank order: descending
  *   logit, ties to the lower expert index), topk_w fp32 [M, k] (softmax
  *   probabilities of the picks renormalised to sum to 1). */
@@ -255,7 +268,9 @@ int moe_mxfp4_forward_ws_prefix(const void* x, const float* router_logits,
                                 void* workspace, size_t workspace_bytes, int n_stages,
                                 hipStream_t stream);
 
-/* Step 2 alone: rows of bf16 [M, K] -> q e4m3 [M, K], s fp32 [M, K/128];
+/* Step 2 alone (the FP8 activation and fp32 activation-scale tensors of the
+ * Netra compiler architecture page, compatibility-engine paragraph):
+ * rows of bf16 [M, K] -> q e4m3 [M, K], s fp32 [M, K/128];
  * s = amax/448 of each 1x128 group, q = E4M3(x / s), all-zero groups give
  * s = 0 and zero codes.  K % 128 == 0. */
 int moe_fp8_act_quant(const void* x, int M, int K, uint8_t* q, float* s,
@@ -279,7 +294,9 @@ int moe_fp8_act_quant(const void* x, int M, int K, uint8_t* q, float* s,
 int moe_fp8_rmsnorm_act_quant(const void* x, const float* gamma, float eps, int M, int h,
                               void* y, uint8_t* q, float* s, hipStream_t stream);
 
-/* Step 3 alone: topk_ids int32 [M*k] with values in [0, E) ->
+/* Step 3 alone (the routing metadata the Netra Kernel README's MoE prefill
+ * producer emits for its route reducer; the activation packing of the kernel
+ * laboratory README's MoE entry): topk_ids int32 [M*k] with values in [0, E) ->
  *   counts int32 [E], offsets int32 [E + 1] (exclusive scan of counts),
  *   sorted_route_ids int32 [M*k] (route ids grouped by expert ascending and
  *   ascending inside each expert).
@@ -294,6 +311,18 @@ int moe_fp8_group(const int32_t* topk_ids, int M, int E, int k,
  * amax/448 per 128x128 block.  N % 128 == 0, K % 128 == 0. */
 int moe_fp8_quantize_weight_block128(const float* w, int64_t batch, int N, int K,
                                      uint8_t* q, float* s, hipStream_t stream);
+
+/* Measurement helpers (not on the forward path; they frame the layer's
+ * timings, Netra Kernel README kernel laboratory, rules: every number says
+ * how it was taken).  moe_fp8_probe_empty enqueues an empty kernel of `grid`
+ * 256-thread workgroups (the cost of a launch by itself in a graph).
+ * moe_fp8_probe_read enqueues one kernel of `grid` workgroups that streams
+ * `bytes` (a multiple of 16) from device memory `src` (16-byte aligned) and
+ * writes 4 * grid words of xor folds to device memory `sink` (the HBM read
+ * rate one launch reaches on that many bytes).  MOE_ERR_INVALID on a null or
+ * misaligned pointer, a ragged size or grid outside [1, 2^20]. */
+int moe_fp8_probe_empty(int grid, hipStream_t stream);
+int moe_fp8_probe_read(const void* src, size_t bytes, int grid, uint32_t* sink, hipStream_t stream);
 
 /* The device E4M3 encoder every kernel uses, applied elementwise:
  * out[j] = E4M3(in[j]) (nearest, ties to even, saturating to +-448). */

@@ -154,3 +154,20 @@ def test_workspace_layout_regions(lib, M, h, i, E, k):
     for a, b in zip(spans, spans[1:]):
         assert a[1] <= b[0], (a, b)
     assert L.total == moe.workspace_bytes(M, h, i, E, k)
+
+
+def test_status_and_probe_argument_checks(lib):
+    """The status reader and the measurement probes reject bad arguments
+    before any HIP call."""
+    flags = ctypes.c_uint32(0)
+    assert lib.moe_fp8_workspace_status(None, 1 << 24, 0, ctypes.byref(flags), None) == -1
+    assert lib.moe_fp8_workspace_status(FAKE, 1 << 24, 0, None, None) == -1
+    assert lib.moe_fp8_workspace_status(ctypes.c_void_p(0x100010), 1 << 24, 0, ctypes.byref(flags), None) == -1
+    assert lib.moe_fp8_workspace_status(FAKE, 1024, 0, ctypes.byref(flags), None) == -3
+    assert lib.moe_fp8_probe_empty(0, None) == -1
+    assert lib.moe_fp8_probe_empty((1 << 20) + 1, None) == -1
+    assert lib.moe_fp8_probe_read(None, 1024, 4, FAKE, None) == -1
+    assert lib.moe_fp8_probe_read(FAKE, 1000, 4, FAKE, None) == -1
+    assert lib.moe_fp8_probe_read(ctypes.c_void_p(0x100008), 1024, 4, FAKE, None) == -1
+    assert lib.moe_fp8_probe_read(FAKE, 1024, 0, FAKE, None) == -1
+    assert lib.moe_fp8_probe_read(FAKE, 0, 4, FAKE, None) == 0
