@@ -38,12 +38,24 @@ def bf16_ulp(v: np.ndarray) -> np.ndarray:
     return 2.0 ** (np.maximum(e, -126) - 7)
 
 
-# The gfx950 FP8 MFMA sums each 128-product block with a precision of about
-# 2^-17 of the block's sum of |products| (measured: up to 7e-6; pinned by
-# test_mfma_block_sum_accuracy), against 2^-24 for the oracle's fp32 sum.  A
-# GPU gate/up value therefore lies within MFMA_REL * sum|terms| of the exact
-# value, which is what the flagging below propagates.
-MFMA_REL = 2e-5
+# Accuracy of a GPU gate/up value.  The method fixes an fp32 accumulation per
+# 128-wide K block with the block scales applied per block, but not the order
+# of the sum inside a block; the matrix cores add a block's 128 exact products
+# in their own order and precision.  Any fp32 summation of n terms, in any
+# order, lies within gamma_{n-1} * sum|terms| of the exact sum (Higham,
+# Accuracy and Stability of Numerical Algorithms, recursive summation bound),
+# gamma_n = n u / (1 - n u), u = 2^-24; the promotion acc += blk * (s_act * s_w)
+# over KB blocks adds the rounding of the scale product, of the scaled block
+# and of the running sum.  mfma_rel(KB) is that bound relative to
+# sum|x_k w_nk| * |scales|; test_mfma_block_sum_accuracy checks that the
+# hardware stays inside it.
+def gamma(n: int) -> float:
+    u = 2.0 ** -24
+    return n * u / (1.0 - n * u)
+
+
+def mfma_rel(KB: int) -> float:
+    return gamma(127) + gamma(KB + 3)
 
 
 def _T64():
@@ -79,7 +91,7 @@ def gate_up_terms(layer, inter) -> np.ndarray:
     return mag
 
 
-def flagged_codes(layer, inter, rel=MFMA_REL, terms=None):
+def flagged_codes(layer, inter, rel=None, terms=None):
     """(lo, hi, s) for every requantised value [R, i]: the E4M3 codes at the two
     ends of the interval the quotient v / s can reach when each gate/up value
     is off by at most rel * sum|terms| (propagated through SiLU(gate) * up and
@@ -88,6 +100,8 @@ def flagged_codes(layer, inter, rel=MFMA_REL, terms=None):
     result of the method."""
     g = inter["g"].astype(np.float64)
     i = g.shape[1] // 2
+    if rel is None:
+        rel = mfma_rel(inter["xs"].shape[1])
     dg = rel * (gate_up_terms(layer, inter) if terms is None else terms)
     a, u = g[:, :i], g[:, i:]
     da, du = dg[:, :i], dg[:, i:]
@@ -109,8 +123,9 @@ def flagged_codes(layer, inter, rel=MFMA_REL, terms=None):
 def flip_allowance(layer, inter, terms=None, w2_dense=None) -> np.ndarray:
     """Largest change of the output [M, h] that the flagged requantisation
     decisions can cause: the gap between the two codes times the scale, times
-    |w2 column|, times the routing weight.  `terms` and `w2_dense(e)` (float64
-    [h, i]) replace the FP8 layer's own for another weight format."""
+    |w2 column|, times the routing weight (routes taken expert by expert).
+    `terms` and `w2_dense(e)` (float64 [h, i]) replace the FP8 layer's own for
+    another weight format."""
     T = _T64()
     lo, hi, s = flagged_codes(layer, inter, terms=terms)
     step = np.abs(T[hi] - T[lo]) * s                # [R, i], 0 where clear
@@ -118,14 +133,16 @@ def flip_allowance(layer, inter, terms=None, w2_dense=None) -> np.ndarray:
     M, k = ids.shape
     h = layer.q2.shape[1]
     allow = np.zeros((M, h))
-    for p in np.nonzero(step.any(axis=1))[0]:
-        t, r = divmod(int(p), k)
-        e = ids[t, r]
+    flat = ids.ravel()
+    live = np.nonzero(step.any(axis=1))[0]
+    for e in np.unique(flat[live]):
+        P = live[flat[live] == e]
         if w2_dense is not None:
             W2 = w2_dense(e)
         else:
             W2 = T[layer.q2[e]] * np.repeat(np.repeat(layer.s2[e].astype(np.float64), 128, 0), 128, 1)
-        allow[t] += abs(tw[t, r]) * (np.abs(W2) @ step[p])
+        contrib = (step[P] @ np.abs(W2).T) * np.abs(tw.ravel()[P])[:, None]   # [nP, h]
+        np.add.at(allow, P // k, contrib)
     return allow
 
 
