@@ -77,6 +77,7 @@ _SIGS = {
     "moe_fp8_workspace_head_bytes": (_SZ, []),
     "moe_fp8_workspace_status": (_I, [_P, _SZ, _I, ctypes.POINTER(ctypes.c_uint32), _P]),
     "moe_fp8_probe_empty": (_I, [_I, _P]),
+    "moe_fp8_forward_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "moe_fp8_probe_read": (_I, [_P, _SZ, _I, _P, _P]),
 }
 
@@ -232,6 +233,21 @@ def moe_fp8_forward_ws(x, router_logits, w13, s13, w2, s2, k: int, workspace, ou
                                   _ptr(s2), _ptr(out), M, h, i, E, int(k), _ptr(workspace),
                                   workspace.numel(), _stream(stream))
     _check(rc, "moe_fp8_forward_ws")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def moe_fp8_forward_noalloc(x, router_logits, w13, s13, w2, s2, k: int, out=None, stream=None):
+    """The layer with the library's fixed per-device workspace (no allocation
+    by the library; `out` is allocated here only when not given).  Sizes whose
+    workspace exceeds NOALLOC_SCRATCH_BYTES raise MoeError (MOE_ERR_WORKSPACE);
+    overlapping calls on one device race."""
+    M, h, i, E, out = _layer_args(x, router_logits, w13, s13, w2, s2, k, out)
+    rc = lib().moe_fp8_forward_noalloc(_ptr(x), _ptr(router_logits), _ptr(w13), _ptr(s13), _ptr(w2), _ptr(s2),
+                                       _ptr(out), M, h, i, E, int(k), _stream(stream))
+    _check(rc, "moe_fp8_forward_noalloc")
     return out
 
 

@@ -29,6 +29,15 @@ struct Binding {
 std::mutex g_bind_mu;
 Binding g_bind[kMaxDevices];
 
+// Workspace of moe_fp8_forward_noalloc: one fixed array per device, zero at
+// module load.  Host code never passes `scratch` itself to a kernel (on the
+// host it is only a stand-in for the symbol); it uses the device address
+// looked up once per device below.
+constexpr size_t kScratchBytes = MOE_FP8_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
 // Shape checks shared by every entry point of the layer.
 int check_shape(int M, int h, int i, int E, int k) {
     if (M < 0 || h <= 0 || i <= 0 || E <= 0 || k <= 0) return MOE_ERR_INVALID;
@@ -472,6 +481,43 @@ int moe_fp8_probe_read(const void* src, size_t bytes, int grid, uint32_t* sink, 
         return MOE_ERR_INVALID;
     if (bytes == 0) return MOE_OK;
     return hip_status(moe::launch_probe_read(src, bytes, grid, sink, stream));
+}
+
+int moe_fp8_forward_noalloc(const void* x, const float* router_logits, const void* w13, const float* s13,
+                            const void* w2, const float* s2, void* out, int M, int h, int i, int E, int k,
+                            hipStream_t stream) {
+    const int rc = check_shape(M, h, i, E, k);
+    if (rc != MOE_OK) return rc;
+    if (M == 0) return MOE_OK;
+    if (!x || !router_logits || !w13 || !s13 || !w2 || !s2 || !out) return MOE_ERR_INVALID;
+    Layout L;
+    make_layout(M, h, i, E, k, &L);
+    if (L.pub.total > kScratchBytes) return MOE_ERR_WORKSPACE;   // beyond the fixed array
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+    void* ws = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        if (!g_scratch_ptr[dev]) {
+            // first call on this device (which is current): the array's
+            // device address, checked; its synchronisation head is zero from
+            // the module load and is cleared once more by a fill kernel ahead
+            // of this forward unless the stream is being captured (a
+            // captured clear would rerun on every replay)
+            void* p = nullptr;
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+            hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+            if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return MOE_ERR_HIP;
+            if (cs == hipStreamCaptureStatusNone &&
+                moe::launch_zero_words(static_cast<uint32_t*>(p), moe::kWorkspaceHead / 4, stream) != hipSuccess)
+                return MOE_ERR_HIP;
+            g_scratch_ptr[dev] = p;
+        }
+        ws = g_scratch_ptr[dev];
+    }
+    return run_forward(x, router_logits, w13, s13, w2, s2, out, M, h, i, E, k, ws, kScratchBytes, nullptr, 0,
+                       stream);
 }
 
 int moe_fp8_forward(const void* x, const float* router_logits, const void* w13, const float* s13,

@@ -146,6 +146,27 @@ int moe_fp8_forward_ws(const void* x, const float* router_logits,
                        void* workspace, size_t workspace_bytes,
                        hipStream_t stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the layer of
+ * moe_fp8_forward_ws with its workspace in a fixed device array of
+ * MOE_FP8_NOALLOC_SCRATCH_BYTES that the library holds on every device it
+ * runs on until the process ends (zero when the module loads; the forwards
+ * keep its synchronisation words consistent from then on).  The caller passes
+ * only inputs and outputs, as for moe_fp8_forward.  Nothing is allocated:
+ * the first call on a device looks up the array's address there.  Sizes whose
+ * workspace (moe_fp8_workspace_bytes) exceeds the array -- the large-batch
+ * prefill path, for one -- return MOE_ERR_WORKSPACE and enqueue nothing; the
+ * caller then uses moe_fp8_forward_ws.  Every call on a device shares that
+ * device's array, so calls that overlap on one device (other streams, other
+ * threads) race: serialise them.  Other arguments, errors and results as
+ * moe_fp8_forward_ws. */
+#define MOE_FP8_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_fp8_forward_noalloc(const void* x, const float* router_logits,
+                            const void* w13, const float* s13,
+                            const void* w2, const float* s2,
+                            void* out, int M, int h, int i, int E, int k,
+                            hipStream_t stream);
+
 /* Measurement variant of moe_fp8_forward_ws: additionally records
  * events[j] on `stream` just before the j-th stage of the forward and
  * events[n] after the last, where n = moe_fp8_forward_kernel_count(...);
