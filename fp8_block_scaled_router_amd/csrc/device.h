@@ -284,6 +284,14 @@ __device__ __forceinline__ v8i load_lines(const uint8_t* __restrict__ row0, size
     const uint4 x1 = *reinterpret_cast<const uint4*>(row0 + (size_t)(r + 8) * stride + chunk_of(r + 8, p) * 16);
     return v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
 }
+// The same tile with nontemporal loads (the weights of a decode forward are
+// read once and need not stay in the caches).
+__device__ __forceinline__ v8i load_lines_nt(const uint8_t* __restrict__ row0, size_t stride, int lane) {
+    const int r = lane >> 3, p = lane & 7;
+    const v4i x0 = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(row0 + (size_t)r * stride + chunk_of(r, p) * 16));
+    const v4i x1 = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(row0 + (size_t)(r + 8) * stride + chunk_of(r + 8, p) * 16));
+    return v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+}
 __device__ __forceinline__ v8i lines_to_frag(const v8i& w, uint8_t* buf, int lane, int col, int kg) {
     *reinterpret_cast<uint4*>(buf + lane * 16) = make_uint4((uint32_t)w[0], (uint32_t)w[1], (uint32_t)w[2], (uint32_t)w[3]);
     *reinterpret_cast<uint4*>(buf + 1024 + lane * 16) = make_uint4((uint32_t)w[4], (uint32_t)w[5], (uint32_t)w[6], (uint32_t)w[7]);

@@ -58,51 +58,63 @@ __device__ __forceinline__ uint32_t readlane_u(uint32_t v, int lane) {
     return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
 }
 
+__device__ __forceinline__ uint32_t row16_min_u(uint32_t v) {
+    v = min(v, dpp_u<kDppQuadXor1>(v));
+    v = min(v, dpp_u<kDppQuadXor2>(v));
+    v = min(v, dpp_u<kDppRowHalfMirror>(v));
+    v = min(v, dpp_u<kDppRowMirror>(v));
+    return v;
+}
+// Unsigned max / min over the wave: DPP inside each row of 16, then the two
+// gfx950 row swaps; every lane gets the result.
+__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
+    v = row16_max_u(v);
+    auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = max(p[0], p[1]);
+    p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return max(p[0], p[1]);
+}
+__device__ __forceinline__ uint32_t wave_min_u(uint32_t v) {
+    v = row16_min_u(v);
+    auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = min(p[0], p[1]);
+    p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return min(p[0], p[1]);
+}
+
 // Router of one token on one wave; lane l holds the logits of experts
-// l + 64j.  Each pick: a DPP max over each 16-lane row, the four row maxima
-// read into scalars, and the lowest expert index holding that key found by
-// ballot (ties go to the lower index, -0 equals +0).  Lane r keeps pick r;
-// the weights exp(l_r - l_0) / sum are summed in rank order.
+// l + 64j as order keys (0 = no expert).  Each pick is branch-free: the wave
+// max of the keys, then the wave min of the expert index among the keys that
+// reach it (ties go to the lower index, -0 equals +0), which is knocked out.
+// Lane r keeps pick r; the weights exp(l_r - l_0) / sum are summed in rank
+// order.
 __device__ __forceinline__ void route_fast(const float lg[4], int E, int k, int* ids_l,
                                            float* w_l, int lane) {
     uint32_t key[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) key[j] = (lane + 64 * j < E) ? float_order_key(lg[j]) : 0u;
-    int my_pick = 0;
-    float my_l = 0.0f, l0 = 0.0f;
+    uint32_t my_pick = 0u, my_key = 0u;
 #pragma unroll 1
     for (int r = 0; r < k; ++r) {
-        uint32_t m = max(max(key[0], key[1]), max(key[2], key[3]));
-        m = row16_max_u(m);
-        const uint32_t smax = max(max(readlane_u(m, 0), readlane_u(m, 16)),
-                                  max(readlane_u(m, 32), readlane_u(m, 48)));
-        int e = E - 1;   // only reached for NaN logits (outside the contract)
-        if (smax != 0u) {
-            const uint64_t b0 = __ballot(key[0] == smax);
-            const uint64_t b1 = __ballot(key[1] == smax);
-            const uint64_t b2 = __ballot(key[2] == smax);
-            const uint64_t b3 = __ballot(key[3] == smax);
-            e = b0 ? __builtin_ctzll(b0)
-              : b1 ? 64 + __builtin_ctzll(b1)
-              : b2 ? 128 + __builtin_ctzll(b2)
-              : b3 ? 192 + __builtin_ctzll(b3) : E - 1;
-        }
+        const uint32_t m = wave_max_u(max(max(key[0], key[1]), max(key[2], key[3])));
+        const uint32_t cand = key[0] == m ? (uint32_t)lane
+                            : key[1] == m ? (uint32_t)(64 + lane)
+                            : key[2] == m ? (uint32_t)(128 + lane)
+                            : key[3] == m ? (uint32_t)(192 + lane) : 0x1FFu;
+        uint32_t e = wave_min_u(cand);
+        e = (m == 0u || e >= (uint32_t)E) ? (uint32_t)(E - 1) : e;   // only for NaN logits (outside the contract)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (lane + 64 * j == e) key[j] = 0u;
-        const float lv = float_from_order_key(smax);
-        if (r == 0) l0 = lv;
-        if (lane == r) {
-            my_pick = e;
-            my_l = lv;
-        }
+        for (int j = 0; j < 4; ++j) key[j] = (uint32_t)(lane + 64 * j) == e ? 0u : key[j];
+        my_pick = lane == r ? e : my_pick;
+        my_key = lane == r ? m : my_key;
     }
-    const float ex = lane < k ? expf(my_l - l0) : 0.0f;
+    const float l0 = float_from_order_key(readlane_u(my_key, 0));
+    const float ex = lane < k ? expf(float_from_order_key(my_key) - l0) : 0.0f;
     float sum = 0.0f;
 #pragma unroll 1
     for (int r = 0; r < k; ++r) sum += __uint_as_float(readlane_u(__float_as_uint(ex), r));
     if (lane < k) {
-        ids_l[lane] = my_pick;
+        ids_l[lane] = (int)my_pick;
         w_l[lane] = ex / sum;
     }
 }
@@ -171,7 +183,7 @@ __device__ __forceinline__ bool read_words(const uint64_t* const (&p)[N], uint32
 
 // LDS carve of one workgroup (all offsets 16-byte aligned).
 struct FusedLds {
-    size_t xq, xs, ids, w, off, act, srt, cnt, misc, sc13, sc2, blk, a2, a2s, y, bounce, total;
+    size_t xq, xs, ids, w, off, act, srt, cnt, misc, sc2, blk, a2, a2s, y, bounce, total;
 };
 
 __host__ __device__ inline size_t r16(size_t v) { return (v + 15) & ~(size_t)15; }
@@ -179,11 +191,11 @@ __host__ __device__ inline size_t r16(size_t v) { return (v + 15) & ~(size_t)15;
 template <int P, int MM>
 __host__ __device__ inline FusedLds fused_lds(int M, int h, int E, int k) {
     constexpr int NT = 128 / P / 16;
-    const int R = M * k, G = h / 128;
+    const int R = M * k;
     FusedLds L;
     size_t o = 0;
     L.xq = o;     o += r16((size_t)M * h);
-    L.xs = o;     o += r16((size_t)M * G * 4);
+    L.xs = o;     o += (size_t)M * kFusedMaxKB * 4;   // one 16-float row per token
     L.ids = o;    o += r16((size_t)R * 4);
     L.w = o;      o += r16((size_t)R * 4);
     L.off = o;    o += r16((size_t)(E + 1) * 4);
@@ -191,7 +203,6 @@ __host__ __device__ inline FusedLds fused_lds(int M, int h, int E, int k) {
     L.srt = o;    o += r16((size_t)R * 4);
     L.cnt = o;    o += r16((size_t)E * 4);
     L.misc = o;   o += 32 * 4;
-    L.sc13 = o;   o += 2 * kFusedMaxKB * 4;
     L.sc2 = o;    o += 16 * 4;
     L.blk = o;    o += (size_t)2 * NT * kFusedMaxKB * 16 * MM * 4;
     L.a2 = o;     o += (size_t)MM * 128;
@@ -224,7 +235,7 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
 
     const FusedLds Lo = fused_lds<P, MM>(M, h, E, k);
     uint8_t* xq_l = smem + Lo.xq;                                   // [M][h]
-    float* xs_l = reinterpret_cast<float*>(smem + Lo.xs);          // [M][G]
+    float* xs_l = reinterpret_cast<float*>(smem + Lo.xs);          // [M][kFusedMaxKB] (G used)
     int* ids_l = reinterpret_cast<int*>(smem + Lo.ids);            // [R]
     float* w_l = reinterpret_cast<float*>(smem + Lo.w);            // [R]
     int* off_l = reinterpret_cast<int*>(smem + Lo.off);            // [E+1]
@@ -232,7 +243,6 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
     int* srt_l = reinterpret_cast<int*>(smem + Lo.srt);            // [R]
     int* cnt_l = reinterpret_cast<int*>(smem + Lo.cnt);            // [E]
     int* misc_l = reinterpret_cast<int*>(smem + Lo.misc);          // [32]
-    float* sc13_l = reinterpret_cast<float*>(smem + Lo.sc13);      // [2][kFusedMaxKB] gate, up
     float* sc2_l = reinterpret_cast<float*>(smem + Lo.sc2);        // [16]
     float* blk_l = reinterpret_cast<float*>(smem + Lo.blk);        // [2NT][kFusedMaxKB][16][MM]
     uint8_t* a2_l = smem + Lo.a2;                                   // [MM][128]
@@ -243,8 +253,6 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
     // ---- phase 0: tag, routing of every token, active experts
     uint32_t epoch = 0u;
     if (tid == 0) epoch = ld_agent(a.sync + kSyncEpoch / 4);
-    uint32_t* bm_l = reinterpret_cast<uint32_t*>(misc_l + 8);   // experts present in the batch
-    if (tid < 8) bm_l[tid] = 0u;
     const int nq = M * G;   // 16-lane rows of activation groups (<= 64)
     const int qbase = wave * 4 + (lane >> 4);
     uint4 xr[4];
@@ -271,16 +279,17 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
     asm volatile("" : "+v"(epoch));   // the count is first needed here
     if (tid == 0) misc_l[3] = (int)(epoch + 1u);
     __syncthreads();
-    for (int p = tid; p < R; p += 256) atomicOr(&bm_l[ids_l[p] >> 5], 1u << (ids_l[p] & 31));
-    __syncthreads();
     if (wave == 0) {
-        int c[4];
+        // experts 4l .. 4l + 3 of lane l present among the R <= 64 routes
+        // (broadcast reads of the ids), then their ascending list by a prefix
+        // sum
+        int c[4] = {0, 0, 0, 0};
+#pragma unroll 4
+        for (int p = 0; p < R; ++p) {
+            const int ep = ids_l[p];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int e = 4 * lane + j;
-            c[j] = e < E ? (int)((bm_l[e >> 5] >> (e & 31)) & 1u) : 0;
-        }
-        const int lact = c[0] + c[1] + c[2] + c[3];
+            for (int j = 0; j < 4; ++j) c[j] |= (ep == 4 * lane + j) ? 1 : 0;
+        }        const int lact = c[0] + c[1] + c[2] + c[3];
         const int iact = wave_scan_incl(lact);
         int arun = iact - lact;
 #pragma unroll
@@ -305,9 +314,9 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
     float sc_v = 0.0f;
     if (has_unit) {
         if (wave == 0) {
-            if (lane < 2 * KB) {
-                const int blk_row = lane < KB ? ib : IB + ib;
-                sc_v = a.s13[((size_t)e * (N13 / 128) + blk_row) * KB + (lane < KB ? lane : lane - KB)];
+            if (lane < 2 * kFusedMaxKB && (lane & (kFusedMaxKB - 1)) < KB) {
+                const int blk_row = lane < kFusedMaxKB ? ib : IB + ib;
+                sc_v = a.s13[((size_t)e * (N13 / 128) + blk_row) * KB + (lane & (kFusedMaxKB - 1))];
             } else if (lane >= 32 && lane - 32 <= (q * drows + drows - 1) / 128 - nb0) {
                 sc_v = a.s2[((size_t)e * (h / 128) + nb0 + lane - 32) * IB + ib];
             }
@@ -320,13 +329,13 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
             const int row = (t2 < NT ? 0 : i) + ib * 128 + q * (128 / P) + (t2 % NT) * 16;
             const uint8_t* base = a.w13 + ((size_t)e * N13 + row) * h;
 #pragma unroll
-            for (int j = 0; j < kKBW; ++j) A[t2][j] = load_lines(base + min(wave + 4 * j, KB - 1) * 128, h, lane);
+            for (int j = 0; j < kKBW; ++j) A[t2][j] = load_lines_nt(base + min(wave + 4 * j, KB - 1) * 128, h, lane);
         }
         if (wave >= kDW0) {
 #pragma unroll
             for (int j = 0; j < NDT; ++j) {
                 const int tt = min(wave - kDW0 + kDWN * j, ndt - 1);
-                D[j] = load_lines(a.w2 + ((size_t)e * h + q * drows + tt * 16) * i + ib * 128, i, lane);
+                D[j] = load_lines_nt(a.w2 + ((size_t)e * h + q * drows + tt * 16) * i + ib * 128, i, lane);
             }
         }
     }
@@ -347,7 +356,7 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
             m = row16_max(m);
             const float sc = m / kE4M3Max;
             *reinterpret_cast<uint2*>(xq_l + t * h + g * 128 + col * 8) = quant8(v, sc);
-            if (col == 0) xs_l[t * G + g] = sc;
+            if (col == 0) xs_l[t * kFusedMaxKB + g] = sc;
         }
     }
     if (wave == 0) {
@@ -392,7 +401,6 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
         }
         // the block scales (the first loads of the batch to arrive)
         if (has_unit) {
-            if (lane < 2 * KB) sc13_l[lane < KB ? lane : kFusedMaxKB + lane - KB] = sc_v;
             if (lane >= 32 && lane < 48) sc2_l[lane - 32] = sc_v;
         }
     }
@@ -426,7 +434,7 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
                     if (valid) {
 #pragma unroll
                         for (int v = 0; v < 4; ++v)
-                            blk_l[((t2 * kFusedMaxKB + kb) * 16 + 4 * kg + v) * MM + col] = blk[v];
+                            blk_l[((t2 * 16 + 4 * kg + v) * MM + col) * kFusedMaxKB + kb] = blk[v];
                     }
                 }
             }
@@ -445,19 +453,28 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
             const int c = min(L / (16 * NT), cntc - 1), r = L % (16 * NT);
             const int tg = r >> 4, rr = r & 15;
             const int p = srt_l[beg + c];
-            const float* xsr = xs_l + (p / k) * G;
+            // this lane's 16 block sums of its gate row and of its up row, and
+            // its token's 16 activation scales: 16-byte LDS reads (entries past
+            // KB or G are dropped below); the weight scales come from lane kb
+            // (gate) and lane 16 + kb (up) of wave 0 by readlane
+            const float4* xsr = reinterpret_cast<const float4*>(xs_l + (p / k) * kFusedMaxKB);
+            const float4* bgr = reinterpret_cast<const float4*>(blk_l + ((tg * 16 + rr) * MM + c) * kFusedMaxKB);
+            const float4* bur = reinterpret_cast<const float4*>(blk_l + (((NT + tg) * 16 + rr) * MM + c) * kFusedMaxKB);
             float xv[kFusedMaxKB], bg[kFusedMaxKB], bu[kFusedMaxKB];
 #pragma unroll
-            for (int kb = 0; kb < kFusedMaxKB; ++kb) {
-                xv[kb] = xsr[kb];   // past G: other LDS words, dropped below
-                bg[kb] = blk_l[((tg * kFusedMaxKB + kb) * 16 + rr) * MM + c];
-                bu[kb] = blk_l[(((NT + tg) * kFusedMaxKB + kb) * 16 + rr) * MM + c];
+            for (int q4 = 0; q4 < kFusedMaxKB / 4; ++q4) {
+                const float4 x4 = xsr[q4], g4 = bgr[q4], u4 = bur[q4];
+                xv[4 * q4] = x4.x; xv[4 * q4 + 1] = x4.y; xv[4 * q4 + 2] = x4.z; xv[4 * q4 + 3] = x4.w;
+                bg[4 * q4] = g4.x; bg[4 * q4 + 1] = g4.y; bg[4 * q4 + 2] = g4.z; bg[4 * q4 + 3] = g4.w;
+                bu[4 * q4] = u4.x; bu[4 * q4 + 1] = u4.y; bu[4 * q4 + 2] = u4.z; bu[4 * q4 + 3] = u4.w;
             }
             float ag = 0.0f, au = 0.0f;
 #pragma unroll
             for (int kb = 0; kb < kFusedMaxKB; ++kb) {
-                const float tg_ = bg[kb] * (xv[kb] * sc13_l[kb]);
-                const float tu_ = bu[kb] * (xv[kb] * sc13_l[kFusedMaxKB + kb]);
+                const float swg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc_v), kb));
+                const float swu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc_v), kFusedMaxKB + kb));
+                const float tg_ = bg[kb] * (xv[kb] * swg);
+                const float tu_ = bu[kb] * (xv[kb] * swu);
                 ag = ag + (kb < KB ? tg_ : -0.0f);   // -0 added leaves any value unchanged
                 au = au + (kb < KB ? tu_ : -0.0f);
             }
@@ -602,7 +619,7 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
         }
         for (int j = tid * 16; j < M * h; j += 256 * 16)
             *reinterpret_cast<uint4*>(a.xq + j) = *reinterpret_cast<const uint4*>(xq_l + j);
-        for (int j = tid; j < M * G; j += 256) a.xs[j] = xs_l[j];
+        for (int j = tid; j < M * G; j += 256) a.xs[j] = xs_l[(j / G) * kFusedMaxKB + j % G];
     }
 
     // ---- exit: the last workgroup advances the forward count

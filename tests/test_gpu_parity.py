@@ -332,6 +332,34 @@ def test_forward_tied_logits_stream_path(dev, moe_mod, M, E, k):
     check_output(to_host_bits(out), ref, allowance=allow)
 
 
+@pytest.mark.parametrize("M,E,k,kind", [(1, 128, 8, "grid"), (2, 128, 8, "grid"), (1, 128, 8, "zeros"),
+                                        (1, 128, 8, "const"), (2, 200, 16, "grid"), (1, 8, 8, "grid")])
+def test_forward_tied_logits_one_kernel_path(dev, moe_mod, M, E, k, kind):
+    """Exact ties through the one-kernel path's router (keys with the expert
+    index below the logit, ranks counted in parallel): logits on a 0.5 grid,
+    a row of mixed -0 / +0, a constant row.  Ids must equal the oracle's
+    (lower expert first on equal logits, -0 equal to +0), weights within
+    1e-6, the output within the flip allowance."""
+    h, i = 256, 128
+    assert moe_mod.workspace_layout(M, h, i, E, k).path == moe_mod.PATH_FUSED_DECODE
+    rng = np.random.default_rng(M * 13 + E + k)
+    if kind == "grid":
+        logits = (rng.integers(-3, 4, (M, E)) * 0.5).astype(np.float32)
+    elif kind == "zeros":
+        logits = np.where(rng.random((M, E)) < 0.5, np.float32(-0.0), np.float32(0.0)).astype(np.float32)
+    else:
+        logits = np.full((M, E), np.float32(-3.5))
+    cfg = synth.LayerConfig(f"m{M}_h{h}_i{i}_e{E}_top{k}", M, h, i, E, k, "normal", "tied logits")
+    L = Layer(cfg, 91 + E + M, dev, logits=logits)
+    log(f"tied-logit one-kernel forward M={M} E={E} k={k} {kind}")
+    out, ws = _run(moe_mod, L)
+    ref, inter = L.oracle(intermediates=True)
+    _check_intermediates(moe_mod, L, ws, inter)
+    allow = flip_allowance(L, inter)
+    r16_report(f"tied1k_m{M}_e{E}_top{k}_{kind}", to_host_bits(out), ref, allow)
+    check_output(to_host_bits(out), ref, allowance=allow)
+
+
 def test_mfma_block_sum_accuracy(dev, moe_mod):
     """The FP8 MFMA block sums: every materialised gate/up value of the
     weight-streaming path lies within mfma_rel(KB) * sum|terms| of the exact
