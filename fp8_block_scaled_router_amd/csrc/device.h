@@ -253,12 +253,15 @@ __device__ __forceinline__ v16f mfma_32x32x64_e4m3(const v8i& a, const v8i& b, c
 
 // Row r of a 16-row fragment holds its 32-byte K group kg as two 16-byte
 // halves: the lower half in slot lo_slot(r, kg), the upper in lo_slot ^ 4.
-// Over the 16 rows the lower halves of one kg cover all 16 slots of a
-// 256-byte bank window (and every 8 consecutive rows all 8 slots of a 128-byte
-// window), so fragment reads are free of bank conflicts; because only the
-// slot, not the order of the two halves, depends on the row, every lane sees
-// its K bytes in the same order.
-__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// A fragment read (lane l: row l % 16, group l / 16) is then free of bank
+// conflicts whether the LDS serves 8, 16 or 32 lanes of a ds_read_b128 at a
+// time: every 8 consecutive rows of one kg fill the 8 slots of a 128-byte
+// window, the 8 rows of one parity fill a 256-byte window, and the rows
+// r, r + 4, r + 8, r + 12 of two adjacent groups fill the 8 slots of their
+// 128-byte quarter of a 512-byte window.  Because only the slot, not the
+// order of the two halves, depends on the row, every lane sees its K bytes
+// in the same order.
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) & 3) | (((r ^ (r >> 3)) & 1) << 2); }
 __device__ __forceinline__ int lo_slot(int r, int kg) {
     const int x = swz(r);
     return (kg ^ (x & 3)) | (x & 4);
