@@ -59,10 +59,13 @@ enum {
 };
 
 /* Forward paths (chosen from the sizes alone, see moe_fp8_workspace_layout):
- * small batches (M <= 16) run the whole layer in one persistent kernel;
- * batches with few routes per expert run weight-streaming GEMMs; batches
- * with many routes per expert (M*k >= 32*E) run tiled MFMA grouped GEMMs
- * with the SiLU requantisation fused into the gate/up epilogue. */
+ * one to four tokens run the whole layer in one kernel whose workgroups are
+ * all resident at once, provided its grid fits 512 workgroups: every unit
+ * (selected expert x 128-column block of the intermediate) is split into 8
+ * or 4 parts (for h 2048, i 768, E 128, top-8 that is M <= 2); other batches
+ * with few routes per expert run weight-streaming GEMMs; batches with many
+ * routes per expert (M*k >= 32*E) run tiled MFMA grouped GEMMs with the SiLU
+ * requantisation fused into the gate/up epilogue. */
 #define MOE_FP8_PATH_STREAM 0
 #define MOE_FP8_PATH_PREFILL 1
 #define MOE_FP8_PATH_FUSED_DECODE 2
