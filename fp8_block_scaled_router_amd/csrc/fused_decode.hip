@@ -303,9 +303,9 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
     const bool has_unit = u < U;
     const int e = has_unit ? act_l[u] : 0;
 
-    // ---- every weight byte of the part requested now: block scales first,
-    // then w13 (the gate/up tiles, this wave's K blocks kb = wave + 4j), then
-    // w2 (this wave's 16-row down tiles), each tile as whole 128-byte lines.
+    // ---- the part's gate/up weights requested now: block scales first, then
+    // w13 (the gate/up tiles, this wave's K blocks kb = wave + 4j), each tile
+    // as whole 128-byte lines (w2 follows after the gate/up MFMAs).
     // Nothing from phase 0 is still in flight; saying so keeps the compiler
     // from draining these loads at the waits below.
     wait_vmem();
@@ -330,13 +330,6 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
             const uint8_t* base = a.w13 + ((size_t)e * N13 + row) * h;
 #pragma unroll
             for (int j = 0; j < kKBW; ++j) A[t2][j] = load_lines_nt(base + min(wave + 4 * j, KB - 1) * 128, h, lane);
-        }
-        if (wave >= kDW0) {
-#pragma unroll
-            for (int j = 0; j < NDT; ++j) {
-                const int tt = min(wave - kDW0 + kDWN * j, ndt - 1);
-                D[j] = load_lines_nt(a.w2 + ((size_t)e * h + q * drows + tt * 16) * i + ib * 128, i, lane);
-            }
         }
     }
 
@@ -439,6 +432,18 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
                 }
             }
         }
+        // w2 (this wave's 16-row down tiles) is requested only now: the w13
+        // requests of every workgroup go out first, so the gate/up inputs of
+        // the whole layer arrive about a third of the stream earlier, and the
+        // w2 stream overlaps the exchange of the SiLU-mul values, which the
+        // down MFMAs wait for anyway.
+        if (wave >= kDW0) {
+#pragma unroll
+            for (int j = 0; j < NDT; ++j) {
+                const int tt = min(wave - kDW0 + kDWN * j, ndt - 1);
+                D[j] = load_lines_nt(a.w2 + ((size_t)e * h + q * drows + tt * 16) * i + ib * 128, i, lane);
+            }
+        }
     }
     __syncthreads();
 
@@ -518,6 +523,17 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
             }
         }
     }
+    // Waves that hold w2 tiles but have no exchange work (all but wave 0)
+    // turn their tiles into MFMA fragments while wave 0 waits for the unit's
+    // other parts, so that after the barrier only the MFMAs remain.
+    const bool frag_early = wave > 0;
+    if (has_unit && wave >= kDW0 && frag_early) {
+#pragma unroll
+        for (int j = 0; j < NDT; ++j) {
+            const int tt = wave - kDW0 + kDWN * j;
+            if (tt < ndt) D[j] = lines_to_frag(D[j], bounce + (j & 1) * 2048, lane, col, kg);
+        }
+    }
     __syncthreads();
 
     // ---- down: this part's rows times the unit's K block, published as block
@@ -532,7 +548,8 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
             const int tt = wave - kDW0 + kDWN * j;
             if (tt < ndt) {
                 const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
-                const v4f blk = mfma_16x16x128_e4m3(lines_to_frag(D[j], bounce + (j & 1) * 2048, lane, col, kg), B, z);
+                const v8i Af = frag_early ? D[j] : lines_to_frag(D[j], bounce + (j & 1) * 2048, lane, col, kg);
+                const v4f blk = mfma_16x16x128_e4m3(Af, B, z);
                 const int n0 = q * drows + tt * 16;
                 const float sc = a2sv * sc2_l[n0 / 128 - nb0];
                 if (valid) {
