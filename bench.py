@@ -117,9 +117,14 @@ def pmc_mean_kb(folder, name_prefix, largest_grid=False):
     import csv
     import glob
     rows = []
+    # name_prefix ends in "(": also take template instances ("name<8, 1>(...)")
+    # and names that carry a "void " return type
+    stem = name_prefix[:-1] if name_prefix.endswith("(") else None
     for path in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
         for r in csv.DictReader(open(path)):
-            if r["Kernel_Name"].startswith(name_prefix):
+            n = r["Kernel_Name"]
+            n = n[5:] if n.startswith("void ") else n
+            if n.startswith(name_prefix) or (stem is not None and n.startswith(stem + "<")):
                 rows.append((int(r["Grid_Size"]), float(r["Counter_Value"])))
     if not rows:
         raise SystemExit(f"no dispatch of {name_prefix} in {folder}")
