@@ -14,10 +14,11 @@
 // Because the SiLU-mul requantisation groups are exactly the 128-column
 // blocks of the intermediate (the 1x128 activation quantisation of the down
 // GEMM's input), a unit's down-partial needs only the unit's own gate/up
-// columns.  So as soon as a workgroup knows its expert it requests every
-// weight byte it will ever use (w13 first, then w2) into registers: the whole
-// selected-expert stream of the forward is in flight at once, and no
-// workgroup waits for another before its weights arrive.
+// columns.  So as soon as a workgroup knows its expert it requests its w13
+// rows into registers, and its w2 rows right after its gate/up MFMAs: the
+// w13 requests of the whole layer go out first, the w2 stream overlaps the
+// exchange of the SiLU-mul values, and no workgroup waits for another before
+// its weights arrive.
 //
 // Exchanges between workgroups (each value one 64-bit word: value | tag of
 // this forward, written and read with agent-scope relaxed atomics; the data
