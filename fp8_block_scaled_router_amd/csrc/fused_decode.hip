@@ -88,36 +88,55 @@ __device__ __forceinline__ uint32_t wave_min_u(uint32_t v) {
 // max of the keys, then the wave min of the expert index among the keys that
 // reach it (ties go to the lower index, -0 equals +0), which is knocked out.
 // Lane r keeps pick r; the weights exp(l_r - l_0) / sum are summed in rank
-// order.
-__device__ __forceinline__ void route_fast(const float lg[4], int E, int k, int* ids_l,
-                                           float* w_l, int lane) {
+// order.  route_rounds(s, r0, r1) makes picks r0 .. r1 - 1, so a caller can
+// act on the first picks before making the rest.
+struct RouteState {
     uint32_t key[4];
+    uint32_t pick, pkey;   // lane r: pick r and its key
+};
+
+__device__ __forceinline__ void route_begin(RouteState& s, const float lg[4], int E, int lane) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) key[j] = (lane + 64 * j < E) ? float_order_key(lg[j]) : 0u;
-    uint32_t my_pick = 0u, my_key = 0u;
+    for (int j = 0; j < 4; ++j) s.key[j] = (lane + 64 * j < E) ? float_order_key(lg[j]) : 0u;
+    s.pick = 0u;
+    s.pkey = 0u;
+}
+
+__device__ __forceinline__ void route_rounds(RouteState& s, int r0, int r1, int E, int lane) {
 #pragma unroll 1
-    for (int r = 0; r < k; ++r) {
-        const uint32_t m = wave_max_u(max(max(key[0], key[1]), max(key[2], key[3])));
-        const uint32_t cand = key[0] == m ? (uint32_t)lane
-                            : key[1] == m ? (uint32_t)(64 + lane)
-                            : key[2] == m ? (uint32_t)(128 + lane)
-                            : key[3] == m ? (uint32_t)(192 + lane) : 0x1FFu;
+    for (int r = r0; r < r1; ++r) {
+        const uint32_t m = wave_max_u(max(max(s.key[0], s.key[1]), max(s.key[2], s.key[3])));
+        const uint32_t cand = s.key[0] == m ? (uint32_t)lane
+                            : s.key[1] == m ? (uint32_t)(64 + lane)
+                            : s.key[2] == m ? (uint32_t)(128 + lane)
+                            : s.key[3] == m ? (uint32_t)(192 + lane) : 0x1FFu;
         uint32_t e = wave_min_u(cand);
         e = (m == 0u || e >= (uint32_t)E) ? (uint32_t)(E - 1) : e;   // only for NaN logits (outside the contract)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) key[j] = (uint32_t)(lane + 64 * j) == e ? 0u : key[j];
-        my_pick = lane == r ? e : my_pick;
-        my_key = lane == r ? m : my_key;
+        for (int j = 0; j < 4; ++j) s.key[j] = (uint32_t)(lane + 64 * j) == e ? 0u : s.key[j];
+        s.pick = lane == r ? e : s.pick;
+        s.pkey = lane == r ? m : s.pkey;
     }
-    const float l0 = float_from_order_key(readlane_u(my_key, 0));
-    const float ex = lane < k ? expf(float_from_order_key(my_key) - l0) : 0.0f;
+}
+
+__device__ __forceinline__ void route_end(const RouteState& s, int k, int* ids_l, float* w_l, int lane) {
+    const float l0 = float_from_order_key(readlane_u(s.pkey, 0));
+    const float ex = lane < k ? expf(float_from_order_key(s.pkey) - l0) : 0.0f;
     float sum = 0.0f;
 #pragma unroll 1
     for (int r = 0; r < k; ++r) sum += __uint_as_float(readlane_u(__float_as_uint(ex), r));
     if (lane < k) {
-        ids_l[lane] = (int)my_pick;
+        ids_l[lane] = (int)s.pick;
         w_l[lane] = ex / sum;
     }
+}
+
+__device__ __forceinline__ void route_fast(const float lg[4], int E, int k, int* ids_l,
+                                           float* w_l, int lane) {
+    RouteState s;
+    route_begin(s, lg, E, lane);
+    route_rounds(s, 0, k, E, lane);
+    route_end(s, k, ids_l, w_l, lane);
 }
 
 // Lanes holding the same expert id (9-bit ids; 0x1FF = no route).
@@ -251,6 +270,33 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
     float* y_l = reinterpret_cast<float*>(smem + Lo.y);            // [16][64]
     uint8_t* bounce = smem + Lo.bounce + wave * 4096;               // [2][2048] per wave
 
+    // The part's gate/up weights: block scales first, then w13 (the gate/up
+    // tiles, this wave's K blocks kb = wave + 4j), each tile as whole 128-byte
+    // lines (w2 follows after the gate/up MFMAs).  Unconditional loads (a K
+    // block or tile past the end re-reads the last one and is not used): a
+    // conditionally loaded register would be copied into place after its
+    // load, which makes the wave wait for it.
+    v8i A[2 * NT][kKBW];
+    v8i D[NDT];
+    float sc_v = 0.0f;
+    auto issue_w13 = [&](int ex) {
+        if (wave == 0) {
+            if (lane < 2 * kFusedMaxKB && (lane & (kFusedMaxKB - 1)) < KB) {
+                const int blk_row = lane < kFusedMaxKB ? ib : IB + ib;
+                sc_v = a.s13[((size_t)ex * (N13 / 128) + blk_row) * KB + (lane & (kFusedMaxKB - 1))];
+            } else if (lane >= 32 && lane - 32 <= (q * drows + drows - 1) / 128 - nb0) {
+                sc_v = a.s2[((size_t)ex * (h / 128) + nb0 + lane - 32) * IB + ib];
+            }
+        }
+#pragma unroll
+        for (int t2 = 0; t2 < 2 * NT; ++t2) {
+            const int row = (t2 < NT ? 0 : i) + ib * 128 + q * (128 / P) + (t2 % NT) * 16;
+            const uint8_t* base = a.w13 + ((size_t)ex * N13 + row) * h;
+#pragma unroll
+            for (int j = 0; j < kKBW; ++j) A[t2][j] = load_lines_nt(base + min(wave + 4 * j, KB - 1) * 128, h, lane);
+        }
+    };
+
     // ---- phase 0: tag, routing of every token, active experts
     uint32_t epoch = 0u;
     if (tid == 0) epoch = ld_agent(a.sync + kSyncEpoch / 4);
@@ -271,11 +317,30 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
             lg[j] = (t < M && e < E) ? a.logits[(size_t)t * E + e] : 0.0f;
         }
     };
-    l_load(wave);
+    int e_rank = 0;
+    if constexpr (MM == 1) {
+        // One token: with the active experts numbered in rank order, unit u
+        // needs only picks 0 .. u to know its expert.  Every wave routes the
+        // token, requests its weights right after pick u and makes the
+        // remaining picks while they stream, so the lower ranks' weights go
+        // out before the whole top-k is known.
+        l_load(0);
+        RouteState rs;
+        route_begin(rs, lg, E, lane);
+        const int ur = min(u, k - 1);
+        route_rounds(rs, 0, ur + 1, E, lane);
+        e_rank = (int)readlane_u(rs.pick, ur);
+        wait_vmem();   // the token's logits and activation rows are in
+        issue_w13(e_rank);
+        route_rounds(rs, ur + 1, k, E, lane);
+        if (wave == 0) route_end(rs, k, ids_l, w_l, lane);
+    } else {
+        l_load(wave);
 #pragma unroll 1
-    for (int t = wave; t < M; t += 4) {
-        if (t != wave) l_load(t);
-        route_fast(lg, E, k, ids_l + t * k, w_l + t * k, lane);
+        for (int t = wave; t < M; t += 4) {
+            if (t != wave) l_load(t);
+            route_fast(lg, E, k, ids_l + t * k, w_l + t * k, lane);
+        }
     }
     asm volatile("" : "+v"(epoch));   // the count is first needed here
     if (tid == 0) misc_l[3] = (int)(epoch + 1u);
@@ -302,36 +367,17 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
     const int U = misc_l[0];
     const uint32_t tag = (uint32_t)misc_l[3];
     const bool has_unit = u < U;
-    const int e = has_unit ? act_l[u] : 0;
+    // the unit's expert: the u-th of the active experts in ascending order,
+    // or for one token the u-th pick
+    const int e = has_unit ? (MM == 1 ? e_rank : act_l[u]) : 0;
 
-    // ---- the part's gate/up weights requested now: block scales first, then
-    // w13 (the gate/up tiles, this wave's K blocks kb = wave + 4j), each tile
-    // as whole 128-byte lines (w2 follows after the gate/up MFMAs).
-    // Nothing from phase 0 is still in flight; saying so keeps the compiler
-    // from draining these loads at the waits below.
-    wait_vmem();
-    v8i A[2 * NT][kKBW];
-    v8i D[NDT];
-    float sc_v = 0.0f;
-    if (has_unit) {
-        if (wave == 0) {
-            if (lane < 2 * kFusedMaxKB && (lane & (kFusedMaxKB - 1)) < KB) {
-                const int blk_row = lane < kFusedMaxKB ? ib : IB + ib;
-                sc_v = a.s13[((size_t)e * (N13 / 128) + blk_row) * KB + (lane & (kFusedMaxKB - 1))];
-            } else if (lane >= 32 && lane - 32 <= (q * drows + drows - 1) / 128 - nb0) {
-                sc_v = a.s2[((size_t)e * (h / 128) + nb0 + lane - 32) * IB + ib];
-            }
-        }
-        // Unconditional loads (a K block or tile past the end re-reads the last
-        // one and is not used): a conditionally loaded register would be
-        // copied into place after its load, which makes the wave wait for it.
-#pragma unroll
-        for (int t2 = 0; t2 < 2 * NT; ++t2) {
-            const int row = (t2 < NT ? 0 : i) + ib * 128 + q * (128 / P) + (t2 % NT) * 16;
-            const uint8_t* base = a.w13 + ((size_t)e * N13 + row) * h;
-#pragma unroll
-            for (int j = 0; j < kKBW; ++j) A[t2][j] = load_lines_nt(base + min(wave + 4 * j, KB - 1) * 128, h, lane);
-        }
+    // ---- the part's gate/up weights requested now (one token: already
+    // requested during the routing, see phase 0)
+    if constexpr (MM != 1) {
+        // Nothing from phase 0 is still in flight; saying so keeps the
+        // compiler from draining these loads at the waits below.
+        wait_vmem();
+        if (has_unit) issue_w13(e);
     }
 
     // ---- activation codes of every token into LDS (while the weights
