@@ -479,20 +479,21 @@ __global__ __launch_bounds__(256) void fused_decode_kernel(FusedArgs a) {
                 }
             }
         }
-        // w2 (this wave's 16-row down tiles) is requested only now: the w13
-        // requests of every workgroup go out first, so the gate/up inputs of
-        // the whole layer arrive about a third of the stream earlier, and the
-        // w2 stream overlaps the exchange of the SiLU-mul values, which the
-        // down MFMAs wait for anyway.
-        if (wave >= kDW0) {
-#pragma unroll
-            for (int j = 0; j < NDT; ++j) {
-                const int tt = min(wave - kDW0 + kDWN * j, ndt - 1);
-                D[j] = load_lines_nt(a.w2 + ((size_t)e * h + q * drows + tt * 16) * i + ib * 128, i, lane);
-            }
-        }
     }
     __syncthreads();
+    // w2 (this wave's 16-row down tiles) is requested only now: the w13
+    // requests of every workgroup go out first, so the gate/up inputs of the
+    // whole layer arrive about a third of the stream earlier, and the w2
+    // stream overlaps the exchange of the SiLU-mul values, which the down
+    // MFMAs wait for anyway.  After the barrier, so that a wave held up
+    // issuing them does not hold up wave 0's promotion.
+    if (has_unit && wave >= kDW0) {
+#pragma unroll
+        for (int j = 0; j < NDT; ++j) {
+            const int tt = min(wave - kDW0 + kDWN * j, ndt - 1);
+            D[j] = load_lines_nt(a.w2 + ((size_t)e * h + q * drows + tt * 16) * i + ib * 128, i, lane);
+        }
+    }
 
     // ---- block promotion in K order: acc += blk * (s_act * s_w), the scale
     // product rounded first, then SiLU(gate) * up, published for the unit's
