@@ -58,6 +58,7 @@ _SIGS = {
     "moe_fp8_forward": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "moe_fp8_forward_ws": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _SZ, _P]),
     "moe_fp8_workspace_layout": (_I, [_I, _I, _I, _I, _I, ctypes.POINTER(WsLayout)]),
+    "moe_mxfp4_workspace_layout": (_I, [_I, _I, _I, _I, _I, ctypes.POINTER(WsLayout)]),
     "router_topk": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "moe_fp8_router_gemm_topk": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P]),
     "moe_mxfp4_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
@@ -73,6 +74,8 @@ _SIGS = {
     "moe_fp8_forward_ws_prefix": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _SZ, _I, _P]),
     "moe_fp8_forward_kernel_count": (_I, [_I, _I, _I, _I, _I]),
     "moe_fp8_forward_kernel_name": (ctypes.c_char_p, [_I, _I, _I, _I, _I, _I]),
+    "moe_mxfp4_forward_kernel_count": (_I, [_I, _I, _I, _I, _I]),
+    "moe_mxfp4_forward_kernel_name": (ctypes.c_char_p, [_I, _I, _I, _I, _I, _I]),
     "moe_fp8_workspace_init": (_I, [_P, _SZ, _P]),
     "moe_fp8_workspace_head_bytes": (_SZ, []),
     "moe_fp8_workspace_status": (_I, [_P, _SZ, _I, ctypes.POINTER(ctypes.c_uint32), _P]),
@@ -264,6 +267,12 @@ def mxfp4_workspace_bytes(M: int, h: int, i: int, E: int, k: int) -> int:
     return int(lib().moe_mxfp4_workspace_bytes(M, h, i, E, k))
 
 
+def mxfp4_workspace_layout(M: int, h: int, i: int, E: int, k: int) -> WsLayout:
+    L = WsLayout()
+    _check(lib().moe_mxfp4_workspace_layout(M, h, i, E, k, ctypes.byref(L)), "moe_mxfp4_workspace_layout")
+    return L
+
+
 def alloc_mxfp4_workspace(M: int, h: int, i: int, E: int, k: int, device=None) -> torch.Tensor:
     """A workspace for moe_mxfp4_forward_ws with its head cleared."""
     n = mxfp4_workspace_bytes(M, h, i, E, k)
@@ -274,10 +283,12 @@ def alloc_mxfp4_workspace(M: int, h: int, i: int, E: int, k: int, device=None) -
     return ws
 
 
-def moe_mxfp4_stage_names(M: int, k: int) -> list:
+def moe_mxfp4_stage_names(M: int, h: int, i: int, E: int, k: int) -> list:
     """Kernels of one MXFP4 forward in launch order (the prefix stages)."""
-    head = ["route_quant_group_kernel"] if M * k <= 256 else ["route_quant_kernel", "group_hist+group_scatter"]
-    return head + ["stream_gate_up_mx_kernel", "stream_down_mx_kernel", "combine_kernel"]
+    n = lib().moe_mxfp4_forward_kernel_count(M, h, i, E, k)
+    if n < 0:
+        raise MoeError(n, "moe_mxfp4_forward_kernel_count")
+    return [lib().moe_mxfp4_forward_kernel_name(M, h, i, E, k, j).decode() for j in range(n)]
 
 
 def moe_mxfp4_forward_ws(x, router_logits, w13, e13, w2, e2, k: int, workspace, out=None, stream=None,

@@ -244,6 +244,17 @@ __device__ __forceinline__ v4f mfma_16x16x128_e4m3(const v8i& a, const v8i& b, c
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// The same instruction with an MXFP4 A operand: lane l (row l % 16, group
+// g = l / 16) supplies 32 E2M1 codes (K elements 32 g .. 32 g + 31, element
+// 2j in the low nibble of byte j) and their one E8M0 scale scale_a; B is the
+// E4M3 operand in the layout the instruction takes for FP8 (lane group g
+// holds K elements 16 g .. 16 g + 15 and 64 + 16 g .. 64 + 16 g + 15) with
+// its scale fixed at 1 (E8M0 127).
+__device__ __forceinline__ v4f mfma_16x16x128_fp4_e4m3(const uint4& a, const v8i& b, int scale_a, const v4f& c) {
+    const v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, b, c, 4, 0, 0, scale_a, 0, 127);
+}
+
 // D = A(32x64) * B(64x32) + C, e4m3.  Lane l supplies row/column l % 32 and
 // K slot group l / 32 (32 bytes); result lane l holds column l % 32, rows
 // 8 * (v / 4) + 4 * (l / 32) + (v % 4) for v = 0..15.

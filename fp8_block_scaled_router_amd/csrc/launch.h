@@ -62,10 +62,12 @@ hipError_t launch_stream_down_mx(const StreamArgs& a, const float* g, const uint
 struct PrefillArgs {
     const uint8_t* xq;
     const float* xs;
-    const uint8_t* w13;
-    const float* s13;
-    const uint8_t* w2;
+    const uint8_t* w13;         // FP8 [E][2i][h], or MXFP4 codes [E][2i][h/2]
+    const float* s13;           // FP8: 128x128 block scales
+    const uint8_t* e13;         // MXFP4: E8M0 scales [E][2i][h/32]
+    const uint8_t* w2;          // FP8 [E][h][i], or MXFP4 codes [E][h][i/2]
     const float* s2;
+    const uint8_t* e2;          // MXFP4: [E][h][i/32]
     const int32_t* offsets;
     const int32_t* sorted;
     const int32_t* mtile_off;   // [E + 1] first M-tile of each expert
@@ -76,8 +78,9 @@ struct PrefillArgs {
 };
 int prefill_tile_m();
 bool prefill_supported(int M, int h, int i, int k);
-hipError_t launch_prefill_gate_up(const PrefillArgs& a, int R, hipStream_t stream);
-hipError_t launch_prefill_down(const PrefillArgs& a, int R, hipStream_t stream);
+// mx: MXFP4 weights (w13 / w2 with e13 / e2), else FP8 (with s13 / s2).
+hipError_t launch_prefill_gate_up(const PrefillArgs& a, bool mx, hipStream_t stream);
+hipError_t launch_prefill_down(const PrefillArgs& a, bool mx, hipStream_t stream);
 
 // Fixed-order combine of the k route partials of each token into bf16.
 hipError_t launch_combine(const float* y, const float* tw, int M, int k, int h, uint16_t* out,

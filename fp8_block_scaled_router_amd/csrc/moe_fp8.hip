@@ -57,14 +57,32 @@ struct Layout {
 // The one-kernel decode path takes every batch it supports: its grid (one
 // workgroup per eighth or quarter of an (expert, 128-column intermediate
 // block) unit, for every expert the batch could select) must be resident at
-// once, which limits it to one or two tokens at the layer shapes.
+// once, which limits it to one or two tokens at the layer shapes.  Above it,
+// the tiled kernels take over from the weight-streaming ones at 8 routes per
+// expert on average: the streaming kernels read each weight tile once per 16
+// routes of its expert, and at h 2048 / 6144, i 768, E 128 the two cost the
+// same between 4 and 8 routes per expert (measured).
+constexpr int kTiledRoutesPerExpert = 8;
+// MXFP4 weights halve the bytes the streaming kernels read per pass, which
+// moves the crossover to between 8 and 16 routes per expert (measured at the
+// same shapes).
+constexpr int kTiledRoutesPerExpertMx = 12;
+
 int choose_path(int M, int h, int i, int E, int k) {
     if (moe::fused_supported(M, h, i, E, k)) return MOE_FP8_PATH_FUSED_DECODE;
-    if ((int64_t)M * k >= (int64_t)32 * E && moe::prefill_supported(M, h, i, k)) return MOE_FP8_PATH_PREFILL;
+    if ((int64_t)M * k >= (int64_t)kTiledRoutesPerExpert * E && moe::prefill_supported(M, h, i, k))
+        return MOE_FP8_PATH_PREFILL;
     return MOE_FP8_PATH_STREAM;
 }
 
-void make_layout(int M, int h, int i, int E, int k, Layout* L, bool stream_only = false) {
+// The MXFP4 layer has no one-kernel path.
+int choose_path_mx(int M, int h, int i, int E, int k) {
+    if ((int64_t)M * k >= (int64_t)kTiledRoutesPerExpertMx * E && moe::prefill_supported(M, h, i, k))
+        return MOE_FP8_PATH_PREFILL;
+    return MOE_FP8_PATH_STREAM;
+}
+
+void make_layout(int M, int h, int i, int E, int k, Layout* L, bool mx = false) {
     const size_t R = (size_t)M * k;
     size_t cur = moe::kWorkspaceHead;   // synchronisation words and exchange region first
     auto take = [&](size_t bytes) {
@@ -84,7 +102,7 @@ void make_layout(int M, int h, int i, int E, int k, Layout* L, bool stream_only 
     p.active = take((size_t)E * 4);
     p.num_active = take(4);
     L->hist = take((size_t)moe::group_chunks((int)R) * E * 4);
-    p.path = stream_only ? MOE_FP8_PATH_STREAM : choose_path(M, h, i, E, k);
+    p.path = mx ? choose_path_mx(M, h, i, E, k) : choose_path(M, h, i, E, k);
     L->mtile_off = take((size_t)(E + 1) * 4);
     p.gate_up = (size_t)-1;
     p.act2 = (size_t)-1;
@@ -118,6 +136,14 @@ const char* const kFusedStages[] = {"fused_decode_kernel"};
 const char* const kPrefillStages[] = {"route_quant_kernel", "group_hist+group_scatter",
                                       "prefill_gate_up_kernel", "prefill_down_kernel",
                                       "combine_bf16_kernel"};
+const char* const kStreamMxStages[] = {"route_quant_kernel", "group_hist+group_scatter",
+                                       "stream_gate_up_mx_kernel", "stream_down_mx_kernel",
+                                       "combine_kernel"};
+const char* const kStreamSmallMxStages[] = {"route_quant_group_kernel", "stream_gate_up_mx_kernel",
+                                            "stream_down_mx_kernel", "combine_kernel"};
+const char* const kPrefillMxStages[] = {"route_quant_kernel", "group_hist+group_scatter",
+                                        "prefill_gate_up_mx_kernel", "prefill_down_mx_kernel",
+                                        "combine_bf16_kernel"};
 
 // The streaming path routes, quantises and groups in one launch when the
 // batch has few enough routes.
@@ -133,6 +159,11 @@ const char* stage_name(int path, int M, int k, int j) {
     if (path == MOE_FP8_PATH_PREFILL) return kPrefillStages[j];
     if (small_group(M, k)) return kStreamSmallStages[j];
     return kStreamStages[j];
+}
+const char* stage_name_mx(int path, int M, int k, int j) {
+    if (path == MOE_FP8_PATH_PREFILL) return kPrefillMxStages[j];
+    if (small_group(M, k)) return kStreamSmallMxStages[j];
+    return kStreamMxStages[j];
 }
 
 // Records events[j] (when given) before stage j, and events[n] after the last.
@@ -239,8 +270,10 @@ int run_forward(const void* x, const float* router_logits, const void* w13, cons
         pa.xs = xs;
         pa.w13 = static_cast<const uint8_t*>(w13);
         pa.s13 = s13;
+        pa.e13 = nullptr;
         pa.w2 = static_cast<const uint8_t*>(w2);
         pa.s2 = s2;
+        pa.e2 = nullptr;
         pa.offsets = offsets;
         pa.sorted = sorted;
         pa.mtile_off = mtile_off;
@@ -251,8 +284,8 @@ int run_forward(const void* x, const float* router_logits, const void* w13, cons
         pa.i = i;
         pa.E = E;
         pa.k = k;
-        MOE_STEP(moe::launch_prefill_gate_up(pa, R, stream));
-        MOE_STEP(moe::launch_prefill_down(pa, R, stream));
+        MOE_STEP(moe::launch_prefill_gate_up(pa, false, stream));
+        MOE_STEP(moe::launch_prefill_down(pa, false, stream));
         MOE_STEP(moe::launch_combine_bf16(pa.y, tw, M, k, h, static_cast<uint16_t*>(out), stream));
         return hook.mark() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
     }
@@ -277,7 +310,8 @@ int run_forward(const void* x, const float* router_logits, const void* w13, cons
 }
 
 // The MXFP4-weight layer: routing, quantisation and grouping as in the FP8
-// layer, then the MXFP4 streaming GEMMs and the fp32 combine.
+// layer, then either the MXFP4 streaming GEMMs and the fp32 combine, or (large
+// batches) the tiled MXFP4 GEMMs and the bf16 combine.
 int run_forward_mx(const void* x, const float* router_logits, const void* w13, const void* e13, const void* w2,
                    const void* e2, void* out, int M, int h, int i, int E, int k, void* workspace,
                    size_t workspace_bytes, hipStream_t stream, int n_stages = 1 << 30) {
@@ -304,8 +338,6 @@ int run_forward_mx(const void* x, const float* router_logits, const void* w13, c
     int32_t* active = at<int32_t>(workspace, p.active);
     int32_t* num_active = at<int32_t>(workspace, p.num_active);
     int32_t* hist = at<int32_t>(workspace, L.hist);
-    float* g = at<float>(workspace, p.gate_up);
-    float* y = at<float>(workspace, p.partial);
     uint32_t* sync = at<uint32_t>(workspace, 0);
     EventHook hook{nullptr, 0, 0, stream, n_stages};
 #define MOE_STEP(call)                 \
@@ -314,6 +346,38 @@ int run_forward_mx(const void* x, const float* router_logits, const void* w13, c
         rc = hip_status(call);         \
         if (rc != MOE_OK) return rc;   \
     } while (0)
+    if (p.path == MOE_FP8_PATH_PREFILL) {
+        int32_t* mtile_off = at<int32_t>(workspace, L.mtile_off);
+        MOE_STEP(moe::launch_route_quant(router_logits, static_cast<const uint16_t*>(x), M, E, k, h, ids, tw, xq,
+                                         xs, moe::kRoute | moe::kQuant, stream));
+        MOE_STEP(moe::launch_group(ids, R, E, hist, counts, offsets, sorted, active, num_active, stream,
+                                   moe::prefill_tile_m(), mtile_off));
+        moe::PrefillArgs pa;
+        pa.xq = xq;
+        pa.xs = xs;
+        pa.w13 = static_cast<const uint8_t*>(w13);
+        pa.s13 = nullptr;
+        pa.e13 = static_cast<const uint8_t*>(e13);
+        pa.w2 = static_cast<const uint8_t*>(w2);
+        pa.s2 = nullptr;
+        pa.e2 = static_cast<const uint8_t*>(e2);
+        pa.offsets = offsets;
+        pa.sorted = sorted;
+        pa.mtile_off = mtile_off;
+        pa.a2 = at<uint8_t>(workspace, p.act2);
+        pa.a2s = at<float>(workspace, p.act2_scale);
+        pa.y = at<uint16_t>(workspace, p.partial);
+        pa.h = h;
+        pa.i = i;
+        pa.E = E;
+        pa.k = k;
+        MOE_STEP(moe::launch_prefill_gate_up(pa, true, stream));
+        MOE_STEP(moe::launch_prefill_down(pa, true, stream));
+        MOE_STEP(moe::launch_combine_bf16(pa.y, tw, M, k, h, static_cast<uint16_t*>(out), stream));
+        return MOE_OK;
+    }
+    float* g = at<float>(workspace, p.gate_up);
+    float* y = at<float>(workspace, p.partial);
     if (small_group(M, k)) {
         MOE_STEP(moe::launch_route_quant_group(router_logits, static_cast<const uint16_t*>(x), M, E, k, h, ids, tw,
                                                xq, xs, counts, offsets, sorted, active, num_active,
@@ -344,6 +408,29 @@ int run_forward_mx(const void* x, const float* router_logits, const void* w13, c
 }  // namespace
 
 extern "C" {
+
+int moe_mxfp4_workspace_layout(int M, int h, int i, int E, int k, moe_fp8_ws_layout* layout) {
+    if (!layout) return MOE_ERR_INVALID;
+    const int rc = check_shape(M, h, i, E, k);
+    if (rc != MOE_OK) return rc;
+    Layout L;
+    make_layout(M, h, i, E, k, &L, true);
+    *layout = L.pub;
+    return MOE_OK;
+}
+
+int moe_mxfp4_forward_kernel_count(int M, int h, int i, int E, int k) {
+    const int rc = check_shape(M, h, i, E, k);
+    if (rc != MOE_OK) return rc;
+    if (M == 0) return 0;
+    return stage_count(choose_path_mx(M, h, i, E, k), M, k);
+}
+
+const char* moe_mxfp4_forward_kernel_name(int M, int h, int i, int E, int k, int j) {
+    const int n = moe_mxfp4_forward_kernel_count(M, h, i, E, k);
+    if (n <= 0 || j < 0 || j >= n) return nullptr;
+    return stage_name_mx(choose_path_mx(M, h, i, E, k), M, k, j);
+}
 
 size_t moe_mxfp4_workspace_bytes(int M, int h, int i, int E, int k) {
     if (M == 0 || check_shape(M, h, i, E, k) != MOE_OK) return 0;

@@ -30,12 +30,6 @@ constexpr int kMxRowsPerWave = 32;               // two A fragments
 constexpr int kMxRowsPerGroup = 4 * kMxRowsPerWave;
 constexpr int kMxUnrollUp = 4;
 constexpr int kMxUnrollDown = 2;
-constexpr int kE8M0One = 127;
-
-__device__ __forceinline__ v4f mfma_fp4_e4m3(const uint4& a, const v8i& b, int scale_a, const v4f& c) {
-    const v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, b, c, 4, 0, 0, scale_a, 0, kE8M0One);
-}
 
 // The B operand of one 128-byte activation K block for lane group g.
 __device__ __forceinline__ v8i act_operand(const uint8_t* blk, int g) {
@@ -172,7 +166,7 @@ __global__ __launch_bounds__(256) void stream_gate_up_mx_kernel(
                 const float sc = valid ? C[u] : 0.0f;                                                \
                 _Pragma("unroll") for (int f = 0; f < 2; ++f) {                                      \
                     const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};                                          \
-                    const v4f blk = mfma_fp4_e4m3(A[f][u], B, scale_of(S[f], u, grp), z);            \
+                    const v4f blk = mfma_16x16x128_fp4_e4m3(A[f][u], B, scale_of(S[f], u, grp), z);            \
                     _Pragma("unroll") for (int v = 0; v < 4; ++v) acc[f][v] = fmaf(blk[v], sc, acc[f][v]); \
                 }                                                                                    \
             }                                                                                        \
@@ -263,7 +257,7 @@ __global__ __launch_bounds__(256) void stream_down_mx_kernel(
 #pragma unroll
                     for (int f = 0; f < 2; ++f) {
                         const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
-                        const v4f blk = mfma_fp4_e4m3(A[f][u], B, (int)((sw[f][u] >> (8 * grp)) & 0xFFu), z);
+                        const v4f blk = mfma_16x16x128_fp4_e4m3(A[f][u], B, (int)((sw[f][u] >> (8 * grp)) & 0xFFu), z);
 #pragma unroll
                         for (int v = 0; v < 4; ++v) acc[f][v] = fmaf(blk[v], sc, acc[f][v]);
                     }

@@ -1,5 +1,6 @@
-// prefill_gemm.hip -- tiled grouped FP8 GEMMs for batches with many tokens
-// per expert (prefill).
+// prefill_gemm.hip -- tiled grouped GEMMs with FP8 (128x128 block-scaled) or
+// MXFP4 weights and E4M3 activations, for batches with many tokens per expert
+// (prefill).
 //
 // Routes are grouped by expert (counts, offsets, routes sorted by expert then
 // route id).  An M-tile is 128 consecutive sorted routes of one expert; the
@@ -29,6 +30,13 @@
 //    table: explicit 128x128 block scales): acc += blk * (s_w * s_act) in
 //    fp32, one K block after the MFMA that produced blk, so the promotion
 //    arithmetic never waits on an MFMA result.
+// MXFP4 weights (the _mx_ kernels; Inferact amd-kernels README, naming
+// section: moe/mxfp4_h6144_i768_e128_top4) take the same loop: 64-byte LDS
+// weight rows (E2M1 codes of one K block) plus each row's four E8M0 scale
+// bytes, copied beside them; the FP4 x FP8 form of the same MFMA applies the
+// weight scales itself, and the promotion carries the activation scale alone.
+// That form issues at the FP8 rate, so the loop's MFMA time is unchanged and
+// only the weight copies halve.
 // gate/up's epilogue computes SiLU(gate) * up and its 1x128 E4M3
 // requantisation on the spot (Netra Kernel README, MoE prefill pair) and
 // writes codes in sorted-route order; down writes bf16 partial rows by route
@@ -48,16 +56,31 @@ namespace {
 constexpr int kBM = 128;                      // routes per tile
 constexpr int kBN = 256;                      // weight rows per tile
 constexpr int kThreads = 512;                 // 8 waves
-constexpr int kAB = kBN * 128;                // weight bytes per stage
 constexpr int kBB = kBM * 128;                // activation bytes per stage
 constexpr int kXS = 8 * 256;                  // activation scales per stage: 256 B per wave, 64 used
-constexpr int kStage = kAB + kBB + kXS;
-constexpr int kDmaA = kAB / 1024 / 8;         // 1 KiB copies per wave per stage
-constexpr int kDmaB = kBB / 1024 / 8;
-constexpr int kVmemPerStage = kDmaA + kDmaB + 1;   // + one copy of 16 route scales
+constexpr int kDmaB = kBB / 1024 / 8;         // 1 KiB activation copies per wave per stage
 constexpr int kMaxKB = 128;                   // scale tables: K blocks (h, i <= 16384)
 
-static_assert(kDmaA == 4 && kDmaB == 2, "stage copy split");
+// Stage layout per weight format.  FP8 weights: 128 bytes per row and K
+// block, fp32 128x128 block scales applied in the promotion.  MXFP4 weights
+// (E2M1 codes two per byte, one E8M0 scale per 32 K elements): 64 bytes per
+// row and K block, plus the rows' four scale bytes per K block, which the
+// MFMA applies itself.
+template <bool kMx>
+struct Fmt {
+    static constexpr int kRowBytes = kMx ? 64 : 128;       // weight bytes per row per K block
+    static constexpr int kAB = kBN * kRowBytes;            // weight bytes per stage
+    static constexpr int kAS = kMx ? 8 * 256 : 0;          // E8M0 scale words: 256 B per wave, 32 rows used
+    static constexpr int kBOff = kAB + kAS;                // activation tile
+    static constexpr int kXOff = kBOff + kBB;              // activation scales
+    static constexpr int kStage = kXOff + kXS;
+    static constexpr int kDmaA = kAB / 1024 / 8;           // 1 KiB weight copies per wave per stage
+    // copies per wave per stage: weights, activations, 16 route scales, and
+    // (MXFP4) 32 rows' scale words
+    static constexpr int kVmem = kDmaA + kDmaB + 1 + (kMx ? 1 : 0);
+};
+
+static_assert(Fmt<false>::kDmaA == 4 && Fmt<true>::kDmaA == 2 && kDmaB == 2, "stage copy split");
 
 // gfx9 s_waitcnt immediate waiting until at most n vector-memory operations
 // are outstanding (expcnt and lgkmcnt left at their maxima).
@@ -112,13 +135,17 @@ struct Loop {
     const uint8_t* gA;              // weight copies of K block 0 start here ...
     const uint8_t* gB;              // ... activation copies here
     const float* gX;                // ... activation-scale copies here (element kb of a route's row)
-    uint32_t offA[kDmaA], offB[kDmaB];   // ... plus these per-lane byte offsets
+    const uint8_t* gS;              // ... (MXFP4) weight-scale copies here
+    uint32_t offA[4], offB[kDmaB];  // ... plus these per-lane byte offsets
     uint32_t offX;                  // ... and this per-lane element offset
+    uint32_t offS;                  // ... and this per-lane byte offset (MXFP4)
     int wave;                       // wave index (uniform)
     // fragment reads: lane's lower / upper half of weight tile 0 and route tile 0
+    // (MXFP4: a_lo only, 16 bytes)
     int a_lo, a_hi, b_lo, b_hi;
     int x_off;                      // byte offset of the lane's route-tile-0 scale in a stage
     int a_step[4];                  // byte offsets of weight tiles 1..3 from tile 0 (constants)
+    int s_off[4];                   // (MXFP4) byte offset of the lane's scale word in weight tile j
 };
 
 // global -> LDS copies.  Written as inline assembly so that the compiler
@@ -140,16 +167,21 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 
 // Issue the copies of K block kb into stage buffer st.
+template <bool kMx>
 __device__ __forceinline__ void issue_stage(const Loop& L, uint8_t* st, int kb) {
-    const uint8_t* gA = L.gA + (size_t)kb * 128;
+    using F = Fmt<kMx>;
+    const uint8_t* gA = L.gA + (size_t)kb * F::kRowBytes;
     const uint8_t* gB = L.gB + (size_t)kb * 128;
     const uint32_t base = lds_addr(st);
 #pragma unroll
-    for (int q = 0; q < kDmaA; ++q) copy16_to_lds(gA + L.offA[q], base + (L.wave * kDmaA + q) * 1024);
+    for (int q = 0; q < F::kDmaA; ++q) copy16_to_lds(gA + L.offA[q], base + (L.wave * F::kDmaA + q) * 1024);
 #pragma unroll
-    for (int q = 0; q < kDmaB; ++q) copy16_to_lds(gB + L.offB[q], base + kAB + (L.wave * kDmaB + q) * 1024);
+    for (int q = 0; q < kDmaB; ++q) copy16_to_lds(gB + L.offB[q], base + F::kBOff + (L.wave * kDmaB + q) * 1024);
     // scales of routes 16 wave .. +16 (lanes 16..63 repeat lanes 0..15)
-    copy4_to_lds(L.gX + L.offX + kb, base + kAB + kBB + L.wave * 256);
+    copy4_to_lds(L.gX + L.offX + kb, base + F::kXOff + L.wave * 256);
+    // (MXFP4) the four scale bytes of K block kb of weight rows 32 wave ..
+    // +32 (lanes 32..63 repeat lanes 0..31)
+    if constexpr (kMx) copy4_to_lds(L.gS + L.offS + 4 * kb, base + F::kAB + L.wave * 256);
 }
 
 // One K block on one wave: 4 weight tiles x 4 route tiles.  The raw block
@@ -157,23 +189,44 @@ __device__ __forceinline__ void issue_stage(const Loop& L, uint8_t* st, int kb) 
 // xr_p[m]) are promoted into acc just before the MFMA that overwrites them,
 // so no promotion waits on the MFMA that has just been issued; this block's
 // scales are handed back in sw_p / xr_p for the next call (before the first
-// block, blk and the scales are zero, so that promotion adds zeros).
+// block, blk and the scales are zero, so that promotion adds zeros).  With
+// MXFP4 weights the MFMA applies the weights' E8M0 scales itself and the
+// promotion carries the activation scale alone.
+template <bool kMx>
 __device__ __forceinline__ void block_mma(v4f acc[16], v4f blk[16], float sw_p[4], float xr_p[4], const Loop& L,
                                           const uint8_t* st, const float sw[4]) {
-    v8i A[4], B[4];
+    v8i B[4];
     float xr[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) B[m] = frag(st + L.b_lo + m * 2048, st + L.b_hi + m * 2048);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) A[j] = frag(st + L.a_lo + L.a_step[j], st + L.a_hi + L.a_step[j]);
-#pragma unroll
     for (int m = 0; m < 4; ++m) xr[m] = *reinterpret_cast<const float*>(st + L.x_off + m * 256);
+    if constexpr (kMx) {
+        uint4 A[4];
+        int sa[4];
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-        const float sc = sw_p[t >> 2] * xr_p[t & 3];
+        for (int j = 0; j < 4; ++j) {
+            A[j] = *reinterpret_cast<const uint4*>(st + L.a_lo + L.a_step[j]);
+            sa[j] = st[L.s_off[j]];
+        }
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[t][v] = fmaf(blk[t][v], sc, acc[t][v]);
-        blk[t] = mfma_16x16x128_e4m3(A[t >> 2], B[t & 3], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+        for (int t = 0; t < 16; ++t) {
+            const float sc = xr_p[t & 3];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[t][v] = fmaf(blk[t][v], sc, acc[t][v]);
+            blk[t] = mfma_16x16x128_fp4_e4m3(A[t >> 2], B[t & 3], sa[t >> 2], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+        }
+    } else {
+        v8i A[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) A[j] = frag(st + L.a_lo + L.a_step[j], st + L.a_hi + L.a_step[j]);
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            const float sc = sw_p[t >> 2] * xr_p[t & 3];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[t][v] = fmaf(blk[t][v], sc, acc[t][v]);
+            blk[t] = mfma_16x16x128_e4m3(A[t >> 2], B[t & 3], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+        }
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -188,53 +241,90 @@ __device__ __forceinline__ void block_mma(v4f acc[16], v4f blk[16], float sw_p[4
 // copies of block kb visible and certifies that every wave has finished
 // reading block kb - 1; only then are the copies of block kb + 2 issued, into
 // kb - 1's buffer, so two blocks are in flight while block kb is multiplied.
-// sw_of(kb, sw) fills the wave's four weight-tile scales of block kb.  The
-// copies of blocks 0 and 1 (into buffers 0 and 1) are issued by the caller,
-// possibly long before (issue_first).
+// sw_of(kb, sw) fills the wave's four weight-tile scales of block kb (FP8
+// weights).  The copies of blocks 0 and 1 (into buffers 0 and 1) are issued
+// by the caller, possibly long before (issue_first).
+template <bool kMx>
 __device__ __forceinline__ void issue_first(const Loop& L, int KB, uint8_t* stages) {
-    issue_stage(L, stages, 0);
-    if (KB > 1) issue_stage(L, stages + kStage, 1);
+    issue_stage<kMx>(L, stages, 0);
+    if (KB > 1) issue_stage<kMx>(L, stages + Fmt<kMx>::kStage, 1);
 }
 
 // after_first() runs once, right after the first barrier: every wave has
 // then finished whatever it did before the loop.
-template <typename SwOf, typename AfterFirst>
+template <bool kMx, typename SwOf, typename AfterFirst>
 __device__ __forceinline__ void k_loop(v4f acc[16], const Loop& L, int KB, uint8_t* stages, SwOf sw_of,
                                        AfterFirst after_first) {
-    float sw[4], sw_p[4] = {0.0f, 0.0f, 0.0f, 0.0f}, xr_p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    using F = Fmt<kMx>;
+    float sw[4] = {1.0f, 1.0f, 1.0f, 1.0f}, sw_p[4] = {0.0f, 0.0f, 0.0f, 0.0f}, xr_p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     v4f blk[16];
 #pragma unroll
     for (int t = 0; t < 16; ++t) blk[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     int rd = 0;   // stage buffer of block kb
     for (int kb = 0; kb < KB; ++kb) {
-        if (kb + 1 < KB) __builtin_amdgcn_s_waitcnt(vm_wait(kVmemPerStage));
+        if (kb + 1 < KB) __builtin_amdgcn_s_waitcnt(vm_wait(F::kVmem));
         else __builtin_amdgcn_s_waitcnt(vm_wait(0));
         block_barrier();
-        if (kb + 2 < KB) issue_stage(L, stages + (rd == 0 ? 2 : rd - 1) * kStage, kb + 2);
+        if (kb + 2 < KB) issue_stage<kMx>(L, stages + (rd == 0 ? 2 : rd - 1) * F::kStage, kb + 2);
         if (kb == 0) after_first();
-        sw_of(kb, sw);
-        block_mma(acc, blk, sw_p, xr_p, L, stages + rd * kStage, sw);
+        if constexpr (!kMx) sw_of(kb, sw);
+        block_mma<kMx>(acc, blk, sw_p, xr_p, L, stages + rd * F::kStage, sw);
         rd = rd == 2 ? 0 : rd + 1;
     }
     block_barrier();   // every wave is done with the stage buffers
 #pragma unroll
     for (int t = 0; t < 16; ++t) {   // promotion of the last block
-        const float sc = sw_p[t >> 2] * xr_p[t & 3];
+        const float sc = kMx ? xr_p[t & 3] : sw_p[t >> 2] * xr_p[t & 3];
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[t][v] = fmaf(blk[t][v], sc, acc[t][v]);
     }
 }
 
+// (MXFP4) Slot of 16-byte chunk g of weight row r in a 64-byte LDS row is
+// g ^ mx_swz(r): every 8 consecutive rows of one chunk fill the 8 16-byte
+// slots of a 128-byte window, and rows 16 q .. 16 q + 15 fill those of a
+// 256-byte window, so the A fragment reads (lane l: row l % 16, chunk l / 16)
+// are free of bank conflicts for 8- or 16-lane service.  The activation rows
+// of the MXFP4 kernels hold chunk p ^ swz(r) in slot p, so the B fragment
+// reads (chunks g and g + 4) are free of conflicts too.
+__device__ __forceinline__ int mx_swz(int r) { return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1); }
+
 // Fragment read offsets of this lane: row col of a 16-row tile, K group kg;
-// weight tile 0 starts at LDS row a_row0, route tile 0 at row b_row0.
-__device__ __forceinline__ void lane_geometry(Loop& L, int lane, int a_row0, int b_row0) {
+// weight tile j starts at LDS row a_row0 + a_rows[j], route tile 0 at row
+// b_row0 (both multiples of 16).
+template <bool kMx>
+__device__ __forceinline__ void lane_geometry(Loop& L, int lane, int a_row0, const int (&a_rows)[4], int b_row0) {
+    using F = Fmt<kMx>;
     const int col = lane & 15, kg = lane >> 4;
-    const int lo = lo_slot(col, kg);
-    L.a_lo = (a_row0 + col) * 128 + lo * 16;
-    L.a_hi = (a_row0 + col) * 128 + (lo ^ 4) * 16;
-    L.b_lo = kAB + (b_row0 + col) * 128 + lo * 16;
-    L.b_hi = kAB + (b_row0 + col) * 128 + (lo ^ 4) * 16;
-    L.x_off = kAB + kBB + (b_row0 / 16) * 256 + col * 4;
+    if constexpr (kMx) {
+        L.a_lo = (a_row0 + col) * 64 + (kg ^ mx_swz(col)) * 16;
+        L.a_hi = L.a_lo;
+        const int lo = kg ^ swz(col);   // chunks kg and kg + 4 of the route row
+        L.b_lo = F::kBOff + (b_row0 + col) * 128 + lo * 16;
+        L.b_hi = F::kBOff + (b_row0 + col) * 128 + (lo ^ 4) * 16;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = a_row0 + a_rows[j] + col;
+            L.a_step[j] = a_rows[j] * 64;
+            L.s_off[j] = F::kAB + (r >> 5) * 256 + (r & 31) * 4 + kg;
+        }
+    } else {
+        const int lo = lo_slot(col, kg);
+        L.a_lo = (a_row0 + col) * 128 + lo * 16;
+        L.a_hi = (a_row0 + col) * 128 + (lo ^ 4) * 16;
+        L.b_lo = F::kBOff + (b_row0 + col) * 128 + lo * 16;
+        L.b_hi = F::kBOff + (b_row0 + col) * 128 + (lo ^ 4) * 16;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) L.a_step[j] = a_rows[j] * 128;
+    }
+    L.x_off = F::kXOff + (b_row0 / 16) * 256 + col * 4;
+}
+
+// Global byte offset, within a route's 128-byte K block, of the 16-byte
+// chunk that lane slot p of route row r copies.
+template <bool kMx>
+__device__ __forceinline__ int act_chunk(int r, int p) {
+    return (kMx ? (p ^ swz(r)) : chunk_of(r, p)) * 16;
 }
 
 // Both kernels are persistent: one workgroup per CU walks the tiles of its
@@ -274,32 +364,42 @@ __device__ __forceinline__ TileInfo decode_tile(const TileMeta& meta, int E, int
 
 namespace {
 
-// Loop state of a gate/up tile whose token list is in tok (LDS).
+// Loop state of a gate/up tile.
 // rt: the tile's route ids by row (padding rows repeat the last route).
+template <bool kMx>
 __device__ __forceinline__ Loop gate_up_loop(const PrefillArgs& a, const TileInfo& t, const int* rt, int wave,
                                              int lane) {
+    using F = Fmt<kMx>;
     const int h = a.h, i = a.i, KB = h / 128, N13 = 2 * i;
     const int wr = wave & 1, wn = wave >> 1;
+    const int hb = kMx ? h / 2 : h;   // weight row bytes
     Loop L;
-    lane_geometry(L, lane, 32 * wn, 64 * wr);   // gate rows 32 wn + {0, 16}, up rows 128 + 32 wn + {0, 16}
-    L.a_step[0] = 0;
-    L.a_step[1] = 16 * 128;
-    L.a_step[2] = 128 * 128;
-    L.a_step[3] = 144 * 128;
+    // gate rows 32 wn + {0, 16}, up rows 128 + 32 wn + {0, 16}
+    lane_geometry<kMx>(L, lane, 32 * wn, {0, 16, 128, 144}, 64 * wr);
     L.wave = wave;
-    L.gA = a.w13 + (size_t)t.e * N13 * h;
+    L.gA = a.w13 + (size_t)t.e * N13 * hb;
     L.gB = a.xq;
     L.gX = a.xs;
+    auto wrow = [&](int r) { return r < 128 ? t.sub * 128 + r : i + t.sub * 128 + (r - 128); };
+    if constexpr (kMx) {
 #pragma unroll
-    for (int q = 0; q < kDmaA; ++q) {
-        const int r = (wave * kDmaA + q) * 8 + (lane >> 3);
-        const int wrow = r < 128 ? t.sub * 128 + r : i + t.sub * 128 + (r - 128);
-        L.offA[q] = (uint32_t)(wrow * h + chunk_of(r, lane & 7) * 16);
+        for (int q = 0; q < F::kDmaA; ++q) {   // 16 rows of 64 bytes per copy
+            const int r = (wave * F::kDmaA + q) * 16 + (lane >> 2);
+            L.offA[q] = (uint32_t)(wrow(r) * hb + ((lane & 3) ^ mx_swz(r)) * 16);
+        }
+        L.gS = a.e13 + (size_t)t.e * N13 * (h / 32);
+        L.offS = (uint32_t)(wrow(32 * wave + (lane & 31)) * (h / 32));
+    } else {
+#pragma unroll
+        for (int q = 0; q < F::kDmaA; ++q) {   // 8 rows of 128 bytes per copy
+            const int r = (wave * F::kDmaA + q) * 8 + (lane >> 3);
+            L.offA[q] = (uint32_t)(wrow(r) * hb + chunk_of(r, lane & 7) * 16);
+        }
     }
 #pragma unroll
     for (int q = 0; q < kDmaB; ++q) {
         const int r = (wave * kDmaB + q) * 8 + (lane >> 3);
-        L.offB[q] = (uint32_t)(rt[r] / a.k * h + chunk_of(r, lane & 7) * 16);
+        L.offB[q] = (uint32_t)(rt[r] / a.k * h + act_chunk<kMx>(r, lane & 7));
     }
     L.offX = (uint32_t)(rt[16 * wave + (lane & 15)] / a.k * KB);
     return L;
@@ -359,16 +459,16 @@ __device__ __forceinline__ void gate_up_epilogue(const PrefillArgs& a, const Til
     }
 }
 
-}  // namespace
-
-__global__ __launch_bounds__(kThreads, 1) void prefill_gate_up_kernel(PrefillArgs a) {
-    __shared__ __align__(16) uint8_t stages[3 * kStage];
+template <bool kMx>
+__device__ __forceinline__ void gate_up_tiles(const PrefillArgs& a) {
+    using F = Fmt<kMx>;
+    __shared__ __align__(16) uint8_t stages[3 * F::kStage];
     __shared__ int rt_l[2][kBM];                // route id of each row, per tile parity
     __shared__ float amax_l[4][kBM];
-    __shared__ float sw_l[2][2][kMaxKB];        // gate / up weight scales per K block, per tile parity
+    __shared__ float sw_l[2][2][kMaxKB];        // (FP8) gate / up weight scales per K block, per tile parity
     __shared__ TileMeta meta;
 
-    const int h = a.h, i = a.i, E = a.E, k = a.k;
+    const int h = a.h, i = a.i, E = a.E;
     const int KB = h / 128, IB = i / 128, N13 = 2 * i;
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
 
@@ -377,38 +477,37 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_gate_up_kernel(PrefillArg
     TileSpan span = tile_span(meta.mtile_off[E] * IB);
     if (span.next >= span.end) return;
 
-    auto scales = [&](const TileInfo& t, int j, int half) {
-        return a.s13[((size_t)t.e * (N13 / 128) + half * IB + t.sub) * KB + j];
-    };
     TileInfo t = decode_tile(meta, E, IB, span.next);
     int par = 0;
     // padding rows repeat the tile's last route (their outputs are dropped)
     for (int r = tid; r < kBM; r += kThreads) rt_l[0][r] = a.sorted[t.beg + min(r, t.rows - 1)];
-    for (int j = tid; j < KB; j += kThreads) {
-        sw_l[0][0][j] = scales(t, j, 0);
-        sw_l[0][1][j] = scales(t, j, 1);
+    if constexpr (!kMx) {
+        for (int j = tid; j < KB; j += kThreads) {
+            sw_l[0][0][j] = a.s13[((size_t)t.e * (N13 / 128) + t.sub) * KB + j];
+            sw_l[0][1][j] = a.s13[((size_t)t.e * (N13 / 128) + IB + t.sub) * KB + j];
+        }
     }
     __syncthreads();
-    Loop L = gate_up_loop(a, t, rt_l[0], wave, lane);
-    issue_first(L, KB, stages);
+    Loop L = gate_up_loop<kMx>(a, t, rt_l[0], wave, lane);
+    issue_first<kMx>(L, KB, stages);
 
     for (;;) {
         span.next += span.step;
         const bool more = span.next < span.end;
         TileInfo tn = t;
         if (more) tn = decode_tile(meta, E, IB, span.next);
-        // The next tile's route ids (waves 0, 1) and gate / up scales (waves
-        // 2, 3) are copied straight into the other parity's LDS lists during
-        // this tile's K loop (once its first barrier shows that no wave still
-        // reads them), and its last wait and barrier also cover these copies.
-        // No register receives them, so the tile loop carries no load the
-        // compiler would wait for.
+        // The next tile's route ids (waves 0, 1) and, for FP8 weights, gate /
+        // up scales (waves 2, 3) are copied straight into the other parity's
+        // LDS lists during this tile's K loop (once its first barrier shows
+        // that no wave still reads them), and its last wait and barrier also
+        // cover these copies.  No register receives them, so the tile loop
+        // carries no load the compiler would wait for.
         auto next_lists = [&]() {
             if (!more) return;
             if (wave < 2) {
                 const int r = 64 * wave + lane;
                 copy4_to_lds(a.sorted + tn.beg + min(r, tn.rows - 1), lds_addr(&rt_l[par ^ 1][64 * wave]));
-            } else if (wave < 4) {
+            } else if (!kMx && wave < 4) {
                 const int half = wave - 2;
                 const float* src = a.s13 + ((size_t)tn.e * (N13 / 128) + half * IB + tn.sub) * KB;
                 for (int c = 0; 64 * c < KB; ++c)
@@ -422,53 +521,69 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_gate_up_kernel(PrefillArg
         v4f acc[16];
 #pragma unroll
         for (int u = 0; u < 16; ++u) acc[u] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-        k_loop(acc, L, KB, stages, sw_of, next_lists);   // ends with every wave done with the stage buffers
+        k_loop<kMx>(acc, L, KB, stages, sw_of, next_lists);   // ends with every wave done with the stage buffers
         if (more) {
-            L = gate_up_loop(a, tn, rt_l[par ^ 1], wave, lane);
-            issue_first(L, KB, stages);   // buffers 0 and 1; the epilogue stages codes in buffer 2
+            L = gate_up_loop<kMx>(a, tn, rt_l[par ^ 1], wave, lane);
+            issue_first<kMx>(L, KB, stages);   // buffers 0 and 1; the epilogue stages codes in buffer 2
         }
-        gate_up_epilogue(a, t, acc, amax_l, stages + 2 * kStage, tid);
+        gate_up_epilogue(a, t, acc, amax_l, stages + 2 * F::kStage, tid);
         if (!more) break;
         t = tn;
         par ^= 1;
     }
 }
 
+}  // namespace
+
+__global__ __launch_bounds__(kThreads, 1) void prefill_gate_up_kernel(PrefillArgs a) { gate_up_tiles<false>(a); }
+__global__ __launch_bounds__(kThreads, 1) void prefill_gate_up_mx_kernel(PrefillArgs a) { gate_up_tiles<true>(a); }
+
 // -------------------------------------------------------------------- down
 
 namespace {
 
+template <bool kMx>
 __device__ __forceinline__ Loop down_loop(const PrefillArgs& a, const TileInfo& t, int wave, int lane) {
+    using F = Fmt<kMx>;
     const int h = a.h, i = a.i, IB = i / 128;
     const int wr = wave & 1, wn = wave >> 1;
+    const int ib = kMx ? i / 2 : i;   // weight row bytes
     Loop L;
-    lane_geometry(L, lane, 64 * wn, 64 * wr);   // weight rows 64 wn + 16 j; route tiles 64 wr + 16 m
-#pragma unroll
-    for (int j = 0; j < 4; ++j) L.a_step[j] = j * 16 * 128;
+    lane_geometry<kMx>(L, lane, 64 * wn, {0, 16, 32, 48}, 64 * wr);   // weight rows 64 wn + 16 j; route tiles 64 wr + 16 m
     L.wave = wave;
-    L.gA = a.w2 + ((size_t)t.e * h + (size_t)t.sub * kBN) * i;
+    L.gA = a.w2 + ((size_t)t.e * h + (size_t)t.sub * kBN) * ib;
     L.gB = a.a2 + (size_t)t.beg * i;
     L.gX = a.a2s + (size_t)t.beg * IB;
+    if constexpr (kMx) {
 #pragma unroll
-    for (int q = 0; q < kDmaA; ++q) {
-        const int r = (wave * kDmaA + q) * 8 + (lane >> 3);
-        L.offA[q] = (uint32_t)(r * i + chunk_of(r, lane & 7) * 16);
+        for (int q = 0; q < F::kDmaA; ++q) {
+            const int r = (wave * F::kDmaA + q) * 16 + (lane >> 2);
+            L.offA[q] = (uint32_t)(r * ib + ((lane & 3) ^ mx_swz(r)) * 16);
+        }
+        L.gS = a.e2 + ((size_t)t.e * h + (size_t)t.sub * kBN) * (i / 32);
+        L.offS = (uint32_t)((32 * wave + (lane & 31)) * (i / 32));
+    } else {
+#pragma unroll
+        for (int q = 0; q < F::kDmaA; ++q) {
+            const int r = (wave * F::kDmaA + q) * 8 + (lane >> 3);
+            L.offA[q] = (uint32_t)(r * ib + chunk_of(r, lane & 7) * 16);
+        }
     }
 #pragma unroll
     for (int q = 0; q < kDmaB; ++q) {
         const int r = (wave * kDmaB + q) * 8 + (lane >> 3);
-        L.offB[q] = (uint32_t)(min(r, t.rows - 1) * i + chunk_of(r, lane & 7) * 16);   // padding repeats the last route
+        L.offB[q] = (uint32_t)(min(r, t.rows - 1) * i + act_chunk<kMx>(r, lane & 7));   // padding repeats the last route
     }
     L.offX = (uint32_t)(min(16 * wave + (lane & 15), t.rows - 1) * IB);
     return L;
 }
 
-}  // namespace
-
-__global__ __launch_bounds__(kThreads, 1) void prefill_down_kernel(PrefillArgs a) {
-    __shared__ __align__(16) uint8_t stages[3 * kStage];
+template <bool kMx>
+__device__ __forceinline__ void down_tiles(const PrefillArgs& a) {
+    using F = Fmt<kMx>;
+    __shared__ __align__(16) uint8_t stages[3 * F::kStage];
     __shared__ int prt_l[2][kBM];               // route id of each row (padding repeats the last), per tile parity
-    __shared__ float sw_l[2][2 * kMaxKB];       // the tile's two 128-row scale blocks, per tile parity
+    __shared__ float sw_l[2][2 * kMaxKB];       // (FP8) the tile's two 128-row scale blocks, per tile parity
     __shared__ TileMeta meta;
 
     const int h = a.h, i = a.i, E = a.E;
@@ -482,16 +597,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_down_kernel(PrefillArgs a
     TileSpan span = tile_span(meta.mtile_off[E] * NT);
     if (span.next >= span.end) return;
 
-    auto scale = [&](const TileInfo& t, int j) {   // j < 2 IB: blocks 2 sub and 2 sub + 1
-        return a.s2[((size_t)t.e * (h / 128) + 2 * t.sub) * IB + j];
-    };
     TileInfo t = decode_tile(meta, E, NT, span.next);
     int par = 0;
     for (int r = tid; r < kBM; r += kThreads) prt_l[0][r] = a.sorted[t.beg + min(r, t.rows - 1)];
-    for (int j = tid; j < 2 * IB; j += kThreads) sw_l[0][j] = scale(t, j);
+    if constexpr (!kMx) {   // j < 2 IB: scale blocks 2 sub and 2 sub + 1
+        for (int j = tid; j < 2 * IB; j += kThreads) sw_l[0][j] = a.s2[((size_t)t.e * (h / 128) + 2 * t.sub) * IB + j];
+    }
     __syncthreads();
-    Loop L = down_loop(a, t, wave, lane);
-    issue_first(L, IB, stages);
+    Loop L = down_loop<kMx>(a, t, wave, lane);
+    issue_first<kMx>(L, IB, stages);
 
     const int sblk = wn >> 1;
     for (;;) {
@@ -506,7 +620,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_down_kernel(PrefillArgs a
             if (wave < 2) {
                 const int r = 64 * wave + lane;
                 copy4_to_lds(a.sorted + tn.beg + min(r, tn.rows - 1), lds_addr(&prt_l[par ^ 1][64 * wave]));
-            } else if (64 * (wave - 2) < 2 * IB) {
+            } else if (!kMx && 64 * (wave - 2) < 2 * IB) {
                 const int c = wave - 2;
                 const float* src = a.s2 + ((size_t)tn.e * (h / 128) + 2 * tn.sub) * IB;
                 copy4_to_lds(src + min(64 * c + lane, 2 * IB - 1), lds_addr(&sw_l[par ^ 1][64 * c]));
@@ -519,10 +633,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_down_kernel(PrefillArgs a
         v4f acc[16];
 #pragma unroll
         for (int u = 0; u < 16; ++u) acc[u] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-        k_loop(acc, L, IB, stages, sw_of, next_lists);
+        k_loop<kMx>(acc, L, IB, stages, sw_of, next_lists);
         if (more) {
-            L = down_loop(a, tn, wave, lane);
-            issue_first(L, IB, stages);
+            L = down_loop<kMx>(a, tn, wave, lane);
+            issue_first<kMx>(L, IB, stages);
         }
         // bf16 partial rows (round to nearest even) by route id; lane holds
         // output rows sub * 256 + 64 wn + 16 j + 4 kg + v of route
@@ -545,6 +659,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_down_kernel(PrefillArgs a
     }
 }
 
+}  // namespace
+
+__global__ __launch_bounds__(kThreads, 1) void prefill_down_kernel(PrefillArgs a) { down_tiles<false>(a); }
+__global__ __launch_bounds__(kThreads, 1) void prefill_down_mx_kernel(PrefillArgs a) { down_tiles<true>(a); }
+
 int prefill_tile_m() { return kBM; }
 
 bool prefill_supported(int M, int h, int i, int k) {
@@ -566,19 +685,21 @@ static int persistent_grid() {
     return cached[dev];
 }
 
-hipError_t launch_prefill_gate_up(const PrefillArgs& a, int R, hipStream_t stream) {
-    (void)R;
+// mx: the weights are MXFP4 (w13 / w2 codes with e13 / e2 scales), else FP8
+// (with s13 / s2).
+hipError_t launch_prefill_gate_up(const PrefillArgs& a, bool mx, hipStream_t stream) {
     const int g = persistent_grid();
     if (g <= 0) return hipErrorInvalidDevice;
-    hipLaunchKernelGGL(prefill_gate_up_kernel, dim3(g), dim3(kThreads), 0, stream, a);
+    if (mx) hipLaunchKernelGGL(prefill_gate_up_mx_kernel, dim3(g), dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL(prefill_gate_up_kernel, dim3(g), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
-hipError_t launch_prefill_down(const PrefillArgs& a, int R, hipStream_t stream) {
-    (void)R;
+hipError_t launch_prefill_down(const PrefillArgs& a, bool mx, hipStream_t stream) {
     const int g = persistent_grid();
     if (g <= 0) return hipErrorInvalidDevice;
-    hipLaunchKernelGGL(prefill_down_kernel, dim3(g), dim3(kThreads), 0, stream, a);
+    if (mx) hipLaunchKernelGGL(prefill_down_mx_kernel, dim3(g), dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL(prefill_down_kernel, dim3(g), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -63,9 +63,10 @@ enum {
  * all resident at once, provided its grid fits 512 workgroups: every unit
  * (selected expert x 128-column block of the intermediate) is split into 8
  * or 4 parts (for h 2048, i 768, E 128, top-8 that is M <= 2); other batches
- * with few routes per expert run weight-streaming GEMMs; batches with many
- * routes per expert (M*k >= 32*E) run tiled MFMA grouped GEMMs with the SiLU
- * requantisation fused into the gate/up epilogue. */
+ * with few routes per expert run weight-streaming GEMMs; batches with at
+ * least 8 routes per expert on average (M*k >= 8*E) and h % 256 == 0 run
+ * tiled MFMA grouped GEMMs with the SiLU requantisation fused into the
+ * gate/up epilogue. */
 #define MOE_FP8_PATH_STREAM 0
 #define MOE_FP8_PATH_PREFILL 1
 #define MOE_FP8_PATH_FUSED_DECODE 2
@@ -271,13 +272,22 @@ int moe_fp8_router_gemm_topk(const void* x, const void* wr, int M, int h, int E,
  * requantisation and the rank-order combine are those of moe_fp8_forward;
  * the GEMMs run on the block-scaled FP4 x FP8 matrix cores and accumulate in
  * fp32 (the result differs from the float64 dequantised reference by the
- * matrix cores' block-sum rounding).  Every batch size takes the
- * weight-streaming kernels.  The workspace (>= moe_mxfp4_workspace_bytes,
+ * matrix cores' block-sum rounding).  Batches with M*k >= 12*E take the
+ * tiled kernels of the FP8 prefill path (bf16 partials, as there) when
+ * h % 256 == 0; the rest take the weight-streaming kernels (fp32 partials).
+ * The workspace (>= moe_mxfp4_workspace_bytes,
  * 256-byte aligned) follows the rules of moe_fp8_forward_ws: its head must
  * be zero before the first forward (moe_fp8_workspace_init).  x, logits, out,
  * w13 and w2 16-byte aligned, e13 and e2 4-byte aligned, else
  * MOE_ERR_INVALID; shapes as moe_fp8_forward_ws.  Enqueued on `stream`. */
 size_t moe_mxfp4_workspace_bytes(int M, int h, int i, int E, int k);
+/* The workspace layout of an MXFP4 forward with these sizes, as
+ * moe_fp8_workspace_layout (path is MOE_FP8_PATH_STREAM or _PREFILL). */
+int moe_mxfp4_workspace_layout(int M, int h, int i, int E, int k, moe_fp8_ws_layout* layout);
+/* Stage count and kernel name(s) of stage j of an MXFP4 forward with these
+ * sizes, as moe_fp8_forward_kernel_count / _name. */
+int moe_mxfp4_forward_kernel_count(int M, int h, int i, int E, int k);
+const char* moe_mxfp4_forward_kernel_name(int M, int h, int i, int E, int k, int j);
 int moe_mxfp4_forward_ws(const void* x, const float* router_logits,
                          const void* w13, const void* e13, const void* w2, const void* e2,
                          void* out, int M, int h, int i, int E, int k,

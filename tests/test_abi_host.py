@@ -156,6 +156,47 @@ def test_workspace_layout_regions(lib, M, h, i, E, k):
     assert L.total == moe.workspace_bytes(M, h, i, E, k)
 
 
+@pytest.mark.parametrize("M,h,i,E,k", [(1, 2048, 768, 128, 8), (2, 2048, 768, 128, 8), (3, 2048, 768, 128, 8),
+                                       (127, 2048, 768, 128, 8), (128, 2048, 768, 128, 8), (40, 384, 128, 2, 1),
+                                       (40, 256, 128, 2, 1), (64, 6144, 768, 128, 4), (256, 6144, 768, 128, 4)])
+def test_fp8_path_rule(lib, M, h, i, E, k):
+    """The FP8 forward's path: the one-kernel path for the smallest batches
+    whose grid fits, else the tiled kernels when M*k >= 8*E and h is a
+    multiple of 256, else the streaming kernels."""
+    import fp8_block_scaled_router_amd as moe
+    path = moe.workspace_layout(M, h, i, E, k).path
+    if path != moe.PATH_FUSED_DECODE:
+        tiled = M * k >= 8 * E and h % 256 == 0
+        assert path == (moe.PATH_PREFILL if tiled else moe.PATH_STREAM)
+    assert (path == moe.PATH_FUSED_DECODE) == (M <= 2 and h == 2048)
+
+
+@pytest.mark.parametrize("M,h,i,E,k", [(1, 128, 128, 1, 1), (64, 6144, 768, 128, 4), (300, 256, 128, 4, 2),
+                                       (1200, 2048, 768, 8, 2), (8192, 2048, 768, 128, 8), (200, 640, 384, 4, 2),
+                                       (191, 2048, 768, 128, 8), (192, 2048, 768, 128, 8)])
+def test_mxfp4_layout_and_path(lib, M, h, i, E, k):
+    """The MXFP4 forward's path: the tiled kernels when M*k >= 12*E and h is a
+    multiple of 256, else the streaming kernels (no one-kernel path); its
+    stage names follow, and its regions fit its workspace."""
+    import fp8_block_scaled_router_amd as moe
+    L = moe.mxfp4_workspace_layout(M, h, i, E, k)
+    tiled = M * k >= 12 * E and h % 256 == 0
+    assert L.path == (moe.PATH_PREFILL if tiled else moe.PATH_STREAM)
+    assert L.total == moe.mxfp4_workspace_bytes(M, h, i, E, k)
+    names = moe.moe_mxfp4_stage_names(M, h, i, E, k)
+    if tiled:
+        assert names == ["route_quant_kernel", "group_hist+group_scatter", "prefill_gate_up_mx_kernel",
+                         "prefill_down_mx_kernel", "combine_bf16_kernel"]
+        assert L.act2 + M * k * i <= L.total and L.partial + 2 * M * k * h <= L.total
+        assert L.gate_up == 2 ** 64 - 1
+    else:
+        assert names[-3:] == ["stream_gate_up_mx_kernel", "stream_down_mx_kernel", "combine_kernel"]
+        assert L.gate_up + 4 * M * k * 2 * i <= L.total and L.partial + 4 * M * k * h <= L.total
+        assert L.act2 == 2 ** 64 - 1
+    assert lib.moe_mxfp4_forward_kernel_count(M, h, i, E, k) == len(names)
+    assert lib.moe_mxfp4_forward_kernel_name(M, h, i, E, k, len(names)) is None
+
+
 def test_status_and_probe_argument_checks(lib):
     """The status reader and the measurement probes reject bad arguments
     before any HIP call."""

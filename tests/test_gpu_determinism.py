@@ -117,10 +117,12 @@ def test_layer_deterministic_stream_path_many_routes(moe_mod):
     assert path == moe_mod.PATH_STREAM
 
 
-def test_mxfp4_layer_deterministic(moe_mod):
+@pytest.mark.parametrize("ci", [3, 4])
+def test_mxfp4_layer_deterministic(moe_mod, ci):
     """The MXFP4-weight layer at its own shape (h 6144, i 768, E 128, top-4,
-    64 tokens), random E2M1 codes and E8M0 scales near 2^-8."""
-    ci = 3
+    64 tokens: the streaming kernels) and at the prefill batch's (8192 tokens,
+    h 2048, i 768, E 128, top-8: the tiled kernels), random E2M1 codes and
+    E8M0 scales near 2^-8."""
     cfg = synth.CONFIGS[ci]
     seed = synth.default_seed(ci)
     M, h, i, E, k = cfg.M, cfg.h, cfg.i, cfg.E, cfg.k

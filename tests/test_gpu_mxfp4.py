@@ -16,7 +16,8 @@ import torch
 
 import oracle
 import synth
-from gpu_util import check_output, flip_allowance, log, mfma_rel, r16_report, read_ws, to_dev_bf16, to_host_bits, _T64
+from gpu_util import (check_output, flagged_codes, flip_allowance, log, mfma_rel, r16_report, read_ws,
+                      to_dev_bf16, to_host_bits, _T64)
 
 pytestmark = pytest.mark.gpu
 
@@ -85,16 +86,17 @@ def _run(moe_mod, L):
     torch.cuda.synchronize()
     got = to_host_bits(out)
     assert np.array_equal(to_host_bits(out2), got), "not deterministic"
-    # The MXFP4 forward always lays its workspace out as the FP8 layer's
-    # streaming path does; ids and activation codes sit at the same offsets
-    # on every path, the gate/up values only where the FP8 layer streams too.
-    lay = moe_mod.workspace_layout(M, h, i, E, k)
+    lay = moe_mod.mxfp4_workspace_layout(M, h, i, E, k)
     R = M * k
     ws_int = dict(ids=read_ws(ws, lay.topk_ids, R, np.int32).reshape(M, k),
                   xq=read_ws(ws, lay.xq, M * h, np.uint8).reshape(M, h),
                   xs=read_ws(ws, lay.xs, M * (h // 128), np.float32).reshape(M, h // 128),
                   g=read_ws(ws, lay.gate_up, R * 2 * i, np.float32).reshape(R, 2 * i)
-                  if lay.path == moe_mod.PATH_STREAM else None)
+                  if lay.path == moe_mod.PATH_STREAM else None,
+                  sorted=read_ws(ws, lay.sorted, R, np.int32),
+                  a2=read_ws(ws, lay.act2, R * i, np.uint8).reshape(R, i)
+                  if lay.path == moe_mod.PATH_PREFILL else None,
+                  path=lay.path)
     return got, ws_int
 
 
@@ -117,6 +119,19 @@ def _check_layer(moe_mod, L, tokens=None):
         bar = mfma_rel(cfg.h // 128)
         log(f"  gate/up: max |gpu - oracle| / sum|terms| = {ratio.max():.3g} (bar {bar:.3g})")
         assert ratio.max() <= bar
+    if wsi["a2"] is not None and tokens is None:
+        # tiled path: the requantised codes (sorted-route order) are the
+        # oracle's, except where the decision sits on a rounding boundary that
+        # the block sums may take either way (then a code within the bracket)
+        a2 = np.empty_like(wsi["a2"])
+        a2[wsi["sorted"]] = wsi["a2"]
+        lo, hi, _ = flagged_codes(L, inter, terms=terms)
+        clear = lo == hi
+        assert np.array_equal(a2[clear], inter["a2"][clear]), "requantised codes differ"
+        T = _T64()
+        fl = ~clear
+        assert np.all((T[a2[fl]] >= T[lo[fl]]) & (T[a2[fl]] <= T[hi[fl]])), "requantised code outside its bracket"
+        log(f"  requantised codes: {int(fl.sum())} of {fl.size} on a rounding boundary")
     allow = flip_allowance(L, inter, terms=terms, w2_dense=L.w2_dense)
     r16_report(f"mxfp4_{cfg.name}_m{cfg.M}_h{cfg.h}_i{cfg.i}_e{cfg.E}_top{k}", got[tok], ref, allow)
     err, mx, cos = check_output(got[tok], ref, allowance=allow)
@@ -147,6 +162,17 @@ def test_mxfp4_edge_shapes(moe_mod, M, h, i, E, k):
     (i 2048: 16 K blocks in the down GEMM)."""
     cfg = synth.LayerConfig("mx_edge", M, h, i, E, k, "normal", "test shape")
     _check_layer(moe_mod, _MxLayer(cfg, 91 + M))
+
+
+@pytest.mark.timeout(600)
+def test_mxfp4_tiled_path(moe_mod):
+    """A batch on the tiled kernels: 1200 tokens over 8 experts, top-2, so each
+    expert holds about 300 routes (two full 128-route tiles and a ragged
+    third); h 2048 (8 row tiles of the down GEMM, 16 K blocks of gate/up),
+    i 768 (6 column groups, 6 K blocks of the down GEMM)."""
+    cfg = synth.LayerConfig("mx_tiled", 1200, 2048, 768, 8, 2, "normal", "test shape")
+    assert moe_mod.mxfp4_workspace_layout(cfg.M, cfg.h, cfg.i, cfg.E, cfg.k).path == moe_mod.PATH_PREFILL
+    _check_layer(moe_mod, _MxLayer(cfg, 1207))
 
 
 def test_mxfp4_zero_input(moe_mod):

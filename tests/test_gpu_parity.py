@@ -287,7 +287,7 @@ def _custom_layer(dev, M, h, i, E, k, seed, logits_kind="normal"):
 
 @pytest.mark.parametrize("M,h,i,E,k", [
     (3, 384, 256, 6, 3),        # ragged K-block counts (3 and 2)
-    (40, 256, 128, 2, 1),       # 20 routes per expert: two token groups per expert
+    (40, 384, 128, 2, 1),       # streaming path (h % 256 != 0), 20 routes per expert: two token groups
     (5, 256, 128, 1, 1),        # one expert, k = 1
     (4, 256, 128, 8, 8),        # k = E
     (7, 1280, 640, 256, 16),    # E = 256, k = 16
@@ -365,7 +365,7 @@ def test_mfma_block_sum_accuracy(dev, moe_mod):
     weight-streaming path lies within mfma_rel(KB) * sum|terms| of the exact
     float64 value computed from the same codes and scales -- the bound of
     any fp32 order of the block sum, which the flip analysis relies on."""
-    M, h, i, E, k = 40, 512, 256, 4, 2
+    M, h, i, E, k = 40, 512, 256, 16, 2
     L = _custom_layer(dev, M, h, i, E, k, seed=4242)
     lay = moe_mod.workspace_layout(M, h, i, E, k)
     assert lay.path == moe_mod.PATH_STREAM
@@ -448,18 +448,18 @@ def test_stream_then_fused_on_one_workspace(dev, moe_mod):
     """A workspace used by the multi-kernel path and then the one-kernel
     path, both outputs checked against the oracle."""
     h, i, E, k = 256, 128, 8, 2
-    cfg = synth.LayerConfig("m40", 40, h, i, E, k, "normal", "mix")
-    L40 = Layer(cfg, 91, dev)
-    assert moe_mod.workspace_layout(40, h, i, E, k).path == moe_mod.PATH_STREAM
-    ws = moe_mod.alloc_workspace(40, h, i, E, k, device=dev)
-    out = moe_mod.moe_fp8_forward_ws(L40.tx, L40.tl, L40.t13, L40.ts13, L40.t2, L40.ts2, k, ws)
+    cfg = synth.LayerConfig("m24", 24, h, i, E, k, "normal", "mix")
+    L24 = Layer(cfg, 91, dev)
+    assert moe_mod.workspace_layout(24, h, i, E, k).path == moe_mod.PATH_STREAM
+    ws = moe_mod.alloc_workspace(24, h, i, E, k, device=dev)
+    out = moe_mod.moe_fp8_forward_ws(L24.tx, L24.tl, L24.t13, L24.ts13, L24.t2, L24.ts2, k, ws)
     torch.cuda.synchronize()
-    check_output(to_host_bits(out), L40.oracle())
+    check_output(to_host_bits(out), L24.oracle())
     for M in (3, 1):
         assert moe_mod.workspace_layout(M, h, i, E, k).path == moe_mod.PATH_FUSED_DECODE
         cfgm = synth.LayerConfig(f"m{M}", M, h, i, E, k, "normal", "mix")
-        Lm = Layer(cfgm, 91, dev, x=L40.x[:M], logits=L40.logits[:M],
-                   weights=(L40.q13, L40.s13, L40.q2, L40.s2))
+        Lm = Layer(cfgm, 91, dev, x=L24.x[:M], logits=L24.logits[:M],
+                   weights=(L24.q13, L24.s13, L24.q2, L24.s2))
         out = moe_mod.moe_fp8_forward_ws(Lm.tx, Lm.tl, Lm.t13, Lm.ts13, Lm.t2, Lm.ts2, k, ws)
         torch.cuda.synchronize()
         _check_sync_clean(ws)
