@@ -11,11 +11,14 @@ Timing: the forwards of C rotation copies (distinct weight copies and
 inputs, together far larger than the 256 MB Infinity Cache, so every step
 streams its experts from HBM) are captured in one HIP graph; W warm-up steps,
 then exactly K timed steps between a synchronisation and HIP events on both
-sides.  A second pass times graph replays of the same forwards cut after
-their first j stages (j = 1..n, HIP events around the replays); the
-differences give each stage's mean duration, and the dominant stage is
-reported against its roofline.  The CPU baseline is the oracle (plain C, all host
-threads) on a bounded sample of the same workload.
+sides.  Each stage's mean duration comes from the GPU's own stamps of its
+dispatches: the library's timed entry launches the stage's kernels with HIP
+start / stop events (hipExtLaunchKernel) in eager forwards on the launch
+stream, queued behind a GPU spin; the dominant stage is reported against its
+roofline.  The differences of graph replays of the forwards cut after their
+first j stages are recorded beside them (stage_us_cut_graphs).  The CPU
+baseline is the oracle (plain C, all host threads) on a bounded sample of the
+same workload.
 """
 from __future__ import annotations
 
@@ -370,7 +373,23 @@ def mxfp4_bench(args):
     for j in range(1, len(names) + 1):
         tj, _, _ = time_single_kernel(lambda c, j=j: fwd(c, j), C, args)
         T.append(tj)
-    stage_ms = np.maximum(np.diff(np.array(T)), 0.0)
+    cut_ms = np.maximum(np.diff(np.array(T)), 0.0)
+    # stage durations from the GPU's stamps of each stage's dispatches
+    nst = len(names)
+    nf = max(1, args.timing_replays) * C
+    evs = [moe.HipEvents(2 * nst) for _ in range(nf)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(20_000_000)
+        for f, ev in enumerate(evs):
+            c = f % C
+            a = W[c]
+            moe.moe_mxfp4_forward_ws_timed(X[c], Lg[c], a[0], a[1], a[2], a[3], k, WS[c], ev, out=OUT[c])
+    torch.cuda.synchronize()
+    stage_ms = np.array([[ev.elapsed_ms(2 * j, 2 * j + 1) for j in range(nst)] for ev in evs]).mean(axis=0)
+    for ev in evs:
+        ev.close()
     dom = int(np.argmax(stage_ms))
     Um = float(np.mean(U))
     # The FP4 x FP8 form of the block-scaled MFMA issues at the FP8 rate (32
@@ -391,7 +410,9 @@ def mxfp4_bench(args):
                    "M": M, "h": h, "i": i, "E": E, "k": k, "rotation_copies": C, "distinct_experts_mean": Um,
                    "layer_bytes_per_step": int(fw_bytes),
                    "stage_us": {n: round(float(t) * 1e3, 3) for n, t in zip(names, stage_ms)},
-                   "timing": "HIP graph of C forwards; stages from graphs of forwards cut after each stage"},
+                   "stage_us_cut_graphs": {n: round(float(t) * 1e3, 3) for n, t in zip(names, cut_ms)},
+                   "timing": "HIP graph of C forwards; stages from the GPU's stamps of their dispatches "
+                             f"(hipExtLaunchKernel events, mean of {nf} eager forwards)"},
         "roofline": {"bound": bound, "kernel": names[dom], "achieved": round(achieved, 2), "peak": peak,
                      "unit": unit, "frac": round(frac, 4),
                      "traffic": load_traffic(names[dom], workload),
@@ -503,9 +524,11 @@ def rotation_copies(cfg, U0, args):
 def time_layer(moe, cfg, W, X, Lg, WS, OUT, steps, warmup, timing_replays):
     """Graph-replay timing of the C rotation copies' forwards: W warm-up and
     exactly `steps` timed forwards between a synchronisation and HIP events
-    on both sides; then stage durations from graphs of the same forwards cut
-    after their first j stages.  Returns (ms per forward, stage names, stage
-    ms, number of forwards per cut)."""
+    on both sides; then stage durations two ways: from graphs of the same
+    forwards cut after their first j stages (differences), and from the GPU's
+    stamps of each stage's dispatches in eager forwards.  Returns (ms per
+    forward, stage names, cut-graph stage ms, forwards per measurement,
+    stamped stage ms)."""
     import numpy as np
     import torch
     M, h, i, E, k = cfg.M, cfg.h, cfg.i, cfg.E, cfg.k
@@ -575,7 +598,23 @@ def time_layer(moe, cfg, W, X, Lg, WS, OUT, steps, warmup, timing_replays):
             del gj
     run_steps(C)   # the full forwards leave every copy's output complete again
     torch.cuda.synchronize()
-    return ms_per_step, names, np.maximum(np.diff(np.array(T)), 0.0), reps * C
+
+    # The same stages timed directly: the library's timed entry launches each
+    # stage's kernels with HIP events that the GPU stamps at the start of the
+    # stage's first dispatch and the end of its last, in reps * C eager
+    # forwards on the launch stream, queued behind a GPU spin.
+    evs = [moe.HipEvents(2 * nst) for _ in range(reps * C)]
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(20_000_000)
+        for f, ev in enumerate(evs):
+            c = f % C
+            a = W[c]
+            moe.moe_fp8_forward_ws_timed(X[c], Lg[c], a[0], a[1], a[2], a[3], k, WS[c], ev, out=OUT[c])
+    torch.cuda.synchronize()
+    ev_ms = np.array([[ev.elapsed_ms(2 * j, 2 * j + 1) for j in range(nst)] for ev in evs]).mean(axis=0)
+    for ev in evs:
+        ev.close()
+    return ms_per_step, names, np.maximum(np.diff(np.array(T)), 0.0), reps * C, ev_ms
 
 
 def layer_record(cfg, names, stage_ms, U_mean, ms_per_step, count, traffic_workload=None):
@@ -595,8 +634,9 @@ def layer_record(cfg, names, stage_ms, U_mean, ms_per_step, count, traffic_workl
                 "avg_launch_us": round(stage_ms[dom] * 1e3, 3),
                 "algorithmic_bytes_per_launch": int(abytes),
                 "algorithmic_flops_per_launch": aflops,
-                "timing": f"HIP-graph replays of forwards cut after each stage, differences, "
-                          f"{count} forwards per cut"}
+                "timing": f"start / end of the stage's dispatches as the GPU stamps them (HIP events passed to "
+                          f"hipExtLaunchKernel by the library's timed entry), mean of {count} eager forwards on "
+                          f"the launch stream"}
     forward = {"bound": bound, "achieved": round(fa, 2), "peak": peak, "unit": unit, "frac": round(ff, 4),
                "algorithmic_bytes": int(fw_bytes), "algorithmic_flops": fw_flops,
                "timing": "HIP graph of the rotation copies' forwards, events around the timed steps"}
@@ -677,7 +717,7 @@ def other_config_records(moe, args, skip, dev):
         U = [int(WS[c][lay.num_active:lay.num_active + 4].view(torch.int32).item()) for c in range(C)]
         assert all(torch.isfinite(OUT[c].float()).all().item() for c in range(C))
         steps = C * max(1, math.ceil(args.other_steps / C))
-        ms, names, stage_ms, count = time_layer(moe, cfg, W, X, Lg, WS, OUT, steps, C, args.timing_replays)
+        ms, names, cut_ms, count, stage_ms = time_layer(moe, cfg, W, X, Lg, WS, OUT, steps, C, args.timing_replays)
         errs = [moe.workspace_error(WS[c]) for c in range(C)]
         U_mean = float(np.mean(U))
         roofline, forward = layer_record(cfg, names, stage_ms, U_mean, ms, count)
@@ -686,6 +726,7 @@ def other_config_records(moe, args, skip, dev):
             "path": {0: "stream", 1: "prefill", 2: "one-kernel"}[lay.path],
             "rotation_copies": C, "distinct_experts_mean": U_mean,
             "stage_us": {n: round(v * 1e3, 3) for n, v in zip(names, stage_ms)},
+            "stage_us_cut_graphs": {n: round(v * 1e3, 3) for n, v in zip(names, cut_ms)},
             "roofline": roofline, "forward": forward, "sync_errors": int(sum(e != 0 for e in errs)),
             "weights": "GPU-drawn N(0, 1/sqrt(K)), library block quantisation",
             "wall_s": round(time.time() - t0, 1)}
@@ -856,8 +897,8 @@ def main():
     U = [int(WS[c][lay.num_active:lay.num_active + 4].view(torch.int32).item()) for c in range(C)]
     assert all(torch.isfinite(OUT[c].float()).all().item() for c in range(C))
 
-    ms_per_step, names, stage_ms, count = time_layer(moe, cfg, W, X, Lg, WS, OUT, args.steps, args.warmup,
-                                                     args.timing_replays)
+    ms_per_step, names, cut_ms, count, stage_ms = time_layer(moe, cfg, W, X, Lg, WS, OUT, args.steps,
+                                                             args.warmup, args.timing_replays)
     errs = [moe.workspace_error(WS[c]) for c in range(C)]
     if any(errs):
         print(f"bench.py: a wait between workgroups timed out in {sum(e != 0 for e in errs)} workspaces",
@@ -905,6 +946,7 @@ def main():
                    "layer_bytes_per_step": int(fw_bytes),
                    "timing": "HIP graph of C forwards, events around K steps",
                    "stage_us": {n: round(v * 1e3, 3) for n, v in zip(names, stage_ms)},
+                   "stage_us_cut_graphs": {n: round(v * 1e3, 3) for n, v in zip(names, cut_ms)},
                    "setup_s": round(setup_s, 1)},
         "roofline": roofline,
         "forward": forward,

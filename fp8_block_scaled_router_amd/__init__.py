@@ -59,6 +59,7 @@ _SIGS = {
     "moe_fp8_forward_ws": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _SZ, _P]),
     "moe_fp8_workspace_layout": (_I, [_I, _I, _I, _I, _I, ctypes.POINTER(WsLayout)]),
     "moe_mxfp4_workspace_layout": (_I, [_I, _I, _I, _I, _I, ctypes.POINTER(WsLayout)]),
+    "moe_mxfp4_forward_ws_timed": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _SZ, _P, _I, _P]),
     "router_topk": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "moe_fp8_router_gemm_topk": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P]),
     "moe_mxfp4_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
@@ -321,6 +322,30 @@ def moe_mxfp4_forward_ws(x, router_logits, w13, e13, w2, e2, k: int, workspace, 
     return out
 
 
+def moe_mxfp4_forward_ws_timed(x, router_logits, w13, e13, w2, e2, k: int, workspace, events, out=None,
+                               stream=None):
+    """moe_mxfp4_forward_ws whose stage j stamps its start and end into events
+    2j and 2j + 1 (HipEvents of at least twice the stage count)."""
+    M, h = x.shape
+    E = router_logits.shape[1]
+    i = w2.shape[2] * 2
+    _dev(x, torch.bfloat16, "x", (M, h))
+    _dev(router_logits, torch.float32, "router_logits", (M, E))
+    _dev(w13, torch.uint8, "w13", (E, 2 * i, h // 2))
+    _dev(e13, torch.uint8, "e13", (E, 2 * i, h // 32))
+    _dev(w2, torch.uint8, "w2", (E, h, i // 2))
+    _dev(e2, torch.uint8, "e2", (E, h, i // 32))
+    _dev(workspace, torch.uint8, "workspace")
+    if out is None:
+        out = torch.empty((M, h), dtype=torch.bfloat16, device=x.device)
+    _dev(out, torch.bfloat16, "out", (M, h))
+    _check(lib().moe_mxfp4_forward_ws_timed(_ptr(x), _ptr(router_logits), _ptr(w13), _ptr(e13), _ptr(w2), _ptr(e2),
+                                            _ptr(out), M, h, i, E, int(k), _ptr(workspace), workspace.numel(),
+                                            events.handles, events.n, _stream(stream)),
+           "moe_mxfp4_forward_ws_timed")
+    return out
+
+
 def router_gemm_topk(x, wr, k: int, want_logits: bool = True, out=None, stream=None):
     """BF16 routing fused with the top-k: bf16 hidden rows x [M, h] and a bf16
     router weight wr [E, h] -> (logits fp32 [M, E] or None, ids int32 [M, k],
@@ -461,7 +486,8 @@ def moe_fp8_forward_ws_prefix(x, router_logits, w13, s13, w2, s2, k: int, worksp
 
 def moe_fp8_forward_ws_timed(x, router_logits, w13, s13, w2, s2, k: int, workspace, events: HipEvents,
                              out=None, stream=None):
-    """moe_fp8_forward_ws that also records events between its stages."""
+    """moe_fp8_forward_ws whose stage j stamps its start and end into events
+    2j and 2j + 1 (HipEvents of at least twice the stage count)."""
     M, h, i, E, out = _layer_args(x, router_logits, w13, s13, w2, s2, k, out)
     _dev(workspace, torch.uint8, "workspace")
     rc = lib().moe_fp8_forward_ws_timed(_ptr(x), _ptr(router_logits), _ptr(w13), _ptr(s13), _ptr(w2),

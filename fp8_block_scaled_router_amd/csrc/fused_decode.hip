@@ -45,6 +45,7 @@
 // last workgroup to exit advances the forward tag.
 #include "device.h"
 #include "fused_decode.h"
+#include "launch.h"
 
 namespace moe {
 
@@ -767,7 +768,7 @@ static hipError_t launch_instance(const FusedArgs& args, int grid, size_t lds, h
         cached_lds[dev] = lds;
     }
     if (cached_cu[dev] * cached_blocks[dev] < grid) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fused_decode_kernel<P, MM>), dim3(grid), dim3(256), lds, stream, args);
+    launch((fused_decode_kernel<P, MM>), dim3(grid), dim3(256), lds, stream, args);
     return hipGetLastError();
 }
 

@@ -175,10 +175,10 @@ hipError_t launch_group(const int32_t* ids, int R, int E, int32_t* hist, int32_t
                         int32_t* offsets, int32_t* sorted, int32_t* active, int32_t* num_active,
                         hipStream_t stream, int tile_m, int32_t* mtile_off) {
     const int nchunks = group_chunks(R);
-    hipLaunchKernelGGL(group_hist_kernel, dim3(nchunks), dim3(kChunk), 0, stream, ids, R, E, hist);
+    launch(group_hist_kernel, dim3(nchunks), dim3(kChunk), 0, stream, ids, R, E, hist);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(group_scatter_kernel, dim3(nchunks), dim3(256 * kScanGroups), 0, stream, ids, R, E, nchunks,
+    launch(group_scatter_kernel, dim3(nchunks), dim3(256 * kScanGroups), 0, stream, ids, R, E, nchunks,
                        hist, counts, offsets, sorted, active, num_active, tile_m, mtile_off);
     return hipGetLastError();
 }

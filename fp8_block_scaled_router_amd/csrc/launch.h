@@ -2,11 +2,35 @@
 // library; the public C ABI is include/moe_fp8.h).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace moe {
+
+// Stage timestamps of a measured forward.  While the calling thread's stamp
+// is armed, the forward's kernels launch through hipExtLaunchKernel with its
+// events: the stage's first dispatch records its start in `start`, and every
+// dispatch records its end in `stop`, so start..stop spans the stage's
+// kernels as the GPU stamps their dispatches (no marker between them).
+struct StageStamp {
+    hipEvent_t start;
+    hipEvent_t stop;
+};
+StageStamp& stage_stamp();   // thread-local
+
+template <typename... KArgs, typename... Args>
+inline void launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t lds, hipStream_t stream,
+                   Args... args) {
+    StageStamp& st = stage_stamp();
+    if (st.start == nullptr && st.stop == nullptr) {
+        hipLaunchKernelGGL(kernel, grid, block, lds, stream, args...);
+        return;
+    }
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, st.start, st.stop, 0, args...);
+    st.start = nullptr;
+}
 
 // Router and/or 1x128 activation quantisation, one workgroup per token.
 enum { kRoute = 1, kQuant = 2 };

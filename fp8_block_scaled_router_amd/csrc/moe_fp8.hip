@@ -13,6 +13,13 @@
 #include "fused_decode.h"
 #include "launch.h"
 
+namespace moe {
+StageStamp& stage_stamp() {
+    static thread_local StageStamp s{nullptr, nullptr};
+    return s;
+}
+}  // namespace moe
+
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -166,20 +173,22 @@ const char* stage_name_mx(int path, int M, int k, int j) {
     return kStreamMxStages[j];
 }
 
-// Records events[j] (when given) before stage j, and events[n] after the last.
-// Stage bookkeeping of one forward: an optional event before every stage
-// and after the last, and an optional cut after `limit` stages.
+// Stage bookkeeping of one forward: optional timing events per stage
+// (events[2j] and events[2j + 1] take the GPU's stamps of the start of stage
+// j's first dispatch and the end of its last; armed on this thread while the
+// stage launches), and an optional cut after `limit` stages.
 struct EventHook {
     hipEvent_t* ev;
     int n;
-    int next = 0;
+    int next = 0;   // stage whose events come next
     hipStream_t s;
     int limit = 1 << 30;
     int stage = 0;
-    hipError_t mark() {
-        if (!ev || next >= n) return hipSuccess;
-        return hipEventRecord(ev[next++], s);
+    void arm() {
+        if (ev && 2 * next + 1 < n) moe::stage_stamp() = moe::StageStamp{ev[2 * next], ev[2 * next + 1]};
+        ++next;
     }
+    static void disarm() { moe::stage_stamp() = moe::StageStamp{nullptr, nullptr}; }
     bool cut() { return stage++ >= limit; }
 };
 
@@ -217,12 +226,13 @@ int run_forward(const void* x, const float* router_logits, const void* w13, cons
     EventHook hook{events, n_events, 0, stream, n_stages};
     uint32_t* sync = at<uint32_t>(workspace, 0);
 
-#define MOE_STEP(call)                                      \
-    do {                                                    \
-        if (hook.cut()) return MOE_OK;                      \
-        if (hook.mark() != hipSuccess) return MOE_ERR_HIP; \
-        rc = hip_status(call);                              \
-        if (rc != MOE_OK) return rc;                        \
+#define MOE_STEP(call)                 \
+    do {                               \
+        if (hook.cut()) return MOE_OK; \
+        hook.arm();                    \
+        rc = hip_status(call);         \
+        EventHook::disarm();           \
+        if (rc != MOE_OK) return rc;   \
     } while (0)
 
     if (p.path == MOE_FP8_PATH_FUSED_DECODE) {
@@ -252,7 +262,7 @@ int run_forward(const void* x, const float* router_logits, const void* w13, cons
         fa.t_ll = fa.v_ll + moe::fused_v_words(M, i, k);
         fa.sync = sync;
         MOE_STEP(moe::launch_fused_decode(fa, stream));
-        return hook.mark() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+        return MOE_OK;
     }
     if (p.path == MOE_FP8_PATH_STREAM && small_group(M, k)) {
         MOE_STEP(moe::launch_route_quant_group(router_logits, static_cast<const uint16_t*>(x), M, E, k, h,
@@ -287,7 +297,7 @@ int run_forward(const void* x, const float* router_logits, const void* w13, cons
         MOE_STEP(moe::launch_prefill_gate_up(pa, false, stream));
         MOE_STEP(moe::launch_prefill_down(pa, false, stream));
         MOE_STEP(moe::launch_combine_bf16(pa.y, tw, M, k, h, static_cast<uint16_t*>(out), stream));
-        return hook.mark() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+        return MOE_OK;
     }
     if (!small_group(M, k))
         MOE_STEP(moe::launch_group(ids, R, E, hist, counts, offsets, sorted, active, num_active,
@@ -306,7 +316,7 @@ int run_forward(const void* x, const float* router_logits, const void* w13, cons
     MOE_STEP(moe::launch_stream_down(sa, g, static_cast<const uint8_t*>(w2), s2, y, stream));
     MOE_STEP(moe::launch_combine(y, tw, M, k, h, static_cast<uint16_t*>(out), stream));
 #undef MOE_STEP
-    return hook.mark() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    return MOE_OK;
 }
 
 // The MXFP4-weight layer: routing, quantisation and grouping as in the FP8
@@ -314,7 +324,8 @@ int run_forward(const void* x, const float* router_logits, const void* w13, cons
 // batches) the tiled MXFP4 GEMMs and the bf16 combine.
 int run_forward_mx(const void* x, const float* router_logits, const void* w13, const void* e13, const void* w2,
                    const void* e2, void* out, int M, int h, int i, int E, int k, void* workspace,
-                   size_t workspace_bytes, hipStream_t stream, int n_stages = 1 << 30) {
+                   size_t workspace_bytes, hipStream_t stream, int n_stages = 1 << 30,
+                   hipEvent_t* events = nullptr, int n_events = 0) {
     int rc = check_shape(M, h, i, E, k);
     if (rc != MOE_OK) return rc;
     if (M == 0) return MOE_OK;
@@ -339,11 +350,13 @@ int run_forward_mx(const void* x, const float* router_logits, const void* w13, c
     int32_t* num_active = at<int32_t>(workspace, p.num_active);
     int32_t* hist = at<int32_t>(workspace, L.hist);
     uint32_t* sync = at<uint32_t>(workspace, 0);
-    EventHook hook{nullptr, 0, 0, stream, n_stages};
+    EventHook hook{events, n_events, 0, stream, n_stages};
 #define MOE_STEP(call)                 \
     do {                               \
         if (hook.cut()) return MOE_OK; \
+        hook.arm();                    \
         rc = hip_status(call);         \
+        EventHook::disarm();           \
         if (rc != MOE_OK) return rc;   \
     } while (0)
     if (p.path == MOE_FP8_PATH_PREFILL) {
@@ -446,6 +459,18 @@ int moe_mxfp4_forward_ws(const void* x, const float* router_logits, const void* 
                           stream);
 }
 
+int moe_mxfp4_forward_ws_timed(const void* x, const float* router_logits, const void* w13, const void* e13,
+                               const void* w2, const void* e2, void* out, int M, int h, int i, int E, int k,
+                               void* workspace, size_t workspace_bytes, hipEvent_t* events, int n_events,
+                               hipStream_t stream) {
+    if (!events) return MOE_ERR_INVALID;
+    const int n = moe_mxfp4_forward_kernel_count(M, h, i, E, k);
+    if (n < 0) return n;
+    if (n_events < 2 * n) return MOE_ERR_INVALID;
+    return run_forward_mx(x, router_logits, w13, e13, w2, e2, out, M, h, i, E, k, workspace, workspace_bytes,
+                          stream, 1 << 30, events, n_events);
+}
+
 int moe_mxfp4_forward_ws_prefix(const void* x, const float* router_logits, const void* w13, const void* e13,
                                 const void* w2, const void* e2, void* out, int M, int h, int i, int E, int k,
                                 void* workspace, size_t workspace_bytes, int n_stages, hipStream_t stream) {
@@ -510,7 +535,7 @@ int moe_fp8_forward_ws_timed(const void* x, const float* router_logits, const vo
     if (!events) return MOE_ERR_INVALID;
     const int n = moe_fp8_forward_kernel_count(M, h, i, E, k);
     if (n < 0) return n;
-    if (n_events < n + 1) return MOE_ERR_INVALID;
+    if (n_events < 2 * n) return MOE_ERR_INVALID;
     return run_forward(x, router_logits, w13, s13, w2, s2, out, M, h, i, E, k, workspace,
                        workspace_bytes, events, n_events, stream);
 }

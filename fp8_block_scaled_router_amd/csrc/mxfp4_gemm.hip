@@ -275,7 +275,7 @@ __global__ __launch_bounds__(256) void stream_down_mx_kernel(
 hipError_t launch_stream_gate_up_mx(const StreamArgs& a, const uint8_t* xq, const float* xs, const uint8_t* w13,
                                     const uint8_t* e13, float* g, hipStream_t stream) {
     const dim3 grid((2 * a.i) / kMxRowsPerGroup, a.max_slots);
-    hipLaunchKernelGGL(stream_gate_up_mx_kernel, grid, dim3(256), 0, stream, xq, xs, w13, e13, a.offsets,
+    launch(stream_gate_up_mx_kernel, grid, dim3(256), 0, stream, xq, xs, w13, e13, a.offsets,
                        a.sorted, a.active, a.num_active, g, a.h, a.i, a.k);
     return hipGetLastError();
 }
@@ -283,7 +283,7 @@ hipError_t launch_stream_gate_up_mx(const StreamArgs& a, const uint8_t* xq, cons
 hipError_t launch_stream_down_mx(const StreamArgs& a, const float* g, const uint8_t* w2, const uint8_t* e2,
                                  float* y, hipStream_t stream) {
     const dim3 grid(a.h / kMxRowsPerGroup, a.max_slots);
-    hipLaunchKernelGGL(stream_down_mx_kernel, grid, dim3(256), mx_down_lds_bytes(a.i), stream, g, w2, e2,
+    launch(stream_down_mx_kernel, grid, dim3(256), mx_down_lds_bytes(a.i), stream, g, w2, e2,
                        a.offsets, a.sorted, a.active, a.num_active, y, a.h, a.i, a.k);
     return hipGetLastError();
 }

@@ -690,16 +690,16 @@ static int persistent_grid() {
 hipError_t launch_prefill_gate_up(const PrefillArgs& a, bool mx, hipStream_t stream) {
     const int g = persistent_grid();
     if (g <= 0) return hipErrorInvalidDevice;
-    if (mx) hipLaunchKernelGGL(prefill_gate_up_mx_kernel, dim3(g), dim3(kThreads), 0, stream, a);
-    else hipLaunchKernelGGL(prefill_gate_up_kernel, dim3(g), dim3(kThreads), 0, stream, a);
+    if (mx) launch(prefill_gate_up_mx_kernel, dim3(g), dim3(kThreads), 0, stream, a);
+    else launch(prefill_gate_up_kernel, dim3(g), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
 hipError_t launch_prefill_down(const PrefillArgs& a, bool mx, hipStream_t stream) {
     const int g = persistent_grid();
     if (g <= 0) return hipErrorInvalidDevice;
-    if (mx) hipLaunchKernelGGL(prefill_down_mx_kernel, dim3(g), dim3(kThreads), 0, stream, a);
-    else hipLaunchKernelGGL(prefill_down_kernel, dim3(g), dim3(kThreads), 0, stream, a);
+    if (mx) launch(prefill_down_mx_kernel, dim3(g), dim3(kThreads), 0, stream, a);
+    else launch(prefill_down_kernel, dim3(g), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -287,7 +287,7 @@ hipError_t launch_route_quant(const float* logits, const uint16_t* x, int M, int
                               int32_t* ids, float* tw, uint8_t* xq, float* xs, int what,
                               hipStream_t stream) {
     if (M <= 0) return hipSuccess;
-    hipLaunchKernelGGL(route_quant_kernel, dim3((M + 3) / 4), dim3(kRouteQuantThreads), 0, stream, logits, x, M, E, k, h,
+    launch(route_quant_kernel, dim3((M + 3) / 4), dim3(kRouteQuantThreads), 0, stream, logits, x, M, E, k, h,
                        ids, tw, xq, xs, what);
     return hipGetLastError();
 }
@@ -387,7 +387,7 @@ hipError_t launch_route_quant_group(const float* logits, const uint16_t* x, int 
                                     int32_t* num_active, uint32_t* arrivals, hipStream_t stream) {
     if (M <= 0) return hipSuccess;
     if ((int64_t)M * k > kGroupTailRoutes || E > 256) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(route_quant_group_kernel, dim3(M), dim3(256), 0, stream, logits, x, E, k, h, ids,
+    launch(route_quant_group_kernel, dim3(M), dim3(256), 0, stream, logits, x, E, k, h, ids,
                        tw, xq, xs, counts, offsets, sorted, active, num_active, arrivals);
     return hipGetLastError();
 }

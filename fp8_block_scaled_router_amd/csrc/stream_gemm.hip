@@ -201,7 +201,7 @@ __global__ __launch_bounds__(256) void stream_down_kernel(
 hipError_t launch_stream_gate_up(const StreamArgs& a, const uint8_t* xq, const float* xs,
                                  const uint8_t* w13, const float* s13, float* g, hipStream_t stream) {
     const dim3 grid((2 * a.i) / kRowsPerGroup, a.max_slots);
-    hipLaunchKernelGGL(stream_gate_up_kernel, grid, dim3(256), 0, stream, xq, xs, w13, s13, a.offsets,
+    launch(stream_gate_up_kernel, grid, dim3(256), 0, stream, xq, xs, w13, s13, a.offsets,
                        a.sorted, a.active, a.num_active, g, a.h, a.i, a.k);
     return hipGetLastError();
 }
@@ -211,7 +211,7 @@ static size_t stream_down_lds_bytes(int i) { return stream_down_lds_base(i) + 4 
 hipError_t launch_stream_down(const StreamArgs& a, const float* g, const uint8_t* w2, const float* s2,
                               float* y, hipStream_t stream) {
     const dim3 grid(a.h / kRowsPerGroup, a.max_slots);
-    hipLaunchKernelGGL(stream_down_kernel, grid, dim3(256), stream_down_lds_bytes(a.i), stream, g, w2,
+    launch(stream_down_kernel, grid, dim3(256), stream_down_lds_bytes(a.i), stream, g, w2,
                        s2, a.offsets, a.sorted, a.active, a.num_active, y, a.h, a.i, a.k);
     return hipGetLastError();
 }
@@ -285,14 +285,14 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(const uint16_t* __res
 hipError_t launch_combine_bf16(const uint16_t* y, const float* tw, int M, int k, int h, uint16_t* out,
                                hipStream_t stream) {
     const dim3 grid((h / 8 + 255) / 256, M);
-    hipLaunchKernelGGL(combine_bf16_kernel, grid, dim3(256), 0, stream, y, tw, k, h, out);
+    launch(combine_bf16_kernel, grid, dim3(256), 0, stream, y, tw, k, h, out);
     return hipGetLastError();
 }
 
 hipError_t launch_combine(const float* y, const float* tw, int M, int k, int h, uint16_t* out,
                           hipStream_t stream) {
     const dim3 grid((h / 4 + 255) / 256, M);
-    hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, stream, y, tw, k, h, out);
+    launch(combine_kernel, grid, dim3(256), 0, stream, y, tw, k, h, out);
     return hipGetLastError();
 }
 

@@ -171,12 +171,16 @@ int moe_fp8_forward_noalloc(const void* x, const float* router_logits,
                             void* out, int M, int h, int i, int E, int k,
                             hipStream_t stream);
 
-/* Measurement variant of moe_fp8_forward_ws: additionally records
- * events[j] on `stream` just before the j-th stage of the forward and
- * events[n] after the last, where n = moe_fp8_forward_kernel_count(...);
- * n_events must be at least n + 1.  Event j..j+1 then brackets stage j, whose
- * kernel names moe_fp8_forward_kernel_name reports.  The events are
- * caller-created (hipEventCreate); results are those of moe_fp8_forward_ws. */
+/* Measurement variant of moe_fp8_forward_ws: the kernels of stage j launch
+ * through hipExtLaunchKernel so that events[2j] takes the GPU's timestamp of
+ * the start of the stage's first dispatch and events[2j + 1] that of the end
+ * of its last (hipEventElapsedTime of the pair is the stage's execution time,
+ * with no marker packets between stages), for j < n =
+ * moe_fp8_forward_kernel_count(...); n_events must be at least 2n, else
+ * MOE_ERR_INVALID.  Stage j's kernel names are those
+ * moe_fp8_forward_kernel_name reports.  The events are caller-created
+ * (hipEventCreate); results are those of moe_fp8_forward_ws.  The stamps are
+ * armed per calling thread. */
 int moe_fp8_forward_ws_timed(const void* x, const float* router_logits,
                              const void* w13, const float* s13,
                              const void* w2, const float* s2,
@@ -284,6 +288,15 @@ size_t moe_mxfp4_workspace_bytes(int M, int h, int i, int E, int k);
 /* The workspace layout of an MXFP4 forward with these sizes, as
  * moe_fp8_workspace_layout (path is MOE_FP8_PATH_STREAM or _PREFILL). */
 int moe_mxfp4_workspace_layout(int M, int h, int i, int E, int k, moe_fp8_ws_layout* layout);
+/* Measurement: the same forward with the stage stamps of
+ * moe_fp8_forward_ws_timed (events[2j], events[2j + 1]: start of stage j's
+ * first dispatch, end of its last; n_events >= 2 * the stage count, else
+ * MOE_ERR_INVALID). */
+int moe_mxfp4_forward_ws_timed(const void* x, const float* router_logits,
+                               const void* w13, const void* e13, const void* w2, const void* e2,
+                               void* out, int M, int h, int i, int E, int k,
+                               void* workspace, size_t workspace_bytes,
+                               hipEvent_t* events, int n_events, hipStream_t stream);
 /* Stage count and kernel name(s) of stage j of an MXFP4 forward with these
  * sizes, as moe_fp8_forward_kernel_count / _name. */
 int moe_mxfp4_forward_kernel_count(int M, int h, int i, int E, int k);

@@ -61,6 +61,24 @@ def _fwd_ws(lib, M, h, i, E, k, ptr=FAKE, ws=FAKE, nws=0):
     return lib.moe_fp8_forward_ws(ptr, ptr, ptr, ptr, ptr, ptr, ptr, M, h, i, E, k, ws, nws, None)
 
 
+def test_timed_forward_needs_two_events_per_stage(lib):
+    """The timed entry takes a start and a stop event per stage: fewer than
+    twice the stage count (or none) is rejected before any HIP call."""
+    import fp8_block_scaled_router_amd as moe
+    for M, h, i, E, k in ((4, 256, 128, 8, 2), (40, 384, 128, 2, 1)):   # one stage; five
+        n = lib.moe_fp8_forward_kernel_count(M, h, i, E, k)
+        assert n > 0
+        evs = (ctypes.c_void_p * (2 * n))(*([0x100000] * (2 * n)))
+        for short in sorted({0, n, n + 1, 2 * n - 1} - {2 * n}):
+            assert lib.moe_fp8_forward_ws_timed(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, M, h, i, E, k, FAKE, 0,
+                                                evs, short, None) == moe.MOE_ERR_INVALID
+        assert lib.moe_fp8_forward_ws_timed(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, M, h, i, E, k, FAKE, 0,
+                                            None, 2 * n, None) == moe.MOE_ERR_INVALID
+        # enough events: the checks go on to the workspace (none given)
+        assert lib.moe_fp8_forward_ws_timed(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, M, h, i, E, k, FAKE, 0,
+                                            evs, 2 * n, None) == moe.MOE_ERR_WORKSPACE
+
+
 def test_forward_argument_checks(lib):
     import fp8_block_scaled_router_amd as moe
     assert _fwd_ws(lib, -1, 256, 128, 8, 2) == moe.MOE_ERR_INVALID

@@ -280,6 +280,36 @@ def test_forward_prefix_stages(dev, moe_mod, ci):
     _check_sync_clean(ws)
 
 
+@pytest.mark.parametrize("ci", [0, 1, 2, 5])
+def test_forward_timed_stages(dev, moe_mod, ci):
+    """The timed entry is the forward itself (same bits); each stage's pair of
+    dispatch stamps gives a positive duration, and the stages' durations add
+    up to no more than the span from the first stage's start to the last's
+    end."""
+    cfg = synth.CONFIGS[ci]
+    L = Layer(cfg, synth.default_seed(ci), dev)
+    M, h, i, E, k = L.dims
+    names = moe_mod.forward_kernel_names(M, h, i, E, k)
+    ws = moe_mod.alloc_workspace(M, h, i, E, k, device=dev)
+    ref = moe_mod.moe_fp8_forward_ws(L.tx, L.tl, L.t13, L.ts13, L.t2, L.ts2, k, ws).clone()
+    torch.cuda.synchronize()
+    ev = moe_mod.HipEvents(2 * len(names))
+    try:
+        for _ in range(2):
+            out = moe_mod.moe_fp8_forward_ws_timed(L.tx, L.tl, L.t13, L.ts13, L.t2, L.ts2, k, ws, ev)
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+            d = [ev.elapsed_ms(2 * j, 2 * j + 1) for j in range(len(names))]
+            span = ev.elapsed_ms(0, 2 * len(names) - 1)
+            log(f"timed stages {cfg.name}: " + ", ".join(f"{n} {t * 1e3:.1f} us" for n, t in zip(names, d))
+                + f"; span {span * 1e3:.1f} us")
+            assert all(t > 0 for t in d)
+            assert sum(d) <= span * 1.0001 + 1e-4
+    finally:
+        ev.close()
+    _check_sync_clean(ws)
+
+
 def _custom_layer(dev, M, h, i, E, k, seed, logits_kind="normal"):
     cfg = synth.LayerConfig(f"m{M}_h{h}_i{i}_e{E}_top{k}", M, h, i, E, k, logits_kind, "edge case")
     return Layer(cfg, seed, dev)
