@@ -376,8 +376,8 @@ def mxfp4_bench(args):
     cut_ms = np.maximum(np.diff(np.array(T)), 0.0)
     # stage durations from the GPU's stamps of each stage's dispatches
     nst = len(names)
-    nf = max(1, args.timing_replays) * C
-    evs = [moe.HipEvents(2 * nst) for _ in range(nf)]
+    nf = max(max(1, args.timing_replays) * C, 64)   # after one unmeasured rotation
+    evs = [moe.HipEvents(2 * nst) for _ in range(C + nf)]
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -387,7 +387,7 @@ def mxfp4_bench(args):
             a = W[c]
             moe.moe_mxfp4_forward_ws_timed(X[c], Lg[c], a[0], a[1], a[2], a[3], k, WS[c], ev, out=OUT[c])
     torch.cuda.synchronize()
-    stage_ms = np.array([[ev.elapsed_ms(2 * j, 2 * j + 1) for j in range(nst)] for ev in evs]).mean(axis=0)
+    stage_ms = np.array([[ev.elapsed_ms(2 * j, 2 * j + 1) for j in range(nst)] for ev in evs[C:]]).mean(axis=0)
     for ev in evs:
         ev.close()
     dom = int(np.argmax(stage_ms))
@@ -601,9 +601,12 @@ def time_layer(moe, cfg, W, X, Lg, WS, OUT, steps, warmup, timing_replays):
 
     # The same stages timed directly: the library's timed entry launches each
     # stage's kernels with HIP events that the GPU stamps at the start of the
-    # stage's first dispatch and the end of its last, in reps * C eager
+    # stage's first dispatch and the end of its last, in eager
     # forwards on the launch stream, queued behind a GPU spin.
-    evs = [moe.HipEvents(2 * nst) for _ in range(reps * C)]
+    # At least 64 forwards are averaged, after one unmeasured rotation (the
+    # first forwards after the spin run at lower clocks).
+    nf = max(reps * C, 64)
+    evs = [moe.HipEvents(2 * nst) for _ in range(C + nf)]
     with torch.cuda.stream(side):
         torch.cuda._sleep(20_000_000)
         for f, ev in enumerate(evs):
@@ -611,10 +614,10 @@ def time_layer(moe, cfg, W, X, Lg, WS, OUT, steps, warmup, timing_replays):
             a = W[c]
             moe.moe_fp8_forward_ws_timed(X[c], Lg[c], a[0], a[1], a[2], a[3], k, WS[c], ev, out=OUT[c])
     torch.cuda.synchronize()
-    ev_ms = np.array([[ev.elapsed_ms(2 * j, 2 * j + 1) for j in range(nst)] for ev in evs]).mean(axis=0)
+    ev_ms = np.array([[ev.elapsed_ms(2 * j, 2 * j + 1) for j in range(nst)] for ev in evs[C:]]).mean(axis=0)
     for ev in evs:
         ev.close()
-    return ms_per_step, names, np.maximum(np.diff(np.array(T)), 0.0), reps * C, ev_ms
+    return ms_per_step, names, np.maximum(np.diff(np.array(T)), 0.0), nf, ev_ms
 
 
 def layer_record(cfg, names, stage_ms, U_mean, ms_per_step, count, traffic_workload=None):
