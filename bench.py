@@ -70,6 +70,9 @@ def parse():
                     help="time BF16 routing fused with the top-k alone on --config's activations")
     ap.add_argument("--mxfp4", action="store_true",
                     help="time the layer with MXFP4 expert weights (default shape: the wide-decode batch)")
+    ap.add_argument("--tiled-paths", action="store_true",
+                    help="time the five-launch tiled path and the producer with its reducer on the same inputs "
+                         "(default shape: the 768-row verify batch)")
     args = ap.parse_args()
     args.config_given = any(a == "--config" or a.startswith("--config=") for a in sys.argv[1:])
     return args
@@ -99,6 +102,10 @@ KERNEL_SOURCES["stream_gate_up_mx_kernel"] = ["fp8_block_scaled_router_amd/csrc/
 KERNEL_SOURCES["stream_down_mx_kernel"] = KERNEL_SOURCES["stream_gate_up_mx_kernel"]
 KERNEL_SOURCES["prefill_down_kernel"] = KERNEL_SOURCES["prefill_gate_up_kernel"]
 KERNEL_SOURCES["prefill_gate_up_mx_kernel"] = KERNEL_SOURCES["prefill_gate_up_kernel"]
+KERNEL_SOURCES["prefill_producer_kernel"] = KERNEL_SOURCES["prefill_gate_up_kernel"] + [
+    "fp8_block_scaled_router_amd/csrc/route_quant.h", "fp8_block_scaled_router_amd/csrc/group.h",
+    "fp8_block_scaled_router_amd/csrc/fused_decode.h"]
+KERNEL_SOURCES["prefill_producer_mx_kernel"] = KERNEL_SOURCES["prefill_producer_kernel"]
 KERNEL_SOURCES["prefill_down_mx_kernel"] = KERNEL_SOURCES["prefill_gate_up_kernel"]
 
 
@@ -184,6 +191,11 @@ def stage_work(cfg, stage, U, wbytes=None):
         return U * w13 + M * k * (h + i + (h // 128 + i // 128) * 4), 4.0 * M * k * h * i
     if stage.startswith("prefill_down"):   # bf16 partials out
         return U * w2 + M * k * (i + (i // 128) * 4 + h * 2), 2.0 * M * k * h * i
+    if stage.startswith("prefill_producer"):
+        # the layer's inputs and the weights once; ids, weights and the bf16
+        # partials out (the activation codes and the requantised intermediate
+        # stay on chip or in the caches between its phases)
+        return M * h * 2 + M * cfg.E * 4 + U * (w13 + w2) + M * k * (8 + h * 2), 6.0 * M * k * h * i
     if stage.startswith("route_quant"):
         return M * h * 2 + M * cfg.E * 4 + act + M * k * 8, 0.0
     if stage.startswith("combine_bf16"):
@@ -421,6 +433,73 @@ def mxfp4_bench(args):
                      "forward_hbm_frac": round(fw_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                      "forward_mfma_frac": round(6.0 * M * k * h * i / (ms / 1e3) / 1e12 / FP8_PEAK_TFLOPS, 4)},
         "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def tiled_paths_bench(args):
+    """The two forms of the tiled path on one workload: five launches
+    (routing and quantisation, grouping, gate/up, down, combine) and the
+    producer (routing through the down partials in one launch) with its route
+    reducer.  Both forced on the same inputs (moe_fp8_forward_ws_path), HIP
+    graphs of the rotation copies' forwards, events around the replays; the
+    two give the same bits (checked here on the first copy)."""
+    import numpy as np
+    import torch
+
+    import fp8_block_scaled_router_amd as moe
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    moe.lib()
+    dev = torch.device("cuda:0")
+    ci = args.config if args.config_given else 5
+    cfg = synth.CONFIGS[ci]
+    seed = synth.default_seed(ci) if args.seed is None else args.seed
+    M, h, i, E, k = cfg.M, cfg.h, cfg.i, cfg.E, cfg.k
+    C = rotation_copies(cfg, min(E, M * k), args)
+    W, X, Lg = [], [], []
+    for c in range(C):
+        W.append(make_device_weights(moe, cfg, seed, dev, c))
+        X.append(torch.from_numpy(synth.make_x(cfg, seed, copy=c).view(np.int16)).view(torch.bfloat16).to(dev))
+        Lg.append(torch.from_numpy(synth.make_logits(cfg, seed, copy=c)).to(dev))
+    OUT = [torch.empty((M, h), dtype=torch.bfloat16, device=dev) for _ in range(C)]
+    res, first = {}, {}
+    for path in (moe.PATH_PREFILL, moe.PATH_PRODUCER):
+        WS = [moe.alloc_workspace(M, h, i, E, k, device=dev, path=path) for _ in range(C)]
+
+        def fwd(c, path=path, WS=WS):
+            a = W[c]
+            moe.moe_fp8_forward_ws_path(X[c], Lg[c], a[0], a[1], a[2], a[3], k, WS[c], path, out=OUT[c])
+
+        for c in range(C):
+            fwd(c)
+        torch.cuda.synchronize()
+        first[path] = OUT[0].clone()
+        ms, reps, _ = time_single_kernel(fwd, C, args)
+        errs = [moe.workspace_error(w) for w in WS]
+        if any(errs):
+            print("bench.py: a wait of the producer timed out", file=sys.stderr)
+            sys.exit(3)
+        res[path] = (ms, reps * C)
+        del WS
+        torch.cuda.empty_cache()
+    same = bool(torch.equal(first[moe.PATH_PREFILL].view(torch.int16), first[moe.PATH_PRODUCER].view(torch.int16)))
+    five, prod = res[moe.PATH_PREFILL][0], res[moe.PATH_PRODUCER][0]
+    line = {
+        "metric": "MoE-layer tokens/s, producer + route reducer (two launches)",
+        "value": round(M / (prod / 1e3), 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": res[moe.PATH_PRODUCER][1], "warmup": None, "ms_per_step": round(prod, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "e4m3 (fp32 accumulate)", "data": "synthetic",
+        "config": {"workload": cfg.name, "M": M, "h": h, "i": i, "E": E, "k": k, "rotation_copies": C,
+                   "five_launch_us_per_forward": round(five * 1e3, 3),
+                   "producer_us_per_forward": round(prod * 1e3, 3),
+                   "producer_vs_five_launch": round(five / prod, 4), "same_bits": same,
+                   "timing": "HIP graph of the rotation copies' forwards on each path, events around the replays"},
+        "roofline": None, "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
 
@@ -726,7 +805,7 @@ def other_config_records(moe, args, skip, dev):
         roofline, forward = layer_record(cfg, names, stage_ms, U_mean, ms, count)
         out[cfg.name] = {
             "tokens_per_s": round(M / (ms / 1e3), 2), "ms_per_step": round(ms, 6), "steps": steps,
-            "path": {0: "stream", 1: "prefill", 2: "one-kernel"}[lay.path],
+            "path": moe.PATH_NAMES[lay.path],
             "rotation_copies": C, "distinct_experts_mean": U_mean,
             "stage_us": {n: round(v * 1e3, 3) for n, v in zip(names, stage_ms)},
             "stage_us_cut_graphs": {n: round(v * 1e3, 3) for n, v in zip(names, cut_ms)},
@@ -851,6 +930,9 @@ def main():
     if args.mxfp4:
         mxfp4_bench(args)
         return
+    if args.tiled_paths:
+        tiled_paths_bench(args)
+        return
 
     import numpy as np
     import torch
@@ -944,7 +1026,7 @@ def main():
         "dtype": "e4m3 (fp32 accumulate)",
         "data": "synthetic",
         "config": {"workload": cfg.name, "M": M, "h": h, "i": i, "E": E, "k": k,
-                   "path": {0: "stream", 1: "prefill", 2: "one-kernel"}[lay.path],
+                   "path": moe.PATH_NAMES[lay.path],
                    "rotation_copies": C, "distinct_experts_mean": U_mean,
                    "layer_bytes_per_step": int(fw_bytes),
                    "timing": "HIP graph of C forwards, events around K steps",

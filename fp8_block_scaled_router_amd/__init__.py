@@ -49,6 +49,11 @@ class WsLayout(ctypes.Structure):
 PATH_STREAM = 0
 PATH_PREFILL = 1
 PATH_FUSED_DECODE = 2
+PATH_PRODUCER = 3
+PATH_NAMES = {PATH_STREAM: "stream", PATH_PREFILL: "prefill", PATH_FUSED_DECODE: "one-kernel",
+              PATH_PRODUCER: "producer"}
+ERR_FUSED_WAIT = 1
+ERR_PRODUCER_WAIT = 2
 
 
 _SIGS = {
@@ -59,6 +64,11 @@ _SIGS = {
     "moe_fp8_forward_ws": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _SZ, _P]),
     "moe_fp8_workspace_layout": (_I, [_I, _I, _I, _I, _I, ctypes.POINTER(WsLayout)]),
     "moe_mxfp4_workspace_layout": (_I, [_I, _I, _I, _I, _I, ctypes.POINTER(WsLayout)]),
+    "moe_fp8_workspace_bytes_path": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "moe_fp8_workspace_layout_path": (_I, [_I, _I, _I, _I, _I, _I, ctypes.POINTER(WsLayout)]),
+    "moe_fp8_forward_ws_path": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _SZ, _I, _P]),
+    "moe_mxfp4_workspace_bytes_path": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "moe_mxfp4_forward_ws_path": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _SZ, _I, _P]),
     "moe_mxfp4_forward_ws_timed": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _SZ, _P, _I, _P]),
     "router_topk": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "moe_fp8_router_gemm_topk": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P]),
@@ -143,12 +153,26 @@ def workspace_layout(M: int, h: int, i: int, E: int, k: int) -> WsLayout:
     return L
 
 
-def alloc_workspace(M: int, h: int, i: int, E: int, k: int, device=None) -> torch.Tensor:
-    """A workspace for these sizes; its synchronisation words start at zero."""
-    n = max(workspace_bytes(M, h, i, E, k), int(lib().moe_fp8_workspace_head_bytes()))
+def alloc_workspace(M: int, h: int, i: int, E: int, k: int, device=None, path: int | None = None) -> torch.Tensor:
+    """A workspace for these sizes (and, when given, that path); its
+    synchronisation words start at zero."""
+    if path is None:
+        need = workspace_bytes(M, h, i, E, k)
+    else:
+        need = int(lib().moe_fp8_workspace_bytes_path(M, h, i, E, k, int(path)))
+        if need == 0:
+            raise MoeError(MOE_ERR_UNSUPPORTED, "moe_fp8_workspace_bytes_path")
+    n = max(need, int(lib().moe_fp8_workspace_head_bytes()))
     ws = torch.empty(n, dtype=torch.uint8, device=device or "cuda")
     workspace_init(ws)
     return ws
+
+
+def workspace_layout_path(M: int, h: int, i: int, E: int, k: int, path: int) -> WsLayout:
+    L = WsLayout()
+    _check(lib().moe_fp8_workspace_layout_path(M, h, i, E, k, int(path), ctypes.byref(L)),
+           "moe_fp8_workspace_layout_path")
+    return L
 
 
 def workspace_init(ws: torch.Tensor, stream=None) -> None:
@@ -240,6 +264,19 @@ def moe_fp8_forward_ws(x, router_logits, w13, s13, w2, s2, k: int, workspace, ou
     return out
 
 
+def moe_fp8_forward_ws_path(x, router_logits, w13, s13, w2, s2, k: int, workspace, path: int, out=None,
+                            stream=None):
+    """The layer on the given path (PATH_*), for measurement and testing; the
+    workspace is sized for that path (alloc_workspace(..., path=path))."""
+    M, h, i, E, out = _layer_args(x, router_logits, w13, s13, w2, s2, k, out)
+    _dev(workspace, torch.uint8, "workspace")
+    rc = lib().moe_fp8_forward_ws_path(_ptr(x), _ptr(router_logits), _ptr(w13), _ptr(s13), _ptr(w2),
+                                       _ptr(s2), _ptr(out), M, h, i, E, int(k), _ptr(workspace),
+                                       workspace.numel(), int(path), _stream(stream))
+    _check(rc, "moe_fp8_forward_ws_path")
+    return out
+
+
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
@@ -274,9 +311,12 @@ def mxfp4_workspace_layout(M: int, h: int, i: int, E: int, k: int) -> WsLayout:
     return L
 
 
-def alloc_mxfp4_workspace(M: int, h: int, i: int, E: int, k: int, device=None) -> torch.Tensor:
-    """A workspace for moe_mxfp4_forward_ws with its head cleared."""
-    n = mxfp4_workspace_bytes(M, h, i, E, k)
+def alloc_mxfp4_workspace(M: int, h: int, i: int, E: int, k: int, device=None,
+                          path: int | None = None) -> torch.Tensor:
+    """A workspace for moe_mxfp4_forward_ws (or, with `path`, for
+    moe_mxfp4_forward_ws_path on that path) with its head cleared."""
+    n = mxfp4_workspace_bytes(M, h, i, E, k) if path is None else \
+        int(lib().moe_mxfp4_workspace_bytes_path(M, h, i, E, k, int(path)))
     if n == 0:
         raise MoeError(MOE_ERR_UNSUPPORTED, "moe_mxfp4_workspace_bytes")
     ws = torch.empty(n, dtype=torch.uint8, device=device or "cuda")
@@ -319,6 +359,30 @@ def moe_mxfp4_forward_ws(x, router_logits, w13, e13, w2, e2, k: int, workspace, 
                                                  _ptr(e2), _ptr(out), M, h, i, E, int(k), _ptr(workspace),
                                                  workspace.numel(), int(n_stages), _stream(stream)),
                "moe_mxfp4_forward_ws_prefix")
+    return out
+
+
+def moe_mxfp4_forward_ws_path(x, router_logits, w13, e13, w2, e2, k: int, workspace, path: int, out=None,
+                              stream=None):
+    """The MXFP4 layer on the given path (PATH_STREAM, PATH_PREFILL or
+    PATH_PRODUCER), for measurement and testing."""
+    M, h = x.shape
+    E = router_logits.shape[1]
+    i = w2.shape[2] * 2
+    _dev(x, torch.bfloat16, "x", (M, h))
+    _dev(router_logits, torch.float32, "router_logits", (M, E))
+    _dev(w13, torch.uint8, "w13", (E, 2 * i, h // 2))
+    _dev(e13, torch.uint8, "e13", (E, 2 * i, h // 32))
+    _dev(w2, torch.uint8, "w2", (E, h, i // 2))
+    _dev(e2, torch.uint8, "e2", (E, h, i // 32))
+    _dev(workspace, torch.uint8, "workspace")
+    if out is None:
+        out = torch.empty((M, h), dtype=torch.bfloat16, device=x.device)
+    _dev(out, torch.bfloat16, "out", (M, h))
+    _check(lib().moe_mxfp4_forward_ws_path(_ptr(x), _ptr(router_logits), _ptr(w13), _ptr(e13), _ptr(w2), _ptr(e2),
+                                           _ptr(out), M, h, i, E, int(k), _ptr(workspace), workspace.numel(),
+                                           int(path), _stream(stream)),
+           "moe_mxfp4_forward_ws_path")
     return out
 
 

@@ -50,6 +50,14 @@ constexpr size_t kSyncEpoch = 0;                // word: forwards run on this wo
 constexpr size_t kSyncExit = 256;               // word: workgroups finished in this forward
 constexpr size_t kSyncErr = 512;                // word: sticky error (a wait timed out)
 constexpr size_t kSyncArrive = 1024;            // word: routing workgroups counted in (grouping tail)
+constexpr size_t kSyncProdBar = 1280;           // two words: the prefill producer's grid barriers
+constexpr size_t kSyncProdExit = 1536;          // word: producer workgroups finished in this forward
+constexpr size_t kSyncProdDone = 4096;          // words: gate/up tiles finished, per M-tile (producer)
+constexpr int kProdMaxTiles = (int)((kSyncBytes - kSyncProdDone) / 4);
+// Bits of the sticky error word: a wait of the one-kernel decode path, or of
+// the prefill producer, timed out.
+constexpr uint32_t kErrFused = 1u;
+constexpr uint32_t kErrProducer = 2u;
 constexpr size_t kLLBytes = (size_t)8 << 20;    // v_ll, then t_ll
 constexpr size_t kLLOffset = kSyncBytes;
 constexpr size_t kWorkspaceHead = kSyncBytes + kLLBytes;   // zero-initialised part

@@ -17,6 +17,7 @@
 // grouped GEMM with tile_m routes per tile (exclusive scan of
 // ceil(count / tile_m)).
 #include "device.h"
+#include "group.h"
 #include "launch.h"
 
 namespace moe {
@@ -33,23 +34,10 @@ __global__ __launch_bounds__(kChunk) void group_hist_kernel(const int32_t* __res
     const int t = threadIdx.x;
     cnt[t] = 0;
     __syncthreads();
-    const int p = blockIdx.x * kChunk + t;
-    if (p < R) {
-        const int e = ids[p];
-        if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);   // ids outside [0, E) are dropped
-    }
+    const int beg = blockIdx.x * kChunk;
+    group_chunk_hist(ids, beg, min(R, beg + kChunk), E, cnt, t, kChunk);
     __syncthreads();
     if (t < E) hist[(size_t)blockIdx.x * E + t] = cnt[t];
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int o = __shfl_up(v, d, kWave);
-        if (lane >= d) v += o;
-    }
-    return v;
 }
 
 __global__ __launch_bounds__(256 * kScanGroups) void group_scatter_kernel(
@@ -57,118 +45,12 @@ __global__ __launch_bounds__(256 * kScanGroups) void group_scatter_kernel(
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted,
     int32_t* __restrict__ active, int32_t* __restrict__ num_active, int tile_m,
     int32_t* __restrict__ mtile_off) {
-    __shared__ int tot_l[kScanGroups][256], pre_l[kScanGroups][256];
-    __shared__ int base[256];
-    const int chunk = blockIdx.x;
-    const int tid = threadIdx.x;
-    {
-        // Thread (g, e) sums expert e's counts over chunks g, g + 4, ...
-        // (all of them, and those before this chunk), 16 requests at a time.
-        const int e = tid & 255, g = tid >> 8;
-        int tot = 0, pre = 0;
-        if (e < E) {
-            for (int c0 = g; c0 < nchunks; c0 += 16 * kScanGroups) {
-                int v[16];
-#pragma unroll
-                for (int u = 0; u < 16; ++u) {
-                    const int c = c0 + kScanGroups * u;
-                    v[u] = c < nchunks ? hist[(size_t)c * E + e] : 0;
-                }
-#pragma unroll
-                for (int u = 0; u < 16; ++u) {
-                    tot += v[u];
-                    if (c0 + kScanGroups * u < chunk) pre += v[u];
-                }
-            }
-        }
-        tot_l[g][e] = tot;
-        pre_l[g][e] = pre;
-    }
-    __syncthreads();
-    if (tid >= kWave) return;
-    // One wave from here on; lane l owns experts 4l .. 4l+3.
-    const int lane = tid;
-    int tot[4], pre[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int e = 4 * lane + j;
-        tot[j] = 0;
-        pre[j] = 0;
-#pragma unroll
-        for (int g = 0; g < kScanGroups; ++g) {
-            tot[j] += tot_l[g][e];
-            pre[j] += pre_l[g][e];
-        }
-    }
-    const int lsum = tot[0] + tot[1] + tot[2] + tot[3];
-    const int lact = (tot[0] > 0) + (tot[1] > 0) + (tot[2] > 0) + (tot[3] > 0);
-    int ltiles = 0;
-    if (tile_m > 0)
-        for (int j = 0; j < 4; ++j) ltiles += (tot[j] + tile_m - 1) / tile_m;
-    const int incl = wave_incl_scan(lsum, lane);
-    const int iact = wave_incl_scan(lact, lane);
-    const int itil = wave_incl_scan(ltiles, lane);
-    int run = incl - lsum, arun = iact - lact, trun = itil - ltiles;
-    if (chunk == 0 && tile_m > 0) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int e = 4 * lane + j;
-            if (e < E) mtile_off[e] = trun;
-            trun += (tot[j] + tile_m - 1) / tile_m;
-        }
-        if (lane == 63) mtile_off[E] = itil;
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int e = 4 * lane + j;
-        if (e < E) {
-            base[e] = run + pre[j];
-            if (chunk == 0) {
-                offsets[e] = run;
-                counts[e] = tot[j];
-                if (tot[j] > 0) active[arun] = e;
-            }
-        }
-        run += tot[j];
-        arun += (tot[j] > 0);
-    }
-    if (chunk == 0 && lane == 63) {
-        offsets[E] = incl;
-        *num_active = iact;
-    }
-
-    // Scatter the chunk's routes in route order, 64 at a time (one wave, so
-    // the LDS reads and updates of base stay in program order).
-    const int beg = chunk * kChunk;
-    const int end = min(R, beg + kChunk);
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    int ev[kChunk / 64];
-#pragma unroll
-    for (int u = 0; u < kChunk / 64; ++u) {
-        const int p = beg + 64 * u + lane;
-        ev[u] = p < end ? ids[p] : 0x1FF;
-    }
-#pragma unroll
-    for (int u = 0; u < kChunk / 64; ++u) {
-        const int p = beg + 64 * u + lane;
-        int e = ev[u];
-        const bool valid = p < end && (unsigned)e < (unsigned)E;
-        if (!valid) e = 0x1FF;
-        uint64_t same = ~0ull;
-#pragma unroll
-        for (int b = 0; b < 9; ++b) {
-            const bool bit = (e >> b) & 1;
-            const uint64_t bal = __ballot(bit);
-            same &= bit ? bal : ~bal;
-        }
-        const int rank = __popcll(same & below);
-        const bool last = (same >> lane) == 1ull;   // highest lane of its expert in this batch
-        const int pos = valid ? base[e] + rank : 0;
-        if (valid) {
-            sorted[pos] = p;
-            if (last) base[e] += __popcll(same);
-        }
-    }
+    __shared__ int tot_l[kScanGroups * 256], pre_l[kScanGroups * 256];
+    __shared__ int base_l[256];
+    const int chunk = blockIdx.x, beg = chunk * kChunk;
+    const GroupOut o{counts, offsets, sorted, active, num_active, tile_m > 0 ? mtile_off : nullptr, tile_m};
+    group_chunk_scatter<kScanGroups>(ids, E, nchunks, hist, chunk, beg, min(R, beg + kChunk), chunk == 0, o, tot_l,
+                                     pre_l, base_l, threadIdx.x);
 }
 
 hipError_t launch_group(const int32_t* ids, int R, int E, int32_t* hist, int32_t* counts,

@@ -98,10 +98,38 @@ struct PrefillArgs {
     uint8_t* a2;                // [R][i]   requantised activations, sorted-route order
     float* a2s;                 // [R][i/128]
     uint16_t* y;                // [R][h]   bf16 partials by route id
+    uint32_t* done;             // producer: gate/up tiles finished per M-tile (null otherwise)
+    uint32_t* err;              // producer: the workspace's sticky error word
     int h, i, E, k;
 };
 int prefill_tile_m();
 bool prefill_supported(int M, int h, int i, int k);
+
+// The prefill producer: routing, quantisation, grouping and both tiled
+// GEMMs in one launch of one workgroup per CU (all resident), feeding the
+// route reducer (launch_combine_bf16 with the error word).
+struct ProducerArgs {
+    PrefillArgs pa;              // the GEMMs' view of the buffers below, with done and err set
+    const float* logits;
+    const uint16_t* x;
+    int32_t* ids;
+    float* tw;
+    uint8_t* xq;
+    float* xs;
+    int32_t* hist;               // [chunks][E] routes per expert of each routing chunk
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* sorted;
+    int32_t* active;
+    int32_t* num_active;
+    int32_t* mtile_off;
+    uint32_t* sync;              // the workspace head's synchronisation words
+    int M;
+    int tpw;                     // tokens per routing chunk (set by the launcher)
+};
+constexpr int kProdMaxGrid = 512;   // routing chunks at most (rows of hist)
+bool producer_supported(int M, int h, int i, int E, int k);
+hipError_t launch_prefill_producer(const ProducerArgs& p, bool mx, hipStream_t stream);
 // mx: MXFP4 weights (w13 / w2 with e13 / e2), else FP8 (with s13 / s2).
 hipError_t launch_prefill_gate_up(const PrefillArgs& a, bool mx, hipStream_t stream);
 hipError_t launch_prefill_down(const PrefillArgs& a, bool mx, hipStream_t stream);
@@ -109,9 +137,10 @@ hipError_t launch_prefill_down(const PrefillArgs& a, bool mx, hipStream_t stream
 // Fixed-order combine of the k route partials of each token into bf16.
 hipError_t launch_combine(const float* y, const float* tw, int M, int k, int h, uint16_t* out,
                           hipStream_t stream);
-// Same, for bf16 partials (the prefill path).
+// Same, for bf16 partials (the prefill path).  err: when given and its
+// kErrProducer bit is set (the producer gave up), every output is NaN.
 hipError_t launch_combine_bf16(const uint16_t* y, const float* tw, int M, int k, int h, uint16_t* out,
-                               hipStream_t stream);
+                               hipStream_t stream, const uint32_t* err = nullptr);
 
 // RMSNorm of bf16 rows fused with the 1x128 activation quantisation; y
 // (bf16 [M][h], the normalised rows) may be null.  h % 128 == 0,

@@ -75,21 +75,43 @@ constexpr int kTiledRoutesPerExpert = 8;
 // same shapes).
 constexpr int kTiledRoutesPerExpertMx = 12;
 
+// Whether a batch of these sizes can take the path (the MXFP4 layer has no
+// one-kernel path).
+bool path_ok(int path, int M, int h, int i, int E, int k, bool mx) {
+    switch (path) {
+        case MOE_FP8_PATH_STREAM: return true;
+        case MOE_FP8_PATH_PREFILL: return moe::prefill_supported(M, h, i, k);
+        case MOE_FP8_PATH_PRODUCER: return moe::producer_supported(M, h, i, E, k);
+        case MOE_FP8_PATH_FUSED_DECODE: return !mx && moe::fused_supported(M, h, i, E, k);
+        default: return false;
+    }
+}
+
+// The tiled kernels run as five launches by default: the producer and its
+// reducer (two launches, the same bits) measured 5-7% slower from 768 to
+// 8192 tokens at h 2048, i 768, E 128, top-8 (its in-kernel grid barriers
+// and the device-scope stores of everything handed across them cost more
+// than the launch boundaries they replace), and 3% faster at 256 tokens; it
+// runs when asked for (moe_fp8_forward_ws_path).
+int tiled_path(int M, int h, int i, int E, int k) {
+    (void)E;
+    if (moe::prefill_supported(M, h, i, k)) return MOE_FP8_PATH_PREFILL;
+    return MOE_FP8_PATH_STREAM;
+}
+
 int choose_path(int M, int h, int i, int E, int k) {
     if (moe::fused_supported(M, h, i, E, k)) return MOE_FP8_PATH_FUSED_DECODE;
-    if ((int64_t)M * k >= (int64_t)kTiledRoutesPerExpert * E && moe::prefill_supported(M, h, i, k))
-        return MOE_FP8_PATH_PREFILL;
+    if ((int64_t)M * k >= (int64_t)kTiledRoutesPerExpert * E) return tiled_path(M, h, i, E, k);
     return MOE_FP8_PATH_STREAM;
 }
 
-// The MXFP4 layer has no one-kernel path.
 int choose_path_mx(int M, int h, int i, int E, int k) {
-    if ((int64_t)M * k >= (int64_t)kTiledRoutesPerExpertMx * E && moe::prefill_supported(M, h, i, k))
-        return MOE_FP8_PATH_PREFILL;
+    if ((int64_t)M * k >= (int64_t)kTiledRoutesPerExpertMx * E) return tiled_path(M, h, i, E, k);
     return MOE_FP8_PATH_STREAM;
 }
 
-void make_layout(int M, int h, int i, int E, int k, Layout* L, bool mx = false) {
+// path < 0: the path the library picks for these sizes.
+void make_layout(int M, int h, int i, int E, int k, Layout* L, bool mx = false, int path = -1) {
     const size_t R = (size_t)M * k;
     size_t cur = moe::kWorkspaceHead;   // synchronisation words and exchange region first
     auto take = [&](size_t bytes) {
@@ -108,8 +130,11 @@ void make_layout(int M, int h, int i, int E, int k, Layout* L, bool mx = false) 
     p.sorted = take(R * 4);
     p.active = take((size_t)E * 4);
     p.num_active = take(4);
-    L->hist = take((size_t)moe::group_chunks((int)R) * E * 4);
-    p.path = mx ? choose_path_mx(M, h, i, E, k) : choose_path(M, h, i, E, k);
+    p.path = path >= 0 ? path : mx ? choose_path_mx(M, h, i, E, k) : choose_path(M, h, i, E, k);
+    // grouping scratch: the chunk counts (the producer's chunks are at most
+    // one per workgroup of its grid)
+    const size_t chunks = (size_t)moe::group_chunks((int)R);
+    L->hist = take((p.path == MOE_FP8_PATH_PRODUCER ? std::max(chunks, (size_t)moe::kProdMaxGrid) : chunks) * E * 4);
     L->mtile_off = take((size_t)(E + 1) * 4);
     p.gate_up = (size_t)-1;
     p.act2 = (size_t)-1;
@@ -118,7 +143,7 @@ void make_layout(int M, int h, int i, int E, int k, Layout* L, bool mx = false) 
     if (p.path == MOE_FP8_PATH_STREAM) {
         p.gate_up = take(R * 2 * i * 4);
         p.partial = take(R * h * 4);
-    } else if (p.path == MOE_FP8_PATH_PREFILL) {
+    } else if (p.path == MOE_FP8_PATH_PREFILL || p.path == MOE_FP8_PATH_PRODUCER) {
         p.act2 = take(R * i);
         p.act2_scale = take(R * (i / 128) * 4);
         p.partial = take(R * h * 2);   // bf16 partials
@@ -151,6 +176,8 @@ const char* const kStreamSmallMxStages[] = {"route_quant_group_kernel", "stream_
 const char* const kPrefillMxStages[] = {"route_quant_kernel", "group_hist+group_scatter",
                                         "prefill_gate_up_mx_kernel", "prefill_down_mx_kernel",
                                         "combine_bf16_kernel"};
+const char* const kProducerStages[] = {"prefill_producer_kernel", "combine_bf16_kernel"};
+const char* const kProducerMxStages[] = {"prefill_producer_mx_kernel", "combine_bf16_kernel"};
 
 // The streaming path routes, quantises and groups in one launch when the
 // batch has few enough routes.
@@ -158,17 +185,20 @@ bool small_group(int M, int k) { return (int64_t)M * k <= moe::kGroupTailRoutes;
 
 int stage_count(int path, int M, int k) {
     if (path == MOE_FP8_PATH_FUSED_DECODE) return 1;
+    if (path == MOE_FP8_PATH_PRODUCER) return 2;
     if (path == MOE_FP8_PATH_STREAM && small_group(M, k)) return 4;
     return 5;
 }
 const char* stage_name(int path, int M, int k, int j) {
     if (path == MOE_FP8_PATH_FUSED_DECODE) return kFusedStages[j];
     if (path == MOE_FP8_PATH_PREFILL) return kPrefillStages[j];
+    if (path == MOE_FP8_PATH_PRODUCER) return kProducerStages[j];
     if (small_group(M, k)) return kStreamSmallStages[j];
     return kStreamStages[j];
 }
 const char* stage_name_mx(int path, int M, int k, int j) {
     if (path == MOE_FP8_PATH_PREFILL) return kPrefillMxStages[j];
+    if (path == MOE_FP8_PATH_PRODUCER) return kProducerMxStages[j];
     if (small_group(M, k)) return kStreamSmallMxStages[j];
     return kStreamMxStages[j];
 }
@@ -192,10 +222,99 @@ struct EventHook {
     bool cut() { return stage++ >= limit; }
 };
 
+// One stage of a forward: the cut of a measurement forward, the stage's
+// timing stamps, the launch.
+#define MOE_STEP(call)                 \
+    do {                               \
+        if (hook.cut()) return MOE_OK; \
+        hook.arm();                    \
+        rc = hip_status(call);         \
+        EventHook::disarm();           \
+        if (rc != MOE_OK) return rc;   \
+    } while (0)
+
+// The tiled paths, for FP8 (s13, s2) or MXFP4 (e13, e2) weights: routing
+// with quantisation, grouping, the gate/up and down GEMMs and the bf16
+// reducer in five launches, or the producer and the reducer in two.
+int tiled_forward(const Layout& L, void* workspace, const void* x, const float* router_logits, const void* w13,
+                  const float* s13, const void* e13, const void* w2, const float* s2, const void* e2, void* out,
+                  int M, int h, int i, int E, int k, EventHook& hook, hipStream_t stream) {
+    int rc = MOE_OK;
+    const moe_fp8_ws_layout& p = L.pub;
+    const bool mx = e13 != nullptr;
+    int32_t* ids = at<int32_t>(workspace, p.topk_ids);
+    float* tw = at<float>(workspace, p.topk_w);
+    uint8_t* xq = at<uint8_t>(workspace, p.xq);
+    float* xs = at<float>(workspace, p.xs);
+    int32_t* counts = at<int32_t>(workspace, p.counts);
+    int32_t* offsets = at<int32_t>(workspace, p.offsets);
+    int32_t* sorted = at<int32_t>(workspace, p.sorted);
+    int32_t* active = at<int32_t>(workspace, p.active);
+    int32_t* num_active = at<int32_t>(workspace, p.num_active);
+    int32_t* hist = at<int32_t>(workspace, L.hist);
+    int32_t* mtile_off = at<int32_t>(workspace, L.mtile_off);
+    uint32_t* sync = at<uint32_t>(workspace, 0);
+    moe::PrefillArgs pa;
+    pa.xq = xq;
+    pa.xs = xs;
+    pa.w13 = static_cast<const uint8_t*>(w13);
+    pa.s13 = s13;
+    pa.e13 = static_cast<const uint8_t*>(e13);
+    pa.w2 = static_cast<const uint8_t*>(w2);
+    pa.s2 = s2;
+    pa.e2 = static_cast<const uint8_t*>(e2);
+    pa.offsets = offsets;
+    pa.sorted = sorted;
+    pa.mtile_off = mtile_off;
+    pa.a2 = at<uint8_t>(workspace, p.act2);
+    pa.a2s = at<float>(workspace, p.act2_scale);
+    pa.y = at<uint16_t>(workspace, p.partial);
+    pa.done = nullptr;
+    pa.err = nullptr;
+    pa.h = h;
+    pa.i = i;
+    pa.E = E;
+    pa.k = k;
+    uint16_t* o = static_cast<uint16_t*>(out);
+    if (p.path == MOE_FP8_PATH_PRODUCER) {
+        pa.done = sync + moe::kSyncProdDone / 4;
+        pa.err = sync + moe::kSyncErr / 4;
+        moe::ProducerArgs pp;
+        pp.pa = pa;
+        pp.logits = router_logits;
+        pp.x = static_cast<const uint16_t*>(x);
+        pp.ids = ids;
+        pp.tw = tw;
+        pp.xq = xq;
+        pp.xs = xs;
+        pp.hist = hist;
+        pp.counts = counts;
+        pp.offsets = offsets;
+        pp.sorted = sorted;
+        pp.active = active;
+        pp.num_active = num_active;
+        pp.mtile_off = mtile_off;
+        pp.sync = sync;
+        pp.M = M;
+        pp.tpw = 0;
+        MOE_STEP(moe::launch_prefill_producer(pp, mx, stream));
+        MOE_STEP(moe::launch_combine_bf16(pa.y, tw, M, k, h, o, stream, pa.err));
+        return MOE_OK;
+    }
+    MOE_STEP(moe::launch_route_quant(router_logits, static_cast<const uint16_t*>(x), M, E, k, h, ids, tw, xq, xs,
+                                     moe::kRoute | moe::kQuant, stream));
+    MOE_STEP(moe::launch_group(ids, M * k, E, hist, counts, offsets, sorted, active, num_active, stream,
+                               moe::prefill_tile_m(), mtile_off));
+    MOE_STEP(moe::launch_prefill_gate_up(pa, mx, stream));
+    MOE_STEP(moe::launch_prefill_down(pa, mx, stream));
+    MOE_STEP(moe::launch_combine_bf16(pa.y, tw, M, k, h, o, stream));
+    return MOE_OK;
+}
+
 int run_forward(const void* x, const float* router_logits, const void* w13, const float* s13,
                 const void* w2, const float* s2, void* out, int M, int h, int i, int E, int k,
                 void* workspace, size_t workspace_bytes, hipEvent_t* events, int n_events,
-                hipStream_t stream, int n_stages = 1 << 30) {
+                hipStream_t stream, int n_stages = 1 << 30, int path = -1) {
     int rc = check_shape(M, h, i, E, k);
     if (rc != MOE_OK) return rc;
     if (M == 0) return MOE_OK;
@@ -203,8 +322,9 @@ int run_forward(const void* x, const float* router_logits, const void* w13, cons
     if (!aligned16(x) || !aligned16(router_logits) || !aligned16(w13) || !aligned16(s13) ||
         !aligned16(w2) || !aligned16(s2) || !aligned16(out))
         return MOE_ERR_INVALID;
+    if (path >= 0 && !path_ok(path, M, h, i, E, k, false)) return MOE_ERR_UNSUPPORTED;
     Layout L;
-    make_layout(M, h, i, E, k, &L);
+    make_layout(M, h, i, E, k, &L, false, path);
     if (!workspace || ((uintptr_t)workspace % kAlign) != 0 || workspace_bytes < L.pub.total)
         return MOE_ERR_WORKSPACE;
 
@@ -222,18 +342,9 @@ int run_forward(const void* x, const float* router_logits, const void* w13, cons
     int32_t* hist = at<int32_t>(workspace, L.hist);
     float* g = p.path == MOE_FP8_PATH_STREAM ? at<float>(workspace, p.gate_up) : nullptr;
     float* y = p.path != MOE_FP8_PATH_FUSED_DECODE ? at<float>(workspace, p.partial) : nullptr;
-    int32_t* mtile_off = at<int32_t>(workspace, L.mtile_off);
     EventHook hook{events, n_events, 0, stream, n_stages};
     uint32_t* sync = at<uint32_t>(workspace, 0);
 
-#define MOE_STEP(call)                 \
-    do {                               \
-        if (hook.cut()) return MOE_OK; \
-        hook.arm();                    \
-        rc = hip_status(call);         \
-        EventHook::disarm();           \
-        if (rc != MOE_OK) return rc;   \
-    } while (0)
 
     if (p.path == MOE_FP8_PATH_FUSED_DECODE) {
         moe::FusedArgs fa;
@@ -264,40 +375,16 @@ int run_forward(const void* x, const float* router_logits, const void* w13, cons
         MOE_STEP(moe::launch_fused_decode(fa, stream));
         return MOE_OK;
     }
-    if (p.path == MOE_FP8_PATH_STREAM && small_group(M, k)) {
+    if (p.path == MOE_FP8_PATH_PREFILL || p.path == MOE_FP8_PATH_PRODUCER)
+        return tiled_forward(L, workspace, x, router_logits, w13, s13, nullptr, w2, s2, nullptr, out, M, h, i, E, k,
+                             hook, stream);
+    if (small_group(M, k)) {
         MOE_STEP(moe::launch_route_quant_group(router_logits, static_cast<const uint16_t*>(x), M, E, k, h,
                                                ids, tw, xq, xs, counts, offsets, sorted, active,
                                                num_active, sync + moe::kSyncArrive / 4, stream));
     } else {
         MOE_STEP(moe::launch_route_quant(router_logits, static_cast<const uint16_t*>(x), M, E, k, h,
                                          ids, tw, xq, xs, moe::kRoute | moe::kQuant, stream));
-    }
-    if (p.path == MOE_FP8_PATH_PREFILL) {
-        MOE_STEP(moe::launch_group(ids, R, E, hist, counts, offsets, sorted, active, num_active,
-                                   stream, moe::prefill_tile_m(), mtile_off));
-        moe::PrefillArgs pa;
-        pa.xq = xq;
-        pa.xs = xs;
-        pa.w13 = static_cast<const uint8_t*>(w13);
-        pa.s13 = s13;
-        pa.e13 = nullptr;
-        pa.w2 = static_cast<const uint8_t*>(w2);
-        pa.s2 = s2;
-        pa.e2 = nullptr;
-        pa.offsets = offsets;
-        pa.sorted = sorted;
-        pa.mtile_off = mtile_off;
-        pa.a2 = at<uint8_t>(workspace, p.act2);
-        pa.a2s = at<float>(workspace, p.act2_scale);
-        pa.y = at<uint16_t>(workspace, p.partial);
-        pa.h = h;
-        pa.i = i;
-        pa.E = E;
-        pa.k = k;
-        MOE_STEP(moe::launch_prefill_gate_up(pa, false, stream));
-        MOE_STEP(moe::launch_prefill_down(pa, false, stream));
-        MOE_STEP(moe::launch_combine_bf16(pa.y, tw, M, k, h, static_cast<uint16_t*>(out), stream));
-        return MOE_OK;
     }
     if (!small_group(M, k))
         MOE_STEP(moe::launch_group(ids, R, E, hist, counts, offsets, sorted, active, num_active,
@@ -315,7 +402,6 @@ int run_forward(const void* x, const float* router_logits, const void* w13, cons
                                         stream));
     MOE_STEP(moe::launch_stream_down(sa, g, static_cast<const uint8_t*>(w2), s2, y, stream));
     MOE_STEP(moe::launch_combine(y, tw, M, k, h, static_cast<uint16_t*>(out), stream));
-#undef MOE_STEP
     return MOE_OK;
 }
 
@@ -325,7 +411,7 @@ int run_forward(const void* x, const float* router_logits, const void* w13, cons
 int run_forward_mx(const void* x, const float* router_logits, const void* w13, const void* e13, const void* w2,
                    const void* e2, void* out, int M, int h, int i, int E, int k, void* workspace,
                    size_t workspace_bytes, hipStream_t stream, int n_stages = 1 << 30,
-                   hipEvent_t* events = nullptr, int n_events = 0) {
+                   hipEvent_t* events = nullptr, int n_events = 0, int path = -1) {
     int rc = check_shape(M, h, i, E, k);
     if (rc != MOE_OK) return rc;
     if (M == 0) return MOE_OK;
@@ -333,8 +419,9 @@ int run_forward_mx(const void* x, const float* router_logits, const void* w13, c
     if (!aligned16(x) || !aligned16(router_logits) || !aligned16(w13) || !aligned16(w2) || !aligned16(out) ||
         ((uintptr_t)e13 & 3u) != 0 || ((uintptr_t)e2 & 3u) != 0)
         return MOE_ERR_INVALID;
+    if (path >= 0 && !path_ok(path, M, h, i, E, k, true)) return MOE_ERR_UNSUPPORTED;
     Layout L;
-    make_layout(M, h, i, E, k, &L, true);
+    make_layout(M, h, i, E, k, &L, true, path);
     if (!workspace || ((uintptr_t)workspace % kAlign) != 0 || workspace_bytes < L.pub.total)
         return MOE_ERR_WORKSPACE;
     const moe_fp8_ws_layout& p = L.pub;
@@ -351,44 +438,9 @@ int run_forward_mx(const void* x, const float* router_logits, const void* w13, c
     int32_t* hist = at<int32_t>(workspace, L.hist);
     uint32_t* sync = at<uint32_t>(workspace, 0);
     EventHook hook{events, n_events, 0, stream, n_stages};
-#define MOE_STEP(call)                 \
-    do {                               \
-        if (hook.cut()) return MOE_OK; \
-        hook.arm();                    \
-        rc = hip_status(call);         \
-        EventHook::disarm();           \
-        if (rc != MOE_OK) return rc;   \
-    } while (0)
-    if (p.path == MOE_FP8_PATH_PREFILL) {
-        int32_t* mtile_off = at<int32_t>(workspace, L.mtile_off);
-        MOE_STEP(moe::launch_route_quant(router_logits, static_cast<const uint16_t*>(x), M, E, k, h, ids, tw, xq,
-                                         xs, moe::kRoute | moe::kQuant, stream));
-        MOE_STEP(moe::launch_group(ids, R, E, hist, counts, offsets, sorted, active, num_active, stream,
-                                   moe::prefill_tile_m(), mtile_off));
-        moe::PrefillArgs pa;
-        pa.xq = xq;
-        pa.xs = xs;
-        pa.w13 = static_cast<const uint8_t*>(w13);
-        pa.s13 = nullptr;
-        pa.e13 = static_cast<const uint8_t*>(e13);
-        pa.w2 = static_cast<const uint8_t*>(w2);
-        pa.s2 = nullptr;
-        pa.e2 = static_cast<const uint8_t*>(e2);
-        pa.offsets = offsets;
-        pa.sorted = sorted;
-        pa.mtile_off = mtile_off;
-        pa.a2 = at<uint8_t>(workspace, p.act2);
-        pa.a2s = at<float>(workspace, p.act2_scale);
-        pa.y = at<uint16_t>(workspace, p.partial);
-        pa.h = h;
-        pa.i = i;
-        pa.E = E;
-        pa.k = k;
-        MOE_STEP(moe::launch_prefill_gate_up(pa, true, stream));
-        MOE_STEP(moe::launch_prefill_down(pa, true, stream));
-        MOE_STEP(moe::launch_combine_bf16(pa.y, tw, M, k, h, static_cast<uint16_t*>(out), stream));
-        return MOE_OK;
-    }
+    if (p.path == MOE_FP8_PATH_PREFILL || p.path == MOE_FP8_PATH_PRODUCER)
+        return tiled_forward(L, workspace, x, router_logits, w13, nullptr, e13, w2, nullptr, e2, out, M, h, i, E, k,
+                             hook, stream);
     float* g = at<float>(workspace, p.gate_up);
     float* y = at<float>(workspace, p.partial);
     if (small_group(M, k)) {
@@ -414,7 +466,6 @@ int run_forward_mx(const void* x, const float* router_logits, const void* w13, c
     MOE_STEP(moe::launch_stream_down_mx(sa, g, static_cast<const uint8_t*>(w2), static_cast<const uint8_t*>(e2),
                                         y, stream));
     MOE_STEP(moe::launch_combine(y, tw, M, k, h, static_cast<uint16_t*>(out), stream));
-#undef MOE_STEP
     return MOE_OK;
 }
 
@@ -430,6 +481,21 @@ int moe_mxfp4_workspace_layout(int M, int h, int i, int E, int k, moe_fp8_ws_lay
     make_layout(M, h, i, E, k, &L, true);
     *layout = L.pub;
     return MOE_OK;
+}
+
+size_t moe_mxfp4_workspace_bytes_path(int M, int h, int i, int E, int k, int path) {
+    if (M == 0 || check_shape(M, h, i, E, k) != MOE_OK || !path_ok(path, M, h, i, E, k, true)) return 0;
+    Layout L;
+    make_layout(M, h, i, E, k, &L, true, path);
+    return L.pub.total;
+}
+
+int moe_mxfp4_forward_ws_path(const void* x, const float* router_logits, const void* w13, const void* e13,
+                              const void* w2, const void* e2, void* out, int M, int h, int i, int E, int k,
+                              void* workspace, size_t workspace_bytes, int path, hipStream_t stream) {
+    if (path < 0) return MOE_ERR_INVALID;
+    return run_forward_mx(x, router_logits, w13, e13, w2, e2, out, M, h, i, E, k, workspace, workspace_bytes,
+                          stream, 1 << 30, nullptr, 0, path);
 }
 
 int moe_mxfp4_forward_kernel_count(int M, int h, int i, int E, int k) {
@@ -498,6 +564,32 @@ int moe_fp8_workspace_layout(int M, int h, int i, int E, int k, moe_fp8_ws_layou
     make_layout(M, h, i, E, k, &L);
     *layout = L.pub;
     return MOE_OK;
+}
+
+size_t moe_fp8_workspace_bytes_path(int M, int h, int i, int E, int k, int path) {
+    if (M == 0 || check_shape(M, h, i, E, k) != MOE_OK || !path_ok(path, M, h, i, E, k, false)) return 0;
+    Layout L;
+    make_layout(M, h, i, E, k, &L, false, path);
+    return L.pub.total;
+}
+
+int moe_fp8_workspace_layout_path(int M, int h, int i, int E, int k, int path, moe_fp8_ws_layout* layout) {
+    if (!layout) return MOE_ERR_INVALID;
+    const int rc = check_shape(M, h, i, E, k);
+    if (rc != MOE_OK) return rc;
+    if (!path_ok(path, M, h, i, E, k, false)) return MOE_ERR_UNSUPPORTED;
+    Layout L;
+    make_layout(M, h, i, E, k, &L, false, path);
+    *layout = L.pub;
+    return MOE_OK;
+}
+
+int moe_fp8_forward_ws_path(const void* x, const float* router_logits, const void* w13, const float* s13,
+                            const void* w2, const float* s2, void* out, int M, int h, int i, int E, int k,
+                            void* workspace, size_t workspace_bytes, int path, hipStream_t stream) {
+    if (path < 0) return MOE_ERR_INVALID;
+    return run_forward(x, router_logits, w13, s13, w2, s2, out, M, h, i, E, k, workspace, workspace_bytes,
+                       nullptr, 0, stream, 1 << 30, path);
 }
 
 size_t moe_fp8_workspace_bytes(int M, int h, int i, int E, int k) {

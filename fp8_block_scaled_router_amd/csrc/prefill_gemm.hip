@@ -48,7 +48,10 @@
 #include <algorithm>
 
 #include "device.h"
+#include "fused_decode.h"
+#include "group.h"
 #include "launch.h"
+#include "route_quant.h"
 
 namespace moe {
 namespace {
@@ -96,12 +99,30 @@ struct TileMeta {
     int offsets[kMaxE + 1];     // first sorted route of each expert
 };
 
+// kCoh: the lists were written by other workgroups of the same launch.
+template <bool kCoh = false>
 __device__ __forceinline__ void load_meta(TileMeta& m, const PrefillArgs& a, int tid) {
     for (int j = tid; j <= a.E; j += kThreads) {
-        m.mtile_off[j] = a.mtile_off[j];
-        m.offsets[j] = a.offsets[j];
+        m.mtile_off[j] = ld_i32<kCoh>(a.mtile_off + j);
+        m.offsets[j] = ld_i32<kCoh>(a.offsets + j);
     }
 }
+
+// LDS of a tiled kernel: the ring of three stage buffers, the tile lists (per
+// tile parity) and the epilogue's row maxima.  The producer runs both GEMMs
+// on it in turn and uses the ring as scratch for its routing and grouping.
+// (The small lists come first: their addresses then fit the DS
+// instructions' 16-bit offsets.)
+template <bool kMx>
+struct TileLds {
+    int rt[2][kBM];             // route id of each row (padding rows repeat the last route)
+    float amax[4][kBM];         // gate/up epilogue: row maxima of the four column quarters
+    float sw[2][2 * kMaxKB];    // FP8 weight scales: gate then up per K block, or the down tile's two row blocks
+    TileMeta meta;
+    int flag;                   // producer: this workgroup gives up the forward (a wait timed out)
+    int last;                   // producer: this workgroup is the last to finish
+    alignas(16) uint8_t stages[3 * Fmt<kMx>::kStage];
+};
 
 // Expert owning M-tile mt: the largest e with mtile_off[e] <= mt.
 __device__ __forceinline__ int tile_expert(const int* mtile_off, int E, int mt) {
@@ -154,20 +175,34 @@ struct Loop {
 // other vector-memory operation whose waits the compiler would place.  M0
 // holds the wave's LDS destination; lane l's data lands at M0 + 16 l (4 l
 // for the dword form).  One wait state separates the M0 write from the copy.
+// kCoh: the copy reads at device scope (sc1), so it sees data that another
+// workgroup of the same launch wrote with device-scope stores, whatever
+// this XCD's L2 holds.
+template <bool kCoh = false>
 __device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                 :: "s"(lds), "v"(src) : "memory", "m0");
+    if constexpr (kCoh)
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off sc1"
+                     :: "s"(lds), "v"(src) : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                     :: "s"(lds), "v"(src) : "memory", "m0");
 }
+template <bool kCoh = false>
 __device__ __forceinline__ void copy4_to_lds(const void* src, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
-                 :: "s"(lds), "v"(src) : "memory", "m0");
+    if constexpr (kCoh)
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off sc1"
+                     :: "s"(lds), "v"(src) : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+                     :: "s"(lds), "v"(src) : "memory", "m0");
 }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// Issue the copies of K block kb into stage buffer st.
-template <bool kMx>
+// Issue the copies of K block kb into stage buffer st (kCoh: the activation
+// tile and its scales at device scope).
+template <bool kMx, bool kCoh = false>
 __device__ __forceinline__ void issue_stage(const Loop& L, uint8_t* st, int kb) {
     using F = Fmt<kMx>;
     const uint8_t* gA = L.gA + (size_t)kb * F::kRowBytes;
@@ -176,9 +211,10 @@ __device__ __forceinline__ void issue_stage(const Loop& L, uint8_t* st, int kb) 
 #pragma unroll
     for (int q = 0; q < F::kDmaA; ++q) copy16_to_lds(gA + L.offA[q], base + (L.wave * F::kDmaA + q) * 1024);
 #pragma unroll
-    for (int q = 0; q < kDmaB; ++q) copy16_to_lds(gB + L.offB[q], base + F::kBOff + (L.wave * kDmaB + q) * 1024);
+    for (int q = 0; q < kDmaB; ++q)
+        copy16_to_lds<kCoh>(gB + L.offB[q], base + F::kBOff + (L.wave * kDmaB + q) * 1024);
     // scales of routes 16 wave .. +16 (lanes 16..63 repeat lanes 0..15)
-    copy4_to_lds(L.gX + L.offX + kb, base + F::kXOff + L.wave * 256);
+    copy4_to_lds<kCoh>(L.gX + L.offX + kb, base + F::kXOff + L.wave * 256);
     // (MXFP4) the four scale bytes of K block kb of weight rows 32 wave ..
     // +32 (lanes 32..63 repeat lanes 0..31)
     if constexpr (kMx) copy4_to_lds(L.gS + L.offS + 4 * kb, base + F::kAB + L.wave * 256);
@@ -244,15 +280,15 @@ __device__ __forceinline__ void block_mma(v4f acc[16], v4f blk[16], float sw_p[4
 // sw_of(kb, sw) fills the wave's four weight-tile scales of block kb (FP8
 // weights).  The copies of blocks 0 and 1 (into buffers 0 and 1) are issued
 // by the caller, possibly long before (issue_first).
-template <bool kMx>
+template <bool kMx, bool kCoh = false>
 __device__ __forceinline__ void issue_first(const Loop& L, int KB, uint8_t* stages) {
-    issue_stage<kMx>(L, stages, 0);
-    if (KB > 1) issue_stage<kMx>(L, stages + Fmt<kMx>::kStage, 1);
+    issue_stage<kMx, kCoh>(L, stages, 0);
+    if (KB > 1) issue_stage<kMx, kCoh>(L, stages + Fmt<kMx>::kStage, 1);
 }
 
 // after_first() runs once, right after the first barrier: every wave has
 // then finished whatever it did before the loop.
-template <bool kMx, typename SwOf, typename AfterFirst>
+template <bool kMx, bool kCoh, typename SwOf, typename AfterFirst>
 __device__ __forceinline__ void k_loop(v4f acc[16], const Loop& L, int KB, uint8_t* stages, SwOf sw_of,
                                        AfterFirst after_first) {
     using F = Fmt<kMx>;
@@ -265,7 +301,7 @@ __device__ __forceinline__ void k_loop(v4f acc[16], const Loop& L, int KB, uint8
         if (kb + 1 < KB) __builtin_amdgcn_s_waitcnt(vm_wait(F::kVmem));
         else __builtin_amdgcn_s_waitcnt(vm_wait(0));
         block_barrier();
-        if (kb + 2 < KB) issue_stage<kMx>(L, stages + (rd == 0 ? 2 : rd - 1) * F::kStage, kb + 2);
+        if (kb + 2 < KB) issue_stage<kMx, kCoh>(L, stages + (rd == 0 ? 2 : rd - 1) * F::kStage, kb + 2);
         if (kb == 0) after_first();
         if constexpr (!kMx) sw_of(kb, sw);
         block_mma<kMx>(acc, blk, sw_p, xr_p, L, stages + rd * F::kStage, sw);
@@ -360,6 +396,46 @@ __device__ __forceinline__ TileInfo decode_tile(const TileMeta& meta, int E, int
 
 }  // namespace
 
+// ------------------------------------------------- producer synchronisation
+
+constexpr uint64_t kProdWaitTicks = 100000000;   // 1 s of the 100 MHz constant clock
+
+// Thread 0 of a workgroup: waits until the device-scope word *ctr reaches n,
+// with a growing sleep between polls.  Returns false when the wait timed out
+// (the error word then carries kErrProducer).
+__device__ __forceinline__ bool wait_count(const uint32_t* ctr, uint32_t n, uint32_t* err) {
+    uint64_t t0 = 0;
+    int nap = 1;
+    for (int tries = 0;; ++tries) {
+        if (ld_agent(ctr) >= n) return true;
+        if (tries == 0) t0 = wall_clock64();
+        if (wall_clock64() - t0 > kProdWaitTicks) {
+            atomicOr(err, kErrProducer);
+            return false;
+        }
+        for (int z = 0; z < nap; ++z) __builtin_amdgcn_s_sleep(2);
+        nap = nap < 8 ? 2 * nap : 8;
+    }
+}
+
+// Every workgroup of the grid arrives once at the device-scope word *ctr;
+// returns when all n have (false when the wait timed out, and then also for
+// the rest of the forward through flag).  Each workgroup's stores have
+// completed before it arrives.  What one workgroup hands to another across a
+// barrier is stored and loaded at device scope, so no cache needs writing
+// back or invalidating (an agent-scope fence does both to a whole XCD L2,
+// which measured about 11 us per barrier here).
+__device__ __forceinline__ bool grid_barrier(uint32_t* ctr, uint32_t n, uint32_t* err, int tid, int& flag) {
+    wait_vmem();
+    __syncthreads();
+    if (tid == 0) {
+        __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (!wait_count(ctr, n, err)) flag = 1;
+    }
+    __syncthreads();
+    return flag == 0;
+}
+
 // ----------------------------------------------------------------- gate/up
 
 namespace {
@@ -412,7 +488,10 @@ __device__ __forceinline__ Loop gate_up_loop(const PrefillArgs& a, const TileInf
 // reciprocal (a few ulp from the correctly rounded quotient; the FP8 block
 // sums feeding it carry far larger error).  The codes are staged in LDS
 // (codes, rows of 144 bytes so the 4-byte writes of 16 routes hit distinct
-// banks) and leave as whole 128-byte rows.
+// banks) and leave as whole 128-byte rows.  kCoh: the codes and scales go
+// out with device-scope stores (the producer's down tiles read them in the
+// same launch, possibly on another XCD).
+template <bool kCoh>
 __device__ __forceinline__ void gate_up_epilogue(const PrefillArgs& a, const TileInfo& t, v4f acc[16],
                                                  float (*amax_l)[kBM], uint8_t* codes, int tid) {
     const int i = a.i, IB = i / 128;
@@ -447,32 +526,45 @@ __device__ __forceinline__ void gate_up_epilogue(const PrefillArgs& a, const Til
             *reinterpret_cast<uint32_t*>(codes + r * 144 + 32 * wn + 16 * j + 4 * kg) =
                 sc == 0.0f ? 0u : quant4(vv[0], vv[1], vv[2], vv[3], sc, rc);
         }
-        if (wn == 0 && kg == 0 && r < t.rows) a.a2s[(size_t)(t.beg + r) * IB + t.sub] = sc;
+        if (wn == 0 && kg == 0 && r < t.rows) {
+            float* ds = a.a2s + (size_t)(t.beg + r) * IB + t.sub;
+            if constexpr (kCoh) st_agent(ds, sc);
+            else *ds = sc;
+        }
     }
     __syncthreads();
     const int r = tid >> 2, c = (tid & 3) * 32;   // 4 threads per route row, 32 bytes each
     if (r < t.rows) {
         const uint4* src = reinterpret_cast<const uint4*>(codes + r * 144 + c);
         uint4* dst = reinterpret_cast<uint4*>(a.a2 + (size_t)(t.beg + r) * i + t.sub * 128 + c);
-        dst[0] = src[0];
-        dst[1] = src[1];
+        if constexpr (kCoh) {
+            const uint64_t* s64 = reinterpret_cast<const uint64_t*>(src);
+            uint64_t* d64 = reinterpret_cast<uint64_t*>(dst);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) st_agent64(d64 + q, s64[q]);
+        } else {
+            dst[0] = src[0];
+            dst[1] = src[1];
+        }
     }
 }
 
-template <bool kMx>
-__device__ __forceinline__ void gate_up_tiles(const PrefillArgs& a) {
+// The gate/up tiles of this workgroup's share.  kProd (the producer): the
+// route lists, activation codes and scales (written earlier in the same
+// launch) are read at device scope, the requantised codes and scales go out
+// at device scope, and each finished tile counts itself in its M-tile's word
+// of a.done.
+template <bool kMx, bool kProd>
+__device__ __forceinline__ void gate_up_tiles(const PrefillArgs& a, TileLds<kMx>& S) {
     using F = Fmt<kMx>;
-    __shared__ __align__(16) uint8_t stages[3 * F::kStage];
-    __shared__ int rt_l[2][kBM];                // route id of each row, per tile parity
-    __shared__ float amax_l[4][kBM];
-    __shared__ float sw_l[2][2][kMaxKB];        // (FP8) gate / up weight scales per K block, per tile parity
-    __shared__ TileMeta meta;
+    uint8_t* const stages = S.stages;
+    TileMeta& meta = S.meta;
 
     const int h = a.h, i = a.i, E = a.E;
     const int KB = h / 128, IB = i / 128, N13 = 2 * i;
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
 
-    load_meta(meta, a, tid);
+    load_meta<kProd>(meta, a, tid);
     __syncthreads();
     TileSpan span = tile_span(meta.mtile_off[E] * IB);
     if (span.next >= span.end) return;
@@ -480,16 +572,16 @@ __device__ __forceinline__ void gate_up_tiles(const PrefillArgs& a) {
     TileInfo t = decode_tile(meta, E, IB, span.next);
     int par = 0;
     // padding rows repeat the tile's last route (their outputs are dropped)
-    for (int r = tid; r < kBM; r += kThreads) rt_l[0][r] = a.sorted[t.beg + min(r, t.rows - 1)];
+    for (int r = tid; r < kBM; r += kThreads) S.rt[0][r] = ld_i32<kProd>(a.sorted + t.beg + min(r, t.rows - 1));
     if constexpr (!kMx) {
         for (int j = tid; j < KB; j += kThreads) {
-            sw_l[0][0][j] = a.s13[((size_t)t.e * (N13 / 128) + t.sub) * KB + j];
-            sw_l[0][1][j] = a.s13[((size_t)t.e * (N13 / 128) + IB + t.sub) * KB + j];
+            S.sw[0][j] = a.s13[((size_t)t.e * (N13 / 128) + t.sub) * KB + j];
+            S.sw[0][kMaxKB + j] = a.s13[((size_t)t.e * (N13 / 128) + IB + t.sub) * KB + j];
         }
     }
     __syncthreads();
-    Loop L = gate_up_loop<kMx>(a, t, rt_l[0], wave, lane);
-    issue_first<kMx>(L, KB, stages);
+    Loop L = gate_up_loop<kMx>(a, t, S.rt[0], wave, lane);
+    issue_first<kMx, kProd>(L, KB, stages);
 
     for (;;) {
         span.next += span.step;
@@ -506,27 +598,33 @@ __device__ __forceinline__ void gate_up_tiles(const PrefillArgs& a) {
             if (!more) return;
             if (wave < 2) {
                 const int r = 64 * wave + lane;
-                copy4_to_lds(a.sorted + tn.beg + min(r, tn.rows - 1), lds_addr(&rt_l[par ^ 1][64 * wave]));
+                copy4_to_lds<kProd>(a.sorted + tn.beg + min(r, tn.rows - 1), lds_addr(&S.rt[par ^ 1][64 * wave]));
             } else if (!kMx && wave < 4) {
                 const int half = wave - 2;
                 const float* src = a.s13 + ((size_t)tn.e * (N13 / 128) + half * IB + tn.sub) * KB;
                 for (int c = 0; 64 * c < KB; ++c)
-                    copy4_to_lds(src + min(64 * c + lane, KB - 1), lds_addr(&sw_l[par ^ 1][half][64 * c]));
+                    copy4_to_lds(src + min(64 * c + lane, KB - 1), lds_addr(&S.sw[par ^ 1][half * kMaxKB + 64 * c]));
             }
         };
         auto sw_of = [&](int kb, float sw[4]) {
-            const float g = sw_l[par][0][kb], u = sw_l[par][1][kb];
+            const float g = S.sw[par][kb], u = S.sw[par][kMaxKB + kb];
             sw[0] = g; sw[1] = g; sw[2] = u; sw[3] = u;
         };
         v4f acc[16];
 #pragma unroll
         for (int u = 0; u < 16; ++u) acc[u] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-        k_loop<kMx>(acc, L, KB, stages, sw_of, next_lists);   // ends with every wave done with the stage buffers
+        k_loop<kMx, kProd>(acc, L, KB, stages, sw_of, next_lists);   // ends with every wave done with the stage buffers
         if (more) {
-            L = gate_up_loop<kMx>(a, tn, rt_l[par ^ 1], wave, lane);
-            issue_first<kMx>(L, KB, stages);   // buffers 0 and 1; the epilogue stages codes in buffer 2
+            L = gate_up_loop<kMx>(a, tn, S.rt[par ^ 1], wave, lane);
+            issue_first<kMx, kProd>(L, KB, stages);   // buffers 0 and 1; the epilogue stages codes in buffer 2
         }
-        gate_up_epilogue(a, t, acc, amax_l, stages + 2 * F::kStage, tid);
+        gate_up_epilogue<kProd>(a, t, acc, S.amax, stages + 2 * F::kStage, tid);
+        if constexpr (kProd) {
+            // every wave's stores of the tile have completed before it counts
+            wait_vmem();
+            __syncthreads();
+            if (tid == 0) __hip_atomic_fetch_add(a.done + t.mt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         if (!more) break;
         t = tn;
         par ^= 1;
@@ -535,8 +633,14 @@ __device__ __forceinline__ void gate_up_tiles(const PrefillArgs& a) {
 
 }  // namespace
 
-__global__ __launch_bounds__(kThreads, 1) void prefill_gate_up_kernel(PrefillArgs a) { gate_up_tiles<false>(a); }
-__global__ __launch_bounds__(kThreads, 1) void prefill_gate_up_mx_kernel(PrefillArgs a) { gate_up_tiles<true>(a); }
+__global__ __launch_bounds__(kThreads, 1) void prefill_gate_up_kernel(PrefillArgs a) {
+    __shared__ TileLds<false> S;
+    gate_up_tiles<false, false>(a, S);
+}
+__global__ __launch_bounds__(kThreads, 1) void prefill_gate_up_mx_kernel(PrefillArgs a) {
+    __shared__ TileLds<true> S;
+    gate_up_tiles<true, false>(a, S);
+}
 
 // -------------------------------------------------------------------- down
 
@@ -578,13 +682,14 @@ __device__ __forceinline__ Loop down_loop(const PrefillArgs& a, const TileInfo& 
     return L;
 }
 
-template <bool kMx>
-__device__ __forceinline__ void down_tiles(const PrefillArgs& a) {
-    using F = Fmt<kMx>;
-    __shared__ __align__(16) uint8_t stages[3 * F::kStage];
-    __shared__ int prt_l[2][kBM];               // route id of each row (padding repeats the last), per tile parity
-    __shared__ float sw_l[2][2 * kMaxKB];       // (FP8) the tile's two 128-row scale blocks, per tile parity
-    __shared__ TileMeta meta;
+// The down tiles of this workgroup's share.  kProd (the producer): a tile
+// starts only once every gate/up tile of its M-tile has counted itself in
+// (a.done), and reads their codes and scales at device scope; a wait that
+// times out makes the workgroup give up the rest of its share.
+template <bool kMx, bool kProd>
+__device__ __forceinline__ void down_tiles(const PrefillArgs& a, TileLds<kMx>& S) {
+    uint8_t* const stages = S.stages;
+    TileMeta& meta = S.meta;
 
     const int h = a.h, i = a.i, E = a.E;
     const int IB = i / 128, NT = h / kBN;
@@ -592,20 +697,33 @@ __device__ __forceinline__ void down_tiles(const PrefillArgs& a) {
     const int col = lane & 15, kg = lane >> 4;
     const int wr = wave & 1, wn = wave >> 1;
 
-    load_meta(meta, a, tid);
+    load_meta<kProd>(meta, a, tid);
     __syncthreads();
     TileSpan span = tile_span(meta.mtile_off[E] * NT);
     if (span.next >= span.end) return;
 
+    // (producer) every wave waits until M-tile mt's IB gate/up tiles are done
+    auto ready = [&](int mt) -> bool {
+        if constexpr (kProd) {
+            if (tid == 0 && S.flag == 0 && !wait_count(a.done + mt, (uint32_t)IB, a.err)) S.flag = 1;
+            __syncthreads();
+            return S.flag == 0;
+        } else {
+            (void)mt;
+            return true;
+        }
+    };
+
     TileInfo t = decode_tile(meta, E, NT, span.next);
     int par = 0;
-    for (int r = tid; r < kBM; r += kThreads) prt_l[0][r] = a.sorted[t.beg + min(r, t.rows - 1)];
+    for (int r = tid; r < kBM; r += kThreads) S.rt[0][r] = ld_i32<kProd>(a.sorted + t.beg + min(r, t.rows - 1));
     if constexpr (!kMx) {   // j < 2 IB: scale blocks 2 sub and 2 sub + 1
-        for (int j = tid; j < 2 * IB; j += kThreads) sw_l[0][j] = a.s2[((size_t)t.e * (h / 128) + 2 * t.sub) * IB + j];
+        for (int j = tid; j < 2 * IB; j += kThreads) S.sw[0][j] = a.s2[((size_t)t.e * (h / 128) + 2 * t.sub) * IB + j];
     }
     __syncthreads();
+    if (!ready(t.mt)) return;
     Loop L = down_loop<kMx>(a, t, wave, lane);
-    issue_first<kMx>(L, IB, stages);
+    issue_first<kMx, kProd>(L, IB, stages);
 
     const int sblk = wn >> 1;
     for (;;) {
@@ -619,24 +737,25 @@ __device__ __forceinline__ void down_tiles(const PrefillArgs& a) {
             if (!more) return;
             if (wave < 2) {
                 const int r = 64 * wave + lane;
-                copy4_to_lds(a.sorted + tn.beg + min(r, tn.rows - 1), lds_addr(&prt_l[par ^ 1][64 * wave]));
+                copy4_to_lds<kProd>(a.sorted + tn.beg + min(r, tn.rows - 1), lds_addr(&S.rt[par ^ 1][64 * wave]));
             } else if (!kMx && 64 * (wave - 2) < 2 * IB) {
                 const int c = wave - 2;
                 const float* src = a.s2 + ((size_t)tn.e * (h / 128) + 2 * tn.sub) * IB;
-                copy4_to_lds(src + min(64 * c + lane, 2 * IB - 1), lds_addr(&sw_l[par ^ 1][64 * c]));
+                copy4_to_lds(src + min(64 * c + lane, 2 * IB - 1), lds_addr(&S.sw[par ^ 1][64 * c]));
             }
         };
         auto sw_of = [&](int kb, float sw[4]) {
-            const float w = sw_l[par][sblk * IB + kb];
+            const float w = S.sw[par][sblk * IB + kb];
             sw[0] = w; sw[1] = w; sw[2] = w; sw[3] = w;
         };
         v4f acc[16];
 #pragma unroll
         for (int u = 0; u < 16; ++u) acc[u] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-        k_loop<kMx>(acc, L, IB, stages, sw_of, next_lists);
+        k_loop<kMx, kProd>(acc, L, IB, stages, sw_of, next_lists);
         if (more) {
+            if (!ready(tn.mt)) return;   // no copy is in flight here
             L = down_loop<kMx>(a, tn, wave, lane);
-            issue_first<kMx>(L, IB, stages);
+            issue_first<kMx, kProd>(L, IB, stages);
         }
         // bf16 partial rows (round to nearest even) by route id; lane holds
         // output rows sub * 256 + 64 wn + 16 j + 4 kg + v of route
@@ -645,7 +764,7 @@ __device__ __forceinline__ void down_tiles(const PrefillArgs& a) {
         for (int m = 0; m < 4; ++m) {
             const int row = 64 * wr + 16 * m + col;
             if (row >= t.rows) continue;
-            const int p = prt_l[par][row];
+            const int p = S.rt[par][row];
             uint16_t* dst = a.y + (size_t)p * h + t.sub * kBN + 64 * wn + 4 * kg;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -661,8 +780,120 @@ __device__ __forceinline__ void down_tiles(const PrefillArgs& a) {
 
 }  // namespace
 
-__global__ __launch_bounds__(kThreads, 1) void prefill_down_kernel(PrefillArgs a) { down_tiles<false>(a); }
-__global__ __launch_bounds__(kThreads, 1) void prefill_down_mx_kernel(PrefillArgs a) { down_tiles<true>(a); }
+__global__ __launch_bounds__(kThreads, 1) void prefill_down_kernel(PrefillArgs a) {
+    __shared__ TileLds<false> S;
+    down_tiles<false, false>(a, S);
+}
+__global__ __launch_bounds__(kThreads, 1) void prefill_down_mx_kernel(PrefillArgs a) {
+    __shared__ TileLds<true> S;
+    down_tiles<true, false>(a, S);
+}
+
+// ---------------------------------------------------------------- producer
+
+namespace {
+
+// The whole layer but the route reducer in one launch (the producer of the
+// Netra Kernel README's MoE prefill pair: routing, gate/up, SiLU and
+// requantisation, down-partial and metadata in one code object; the
+// reducer, combine_bf16_kernel, is the second).  One workgroup per CU, all
+// resident at once:
+//   1. every workgroup routes and quantises its chunk of tpw tokens and
+//      counts the chunk's routes per expert into its row of hist;
+//   2. grid barrier; each chunk sums the counts and scatters its routes in
+//      route order (group_chunk_scatter; chunk 0 writes counts, offsets, the
+//      active list and the M-tile numbering);
+//   3. grid barrier; the gate/up tiles of the workgroup's share, each
+//      counted in its M-tile's word of done once its codes are stored;
+//   4. the down tiles of its share, each after its M-tile's count reaches
+//      i/128.
+// A workgroup reaches step 4 only after all its gate/up tiles, so every wait
+// is for work that waits on nothing, and every wait is bounded in time (a
+// timeout sets kErrProducer in the error word, the workgroup gives up its
+// share, and the reducer writes NaN).  The last workgroup to finish clears
+// the counters for the next forward.
+template <bool kMx>
+__device__ __forceinline__ void producer_tiles(const ProducerArgs& p) {
+    __shared__ TileLds<kMx> S;
+    const PrefillArgs& a = p.pa;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int M = p.M, E = a.E, k = a.k, h = a.h;
+    const uint32_t G = gridDim.x;
+    const int nchunks = (M + p.tpw - 1) / p.tpw;
+    const int t0 = blockIdx.x * p.tpw, t1 = min(M, t0 + p.tpw);
+    int* scr = reinterpret_cast<int*>(S.stages);   // the stage ring is free until step 3
+    uint32_t* bar = p.sync + kSyncProdBar / 4;
+    if (tid == 0) {
+        S.flag = 0;
+        S.last = 0;
+    }
+    for (int e = tid; e < 256; e += kThreads) scr[e] = 0;
+
+    // 1. routing (four tokens per wave and pass) and quantisation (one row
+    // per wave at a time): the loads of a wave's first four rows go out
+    // first and the routing runs under them
+    if (t0 < M) {
+        constexpr int kNW = kThreads / kWave;
+        uint4 u[4][kQuantBatch];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int t = t0 + wave + kNW * j;
+            if (t < t1) act_quant_load(p.x + (size_t)t * h, h, 0, 0, 1, lane, u[j]);
+        }
+        for (int c = wave; t0 + 4 * c < t1; c += kNW) router_rows16(p.logits, t0 + 4 * c, t1, E, k, p.ids, p.tw, lane);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int t = t0 + wave + kNW * j;
+            if (t < t1)
+                act_quant_finish<true>(p.x + (size_t)t * h, h, p.xq + (size_t)t * h, p.xs + (size_t)t * (h / 128), 0,
+                                       1, lane, u[j]);
+        }
+        for (int t = t0 + wave + 4 * kNW; t < t1; t += kNW)
+            act_quant_row<true>(p.x + (size_t)t * h, h, p.xq + (size_t)t * h, p.xs + (size_t)t * (h / 128), 0, 1, lane);
+    }
+    wait_vmem();
+    __syncthreads();
+    if (t0 < M) group_chunk_hist(p.ids, t0 * k, t1 * k, E, scr, tid, kThreads);
+    __syncthreads();
+    if ((int)blockIdx.x < nchunks && tid < E) st_i32<true>(p.hist + (size_t)blockIdx.x * E + tid, scr[tid]);
+    bool ok = grid_barrier(bar, G, a.err, tid, S.flag);
+
+    // 2. grouping
+    if (ok && (int)blockIdx.x < nchunks) {
+        const GroupOut o{p.counts, p.offsets, p.sorted, p.active, p.num_active, p.mtile_off, kBM};
+        group_chunk_scatter<kThreads / 256, true, 32>(p.ids, E, nchunks, p.hist, blockIdx.x, t0 * k, t1 * k,
+                                                      blockIdx.x == 0, o, scr, scr + 512, scr + 1024, tid);
+    }
+    ok = grid_barrier(bar + 1, G, a.err, tid, S.flag);
+
+    // 3., 4. the GEMMs
+    if (ok) gate_up_tiles<kMx, true>(a, S);
+    __syncthreads();
+    if (S.flag == 0) down_tiles<kMx, true>(a, S);
+
+    // the last workgroup to finish clears the counters (all of them after a
+    // timeout, else the M-tiles of this forward)
+    wait_vmem();
+    __syncthreads();
+    if (tid == 0) S.last = __hip_atomic_fetch_add(p.sync + kSyncProdExit / 4, 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT) == G - 1;
+    __syncthreads();
+    if (S.last) {
+        const bool timed_out = (ld_agent(a.err) & kErrProducer) != 0u;
+        const int n = timed_out ? kProdMaxTiles : min(kProdMaxTiles, ld_agent(reinterpret_cast<const uint32_t*>(p.mtile_off) + E));
+        for (int j = tid; j < n; j += kThreads) st_agent(a.done + j, 0u);
+        if (tid == 0) {
+            st_agent(bar, 0u);
+            st_agent(bar + 1, 0u);
+            st_agent(p.sync + kSyncProdExit / 4, 0u);
+        }
+    }
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(kThreads, 1) void prefill_producer_kernel(ProducerArgs p) { producer_tiles<false>(p); }
+__global__ __launch_bounds__(kThreads, 1) void prefill_producer_mx_kernel(ProducerArgs p) { producer_tiles<true>(p); }
 
 int prefill_tile_m() { return kBM; }
 
@@ -687,6 +918,38 @@ static int persistent_grid() {
 
 // mx: the weights are MXFP4 (w13 / w2 codes with e13 / e2 scales), else FP8
 // (with s13 / s2).
+// Every M-tile needs a counter word: at most ceil(R / 128) + E tiles.
+bool producer_supported(int M, int h, int i, int E, int k) {
+    const int64_t R = (int64_t)M * k;
+    return prefill_supported(M, h, i, k) && (R + kBM - 1) / kBM + E <= kProdMaxTiles;
+}
+
+// One workgroup per CU, and all of them resident at once (checked against
+// the kernel's occupancy, cached per device).
+hipError_t launch_prefill_producer(const ProducerArgs& p, bool mx, hipStream_t stream) {
+    const int g = persistent_grid();
+    if (g <= 0 || g > kProdMaxGrid) return hipErrorInvalidDevice;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    static int fits[2][64] = {{0}};   // 0: not known, 1: fits, -1: does not
+    int& f = fits[mx ? 1 : 0][dev];
+    if (f == 0) {
+        int cu = 0, nb = 0;
+        if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return hipErrorInvalidDevice;
+        const hipError_t e = mx ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, prefill_producer_mx_kernel, kThreads, 0)
+                                : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, prefill_producer_kernel, kThreads, 0);
+        if (e != hipSuccess) return hipErrorInvalidConfiguration;
+        f = cu * nb >= g ? 1 : -1;
+    }
+    if (f < 0) return hipErrorInvalidConfiguration;
+    ProducerArgs q = p;
+    q.tpw = std::max(4, (p.M + g - 1) / g);   // at most g routing chunks
+    if (mx) launch(prefill_producer_mx_kernel, dim3(g), dim3(kThreads), 0, stream, q);
+    else launch(prefill_producer_kernel, dim3(g), dim3(kThreads), 0, stream, q);
+    return hipGetLastError();
+}
+
 hipError_t launch_prefill_gate_up(const PrefillArgs& a, bool mx, hipStream_t stream) {
     const int g = persistent_grid();
     if (g <= 0) return hipErrorInvalidDevice;

@@ -17,6 +17,7 @@
 // and writes one fp32 partial row per route (Netra Kernel README, MoE
 // prefill pair: SiLU and quantisation, then down-partial).
 #include "device.h"
+#include "fused_decode.h"
 #include "launch.h"
 
 namespace moe {
@@ -253,11 +254,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 // The same combine over bf16 partials: eight columns per thread.
 __global__ __launch_bounds__(256) void combine_bf16_kernel(const uint16_t* __restrict__ y,
                                                            const float* __restrict__ tw, int k, int h,
-                                                           uint16_t* __restrict__ out) {
+                                                           uint16_t* __restrict__ out, const uint32_t* err) {
 #pragma clang fp contract(off)
     const int t = blockIdx.y;
     const int n = (blockIdx.x * 256 + threadIdx.x) * 8;
     if (n >= h) return;
+    if (err != nullptr && (ld_agent(err) & kErrProducer) != 0u) {   // the producer gave up: NaN
+        *reinterpret_cast<uint4*>(out + (size_t)t * h + n) = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
+        return;
+    }
     v4i v[16];   // streaming loads: every partial is read once
     float w[16];
 #pragma unroll
@@ -283,9 +288,9 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(const uint16_t* __res
 }
 
 hipError_t launch_combine_bf16(const uint16_t* y, const float* tw, int M, int k, int h, uint16_t* out,
-                               hipStream_t stream) {
+                               hipStream_t stream, const uint32_t* err) {
     const dim3 grid((h / 8 + 255) / 256, M);
-    launch(combine_bf16_kernel, grid, dim3(256), 0, stream, y, tw, k, h, out);
+    launch(combine_bf16_kernel, grid, dim3(256), 0, stream, y, tw, k, h, out, err);
     return hipGetLastError();
 }
 

@@ -66,10 +66,22 @@ enum {
  * with few routes per expert run weight-streaming GEMMs; batches with at
  * least 8 routes per expert on average (M*k >= 8*E) and h % 256 == 0 run
  * tiled MFMA grouped GEMMs with the SiLU requantisation fused into the
- * gate/up epilogue. */
+ * gate/up epilogue, in five launches (routing and quantisation, grouping,
+ * gate/up, down, combine).  The same tiled GEMMs also run as the prefill
+ * producer and its route reducer (the Netra Kernel README's MoE prefill
+ * pair, two launches: routing, quantisation, grouping and both GEMMs in one
+ * kernel whose workgroups, one per CU, are all resident at once, then the
+ * fixed-order combine; batches of at most 7168 - E M-tiles of 128 routes),
+ * bit for bit the same result, when a caller asks for that path
+ * (moe_fp8_forward_ws_path). */
 #define MOE_FP8_PATH_STREAM 0
 #define MOE_FP8_PATH_PREFILL 1
 #define MOE_FP8_PATH_FUSED_DECODE 2
+#define MOE_FP8_PATH_PRODUCER 3
+
+/* Bits of the workspace's sticky error word (moe_fp8_workspace_status). */
+#define MOE_FP8_ERR_FUSED_WAIT 1u      /* a wait of the one-kernel decode path timed out */
+#define MOE_FP8_ERR_PRODUCER_WAIT 2u   /* a wait of the prefill producer timed out (its output is NaN) */
 
 /* Shape limits of this build. */
 #define MOE_FP8_MAX_EXPERTS 256
@@ -97,7 +109,8 @@ size_t moe_fp8_workspace_bytes(int M, int h, int i, int E, int k);
 /* Reads the sticky error word of a workspace into *flags (0: every wait
  * between workgroups completed; nonzero: a wait of some earlier forward on
  * this workspace timed out and that forward's output is invalid -- it also
- * holds NaN where the late data was needed), after the work already queued
+ * holds NaN where the late data was needed; the MOE_FP8_ERR_* bits say which
+ * path), after the work already queued
  * on `stream`; with `clear` nonzero the word is then reset to 0.  `flags` is
  * host memory.  Synchronises `stream`: not for the launch path or graph
  * capture.  MOE_ERR_INVALID on a null or misaligned pointer,
@@ -233,6 +246,22 @@ typedef struct {
  * moe_fp8_forward would. */
 int moe_fp8_workspace_layout(int M, int h, int i, int E, int k, moe_fp8_ws_layout* layout);
 
+/* Measurement and testing: the forward on a given path (MOE_FP8_PATH_*)
+ * instead of the one the library picks, with a workspace of at least
+ * moe_fp8_workspace_bytes_path bytes (laid out as
+ * moe_fp8_workspace_layout_path reports).  MOE_ERR_UNSUPPORTED (size 0) when
+ * the path cannot take the batch: the one-kernel path beyond its grid, the
+ * tiled paths for h % 256 != 0, the producer beyond its M-tile count.  The
+ * results are bitwise those of the same arithmetic on any path that shares
+ * it (the two tiled paths give the same bits). */
+size_t moe_fp8_workspace_bytes_path(int M, int h, int i, int E, int k, int path);
+int moe_fp8_workspace_layout_path(int M, int h, int i, int E, int k, int path, moe_fp8_ws_layout* layout);
+int moe_fp8_forward_ws_path(const void* x, const float* router_logits,
+                            const void* w13, const float* s13,
+                            const void* w2, const float* s2,
+                            void* out, int M, int h, int i, int E, int k,
+                            void* workspace, size_t workspace_bytes, int path, hipStream_t stream);
+
 /* Step 1 alone (the same kernel the forward runs): the routing stage that
  * opens the Netra Kernel README's MoE prefill pair and the M=1 MoE objects of
  * the Netra compiler architecture page (scope paragraph).
@@ -277,8 +306,9 @@ int moe_fp8_router_gemm_topk(const void* x, const void* wr, int M, int h, int E,
  * the GEMMs run on the block-scaled FP4 x FP8 matrix cores and accumulate in
  * fp32 (the result differs from the float64 dequantised reference by the
  * matrix cores' block-sum rounding).  Batches with M*k >= 12*E take the
- * tiled kernels of the FP8 prefill path (bf16 partials, as there) when
- * h % 256 == 0; the rest take the weight-streaming kernels (fp32 partials).
+ * tiled kernels of the FP8 prefill path (bf16 partials, as there; the
+ * producer and its reducer on request) when h % 256 == 0; the rest take the
+ * weight-streaming kernels (fp32 partials).
  * The workspace (>= moe_mxfp4_workspace_bytes,
  * 256-byte aligned) follows the rules of moe_fp8_forward_ws: its head must
  * be zero before the first forward (moe_fp8_workspace_init).  x, logits, out,
@@ -286,12 +316,20 @@ int moe_fp8_router_gemm_topk(const void* x, const void* wr, int M, int h, int E,
  * MOE_ERR_INVALID; shapes as moe_fp8_forward_ws.  Enqueued on `stream`. */
 size_t moe_mxfp4_workspace_bytes(int M, int h, int i, int E, int k);
 /* The workspace layout of an MXFP4 forward with these sizes, as
- * moe_fp8_workspace_layout (path is MOE_FP8_PATH_STREAM or _PREFILL). */
+ * moe_fp8_workspace_layout (path is MOE_FP8_PATH_STREAM, _PREFILL or
+ * _PRODUCER). */
 int moe_mxfp4_workspace_layout(int M, int h, int i, int E, int k, moe_fp8_ws_layout* layout);
 /* Measurement: the same forward with the stage stamps of
  * moe_fp8_forward_ws_timed (events[2j], events[2j + 1]: start of stage j's
  * first dispatch, end of its last; n_events >= 2 * the stage count, else
  * MOE_ERR_INVALID). */
+/* The MXFP4 forward on a given path (MOE_FP8_PATH_STREAM, _PREFILL or
+ * _PRODUCER), as moe_fp8_forward_ws_path. */
+size_t moe_mxfp4_workspace_bytes_path(int M, int h, int i, int E, int k, int path);
+int moe_mxfp4_forward_ws_path(const void* x, const float* router_logits,
+                              const void* w13, const void* e13, const void* w2, const void* e2,
+                              void* out, int M, int h, int i, int E, int k,
+                              void* workspace, size_t workspace_bytes, int path, hipStream_t stream);
 int moe_mxfp4_forward_ws_timed(const void* x, const float* router_logits,
                                const void* w13, const void* e13, const void* w2, const void* e2,
                                void* out, int M, int h, int i, int E, int k,

@@ -159,7 +159,7 @@ def test_workspace_layout_regions(lib, M, h, i, E, k):
     sizes = {"topk_ids": 4 * R, "topk_w": 4 * R, "xq": M * h, "xs": 4 * M * h // 128,
              "counts": 4 * E, "offsets": 4 * (E + 1), "sorted": 4 * R, "active": 4 * E,
              "num_active": 4, "gate_up": 4 * R * 2 * i, "act2": R * i, "act2_scale": 4 * R * i // 128,
-             "partial": (2 if L.path == moe.PATH_PREFILL else 4) * R * h}   # bf16 / fp32 partials
+             "partial": (2 if L.path in (moe.PATH_PREFILL, moe.PATH_PRODUCER) else 4) * R * h}   # bf16 / fp32 partials
     spans = []
     for name, n in sizes.items():
         off = getattr(L, name)
@@ -179,8 +179,8 @@ def test_workspace_layout_regions(lib, M, h, i, E, k):
                                        (40, 256, 128, 2, 1), (64, 6144, 768, 128, 4), (256, 6144, 768, 128, 4)])
 def test_fp8_path_rule(lib, M, h, i, E, k):
     """The FP8 forward's path: the one-kernel path for the smallest batches
-    whose grid fits, else the tiled kernels when M*k >= 8*E and h is a
-    multiple of 256, else the streaming kernels."""
+    whose grid fits, else the five-launch tiled kernels when M*k >= 8*E and h
+    is a multiple of 256, else the streaming kernels."""
     import fp8_block_scaled_router_amd as moe
     path = moe.workspace_layout(M, h, i, E, k).path
     if path != moe.PATH_FUSED_DECODE:
@@ -213,6 +213,27 @@ def test_mxfp4_layout_and_path(lib, M, h, i, E, k):
         assert L.act2 == 2 ** 64 - 1
     assert lib.moe_mxfp4_forward_kernel_count(M, h, i, E, k) == len(names)
     assert lib.moe_mxfp4_forward_kernel_name(M, h, i, E, k, len(names)) is None
+
+
+@pytest.mark.parametrize("M,h,i,E,k", [(768, 2048, 768, 128, 8), (8192, 2048, 768, 128, 8), (3, 384, 256, 6, 3),
+                                       (1, 2048, 768, 128, 8), (900000, 256, 128, 8, 1)])
+def test_forced_path_sizes(lib, M, h, i, E, k):
+    """Each path's workspace size for the forced-path entries: 0 exactly when
+    the path cannot take the batch; the chosen path's size is the default."""
+    import fp8_block_scaled_router_amd as moe
+    R = M * k
+    tiled_ok = h % 256 == 0
+    prod_ok = tiled_ok and (R + 127) // 128 + E <= 7168
+    for path, ok in ((moe.PATH_STREAM, True), (moe.PATH_PREFILL, tiled_ok), (moe.PATH_PRODUCER, prod_ok)):
+        n = lib.moe_fp8_workspace_bytes_path(M, h, i, E, k, path)
+        assert (n > 0) == ok, (path, n)
+        if ok:
+            L = moe.workspace_layout_path(M, h, i, E, k, path)
+            assert L.path == path and L.total == n
+    chosen = moe.workspace_layout(M, h, i, E, k)
+    assert lib.moe_fp8_workspace_bytes_path(M, h, i, E, k, chosen.path) == moe.workspace_bytes(M, h, i, E, k)
+    if M * k >= 8 * E and tiled_ok:
+        assert chosen.path == moe.PATH_PREFILL
 
 
 def test_status_and_probe_argument_checks(lib):

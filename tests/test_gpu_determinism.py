@@ -110,6 +110,25 @@ def test_layer_deterministic(moe_mod, ci):
     _layer_case(moe_mod, cfg.name, cfg.M, cfg.h, cfg.i, cfg.E, cfg.k, synth.default_seed(ci), cfg)
 
 
+@pytest.mark.parametrize("ci", [4, 5])
+def test_producer_path_deterministic(moe_mod, ci):
+    """The prefill producer and its reducer (asked for by path) on the
+    prefill batch and the 768-row verify batch: grid barriers, device-scope
+    hand-offs and per-M-tile counters reproduce the same bits every run, and
+    leave no error."""
+    cfg = synth.CONFIGS[ci]
+    seed = synth.default_seed(ci)
+    M, h, i, E, k = cfg.M, cfg.h, cfg.i, cfg.E, cfg.k
+    x, lg, q13, s13, q2, s2 = _device_layer(moe_mod, M, h, i, E, k, seed, cfg)
+    path = moe_mod.PATH_PRODUCER
+    ws = moe_mod.alloc_workspace(M, h, i, E, k, device=x.device, path=path)
+    out = torch.empty((M, h), dtype=torch.bfloat16, device=x.device)
+    log(f"determinism producer {cfg.name}")
+    _check_replays("producer_" + cfg.name,
+                   lambda: moe_mod.moe_fp8_forward_ws_path(x, lg, q13, s13, q2, s2, k, ws, path, out=out), [out])
+    assert moe_mod.workspace_error(ws) == 0, "a wait of the producer timed out"
+
+
 def test_layer_deterministic_stream_path_many_routes(moe_mod):
     """The streaming path beyond the one-launch grouping (320 routes: routing
     and quantisation, then the chunked histogram and scatter)."""

@@ -95,7 +95,7 @@ def _run(moe_mod, L):
                   if lay.path == moe_mod.PATH_STREAM else None,
                   sorted=read_ws(ws, lay.sorted, R, np.int32),
                   a2=read_ws(ws, lay.act2, R * i, np.uint8).reshape(R, i)
-                  if lay.path == moe_mod.PATH_PREFILL else None,
+                  if lay.path in (moe_mod.PATH_PREFILL, moe_mod.PATH_PRODUCER) else None,
                   path=lay.path)
     return got, ws_int
 
@@ -173,6 +173,32 @@ def test_mxfp4_tiled_path(moe_mod):
     cfg = synth.LayerConfig("mx_tiled", 1200, 2048, 768, 8, 2, "normal", "test shape")
     assert moe_mod.mxfp4_workspace_layout(cfg.M, cfg.h, cfg.i, cfg.E, cfg.k).path == moe_mod.PATH_PREFILL
     _check_layer(moe_mod, _MxLayer(cfg, 1207))
+
+
+@pytest.mark.parametrize("M,h,i,E,k", [(300, 256, 128, 4, 2), (1200, 2048, 768, 8, 2), (768, 2048, 768, 128, 8)])
+def test_mxfp4_tiled_paths_agree(moe_mod, M, h, i, E, k):
+    """The producer with its reducer and the five-launch tiled path give the
+    same bits (output, ids, codes, grouping and requantised activations)."""
+    cfg = synth.LayerConfig("mx_tiled_pair", M, h, i, E, k, "normal", "test shape")
+    L = _MxLayer(cfg, 4321 + M)
+    dev = torch.device("cuda:0")
+    args = [to_dev_bf16(L.x, dev), torch.from_numpy(np.ascontiguousarray(L.logits)).to(dev)] + \
+        [torch.from_numpy(np.ascontiguousarray(a)).to(dev) for a in (L.q13, L.e13, L.q2, L.e2)]
+    got = {}
+    for path in (moe_mod.PATH_PREFILL, moe_mod.PATH_PRODUCER):
+        ws = moe_mod.alloc_mxfp4_workspace(M, h, i, E, k, device=dev, path=path)
+        out = moe_mod.moe_mxfp4_forward_ws_path(*args, k, ws, path)
+        torch.cuda.synchronize()
+        lay = moe_mod.workspace_layout_path(M, h, i, E, k, path)   # the same offsets for both weight formats
+        R = M * k
+        got[path] = dict(out=to_host_bits(out), ids=read_ws(ws, lay.topk_ids, R, np.int32),
+                         xq=read_ws(ws, lay.xq, M * h, np.uint8), sorted=read_ws(ws, lay.sorted, R, np.int32),
+                         a2=read_ws(ws, lay.act2, R * i, np.uint8), a2s=read_ws(ws, lay.act2_scale, R * i // 128,
+                                                                                 np.float32).view(np.uint32))
+        assert moe_mod.workspace_error(ws) == 0
+    a, b = got[moe_mod.PATH_PREFILL], got[moe_mod.PATH_PRODUCER]
+    for name in a:
+        assert np.array_equal(a[name], b[name]), name
 
 
 def test_mxfp4_zero_input(moe_mod):

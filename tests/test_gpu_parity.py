@@ -184,10 +184,11 @@ def _check_sync_clean(ws):
     assert not rest.any(), f"unexpected sync words: {np.nonzero(rest)[0][:10]}"
 
 
-def _check_intermediates(moe_mod, L: Layer, ws, inter, tokens=None, terms=None):
+def _check_intermediates(moe_mod, L: Layer, ws, inter, tokens=None, terms=None, path=None):
     M, h, i, E, k = L.dims
     _check_sync_clean(ws)
-    lay = moe_mod.workspace_layout(M, h, i, E, k)
+    lay = moe_mod.workspace_layout(M, h, i, E, k) if path is None else moe_mod.workspace_layout_path(M, h, i, E, k,
+                                                                                                      path)
     ids = read_ws(ws, lay.topk_ids, M * k, np.int32).reshape(M, k)
     tw = read_ws(ws, lay.topk_w, M * k, np.float32).reshape(M, k)
     xq = read_ws(ws, lay.xq, M * h, np.uint8).reshape(M, h)
@@ -205,7 +206,7 @@ def _check_intermediates(moe_mod, L: Layer, ws, inter, tokens=None, terms=None):
     nact = int(read_ws(ws, lay.num_active, 1, np.int32)[0])
     act = read_ws(ws, lay.active, E, np.int32)[:nact]
     assert np.array_equal(act, np.nonzero(cr)[0])
-    if lay.path == moe_mod.PATH_PREFILL and tokens is None:
+    if lay.path in (moe_mod.PATH_PREFILL, moe_mod.PATH_PRODUCER) and tokens is None:
         # requantised activations (sorted-route order): the oracle's codes,
         # except where the decision sits on a rounding boundary, where either
         # neighbouring code is the method's result
@@ -307,6 +308,75 @@ def test_forward_timed_stages(dev, moe_mod, ci):
             assert sum(d) <= span * 1.0001 + 1e-4
     finally:
         ev.close()
+    _check_sync_clean(ws)
+
+
+@pytest.mark.parametrize("M,h,i,E,k", [(300, 256, 128, 4, 2), (130, 256, 256, 1, 1), (1000, 512, 384, 8, 3),
+                                       (768, 2048, 768, 128, 8), (4096, 2048, 768, 128, 8)])
+def test_tiled_paths_agree(dev, moe_mod, M, h, i, E, k):
+    """The producer with its reducer (one launch for routing, quantisation,
+    grouping and both GEMMs) and the five-launch tiled path give the same
+    bits: output, ids and weights, activation codes and scales, grouping, the
+    requantised activations and their scales, and clean sync words."""
+    cfg = synth.LayerConfig(f"m{M}_h{h}_i{i}_e{E}_top{k}", M, h, i, E, k, "normal", "tiled pair")
+    L = Layer(cfg, 97 + M, dev)
+    R = M * k
+    got = {}
+    for path in (moe_mod.PATH_PREFILL, moe_mod.PATH_PRODUCER):
+        ws = moe_mod.alloc_workspace(M, h, i, E, k, device=dev, path=path)
+        outs = []
+        for _ in range(2):   # the second forward runs on counters the first cleared
+            outs.append(to_host_bits(moe_mod.moe_fp8_forward_ws_path(L.tx, L.tl, L.t13, L.ts13, L.t2, L.ts2, k, ws,
+                                                                     path)))
+            torch.cuda.synchronize()
+            _check_sync_clean(ws)
+        assert np.array_equal(outs[0], outs[1])
+        lay = moe_mod.workspace_layout_path(M, h, i, E, k, path)
+        assert lay.path == path
+        got[path] = dict(out=outs[0], ids=read_ws(ws, lay.topk_ids, R, np.int32),
+                         tw=read_ws(ws, lay.topk_w, R, np.float32).view(np.uint32),
+                         xq=read_ws(ws, lay.xq, M * h, np.uint8),
+                         xs=read_ws(ws, lay.xs, M * h // 128, np.float32).view(np.uint32),
+                         counts=read_ws(ws, lay.counts, E, np.int32), offsets=read_ws(ws, lay.offsets, E + 1, np.int32),
+                         sorted=read_ws(ws, lay.sorted, R, np.int32), a2=read_ws(ws, lay.act2, R * i, np.uint8),
+                         a2s=read_ws(ws, lay.act2_scale, R * i // 128, np.float32).view(np.uint32))
+    a, b = got[moe_mod.PATH_PREFILL], got[moe_mod.PATH_PRODUCER]
+    for name in a:
+        assert np.array_equal(a[name], b[name]), name
+    log(f"tiled paths agree: M={M} h={h} i={i} E={E} k={k}")
+
+
+def test_producer_matches_oracle(dev, moe_mod):
+    """The producer and its reducer on the 768-row verify batch (64 x 12
+    tokens), every intermediate and the output against the oracle at the
+    unwidened bar."""
+    ci = 5
+    cfg = synth.CONFIGS[ci]
+    L = Layer(cfg, synth.default_seed(ci), dev)
+    M, h, i, E, k = L.dims
+    path = moe_mod.PATH_PRODUCER
+    ws = moe_mod.alloc_workspace(M, h, i, E, k, device=dev, path=path)
+    out = moe_mod.moe_fp8_forward_ws_path(L.tx, L.tl, L.t13, L.ts13, L.t2, L.ts2, k, ws, path)
+    torch.cuda.synchronize()
+    ref, inter = L.oracle(intermediates=True)
+    terms = gpu_util.gate_up_terms(L, inter)
+    _check_intermediates(moe_mod, L, ws, inter, terms=terms, path=path)
+    got = to_host_bits(out)
+    allow = flip_allowance(L, inter, terms=terms)
+    assert r16_report("producer_" + cfg.name, got, ref, allow), "the producer misses the unwidened bar"
+    check_output(got, ref, allowance=allow)
+
+
+def test_forced_path_rejections(dev, moe_mod):
+    """A forced path that cannot take the batch is rejected before any launch."""
+    L = _custom_layer(dev, 3, 384, 256, 6, 3, seed=5)
+    ws = moe_mod.alloc_workspace(3, 384, 256, 6, 3, device=dev)
+    for path in (moe_mod.PATH_PREFILL, moe_mod.PATH_PRODUCER):   # h % 256 != 0
+        with pytest.raises(moe_mod.MoeError):
+            moe_mod.moe_fp8_forward_ws_path(L.tx, L.tl, L.t13, L.ts13, L.t2, L.ts2, 3, ws, path)
+    with pytest.raises(moe_mod.MoeError):
+        moe_mod.moe_fp8_forward_ws_path(L.tx, L.tl, L.t13, L.ts13, L.t2, L.ts2, 3, ws, 7)
+    torch.cuda.synchronize()
     _check_sync_clean(ws)
 
 
