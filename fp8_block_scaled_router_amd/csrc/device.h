@@ -225,6 +225,26 @@ __device__ __forceinline__ uint64_t ll_pack(float v, uint32_t tag) {
 __device__ __forceinline__ float ll_value(uint64_t w) { return __uint_as_float((uint32_t)w); }
 __device__ __forceinline__ uint32_t ll_tag(uint64_t w) { return (uint32_t)(w >> 32); }
 
+// Thread 0 of a workgroup: waits until the device-scope word *ctr reaches
+// n, with a growing sleep between polls, for at most 1 s of the 100 MHz
+// constant clock.  Returns false when the wait timed out; `bit` is then set
+// in the sticky error word *err.
+__device__ __forceinline__ bool wait_count(const uint32_t* ctr, uint32_t n, uint32_t* err, uint32_t bit) {
+    constexpr uint64_t kTicks = 100000000;
+    uint64_t t0 = 0;
+    int nap = 1;
+    for (int tries = 0;; ++tries) {
+        if (ld_agent(ctr) >= n) return true;
+        if (tries == 0) t0 = wall_clock64();
+        if (wall_clock64() - t0 > kTicks) {
+            atomicOr(err, bit);
+            return false;
+        }
+        for (int z = 0; z < nap; ++z) __builtin_amdgcn_s_sleep(2);
+        nap = nap < 8 ? 2 * nap : 8;
+    }
+}
+
 // Wait until every vector-memory operation this wave issued has completed
 // (s_waitcnt vmcnt(0)); the signal fences keep the compiler from moving
 // memory operations across it.

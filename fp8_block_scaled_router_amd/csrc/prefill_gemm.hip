@@ -398,26 +398,6 @@ __device__ __forceinline__ TileInfo decode_tile(const TileMeta& meta, int E, int
 
 // ------------------------------------------------- producer synchronisation
 
-constexpr uint64_t kProdWaitTicks = 100000000;   // 1 s of the 100 MHz constant clock
-
-// Thread 0 of a workgroup: waits until the device-scope word *ctr reaches n,
-// with a growing sleep between polls.  Returns false when the wait timed out
-// (the error word then carries kErrProducer).
-__device__ __forceinline__ bool wait_count(const uint32_t* ctr, uint32_t n, uint32_t* err) {
-    uint64_t t0 = 0;
-    int nap = 1;
-    for (int tries = 0;; ++tries) {
-        if (ld_agent(ctr) >= n) return true;
-        if (tries == 0) t0 = wall_clock64();
-        if (wall_clock64() - t0 > kProdWaitTicks) {
-            atomicOr(err, kErrProducer);
-            return false;
-        }
-        for (int z = 0; z < nap; ++z) __builtin_amdgcn_s_sleep(2);
-        nap = nap < 8 ? 2 * nap : 8;
-    }
-}
-
 // Every workgroup of the grid arrives once at the device-scope word *ctr;
 // returns when all n have (false when the wait timed out, and then also for
 // the rest of the forward through flag).  Each workgroup's stores have
@@ -430,7 +410,7 @@ __device__ __forceinline__ bool grid_barrier(uint32_t* ctr, uint32_t n, uint32_t
     __syncthreads();
     if (tid == 0) {
         __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (!wait_count(ctr, n, err)) flag = 1;
+        if (!wait_count(ctr, n, err, kErrProducer)) flag = 1;
     }
     __syncthreads();
     return flag == 0;
@@ -705,7 +685,7 @@ __device__ __forceinline__ void down_tiles(const PrefillArgs& a, TileLds<kMx>& S
     // (producer) every wave waits until M-tile mt's IB gate/up tiles are done
     auto ready = [&](int mt) -> bool {
         if constexpr (kProd) {
-            if (tid == 0 && S.flag == 0 && !wait_count(a.done + mt, (uint32_t)IB, a.err)) S.flag = 1;
+            if (tid == 0 && S.flag == 0 && !wait_count(a.done + mt, (uint32_t)IB, a.err, kErrProducer)) S.flag = 1;
             __syncthreads();
             return S.flag == 0;
         } else {
