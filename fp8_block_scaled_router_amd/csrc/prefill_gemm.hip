@@ -207,17 +207,20 @@ __device__ __forceinline__ void issue_stage(const Loop& L, uint8_t* st, int kb) 
     using F = Fmt<kMx>;
     const uint8_t* gA = L.gA + (size_t)kb * F::kRowBytes;
     const uint8_t* gB = L.gB + (size_t)kb * 128;
+    // (the destinations are wave-uniform; readfirstlane keeps them in scalar
+    // registers for M0 whatever the compiler proves)
     const uint32_t base = lds_addr(st);
+    auto dst = [&](uint32_t off) { return (uint32_t)__builtin_amdgcn_readfirstlane(base + off); };
 #pragma unroll
-    for (int q = 0; q < F::kDmaA; ++q) copy16_to_lds(gA + L.offA[q], base + (L.wave * F::kDmaA + q) * 1024);
+    for (int q = 0; q < F::kDmaA; ++q) copy16_to_lds(gA + L.offA[q], dst((L.wave * F::kDmaA + q) * 1024));
 #pragma unroll
     for (int q = 0; q < kDmaB; ++q)
-        copy16_to_lds<kCoh>(gB + L.offB[q], base + F::kBOff + (L.wave * kDmaB + q) * 1024);
+        copy16_to_lds<kCoh>(gB + L.offB[q], dst(F::kBOff + (L.wave * kDmaB + q) * 1024));
     // scales of routes 16 wave .. +16 (lanes 16..63 repeat lanes 0..15)
-    copy4_to_lds<kCoh>(L.gX + L.offX + kb, base + F::kXOff + L.wave * 256);
+    copy4_to_lds<kCoh>(L.gX + L.offX + kb, dst(F::kXOff + L.wave * 256));
     // (MXFP4) the four scale bytes of K block kb of weight rows 32 wave ..
     // +32 (lanes 32..63 repeat lanes 0..31)
-    if constexpr (kMx) copy4_to_lds(L.gS + L.offS + 4 * kb, base + F::kAB + L.wave * 256);
+    if constexpr (kMx) copy4_to_lds(L.gS + L.offS + 4 * kb, dst(F::kAB + L.wave * 256));
 }
 
 // One K block on one wave: 4 weight tiles x 4 route tiles.  The raw block
@@ -288,32 +291,52 @@ __device__ __forceinline__ void issue_first(const Loop& L, int KB, uint8_t* stag
 
 // after_first() runs once, right after the first barrier: every wave has
 // then finished whatever it did before the loop.
-template <bool kMx, bool kCoh, typename SwOf, typename AfterFirst>
-__device__ __forceinline__ void k_loop(v4f acc[16], const Loop& L, int KB, uint8_t* stages, SwOf sw_of,
-                                       AfterFirst after_first) {
+// Ring run-on (run_on, KB >= 2): the ring does not stop at the tile's end.
+// At step KB - 2 (when this tile's copies are all issued) retarget(L) points
+// L's copies at the next tile (its fragment geometry stays), the last two
+// steps issue that tile's K blocks 0 and 1, the last step waits only for
+// its own block, and the loop returns without a final barrier (the next
+// tile's first barrier certifies that every wave has finished reading this
+// tile's buffers before they are written again).  Block 0 sits in buffer
+// rd0; the return value is the buffer of the next tile's block 0.
+struct NoRetarget {
+    __device__ void operator()(Loop&) const {}
+};
+template <bool kMx, bool kCoh, typename SwOf, typename AfterFirst, typename Retarget = NoRetarget>
+__device__ __forceinline__ int k_loop(v4f acc[16], Loop& L, int KB, uint8_t* stages, SwOf sw_of,
+                                      AfterFirst after_first, int rd0 = 0, bool run_on = false,
+                                      Retarget retarget = Retarget{}) {
     using F = Fmt<kMx>;
     float sw[4] = {1.0f, 1.0f, 1.0f, 1.0f}, sw_p[4] = {0.0f, 0.0f, 0.0f, 0.0f}, xr_p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     v4f blk[16];
 #pragma unroll
     for (int t = 0; t < 16; ++t) blk[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    int rd = 0;   // stage buffer of block kb
+    run_on = run_on && KB >= 2;
+    int rd = rd0;   // stage buffer of block kb
     for (int kb = 0; kb < KB; ++kb) {
-        if (kb + 1 < KB) __builtin_amdgcn_s_waitcnt(vm_wait(F::kVmem));
+        if (kb + 1 < KB || run_on) __builtin_amdgcn_s_waitcnt(vm_wait(F::kVmem));
         else __builtin_amdgcn_s_waitcnt(vm_wait(0));
         block_barrier();
-        if (kb + 2 < KB) issue_stage<kMx, kCoh>(L, stages + (rd == 0 ? 2 : rd - 1) * F::kStage, kb + 2);
+        uint8_t* const wr = stages + (rd == 0 ? 2 : rd - 1) * F::kStage;
+        if (kb + 2 < KB) {
+            issue_stage<kMx, kCoh>(L, wr, kb + 2);
+        } else if (run_on) {
+            if (kb + 2 == KB) retarget(L);
+            issue_stage<kMx, kCoh>(L, wr, kb + 2 - KB);
+        }
         if (kb == 0) after_first();
         if constexpr (!kMx) sw_of(kb, sw);
         block_mma<kMx>(acc, blk, sw_p, xr_p, L, stages + rd * F::kStage, sw);
         rd = rd == 2 ? 0 : rd + 1;
     }
-    block_barrier();   // every wave is done with the stage buffers
+    if (!run_on) block_barrier();   // every wave is done with the stage buffers
 #pragma unroll
     for (int t = 0; t < 16; ++t) {   // promotion of the last block
         const float sc = kMx ? xr_p[t & 3] : sw_p[t >> 2] * xr_p[t & 3];
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[t][v] = fmaf(blk[t][v], sc, acc[t][v]);
     }
+    return rd;
 }
 
 // (MXFP4) Slot of 16-byte chunk g of weight row r in a 64-byte LDS row is
@@ -706,11 +729,16 @@ __device__ __forceinline__ void down_tiles(const PrefillArgs& a, TileLds<kMx>& S
     issue_first<kMx, kProd>(L, IB, stages);
 
     const int sblk = wn >> 1;
+    int rd0 = 0;   // stage buffer of the tile's first K block
     for (;;) {
         span.next += span.step;
         const bool more = span.next < span.end;
         TileInfo tn = t;
         if (more) tn = decode_tile(meta, E, NT, span.next);
+        // Outside the producer the ring runs on into the next tile (its
+        // operands need no list from LDS), so that tile's first copies
+        // travel during this tile's last K blocks instead of after them.
+        constexpr bool kRunOn = !kProd;
         // the next tile's lists, copied straight into LDS as in the gate/up
         // kernel (the previous tile's epilogue read this parity's route list)
         auto next_lists = [&]() {
@@ -731,11 +759,15 @@ __device__ __forceinline__ void down_tiles(const PrefillArgs& a, TileLds<kMx>& S
         v4f acc[16];
 #pragma unroll
         for (int u = 0; u < 16; ++u) acc[u] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-        k_loop<kMx, kProd>(acc, L, IB, stages, sw_of, next_lists);
-        if (more) {
-            if (!ready(tn.mt)) return;   // no copy is in flight here
-            L = down_loop<kMx>(a, tn, wave, lane);
-            issue_first<kMx, kProd>(L, IB, stages);
+        auto retarget = [&](Loop& Lr) { Lr = down_loop<kMx>(a, tn, wave, lane); };
+        rd0 = k_loop<kMx, kProd>(acc, L, IB, stages, sw_of, next_lists, rd0, kRunOn && more, retarget);
+        if (!(kRunOn && IB >= 2)) {
+            rd0 = 0;
+            if (more) {
+                if (!ready(tn.mt)) return;   // no copy is in flight here
+                L = down_loop<kMx>(a, tn, wave, lane);
+                issue_first<kMx, kProd>(L, IB, stages);
+            }
         }
         // bf16 partial rows (round to nearest even) by route id; lane holds
         // output rows sub * 256 + 64 wn + 16 j + 4 kg + v of route
