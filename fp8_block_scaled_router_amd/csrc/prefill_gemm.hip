@@ -165,6 +165,7 @@ struct Loop {
     // (MXFP4: a_lo only, 16 bytes)
     int a_lo, a_hi, b_lo, b_hi;
     int x_off;                      // byte offset of the lane's route-tile-0 scale in a stage
+    int na;                         // route tiles of this wave holding a route (uniform; the rest is padding)
     int a_step[4];                  // byte offsets of weight tiles 1..3 from tile 0 (constants)
     int s_off[4];                   // (MXFP4) byte offset of the lane's scale word in weight tile j
 };
@@ -231,15 +232,24 @@ __device__ __forceinline__ void issue_stage(const Loop& L, uint8_t* st, int kb) 
 // block, blk and the scales are zero, so that promotion adds zeros).  With
 // MXFP4 weights the MFMA applies the weights' E8M0 scales itself and the
 // promotion carries the activation scale alone.
-template <bool kMx>
+// NA: only the wave's first NA route tiles hold routes (the others are
+// padding rows, whose outputs are dropped): their fragments, MFMAs and
+// promotions are left out, and each accumulator of the others sees the
+// same operations in the same order.
+template <bool kMx, int NA = 4>
 __device__ __forceinline__ void block_mma(v4f acc[16], v4f blk[16], float sw_p[4], float xr_p[4], const Loop& L,
                                           const uint8_t* st, const float sw[4]) {
+    if constexpr (NA == 0) return;
     v8i B[4];
     float xr[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) B[m] = frag(st + L.b_lo + m * 2048, st + L.b_hi + m * 2048);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) xr[m] = *reinterpret_cast<const float*>(st + L.x_off + m * 256);
+    for (int m = 0; m < 4; ++m) {
+        xr[m] = 0.0f;
+        if (m < NA) {   // (a constant once unrolled)
+            B[m] = frag(st + L.b_lo + m * 2048, st + L.b_hi + m * 2048);
+            xr[m] = *reinterpret_cast<const float*>(st + L.x_off + m * 256);
+        }
+    }
     if constexpr (kMx) {
         uint4 A[4];
         int sa[4];
@@ -250,6 +260,7 @@ __device__ __forceinline__ void block_mma(v4f acc[16], v4f blk[16], float sw_p[4
         }
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
+            if ((t & 3) >= NA) continue;
             const float sc = xr_p[t & 3];
 #pragma unroll
             for (int v = 0; v < 4; ++v) acc[t][v] = fmaf(blk[t][v], sc, acc[t][v]);
@@ -261,6 +272,7 @@ __device__ __forceinline__ void block_mma(v4f acc[16], v4f blk[16], float sw_p[4
         for (int j = 0; j < 4; ++j) A[j] = frag(st + L.a_lo + L.a_step[j], st + L.a_hi + L.a_step[j]);
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
+            if ((t & 3) >= NA) continue;
             const float sc = sw_p[t >> 2] * xr_p[t & 3];
 #pragma unroll
             for (int v = 0; v < 4; ++v) acc[t][v] = fmaf(blk[t][v], sc, acc[t][v]);
@@ -302,10 +314,9 @@ __device__ __forceinline__ void issue_first(const Loop& L, int KB, uint8_t* stag
 struct NoRetarget {
     __device__ void operator()(Loop&) const {}
 };
-template <bool kMx, bool kCoh, typename SwOf, typename AfterFirst, typename Retarget = NoRetarget>
-__device__ __forceinline__ int k_loop(v4f acc[16], Loop& L, int KB, uint8_t* stages, SwOf sw_of,
-                                      AfterFirst after_first, int rd0 = 0, bool run_on = false,
-                                      Retarget retarget = Retarget{}) {
+template <bool kMx, bool kCoh, int NA, typename SwOf, typename AfterFirst, typename Retarget>
+__device__ __forceinline__ int k_loop_na(v4f acc[16], Loop& L, int KB, uint8_t* stages, SwOf sw_of,
+                                         AfterFirst after_first, int rd0, bool run_on, Retarget retarget) {
     using F = Fmt<kMx>;
     float sw[4] = {1.0f, 1.0f, 1.0f, 1.0f}, sw_p[4] = {0.0f, 0.0f, 0.0f, 0.0f}, xr_p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     v4f blk[16];
@@ -326,7 +337,7 @@ __device__ __forceinline__ int k_loop(v4f acc[16], Loop& L, int KB, uint8_t* sta
         }
         if (kb == 0) after_first();
         if constexpr (!kMx) sw_of(kb, sw);
-        block_mma<kMx>(acc, blk, sw_p, xr_p, L, stages + rd * F::kStage, sw);
+        block_mma<kMx, NA>(acc, blk, sw_p, xr_p, L, stages + rd * F::kStage, sw);
         rd = rd == 2 ? 0 : rd + 1;
     }
     if (!run_on) block_barrier();   // every wave is done with the stage buffers
@@ -337,6 +348,33 @@ __device__ __forceinline__ int k_loop(v4f acc[16], Loop& L, int KB, uint8_t* sta
         for (int v = 0; v < 4; ++v) acc[t][v] = fmaf(blk[t][v], sc, acc[t][v]);
     }
     return rd;
+}
+
+// The K loop for this wave's count of route tiles holding routes (L.na,
+// wave-uniform; every instance waits, copies and meets the barriers alike):
+// all four (one to four), or none; with kHalf also the first two (one or
+// two).  The down kernel has the register room for two instances only.
+template <bool kMx, bool kCoh, bool kHalf, typename SwOf, typename AfterFirst, typename Retarget = NoRetarget>
+__device__ __forceinline__ int k_loop(v4f acc[16], Loop& L, int KB, uint8_t* stages, SwOf sw_of,
+                                      AfterFirst after_first, int rd0 = 0, bool run_on = false,
+                                      Retarget retarget = Retarget{}) {
+    if (L.na > (kHalf ? 2 : 0))
+        return k_loop_na<kMx, kCoh, 4>(acc, L, KB, stages, sw_of, after_first, rd0, run_on, retarget);
+    if (kHalf && L.na > 0)
+        return k_loop_na<kMx, kCoh, 2>(acc, L, KB, stages, sw_of, after_first, rd0, run_on, retarget);
+    return k_loop_na<kMx, kCoh, 0>(acc, L, KB, stages, sw_of, after_first, rd0, run_on, retarget);
+}
+
+// Roles of the 8 waves: wn (0..3) picks the weight rows of the tile, wr
+// (0, 1) its 64-route half.  Waves w and w + 4 share a SIMD, so each SIMD
+// holds one wave of each half: a tile whose second half is padding (an
+// expert's last M-tile, every M-tile of a cold expert) then halves every
+// SIMD's MFMA work instead of leaving two SIMDs with all of it.
+__device__ __forceinline__ int route_half(int wave) { return wave >> 2; }
+__device__ __forceinline__ int row_group(int wave) { return wave & 3; }
+// Route tiles (of 16) of half wr that hold a route of a tile with `rows` routes.
+__device__ __forceinline__ int route_tiles(int rows, int wr) {
+    return __builtin_amdgcn_readfirstlane(min(4, max(0, (rows - 64 * wr + 15) >> 4)));
 }
 
 // (MXFP4) Slot of 16-byte chunk g of weight row r in a 64-byte LDS row is
@@ -450,12 +488,13 @@ __device__ __forceinline__ Loop gate_up_loop(const PrefillArgs& a, const TileInf
                                              int lane) {
     using F = Fmt<kMx>;
     const int h = a.h, i = a.i, KB = h / 128, N13 = 2 * i;
-    const int wr = wave & 1, wn = wave >> 1;
+    const int wr = route_half(wave), wn = row_group(wave);
     const int hb = kMx ? h / 2 : h;   // weight row bytes
     Loop L;
     // gate rows 32 wn + {0, 16}, up rows 128 + 32 wn + {0, 16}
     lane_geometry<kMx>(L, lane, 32 * wn, {0, 16, 128, 144}, 64 * wr);
     L.wave = wave;
+    L.na = route_tiles(t.rows, wr);
     L.gA = a.w13 + (size_t)t.e * N13 * hb;
     L.gB = a.xq;
     L.gX = a.xs;
@@ -499,9 +538,11 @@ __device__ __forceinline__ void gate_up_epilogue(const PrefillArgs& a, const Til
                                                  float (*amax_l)[kBM], uint8_t* codes, int tid) {
     const int i = a.i, IB = i / 128;
     const int wave = tid >> 6, lane = tid & 63, col = lane & 15, kg = lane >> 4;
-    const int wr = wave & 1, wn = wave >> 1;
+    const int wr = route_half(wave), wn = row_group(wave);
+    const int na = route_tiles(t.rows, wr);   // route tiles past it hold only padding rows (never stored)
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
+        if (m >= na) continue;
         float pm = 0.0f;
 #pragma unroll
         for (int j = 0; j < 2; ++j)
@@ -519,6 +560,7 @@ __device__ __forceinline__ void gate_up_epilogue(const PrefillArgs& a, const Til
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
+        if (m >= na) continue;
         const int r = 64 * wr + 16 * m + col;
         const float sc =
             fmaxf(fmaxf(amax_l[0][r], amax_l[1][r]), fmaxf(amax_l[2][r], amax_l[3][r])) / kE4M3Max;
@@ -616,7 +658,7 @@ __device__ __forceinline__ void gate_up_tiles(const PrefillArgs& a, TileLds<kMx>
         v4f acc[16];
 #pragma unroll
         for (int u = 0; u < 16; ++u) acc[u] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-        k_loop<kMx, kProd>(acc, L, KB, stages, sw_of, next_lists);   // ends with every wave done with the stage buffers
+        k_loop<kMx, kProd, true>(acc, L, KB, stages, sw_of, next_lists);   // ends with every wave done with the stage buffers
         if (more) {
             L = gate_up_loop<kMx>(a, tn, S.rt[par ^ 1], wave, lane);
             issue_first<kMx, kProd>(L, KB, stages);   // buffers 0 and 1; the epilogue stages codes in buffer 2
@@ -653,11 +695,12 @@ template <bool kMx>
 __device__ __forceinline__ Loop down_loop(const PrefillArgs& a, const TileInfo& t, int wave, int lane) {
     using F = Fmt<kMx>;
     const int h = a.h, i = a.i, IB = i / 128;
-    const int wr = wave & 1, wn = wave >> 1;
+    const int wr = route_half(wave), wn = row_group(wave);
     const int ib = kMx ? i / 2 : i;   // weight row bytes
     Loop L;
     lane_geometry<kMx>(L, lane, 64 * wn, {0, 16, 32, 48}, 64 * wr);   // weight rows 64 wn + 16 j; route tiles 64 wr + 16 m
     L.wave = wave;
+    L.na = route_tiles(t.rows, wr);
     L.gA = a.w2 + ((size_t)t.e * h + (size_t)t.sub * kBN) * ib;
     L.gB = a.a2 + (size_t)t.beg * i;
     L.gX = a.a2s + (size_t)t.beg * IB;
@@ -698,7 +741,7 @@ __device__ __forceinline__ void down_tiles(const PrefillArgs& a, TileLds<kMx>& S
     const int IB = i / 128, NT = h / kBN;
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int col = lane & 15, kg = lane >> 4;
-    const int wr = wave & 1, wn = wave >> 1;
+    const int wr = route_half(wave), wn = row_group(wave);
 
     load_meta<kProd>(meta, a, tid);
     __syncthreads();
@@ -760,7 +803,7 @@ __device__ __forceinline__ void down_tiles(const PrefillArgs& a, TileLds<kMx>& S
 #pragma unroll
         for (int u = 0; u < 16; ++u) acc[u] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
         auto retarget = [&](Loop& Lr) { Lr = down_loop<kMx>(a, tn, wave, lane); };
-        rd0 = k_loop<kMx, kProd>(acc, L, IB, stages, sw_of, next_lists, rd0, kRunOn && more, retarget);
+        rd0 = k_loop<kMx, kProd, false>(acc, L, IB, stages, sw_of, next_lists, rd0, kRunOn && more, retarget);
         if (!(kRunOn && IB >= 2)) {
             rd0 = 0;
             if (more) {
@@ -772,8 +815,10 @@ __device__ __forceinline__ void down_tiles(const PrefillArgs& a, TileLds<kMx>& S
         // bf16 partial rows (round to nearest even) by route id; lane holds
         // output rows sub * 256 + 64 wn + 16 j + 4 kg + v of route
         // 64 wr + 16 m + col
+        const int na = route_tiles(t.rows, wr);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
+            if (m >= na) continue;
             const int row = 64 * wr + 16 * m + col;
             if (row >= t.rows) continue;
             const int p = S.rt[par][row];
