@@ -343,6 +343,44 @@ __device__ __forceinline__ v8i load32(const uint8_t* p) {
     return r;
 }
 
+// gfx9 s_waitcnt immediate waiting until at most n vector-memory operations
+// are outstanding (expcnt and lgkmcnt left at their maxima).
+constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
+// global -> LDS copies (global_load_lds: no register receives the data).
+// Written as inline assembly so that the compiler does not track them: a
+// kernel that uses them waits for them itself (an explicit s_waitcnt before
+// the barrier that publishes the bytes), and the compiler's own waits for
+// later loads count only those loads (the hardware counter still retires in
+// issue order, so a wave should issue its copies after the loads it needs
+// first).  M0 holds the wave's LDS destination; lane l's data lands at
+// M0 + 16 l (4 l for the dword form).  One wait state separates the M0
+// write from the copy.
+// kCoh: the copy reads at device scope (sc1), so it sees data that another
+// workgroup of the same launch wrote with device-scope stores, whatever
+// this XCD's L2 holds.
+template <bool kCoh = false>
+__device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds) {
+    if constexpr (kCoh)
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off sc1"
+                     :: "s"(lds), "v"(src) : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                     :: "s"(lds), "v"(src) : "memory", "m0");
+}
+template <bool kCoh = false>
+__device__ __forceinline__ void copy4_to_lds(const void* src, uint32_t lds) {
+    if constexpr (kCoh)
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off sc1"
+                     :: "s"(lds), "v"(src) : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+                     :: "s"(lds), "v"(src) : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 __device__ __forceinline__ v8i zero8() {
     v8i r;
     for (int j = 0; j < 8; ++j) r[j] = 0;

@@ -85,9 +85,6 @@ struct Fmt {
 
 static_assert(Fmt<false>::kDmaA == 4 && Fmt<true>::kDmaA == 2 && kDmaB == 2, "stage copy split");
 
-// gfx9 s_waitcnt immediate waiting until at most n vector-memory operations
-// are outstanding (expcnt and lgkmcnt left at their maxima).
-constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
 
 // Per-tile routing metadata, staged in LDS with one coalesced load so a
@@ -170,36 +167,6 @@ struct Loop {
     int s_off[4];                   // (MXFP4) byte offset of the lane's scale word in weight tile j
 };
 
-// global -> LDS copies.  Written as inline assembly so that the compiler
-// does not track them: the K loop's explicit s_waitcnt / s_barrier pairs are
-// the only synchronisation of the stage buffers, and the loop issues no
-// other vector-memory operation whose waits the compiler would place.  M0
-// holds the wave's LDS destination; lane l's data lands at M0 + 16 l (4 l
-// for the dword form).  One wait state separates the M0 write from the copy.
-// kCoh: the copy reads at device scope (sc1), so it sees data that another
-// workgroup of the same launch wrote with device-scope stores, whatever
-// this XCD's L2 holds.
-template <bool kCoh = false>
-__device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds) {
-    if constexpr (kCoh)
-        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off sc1"
-                     :: "s"(lds), "v"(src) : "memory", "m0");
-    else
-        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                     :: "s"(lds), "v"(src) : "memory", "m0");
-}
-template <bool kCoh = false>
-__device__ __forceinline__ void copy4_to_lds(const void* src, uint32_t lds) {
-    if constexpr (kCoh)
-        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off sc1"
-                     :: "s"(lds), "v"(src) : "memory", "m0");
-    else
-        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
-                     :: "s"(lds), "v"(src) : "memory", "m0");
-}
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
 
 // Issue the copies of K block kb into stage buffer st (kCoh: the activation
 // tile and its scales at device scope).
