@@ -157,8 +157,10 @@ __device__ __forceinline__ uint64_t match_id(int e) {
 // many workgroups re-reading all of its words, a producer's stores stalled
 // until the pollers gave up), so a wait first polls one sentinel word per
 // producer -- the last word that producer writes into the range -- with one
-// load per lane and a growing sleep between rounds, then reads the data once
-// and re-reads only while some word still lacks the tag.
+// load per lane and a short sleep between rounds (two rounds of s_sleep 2 at
+// most: longer sleeps add their length to the hand-off, shorter ones slow the
+// producers' stores; measured), then reads the data once and re-reads only
+// while some word still lacks the tag.
 
 // Lane-wise: loads *p until it carries `tag` (lanes with p == nullptr are
 // done at once).  Returns false when the wait timed out (the sticky error
@@ -175,7 +177,7 @@ __device__ __forceinline__ bool wait_sentinel(const uint64_t* p, uint32_t tag, u
             return false;
         }
         for (int z = 0; z < nap; ++z) __builtin_amdgcn_s_sleep(2);
-        nap = nap < 8 ? 2 * nap : 8;
+        nap = nap < 2 ? 2 * nap : 2;
     }
 }
 
@@ -198,7 +200,7 @@ __device__ __forceinline__ bool read_words(const uint64_t* const (&p)[N], uint32
             atomicOr(err, 1u);
             return ok;
         }
-        __builtin_amdgcn_s_sleep(8);
+        __builtin_amdgcn_s_sleep(2);
     }
 }
 
