@@ -346,6 +346,38 @@ def test_tiled_paths_agree(dev, moe_mod, M, h, i, E, k):
     log(f"tiled paths agree: M={M} h={h} i={i} E={E} k={k}")
 
 
+@pytest.mark.parametrize("k", [1, 2])
+def test_tiled_route_tile_counts(dev, moe_mod, k):
+    """Experts holding 1, 16, 17, 33, 64, 65, 97 and 128 routes (k = 2: every
+    token also routes to a ninth expert, which then holds three full M-tiles
+    and a ragged last one): every count of 16-route tiles holding a route in
+    both 64-route halves of an M-tile, the K-loop instance that also
+    multiplies a tile of padding included.  Both tiled paths against the
+    oracle, and against each other bit for bit."""
+    counts = [1, 16, 17, 33, 64, 65, 97, 128]
+    M, h, i, E = sum(counts), 512, 256, 9
+    cfg = synth.LayerConfig(f"rows_m{M}_h{h}_i{i}_e{E}_top{k}", M, h, i, E, k, "normal", "tile row counts")
+    owner = np.repeat(np.arange(8), counts)[np.random.default_rng(5).permutation(M)]   # spread over the batch
+    logits = np.zeros((M, E), np.float32)
+    logits[np.arange(M), owner] = 3.0
+    if k == 2:
+        logits[:, 8] = 2.0
+    L = Layer(cfg, 4242 + k, dev, logits=logits)
+    ref, inter = L.oracle(intermediates=True)
+    assert np.array_equal(np.bincount(inter["ids"].ravel(), minlength=E)[:8], counts)
+    outs = {}
+    for path in (moe_mod.PATH_PREFILL, moe_mod.PATH_PRODUCER):
+        ws = moe_mod.alloc_workspace(M, h, i, E, k, device=dev, path=path)
+        out = moe_mod.moe_fp8_forward_ws_path(L.tx, L.tl, L.t13, L.ts13, L.t2, L.ts2, k, ws, path)
+        torch.cuda.synchronize()
+        _check_intermediates(moe_mod, L, ws, inter, path=path)
+        outs[path] = to_host_bits(out)
+    assert np.array_equal(outs[moe_mod.PATH_PREFILL], outs[moe_mod.PATH_PRODUCER])
+    allow = flip_allowance(L, inter)
+    r16_report(cfg.name, outs[moe_mod.PATH_PREFILL], ref, allow)
+    check_output(outs[moe_mod.PATH_PREFILL], ref, allowance=allow)
+
+
 def test_producer_matches_oracle(dev, moe_mod):
     """The producer and its reducer on the 768-row verify batch (64 x 12
     tokens), every intermediate and the output against the oracle at the
