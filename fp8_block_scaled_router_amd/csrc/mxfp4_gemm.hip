@@ -28,7 +28,11 @@ namespace {
 
 constexpr int kMxRowsPerWave = 32;               // two A fragments
 constexpr int kMxRowsPerGroup = 4 * kMxRowsPerWave;
-constexpr int kMxUnrollUp = 4;
+// K blocks per gate/up batch: a wave covers 32 weight rows, so the grid is
+// half the FP8 kernel's, and 8 blocks (twice 4) keep the bytes in flight of
+// that kernel per CU.
+constexpr int kMxUnrollUp = 8;
+constexpr int kMxScaleWords = kMxUnrollUp / 4;   // 16-byte words of E8M0 scales per row and batch
 constexpr int kMxUnrollDown = 2;
 
 // The B operand of one 128-byte activation K block for lane group g.
@@ -84,9 +88,11 @@ __device__ __forceinline__ int scale_of(const uint4& s4, int u, int grp) {
 }
 
 // Activation staging of the gate/up kernel: a batch of kMxUnrollUp K blocks
-// of the 16 routes of a column block, one 528-byte LDS row per route (512
-// bytes plus 16 of padding, so the 16 routes' fragment reads hit distinct
-// banks), two buffers.
+// of the 16 routes of a column block, one LDS row per route (the batch's
+// 1024 bytes plus 16 of padding, so the 16 routes' fragment reads hit
+// distinct banks), two buffers.  Copied straight from global memory
+// (global_load_lds: one 1 KiB copy per route, four per wave), so no
+// register holds them.
 constexpr int kMxStageRow = 128 * kMxUnrollUp + 16;
 constexpr int kMxStageBytes = 16 * kMxStageRow;
 
@@ -94,11 +100,11 @@ constexpr int kMxStageBytes = 16 * kMxStageRow;
 // weight rows of blockIdx.x (32 per wave: two A fragments share each
 // activation operand): sum over K blocks of the block-scaled MFMA sum times
 // the activation scale.  The activation operands come from LDS: each batch of
-// four K blocks of the column block's 16 routes is fetched once per
-// workgroup (32 bytes per thread), not once per wave, so the waves' vector
-// memory requests are the weights'; the next batch's weights, scales and
-// activations are requested before the current batch is multiplied.
-__global__ __launch_bounds__(256) void stream_gate_up_mx_kernel(
+// kMxUnrollUp K blocks of the column block's 16 routes is copied once per
+// workgroup, not once per wave, so the waves' register loads are the
+// weights'; the next batch's weights, scales and activations are requested
+// before the current batch is multiplied.
+__global__ __launch_bounds__(256, 2) void stream_gate_up_mx_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ w13,
     const uint8_t* __restrict__ e13, const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted,
     const int32_t* __restrict__ active, const int32_t* __restrict__ num_active, float* __restrict__ g, int h,
@@ -121,43 +127,52 @@ __global__ __launch_bounds__(256) void stream_gate_up_mx_kernel(
         wrow[f] = w13 + ((size_t)e * N + n0 + 16 * f + col) * (h / 2) + 16 * grp;
         srow[f] = e13 + ((size_t)e * N + n0 + 16 * f + col) * (h / 32);
     }
-    // staging thread: route sr of the column block, 32-byte piece sp of a batch
-    const int sr = tid >> 4, sp = tid & 15;
-
     for (int j0 = 0; j0 < cnt; j0 += 16) {
         const bool valid = j0 + col < cnt;
         const int p = valid ? sorted[beg + j0 + col] : sorted[beg];
         const float* xsr = xs + (size_t)(p / k) * KB;
-        const int ps = j0 + sr < cnt ? sorted[beg + j0 + sr] : sorted[beg];
-        const uint8_t* xst = xq + (size_t)(ps / k) * h + 32 * (sp & 3);
+        // the activation rows this wave copies: routes 4 wave .. 4 wave + 3 of
+        // the column block (past the expert's routes: its first, never read)
+        const uint8_t* xst[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int jr = j0 + 4 * wave + r;
+            xst[r] = xq + (size_t)((jr < cnt ? sorted[beg + jr] : sorted[beg]) / k) * h;
+        }
 
         // Two register sets (batch b uses set b & 1 and stage buffer b & 1);
         // the loop below is unrolled by two so that each set has a name.
-        uint4 A0[2][kMxUnrollUp], S0[2], X0a, X0b, A1[2][kMxUnrollUp], S1[2], X1a, X1b;
+        uint4 A0[2][kMxUnrollUp], S0[2][kMxScaleWords], A1[2][kMxUnrollUp], S1[2][kMxScaleWords];
         float C0[kMxUnrollUp], C1[kMxUnrollUp];   // activation scales of the batch
         v4f acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
-#define MX_ISSUE(A, S, Xa, Xb, C, b)                                                                       \
+#define MX_ISSUE(A, S, C, bi, b)                                                                     \
     do {                                                                                             \
         const int kb0_ = (b) * kMxUnrollUp;                                                          \
-        _Pragma("unroll") for (int f = 0; f < 2; ++f) S[f] = load_scales4(srow[f], kb0_, KB, vec);   \
+        /* lane l copies bytes 16 l .. 16 l + 15 of the batch (clamped to the row; past the last */ \
+        /* K block they are never read) */                                                           \
+        const int off_ = min(kb0_ * 128 + 16 * lane, h - 16);                                       \
+        _Pragma("unroll") for (int r = 0; r < 4; ++r)                                                \
+            copy16_to_lds(xst[r] + off_, (uint32_t)__builtin_amdgcn_readfirstlane(                  \
+                              lds_addr(stage[bi] + (4 * wave + r) * kMxStageRow)));                  \
+        _Pragma("unroll") for (int f = 0; f < 2; ++f)                                                \
+            _Pragma("unroll") for (int w = 0; w < kMxScaleWords; ++w)                                \
+                S[f][w] = kb0_ + 4 * w < KB ? load_scales4(srow[f], kb0_ + 4 * w, KB, vec)           \
+                                            : make_uint4(0u, 0u, 0u, 0u);                            \
         _Pragma("unroll") for (int u = 0; u < kMxUnrollUp; ++u) if (kb0_ + u < KB) {                 \
             _Pragma("unroll") for (int f = 0; f < 2; ++f)                                            \
                 A[f][u] = *reinterpret_cast<const uint4*>(wrow[f] + (kb0_ + u) * 64);                \
             C[u] = xsr[kb0_ + u];                                                                    \
         }                                                                                            \
-        /* past the last K block the piece reloads the last one (never read) */                    \
-        const int kbs_ = min(kb0_ + sp / 4, KB - 1);                                                 \
-        Xa = *reinterpret_cast<const uint4*>(xst + kbs_ * 128);                                      \
-        Xb = *reinterpret_cast<const uint4*>(xst + kbs_ * 128 + 16);                                 \
     } while (0)
-#define MX_STEP(A, S, Xa, Xb, C, An, Sn, Xna, Xnb, Cn, bi, b)                                                        \
+#define MX_STEP(A, S, C, An, Sn, Cn, bi, b)                                                          \
     do {                                                                                             \
         const int kb0_ = (b) * kMxUnrollUp;                                                          \
         uint8_t* st_ = stage[bi];                                                                    \
-        *reinterpret_cast<uint4*>(st_ + sr * kMxStageRow + 32 * sp) = Xa;                           \
-        *reinterpret_cast<uint4*>(st_ + sr * kMxStageRow + 32 * sp + 16) = Xb;                      \
-        __syncthreads(); /* the batch's activations are in LDS; the other buffer is free */         \
-        if ((b) + 1 < nb) MX_ISSUE(An, Sn, Xna, Xnb, Cn, (b) + 1);                                           \
+        /* this wave's copies of the batch have landed (and its loads); the barrier publishes */    \
+        /* every wave's, and certifies that the other buffer is no longer read */                   \
+        __builtin_amdgcn_s_waitcnt(vm_wait(0));                                                      \
+        __syncthreads();                                                                             \
+        if ((b) + 1 < nb) MX_ISSUE(An, Sn, Cn, (bi) ^ 1, (b) + 1);                                  \
         __builtin_amdgcn_sched_barrier(0);                                                           \
         _Pragma("unroll") for (int u = 0; u < kMxUnrollUp; ++u) {                                    \
             const int kb = kb0_ + u;                                                                 \
@@ -166,16 +181,16 @@ __global__ __launch_bounds__(256) void stream_gate_up_mx_kernel(
                 const float sc = valid ? C[u] : 0.0f;                                                \
                 _Pragma("unroll") for (int f = 0; f < 2; ++f) {                                      \
                     const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};                                          \
-                    const v4f blk = mfma_16x16x128_fp4_e4m3(A[f][u], B, scale_of(S[f], u, grp), z);            \
+                    const v4f blk = mfma_16x16x128_fp4_e4m3(A[f][u], B, scale_of(S[f][u >> 2], u & 3, grp), z); \
                     _Pragma("unroll") for (int v = 0; v < 4; ++v) acc[f][v] = fmaf(blk[v], sc, acc[f][v]); \
                 }                                                                                    \
             }                                                                                        \
         }                                                                                            \
     } while (0)
-        MX_ISSUE(A0, S0, X0a, X0b, C0, 0);
+        MX_ISSUE(A0, S0, C0, 0, 0);
         for (int b = 0; b < nb; b += 2) {
-            MX_STEP(A0, S0, X0a, X0b, C0, A1, S1, X1a, X1b, C1, 0, b);
-            if (b + 1 < nb) MX_STEP(A1, S1, X1a, X1b, C1, A0, S0, X0a, X0b, C0, 1, b + 1);
+            MX_STEP(A0, S0, C0, A1, S1, C1, 0, b);
+            if (b + 1 < nb) MX_STEP(A1, S1, C1, A0, S0, C0, 1, b + 1);
         }
 #undef MX_STEP
 #undef MX_ISSUE
