@@ -33,6 +33,15 @@ constexpr int kRowsPerGroup = kRowsPerWave * kWavesPerGroup;  // 64
 constexpr int kUnrollUp = 4;
 constexpr int kUnrollDown = 2;
 
+// Gate/up batches: kUpBatch K blocks of the wave's weight lines in registers;
+// the 16 routes' activation codes and scales of the batch copied once per
+// workgroup straight into LDS (global_load_lds: one 1 KiB copy per route,
+// four per wave, and one copy of their scales), two buffers, one barrier per
+// batch.  With no activation operand held in registers, a batch of 8 blocks
+// (16 KiB of weights per wave in flight) fits four waves per SIMD.
+constexpr int kUpBatch = 8;
+constexpr int kUpStageRow = 128 * kUpBatch + 16;   // one route's codes of a batch (padded: conflict-free reads)
+
 __global__ __launch_bounds__(256) void stream_gate_up_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ w13,
     const float* __restrict__ s13, const int32_t* __restrict__ offsets,
@@ -42,52 +51,77 @@ __global__ __launch_bounds__(256) void stream_gate_up_kernel(
     if (slot >= *num_active) return;
     const int e = active[slot];
     const int beg = offsets[e], cnt = offsets[e + 1] - beg;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int N = 2 * i, KB = h / 128;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int N = 2 * i, KB = h / 128, nb = (KB + kUpBatch - 1) / kUpBatch;
     const int n0 = blockIdx.x * kRowsPerGroup + wave * kRowsPerWave;
     const int col = lane & 15, kg = lane >> 4;
     const uint8_t* wrow = w13 + ((size_t)e * N + n0) * h;
     const float* ws = s13 + ((size_t)e * (N / 128) + n0 / 128) * KB;
     __shared__ __align__(16) uint8_t bounce[kWavesPerGroup][2][2048];   // line-to-fragment buffers
+    __shared__ __align__(16) uint8_t stage[2][16 * kUpStageRow];        // activation codes of a batch
+    __shared__ __align__(16) float xsl[2][kWavesPerGroup][64];          // their scales: wave w's routes 4 w .. 4 w + 3
 
     for (int j0 = 0; j0 < cnt; j0 += 16) {
         const bool valid = j0 + col < cnt;
         const int p = valid ? sorted[beg + j0 + col] : 0;
-        const int t = p / k;
-        const uint8_t* xrow = xq + (size_t)t * h + kg * 32;
-        const float* xsr = xs + (size_t)t * KB;
-        v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int kb0 = 0; kb0 < KB; kb0 += kUnrollUp) {
-            // Every load of the batch is issued before any of them is used: the
-            // scales are multiplied only in the MFMA loop (a product here would
-            // make the wave wait for all earlier loads of the batch, since the
-            // memory counter retires in order), and a column past the expert's
-            // routes reads route 0's row (finite codes) and gets a zero scale.
-            v8i A[kUnrollUp], B[kUnrollUp];
-            float xsv[kUnrollUp], wsv[kUnrollUp];
+        // the routes this wave copies (past the expert's routes: its first; its scale is never used)
+        const uint8_t* xst[4];
+        const float* xsst[4];
 #pragma unroll
-            for (int u = 0; u < kUnrollUp; ++u) {
+        for (int r = 0; r < 4; ++r) {
+            const int jr = j0 + 4 * wave + r;
+            const int tr = (jr < cnt ? sorted[beg + jr] : sorted[beg]) / k;
+            xst[r] = xq + (size_t)tr * h;
+            xsst[r] = xs + (size_t)tr * KB;
+        }
+        const int lr = (lane & 31) >> 3;   // scale copy: route 4 wave + lr, block kb0 + lane % 8
+        const float* xss = lr == 0 ? xsst[0] : lr == 1 ? xsst[1] : lr == 2 ? xsst[2] : xsst[3];
+        v8i A[kUpBatch];
+        float wsv[kUpBatch];
+        // batch b into buffer bi: the activation codes and scales by copies,
+        // the weight lines and scales into registers
+        auto issue = [&](int b, int bi) {
+            const int kb0 = b * kUpBatch;
+            const int off = min(kb0 * 128 + 16 * lane, h - 16);   // past the last K block: never read
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                copy16_to_lds(xst[r] + off,
+                              (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(&stage[bi][(4 * wave + r) * kUpStageRow])));
+            copy4_to_lds(xss + min(kb0 + (lane & 7), KB - 1),
+                         (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(&xsl[bi][wave][0])));
+#pragma unroll
+            for (int u = 0; u < kUpBatch; ++u) {
                 const int kb = kb0 + u;
                 if (kb < KB) {
                     A[u] = load_lines(wrow + kb * 128, h, lane);
-                    B[u] = load32(xrow + kb * 128);
-                    xsv[u] = xsr[kb];
                     wsv[u] = ws[kb];
                 }
             }
-            __builtin_amdgcn_sched_barrier(0);
+        };
+        v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        issue(0, 0);
+        for (int b = 0; b < nb; ++b) {
+            const int bi = b & 1;
+            // this wave's copies and loads of the batch have landed; the barrier
+            // publishes every wave's copies (and certifies that the other buffer
+            // is no longer read)
+            __builtin_amdgcn_s_waitcnt(vm_wait(0));
+            __syncthreads();
 #pragma unroll
-            for (int u = 0; u < kUnrollUp; ++u) {
-                const int kb = kb0 + u;
+            for (int u = 0; u < kUpBatch; ++u) {
+                const int kb = b * kUpBatch + u;
                 if (kb < KB) {
-                    const float sc = valid ? xsv[u] * wsv[u] : 0.0f;
+                    const v8i B = load32(&stage[bi][col * kUpStageRow + u * 128 + kg * 32]);
+                    const float sc = valid ? xsl[bi][col >> 2][(col & 3) * 8 + u] * wsv[u] : 0.0f;
                     const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
-                    const v4f blk = mfma_16x16x128_e4m3(lines_to_frag(A[u], &bounce[wave][u & 1][0], lane, col, kg), B[u], z);
+                    const v4f blk = mfma_16x16x128_e4m3(lines_to_frag(A[u], &bounce[wave][u & 1][0], lane, col, kg), B, z);
 #pragma unroll
                     for (int v = 0; v < 4; ++v) acc[v] = fmaf(blk[v], sc, acc[v]);
                 }
             }
+            if (b + 1 < nb) issue(b + 1, bi ^ 1);
         }
+        __syncthreads();   // the stage buffers are reused by the next group of routes
         if (valid)
             *reinterpret_cast<float4*>(g + (size_t)p * N + n0 + kg * 4) =
                 make_float4(acc[0], acc[1], acc[2], acc[3]);
