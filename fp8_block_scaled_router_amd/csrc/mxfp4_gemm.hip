@@ -33,7 +33,7 @@ constexpr int kMxRowsPerGroup = 4 * kMxRowsPerWave;
 // that kernel per CU.
 constexpr int kMxUnrollUp = 8;
 constexpr int kMxScaleWords = kMxUnrollUp / 4;   // 16-byte words of E8M0 scales per row and batch
-constexpr int kMxUnrollDown = 2;
+constexpr int kMxUnrollDown = 3;
 
 // The B operand of one 128-byte activation K block for lane group g.
 __device__ __forceinline__ v8i act_operand(const uint8_t* blk, int g) {
@@ -42,17 +42,24 @@ __device__ __forceinline__ v8i act_operand(const uint8_t* blk, int g) {
     return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
+// One route's gate and up values of one 128-column group, 8 columns per lane
+// of a 16-lane row.
+struct GateUp8Mx {
+    float4 g0, g1, u0, u1;
+};
+__device__ __forceinline__ GateUp8Mx load_gate_up8_mx(const float* __restrict__ gate, int sub, int i) {
+    const float4* gp = reinterpret_cast<const float4*>(gate + sub * 8);
+    const float4* up = reinterpret_cast<const float4*>(gate + i + sub * 8);
+    return {gp[0], gp[1], up[0], up[1]};
+}
+
 // SiLU(gate) * up of one 128-column group of one route on one 16-lane row,
-// requantised to E4M3 (the same arithmetic as the FP8 streaming path).
-__device__ __forceinline__ void silu_quant_row_mx(const float* __restrict__ gate, const float* __restrict__ up,
-                                                  int sub, uint8_t* __restrict__ q, float* __restrict__ s,
-                                                  bool write_scale) {
-    const float4 g0 = reinterpret_cast<const float4*>(gate + sub * 8)[0];
-    const float4 g1 = reinterpret_cast<const float4*>(gate + sub * 8)[1];
-    const float4 u0 = reinterpret_cast<const float4*>(up + sub * 8)[0];
-    const float4 u1 = reinterpret_cast<const float4*>(up + sub * 8)[1];
-    const float a[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-    const float b[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+// requantised to E4M3 (the same arithmetic as the FP8 streaming path); stored
+// only where live.
+__device__ __forceinline__ void silu_quant_row_mx(const GateUp8Mx& x, int sub, uint8_t* __restrict__ q,
+                                                  float* __restrict__ s, bool write_scale, bool live = true) {
+    const float a[8] = {x.g0.x, x.g0.y, x.g0.z, x.g0.w, x.g1.x, x.g1.y, x.g1.z, x.g1.w};
+    const float b[8] = {x.u0.x, x.u0.y, x.u0.z, x.u0.w, x.u1.x, x.u1.y, x.u1.z, x.u1.w};
     float v[8];
     float m = 0.0f;
 #pragma unroll
@@ -62,8 +69,11 @@ __device__ __forceinline__ void silu_quant_row_mx(const float* __restrict__ gate
     }
     m = row16_max(m);
     const float sc = m / kE4M3Max;
-    *reinterpret_cast<uint2*>(q + sub * 8) = quant8(v, sc);
-    if (write_scale) *s = sc;
+    const uint2 codes = quant8(v, sc);
+    if (live) {
+        *reinterpret_cast<uint2*>(q + sub * 8) = codes;
+        if (write_scale) *s = sc;
+    }
 }
 
 }  // namespace
@@ -233,33 +243,54 @@ __global__ __launch_bounds__(256) void stream_down_mx_kernel(
         srow[f] = e2 + ((size_t)e * h + n0 + 16 * f + col) * (i / 32);
     }
 
+    const int sub = lane & 15;
+
     for (int j0 = 0; j0 < cnt; j0 += 16) {
-        const int nr = min(16, cnt - j0);
+        const int nr = min(16, cnt - j0), ntask = nr * IB;
         __syncthreads();
-        for (int task = wave * 4 + (lane >> 4); task < nr * IB; task += 16) {
+        // As in the FP8 down kernel: the prologue's first task per 16-lane row
+        // reads its gate/up values, then the first weight batch goes out, so
+        // the weights stream while the SiLU codes are computed (both requests
+        // unconditional, with clamped indices, so that the compiler's count of
+        // outstanding loads is the same on every path).
+        const int t0 = wave * 4 + (lane >> 4);
+        const int tc = min(t0, ntask - 1), jr0 = tc / IB, b0 = tc - jr0 * IB;
+        const GateUp8Mx x0 = load_gate_up8_mx(g + (size_t)sorted[beg + j0 + jr0] * 2 * i + b0 * 128, sub, i);
+        uint4 A[2][kMxUnrollDown];
+        uint32_t sw[2][kMxUnrollDown];
+        // a zero K-block offset through an empty asm: the first batch is neither
+        // hoisted out of the route-group loop nor moved above the gate/up reads
+        int kz = 0;
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" : "+s"(kz));
+        // batch kb0's weight codes and scales (past the last K block: the last
+        // block again, never used)
+        auto load_w = [&](int kb0) {
+#pragma unroll
+            for (int u = 0; u < kMxUnrollDown; ++u) {
+                const int kb = min(kb0 + u, IB - 1) + kz;
+#pragma unroll
+                for (int f = 0; f < 2; ++f) {
+                    A[f][u] = *reinterpret_cast<const uint4*>(wrow[f] + kb * 64);
+                    sw[f][u] = *reinterpret_cast<const uint32_t*>(srow[f] + 4 * kb);
+                }
+            }
+        };
+        load_w(0);
+        __builtin_amdgcn_sched_barrier(0);   // every request of the batch before the SiLU codes
+        // (computed on every row, so that the gate/up loads stay in this block)
+        silu_quant_row_mx(x0, sub, a2l + jr0 * astride + b0 * 128, a2sl + jr0 * IB + b0, sub == 0, t0 < ntask);
+        for (int task = t0 + 16; task < ntask; task += 16) {
             const int jr = task / IB, b = task - jr * IB;
-            const int p = sorted[beg + j0 + jr];
-            const float* gate = g + (size_t)p * 2 * i + b * 128;
-            silu_quant_row_mx(gate, gate + i, lane & 15, a2l + jr * astride + b * 128, a2sl + jr * IB + b,
-                              (lane & 15) == 0);
+            const GateUp8Mx x = load_gate_up8_mx(g + (size_t)sorted[beg + j0 + jr] * 2 * i + b * 128, sub, i);
+            silu_quant_row_mx(x, sub, a2l + jr * astride + b * 128, a2sl + jr * IB + b, sub == 0);
         }
         __syncthreads();
         const bool valid = col < nr;
         const int p = valid ? sorted[beg + j0 + col] : 0;
         v4f acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
         for (int kb0 = 0; kb0 < IB; kb0 += kMxUnrollDown) {
-            uint4 A[2][kMxUnrollDown];
-            uint32_t sw[2][kMxUnrollDown];
-#pragma unroll
-            for (int u = 0; u < kMxUnrollDown; ++u) {
-                const int kb = kb0 + u;
-                if (kb < IB)
-#pragma unroll
-                    for (int f = 0; f < 2; ++f) {
-                        A[f][u] = *reinterpret_cast<const uint4*>(wrow[f] + kb * 64);
-                        sw[f][u] = *reinterpret_cast<const uint32_t*>(srow[f] + 4 * kb);
-                    }
-            }
+            if (kb0 > 0) load_w(kb0);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int u = 0; u < kMxUnrollDown; ++u) {

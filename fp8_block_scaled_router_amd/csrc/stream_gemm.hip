@@ -31,7 +31,7 @@ constexpr int kRowsPerGroup = kRowsPerWave * kWavesPerGroup;  // 64
 // 8 -> 2 cut down time by 34%; holding a whole down tile in registers ahead
 // of the SiLU prologue was slower for the occupancy it costs).
 constexpr int kUnrollUp = 4;
-constexpr int kUnrollDown = 2;
+constexpr int kUnrollDown = 3;
 
 // Gate/up batches: kUpBatch K blocks of the wave's weight lines in registers;
 // the 16 routes' activation codes and scales of the batch copied once per
@@ -128,18 +128,23 @@ __global__ __launch_bounds__(256) void stream_gate_up_kernel(
     }
 }
 
+// One route's gate and up values of one 128-column group, 8 columns per lane
+// of a 16-lane row.
+struct GateUp8 {
+    float4 g0, g1, u0, u1;
+};
+__device__ __forceinline__ GateUp8 load_gate_up8(const float* __restrict__ gate, int sub, int i) {
+    const float4* gp = reinterpret_cast<const float4*>(gate + sub * 8);
+    const float4* up = reinterpret_cast<const float4*>(gate + i + sub * 8);
+    return {gp[0], gp[1], up[0], up[1]};
+}
+
 // SiLU(gate) * up of one 128-column group for one route on one 16-lane row,
-// requantised to E4M3 (amax over the row by DPP).
-__device__ __forceinline__ void silu_quant_row(const float* __restrict__ gate,
-                                               const float* __restrict__ up, int sub,
-                                               uint8_t* __restrict__ q, float* __restrict__ s,
-                                               bool write_scale) {
-    const float4 g0 = reinterpret_cast<const float4*>(gate + sub * 8)[0];
-    const float4 g1 = reinterpret_cast<const float4*>(gate + sub * 8)[1];
-    const float4 u0 = reinterpret_cast<const float4*>(up + sub * 8)[0];
-    const float4 u1 = reinterpret_cast<const float4*>(up + sub * 8)[1];
-    const float a[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-    const float b[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+// requantised to E4M3 (amax over the row by DPP); stored only where live.
+__device__ __forceinline__ void silu_quant_row(const GateUp8& x, int sub, uint8_t* __restrict__ q,
+                                               float* __restrict__ s, bool write_scale, bool live = true) {
+    const float a[8] = {x.g0.x, x.g0.y, x.g0.z, x.g0.w, x.g1.x, x.g1.y, x.g1.z, x.g1.w};
+    const float b[8] = {x.u0.x, x.u0.y, x.u0.z, x.u0.w, x.u1.x, x.u1.y, x.u1.z, x.u1.w};
     float v[8];
     float m = 0.0f;
 #pragma unroll
@@ -149,8 +154,11 @@ __device__ __forceinline__ void silu_quant_row(const float* __restrict__ gate,
     }
     m = row16_max(m);
     const float sc = m / kE4M3Max;
-    *reinterpret_cast<uint2*>(q + sub * 8) = quant8(v, sc);
-    if (write_scale) *s = sc;
+    const uint2 codes = quant8(v, sc);
+    if (live) {
+        *reinterpret_cast<uint2*>(q + sub * 8) = codes;
+        if (write_scale) *s = sc;
+    }
 }
 
 __host__ __device__ inline size_t stream_down_lds_base(int i) {
@@ -177,36 +185,62 @@ __global__ __launch_bounds__(256) void stream_down_kernel(
     const uint8_t* wrow = w2 + ((size_t)e * h + n0) * i;
     const float* ws = s2 + ((size_t)e * (h / 128) + n0 / 128) * IB;
     uint8_t* bnc = lds + stream_down_lds_base(i) + wave * 4096;
+    const int sub = lane & 15;
 
     for (int j0 = 0; j0 < cnt; j0 += 16) {
-        const int nr = min(16, cnt - j0);
+        const int nr = min(16, cnt - j0), ntask = nr * IB;
         __syncthreads();
-        for (int task = wave * 4 + (lane >> 4); task < nr * IB; task += 16) {
+        // The prologue's first task per 16-lane row (route jr, column group
+        // b): its gate/up reads go out first, then the first weight batch, so
+        // the weights stream while the SiLU codes are computed (the memory
+        // counter retires in order: waiting for the gate/up values does not
+        // wait for the weights issued after them).
+        // (Both unconditional, with clamped indices, so that the compiler's
+        // count of outstanding loads is the same on every path.)
+        const int t0 = wave * 4 + (lane >> 4);
+        const int tc = min(t0, ntask - 1), jr0 = tc / IB, b0 = tc - jr0 * IB;
+        const GateUp8 x0 = load_gate_up8(g + (size_t)sorted[beg + j0 + jr0] * 2 * i + b0 * 128, sub, i);
+        v8i A[kUnrollDown];
+        float wsv[kUnrollDown];
+        // The weight loads take a zero K-block offset that passes through an
+        // empty asm here, so the compiler neither hoists the first batch out of
+        // the route-group loop (ahead of the gate/up reads) nor moves it above
+        // them.
+        int kz = 0;
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" : "+s"(kz));
+        // batch kb0's weight lines and scales (past the last K block: the last
+        // block again, never used)
+        auto load_w = [&](int kb0) {
+#pragma unroll
+            for (int u = 0; u < kUnrollDown; ++u) {
+                const int kb = min(kb0 + u, IB - 1) + kz;
+                A[u] = load_lines(wrow + kb * 128, i, lane);
+                wsv[u] = ws[kb];
+            }
+        };
+        load_w(0);
+        __builtin_amdgcn_sched_barrier(0);   // every request of the batch before the SiLU codes
+        // (computed on every row, so that the gate/up loads stay in this block)
+        silu_quant_row(x0, sub, a2l + jr0 * astride + b0 * 128, a2sl + jr0 * IB + b0, sub == 0, t0 < ntask);
+        for (int task = t0 + 16; task < ntask; task += 16) {
             const int jr = task / IB, b = task - jr * IB;
-            const int p = sorted[beg + j0 + jr];
-            const float* gate = g + (size_t)p * 2 * i + b * 128;
-            silu_quant_row(gate, gate + i, lane & 15, a2l + jr * astride + b * 128, a2sl + jr * IB + b,
-                           (lane & 15) == 0);
+            const GateUp8 x = load_gate_up8(g + (size_t)sorted[beg + j0 + jr] * 2 * i + b * 128, sub, i);
+            silu_quant_row(x, sub, a2l + jr * astride + b * 128, a2sl + jr * IB + b, sub == 0);
         }
         __syncthreads();
         const bool valid = col < nr;
         const int p = valid ? sorted[beg + j0 + col] : 0;
         v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
         for (int kb0 = 0; kb0 < IB; kb0 += kUnrollDown) {
-            // As in gate/up: all loads of the batch first, scales multiplied
-            // in the MFMA loop.  The activation codes are read from LDS for
-            // every column; a column past the routes gets a zero scale.
-            v8i A[kUnrollDown], B[kUnrollDown];
-            float asv[kUnrollDown], wsv[kUnrollDown];
-#pragma unroll
-            for (int u = 0; u < kUnrollDown; ++u) {
-                const int kb = kb0 + u;
-                if (kb < IB) {
-                    A[u] = load_lines(wrow + kb * 128, i, lane);
-                    wsv[u] = ws[kb];
-                }
-            }
+            // As in gate/up: all loads of the batch first (the first batch's
+            // before the prologue), scales multiplied in the MFMA loop.  The
+            // activation codes are read from LDS for every column; a column
+            // past the routes gets a zero scale.
+            if (kb0 > 0) load_w(kb0);
             __builtin_amdgcn_sched_barrier(0);
+            v8i B[kUnrollDown];
+            float asv[kUnrollDown];
 #pragma unroll
             for (int u = 0; u < kUnrollDown; ++u) {
                 const int kb = kb0 + u;

@@ -423,6 +423,8 @@ def _custom_layer(dev, M, h, i, E, k, seed, logits_kind="normal"):
     (5, 256, 128, 1, 1),        # one expert, k = 1
     (4, 256, 128, 8, 8),        # k = E
     (7, 1280, 640, 256, 16),    # E = 256, k = 16
+    (6, 1152, 256, 16, 4),      # streaming gate/up: 9 K blocks, a last batch of one
+    (10, 896, 384, 12, 3),      # streaming gate/up: 7 K blocks, one partial batch
     (1, 128, 128, 4, 2),        # smallest dims
     (300, 256, 128, 4, 2),      # tiled path: ragged 128-route tiles per expert
     (1000, 512, 384, 8, 3),     # tiled path: several tiles per expert, 3 groups
