@@ -3,8 +3,9 @@
 //
 // Each wave owns 16 weight rows of one expert and streams them once from HBM
 // (K contiguous, 128 bytes per row per K block, fetched as whole lines by
-// load_lines and turned into MFMA fragments through a 4 KiB LDS buffer per
-// wave: 6-11% faster than per-lane fragment loads, measured), feeding
+// nontemporal loads (load_lines_nt: the weights are read once, so they are
+// not kept in the caches) and turned into MFMA fragments through a 4 KiB LDS
+// buffer per wave: 6-11% faster than per-lane fragment loads, measured), feeding
 // v_mfma_f32_16x16x128 with the weights as the A
 // operand and up to 16 of the expert's routes as the B operand (unused
 // columns are zero).  One MFMA covers one 128-wide K block, so the block
@@ -93,7 +94,7 @@ __global__ __launch_bounds__(256) void stream_gate_up_kernel(
             for (int u = 0; u < kUpBatch; ++u) {
                 const int kb = kb0 + u;
                 if (kb < KB) {
-                    A[u] = load_lines(wrow + kb * 128, h, lane);
+                    A[u] = load_lines_nt(wrow + kb * 128, h, lane);
                     wsv[u] = ws[kb];
                 }
             }
@@ -215,7 +216,7 @@ __global__ __launch_bounds__(256) void stream_down_kernel(
 #pragma unroll
             for (int u = 0; u < kUnrollDown; ++u) {
                 const int kb = min(kb0 + u, IB - 1) + kz;
-                A[u] = load_lines(wrow + kb * 128, i, lane);
+                A[u] = load_lines_nt(wrow + kb * 128, i, lane);
                 wsv[u] = ws[kb];
             }
         };
