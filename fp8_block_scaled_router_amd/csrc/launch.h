@@ -101,6 +101,7 @@ struct PrefillArgs {
     uint32_t* done;             // producer: gate/up tiles finished per M-tile (null otherwise)
     uint32_t* err;              // producer: the workspace's sticky error word
     int h, i, E, k;
+    int weights_nt;             // FP8: nonzero copies the weight tiles with nontemporal loads
 };
 int prefill_tile_m();
 bool prefill_supported(int M, int h, int i, int k);

@@ -275,6 +275,13 @@ int tiled_forward(const Layout& L, void* workspace, const void* x, const float* 
     pa.i = i;
     pa.E = E;
     pa.k = k;
+    // With at most 64 routes per expert on average most experts fill one
+    // 128-route tile, so each FP8 weight tile is copied once per forward and
+    // need not stay in the caches; with more, the route tiles of an expert
+    // share its weight tiles through the L2.  (The 64-byte MXFP4 rows keep
+    // ordinary copies: the two K blocks of a 128-byte line go out in
+    // different stages.)
+    pa.weights_nt = !mx && (int64_t)M * k <= (int64_t)64 * E;
     uint16_t* o = static_cast<uint16_t*>(out);
     if (p.path == MOE_FP8_PATH_PRODUCER) {
         pa.done = sync + moe::kSyncProdDone / 4;

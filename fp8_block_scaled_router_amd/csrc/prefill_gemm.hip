@@ -168,10 +168,21 @@ struct Loop {
 };
 
 
-// Issue the copies of K block kb into stage buffer st (kCoh: the activation
-// tile and its scales at device scope).
-template <bool kMx, bool kCoh = false>
+// A 16-byte global->LDS copy with a nontemporal load (data read once).
+__device__ __forceinline__ void copy16_to_lds_nt(const void* src, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
+                 :: "s"(lds), "v"(src) : "memory", "m0");
+}
+
+// Copy modes of the K loop's stage copies: plain; the activation tile and its
+// scales at device scope (the producer); the FP8 weight tiles by nontemporal
+// loads (read once per forward).
+constexpr int kCopyPlain = 0, kCopyCoherent = 1, kCopyWeightsNt = 2;
+
+// Issue the copies of K block kb into stage buffer st in copy mode kCopy.
+template <bool kMx, int kCopy = kCopyPlain>
 __device__ __forceinline__ void issue_stage(const Loop& L, uint8_t* st, int kb) {
+    constexpr bool kCoh = kCopy == kCopyCoherent;
     using F = Fmt<kMx>;
     const uint8_t* gA = L.gA + (size_t)kb * F::kRowBytes;
     const uint8_t* gB = L.gB + (size_t)kb * 128;
@@ -179,8 +190,13 @@ __device__ __forceinline__ void issue_stage(const Loop& L, uint8_t* st, int kb) 
     // registers for M0 whatever the compiler proves)
     const uint32_t base = lds_addr(st);
     auto dst = [&](uint32_t off) { return (uint32_t)__builtin_amdgcn_readfirstlane(base + off); };
+    if constexpr (!kMx && kCopy == kCopyWeightsNt) {
 #pragma unroll
-    for (int q = 0; q < F::kDmaA; ++q) copy16_to_lds(gA + L.offA[q], dst((L.wave * F::kDmaA + q) * 1024));
+        for (int q = 0; q < F::kDmaA; ++q) copy16_to_lds_nt(gA + L.offA[q], dst((L.wave * F::kDmaA + q) * 1024));
+    } else {
+#pragma unroll
+        for (int q = 0; q < F::kDmaA; ++q) copy16_to_lds(gA + L.offA[q], dst((L.wave * F::kDmaA + q) * 1024));
+    }
 #pragma unroll
     for (int q = 0; q < kDmaB; ++q)
         copy16_to_lds<kCoh>(gB + L.offB[q], dst(F::kBOff + (L.wave * kDmaB + q) * 1024));
@@ -262,10 +278,10 @@ __device__ __forceinline__ void block_mma(v4f acc[16], v4f blk[16], float sw_p[4
 // sw_of(kb, sw) fills the wave's four weight-tile scales of block kb (FP8
 // weights).  The copies of blocks 0 and 1 (into buffers 0 and 1) are issued
 // by the caller, possibly long before (issue_first).
-template <bool kMx, bool kCoh = false>
+template <bool kMx, int kCopy = kCopyPlain>
 __device__ __forceinline__ void issue_first(const Loop& L, int KB, uint8_t* stages) {
-    issue_stage<kMx, kCoh>(L, stages, 0);
-    if (KB > 1) issue_stage<kMx, kCoh>(L, stages + Fmt<kMx>::kStage, 1);
+    issue_stage<kMx, kCopy>(L, stages, 0);
+    if (KB > 1) issue_stage<kMx, kCopy>(L, stages + Fmt<kMx>::kStage, 1);
 }
 
 // after_first() runs once, right after the first barrier: every wave has
@@ -281,7 +297,7 @@ __device__ __forceinline__ void issue_first(const Loop& L, int KB, uint8_t* stag
 struct NoRetarget {
     __device__ void operator()(Loop&) const {}
 };
-template <bool kMx, bool kCoh, int NA, typename SwOf, typename AfterFirst, typename Retarget>
+template <bool kMx, int kCopy, int NA, typename SwOf, typename AfterFirst, typename Retarget>
 __device__ __forceinline__ int k_loop_na(v4f acc[16], Loop& L, int KB, uint8_t* stages, SwOf sw_of,
                                          AfterFirst after_first, int rd0, bool run_on, Retarget retarget) {
     using F = Fmt<kMx>;
@@ -297,10 +313,10 @@ __device__ __forceinline__ int k_loop_na(v4f acc[16], Loop& L, int KB, uint8_t* 
         block_barrier();
         uint8_t* const wr = stages + (rd == 0 ? 2 : rd - 1) * F::kStage;
         if (kb + 2 < KB) {
-            issue_stage<kMx, kCoh>(L, wr, kb + 2);
+            issue_stage<kMx, kCopy>(L, wr, kb + 2);
         } else if (run_on) {
             if (kb + 2 == KB) retarget(L);
-            issue_stage<kMx, kCoh>(L, wr, kb + 2 - KB);
+            issue_stage<kMx, kCopy>(L, wr, kb + 2 - KB);
         }
         if (kb == 0) after_first();
         if constexpr (!kMx) sw_of(kb, sw);
@@ -321,15 +337,15 @@ __device__ __forceinline__ int k_loop_na(v4f acc[16], Loop& L, int KB, uint8_t* 
 // wave-uniform; every instance waits, copies and meets the barriers alike):
 // all four (one to four), or none; with kHalf also the first two (one or
 // two).  The down kernel has the register room for two instances only.
-template <bool kMx, bool kCoh, bool kHalf, typename SwOf, typename AfterFirst, typename Retarget = NoRetarget>
+template <bool kMx, int kCopy, bool kHalf, typename SwOf, typename AfterFirst, typename Retarget = NoRetarget>
 __device__ __forceinline__ int k_loop(v4f acc[16], Loop& L, int KB, uint8_t* stages, SwOf sw_of,
                                       AfterFirst after_first, int rd0 = 0, bool run_on = false,
                                       Retarget retarget = Retarget{}) {
     if (L.na > (kHalf ? 2 : 0))
-        return k_loop_na<kMx, kCoh, 4>(acc, L, KB, stages, sw_of, after_first, rd0, run_on, retarget);
+        return k_loop_na<kMx, kCopy, 4>(acc, L, KB, stages, sw_of, after_first, rd0, run_on, retarget);
     if (kHalf && L.na > 0)
-        return k_loop_na<kMx, kCoh, 2>(acc, L, KB, stages, sw_of, after_first, rd0, run_on, retarget);
-    return k_loop_na<kMx, kCoh, 0>(acc, L, KB, stages, sw_of, after_first, rd0, run_on, retarget);
+        return k_loop_na<kMx, kCopy, 2>(acc, L, KB, stages, sw_of, after_first, rd0, run_on, retarget);
+    return k_loop_na<kMx, kCopy, 0>(acc, L, KB, stages, sw_of, after_first, rd0, run_on, retarget);
 }
 
 // Roles of the 8 waves: wn (0..3) picks the weight rows of the tile, wr
@@ -566,8 +582,9 @@ __device__ __forceinline__ void gate_up_epilogue(const PrefillArgs& a, const Til
 // launch) are read at device scope, the requantised codes and scales go out
 // at device scope, and each finished tile counts itself in its M-tile's word
 // of a.done.
-template <bool kMx, bool kProd>
+template <bool kMx, bool kProd, bool kNt = false>
 __device__ __forceinline__ void gate_up_tiles(const PrefillArgs& a, TileLds<kMx>& S) {
+    constexpr int kCopy = kProd ? kCopyCoherent : kNt ? kCopyWeightsNt : kCopyPlain;
     using F = Fmt<kMx>;
     uint8_t* const stages = S.stages;
     TileMeta& meta = S.meta;
@@ -593,7 +610,7 @@ __device__ __forceinline__ void gate_up_tiles(const PrefillArgs& a, TileLds<kMx>
     }
     __syncthreads();
     Loop L = gate_up_loop<kMx>(a, t, S.rt[0], wave, lane);
-    issue_first<kMx, kProd>(L, KB, stages);
+    issue_first<kMx, kCopy>(L, KB, stages);
 
     for (;;) {
         span.next += span.step;
@@ -625,10 +642,10 @@ __device__ __forceinline__ void gate_up_tiles(const PrefillArgs& a, TileLds<kMx>
         v4f acc[16];
 #pragma unroll
         for (int u = 0; u < 16; ++u) acc[u] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-        k_loop<kMx, kProd, true>(acc, L, KB, stages, sw_of, next_lists);   // ends with every wave done with the stage buffers
+        k_loop<kMx, kCopy, true>(acc, L, KB, stages, sw_of, next_lists);   // ends with every wave done with the stage buffers
         if (more) {
             L = gate_up_loop<kMx>(a, tn, S.rt[par ^ 1], wave, lane);
-            issue_first<kMx, kProd>(L, KB, stages);   // buffers 0 and 1; the epilogue stages codes in buffer 2
+            issue_first<kMx, kCopy>(L, KB, stages);   // buffers 0 and 1; the epilogue stages codes in buffer 2
         }
         gate_up_epilogue<kProd>(a, t, acc, S.amax, stages + 2 * F::kStage, tid);
         if constexpr (kProd) {
@@ -645,9 +662,11 @@ __device__ __forceinline__ void gate_up_tiles(const PrefillArgs& a, TileLds<kMx>
 
 }  // namespace
 
+// kNt: the weight tiles copied with nontemporal loads.
+template <bool kNt>
 __global__ __launch_bounds__(kThreads, 1) void prefill_gate_up_kernel(PrefillArgs a) {
     __shared__ TileLds<false> S;
-    gate_up_tiles<false, false>(a, S);
+    gate_up_tiles<false, false, kNt>(a, S);
 }
 __global__ __launch_bounds__(kThreads, 1) void prefill_gate_up_mx_kernel(PrefillArgs a) {
     __shared__ TileLds<true> S;
@@ -699,8 +718,9 @@ __device__ __forceinline__ Loop down_loop(const PrefillArgs& a, const TileInfo& 
 // starts only once every gate/up tile of its M-tile has counted itself in
 // (a.done), and reads their codes and scales at device scope; a wait that
 // times out makes the workgroup give up the rest of its share.
-template <bool kMx, bool kProd>
+template <bool kMx, bool kProd, bool kNt = false>
 __device__ __forceinline__ void down_tiles(const PrefillArgs& a, TileLds<kMx>& S) {
+    constexpr int kCopy = kProd ? kCopyCoherent : kNt ? kCopyWeightsNt : kCopyPlain;
     uint8_t* const stages = S.stages;
     TileMeta& meta = S.meta;
 
@@ -736,7 +756,7 @@ __device__ __forceinline__ void down_tiles(const PrefillArgs& a, TileLds<kMx>& S
     __syncthreads();
     if (!ready(t.mt)) return;
     Loop L = down_loop<kMx>(a, t, wave, lane);
-    issue_first<kMx, kProd>(L, IB, stages);
+    issue_first<kMx, kCopy>(L, IB, stages);
 
     const int sblk = wn >> 1;
     int rd0 = 0;   // stage buffer of the tile's first K block
@@ -770,13 +790,13 @@ __device__ __forceinline__ void down_tiles(const PrefillArgs& a, TileLds<kMx>& S
 #pragma unroll
         for (int u = 0; u < 16; ++u) acc[u] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
         auto retarget = [&](Loop& Lr) { Lr = down_loop<kMx>(a, tn, wave, lane); };
-        rd0 = k_loop<kMx, kProd, false>(acc, L, IB, stages, sw_of, next_lists, rd0, kRunOn && more, retarget);
+        rd0 = k_loop<kMx, kCopy, false>(acc, L, IB, stages, sw_of, next_lists, rd0, kRunOn && more, retarget);
         if (!(kRunOn && IB >= 2)) {
             rd0 = 0;
             if (more) {
                 if (!ready(tn.mt)) return;   // no copy is in flight here
                 L = down_loop<kMx>(a, tn, wave, lane);
-                issue_first<kMx, kProd>(L, IB, stages);
+                issue_first<kMx, kCopy>(L, IB, stages);
             }
         }
         // bf16 partial rows (round to nearest even) by route id; lane holds
@@ -804,9 +824,10 @@ __device__ __forceinline__ void down_tiles(const PrefillArgs& a, TileLds<kMx>& S
 
 }  // namespace
 
+template <bool kNt>
 __global__ __launch_bounds__(kThreads, 1) void prefill_down_kernel(PrefillArgs a) {
     __shared__ TileLds<false> S;
-    down_tiles<false, false>(a, S);
+    down_tiles<false, false, kNt>(a, S);
 }
 __global__ __launch_bounds__(kThreads, 1) void prefill_down_mx_kernel(PrefillArgs a) {
     __shared__ TileLds<true> S;
@@ -978,7 +999,8 @@ hipError_t launch_prefill_gate_up(const PrefillArgs& a, bool mx, hipStream_t str
     const int g = persistent_grid();
     if (g <= 0) return hipErrorInvalidDevice;
     if (mx) launch(prefill_gate_up_mx_kernel, dim3(g), dim3(kThreads), 0, stream, a);
-    else launch(prefill_gate_up_kernel, dim3(g), dim3(kThreads), 0, stream, a);
+    else if (a.weights_nt) launch(prefill_gate_up_kernel<true>, dim3(g), dim3(kThreads), 0, stream, a);
+    else launch(prefill_gate_up_kernel<false>, dim3(g), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -986,7 +1008,8 @@ hipError_t launch_prefill_down(const PrefillArgs& a, bool mx, hipStream_t stream
     const int g = persistent_grid();
     if (g <= 0) return hipErrorInvalidDevice;
     if (mx) launch(prefill_down_mx_kernel, dim3(g), dim3(kThreads), 0, stream, a);
-    else launch(prefill_down_kernel, dim3(g), dim3(kThreads), 0, stream, a);
+    else if (a.weights_nt) launch(prefill_down_kernel<true>, dim3(g), dim3(kThreads), 0, stream, a);
+    else launch(prefill_down_kernel<false>, dim3(g), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
