@@ -34,12 +34,30 @@ constexpr int kMxRowsPerGroup = 4 * kMxRowsPerWave;
 constexpr int kMxUnrollUp = 8;
 constexpr int kMxScaleWords = kMxUnrollUp / 4;   // 16-byte words of E8M0 scales per row and batch
 constexpr int kMxUnrollDown = 3;
+constexpr int kMxPairsDown = 3;   // (whole-line loads) K block pairs per down batch
 
 // The B operand of one 128-byte activation K block for lane group g.
 __device__ __forceinline__ v8i act_operand(const uint8_t* blk, int g) {
     const uint4 lo = *reinterpret_cast<const uint4*>(blk + 16 * g);
     const uint4 hi = *reinterpret_cast<const uint4*>(blk + 64 + 16 * g);
     return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+// Whole-line weight loads: load_lines_nt fetches 16 rows x 128 bytes, the
+// two K blocks kb, kb + 1 of each row (64 bytes each), as whole lines
+// (nontemporal: read once); this turns them into the two FP4 A fragments of
+// lane (row col, group g) through a wave-private 2 KiB LDS buffer: 16-byte
+// chunk g of the line (block kb, MX block g) and chunk 4 + g (block kb + 1).
+// The buffer holds the lines in the slot order of load_lines (chunk c = 2 kg
+// + upper of row r in slot lo_slot(r, kg) ^ 4 upper), so 16 lanes of one g
+// read 16 distinct 16-byte bank groups.
+__device__ __forceinline__ void lines_to_mx_frags(const v8i& w, uint8_t* buf, int lane, int col, int g,
+                                                  uint4& a0, uint4& a1) {
+    *reinterpret_cast<uint4*>(buf + lane * 16) = make_uint4((uint32_t)w[0], (uint32_t)w[1], (uint32_t)w[2], (uint32_t)w[3]);
+    *reinterpret_cast<uint4*>(buf + 1024 + lane * 16) = make_uint4((uint32_t)w[4], (uint32_t)w[5], (uint32_t)w[6], (uint32_t)w[7]);
+    const int up = (g & 1) << 2;
+    a0 = *reinterpret_cast<const uint4*>(buf + col * 128 + (lo_slot(col, g >> 1) ^ up) * 16);
+    a1 = *reinterpret_cast<const uint4*>(buf + col * 128 + (lo_slot(col, 2 + (g >> 1)) ^ up) * 16);
 }
 
 // One route's gate and up values of one 128-column group, 8 columns per lane
@@ -113,28 +131,35 @@ constexpr int kMxStageBytes = 16 * kMxStageRow;
 // kMxUnrollUp K blocks of the column block's 16 routes is copied once per
 // workgroup, not once per wave, so the waves' register loads are the
 // weights'; the next batch's weights, scales and activations are requested
-// before the current batch is multiplied.
+// before the current batch is multiplied.  kLines (h a multiple of 256, so
+// that K blocks 2j and 2j + 1 of a row fill one 128-byte line): the weights
+// come as whole lines by nontemporal loads (load_lines_nt, two K blocks per
+// load) and reach the fragment layout through a wave-private LDS buffer.
+template <bool kLines>
 __global__ __launch_bounds__(256, 2) void stream_gate_up_mx_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ w13,
     const uint8_t* __restrict__ e13, const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted,
     const int32_t* __restrict__ active, const int32_t* __restrict__ num_active, float* __restrict__ g, int h,
     int i, int k) {
     __shared__ __align__(16) uint8_t stage[2][kMxStageBytes];
+    __shared__ __align__(16) uint8_t bounce[kLines ? 4 : 1][2][kLines ? 2048 : 16];   // [wave][f] (kLines)
     const int slot = blockIdx.y;
     if (slot >= *num_active) return;
     const int e = active[slot];
     const int beg = offsets[e], cnt = offsets[e + 1] - beg;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int N = 2 * i, KB = h / 128;
     const int nb = (KB + kMxUnrollUp - 1) / kMxUnrollUp;
     const int n0 = blockIdx.x * kMxRowsPerGroup + wave * kMxRowsPerWave;
     const int col = lane & 15, grp = lane >> 4;
     const bool vec = ((h / 32) & 15) == 0 && ((uintptr_t)e13 & 15u) == 0;
     const uint8_t* wrow[2];
+    const uint8_t* wtile[2];   // (kLines) row 0 of the wave's two 16-row tiles
     const uint8_t* srow[2];
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
         wrow[f] = w13 + ((size_t)e * N + n0 + 16 * f + col) * (h / 2) + 16 * grp;
+        wtile[f] = w13 + ((size_t)e * N + n0 + 16 * f) * (h / 2);
         srow[f] = e13 + ((size_t)e * N + n0 + 16 * f + col) * (h / 32);
     }
     for (int j0 = 0; j0 < cnt; j0 += 16) {
@@ -150,11 +175,80 @@ __global__ __launch_bounds__(256, 2) void stream_gate_up_mx_kernel(
             xst[r] = xq + (size_t)((jr < cnt ? sorted[beg + jr] : sorted[beg]) / k) * h;
         }
 
+        v4f acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+        if constexpr (kLines) {
+        // Two register sets (batch b uses set b & 1 and stage buffer b & 1);
+        // the loop below is unrolled by two so that each set has a name.
+        // A0/A1: K blocks u, u + 1 of both 16-row tiles as whole lines.
+        v8i A0[2][kMxUnrollUp / 2], A1[2][kMxUnrollUp / 2];
+        uint4 S0[2][kMxScaleWords], S1[2][kMxScaleWords];
+        float C0[kMxUnrollUp], C1[kMxUnrollUp];   // activation scales of the batch
+#define MX_ISSUE(A, S, C, bi, b)                                                                     \
+    do {                                                                                             \
+        const int kb0_ = (b) * kMxUnrollUp;                                                          \
+        /* lane l copies bytes 16 l .. 16 l + 15 of the batch (clamped to the row; past the last */ \
+        /* K block they are never read) */                                                           \
+        const int off_ = min(kb0_ * 128 + 16 * lane, h - 16);                                       \
+        _Pragma("unroll") for (int r = 0; r < 4; ++r)                                                \
+            copy16_to_lds(xst[r] + off_, (uint32_t)__builtin_amdgcn_readfirstlane(                  \
+                              lds_addr(stage[bi] + (4 * wave + r) * kMxStageRow)));                  \
+        _Pragma("unroll") for (int f = 0; f < 2; ++f)                                                \
+            _Pragma("unroll") for (int w = 0; w < kMxScaleWords; ++w)                                \
+                S[f][w] = kb0_ + 4 * w < KB ? load_scales4(srow[f], kb0_ + 4 * w, KB, vec)           \
+                                            : make_uint4(0u, 0u, 0u, 0u);                            \
+        /* (KB is even: block u + 1 exists wherever block u does) */                                \
+        _Pragma("unroll") for (int u = 0; u < kMxUnrollUp; u += 2) if (kb0_ + u < KB) {              \
+            _Pragma("unroll") for (int f = 0; f < 2; ++f)                                            \
+                A[f][u >> 1] = load_lines_nt(wtile[f] + (kb0_ + u) * 64, h / 2, lane);               \
+            C[u] = xsr[kb0_ + u];                                                                    \
+            C[u + 1] = xsr[kb0_ + u + 1];                                                            \
+        }                                                                                            \
+    } while (0)
+#define MX_STEP(A, S, C, An, Sn, Cn, bi, b)                                                          \
+    do {                                                                                             \
+        const int kb0_ = (b) * kMxUnrollUp;                                                          \
+        uint8_t* st_ = stage[bi];                                                                    \
+        /* this wave's copies of the batch have landed (and its loads); the barrier publishes */    \
+        /* every wave's, and certifies that the other buffer is no longer read */                   \
+        __builtin_amdgcn_s_waitcnt(vm_wait(0));                                                      \
+        __syncthreads();                                                                             \
+        if ((b) + 1 < nb) MX_ISSUE(An, Sn, Cn, (bi) ^ 1, (b) + 1);                                  \
+        __builtin_amdgcn_sched_barrier(0);                                                           \
+        _Pragma("unroll") for (int u = 0; u < kMxUnrollUp; u += 2) {                                 \
+            if (kb0_ + u < KB) {                                                                     \
+                /* block u of both tiles, then block u + 1 (per tile the same order as one block */ \
+                /* at a time) */                                                                     \
+                uint4 a1[2];                                                                         \
+                const v8i B0 = act_operand(st_ + col * kMxStageRow + u * 128, grp);                  \
+                const float sc0 = valid ? C[u] : 0.0f, sc1 = valid ? C[u + 1] : 0.0f;                \
+                _Pragma("unroll") for (int f = 0; f < 2; ++f) {                                      \
+                    uint4 a0;                                                                        \
+                    lines_to_mx_frags(A[f][u >> 1], &bounce[wave][f][0], lane, col, grp, a0, a1[f]); \
+                    const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};                                          \
+                    const v4f blk0 = mfma_16x16x128_fp4_e4m3(a0, B0, scale_of(S[f][u >> 2], u & 3, grp), z); \
+                    _Pragma("unroll") for (int v = 0; v < 4; ++v) acc[f][v] = fmaf(blk0[v], sc0, acc[f][v]); \
+                }                                                                                    \
+                const v8i B1 = act_operand(st_ + col * kMxStageRow + (u + 1) * 128, grp);            \
+                _Pragma("unroll") for (int f = 0; f < 2; ++f) {                                      \
+                    const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};                                          \
+                    const v4f blk1 = mfma_16x16x128_fp4_e4m3(a1[f], B1, scale_of(S[f][(u + 1) >> 2], (u + 1) & 3, grp), z); \
+                    _Pragma("unroll") for (int v = 0; v < 4; ++v) acc[f][v] = fmaf(blk1[v], sc1, acc[f][v]); \
+                }                                                                                    \
+            }                                                                                        \
+        }                                                                                            \
+    } while (0)
+        MX_ISSUE(A0, S0, C0, 0, 0);
+        for (int b = 0; b < nb; b += 2) {
+            MX_STEP(A0, S0, C0, A1, S1, C1, 0, b);
+            if (b + 1 < nb) MX_STEP(A1, S1, C1, A0, S0, C0, 1, b + 1);
+        }
+#undef MX_STEP
+#undef MX_ISSUE
+        } else {
         // Two register sets (batch b uses set b & 1 and stage buffer b & 1);
         // the loop below is unrolled by two so that each set has a name.
         uint4 A0[2][kMxUnrollUp], S0[2][kMxScaleWords], A1[2][kMxUnrollUp], S1[2][kMxScaleWords];
         float C0[kMxUnrollUp], C1[kMxUnrollUp];   // activation scales of the batch
-        v4f acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
 #define MX_ISSUE(A, S, C, bi, b)                                                                     \
     do {                                                                                             \
         const int kb0_ = (b) * kMxUnrollUp;                                                          \
@@ -204,6 +298,7 @@ __global__ __launch_bounds__(256, 2) void stream_gate_up_mx_kernel(
         }
 #undef MX_STEP
 #undef MX_ISSUE
+        }
         __syncthreads();   // the stage buffers are reused by the next column block
         if (valid)
 #pragma unroll
@@ -219,16 +314,20 @@ __host__ __device__ inline size_t mx_down_lds_bytes(int i) {
 
 // y[p][n]: SiLU(gate) * up of up to 16 routes requantised into LDS, then the
 // expert's w2 rows (32 per wave) streamed with the same block-scaled MFMA.
+// kLines (i a multiple of 256): the weights as whole lines by nontemporal
+// loads, two K blocks per load, as in the gate/up kernel.
+template <bool kLines>
 __global__ __launch_bounds__(256) void stream_down_mx_kernel(
     const float* __restrict__ g, const uint8_t* __restrict__ w2, const uint8_t* __restrict__ e2,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ sorted, const int32_t* __restrict__ active,
     const int32_t* __restrict__ num_active, float* __restrict__ y, int h, int i, int k) {
     extern __shared__ __align__(16) uint8_t lds[];
+    __shared__ __align__(16) uint8_t bounce[kLines ? 4 : 1][2][kLines ? 2048 : 16];   // [wave][f] (kLines)
     const int slot = blockIdx.y;
     if (slot >= *num_active) return;
     const int e = active[slot];
     const int beg = offsets[e], cnt = offsets[e + 1] - beg;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int IB = i / 128;
     const int astride = i + 16;
     uint8_t* a2l = lds;                                            // [16][astride]
@@ -236,10 +335,12 @@ __global__ __launch_bounds__(256) void stream_down_mx_kernel(
     const int n0 = blockIdx.x * kMxRowsPerGroup + wave * kMxRowsPerWave;
     const int col = lane & 15, grp = lane >> 4;
     const uint8_t* wrow[2];
+    const uint8_t* wtile[2];   // (kLines) row 0 of the wave's two 16-row tiles
     const uint8_t* srow[2];
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
         wrow[f] = w2 + ((size_t)e * h + n0 + 16 * f + col) * (i / 2) + 16 * grp;
+        wtile[f] = w2 + ((size_t)e * h + n0 + 16 * f) * (i / 2);
         srow[f] = e2 + ((size_t)e * h + n0 + 16 * f + col) * (i / 32);
     }
 
@@ -256,6 +357,81 @@ __global__ __launch_bounds__(256) void stream_down_mx_kernel(
         const int t0 = wave * 4 + (lane >> 4);
         const int tc = min(t0, ntask - 1), jr0 = tc / IB, b0 = tc - jr0 * IB;
         const GateUp8Mx x0 = load_gate_up8_mx(g + (size_t)sorted[beg + j0 + jr0] * 2 * i + b0 * 128, sub, i);
+        if constexpr (kLines) {
+        v8i A[2][kMxPairsDown];   // K blocks 2q, 2q + 1 of the batch, both 16-row tiles
+        uint32_t sw[2][2 * kMxPairsDown];
+        // a zero K-block offset through an empty asm: the first batch is neither
+        // hoisted out of the route-group loop nor moved above the gate/up reads
+        int kz = 0;
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" : "+s"(kz));
+        // batch kb0's weight lines and scales (past the last K block pair: the
+        // last pair again, never used; IB is even)
+        auto load_w = [&](int kb0) {
+#pragma unroll
+            for (int q = 0; q < kMxPairsDown; ++q) {
+                const int kb = min(kb0 + 2 * q, IB - 2) + kz;
+#pragma unroll
+                for (int f = 0; f < 2; ++f) {
+                    A[f][q] = load_lines_nt(wtile[f] + kb * 64, i / 2, lane);
+                    sw[f][2 * q] = *reinterpret_cast<const uint32_t*>(srow[f] + 4 * kb);
+                    sw[f][2 * q + 1] = *reinterpret_cast<const uint32_t*>(srow[f] + 4 * (kb + 1));
+                }
+            }
+        };
+        load_w(0);
+        __builtin_amdgcn_sched_barrier(0);   // every request of the batch before the SiLU codes
+        // (computed on every row, so that the gate/up loads stay in this block)
+        silu_quant_row_mx(x0, sub, a2l + jr0 * astride + b0 * 128, a2sl + jr0 * IB + b0, sub == 0, t0 < ntask);
+        for (int task = t0 + 16; task < ntask; task += 16) {
+            const int jr = task / IB, b = task - jr * IB;
+            const GateUp8Mx x = load_gate_up8_mx(g + (size_t)sorted[beg + j0 + jr] * 2 * i + b * 128, sub, i);
+            silu_quant_row_mx(x, sub, a2l + jr * astride + b * 128, a2sl + jr * IB + b, sub == 0);
+        }
+        __syncthreads();
+        const bool valid = col < nr;
+        const int p = valid ? sorted[beg + j0 + col] : 0;
+        v4f acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+        for (int kb0 = 0; kb0 < IB; kb0 += 2 * kMxPairsDown) {
+            if (kb0 > 0) load_w(kb0);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int q = 0; q < kMxPairsDown; ++q) {
+                const int kb = kb0 + 2 * q;
+                if (kb < IB) {
+                    // block kb of both tiles, then block kb + 1 (per tile the same
+                    // order as one block at a time); rows of the LDS tile past the
+                    // routes are never read into a stored result (zero scale)
+                    uint4 a1[2];
+                    const v8i B0 = act_operand(a2l + col * astride + kb * 128, grp);
+                    const float sc0 = valid ? a2sl[col * IB + kb] : 0.0f;
+                    const float sc1 = valid ? a2sl[col * IB + kb + 1] : 0.0f;
+#pragma unroll
+                    for (int f = 0; f < 2; ++f) {
+                        uint4 a0;
+                        lines_to_mx_frags(A[f][q], &bounce[wave][f][0], lane, col, grp, a0, a1[f]);
+                        const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+                        const v4f blk = mfma_16x16x128_fp4_e4m3(a0, B0, (int)((sw[f][2 * q] >> (8 * grp)) & 0xFFu), z);
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) acc[f][v] = fmaf(blk[v], sc0, acc[f][v]);
+                    }
+                    const v8i B1 = act_operand(a2l + col * astride + (kb + 1) * 128, grp);
+#pragma unroll
+                    for (int f = 0; f < 2; ++f) {
+                        const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+                        const v4f blk = mfma_16x16x128_fp4_e4m3(a1[f], B1, (int)((sw[f][2 * q + 1] >> (8 * grp)) & 0xFFu), z);
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) acc[f][v] = fmaf(blk[v], sc1, acc[f][v]);
+                    }
+                }
+            }
+        }
+        if (valid)
+#pragma unroll
+            for (int f = 0; f < 2; ++f)
+                *reinterpret_cast<float4*>(y + (size_t)p * h + n0 + 16 * f + grp * 4) =
+                    make_float4(acc[f][0], acc[f][1], acc[f][2], acc[f][3]);
+        } else {
         uint4 A[2][kMxUnrollDown];
         uint32_t sw[2][kMxUnrollDown];
         // a zero K-block offset through an empty asm: the first batch is neither
@@ -315,22 +491,33 @@ __global__ __launch_bounds__(256) void stream_down_mx_kernel(
             for (int f = 0; f < 2; ++f)
                 *reinterpret_cast<float4*>(y + (size_t)p * h + n0 + 16 * f + grp * 4) =
                     make_float4(acc[f][0], acc[f][1], acc[f][2], acc[f][3]);
+        }
     }
 }
 
 hipError_t launch_stream_gate_up_mx(const StreamArgs& a, const uint8_t* xq, const float* xs, const uint8_t* w13,
                                     const uint8_t* e13, float* g, hipStream_t stream) {
     const dim3 grid((2 * a.i) / kMxRowsPerGroup, a.max_slots);
-    launch(stream_gate_up_mx_kernel, grid, dim3(256), 0, stream, xq, xs, w13, e13, a.offsets,
-                       a.sorted, a.active, a.num_active, g, a.h, a.i, a.k);
+    // whole-line weight loads when K blocks pair into 128-byte lines
+    if (a.h % 256 == 0 && ((uintptr_t)w13 & 127u) == 0)
+        launch(stream_gate_up_mx_kernel<true>, grid, dim3(256), 0, stream, xq, xs, w13, e13, a.offsets,
+               a.sorted, a.active, a.num_active, g, a.h, a.i, a.k);
+    else
+        launch(stream_gate_up_mx_kernel<false>, grid, dim3(256), 0, stream, xq, xs, w13, e13, a.offsets,
+               a.sorted, a.active, a.num_active, g, a.h, a.i, a.k);
     return hipGetLastError();
 }
 
 hipError_t launch_stream_down_mx(const StreamArgs& a, const float* g, const uint8_t* w2, const uint8_t* e2,
                                  float* y, hipStream_t stream) {
     const dim3 grid(a.h / kMxRowsPerGroup, a.max_slots);
-    launch(stream_down_mx_kernel, grid, dim3(256), mx_down_lds_bytes(a.i), stream, g, w2, e2,
-                       a.offsets, a.sorted, a.active, a.num_active, y, a.h, a.i, a.k);
+    // whole-line weight loads when K blocks pair into 128-byte lines
+    if (a.i % 256 == 0 && ((uintptr_t)w2 & 127u) == 0)
+        launch(stream_down_mx_kernel<true>, grid, dim3(256), mx_down_lds_bytes(a.i), stream, g, w2, e2,
+               a.offsets, a.sorted, a.active, a.num_active, y, a.h, a.i, a.k);
+    else
+        launch(stream_down_mx_kernel<false>, grid, dim3(256), mx_down_lds_bytes(a.i), stream, g, w2, e2,
+               a.offsets, a.sorted, a.active, a.num_active, y, a.h, a.i, a.k);
     return hipGetLastError();
 }
 
