@@ -154,12 +154,14 @@ def test_mxfp4_wide_decode_shape(moe_mod):
 
 
 @pytest.mark.parametrize("M,h,i,E,k", [(1, 128, 128, 1, 1), (300, 256, 128, 4, 2), (7, 640, 384, 16, 5),
-                                       (5, 256, 2048, 2, 1)])
+                                       (5, 256, 2048, 2, 1), (9, 640, 512, 8, 2), (5, 1536, 384, 8, 3)])
 def test_mxfp4_edge_shapes(moe_mod, M, h, i, E, k):
     """One expert and one K block; a batch beyond the one-launch grouping (300
     tokens, several 16-route column blocks per expert); ragged K batches and
     scale rows not 16-byte aligned (h 640); the largest intermediate size
-    (i 2048: 16 K blocks in the down GEMM)."""
+    (i 2048: 16 K blocks in the down GEMM); whole-line weight loads in one of
+    the two streaming kernels only (h 640 with i 512: down; h 1536 with i 384:
+    gate/up, 12 K blocks, a last batch of 4)."""
     cfg = synth.LayerConfig("mx_edge", M, h, i, E, k, "normal", "test shape")
     _check_layer(moe_mod, _MxLayer(cfg, 91 + M))
 

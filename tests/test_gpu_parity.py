@@ -346,16 +346,19 @@ def test_tiled_paths_agree(dev, moe_mod, M, h, i, E, k):
     log(f"tiled paths agree: M={M} h={h} i={i} E={E} k={k}")
 
 
-@pytest.mark.parametrize("k", [1, 2])
-def test_tiled_route_tile_counts(dev, moe_mod, k):
+@pytest.mark.parametrize("k,E", [(1, 9), (2, 9), (2, 16)])
+def test_tiled_route_tile_counts(dev, moe_mod, k, E):
     """Experts holding 1, 16, 17, 33, 64, 65, 97 and 128 routes (k = 2: every
     token also routes to a ninth expert, which then holds three full M-tiles
     and a ragged last one): every count of 16-route tiles holding a route in
     both 64-route halves of an M-tile, the K-loop instance that also
     multiplies a tile of padding included.  Both tiled paths against the
-    oracle, and against each other bit for bit."""
+    oracle, and against each other bit for bit.  With k = 1, and with k = 2
+    over 16 experts (seven of them unused), the batch has at most 64 routes
+    per expert, so the tiled kernels copy the weight tiles with nontemporal
+    loads, there also for the expert of four M-tiles."""
     counts = [1, 16, 17, 33, 64, 65, 97, 128]
-    M, h, i, E = sum(counts), 512, 256, 9
+    M, h, i = sum(counts), 512, 256
     cfg = synth.LayerConfig(f"rows_m{M}_h{h}_i{i}_e{E}_top{k}", M, h, i, E, k, "normal", "tile row counts")
     owner = np.repeat(np.arange(8), counts)[np.random.default_rng(5).permutation(M)]   # spread over the batch
     logits = np.zeros((M, E), np.float32)
